@@ -1,0 +1,257 @@
+// C-ABI host code of the activation-sparse FFN decode library: argument validation,
+// handle creation, workspace carve-up, load-balanced neuron ranges, and the offline
+// helpers. Every check happens before anything is enqueued; no C++ exception escapes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "../../include/sparse_ffn.h"
+#include "sffn_internal.h"
+
+struct sparse_ffn_s {
+  sffn_desc desc;
+  sffn::LayerDev L;
+  int max_batch;
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int t) { return t == SFFN_F32 || t == SFFN_F16; }
+
+// Shape and pointer checks shared by workspace sizing and create (no HIP calls).
+int check_desc(const sffn_desc* d) {
+  if (!d) return SFFN_ERR_INVALID;
+  if (d->d <= 0 || d->d_ffn <= 0 || d->rank <= 0) return SFFN_ERR_INVALID;
+  if (d->max_batch < 1 || d->max_batch > SFFN_MAX_BATCH) return SFFN_ERR_INVALID;
+  if (d->gated != 0 && d->gated != 1) return SFFN_ERR_INVALID;
+  if (!dtype_ok(d->w_dtype) || !dtype_ok(d->p_dtype)) return SFFN_ERR_INVALID;
+  if (d->d % 8 != 0 || d->rank % 8 != 0) return SFFN_ERR_INVALID;
+  if (d->d_ffn > (1 << 24)) return SFFN_ERR_UNSUPPORTED;
+  return SFFN_OK;
+}
+
+int check_ptrs(const sffn_desc* d) {
+  if (!d->w_act || !d->w_down_t || !d->p1 || !d->p2 || !d->workspace) return SFFN_ERR_INVALID;
+  if (!aligned16(d->w_act) || !aligned16(d->w_down_t) || !aligned16(d->p1) ||
+      !aligned16(d->p2) || !aligned16(d->workspace))
+    return SFFN_ERR_INVALID;
+  if (d->b_out && !aligned16(d->b_out)) return SFFN_ERR_INVALID;
+  return SFFN_OK;
+}
+
+// Split neurons [0, n) into contiguous ranges of at most MID_RANGE_MAX neurons whose
+// expected costs (predictor row bytes plus expected activation frequency times the bytes
+// of the neuron's two weight rows) are about equal. With no frequencies every neuron
+// costs the same. The greedy cut is deterministic.
+std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_bytes,
+                                     double act_row_bytes, int target_groups) {
+  std::vector<double> cost(n);
+  for (int i = 0; i < n; ++i) {
+    double f = freq ? (double)freq[i] : 0.0;
+    if (!(f >= 0.0)) f = 0.0;
+    if (f > 1.0) f = 1.0;
+    cost[i] = p2_row_bytes + f * act_row_bytes;
+  }
+  const double total = std::accumulate(cost.begin(), cost.end(), 0.0);
+  double target = total / std::max(1, target_groups);
+  for (int attempt = 0; attempt < 64; ++attempt) {
+    std::vector<int32_t> rs{0};
+    double acc = 0.0;
+    int len = 0;
+    for (int i = 0; i < n; ++i) {
+      if (len > 0 && (len == sffn::MID_RANGE_MAX || acc + cost[i] > target)) {
+        rs.push_back(i);
+        acc = 0.0;
+        len = 0;
+      }
+      acc += cost[i];
+      ++len;
+    }
+    rs.push_back(n);
+    if ((int)rs.size() - 1 <= sffn::G_MID_MAX) return rs;
+    target *= 1.25;
+  }
+  return {};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_ffn_status_string(int status) {
+  switch (status) {
+    case SFFN_OK: return "ok";
+    case SFFN_ERR_INVALID: return "invalid argument";
+    case SFFN_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case SFFN_ERR_HIP: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sparse_ffn_workspace_bytes(const sffn_desc* desc) {
+  if (check_desc(desc) != SFFN_OK) return 0;
+  return sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch);
+}
+
+int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
+  try {
+    if (!out) return SFFN_ERR_INVALID;
+    int rc = check_desc(desc);
+    if (rc != SFFN_OK) return rc;
+    rc = check_ptrs(desc);
+    if (rc != SFFN_OK) return rc;
+    const size_t need = sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch);
+    if (desc->workspace_bytes < need) return SFFN_ERR_INVALID;
+
+    sffn::LayerDev L{};
+    L.d = desc->d;
+    L.n = desc->d_ffn;
+    L.r = desc->rank;
+    L.gated = desc->gated;
+    L.w_f16 = desc->w_dtype == SFFN_F16;
+    L.p_f16 = desc->p_dtype == SFFN_F16;
+    L.tau = desc->threshold;
+    L.w_act = desc->w_act;
+    L.w_down_t = desc->w_down_t;
+    L.b_act = desc->b_act;
+    L.b_out = desc->b_out;
+    L.p1 = desc->p1;
+    L.p2 = desc->p2;
+    L.p_bias = desc->p_bias;
+    sffn::carve_workspace(L, desc->workspace, desc->max_batch);
+    if (!sffn::shape_supported(L, false)) return SFFN_ERR_UNSUPPORTED;
+
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SFFN_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return SFFN_ERR_HIP;
+    L.n_cus = cus;
+    L.g_gather = std::max(1, 2 * cus);
+
+    const double wb = desc->w_dtype == SFFN_F16 ? 2.0 : 4.0;
+    const double pb = desc->p_dtype == SFFN_F16 ? 2.0 : 4.0;
+    const double act_row = wb * desc->d * (desc->gated ? 3.0 : 2.0);
+    const int target = std::max(2 * cus, (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX);
+    std::vector<int32_t> rs = balanced_ranges(desc->d_ffn, desc->neuron_freq, pb * desc->rank,
+                                              act_row, std::min(target, sffn::G_MID_MAX));
+    L.g_mid = rs.empty() ? 0 : (int)rs.size() - 1;
+    if (L.g_mid > 0) {
+      if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
+          hipSuccess)
+        return SFFN_ERR_HIP;
+    }
+    sparse_ffn_s* h = new (std::nothrow) sparse_ffn_s;
+    if (!h) return SFFN_ERR_HIP;
+    h->desc = *desc;
+    h->desc.neuron_freq = nullptr;  // host array is only read here
+    h->L = L;
+    h->max_batch = desc->max_batch;
+    *out = h;
+    return SFFN_OK;
+  } catch (...) {
+    return SFFN_ERR_HIP;
+  }
+}
+
+int sparse_ffn_destroy(sparse_ffn_t h) {
+  delete h;
+  return SFFN_OK;
+}
+
+int sparse_ffn_predict(sparse_ffn_t h, const float* x, int32_t B, float* scores, void* stream) {
+  if (!h || !x || !scores || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(scores)) return SFFN_ERR_INVALID;
+  return sffn::launch_predict(h->L, x, B, scores, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_compact(sparse_ffn_t h, const float* scores, int32_t B, int32_t* idx,
+                       int32_t* count, uint64_t* tokmask, void* stream) {
+  if (!h || !scores || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (B > 1 && !tokmask) return SFFN_ERR_INVALID;
+  return sffn::launch_compact(h->L, scores, B, idx, count, tokmask,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t* idx,
+                       const int32_t* count, const uint64_t* tokmask, float* y, void* stream) {
+  if (!h || !x || !idx || !count || !y || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
+  return sffn::launch_forward(h->L, x, B, idx, count, tokmask, y,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
+                      int32_t* count, uint64_t* tokmask, float* scores, void* stream) {
+  if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
+  if (!sffn::shape_supported(h->L, true)) return SFFN_ERR_UNSUPPORTED;
+  return sffn::launch_decode(h->L, x, B, y, idx, count, tokmask, scores,
+                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_profile_counts(const void* w_act, int32_t w_dtype, int32_t gated,
+                              const float* b_act, int32_t d, int32_t d_ffn, const float* x,
+                              int32_t N, int64_t* counts, void* stream) {
+  if (!w_act || !x || !counts || d <= 0 || d_ffn <= 0 || N <= 0) return SFFN_ERR_INVALID;
+  if (!dtype_ok(w_dtype) || (gated != 0 && gated != 1)) return SFFN_ERR_INVALID;
+  return sffn::launch_profile_counts(w_act, w_dtype == SFFN_F16, gated, b_act, d, d_ffn, x, N,
+                                     counts, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_permutation(const int64_t* counts, int32_t d_ffn, int32_t n_hot,
+                           int32_t* perm_new_to_old) {
+  if (!counts || !perm_new_to_old || d_ffn <= 0 || n_hot < 0 || n_hot > d_ffn)
+    return SFFN_ERR_INVALID;
+  try {
+    std::vector<int32_t> order(d_ffn);
+    std::iota(order.begin(), order.end(), 0);
+    // hottest first; equal counts keep the smaller original index first
+    std::partial_sort(order.begin(), order.begin() + n_hot, order.end(),
+                      [counts](int32_t a, int32_t b) {
+                        return counts[a] != counts[b] ? counts[a] > counts[b] : a < b;
+                      });
+    std::vector<char> hot(d_ffn, 0);
+    for (int32_t k = 0; k < n_hot; ++k) {
+      perm_new_to_old[k] = order[k];
+      hot[order[k]] = 1;
+    }
+    int32_t k = n_hot;
+    for (int32_t i = 0; i < d_ffn; ++i)
+      if (!hot[i]) perm_new_to_old[k++] = i;
+    return SFFN_OK;
+  } catch (...) {
+    return SFFN_ERR_HIP;
+  }
+}
+
+int sparse_ffn_pack_rows(const void* src, const int32_t* perm, void* dst, int32_t rows,
+                         int64_t row_bytes, int64_t dst_stride_bytes, void* stream) {
+  if (dst_stride_bytes == 0) dst_stride_bytes = row_bytes;
+  if (!src || !perm || !dst || rows <= 0 || row_bytes <= 0 || row_bytes % 4 != 0 ||
+      dst_stride_bytes < row_bytes || dst_stride_bytes % 4 != 0)
+    return SFFN_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(src) & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u))
+    return SFFN_ERR_INVALID;
+  return sffn::launch_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal interface between the C-ABI host code (sffn_api.hip) and the kernels
+// (sffn_kernels.hip). Not installed; the public interface is include/sparse_ffn.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sffn {
+
+// Device-side view of one layer plus the workspace carve-up.
+struct LayerDev {
+  int d, n, r;
+  int gated;
+  int w_f16, p_f16;  // 1 = fp16 storage, 0 = fp32
+  float tau;
+  const void* w_act;
+  const void* w_down_t;
+  const float* b_act;
+  const float* b_out;
+  const void* p1;
+  const void* p2;
+  const float* p_bias;
+  // workspace regions
+  float* q;            // [max_batch][r] predictor stage-1 output
+  float* h_full;       // [n][B] activations by neuron (stride B of the call)
+  uint64_t* tok_full;  // [n] token bits by neuron
+  int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
+  int32_t* cnt_g;      // [g_mid] active count per middle workgroup
+  int32_t* list_g;     // [g_mid][64] ascending active list per middle workgroup
+  int32_t* tile_cnt;   // [n_tiles] compaction tile counts
+  uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
+  // launch geometry fixed at create time
+  int g_mid;     // workgroups of the fused middle kernel (<= G_MID_MAX)
+  int n_tiles;   // compaction tiles of 256 neurons
+  int g_gather;  // workgroups of the balanced gather
+  int n_cus;     // compute units on the device
+};
+
+constexpr int G_MID_MAX = 1024;  // most workgroups the fused middle kernel may use
+constexpr int MID_RANGE_MAX = 64;  // most neurons one middle workgroup may own
+
+// workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
+size_t workspace_bytes(int d, int n, int r, int max_batch);
+void carve_workspace(LayerDev& L, void* ws, int max_batch);
+// whether kernels exist for this shape (fused = the single-call decode path)
+bool shape_supported(const LayerDev& L, bool fused);
+
+// launchers; each returns hipGetLastError() after enqueueing
+hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s);
+hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t* idx,
+                          int32_t* count, uint64_t* tokmask, hipStream_t s);
+hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                          const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s);
+hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
+                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s);
+hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const float* b_act,
+                                 int d, int n, const float* x, int N, int64_t* counts,
+                                 hipStream_t s);
+hipError_t launch_pack_rows(const void* src, const int32_t* perm, void* dst, int rows,
+                            int64_t row_bytes, int64_t dst_stride_bytes, hipStream_t s);
+
+}  // namespace sffn

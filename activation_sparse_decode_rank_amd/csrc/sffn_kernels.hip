@@ -1,0 +1,975 @@
+// HIP kernels of the activation-sparse FFN decode path, written for gfx950 (CDNA4):
+// 64-lane wavefronts, 256-thread workgroups, 16-byte vector loads, LDS staging.
+//
+// The method (what is computed) comes from the pages:
+//  - a predictor scores every neuron and only the predicted-active ones are computed
+//    (unite.ai PowerInfer overview, "Fase en línea"; novita.ai activation-sparsity
+//    article, section 單層計算優化);
+//  - neuron-aware operators touch whole rows of the up matrix and whole rows of the
+//    transposed down matrix, with no sparse-format conversion (unite.ai overview,
+//    "Operador consciente de neuronas");
+//  - ReLU between up and down (novita.ai article, section 激活稀疏性的可行性), on the gate in
+//    the ReLU-fied gated FFN (section 第一階段); gate and up rows of one neuron are stored
+//    together because they co-activate (PowerInfer-2 article, section 4.4);
+//  - memory is read in whole coalesced blocks and operators are fused (novita.ai article,
+//    section 工程影響).
+// How it is computed here is specific to this chip: kernel boundaries are the only
+// grid-wide synchronization (they cost about a microsecond and a half inside a HIP graph,
+// far less than any in-kernel grid barrier on this part), no atomics are used at all, and
+// every reduction has a fixed order, so results are bit-reproducible.
+#include "sffn_internal.h"
+
+#include <algorithm>
+
+namespace sffn {
+namespace {
+
+constexpr int TPB = 256;        // threads per workgroup for every kernel here
+constexpr int MAXB = 64;        // tokens per call (one bit each in a 64-bit word)
+constexpr int LOADS = 16;       // 16-byte loads a thread keeps in flight in the row loops
+constexpr int LIST_CAP = 8192;  // active-list window held in LDS by the down kernel
+constexpr int X_LDS_MAX = 48 * 1024;  // tokens are staged in LDS when they fit in this
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// A "chunk" is 16 bytes of weights: 8 fp16 or 4 fp32 elements.
+template <bool F16>
+struct Elt {
+  static constexpr int EPC = F16 ? 8 : 4;
+};
+
+__device__ __forceinline__ u32x4 ld_chunk(const void* base, size_t chunk) {
+  return reinterpret_cast<const u32x4*>(base)[chunk];
+}
+
+template <bool F16>
+__device__ __forceinline__ void unpack(const u32x4& v, float* f) {
+  if constexpr (F16) {
+    half8_t h = __builtin_bit_cast(half8_t, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)h[e];
+  } else {
+    float4_t g = __builtin_bit_cast(float4_t, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = g[e];
+  }
+}
+
+// acc + sum_e w[e] * x[e], e ascending
+template <bool F16>
+__device__ __forceinline__ float dot_chunk(const u32x4& v, const float* x, float acc) {
+  float f[Elt<F16>::EPC];
+  unpack<F16>(v, f);
+#pragma unroll
+  for (int e = 0; e < Elt<F16>::EPC; ++e) acc = fmaf(f[e], x[e], acc);
+  return acc;
+}
+
+template <int EPC>
+__device__ __forceinline__ void load_x(const float* p, float* xs) {
+  const float4_t* q = reinterpret_cast<const float4_t*>(p);
+#pragma unroll
+  for (int u = 0; u < EPC / 4; ++u) {
+    float4_t v = q[u];
+    xs[4 * u + 0] = v[0];
+    xs[4 * u + 1] = v[1];
+    xs[4 * u + 2] = v[2];
+    xs[4 * u + 3] = v[3];
+  }
+}
+
+// Sum over the L consecutive lanes of an aligned lane group (L a power of two <= 64).
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Cooperative copy of x [B][d] fp32 into LDS.
+__device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats) {
+  const float4_t* src = reinterpret_cast<const float4_t*>(x);
+  float4_t* dst = reinterpret_cast<float4_t*>(s_x);
+  for (int u = threadIdx.x; u < n_floats / 4; u += TPB) dst[u] = src[u];
+}
+
+// ============================================================================ predictor
+// Stage 1: q[b][j] = P1[j] . x_b. One workgroup per predictor row; each thread holds up
+// to MAXC chunks of the row in registers and reuses them for every token group of TBG.
+template <bool PF16, int TBG>
+__global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
+                                                     const float* __restrict__ x, int d, int r,
+                                                     int B, float* __restrict__ q) {
+  constexpr int EPC = Elt<PF16>::EPC;
+  constexpr int MAXC = 8;
+  const int j = blockIdx.x, tid = threadIdx.x;
+  const int nch = d / EPC;
+  const size_t row0 = (size_t)j * nch;
+  __shared__ float red[TPB / 64][MAXB];
+  u32x4 wv[MAXC];
+#pragma unroll
+  for (int m = 0; m < MAXC; ++m) {
+    const int c = tid + m * TPB;
+    if (c < nch) wv[m] = ld_chunk(p1, row0 + c);
+  }
+  for (int b0 = 0; b0 < B; b0 += TBG) {
+    float acc[TBG];
+#pragma unroll
+    for (int b = 0; b < TBG; ++b) acc[b] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MAXC; ++m) {
+      const int c = tid + m * TPB;
+      if (c < nch) {
+        float f[EPC];
+        unpack<PF16>(wv[m], f);
+#pragma unroll
+        for (int b = 0; b < TBG; ++b) {
+          if (b0 + b < B) {
+            float xs[EPC];
+            load_x<EPC>(x + (size_t)(b0 + b) * d + (size_t)c * EPC, xs);
+#pragma unroll
+            for (int e2 = 0; e2 < EPC; ++e2) acc[b] = fmaf(f[e2], xs[e2], acc[b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < TBG; ++b) {
+      const float v = group_sum<64>(acc[b]);
+      if ((tid & 63) == 0 && b0 + b < B) red[tid >> 6][b0 + b] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < B) q[(size_t)tid * r + j] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+// scores[b][i] = P2[i] . q_b + c_i for rows [row_begin, row_end) of this workgroup.
+template <bool PF16, int L, int CPLP, int PASSES>
+__global__ __launch_bounds__(TPB) void k_pred_scores(const void* __restrict__ p2,
+                                                     const float* __restrict__ pbias,
+                                                     const float* __restrict__ q, int n, int r,
+                                                     int B, float* __restrict__ scores) {
+  constexpr int EPC = Elt<PF16>::EPC;
+  constexpr int RPP = TPB / L;
+  const int tid = threadIdx.x;
+  const int g = tid / L, gl = tid % L;
+  const int nchp = r / EPC;
+  const int row_base = blockIdx.x * RPP * PASSES;
+  u32x4 wv[PASSES][CPLP];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = row_base + p * RPP + g;
+#pragma unroll
+    for (int m = 0; m < CPLP; ++m) {
+      const int c = gl + m * L;
+      if (row < n && c < nchp) wv[p][m] = ld_chunk(p2, (size_t)row * nchp + c);
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    float qs[CPLP][EPC];
+#pragma unroll
+    for (int m = 0; m < CPLP; ++m) {
+      const int c = gl + m * L;
+      if (c < nchp) load_x<EPC>(q + (size_t)b * r + (size_t)c * EPC, qs[m]);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = row_base + p * RPP + g;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < CPLP; ++m) {
+        const int c = gl + m * L;
+        if (c < nchp && row < n) acc = dot_chunk<PF16>(wv[p][m], qs[m], acc);
+      }
+      acc = group_sum<L>(acc);
+      if (gl == 0 && row < n) scores[(size_t)b * n + row] = acc + (pbias ? pbias[row] : 0.f);
+    }
+  }
+}
+
+// ============================================================================ compaction
+// Pass 1, one thread per neuron, 256-neuron tiles: token bits, union ballot words, and
+// the tile's active count.
+__global__ __launch_bounds__(TPB) void k_cmp_tiles(const float* __restrict__ scores, int n,
+                                                   int B, float tau,
+                                                   uint64_t* __restrict__ tok_full,
+                                                   uint64_t* __restrict__ words,
+                                                   int32_t* __restrict__ tile_cnt) {
+  __shared__ int s_cnt[TPB / 64];
+  const int i = blockIdx.x * TPB + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t bits = 0;
+  if (i < n)
+    for (int b = 0; b < B; ++b)
+      if (scores[(size_t)b * n + i] > tau) bits |= (uint64_t)1 << b;  // NaN compares false
+  const uint64_t word = __ballot(bits != 0);
+  if (i < n) tok_full[i] = bits;
+  if (lane == 0) {
+    if (i < n) words[i >> 6] = word;
+    s_cnt[wave] = __popcll(word);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) tile_cnt[blockIdx.x] = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+}
+
+// Pass 2, same tiling: exclusive prefix of the tile counts, then every active neuron
+// writes itself at its ascending position. The last tile writes the total.
+__global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict__ tok_full,
+                                                     const uint64_t* __restrict__ words,
+                                                     const int32_t* __restrict__ tile_cnt, int n,
+                                                     int n_tiles, int32_t* __restrict__ idx,
+                                                     int32_t* __restrict__ count,
+                                                     uint64_t* __restrict__ tokmask) {
+  __shared__ int s_off;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < 64) {
+    int acc = 0;
+    for (int u = lane; u < t; u += 64) acc += tile_cnt[u];
+    acc = wave_sum_i(acc);
+    if (lane == 0) s_off = acc;
+  }
+  __syncthreads();
+  const int i = t * TPB + threadIdx.x;
+  if (i < n) {
+    const uint64_t word = words[i >> 6];
+    if ((word >> lane) & 1) {
+      int before = 0;
+      for (int v = 0; v < wave; ++v) before += __popcll(words[t * 4 + v]);
+      const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+      const int k = s_off + before + __popcll(lower);
+      idx[k] = i;
+      if (tokmask) tokmask[k] = tok_full[i];
+    }
+  }
+  if (t == n_tiles - 1 && threadIdx.x == 0) *count = s_off + tile_cnt[t];
+}
+
+// ============================================================================ gather
+// Workgroup-cooperative gather-GEMV + ReLU over a list of active rows. All 256 threads
+// share every row: thread t reads chunks t, t+256, ... of each row (16-byte loads, so a
+// wave reads 1 KB contiguous per instruction), and up to RB rows' loads are in flight at
+// once however many rows the workgroup owns. Each chunk is widened once per group of TBG
+// tokens. Per-row partial dots are reduced in a fixed order (wave shuffle tree, then the
+// four waves in order).
+//   plain: h = relu(w[i] . x + b[i]);  gated (row = [gate | up]): h = relu(g . x + b) * (u . x)
+// h_full[i*B + b] is written for every token (0 when the token's bit is clear).
+template <bool WF16, bool GATED, int CPT, int TBG>
+struct Gather {
+  static constexpr int EPC = Elt<WF16>::EPC;
+  static constexpr int LOADS_G = 8;
+  static constexpr int RB = (LOADS_G / CPT) > 0 ? (LOADS_G / CPT) : 1;  // rows per batch
+  static constexpr int NV = GATED ? 2 : 1;
+  static constexpr int RED_FLOATS = 4 * RB * TBG * NV;
+
+  // rows: LDS list of `nrows` neuron ids; bits: LDS token bits per row
+  __device__ static void run(const void* __restrict__ w_act, const float* __restrict__ b_act,
+                             const float* xsrc, int d, int n, int B, const int32_t* rows,
+                             const uint64_t* bits, int nrows, float* __restrict__ h_full,
+                             float* s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = d / EPC;                  // chunks per matrix row
+    const int rowch = GATED ? 2 * nch : nch;  // chunks per stored row
+    for (int base = 0; base < nrows; base += RB) {
+      const int nb = min(RB, nrows - base);
+      u32x4 wv[RB][CPT];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int ri = rr < nb ? rows[base + rr] : -1;
+        if (ri >= 0 && ri < n) {
+          const size_t row0 = (size_t)ri * rowch;
+#pragma unroll
+          for (int m = 0; m < CPT; ++m) {
+            const int c = tid + m * TPB;
+            if (c < rowch) wv[rr][m] = ld_chunk(w_act, row0 + c);
+          }
+        }
+      }
+      for (int b0 = 0; b0 < B; b0 += TBG) {
+        float acc[RB][TBG][NV];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int b = 0; b < TBG; ++b)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[rr][b][v] = 0.f;
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+          const int c = tid + m * TPB;
+          if (c < rowch) {
+            const bool up = GATED && c >= nch;
+            const int xc = up ? c - nch : c;
+            float xs[TBG][EPC];
+#pragma unroll
+            for (int b = 0; b < TBG; ++b)
+              if (b0 + b < B) load_x<EPC>(xsrc + (size_t)(b0 + b) * d + (size_t)xc * EPC, xs[b]);
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+              if (rr < nb) {
+                float f[EPC];
+                unpack<WF16>(wv[rr][m], f);
+#pragma unroll
+                for (int b = 0; b < TBG; ++b) {
+                  if (b0 + b < B) {
+                    float a = acc[rr][b][up ? NV - 1 : 0];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) a = fmaf(f[e], xs[b][e], a);
+                    acc[rr][b][up ? NV - 1 : 0] = a;
+                  }
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int b = 0; b < TBG; ++b)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              const float s = group_sum<64>(acc[rr][b][v]);
+              if (lane == 0) s_red[((wave * RB + rr) * TBG + b) * NV + v] = s;
+            }
+        __syncthreads();
+        if (tid < nb * TBG) {
+          const int rr = tid / TBG, b = tid % TBG;
+          const int i = rows[base + rr];
+          if (b0 + b < B && i >= 0 && i < n) {
+            const bool on = (bits[base + rr] >> (b0 + b)) & 1;
+            float h = 0.f;
+            if (on) {
+              float a = s_red[((0 * RB + rr) * TBG + b) * NV];
+              a += s_red[((1 * RB + rr) * TBG + b) * NV];
+              a += s_red[((2 * RB + rr) * TBG + b) * NV];
+              a += s_red[((3 * RB + rr) * TBG + b) * NV];
+              a += b_act ? b_act[i] : 0.f;
+              h = a > 0.f ? a : 0.f;
+              if (GATED) {
+                float u = s_red[((0 * RB + rr) * TBG + b) * NV + 1];
+                u += s_red[((1 * RB + rr) * TBG + b) * NV + 1];
+                u += s_red[((2 * RB + rr) * TBG + b) * NV + 1];
+                u += s_red[((3 * RB + rr) * TBG + b) * NV + 1];
+                h = h * u;
+              }
+            }
+            h_full[(size_t)i * B + b0 + b] = h;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+};
+
+// Balanced gather for the forward entry point: workgroup w takes the contiguous slice
+// [w*per, (w+1)*per) of the given ascending list (per = ceil(count / grid)).
+template <bool WF16, bool GATED, int CPT, int TBG>
+__global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
+                                                const float* __restrict__ b_act,
+                                                const float* __restrict__ x, int d, int n, int B,
+                                                const int32_t* __restrict__ idx,
+                                                const int32_t* __restrict__ count,
+                                                const uint64_t* __restrict__ tokmask,
+                                                float* __restrict__ h_full, int x_lds) {
+  using G = Gather<WF16, GATED, CPT, TBG>;
+  extern __shared__ float4_t s_dyn4[];
+  float* s_x = reinterpret_cast<float*>(s_dyn4);
+  __shared__ int32_t s_rows[LIST_CAP / 8];
+  __shared__ uint64_t s_bits[LIST_CAP / 8];
+  __shared__ float s_red[G::RED_FLOATS];
+  const int cnt = min(max(*count, 0), n);  // a count beyond the list is clamped
+  const int per = (cnt + gridDim.x - 1) / gridDim.x;
+  const int k0 = min(cnt, (int)blockIdx.x * per), k1 = min(cnt, k0 + per);
+  if (k0 >= k1) return;
+  if (x_lds) stage_x(s_x, x, B * d);
+  const float* xsrc = x_lds ? s_x : x;
+  for (int kb = k0; kb < k1; kb += LIST_CAP / 8) {
+    const int nr = min(LIST_CAP / 8, k1 - kb);
+    __syncthreads();
+    for (int u = threadIdx.x; u < nr; u += TPB) {
+      s_rows[u] = idx[kb + u];
+      s_bits[u] = tokmask ? tokmask[kb + u] : ~(uint64_t)0;
+    }
+    __syncthreads();
+    G::run(w_act, b_act, xsrc, d, n, B, s_rows, s_bits, nr, h_full, s_red);
+  }
+}
+
+// ============================================================================ fused middle
+// One kernel for predictor stage 2, threshold, per-workgroup compaction and the gather.
+// Workgroup w owns the contiguous neuron range [rs[w], rs[w+1]) (at most 64 neurons; the
+// ranges are balanced offline by expected cost, so the hot prefix is split into short
+// ranges). Its P2 rows form one contiguous block, read linearly (thread t takes chunks
+// t, t+256, ...); with NCHP = chunks per P2 row a power of two, a row's chunks sit in NCHP
+// consecutive lanes (or, above 64, in consecutive waves). It writes: cnt_g[w]; its
+// ascending active list at list_g[w*64 ..]; token bits tok_full[i] and activations
+// h_full[i*B + b] for its active neurons; and scores if requested.
+template <bool F16, bool GATED, int CPT, int TBG>
+__global__ __launch_bounds__(TPB) void k_fused_mid(
+    const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
+    int r, const void* __restrict__ w_act, const float* __restrict__ b_act,
+    const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
+    int32_t* __restrict__ cnt_g, int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_full,
+    float* __restrict__ h_full, float* __restrict__ scores, int x_lds) {
+  constexpr int EPC = Elt<F16>::EPC;
+  constexpr int PL = 16;  // P2 chunks a thread keeps in flight
+  using G = Gather<F16, GATED, CPT, TBG>;
+  extern __shared__ float4_t s_dyn4[];
+  float* s_x = reinterpret_cast<float*>(s_dyn4);
+  __shared__ uint64_t s_tok[64];
+  __shared__ int32_t s_rows[64];
+  __shared__ uint64_t s_bits[64];
+  __shared__ float s_part[64 * 4];  // per-row partial scores from up to 4 waves
+  __shared__ float s_red[G::RED_FLOATS];
+  __shared__ int s_nact;
+
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = rs[w], r1 = rs[w + 1];
+  const int nown = r1 - r0;  // 1..64
+  const int nchp = r / EPC;  // power of two, <= 128
+  const int lg = 31 - __clz(nchp);
+  const int total = nown * nchp;
+  const int grp = nchp < 64 ? nchp : 64;  // lanes of one row inside a wave
+  const int wpr = nchp > 64 ? nchp / 64 : 1;  // waves per row
+  const size_t blk0 = (size_t)r0 * nchp;
+
+  if (tid < 64) s_tok[tid] = 0;
+  if (x_lds) stage_x(s_x, x, B * d);
+  for (int c0 = 0; c0 < total; c0 += PL * TPB) {
+    u32x4 wv[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
+      const int f = c0 + tid + m * TPB;
+      if (f < total) wv[m] = ld_chunk(p2, blk0 + f);
+    }
+    __syncthreads();
+    const int pos = tid & (nchp - 1);  // same for every m since 256 % nchp == 0
+    for (int b = 0; b < B; ++b) {
+      float qs[EPC];
+      load_x<EPC>(q + (size_t)b * r + (size_t)pos * EPC, qs);
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int f = c0 + tid + m * TPB;
+        float acc = 0.f;
+        if (f < total) acc = dot_chunk<F16>(wv[m], qs, 0.f);
+        for (int o = grp / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (f < total && (lane & (grp - 1)) == 0) {
+          const int j = f >> lg;
+          s_part[j * 4 + (wpr > 1 ? (wave & (wpr - 1)) : 0)] = acc;
+        }
+      }
+      __syncthreads();
+      if (tid < nown && tid * nchp >= c0 && tid * nchp < c0 + PL * TPB) {
+        // rows whose chunks all lie in this pass: finish score, threshold
+        const int j = tid;
+        float s = s_part[j * 4];
+        for (int u = 1; u < wpr; ++u) s += s_part[j * 4 + u];
+        const int i = r0 + j;
+        s += pbias ? pbias[i] : 0.f;
+        if (scores) scores[(size_t)b * n + i] = s;
+        if (s > tau) s_tok[j] |= (uint64_t)1 << b;
+      }
+      __syncthreads();
+    }
+  }
+  // ---- compaction of the owned range (one wave: ballot + prefix popcount)
+  if (tid < 64) {
+    const uint64_t bits = (tid < nown) ? s_tok[tid] : 0;
+    const bool act = bits != 0;
+    const uint64_t word = __ballot(act);
+    const uint64_t lower = tid ? (word & ((~(uint64_t)0) >> (64 - tid))) : 0;
+    if (act) {
+      const int pos = __popcll(lower);
+      const int i = r0 + tid;
+      s_rows[pos] = i;
+      s_bits[pos] = bits;
+      list_g[(size_t)w * 64 + pos] = i;
+      tok_full[i] = bits;
+    }
+    if (tid == 0) {
+      s_nact = __popcll(word);
+      cnt_g[w] = __popcll(word);
+    }
+  }
+  __syncthreads();
+  // ---- gather + ReLU over the owned active rows
+  G::run(w_act, b_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_nact, h_full, s_red);
+}
+
+// ============================================================================ down
+// Down projection with column ownership: workgroup w owns 2 chunks (32 bytes) of every
+// row of W_down^T, i.e. 16 fp16 / 8 fp32 output columns, and sums over the whole active
+// list, so no cross-workgroup reduction exists. The four workgroups that share a 128-byte
+// line are placed on the same XCD (workgroups are dealt to the 8 XCDs round-robin), so
+// each line is fetched into one L2 once. Thread t handles chunk t&1 and the active rows
+// k = t>>1, t>>1 + 128, ... (LOADS rows in flight), then the 128 row-lane partials are
+// summed in ascending order.
+// LIST_FROM_WG: the active list is the concatenation, in workgroup order, of the fused
+// middle kernel's per-workgroup lists (which is ascending); this kernel also writes idx,
+// count and tokmask. Otherwise the list is idx[0..*count).
+template <bool WF16, bool LIST_FROM_WG, int TB>
+__global__ __launch_bounds__(TPB) void k_down(
+    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const float* __restrict__ h_full, int d, int n, int B, const int32_t* __restrict__ idx_in,
+    const int32_t* __restrict__ count_in, const int32_t* __restrict__ cnt_g,
+    const int32_t* __restrict__ list_g, int g_mid, const uint64_t* __restrict__ tok_full,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
+    uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
+  constexpr int EPC = Elt<WF16>::EPC;
+  constexpr int NRL = TPB / 2;  // row lanes
+  extern __shared__ float4_t s_dyn4[];
+  int32_t* s_list = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
+  float* s_red = reinterpret_cast<float*>(s_dyn4);       // aliases s_list after the sum
+  __shared__ int32_t s_off[1024 + 1];                    // per-middle-workgroup offsets
+  __shared__ int s_total;
+
+  const int tid = threadIdx.x;
+  const int nch = d / EPC;
+  const int G = gridDim.x;
+  int s = blockIdx.x;
+  if ((G & 7) == 0) s = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int ch = tid & 1, rl = tid >> 1;
+  const int chunk = 2 * s + ch;
+
+  int total;
+  if (LIST_FROM_WG) {
+    // exclusive scan of the middle kernel's per-workgroup counts (g_mid <= 1024)
+    if (tid < 64) {
+      // each lane sums a contiguous block of counts, then a lane-ordered scan
+      const int per = (g_mid + 63) / 64;
+      const int a0 = tid * per, a1 = min(g_mid, a0 + per);
+      int sum = 0;
+      for (int u = a0; u < a1; ++u) sum += cnt_g[u];
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += v;
+      }
+      int run = incl - sum;
+      for (int u = a0; u < a1; ++u) {
+        s_off[u] = run;
+        run += cnt_g[u];
+      }
+      if (tid == 63) s_total = incl;
+    }
+    __syncthreads();
+    total = s_total;
+    if (blockIdx.x == 0 && tid == 0) *count_out = total;
+  } else {
+    total = min(max(*count_in, 0), n);  // a count beyond the list is clamped
+  }
+
+  float acc[TB][EPC];
+  const int ntg = (B + TB - 1) / TB;
+  for (int tg = 0; tg < ntg; ++tg) {
+    const int b0 = tg * TB;
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
+    for (int wb = 0; wb < total; wb += LIST_CAP) {
+      const int wl = min(LIST_CAP, total - wb);
+      __syncthreads();
+      if (LIST_FROM_WG) {
+        for (int u = tid; u < g_mid; u += TPB) {
+          const int c = cnt_g[u], o = s_off[u];
+          for (int jj = 0; jj < c; ++jj) {
+            const int k = o + jj;
+            if (k >= wb && k < wb + wl) s_list[k - wb] = list_g[(size_t)u * 64 + jj];
+          }
+        }
+      } else {
+        for (int u = tid; u < wl; u += TPB) s_list[u] = idx_in[wb + u];
+      }
+      __syncthreads();
+      if (LIST_FROM_WG && tg == 0) {
+        // publish the ascending list and token bits: workgroup w writes k = w (mod G)
+        for (int u = blockIdx.x + tid * G; u < wl; u += TPB * G) {
+          const int i = s_list[u];
+          idx_out[wb + u] = i;
+          if (tokmask_out) tokmask_out[wb + u] = tok_full[i];
+        }
+      }
+      for (int kb = rl; kb < wl; kb += NRL * LOADS) {
+        u32x4 wv[LOADS];
+        int ii[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int k = kb + u * NRL;
+          ii[u] = (k < wl) ? s_list[k] : -1;
+          if (ii[u] >= n) ii[u] = -1;  // out-of-range entries are skipped
+          if (ii[u] >= 0) wv[u] = ld_chunk(w_down_t, (size_t)ii[u] * nch + chunk);
+        }
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          if (ii[u] >= 0) {
+            float f[EPC];
+            unpack<WF16>(wv[u], f);
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+              if (b0 + b < B) {
+                const float h = h_full[(size_t)ii[u] * B + b0 + b];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[b][e] = fmaf(h, f[e], acc[b][e]);
+              }
+            }
+          }
+        }
+      }
+    }
+    // fixed-order reduction over the 128 row lanes
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) s_red[((b * EPC + e) * 2 + ch) * NRL + rl] = acc[b][e];
+    __syncthreads();
+    const int nout = TB * EPC * 2;
+    if (tid < nout) {
+      const int b = tid / (EPC * 2), rem = tid % (EPC * 2), e = rem / 2, c2 = rem % 2;
+      if (b0 + b < B) {
+        const float* p = s_red + (size_t)((b * EPC + e) * 2 + c2) * NRL;
+        float sum = 0.f;
+        for (int u = 0; u < NRL; ++u) sum += p[u];
+        const int col = (2 * s + c2) * EPC + e;
+        y[(size_t)(b0 + b) * d + col] = sum + (b_out ? b_out[col] : 0.f);
+      }
+    }
+  }
+}
+
+// ============================================================================ offline
+// Activation profile: counts[i] = #{tokens t : w_act[i] . x_t + b_act[i] > 0}. A plain
+// LDS-tiled fp32 product: workgroup owns 64 neurons and walks every token in tiles of 64;
+// a thread computes a 4x4 block. Integer counts per neuron stay in the owner thread.
+template <bool WF16>
+__global__ __launch_bounds__(TPB) void k_profile(const void* __restrict__ w_act, int row_elems,
+                                                 const float* __restrict__ b_act,
+                                                 const float* __restrict__ x, int d, int n,
+                                                 int N, int64_t* __restrict__ counts) {
+  constexpr int TK = 32;
+  __shared__ float s_w[TK][64 + 1];
+  __shared__ float s_xt[TK][64 + 1];
+  __shared__ int s_cnt[16][64];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int i0 = blockIdx.x * 64;
+  int cnt[4] = {0, 0, 0, 0};
+  for (int t0 = 0; t0 < N; t0 += 64) {
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < d; k0 += TK) {
+      for (int u = tid; u < 64 * TK; u += TPB) {
+        const int rr = u / TK, kk = u % TK;
+        const int i = i0 + rr, t = t0 + rr, k = k0 + kk;
+        float wvv = 0.f, xv = 0.f;
+        if (i < n && k < d) {
+          if (WF16)
+            wvv = (float)reinterpret_cast<const _Float16*>(w_act)[(size_t)i * row_elems + k];
+          else
+            wvv = reinterpret_cast<const float*>(w_act)[(size_t)i * row_elems + k];
+        }
+        if (t < N && k < d) xv = x[(size_t)t * d + k];
+        s_w[kk][rr] = wvv;
+        s_xt[kk][rr] = xv;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < TK; ++kk) {
+        float a[4], bb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = s_w[kk][ty * 4 + u];
+          bb[u] = s_xt[kk][tx * 4 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], bb[v], acc[u][v]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + ty * 4 + u;
+      const float bias = (i < n && b_act) ? b_act[i] : 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + tx * 4 + v;
+        if (i < n && t < N && acc[u][v] + bias > 0.f) ++cnt[u];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s_cnt[tx][ty * 4 + u] = cnt[u];
+  __syncthreads();
+  if (tid < 64 && i0 + tid < n) {
+    int sum = 0;
+    for (int u = 0; u < 16; ++u) sum += s_cnt[u][tid];
+    counts[i0 + tid] = sum;
+  }
+}
+
+// dst row i (at word offset i*dst_wstride) = src row perm[i]; 4-byte words, grid-stride;
+// out-of-range perm entries leave their destination row untouched.
+__global__ __launch_bounds__(TPB) void k_pack_rows(const uint32_t* __restrict__ src,
+                                                   const int32_t* __restrict__ perm,
+                                                   uint32_t* __restrict__ dst, int rows,
+                                                   int64_t wpr, int64_t dst_wstride) {
+  const int64_t total = (int64_t)rows * wpr;
+  for (int64_t u = blockIdx.x * (int64_t)TPB + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * TPB) {
+    const int64_t rr = u / wpr, ww = u % wpr;
+    const int p = perm[rr];
+    if (p >= 0 && p < rows) dst[rr * dst_wstride + ww] = src[(int64_t)p * wpr + ww];
+  }
+}
+
+}  // namespace
+
+// ============================================================================ host side
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int d, int n, int r, int max_batch) {
+  (void)d;
+  const int n_tiles = (n + TPB - 1) / TPB;
+  size_t b = 0;
+  b += align256((size_t)max_batch * r * 4);      // q
+  b += align256((size_t)n * max_batch * 4);      // h_full
+  b += align256((size_t)n * 8);                  // tok_full
+  b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
+  b += align256((size_t)G_MID_MAX * 4);          // cnt_g
+  b += align256((size_t)G_MID_MAX * 64 * 4);     // list_g
+  b += align256((size_t)n_tiles * 4);            // tile_cnt
+  b += align256((size_t)((n + 63) / 64) * 8);    // words
+  return b;
+}
+
+void carve_workspace(LayerDev& L, void* ws, int max_batch) {
+  char* p = static_cast<char*>(ws);
+  const int n = L.n;
+  const int n_tiles = (n + TPB - 1) / TPB;
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  L.q = reinterpret_cast<float*>(take((size_t)max_batch * L.r * 4));
+  L.h_full = reinterpret_cast<float*>(take((size_t)n * max_batch * 4));
+  L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
+  L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
+  L.cnt_g = reinterpret_cast<int32_t*>(take((size_t)G_MID_MAX * 4));
+  L.list_g = reinterpret_cast<int32_t*>(take((size_t)G_MID_MAX * 64 * 4));
+  L.tile_cnt = reinterpret_cast<int32_t*>(take((size_t)n_tiles * 4));
+  L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
+  L.n_tiles = n_tiles;
+}
+
+namespace {
+
+// chunks per stored row (gated rows hold gate and up)
+int row_chunks(const LayerDev& L) {
+  const int epc = L.w_f16 ? 8 : 4;
+  return (L.gated ? 2 : 1) * (L.d / epc);
+}
+int pick_cpt(int rowch) {
+  const int need = (rowch + TPB - 1) / TPB;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  return 0;
+}
+// lane-group width for stage-2 rows of nchp chunks
+void pick_group(int nchp, int& Lw, int& cplp) {
+  Lw = 8;
+  while (Lw < nchp && Lw < 64) Lw <<= 1;
+  cplp = (nchp + Lw - 1) / Lw;
+}
+bool x_in_lds(int B, int d) { return (size_t)B * d * 4 <= (size_t)X_LDS_MAX; }
+
+template <bool F16>
+void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s) {
+  if (B == 1)
+    hipLaunchKernelGGL((k_pred_stage1<F16, 1>), dim3(L.r), dim3(TPB), 0, s, L.p1, x, L.d, L.r, B, L.q);
+  else
+    hipLaunchKernelGGL((k_pred_stage1<F16, 4>), dim3(L.r), dim3(TPB), 0, s, L.p1, x, L.d, L.r, B, L.q);
+}
+
+template <bool F16>
+hipError_t predict_t(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  stage1_launch<F16>(L, x, B, s);
+  const int nchp = L.r / (F16 ? 8 : 4);
+  int Lw, cplp;
+  pick_group(nchp, Lw, cplp);
+  constexpr int PASSES = 4;
+  const int rows_per_wg = (TPB / Lw) * PASSES;
+  const dim3 grid((L.n + rows_per_wg - 1) / rows_per_wg);
+#define SCORES(LL, CC)                                                                       \
+  hipLaunchKernelGGL((k_pred_scores<F16, LL, CC, PASSES>), grid, dim3(TPB), 0, s, L.p2,      \
+                     L.p_bias, L.q, L.n, L.r, B, scores)
+  if (Lw == 8) SCORES(8, 1);
+  else if (Lw == 16) SCORES(16, 1);
+  else if (Lw == 32) SCORES(32, 1);
+  else if (cplp == 1) SCORES(64, 1);
+  else if (cplp == 2) SCORES(64, 2);
+  else SCORES(64, 4);
+#undef SCORES
+  return hipGetLastError();
+}
+
+template <bool F16, bool GATED, int CPT>
+void gather_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                   const int32_t* count, const uint64_t* tokmask, hipStream_t s) {
+  const bool xl = x_in_lds(B, L.d);
+  const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
+  if (B == 1)
+    hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 1>), dim3(L.g_gather), dim3(TPB), lds, s,
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_full, xl ? 1 : 0);
+  else
+    hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 4>), dim3(L.g_gather), dim3(TPB), lds, s,
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_full, xl ? 1 : 0);
+}
+
+template <bool F16, bool GATED>
+void gather_dispatch(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                     const int32_t* count, const uint64_t* tokmask, hipStream_t s) {
+  switch (pick_cpt(row_chunks(L))) {
+    case 1: gather_launch<F16, GATED, 1>(L, x, B, idx, count, tokmask, s); break;
+    case 2: gather_launch<F16, GATED, 2>(L, x, B, idx, count, tokmask, s); break;
+    case 4: gather_launch<F16, GATED, 4>(L, x, B, idx, count, tokmask, s); break;
+    default: gather_launch<F16, GATED, 8>(L, x, B, idx, count, tokmask, s); break;
+  }
+}
+
+template <bool F16, bool FROM_WG>
+void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                 int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
+                 hipStream_t s) {
+  constexpr int EPC = F16 ? 8 : 4;
+  const int grid = (L.d / EPC) / 2;
+  if (B == 1) {
+    const size_t lds = std::max((size_t)LIST_CAP * 4, (size_t)1 * EPC * 2 * (TPB / 2) * 4);
+    hipLaunchKernelGGL((k_down<F16, FROM_WG, 1>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
+                       L.b_out, L.h_full, L.d, L.n, B, idx, count, L.cnt_g, L.list_g, L.g_mid,
+                       L.tok_full, idx_out, count_out, tok_out, y);
+  } else {
+    const size_t lds = std::max((size_t)LIST_CAP * 4, (size_t)4 * EPC * 2 * (TPB / 2) * 4);
+    hipLaunchKernelGGL((k_down<F16, FROM_WG, 4>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
+                       L.b_out, L.h_full, L.d, L.n, B, idx, count, L.cnt_g, L.list_g, L.g_mid,
+                       L.tok_full, idx_out, count_out, tok_out, y);
+  }
+}
+
+template <bool F16, bool GATED, int CPT>
+void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  const bool xl = x_in_lds(B, L.d);
+  const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
+  if (B == 1)
+    hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 1>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+                       L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
+                       L.list_g, L.tok_full, L.h_full, scores, xl ? 1 : 0);
+  else
+    hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 4>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+                       L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
+                       L.list_g, L.tok_full, L.h_full, scores, xl ? 1 : 0);
+}
+
+template <bool F16, bool GATED>
+void mid_dispatch(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  switch (pick_cpt(row_chunks(L))) {
+    case 1: mid_launch_cpt<F16, GATED, 1>(L, x, B, scores, s); break;
+    case 2: mid_launch_cpt<F16, GATED, 2>(L, x, B, scores, s); break;
+    case 4: mid_launch_cpt<F16, GATED, 4>(L, x, B, scores, s); break;
+    default: mid_launch_cpt<F16, GATED, 8>(L, x, B, scores, s); break;
+  }
+}
+
+}  // namespace
+
+bool shape_supported(const LayerDev& L, bool fused) {
+  if (pick_cpt(row_chunks(L)) == 0) return false;
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  if (nchp > 256) return false;
+  const int epc_p = L.p_f16 ? 8 : 4;
+  if (L.d / epc_p > 8 * TPB) return false;  // stage 1 register budget
+  if (fused) {
+    if (L.w_f16 != L.p_f16) return false;
+    if (nchp > 128 || (nchp & (nchp - 1)) != 0) return false;  // P2 row = power-of-two chunks
+    if (L.g_mid < 1 || L.g_mid > G_MID_MAX) return false;
+  }
+  return true;
+}
+
+hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  return L.p_f16 ? predict_t<true>(L, x, B, scores, s) : predict_t<false>(L, x, B, scores, s);
+}
+
+hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t* idx,
+                          int32_t* count, uint64_t* tokmask, hipStream_t s) {
+  hipLaunchKernelGGL(k_cmp_tiles, dim3(L.n_tiles), dim3(TPB), 0, s, scores, L.n, B, L.tau,
+                     L.tok_full, L.words, L.tile_cnt);
+  hipLaunchKernelGGL(k_cmp_scatter, dim3(L.n_tiles), dim3(TPB), 0, s, L.tok_full, L.words,
+                     L.tile_cnt, L.n, L.n_tiles, idx, count, tokmask);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                          const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s) {
+  if (L.w_f16) {
+    if (L.gated) gather_dispatch<true, true>(L, x, B, idx, count, tokmask, s);
+    else gather_dispatch<true, false>(L, x, B, idx, count, tokmask, s);
+    down_launch<true, false>(L, B, idx, count, nullptr, nullptr, nullptr, y, s);
+  } else {
+    if (L.gated) gather_dispatch<false, true>(L, x, B, idx, count, tokmask, s);
+    else gather_dispatch<false, false>(L, x, B, idx, count, tokmask, s);
+    down_launch<false, false>(L, B, idx, count, nullptr, nullptr, nullptr, y, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
+                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s) {
+  if (L.p_f16)
+    stage1_launch<true>(L, x, B, s);
+  else
+    stage1_launch<false>(L, x, B, s);
+  if (L.w_f16) {
+    if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s);
+    else mid_dispatch<true, false>(L, x, B, scores, s);
+    down_launch<true, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
+  } else {
+    if (L.gated) mid_dispatch<false, true>(L, x, B, scores, s);
+    else mid_dispatch<false, false>(L, x, B, scores, s);
+    down_launch<false, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const float* b_act,
+                                 int d, int n, const float* x, int N, int64_t* counts,
+                                 hipStream_t s) {
+  const int row_elems = gated ? 2 * d : d;
+  const dim3 grid((n + 63) / 64);
+  if (w_f16)
+    hipLaunchKernelGGL(k_profile<true>, grid, dim3(TPB), 0, s, w_act, row_elems, b_act, x, d, n, N, counts);
+  else
+    hipLaunchKernelGGL(k_profile<false>, grid, dim3(TPB), 0, s, w_act, row_elems, b_act, x, d, n, N, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const void* src, const int32_t* perm, void* dst, int rows,
+                            int64_t row_bytes, int64_t dst_stride_bytes, hipStream_t s) {
+  const int64_t wpr = row_bytes / 4;
+  const int64_t total = (int64_t)rows * wpr;
+  int64_t blocks = (total + TPB - 1) / TPB;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)blocks), dim3(TPB), 0, s,
+                     static_cast<const uint32_t*>(src), perm, static_cast<uint32_t*>(dst), rows, wpr,
+                     dst_stride_bytes / 4);
+  return hipGetLastError();
+}
+}  // namespace sffn

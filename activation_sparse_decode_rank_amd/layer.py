@@ -1,0 +1,199 @@
+"""SparseFFN: one activation-sparse FFN layer held in device memory, prepared offline and
+called through the C ABI. torch supplies device memory and the current stream; every step
+of the method (profile counts, permutation, row packing, predict, compact, forward) runs in
+the library.
+
+Offline preparation (unite.ai PowerInfer overview, "Fase fuera de línea" and "Colocación y
+gestión de neuronas"): activation counts over profiling tokens -> hot-first permutation ->
+rows packed in that order; `perm[p]` maps packed position p back to the original neuron.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+_DT = {torch.float16: N.SFFN_F16, torch.float32: N.SFFN_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def n_hot_for(n: int, hot_frac: float) -> int:
+    return int(math.ceil(float(hot_frac) * n))
+
+
+def profile_counts(w_act: torch.Tensor, b_act: Optional[torch.Tensor], x: torch.Tensor,
+                   gated: bool = False, stream=None) -> torch.Tensor:
+    """counts[i] (int64, device) = #profiling tokens with w_act[i] . x + b_act[i] > 0.
+    For gated layers pass the gate matrix [n, d] (gated=False) or a bundle (gated=True)."""
+    n = w_act.shape[0]
+    d = x.shape[1]
+    counts = torch.empty(n, dtype=torch.int64, device=w_act.device)
+    N.sparse_ffn_profile_counts(_ptr(w_act), _DT[w_act.dtype], int(gated), _ptr(b_act), d, n,
+                                _ptr(x), x.shape[0], _ptr(counts), _stream(stream))
+    return counts
+
+
+def permutation(counts: np.ndarray, n_hot: int) -> np.ndarray:
+    """perm[new] = old, hot-first (host)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int64)
+    perm = np.empty(counts.shape[0], np.int32)
+    N.sparse_ffn_permutation(counts.ctypes.data, counts.shape[0], int(n_hot), perm.ctypes.data)
+    return perm
+
+
+def pack_rows(src: torch.Tensor, perm_dev: torch.Tensor, dst: Optional[torch.Tensor] = None,
+              dst_offset_bytes: int = 0, dst_stride_bytes: int = 0, stream=None) -> torch.Tensor:
+    """Row gather copy on the device: dst row i = src row perm[i]."""
+    rows = src.shape[0]
+    row_bytes = src.numel() * src.element_size() // rows
+    if dst is None:
+        dst = torch.empty_like(src)
+    N.sparse_ffn_pack_rows(_ptr(src), _ptr(perm_dev), dst.data_ptr() + dst_offset_bytes, rows,
+                           row_bytes, dst_stride_bytes, _stream(stream))
+    return dst
+
+
+class SparseFFN:
+    """An FFN layer in packed order with a library handle.
+
+    w_act: [n, d] W_up (plain) or W_gate (gated); w_up: [n, d] for the gated form, else None;
+    w_down_t: [n, d] W_down transposed; p1: [r, d]; p2: [n, r]; biases fp32.
+    profile_x: [N, d] fp32 profiling tokens; when given, neurons are profiled and the
+    hottest ceil(hot_frac * n) packed first, and their frequencies balance the work split.
+    """
+
+    def __init__(self, *, w_act, w_down_t, p1, p2, b_act=None, b_out=None, p_bias=None,
+                 w_up=None, threshold: float = 0.0, max_batch: int = 1,
+                 profile_x: Optional[torch.Tensor] = None, hot_frac: float = 0.2,
+                 perm: Optional[np.ndarray] = None, stream=None):
+        dev = w_act.device
+        if dev.type != "cuda":
+            raise ValueError("SparseFFN needs device tensors")
+        for t in (w_act, w_down_t, p1, p2, w_up, b_act, b_out, p_bias, profile_x):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+        n, d = w_act.shape
+        r = p1.shape[0]
+        self.n, self.d, self.r = n, d, r
+        self.gated = w_up is not None
+        self.max_batch = int(max_batch)
+        self.threshold = float(threshold)
+        s = _stream(stream)
+
+        freq = None
+        if perm is None and profile_x is not None:
+            counts = profile_counts(w_act, b_act, profile_x, gated=False, stream=stream)
+            counts_h = counts.cpu().numpy()
+            perm = permutation(counts_h, n_hot_for(n, hot_frac))
+            freq = (counts_h[perm] / float(profile_x.shape[0])).astype(np.float32)
+            self.profile_counts = counts_h
+        elif perm is None:
+            perm = np.arange(n, dtype=np.int32)
+        self.perm = np.ascontiguousarray(perm, dtype=np.int32)
+        perm_dev = torch.from_numpy(self.perm).to(dev)
+
+        # packed copies, made by the library's row-gather kernel
+        if self.gated:
+            eb = w_act.element_size()
+            self.w_act = torch.empty((n, 2, d), dtype=w_act.dtype, device=dev)
+            pack_rows(w_act, perm_dev, self.w_act, 0, 2 * d * eb, stream)
+            pack_rows(w_up, perm_dev, self.w_act, d * eb, 2 * d * eb, stream)
+        else:
+            self.w_act = pack_rows(w_act, perm_dev, stream=stream)
+        self.w_down_t = pack_rows(w_down_t, perm_dev, stream=stream)
+        self.p2 = pack_rows(p2, perm_dev, stream=stream)
+        self.b_act = None if b_act is None else pack_rows(b_act.contiguous(), perm_dev, stream=stream)
+        self.p_bias = None if p_bias is None else pack_rows(p_bias.contiguous(), perm_dev, stream=stream)
+        self.p1 = p1
+        self.b_out = b_out
+        torch.cuda.current_stream(dev).synchronize() if stream is None else stream.synchronize()
+
+        self.desc = N.SffnDesc()
+        D = self.desc
+        D.d, D.d_ffn, D.rank, D.max_batch = d, n, r, self.max_batch
+        D.gated = int(self.gated)
+        D.w_dtype, D.p_dtype = _DT[w_act.dtype], _DT[p1.dtype]
+        D.threshold = self.threshold
+        D.w_act, D.w_down_t = _ptr(self.w_act), _ptr(self.w_down_t)
+        D.b_act, D.b_out = _ptr(self.b_act), _ptr(self.b_out)
+        D.p1, D.p2, D.p_bias = _ptr(self.p1), _ptr(self.p2), _ptr(self.p_bias)
+        ws = N.sparse_ffn_workspace_bytes(D)
+        if ws == 0:
+            raise N.SparseFFNError(N.SFFN_ERR_INVALID, "sparse_ffn_workspace_bytes")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        D.workspace, D.workspace_bytes = self.workspace.data_ptr(), ws
+        self._freq = freq  # keep the host array alive across create
+        D.neuron_freq = None if freq is None else freq.ctypes.data
+        self.handle = N.sparse_ffn_create(D)
+        D.neuron_freq = None
+        self.perm_dev = perm_dev
+
+    # ---------------------------------------------------------------- calls
+    def _check_x(self, x):
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous fp32 [B, d] device tensor")
+        B = x.shape[0]
+        if not 1 <= B <= self.max_batch:
+            raise ValueError(f"batch {B} outside 1..{self.max_batch}")
+        return B
+
+    def predict(self, x, scores=None, stream=None):
+        B = self._check_x(x)
+        if scores is None:
+            scores = torch.empty((B, self.n), dtype=torch.float32, device=x.device)
+        N.sparse_ffn_predict(self.handle, x.data_ptr(), B, scores.data_ptr(), _stream(stream))
+        return scores
+
+    def compact(self, scores, idx=None, count=None, tokmask=None, stream=None):
+        B = scores.shape[0]
+        dev = scores.device
+        idx = torch.empty(self.n, dtype=torch.int32, device=dev) if idx is None else idx
+        count = torch.empty(1, dtype=torch.int32, device=dev) if count is None else count
+        if tokmask is None:
+            tokmask = torch.empty(self.n, dtype=torch.int64, device=dev)
+        N.sparse_ffn_compact(self.handle, scores.data_ptr(), B, idx.data_ptr(), count.data_ptr(),
+                             tokmask.data_ptr(), _stream(stream))
+        return idx, count, tokmask
+
+    def forward(self, x, idx, count, tokmask=None, y=None, stream=None):
+        B = self._check_x(x)
+        if y is None:
+            y = torch.empty((B, self.d), dtype=torch.float32, device=x.device)
+        N.sparse_ffn_forward(self.handle, x.data_ptr(), B, idx.data_ptr(), count.data_ptr(),
+                             _ptr(tokmask), y.data_ptr(), _stream(stream))
+        return y
+
+    def decode(self, x, y=None, idx=None, count=None, tokmask=None, scores=None, stream=None):
+        B = self._check_x(x)
+        dev = x.device
+        y = torch.empty((B, self.d), dtype=torch.float32, device=dev) if y is None else y
+        idx = torch.empty(self.n, dtype=torch.int32, device=dev) if idx is None else idx
+        count = torch.empty(1, dtype=torch.int32, device=dev) if count is None else count
+        if tokmask is None:
+            tokmask = torch.empty(self.n, dtype=torch.int64, device=dev)
+        N.sparse_ffn_decode(self.handle, x.data_ptr(), B, y.data_ptr(), idx.data_ptr(),
+                            count.data_ptr(), tokmask.data_ptr(), _ptr(scores), _stream(stream))
+        return y, idx, count, tokmask
+
+    def close(self):
+        if getattr(self, "handle", None):
+            N.sparse_ffn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,175 @@
+/*
+ * sparse_ffn.h -- C ABI of the activation-sparse FFN decode library (MI355X, gfx950).
+ *
+ * One FFN layer at decode time: a low-rank predictor scores every neuron, the scores are
+ * thresholded and compacted into an ascending list of active neurons, and only those
+ * neurons' rows are read: the ReLU-input rows (W_up, or W_gate and W_up in the ReLU-fied
+ * gated form) and the matching rows of W_down transposed.
+ *
+ * Sources (web pages; no page states an API, so the calls below follow from what the
+ * method does):
+ *  - predict the active neurons and skip the rest: unite.ai PowerInfer overview,
+ *    "Fase en línea" and "Predictores de espacialidad adaptativa"; novita.ai
+ *    activation-sparsity article, sections 單層計算優化 and 自適應稀疏預測器;
+ *  - operate on individual row/column vectors with no sparse-format conversion at run
+ *    time: unite.ai overview, "Operador consciente de neuronas";
+ *  - ReLU between up and down makes skipped rows contribute exactly zero: novita.ai
+ *    article, section 激活稀疏性的可行性; ReLU on the gate for gated FFNs: section 第一階段;
+ *  - gate/up of neuron i co-activate, so they are stored as one bundle: PowerInfer-2
+ *    article, section 4.4 Neuron-Cluster-Level Pipeline;
+ *  - offline activation profile, hot neurons first, and a neuron table back to original
+ *    positions: unite.ai overview, "Fase fuera de línea" and "Colocación y gestión de
+ *    neuronas";
+ *  - batch: each token has its own active set; the union decides which rows are read:
+ *    novita.ai article, section 批次大小影響.
+ *
+ * Conventions
+ *  - Every pointer named *_dev or documented "device" is HIP device memory owned by the
+ *    caller. Host pointers are documented "host".
+ *  - `stream` is a hipStream_t passed as void*. Every device call is enqueued on it and
+ *    nothing synchronizes; results are ready when the caller synchronizes the stream.
+ *  - Errors: arguments are validated on the host before anything is enqueued. A rejected
+ *    call returns SFFN_ERR_INVALID (or SFFN_ERR_UNSUPPORTED) and enqueues nothing. A
+ *    launch failure returns SFFN_ERR_HIP. Faults inside kernels surface at the caller's
+ *    next synchronization. No C++ exception crosses this interface.
+ *  - Index space: indices are positions in the (packed) row order the weights are stored
+ *    in. The original neuron id of packed position p is perm[p] (sparse_ffn_permutation).
+ *  - Layout: all matrices are row-major with one row per neuron, rows contiguous:
+ *      plain  w_act:    [d_ffn][d]        row i = W_up row of neuron i
+ *      gated  w_act:    [d_ffn][2][d]     neuron i's gate row followed by its up row
+ *      w_down_t:        [d_ffn][d]        row i = neuron i's column of W_down
+ *      p1:              [rank][d]         predictor stage 1
+ *      p2:              [d_ffn][rank]     predictor stage 2, one row per neuron
+ *      x:               [B][d] fp32       tokens;  y: [B][d] fp32
+ *      scores:          [B][d_ffn] fp32
+ *  - Arithmetic: weights are read as stored (fp16 or fp32) and widened to fp32; every
+ *    accumulation is fp32. Results are deterministic: the same inputs give bit-identical
+ *    outputs (no floating-point atomics anywhere).
+ */
+#ifndef SPARSE_FFN_H
+#define SPARSE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SFFN_OK = 0,
+  SFFN_ERR_INVALID = -1,      /* bad argument; nothing was enqueued */
+  SFFN_ERR_UNSUPPORTED = -2,  /* valid but no kernel for this dtype/shape */
+  SFFN_ERR_HIP = -3           /* a HIP call failed (device query or launch) */
+};
+
+typedef enum { SFFN_F32 = 0, SFFN_F16 = 1 } sffn_dtype;
+
+/* Largest batch: one bit per token in the 64-bit membership words. */
+#define SFFN_MAX_BATCH 64
+
+typedef struct sparse_ffn_s* sparse_ffn_t;
+
+/* Layer descriptor. The handle borrows every pointer: weights and workspace must outlive
+ * the handle. d and rank must be multiples of 8 (16-byte aligned fp16 rows; fp32 rows are
+ * then 32-byte aligned), all device pointers 16-byte aligned. */
+typedef struct {
+  int32_t d;          /* model dimension */
+  int32_t d_ffn;      /* number of FFN neurons */
+  int32_t rank;       /* predictor rank r */
+  int32_t max_batch;  /* 1 .. SFFN_MAX_BATCH; sizes the workspace */
+  int32_t gated;      /* 0: h = relu(W_up x + b);  1: h = relu(W_gate x + b) * (W_up x) */
+  int32_t w_dtype;    /* sffn_dtype of w_act and w_down_t */
+  int32_t p_dtype;    /* sffn_dtype of p1 and p2 */
+  float threshold;    /* tau: neuron i is active for a token iff its score > tau (strict; NaN inactive) */
+  const void* w_act;     /* device, see layout above */
+  const void* w_down_t;  /* device, [d_ffn][d] */
+  const float* b_act;    /* device [d_ffn]: bias inside the ReLU (b_up, or b_gate); NULL = 0 */
+  const float* b_out;    /* device [d]: output bias; NULL = 0 */
+  const void* p1;        /* device [rank][d] */
+  const void* p2;        /* device [d_ffn][rank] */
+  const float* p_bias;   /* device [d_ffn]: predictor bias c; NULL = 0 */
+  void* workspace;       /* device scratch of at least sparse_ffn_workspace_bytes() */
+  size_t workspace_bytes;
+  const float* neuron_freq; /* host [d_ffn], optional: expected activation frequency of each
+                               neuron (e.g. profile counts / profile tokens). Read only by
+                               sparse_ffn_create, to cut the neurons into contiguous ranges
+                               of about equal expected work. NULL = every neuron equal. */
+} sffn_desc;
+
+/* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The
+ * workspace holds predictor intermediates, per-neuron activations, compaction state and a
+ * small table of neuron ranges that sparse_ffn_create writes (synchronously) and every
+ * later call reads. Give each handle its own workspace. */
+size_t sparse_ffn_workspace_bytes(const sffn_desc* desc);
+
+/* Validate `desc` and create a handle (host metadata only). Queries the current HIP device
+ * and writes the range table into the workspace with one synchronous copy. The handle is
+ * bound to that device. *out is set only on SFFN_OK. */
+int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out);
+
+/* Free the handle's host metadata. Borrowed memory is untouched. NULL is accepted. */
+int sparse_ffn_destroy(sparse_ffn_t h);
+
+/* Predictor (both stages): scores[b][i] = P2[i] . (P1 x_b) + c[i], fp32.
+ * x: device [B][d] fp32; scores: device [B][d_ffn] fp32; 1 <= B <= max_batch. */
+int sparse_ffn_predict(sparse_ffn_t h, const float* x, int32_t B, float* scores, void* stream);
+
+/* Threshold and compaction: idx = ascending list of neurons whose score exceeds tau for at
+ * least one of the B tokens; *count (device int32) = its length; tokmask[k] bit b = token b
+ * has neuron idx[k] active. idx: device [d_ffn] int32; count: device [1] int32; tokmask:
+ * device [d_ffn] uint64, may be NULL only when B == 1. Integer results are bit-exact given
+ * the scores. */
+int sparse_ffn_compact(sparse_ffn_t h, const float* scores, int32_t B, int32_t* idx,
+                       int32_t* count, uint64_t* tokmask, void* stream);
+
+/* Forward over a given active list (device idx/count/tokmask as produced by
+ * sparse_ffn_compact; tokmask NULL = every token uses every listed neuron):
+ *   h_{k,b} = relu(w_act[idx_k] . x_b + b_act) (gated: times w_up[idx_k] . x_b), zero when
+ *   bit b of tokmask[k] is 0;  y_b = sum_k h_{k,b} w_down_t[idx_k] + b_out.
+ * y: device [B][d] fp32, fully overwritten (count == 0 gives y = b_out). The count is read
+ * on the device; launches have fixed sizes, so the call can be captured in a HIP graph. */
+int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t* idx,
+                       const int32_t* count, const uint64_t* tokmask, float* y, void* stream);
+
+/* The whole decode step for one layer with the fewest launches: predict, threshold,
+ * compact and forward. Outputs y as sparse_ffn_forward would for the list that
+ * sparse_ffn_compact would produce from sparse_ffn_predict's scores, and also writes that
+ * list: idx, count and (if non-NULL) tokmask, same meaning as above. scores, if non-NULL,
+ * receives the predictor scores. */
+int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
+                      int32_t* count, uint64_t* tokmask, float* scores, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* sparse_ffn_status_string(int status);
+
+/* ---- offline helpers: run once per layer before sparse_ffn_create ---- */
+
+/* Activation profile: counts[i] (device int64, overwritten) = number of the N tokens x
+ * (device [N][d] fp32) for which neuron i's ReLU input w_act[i] . x + b_act[i] is > 0
+ * (the gate row for gated layers, whose row stride is 2*d). Computed in fp32. */
+int sparse_ffn_profile_counts(const void* w_act, int32_t w_dtype, int32_t gated,
+                              const float* b_act, int32_t d, int32_t d_ffn, const float* x,
+                              int32_t N, int64_t* counts, void* stream);
+
+/* Hot-first permutation (host, pure): perm[new] = old. The n_hot neurons with the largest
+ * counts come first, by count descending and original index ascending on ties; the rest
+ * follow in ascending original index. counts, perm: host arrays of d_ffn. */
+int sparse_ffn_permutation(const int64_t* counts, int32_t d_ffn, int32_t n_hot,
+                           int32_t* perm_new_to_old);
+
+/* Row gather copy (device): the row_bytes bytes at dst + i*dst_stride_bytes become source
+ * row perm[i] (source rows are contiguous, row_bytes apart). row_bytes and
+ * dst_stride_bytes are multiples of 4; dst_stride_bytes = 0 means row_bytes. A stride
+ * larger than the row interleaves matrices, e.g. the gated [d_ffn][2][d] bundle is two
+ * calls with stride 2*d*elem, the second at dst + d*elem. src, dst: device; perm: device
+ * int32 [rows], values in 0..rows-1 (bounds-checked on the device: an out-of-range entry
+ * leaves that destination row untouched). */
+int sparse_ffn_pack_rows(const void* src, const int32_t* perm, void* dst, int32_t rows,
+                         int64_t row_bytes, int64_t dst_stride_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FFN_H */

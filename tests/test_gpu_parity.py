@@ -1,0 +1,345 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded
+inputs. Integer work (compaction, index lists, counts, packing) is compared bit for bit;
+floating-point outputs to max |y - y_ref| / max |y_ref| <= 1e-3 per token; predictor masks
+exactly, except neurons whose oracle score lies within 1e-4 of the threshold."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (BAND, REL_TOL, build, check_mask, gpu_mask_orig, oracle_pipeline,
+                      rel_err_rows, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import activation_sparse_decode_rank_amd  # noqa: F401  (fails loudly without the HIP library)
+    torch.cuda.init()
+    yield
+
+
+def cfg(name):
+    from synth import get_config
+    return get_config(name)
+
+
+def tokens(c, B, d, tag=200):
+    from synth import make_tokens
+    return make_tokens(c, B, tag, "cuda", d=d)
+
+
+# --------------------------------------------------------------------------- compaction
+def _compact_handle(n, max_batch=64):
+    from synth import get_config
+    s, _, _ = build(get_config("C2"), 0, d=16, n=n, rank=16, max_batch=max_batch, pack=False)
+    return s
+
+
+def _check_compact(s, S_np, tau=0.0):
+    B = S_np.shape[0]
+    S = torch.from_numpy(np.ascontiguousarray(S_np, np.float32)).cuda()
+    idx, count, tok = s.compact(S)
+    torch.cuda.synchronize()
+    k = int(count.item())
+    ri, rk, rt = oracle.compact(oracle.threshold(S_np.astype(np.float32), tau))
+    assert k == rk
+    assert np.array_equal(to_np(idx)[:k], ri)
+    assert np.array_equal(to_np(tok)[:k].astype(np.uint64), rt)
+
+
+def test_compact_exhaustive_16():
+    """Every sign pattern of 16 scores (65,536 patterns, 64 per call as a batch of tokens):
+    union, count and per-token bits exact."""
+    n = 16
+    say("compact exhaustive n=16")
+    s = _compact_handle(n)
+    pats = np.arange(1 << n, dtype=np.int64)
+    bits = ((pats[:, None] >> np.arange(n)[None, :]) & 1).astype(np.float32)
+    allS = np.where(bits > 0, 1.0, -1.0).astype(np.float32)
+    for c0 in range(0, 1 << n, 64):
+        _check_compact(s, allS[c0:c0 + 64])
+
+
+def test_compact_exhaustive_single_token_10():
+    n = 10
+    say("compact exhaustive single token n=10")
+    s = _compact_handle(n, max_batch=1)
+    for p in range(1 << n):
+        S = np.where((p >> np.arange(n)) & 1, 1.0, -1.0).astype(np.float32)[None, :]
+        _check_compact(s, S)
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 3072, 16391])
+@pytest.mark.parametrize("B", [1, 3, 64])
+def test_compact_boundaries(n, B):
+    say(f"compact boundaries n={n} B={B}")
+    s = _compact_handle(n, max_batch=64)
+    rng = np.random.Generator(np.random.PCG64(n * 131 + B))
+    cases = [np.full((B, n), -1.0), np.full((B, n), 1.0),
+             np.tile(np.where(np.arange(n) % 2 == 0, 1.0, -1.0), (B, 1)),
+             np.where(rng.random((B, n)) < 0.1, 1.0, -1.0),
+             np.zeros((B, n)),                                    # exact ties: inactive
+             rng.choice([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-38, -1e-38], size=(B, n))]
+    for S in cases:
+        _check_compact(s, S.astype(np.float32))
+
+
+# --------------------------------------------------------------------------- predictor
+@pytest.mark.parametrize("name,d,n,r,B", [("C1", 768, 3072, 64, 1), ("C2", 512, 1000, 64, 1),
+                                          ("C2", 256, 777, 128, 4), ("C3", 256, 555, 64, 2),
+                                          ("C5", 1024, 2100, 256, 1)])
+def test_predict_scores_and_mask(name, d, n, r, B):
+    c = cfg(name)
+    say(f"predict {name} d={d} n={n} r={r} B={B}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=r, max_batch=max(B, 1))
+    X = tokens(c, B, d)
+    Sg = to_np(s.predict(X))
+    Xh = to_np(X)
+    S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
+    Sg_orig = np.empty_like(Sg)
+    Sg_orig[:, s.perm] = Sg          # packed position p holds neuron perm[p]
+    err = np.max(np.abs(Sg_orig - S))
+    assert err <= 2e-5 * max(1.0, np.max(np.abs(S))), err
+    band = np.abs(S) < BAND
+    assert np.array_equal((Sg_orig > 0)[~band], (S > 0)[~band])
+
+
+# --------------------------------------------------------------------------- forward / decode
+SHAPES = [
+    # name, d, n, r, B          (several 256-neuron tiles and a ragged tail each)
+    ("C1", 768, 3072, 64, 1),
+    ("C2", 512, 1000, 64, 1),
+    ("C2", 256, 777, 64, 3),
+    ("C3", 256, 555, 64, 1),
+    ("C3", 512, 1100, 64, 4),
+    ("C5", 1024, 2100, 256, 1),
+    ("C2", 4096, 1500, 256, 2),
+]
+
+
+@pytest.mark.parametrize("name,d,n,r,B", SHAPES)
+def test_forward_given_mask(name, d, n, r, B):
+    """Forward entry point on the oracle's own list (the same list goes to both sides)."""
+    c = cfg(name)
+    say(f"forward {name} d={d} n={n} r={r} B={B}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=r, max_batch=B)
+    X = tokens(c, B, d)
+    Xh = to_np(X)
+    S, M, idx_o, tok_o, Y = oracle_pipeline(L, Xh)
+    inv = np.empty(n, np.int64)
+    inv[s.perm] = np.arange(n)
+    order = np.argsort(inv[idx_o])                 # ascending packed positions
+    idx_p = inv[idx_o][order].astype(np.int32)
+    tok_p = tok_o[order]
+    dev = X.device
+    idx_t = torch.from_numpy(idx_p).to(dev) if len(idx_p) else torch.zeros(1, dtype=torch.int32, device=dev)
+    cnt_t = torch.tensor([len(idx_p)], dtype=torch.int32, device=dev)
+    tok_t = torch.from_numpy(tok_p.view(np.int64)).to(dev) if len(idx_p) else torch.zeros(1, dtype=torch.int64, device=dev)
+    y = to_np(s.forward(X, idx_t, cnt_t, tok_t if B > 1 else None))
+    errs = rel_err_rows(y, Y)
+    assert max(errs) <= REL_TOL, errs
+
+
+@pytest.mark.parametrize("name,d,n,r,B", SHAPES)
+def test_decode_pipeline(name, d, n, r, B):
+    """Fused decode: mask checked against the oracle outside the band, output against the
+    oracle under that mask, and the separate predict/compact/forward calls agree."""
+    c = cfg(name)
+    say(f"decode {name} d={d} n={n} r={r} B={B}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=r, max_batch=B)
+    X = tokens(c, B, d)
+    Xh = to_np(X)
+    scores = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    y, idx, count, tok = s.decode(X, scores=scores)
+    torch.cuda.synchronize()
+    k = int(count.item())
+    idx_h, tok_h = to_np(idx), to_np(tok)
+    assert np.all(np.diff(idx_h[:k]) > 0)          # ascending, no repeats
+    S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
+    Mg = gpu_mask_orig(s.perm, idx_h, k, tok_h, B, n)
+    M, nband = check_mask(Mg, S)
+    ri, rk, rt = oracle.compact(M)
+    Y = oracle.forward(Xh, L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    errs = rel_err_rows(to_np(y), Y)
+    assert max(errs) <= REL_TOL, errs
+    # the scores the fused kernel wrote equal the predict entry point's (same arithmetic)
+    Sg = to_np(s.predict(X))
+    assert np.array_equal(Sg, to_np(scores))
+    # separate entry points give the same list and (to rounding) the same output
+    i2, c2, t2 = s.compact(torch.from_numpy(Sg).cuda())
+    torch.cuda.synchronize()
+    assert int(c2.item()) == k
+    assert np.array_equal(to_np(i2)[:k], idx_h[:k])
+    if B > 1:
+        assert np.array_equal(to_np(t2)[:k], tok_h[:k])
+    y2 = to_np(s.forward(X, i2, c2, t2 if B > 1 else None))
+    assert max(rel_err_rows(y2, Y)) <= REL_TOL
+    say(f"  count={k} band={nband} err={max(errs):.2e}")
+
+
+def test_decode_deterministic():
+    c = cfg("C2")
+    say("decode determinism")
+    s, _, _ = build(c, 0, d=1024, n=4096, rank=128, max_batch=4)
+    X = tokens(c, 4, 1024)
+    outs = []
+    for _ in range(3):
+        y, idx, count, tok = s.decode(X)
+        torch.cuda.synchronize()
+        outs.append((to_np(y).copy(), to_np(idx)[: int(count.item())].copy()))
+    for y, idx in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(idx, outs[0][1])
+
+
+def test_batch_rows_equal_single_token_calls():
+    """Row b of a batched decode equals decoding token b alone (to fp32 rounding of a
+    different summation grouping)."""
+    c = cfg("C3")
+    say("batch vs single")
+    s, _, _ = build(c, 0, d=512, n=1100, rank=64, max_batch=8)
+    X = tokens(c, 8, 512)
+    yb = to_np(s.decode(X)[0])
+    for b in range(8):
+        y1 = to_np(s.decode(X[b:b + 1].contiguous())[0])
+        assert max(rel_err_rows(yb[b:b + 1], y1)) <= 1e-5
+
+
+# --------------------------------------------------------------------------- invariants on the GPU
+@pytest.mark.parametrize("gated", [False, True])
+def test_all_active_and_true_sign_equal_dense(gated):
+    """I1/I2 on the GPU: with every neuron listed, and with the list of truly active
+    neurons, the sparse output equals the dense FFN (oracle)."""
+    c = cfg("C3" if gated else "C2")
+    d, n, r, B = 512, 1200, 64, 2
+    say(f"all-active / true-sign gated={gated}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=r, max_batch=B)
+    X = tokens(c, B, d)
+    Xh = to_np(X)
+    D = oracle.dense(Xh, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    dev = X.device
+    allp = torch.arange(n, dtype=torch.int32, device=dev)
+    y = to_np(s.forward(X, allp, torch.tensor([n], dtype=torch.int32, device=dev),
+                        torch.full((n,), -1, dtype=torch.int64, device=dev)))
+    assert max(rel_err_rows(y, D)) <= REL_TOL
+    A = oracle.preact(Xh, L["w_a"], L["b_a"])
+    T = (A > 0).astype(np.uint8)
+    inv = np.empty(n, np.int64)
+    inv[s.perm] = np.arange(n)
+    idx_o, k, tok_o = oracle.compact(T)
+    order = np.argsort(inv[idx_o])
+    y2 = to_np(s.forward(X, torch.from_numpy(inv[idx_o][order].astype(np.int32)).to(dev),
+                         torch.tensor([k], dtype=torch.int32, device=dev),
+                         torch.from_numpy(tok_o[order].view(np.int64)).to(dev)))
+    assert max(rel_err_rows(y2, D)) <= REL_TOL
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("B", [1, 5])
+def test_integer_fixture_bit_exact(gated, B):
+    """Integer weights and tokens: every partial sum is exact in fp32, so the HIP path must
+    reproduce the oracle bit for bit, scores, list and output."""
+    from activation_sparse_decode_rank_amd import SparseFFN
+    from synth import integer_layer
+    d, n, r = 64, 1000, 16
+    say(f"integer fixture gated={gated} B={B}")
+    lo, hi = (-1, 1) if gated else (-2, 2)
+    L = integer_layer(d, n, r, gated=gated, seed=77 + B, B=B, lo=lo, hi=hi)
+    T = {k: (torch.from_numpy(v).cuda() if v is not None else None) for k, v in L.items()}
+    Xp = torch.from_numpy(integer_layer(d, n, r, gated=gated, seed=5, B=64, lo=lo, hi=hi)["x"]).cuda()
+    s = SparseFFN(w_act=T["w_a"], w_up=T["w_u"], w_down_t=T["w_o"], p1=T["p1"], p2=T["p2"],
+                  b_act=T["b_a"], b_out=T["b_o"], p_bias=T["c"], max_batch=B, profile_x=Xp,
+                  hot_frac=0.2)
+    # profile counts: exact integers on both sides
+    cnt_o = oracle.profile_counts(to_np(Xp), L["w_a"], L["b_a"])
+    assert np.array_equal(s.profile_counts, cnt_o)
+    assert np.array_equal(s.perm, oracle.permutation(cnt_o, int(np.ceil(0.2 * n))))
+    X = T["x"]
+    scores = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    y, idx, count, tok = s.decode(X, scores=scores)
+    torch.cuda.synchronize()
+    S = oracle.predict(L["x"], L["p1"], L["p2"], L["c"])
+    Sg = np.empty_like(to_np(scores))
+    Sg[:, s.perm] = to_np(scores)
+    assert np.array_equal(Sg.astype(np.float64), S)
+    k = int(count.item())
+    M = oracle.threshold(S)
+    Mg = gpu_mask_orig(s.perm, to_np(idx), k, to_np(tok), B, n)
+    assert np.array_equal(Mg, M)
+    ri, rk, rt = oracle.compact(M)
+    Y = oracle.forward(L["x"], L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    assert np.array_equal(to_np(y).astype(np.float64), Y)
+
+
+def test_empty_mask_gives_output_bias():
+    c = cfg("C2")
+    say("empty mask")
+    s, L, _ = build(c, 0, d=256, n=700, rank=64, max_batch=2, threshold=float("inf"))
+    X = tokens(c, 2, 256)
+    y, idx, count, tok = s.decode(X)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 0
+    assert np.array_equal(to_np(y), np.tile(L["b_o"], (2, 1)))
+
+
+# --------------------------------------------------------------------------- offline steps
+def test_pack_rows_bit_exact():
+    from activation_sparse_decode_rank_amd import pack_rows
+    say("pack rows")
+    rng = np.random.Generator(np.random.PCG64(3))
+    for rows, shape, dt in [(1000, (1000, 72), np.float16), (777, (777,), np.float32),
+                            (300, (300, 2, 40), np.float16)]:
+        src = rng.standard_normal(shape).astype(dt)
+        perm = rng.permutation(rows).astype(np.int32)
+        dst = to_np(pack_rows(torch.from_numpy(src).cuda(), torch.from_numpy(perm).cuda()))
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.view(np.uint8), oracle.pack_rows(src, perm).view(np.uint8))
+    # strided: the gated bundle
+    g = rng.standard_normal((50, 24)).astype(np.float16)
+    u = rng.standard_normal((50, 24)).astype(np.float16)
+    perm = rng.permutation(50).astype(np.int32)
+    pd = torch.from_numpy(perm).cuda()
+    bundle = torch.empty((50, 2, 24), dtype=torch.float16, device="cuda")
+    pack_rows(torch.from_numpy(g).cuda(), pd, bundle, 0, 96)
+    pack_rows(torch.from_numpy(u).cuda(), pd, bundle, 48, 96)
+    b = to_np(bundle)
+    assert np.array_equal(b[:, 0], oracle.pack_rows(g, perm)) and np.array_equal(b[:, 1], oracle.pack_rows(u, perm))
+
+
+def test_profile_counts_float_within_band():
+    from activation_sparse_decode_rank_amd import profile_counts
+    from synth import make_layer, make_tokens
+    c = cfg("C2")
+    say("profile counts float")
+    Lt = make_layer(c, 0, "cuda", d=512, n=1000, rank=64)
+    X = make_tokens(c, 300, 100, "cuda", d=512)
+    cg = to_np(profile_counts(Lt.w_a, Lt.b_a, X))
+    A = oracle.preact(to_np(X), to_np(Lt.w_a), to_np(Lt.b_a))
+    co = (A > 0).sum(axis=0)
+    slack = (np.abs(A) < BAND).sum(axis=0)
+    assert np.all(np.abs(cg - co) <= slack)
+
+
+# --------------------------------------------------------------------------- full sizes
+@pytest.mark.parametrize("name,layer", [("C1", 0), ("C2", 31), ("C3", 0), ("C5", 0)])
+def test_full_size_layer_decode(name, layer):
+    """Full configuration shapes, the launch configuration the benchmark times: one layer,
+    one token (C2's last layer is its 10%-active one)."""
+    c = cfg(name)
+    say(f"full size {name} layer {layer}")
+    s, L, Lt = build(c, layer, max_batch=1, profile_tokens=1024)
+    del Lt
+    X = tokens(c, 1, c.d)
+    Xh = to_np(X)
+    y, idx, count, tok = s.decode(X)
+    torch.cuda.synchronize()
+    k = int(count.item())
+    S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
+    Mg = gpu_mask_orig(s.perm, to_np(idx), k, to_np(tok), 1, c.n)
+    M, nband = check_mask(Mg, S)
+    ri, rk, rt = oracle.compact(M)
+    Y = oracle.forward(Xh, L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    errs = rel_err_rows(to_np(y), Y)
+    say(f"  count={k} ({k / c.n:.3f}) band={nband} err={max(errs):.2e}")
+    assert max(errs) <= REL_TOL
