@@ -8,7 +8,7 @@ from ._native import (  # noqa: F401
     EXPORTED, SFFN_ERR_HIP, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_F16, SFFN_F32,
     SFFN_MAX_BATCH, SFFN_OK, SffnDesc, SparseFFNError, sparse_ffn_compact, sparse_ffn_create,
     sparse_ffn_decode, sparse_ffn_destroy, sparse_ffn_forward, sparse_ffn_pack_rows,
-    sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts,
+    sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts, sparse_ffn_set_timing_events,
     sparse_ffn_status_string, sparse_ffn_workspace_bytes,
 )
 from .layer import SparseFFN, n_hot_for, pack_rows, permutation, profile_counts  # noqa: F401

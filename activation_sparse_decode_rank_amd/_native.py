@@ -49,6 +49,7 @@ def _load():
         "sparse_ffn_forward": (C.c_int, [P, P, I32, P, P, P, P, P]),
         "sparse_ffn_decode": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
         "sparse_ffn_status_string": (C.c_char_p, [C.c_int]),
+        "sparse_ffn_set_timing_events": (C.c_int, [P, C.POINTER(P)]),
         "sparse_ffn_profile_counts": (C.c_int, [P, I32, I32, P, I32, I32, P, I32, P, P]),
         "sparse_ffn_permutation": (C.c_int, [P, I32, I32, P]),
         "sparse_ffn_pack_rows": (C.c_int, [P, P, P, I32, I64, I64, P]),
@@ -63,8 +64,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destroy",
             "sparse_ffn_predict", "sparse_ffn_compact", "sparse_ffn_forward", "sparse_ffn_decode",
-            "sparse_ffn_status_string", "sparse_ffn_profile_counts", "sparse_ffn_permutation",
-            "sparse_ffn_pack_rows")
+            "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
+            "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows")
 
 
 def lib():
@@ -108,6 +109,12 @@ def sparse_ffn_forward(h, x, B, idx, count, tokmask, y, stream) -> None:
 
 def sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
     _ck(_lib.sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream), "sparse_ffn_decode")
+
+
+def sparse_ffn_set_timing_events(h, events) -> None:
+    """events: None or four hipEvent_t handles (ints)."""
+    arr = None if events is None else (C.c_void_p * 4)(*events)
+    _ck(_lib.sparse_ffn_set_timing_events(h, arr), "sparse_ffn_set_timing_events")
 
 
 def sparse_ffn_profile_counts(w_act, w_dtype, gated, b_act, d, d_ffn, x, N, counts, stream) -> None:

@@ -1,6 +1,7 @@
 """Build libsparse_ffn.so (HIP, gfx950 only) in-tree with hipcc.
 
-Usage: python -m activation_sparse_decode_rank_amd.build   (or call build()).
+Usage: python activation_sparse_decode_rank_amd/build.py   (or __graft_entry__.build()).
+Run it as a script: importing the package loads the library this builds.
 Sources are compiled in parallel into objects under _build/ and linked into the package
 directory, where the Python binding loads it.
 """

@@ -17,6 +17,8 @@ struct sparse_ffn_s {
   sffn_desc desc;
   sffn::LayerDev L;
   int max_batch;
+  hipEvent_t ev[4];
+  bool timing;
 };
 
 namespace {
@@ -74,7 +76,7 @@ std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_byt
       ++len;
     }
     rs.push_back(n);
-    if ((int)rs.size() - 1 <= sffn::G_MID_MAX) return rs;
+    if ((int)rs.size() - 1 <= std::max(target_groups, 1)) return rs;
     target *= 1.25;
   }
   return {};
@@ -134,12 +136,18 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.n_cus = cus;
     L.g_gather = std::max(1, 2 * cus);
 
+    // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
+    // of the active ones; as many ranges as can be resident at once, at most G_MID_MAX
     const double wb = desc->w_dtype == SFFN_F16 ? 2.0 : 4.0;
     const double pb = desc->p_dtype == SFFN_F16 ? 2.0 : 4.0;
-    const double act_row = wb * desc->d * (desc->gated ? 3.0 : 2.0);
-    const int target = std::max(2 * cus, (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX);
+    const double act_row = wb * desc->d * (desc->gated ? 2.0 : 1.0);
+    int target = sffn::mid_resident_groups(L, desc->max_batch);
+    if (target <= 0) target = 2 * cus;
+    target = std::min(target, sffn::G_MID_MAX);
+    const int min_groups = (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX;
+    if (target < min_groups) target = min_groups;
     std::vector<int32_t> rs = balanced_ranges(desc->d_ffn, desc->neuron_freq, pb * desc->rank,
-                                              act_row, std::min(target, sffn::G_MID_MAX));
+                                              act_row, target);
     L.g_mid = rs.empty() ? 0 : (int)rs.size() - 1;
     if (L.g_mid > 0) {
       if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
@@ -152,6 +160,8 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     h->desc.neuron_freq = nullptr;  // host array is only read here
     h->L = L;
     h->max_batch = desc->max_batch;
+    for (auto& e : h->ev) e = nullptr;
+    h->timing = false;
     *out = h;
     return SFFN_OK;
   } catch (...) {
@@ -198,9 +208,23 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (!sffn::shape_supported(h->L, true)) return SFFN_ERR_UNSUPPORTED;
   return sffn::launch_decode(h->L, x, B, y, idx, count, tokmask, scores,
-                             static_cast<hipStream_t>(stream)) == hipSuccess
+                             static_cast<hipStream_t>(stream), h->timing ? h->ev : nullptr) ==
+                 hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events) {
+  if (!h) return SFFN_ERR_INVALID;
+  if (!events) {
+    h->timing = false;
+    return SFFN_OK;
+  }
+  for (int k = 0; k < 4; ++k)
+    if (!events[k]) return SFFN_ERR_INVALID;
+  for (int k = 0; k < 4; ++k) h->ev[k] = static_cast<hipEvent_t>(events[k]);
+  h->timing = true;
+  return SFFN_OK;
 }
 
 int sparse_ffn_profile_counts(const void* w_act, int32_t w_dtype, int32_t gated,

@@ -22,11 +22,12 @@ struct LayerDev {
   const float* p_bias;
   // workspace regions
   float* q;            // [max_batch][r] predictor stage-1 output
-  float* h_full;       // [n][B] activations by neuron (stride B of the call)
-  uint64_t* tok_full;  // [n] token bits by neuron
+  float* h_buf;        // [n][B] activations: by list position (forward) or slot (decode)
+  uint64_t* tok_full;  // [n] token bits by neuron (compaction)
+  uint64_t* tok_g;     // [n] token bits by slot (decode)
+  int32_t* list_g;     // [n] neuron id by slot (decode)
   int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
   int32_t* cnt_g;      // [g_mid] active count per middle workgroup
-  int32_t* list_g;     // [g_mid][64] ascending active list per middle workgroup
   int32_t* tile_cnt;   // [n_tiles] compaction tile counts
   uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
   // launch geometry fixed at create time
@@ -36,14 +37,16 @@ struct LayerDev {
   int n_cus;     // compute units on the device
 };
 
-constexpr int G_MID_MAX = 1024;  // most workgroups the fused middle kernel may use
-constexpr int MID_RANGE_MAX = 64;  // most neurons one middle workgroup may own
+constexpr int G_MID_MAX = 1024;    // most workgroups the fused middle kernel may use
+constexpr int MID_RANGE_MAX = 256;  // most neurons one middle workgroup may own
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
 size_t workspace_bytes(int d, int n, int r, int max_batch);
 void carve_workspace(LayerDev& L, void* ws, int max_batch);
 // whether kernels exist for this shape (fused = the single-call decode path)
 bool shape_supported(const LayerDev& L, bool fused);
+// middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch
+int mid_resident_groups(const LayerDev& L, int max_batch);
 
 // launchers; each returns hipGetLastError() after enqueueing
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s);
@@ -51,8 +54,10 @@ hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t
                           int32_t* count, uint64_t* tokmask, hipStream_t s);
 hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
                           const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s);
+// ev: optional four events recorded around the three kernels (see sparse_ffn_set_timing_events)
 hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
-                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s);
+                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
+                         hipEvent_t* ev);
 hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const float* b_act,
                                  int d, int n, const float* x, int N, int64_t* counts,
                                  hipStream_t s);

@@ -80,18 +80,62 @@ __device__ __forceinline__ void load_x(const float* p, float* xs) {
   }
 }
 
-// Sum over the L consecutive lanes of an aligned lane group (L a power of two <= 64).
+// Cross-lane adds through DPP: VALU operations that read a neighbouring lane's register
+// directly, with no LDS round trip. Lanes whose source is outside the pattern, or whose
+// 16-lane row is masked off, add 0. Patterns used (each adds the value of lane src(l)):
+//   QP_XOR1 / QP_XOR2   quad permutations l^1 and l^2
+//   HALF_MIRROR         l -> 7-l within each 8 lanes; MIRROR: l -> 15-l within each row
+//   SHR(k)              l -> l-k within the row
+//   BCAST15 (rows 1,3)  += lane 15 of the previous row; BCAST31 (rows 2,3) += lane 31
+constexpr int DPP_QP_XOR1 = 0xB1, DPP_QP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141,
+              DPP_MIRROR = 0x140, DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143;
+constexpr int dpp_shr(int k) { return 0x110 + k; }
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_add_i(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Sum over all 64 lanes; the total is complete in lanes 48..63.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<DPP_QP_XOR1>(v);
+  v = dpp_add<DPP_QP_XOR2>(v);
+  v = dpp_add<DPP_HALF_MIRROR>(v);
+  v = dpp_add<DPP_MIRROR>(v);
+  v = dpp_add<DPP_BCAST15, 0xA>(v);
+  return dpp_add<DPP_BCAST31, 0xC>(v);
+}
+constexpr int WAVE_SUM_LANE = 63;
+
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v = dpp_add_i<dpp_shr(1)>(v);
+  v = dpp_add_i<dpp_shr(2)>(v);
+  v = dpp_add_i<dpp_shr(4)>(v);
+  v = dpp_add_i<dpp_shr(8)>(v);
+  v = dpp_add_i<DPP_BCAST15, 0xA>(v);
+  return dpp_add_i<DPP_BCAST31, 0xC>(v);
+}
+
+// Sum over aligned groups of L lanes (L = 1, 2, 4, ..., 64). The group's sum is complete in
+// its lane group_leader(L): the first lane for L <= 16 (every lane, in fact), the last lane
+// for L = 32 and 64.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (L >= 2) v = dpp_add<DPP_QP_XOR1>(v);
+  if (L >= 4) v = dpp_add<DPP_QP_XOR2>(v);
+  if (L >= 8) v = dpp_add<DPP_HALF_MIRROR>(v);
+  if (L >= 16) v = dpp_add<DPP_MIRROR>(v);
+  if (L >= 32) v = dpp_add<DPP_BCAST15, 0xA>(v);
+  if (L >= 64) v = dpp_add<DPP_BCAST31, 0xC>(v);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__host__ __device__ constexpr int group_leader(int L) { return L <= 16 ? 0 : L - 1; }
 
 // Cooperative copy of x [B][d] fp32 into LDS.
 __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats) {
@@ -141,10 +185,10 @@ __global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1
       }
     }
 #pragma unroll
-    for (int b = 0; b < TBG; ++b) {
-      const float v = group_sum<64>(acc[b]);
-      if ((tid & 63) == 0 && b0 + b < B) red[tid >> 6][b0 + b] = v;
-    }
+    for (int b = 0; b < TBG; ++b) acc[b] = wave_sum(acc[b]);
+#pragma unroll
+    for (int b = 0; b < TBG; ++b)
+      if ((tid & 63) == WAVE_SUM_LANE && b0 + b < B) red[tid >> 6][b0 + b] = acc[b];
   }
   __syncthreads();
   if (tid < B) q[(size_t)tid * r + j] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
@@ -189,7 +233,7 @@ __global__ __launch_bounds__(TPB) void k_pred_scores(const void* __restrict__ p2
         if (c < nchp && row < n) acc = dot_chunk<PF16>(wv[p][m], qs[m], acc);
       }
       acc = group_sum<L>(acc);
-      if (gl == 0 && row < n) scores[(size_t)b * n + row] = acc + (pbias ? pbias[row] : 0.f);
+      if (gl == group_leader(L) && row < n) scores[(size_t)b * n + row] = acc + (pbias ? pbias[row] : 0.f);
     }
   }
 }
@@ -233,8 +277,8 @@ __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict_
   if (threadIdx.x < 64) {
     int acc = 0;
     for (int u = lane; u < t; u += 64) acc += tile_cnt[u];
-    acc = wave_sum_i(acc);
-    if (lane == 0) s_off = acc;
+    acc = wave_incl_scan(acc);
+    if (lane == 63) s_off = acc;
   }
   __syncthreads();
   const int i = t * TPB + threadIdx.x;
@@ -260,7 +304,8 @@ __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict_
 // tokens. Per-row partial dots are reduced in a fixed order (wave shuffle tree, then the
 // four waves in order).
 //   plain: h = relu(w[i] . x + b[i]);  gated (row = [gate | up]): h = relu(g . x + b) * (u . x)
-// h_full[i*B + b] is written for every token (0 when the token's bit is clear).
+// Inputs are LDS arrays per listed row: neuron id (-1 = skip), token bits, bias, and the
+// output position p: h_out[p*B + b] receives h for every token (0 where the bit is clear).
 template <bool WF16, bool GATED, int CPT, int TBG>
 struct Gather {
   static constexpr int EPC = Elt<WF16>::EPC;
@@ -269,10 +314,9 @@ struct Gather {
   static constexpr int NV = GATED ? 2 : 1;
   static constexpr int RED_FLOATS = 4 * RB * TBG * NV;
 
-  // rows: LDS list of `nrows` neuron ids; bits: LDS token bits per row
-  __device__ static void run(const void* __restrict__ w_act, const float* __restrict__ b_act,
-                             const float* xsrc, int d, int n, int B, const int32_t* rows,
-                             const uint64_t* bits, int nrows, float* __restrict__ h_full,
+  __device__ static void run(const void* __restrict__ w_act, const float* xsrc, int d, int n,
+                             int B, const int32_t* rows, const uint64_t* bits, const float* bias,
+                             const int32_t* outpos, int nrows, float* __restrict__ h_out,
                              float* s_red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nch = d / EPC;                  // chunks per matrix row
@@ -328,15 +372,21 @@ struct Gather {
             }
           }
         }
+        // wave reductions, independent chains interleaved
 #pragma unroll
         for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
           for (int b = 0; b < TBG; ++b)
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-              const float s = group_sum<64>(acc[rr][b][v]);
-              if (lane == 0) s_red[((wave * RB + rr) * TBG + b) * NV + v] = s;
-            }
+            for (int v = 0; v < NV; ++v) acc[rr][b][v] = wave_sum(acc[rr][b][v]);
+        if (lane == WAVE_SUM_LANE) {
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int b = 0; b < TBG; ++b)
+#pragma unroll
+              for (int v = 0; v < NV; ++v) s_red[((wave * RB + rr) * TBG + b) * NV + v] = acc[rr][b][v];
+        }
         __syncthreads();
         if (tid < nb * TBG) {
           const int rr = tid / TBG, b = tid % TBG;
@@ -349,7 +399,7 @@ struct Gather {
               a += s_red[((1 * RB + rr) * TBG + b) * NV];
               a += s_red[((2 * RB + rr) * TBG + b) * NV];
               a += s_red[((3 * RB + rr) * TBG + b) * NV];
-              a += b_act ? b_act[i] : 0.f;
+              a += bias[base + rr];
               h = a > 0.f ? a : 0.f;
               if (GATED) {
                 float u = s_red[((0 * RB + rr) * TBG + b) * NV + 1];
@@ -359,7 +409,7 @@ struct Gather {
                 h = h * u;
               }
             }
-            h_full[(size_t)i * B + b0 + b] = h;
+            h_out[(size_t)outpos[base + rr] * B + b0 + b] = h;
           }
         }
         __syncthreads();
@@ -369,7 +419,8 @@ struct Gather {
 };
 
 // Balanced gather for the forward entry point: workgroup w takes the contiguous slice
-// [w*per, (w+1)*per) of the given ascending list (per = ceil(count / grid)).
+// [w*per, (w+1)*per) of the given list (per = ceil(count / grid)); h of list position k
+// goes to h_pos[k*B + b].
 template <bool WF16, bool GATED, int CPT, int TBG>
 __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
                                                 const float* __restrict__ b_act,
@@ -377,12 +428,15 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
                                                 const int32_t* __restrict__ idx,
                                                 const int32_t* __restrict__ count,
                                                 const uint64_t* __restrict__ tokmask,
-                                                float* __restrict__ h_full, int x_lds) {
+                                                float* __restrict__ h_pos, int x_lds) {
   using G = Gather<WF16, GATED, CPT, TBG>;
+  constexpr int RCAP = 512;
   extern __shared__ float4_t s_dyn4[];
   float* s_x = reinterpret_cast<float*>(s_dyn4);
-  __shared__ int32_t s_rows[LIST_CAP / 8];
-  __shared__ uint64_t s_bits[LIST_CAP / 8];
+  __shared__ int32_t s_rows[RCAP];
+  __shared__ uint64_t s_bits[RCAP];
+  __shared__ float s_bias[RCAP];
+  __shared__ int32_t s_pos[RCAP];
   __shared__ float s_red[G::RED_FLOATS];
   const int cnt = min(max(*count, 0), n);  // a count beyond the list is clamped
   const int per = (cnt + gridDim.x - 1) / gridDim.x;
@@ -390,117 +444,380 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
   if (k0 >= k1) return;
   if (x_lds) stage_x(s_x, x, B * d);
   const float* xsrc = x_lds ? s_x : x;
-  for (int kb = k0; kb < k1; kb += LIST_CAP / 8) {
-    const int nr = min(LIST_CAP / 8, k1 - kb);
+  for (int kb = k0; kb < k1; kb += RCAP) {
+    const int nr = min(RCAP, k1 - kb);
     __syncthreads();
     for (int u = threadIdx.x; u < nr; u += TPB) {
-      s_rows[u] = idx[kb + u];
+      const int i = idx[kb + u];
+      const bool ok = i >= 0 && i < n;
+      s_rows[u] = ok ? i : -1;
       s_bits[u] = tokmask ? tokmask[kb + u] : ~(uint64_t)0;
+      s_bias[u] = (ok && b_act) ? b_act[i] : 0.f;
+      s_pos[u] = kb + u;
     }
     __syncthreads();
-    G::run(w_act, b_act, xsrc, d, n, B, s_rows, s_bits, nr, h_full, s_red);
+    G::run(w_act, xsrc, d, n, B, s_rows, s_bits, s_bias, s_pos, nr, h_pos, s_red);
   }
 }
 
 // ============================================================================ fused middle
 // One kernel for predictor stage 2, threshold, per-workgroup compaction and the gather.
-// Workgroup w owns the contiguous neuron range [rs[w], rs[w+1]) (at most 64 neurons; the
-// ranges are balanced offline by expected cost, so the hot prefix is split into short
-// ranges). Its P2 rows form one contiguous block, read linearly (thread t takes chunks
-// t, t+256, ...); with NCHP = chunks per P2 row a power of two, a row's chunks sit in NCHP
-// consecutive lanes (or, above 64, in consecutive waves). It writes: cnt_g[w]; its
-// ascending active list at list_g[w*64 ..]; token bits tok_full[i] and activations
-// h_full[i*B + b] for its active neurons; and scores if requested.
+// Workgroup w owns the contiguous neuron range [rs[w], rs[w+1]) (1..MID_RANGE_MAX neurons;
+// the ranges are balanced offline by expected cost, so the hot prefix is split into short
+// ranges). Its P2 rows form one contiguous block, read linearly (thread t takes chunks t,
+// t+256, ...); with NCHP = chunks per P2 row a power of two, a row's chunks sit in NCHP
+// consecutive lanes (above 64, in consecutive waves). Every load that does not depend on
+// the scores (P2 block, q, biases, x) is issued before the first wait.
+// Outputs, for its k-th active neuron i (k ascending with i), at slot rs[w] + k:
+// list_g = i, tok_g = token bits, h_g[slot*B + b] = activation. cnt_g[w] = active count.
+// scores is written when non-null.
 template <bool F16, bool GATED, int CPT, int TBG>
 __global__ __launch_bounds__(TPB) void k_fused_mid(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
     int r, const void* __restrict__ w_act, const float* __restrict__ b_act,
     const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
-    int32_t* __restrict__ cnt_g, int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_full,
-    float* __restrict__ h_full, float* __restrict__ scores, int x_lds) {
+    int32_t* __restrict__ cnt_g, int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_g,
+    float* __restrict__ h_g, float* __restrict__ scores, int x_lds) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int PL = 16;  // P2 chunks a thread keeps in flight
+  constexpr int RMAX = MID_RANGE_MAX;
   using G = Gather<F16, GATED, CPT, TBG>;
   extern __shared__ float4_t s_dyn4[];
   float* s_x = reinterpret_cast<float*>(s_dyn4);
-  __shared__ uint64_t s_tok[64];
-  __shared__ int32_t s_rows[64];
-  __shared__ uint64_t s_bits[64];
-  __shared__ float s_part[64 * 4];  // per-row partial scores from up to 4 waves
+  __shared__ uint64_t s_tok[RMAX];
+  __shared__ int32_t s_rows[RMAX];
+  __shared__ uint64_t s_bits[RMAX];
+  __shared__ float s_bias[RMAX];
+  __shared__ int32_t s_pos[RMAX];
+  __shared__ float s_part[RMAX * 2];  // per-row partial scores from up to 2 waves
+  __shared__ float s_pb[RMAX];
+  __shared__ float s_ba[RMAX];
+  __shared__ int s_wcnt[TPB / 64];
   __shared__ float s_red[G::RED_FLOATS];
-  __shared__ int s_nact;
 
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = rs[w], r1 = rs[w + 1];
-  const int nown = r1 - r0;  // 1..64
+  const int nown = r1 - r0;  // 1..RMAX
   const int nchp = r / EPC;  // power of two, <= 128
   const int lg = 31 - __clz(nchp);
   const int total = nown * nchp;
-  const int grp = nchp < 64 ? nchp : 64;  // lanes of one row inside a wave
-  const int wpr = nchp > 64 ? nchp / 64 : 1;  // waves per row
+  const int grp = nchp < 64 ? nchp : 64;      // lanes of one row inside a wave
+  const int wpr = nchp > 64 ? nchp / 64 : 1;  // waves per row (1 or 2)
   const size_t blk0 = (size_t)r0 * nchp;
+  const int pos = tid & (nchp - 1);  // this thread's chunk within its row (256 % nchp == 0)
 
-  if (tid < 64) s_tok[tid] = 0;
-  if (x_lds) stage_x(s_x, x, B * d);
-  for (int c0 = 0; c0 < total; c0 += PL * TPB) {
-    u32x4 wv[PL];
+  // ---- every score-independent load first
+  u32x4 wv[PL];
 #pragma unroll
-    for (int m = 0; m < PL; ++m) {
-      const int f = c0 + tid + m * TPB;
-      if (f < total) wv[m] = ld_chunk(p2, blk0 + f);
-    }
-    __syncthreads();
-    const int pos = tid & (nchp - 1);  // same for every m since 256 % nchp == 0
-    for (int b = 0; b < B; ++b) {
-      float qs[EPC];
-      load_x<EPC>(q + (size_t)b * r + (size_t)pos * EPC, qs);
+  for (int m = 0; m < PL; ++m) {
+    const int f = tid + m * TPB;
+    if (f < total) wv[m] = ld_chunk(p2, blk0 + f);
+  }
+  float qs[EPC];
+  load_x<EPC>(q + (size_t)pos * EPC, qs);
+  float pb = 0.f, ba = 0.f;
+  if (tid < nown) {
+    pb = pbias ? pbias[r0 + tid] : 0.f;
+    ba = b_act ? b_act[r0 + tid] : 0.f;
+  }
+  s_tok[tid] = 0;
+  if (x_lds) stage_x(s_x, x, B * d);
+  if (tid < nown) {
+    s_pb[tid] = pb;
+    s_ba[tid] = ba;
+  }
+  __syncthreads();
+
+  // ---- predictor stage 2 and threshold
+  for (int c0 = 0; c0 < total; c0 += PL * TPB) {
+    if (c0 > 0) {  // rows beyond the first PL*256 chunks: next block (rare)
+      __syncthreads();
 #pragma unroll
       for (int m = 0; m < PL; ++m) {
         const int f = c0 + tid + m * TPB;
-        float acc = 0.f;
-        if (f < total) acc = dot_chunk<F16>(wv[m], qs, 0.f);
-        for (int o = grp / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (f < total && (lane & (grp - 1)) == 0) {
-          const int j = f >> lg;
-          s_part[j * 4 + (wpr > 1 ? (wave & (wpr - 1)) : 0)] = acc;
+        if (f < total) wv[m] = ld_chunk(p2, blk0 + f);
+      }
+    }
+    for (int b = 0; b < B; ++b) {
+      if (b > 0 || c0 > 0) load_x<EPC>(q + (size_t)b * r + (size_t)pos * EPC, qs);
+      const int mlim = min(PL, (total - c0 + TPB - 1) / TPB);  // chunk slots in use (uniform)
+      float acc[PL];
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        acc[m] = 0.f;
+        if (m < mlim) {
+          const int f = c0 + tid + m * TPB;
+          if (f < total) acc[m] = dot_chunk<F16>(wv[m], qs, 0.f);
         }
+      }
+      // group sums over grp lanes (uniform branches; the PL chains interleave)
+      if (grp >= 2) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_QP_XOR1>(acc[m]);
+      }
+      if (grp >= 4) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_QP_XOR2>(acc[m]);
+      }
+      if (grp >= 8) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_HALF_MIRROR>(acc[m]);
+      }
+      if (grp >= 16) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_MIRROR>(acc[m]);
+      }
+      if (grp >= 32) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_BCAST15, 0xA>(acc[m]);
+      }
+      if (grp >= 64) {
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+          if (m < mlim) acc[m] = dpp_add<DPP_BCAST31, 0xC>(acc[m]);
+      }
+      const int leader = group_leader(grp);
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int f = c0 + tid + m * TPB;
+        if (m < mlim && f < total && (lane & (grp - 1)) == leader)
+          s_part[(f >> lg) * 2 + (wpr > 1 ? (wave & 1) : 0)] = acc[m];
       }
       __syncthreads();
       if (tid < nown && tid * nchp >= c0 && tid * nchp < c0 + PL * TPB) {
-        // rows whose chunks all lie in this pass: finish score, threshold
-        const int j = tid;
-        float s = s_part[j * 4];
-        for (int u = 1; u < wpr; ++u) s += s_part[j * 4 + u];
-        const int i = r0 + j;
-        s += pbias ? pbias[i] : 0.f;
-        if (scores) scores[(size_t)b * n + i] = s;
-        if (s > tau) s_tok[j] |= (uint64_t)1 << b;
+        float s = s_part[tid * 2];
+        if (wpr > 1) s += s_part[tid * 2 + 1];
+        s += s_pb[tid];
+        if (scores) scores[(size_t)b * n + r0 + tid] = s;
+        if (s > tau) s_tok[tid] |= (uint64_t)1 << b;
       }
       __syncthreads();
     }
   }
-  // ---- compaction of the owned range (one wave: ballot + prefix popcount)
-  if (tid < 64) {
-    const uint64_t bits = (tid < nown) ? s_tok[tid] : 0;
-    const bool act = bits != 0;
-    const uint64_t word = __ballot(act);
-    const uint64_t lower = tid ? (word & ((~(uint64_t)0) >> (64 - tid))) : 0;
-    if (act) {
-      const int pos = __popcll(lower);
-      const int i = r0 + tid;
-      s_rows[pos] = i;
-      s_bits[pos] = bits;
-      list_g[(size_t)w * 64 + pos] = i;
-      tok_full[i] = bits;
+  // ---- compaction of the owned range: ballot per wave, prefix over the four waves
+  const uint64_t bits = (tid < nown) ? s_tok[tid] : 0;
+  const bool act = bits != 0;
+  const uint64_t word = __ballot(act);
+  if (lane == 0) s_wcnt[wave] = __popcll(word);
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < wave; ++v) before += s_wcnt[v];
+  const int nact = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  if (act) {
+    const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+    const int k = before + __popcll(lower);
+    const int i = r0 + tid;
+    s_rows[k] = i;
+    s_bits[k] = bits;
+    s_bias[k] = s_ba[tid];
+    s_pos[k] = r0 + k;
+    list_g[r0 + k] = i;
+    tok_g[r0 + k] = bits;
+  }
+  if (tid == 0) cnt_g[w] = nact;
+  __syncthreads();
+  // ---- gather + ReLU over the owned active rows
+  G::run(w_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_bias, s_pos, nact, h_g, s_red);
+}
+
+// ---------------------------------------------------------------------------- B = 1
+// The single-token form of the middle kernel, specialized on NCHP (chunks per predictor
+// row) so that the lane-group reductions are straight-line DPP code. Addresses of unused
+// slots are clamped into the owned block instead of branching per lane.
+template <bool F16, bool GATED, int CPT, int NCHP>
+__global__ __launch_bounds__(TPB) void k_mid_b1(
+    const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
+    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
+    int d, int n, float tau, const int32_t* __restrict__ rs, int32_t* __restrict__ cnt_g,
+    int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_g, float* __restrict__ h_g,
+    float* __restrict__ scores, int x_lds) {
+  constexpr int EPC = Elt<F16>::EPC;
+  constexpr int GRP = NCHP < 64 ? NCHP : 64;   // lanes holding one predictor row in a wave
+  constexpr int WPR = NCHP > 64 ? NCHP / 64 : 1;  // waves per predictor row
+  constexpr int RPP = TPB / NCHP;              // predictor rows per slot of the workgroup
+  constexpr int PL = 8;                        // slots in flight per thread
+  constexpr int RMAX = MID_RANGE_MAX;
+  constexpr int RB = (16 / CPT) > 0 ? (16 / CPT) : 1;  // gathered rows in flight
+  constexpr int NV = GATED ? 2 : 1;
+  static_assert(NCHP >= 1 && NCHP <= 128 && (NCHP & (NCHP - 1)) == 0, "NCHP");
+  extern __shared__ float4_t s_dyn4[];
+  float* s_x = reinterpret_cast<float*>(s_dyn4);
+  __shared__ uint8_t s_act[RMAX];
+  __shared__ int32_t s_rows[RMAX];
+  __shared__ float s_bias[RMAX];
+  __shared__ float s_part[WPR > 1 ? RMAX * WPR : 1];
+  __shared__ float s_pb[RMAX];
+  __shared__ float s_ba[RMAX];
+  __shared__ int s_wcnt[TPB / 64];
+  __shared__ float s_red[4 * RB * NV];
+
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = rs[w], r1 = rs[w + 1];
+  const int nown = r1 - r0;  // 1..RMAX
+  const int pos = tid & (NCHP - 1);
+  const int rsub = tid / NCHP;
+  const int nslots = (nown + RPP - 1) / RPP;
+  const size_t blk0 = (size_t)r0 * NCHP;
+
+  // ---- every score-independent load first: P2 (first PL slots), q, biases, x
+  u32x4 wv[PL];
+#pragma unroll
+  for (int m = 0; m < PL; ++m) {
+    const int j = min(m * RPP + rsub, nown - 1);
+    wv[m] = ld_chunk(p2, blk0 + (size_t)j * NCHP + pos);
+  }
+  float qs[EPC];
+  load_x<EPC>(q + (size_t)pos * EPC, qs);
+  float pb = 0.f, ba = 0.f;
+  if (tid < nown) {
+    pb = pbias ? pbias[r0 + tid] : 0.f;
+    ba = b_act ? b_act[r0 + tid] : 0.f;
+  }
+  s_act[tid] = 0;
+  if (x_lds) stage_x(s_x, x, d);
+  if (tid < nown) {
+    s_pb[tid] = pb;
+    s_ba[tid] = ba;
+  }
+  __syncthreads();
+
+  // ---- predictor stage 2 and threshold
+  for (int s0 = 0; s0 < nslots; s0 += PL) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int j = min((s0 + m) * RPP + rsub, nown - 1);
+        wv[m] = ld_chunk(p2, blk0 + (size_t)j * NCHP + pos);
+      }
     }
-    if (tid == 0) {
-      s_nact = __popcll(word);
-      cnt_g[w] = __popcll(word);
+    float acc[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m) acc[m] = dot_chunk<F16>(wv[m], qs, 0.f);
+#pragma unroll
+    for (int m = 0; m < PL; ++m) acc[m] = group_sum<GRP>(acc[m]);
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
+      const int j = (s0 + m) * RPP + rsub;
+      if (j < nown && (lane & (GRP - 1)) == group_leader(GRP)) {
+        if (WPR == 1) {
+          const float sc = acc[m] + s_pb[j];
+          if (scores) scores[r0 + j] = sc;
+          s_act[j] = sc > tau ? 1 : 0;
+        } else {
+          s_part[j * WPR + (wave & (WPR - 1))] = acc[m];
+        }
+      }
+    }
+    if (WPR > 1) {
+      __syncthreads();
+      const int jlo = s0 * RPP, jhi = min(nown, (s0 + PL) * RPP);
+      if (tid >= jlo && tid < jhi) {
+        float sc = s_part[tid * WPR];
+#pragma unroll
+        for (int u = 1; u < WPR; ++u) sc += s_part[tid * WPR + u];
+        sc += s_pb[tid];
+        if (scores) scores[r0 + tid] = sc;
+        s_act[tid] = sc > tau ? 1 : 0;
+      }
+      __syncthreads();
     }
   }
   __syncthreads();
-  // ---- gather + ReLU over the owned active rows
-  G::run(w_act, b_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_nact, h_full, s_red);
+  // ---- compaction of the owned range: ballot per wave, prefix over the four waves
+  const bool act = tid < nown && s_act[tid];
+  const uint64_t word = __ballot(act);
+  if (lane == 0) s_wcnt[wave] = __popcll(word);
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wcnt[v] : 0;
+  const int nact = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  if (act) {
+    const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+    const int k = before + __popcll(lower);
+    s_rows[k] = r0 + tid;
+    s_bias[k] = s_ba[tid];
+    list_g[r0 + k] = r0 + tid;
+    tok_g[r0 + k] = 1;
+  }
+  if (tid == 0) cnt_g[w] = nact;
+  __syncthreads();
+
+  // ---- gather-GEMV + ReLU over the active rows, RB rows in flight
+  const float* xsrc = x_lds ? s_x : x;
+  const int nch = d / EPC;
+  const int rowch = GATED ? 2 * nch : nch;
+  for (int base = 0; base < nact; base += RB) {
+    const int nb = min(RB, nact - base);  // uniform
+    u32x4 gv[RB][CPT];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      if (rr < nb) {
+        const size_t row0 = (size_t)s_rows[base + rr] * rowch;
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_chunk(w_act, row0 + min(tid + m * TPB, rowch - 1));
+      }
+    }
+    float acc[RB][NV];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[rr][v] = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * TPB;
+      const bool cv = c < rowch;
+      const bool up = GATED && c >= nch;
+      const int xc = min(up ? c - nch : c, nch - 1);
+      float xs[EPC];
+      load_x<EPC>(xsrc + (size_t)xc * EPC, xs);
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        if (rr < nb) {
+          const float dv = dot_chunk<F16>(gv[rr][m], xs, 0.f);
+          const float add = cv ? dv : 0.f;
+          if (GATED && up) acc[rr][NV - 1] += add;
+          else acc[rr][0] += add;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if (rr < nb) acc[rr][v] = wave_sum(acc[rr][v]);
+    if (lane == WAVE_SUM_LANE) {
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (rr < nb) s_red[(wave * RB + rr) * NV + v] = acc[rr][v];
+    }
+    __syncthreads();
+    if (tid < nb) {
+      const int rr = tid;
+      float a = s_red[(0 * RB + rr) * NV];
+      a += s_red[(1 * RB + rr) * NV];
+      a += s_red[(2 * RB + rr) * NV];
+      a += s_red[(3 * RB + rr) * NV];
+      a += s_bias[base + rr];
+      float h = a > 0.f ? a : 0.f;
+      if (GATED) {
+        float u = s_red[(0 * RB + rr) * NV + 1];
+        u += s_red[(1 * RB + rr) * NV + 1];
+        u += s_red[(2 * RB + rr) * NV + 1];
+        u += s_red[(3 * RB + rr) * NV + 1];
+        h = h * u;
+      }
+      h_g[r0 + base + rr] = h;
+    }
+    __syncthreads();
+  }
 }
 
 // ============================================================================ down
@@ -508,29 +825,31 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
 // row of W_down^T, i.e. 16 fp16 / 8 fp32 output columns, and sums over the whole active
 // list, so no cross-workgroup reduction exists. The four workgroups that share a 128-byte
 // line are placed on the same XCD (workgroups are dealt to the 8 XCDs round-robin), so
-// each line is fetched into one L2 once. Thread t handles chunk t&1 and the active rows
-// k = t>>1, t>>1 + 128, ... (LOADS rows in flight), then the 128 row-lane partials are
-// summed in ascending order.
-// LIST_FROM_WG: the active list is the concatenation, in workgroup order, of the fused
-// middle kernel's per-workgroup lists (which is ascending); this kernel also writes idx,
-// count and tokmask. Otherwise the list is idx[0..*count).
-template <bool WF16, bool LIST_FROM_WG, int TB>
+// each line is fetched into one L2 once. Thread t handles chunk t&1 and list positions
+// k = t>>1 + 128j; per batch, the row ids and activations are loaded first, then the
+// weight chunks (LOADS rows in flight), then the FMAs. Partial sums are reduced by a
+// fixed shuffle tree across the row lanes of a wave, then across the four waves in order.
+// FROM_WG: the list is the middle kernel's: workgroup u's active neurons sit at slots
+// rs[u] .. rs[u] + cnt_g[u]; concatenated in u order they are ascending. This kernel also
+// writes idx, count and tokmask (if non-null) for that list. Otherwise the list is
+// idx_in[0..*count) and activations are indexed by list position.
+template <bool WF16, bool FROM_WG, int TB>
 __global__ __launch_bounds__(TPB) void k_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
-    const float* __restrict__ h_full, int d, int n, int B, const int32_t* __restrict__ idx_in,
+    const float* __restrict__ h_in, int d, int n, int B, const int32_t* __restrict__ idx_in,
     const int32_t* __restrict__ count_in, const int32_t* __restrict__ cnt_g,
-    const int32_t* __restrict__ list_g, int g_mid, const uint64_t* __restrict__ tok_full,
-    int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
-    uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
+    const int32_t* __restrict__ rs, const int32_t* __restrict__ list_g,
+    const uint64_t* __restrict__ tok_g, int g_mid, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int NRL = TPB / 2;  // row lanes
+  constexpr int UPT = G_MID_MAX / TPB;  // middle workgroups per thread in the scan
   extern __shared__ float4_t s_dyn4[];
-  int32_t* s_list = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
-  float* s_red = reinterpret_cast<float*>(s_dyn4);       // aliases s_list after the sum
-  __shared__ int32_t s_off[1024 + 1];                    // per-middle-workgroup offsets
-  __shared__ int s_total;
+  int32_t* s_slot = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
+  __shared__ int s_wsum[TPB / 64];
+  __shared__ float s_red[TPB / 64][4][2][TB * EPC];  // [wave][row][chunk parity][value]
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = d / EPC;
   const int G = gridDim.x;
   int s = blockIdx.x;
@@ -539,29 +858,28 @@ __global__ __launch_bounds__(TPB) void k_down(
   const int chunk = 2 * s + ch;
 
   int total;
-  if (LIST_FROM_WG) {
-    // exclusive scan of the middle kernel's per-workgroup counts (g_mid <= 1024)
-    if (tid < 64) {
-      // each lane sums a contiguous block of counts, then a lane-ordered scan
-      const int per = (g_mid + 63) / 64;
-      const int a0 = tid * per, a1 = min(g_mid, a0 + per);
-      int sum = 0;
-      for (int u = a0; u < a1; ++u) sum += cnt_g[u];
-      int incl = sum;
+  int cu[UPT], ru[UPT], offu[UPT];
+  if (FROM_WG) {
+    int tsum = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += v;
-      }
-      int run = incl - sum;
-      for (int u = a0; u < a1; ++u) {
-        s_off[u] = run;
-        run += cnt_g[u];
-      }
-      if (tid == 63) s_total = incl;
+    for (int v = 0; v < UPT; ++v) {
+      const int u = tid * UPT + v;
+      cu[v] = u < g_mid ? cnt_g[u] : 0;
+      ru[v] = u < g_mid ? rs[u] : 0;
+      tsum += cu[v];
     }
+    const int incl = wave_incl_scan(tsum);
+    if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
-    total = s_total;
+    int woff = 0;
+    for (int v = 0; v < wave; ++v) woff += s_wsum[v];
+    total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    int run = woff + incl - tsum;
+#pragma unroll
+    for (int v = 0; v < UPT; ++v) {
+      offu[v] = run;
+      run += cu[v];
+    }
     if (blockIdx.x == 0 && tid == 0) *count_out = total;
   } else {
     total = min(max(*count_in, 0), n);  // a count beyond the list is clamped
@@ -569,80 +887,113 @@ __global__ __launch_bounds__(TPB) void k_down(
 
   float acc[TB][EPC];
   const int ntg = (B + TB - 1) / TB;
+  const int wcap = FROM_WG ? LIST_CAP : (total > 0 ? total : 1);
+  const int pub = (total + G - 1) / G;
+  const int pub0 = blockIdx.x * pub, pub1 = pub0 + pub;
   for (int tg = 0; tg < ntg; ++tg) {
     const int b0 = tg * TB;
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
-    for (int wb = 0; wb < total; wb += LIST_CAP) {
-      const int wl = min(LIST_CAP, total - wb);
-      __syncthreads();
-      if (LIST_FROM_WG) {
-        for (int u = tid; u < g_mid; u += TPB) {
-          const int c = cnt_g[u], o = s_off[u];
-          for (int jj = 0; jj < c; ++jj) {
-            const int k = o + jj;
-            if (k >= wb && k < wb + wl) s_list[k - wb] = list_g[(size_t)u * 64 + jj];
+    for (int wb = 0; wb < total; wb += wcap) {
+      const int wl = min(wcap, total - wb);
+      if (FROM_WG) {
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < UPT; ++v) {
+          const int lo = max(offu[v], wb), hi = min(offu[v] + cu[v], wb + wl);
+          for (int k = lo; k < hi; ++k) s_slot[k - wb] = ru[v] + (k - offu[v]);
+        }
+        __syncthreads();
+      }
+      // Per batch: every row id and activation load first, then every weight-chunk load,
+      // then stores, then the FMAs. All slots are executed; a slot past the end of the
+      // list reads the last listed position again and contributes 0. Straight-line code
+      // keeps the compiler's wait counts exact, so no weight load waits on another.
+      for (int kb0 = 0; kb0 < wl; kb0 += NRL * LOADS) {
+        int hp[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int kc = min(kb0 + u * NRL + rl, wl - 1);
+          hp[u] = FROM_WG ? s_slot[kc] : wb + kc;
+        }
+        int ii[LOADS];
+        float hv[LOADS][TB];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          ii[u] = FROM_WG ? list_g[hp[u]] : idx_in[hp[u]];
+#pragma unroll
+          for (int b = 0; b < TB; ++b) hv[u][b] = h_in[(size_t)hp[u] * B + min(b0 + b, B - 1)];
+        }
+        uint64_t tb[LOADS];
+        const bool publish = FROM_WG && tg == 0;
+        if (publish && tokmask_out) {
+#pragma unroll
+          for (int u = 0; u < LOADS; ++u) tb[u] = tok_g[hp[u]];
+        }
+        u32x4 wv[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int ic = (ii[u] >= 0 && ii[u] < n) ? ii[u] : 0;  // out-of-range entries add 0
+          wv[u] = ld_chunk(w_down_t, (size_t)ic * nch + chunk);
+        }
+        if (publish && ch == 0) {
+          // the ascending list with token bits: workgroup g owns positions [g*pub, (g+1)*pub)
+#pragma unroll
+          for (int u = 0; u < LOADS; ++u) {
+            const int k = kb0 + u * NRL + rl;
+            if (k < wl && wb + k >= pub0 && wb + k < pub1) {
+              idx_out[wb + k] = ii[u];
+              if (tokmask_out) tokmask_out[wb + k] = tb[u];
+            }
           }
         }
-      } else {
-        for (int u = tid; u < wl; u += TPB) s_list[u] = idx_in[wb + u];
-      }
-      __syncthreads();
-      if (LIST_FROM_WG && tg == 0) {
-        // publish the ascending list and token bits: workgroup w writes k = w (mod G)
-        for (int u = blockIdx.x + tid * G; u < wl; u += TPB * G) {
-          const int i = s_list[u];
-          idx_out[wb + u] = i;
-          if (tokmask_out) tokmask_out[wb + u] = tok_full[i];
-        }
-      }
-      for (int kb = rl; kb < wl; kb += NRL * LOADS) {
-        u32x4 wv[LOADS];
-        int ii[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-          const int k = kb + u * NRL;
-          ii[u] = (k < wl) ? s_list[k] : -1;
-          if (ii[u] >= n) ii[u] = -1;  // out-of-range entries are skipped
-          if (ii[u] >= 0) wv[u] = ld_chunk(w_down_t, (size_t)ii[u] * nch + chunk);
-        }
+          const int k = kb0 + u * NRL + rl;
+          const bool ok = k < wl && ii[u] >= 0 && ii[u] < n;
+          float f[EPC];
+          unpack<WF16>(wv[u], f);
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-          if (ii[u] >= 0) {
-            float f[EPC];
-            unpack<WF16>(wv[u], f);
+          for (int b = 0; b < TB; ++b) {
+            const float h = (ok && b0 + b < B) ? hv[u][b] : 0.f;
 #pragma unroll
-            for (int b = 0; b < TB; ++b) {
-              if (b0 + b < B) {
-                const float h = h_full[(size_t)ii[u] * B + b0 + b];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[b][e] = fmaf(h, f[e], acc[b][e]);
-              }
-            }
+            for (int e2 = 0; e2 < EPC; ++e2) acc[b][e2] = fmaf(h, f[e2], acc[b][e2]);
           }
         }
       }
     }
-    // fixed-order reduction over the 128 row lanes
-    __syncthreads();
+    // fixed-order reduction: within each 16-lane row over lanes of equal chunk parity
+    // (DPP: lanes l^2, l-4, l-8; complete in lanes 12 and 13), then rows and waves in order
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) s_red[((b * EPC + e) * 2 + ch) * NRL + rl] = acc[b][e];
+      for (int e = 0; e < EPC; ++e) {
+        float v = dpp_add<DPP_QP_XOR2>(acc[b][e]);
+        v = dpp_add<dpp_shr(4)>(v);
+        acc[b][e] = dpp_add<dpp_shr(8)>(v);
+      }
+    if ((lane & 15) == 12 || (lane & 15) == 13) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_red[wave][lane >> 4][lane & 1][b * EPC + e] = acc[b][e];
+    }
     __syncthreads();
-    const int nout = TB * EPC * 2;
-    if (tid < nout) {
-      const int b = tid / (EPC * 2), rem = tid % (EPC * 2), e = rem / 2, c2 = rem % 2;
+    if (tid < TB * EPC * 2) {
+      const int c2 = tid & 1, be = tid >> 1, b = be / EPC, e = be % EPC;
       if (b0 + b < B) {
-        const float* p = s_red + (size_t)((b * EPC + e) * 2 + c2) * NRL;
         float sum = 0.f;
-        for (int u = 0; u < NRL; ++u) sum += p[u];
+#pragma unroll
+        for (int wv2 = 0; wv2 < TPB / 64; ++wv2)
+#pragma unroll
+          for (int row = 0; row < 4; ++row) sum += s_red[wv2][row][c2][be];
         const int col = (2 * s + c2) * EPC + e;
         y[(size_t)(b0 + b) * d + col] = sum + (b_out ? b_out[col] : 0.f);
       }
     }
+    __syncthreads();
   }
 }
 
@@ -741,11 +1092,12 @@ size_t workspace_bytes(int d, int n, int r, int max_batch) {
   const int n_tiles = (n + TPB - 1) / TPB;
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
-  b += align256((size_t)n * max_batch * 4);      // h_full
+  b += align256((size_t)n * max_batch * 4);      // h_buf
   b += align256((size_t)n * 8);                  // tok_full
+  b += align256((size_t)n * 8);                  // tok_g
+  b += align256((size_t)n * 4);                  // list_g
   b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
   b += align256((size_t)G_MID_MAX * 4);          // cnt_g
-  b += align256((size_t)G_MID_MAX * 64 * 4);     // list_g
   b += align256((size_t)n_tiles * 4);            // tile_cnt
   b += align256((size_t)((n + 63) / 64) * 8);    // words
   return b;
@@ -757,11 +1109,12 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   const int n_tiles = (n + TPB - 1) / TPB;
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
   L.q = reinterpret_cast<float*>(take((size_t)max_batch * L.r * 4));
-  L.h_full = reinterpret_cast<float*>(take((size_t)n * max_batch * 4));
+  L.h_buf = reinterpret_cast<float*>(take((size_t)n * max_batch * 4));
   L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
+  L.tok_g = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
+  L.list_g = reinterpret_cast<int32_t*>(take((size_t)n * 4));
   L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
   L.cnt_g = reinterpret_cast<int32_t*>(take((size_t)G_MID_MAX * 4));
-  L.list_g = reinterpret_cast<int32_t*>(take((size_t)G_MID_MAX * 64 * 4));
   L.tile_cnt = reinterpret_cast<int32_t*>(take((size_t)n_tiles * 4));
   L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
   L.n_tiles = n_tiles;
@@ -827,10 +1180,10 @@ void gather_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
   if (B == 1)
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 1>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_full, xl ? 1 : 0);
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0);
   else
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 4>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_full, xl ? 1 : 0);
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0);
 }
 
 template <bool F16, bool GATED>
@@ -850,31 +1203,85 @@ void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* co
                  hipStream_t s) {
   constexpr int EPC = F16 ? 8 : 4;
   const int grid = (L.d / EPC) / 2;
-  if (B == 1) {
-    const size_t lds = std::max((size_t)LIST_CAP * 4, (size_t)1 * EPC * 2 * (TPB / 2) * 4);
+  const size_t lds = FROM_WG ? (size_t)LIST_CAP * 4 : 0;
+  if (B == 1)
     hipLaunchKernelGGL((k_down<F16, FROM_WG, 1>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
-                       L.b_out, L.h_full, L.d, L.n, B, idx, count, L.cnt_g, L.list_g, L.g_mid,
-                       L.tok_full, idx_out, count_out, tok_out, y);
-  } else {
-    const size_t lds = std::max((size_t)LIST_CAP * 4, (size_t)4 * EPC * 2 * (TPB / 2) * 4);
+                       L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
+                       L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
+  else
     hipLaunchKernelGGL((k_down<F16, FROM_WG, 4>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
-                       L.b_out, L.h_full, L.d, L.n, B, idx, count, L.cnt_g, L.list_g, L.g_mid,
-                       L.tok_full, idx_out, count_out, tok_out, y);
+                       L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
+                       L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
+}
+
+template <bool F16, bool GATED, int CPT, int NCHP>
+void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s) {
+  const bool xl = x_in_lds(1, L.d);
+  const size_t lds = xl ? (size_t)L.d * 4 : 0;
+  hipLaunchKernelGGL((k_mid_b1<F16, GATED, CPT, NCHP>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+                     L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs, L.cnt_g, L.list_g,
+                     L.tok_g, L.h_buf, scores, xl ? 1 : 0);
+}
+
+template <bool F16, bool GATED, int CPT>
+bool mid_b1_dispatch(const LayerDev& L, const float* x, float* scores, hipStream_t s) {
+  switch (L.r / (F16 ? 8 : 4)) {
+    case 8: mid_b1_launch<F16, GATED, CPT, 8>(L, x, scores, s); return true;
+    case 16: mid_b1_launch<F16, GATED, CPT, 16>(L, x, scores, s); return true;
+    case 32: mid_b1_launch<F16, GATED, CPT, 32>(L, x, scores, s); return true;
+    case 64: mid_b1_launch<F16, GATED, CPT, 64>(L, x, scores, s); return true;
+    case 128: mid_b1_launch<F16, GATED, CPT, 128>(L, x, scores, s); return true;
+    default: return false;
   }
 }
 
 template <bool F16, bool GATED, int CPT>
 void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  if (B == 1 && mid_b1_dispatch<F16, GATED, CPT>(L, x, scores, s)) return;
   const bool xl = x_in_lds(B, L.d);
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
   if (B == 1)
     hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 1>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
                        L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
-                       L.list_g, L.tok_full, L.h_full, scores, xl ? 1 : 0);
+                       L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
   else
     hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 4>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
                        L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
-                       L.list_g, L.tok_full, L.h_full, scores, xl ? 1 : 0);
+                       L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
+}
+
+template <bool F16, bool GATED, int CPT, int NCHP>
+int mid_b1_occ(size_t lds) {
+  int a = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_mid_b1<F16, GATED, CPT, NCHP>, TPB, lds) != hipSuccess) a = 0;
+  return a;
+}
+
+template <bool F16, bool GATED, int CPT>
+int mid_occupancy_cpt(const LayerDev& L, int B) {
+  const size_t lds = x_in_lds(B, L.d) ? (size_t)B * L.d * 4 : 0;
+  int a = 0, b = 0;
+  switch (L.r / (F16 ? 8 : 4)) {
+    case 8: a = mid_b1_occ<F16, GATED, CPT, 8>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    case 16: a = mid_b1_occ<F16, GATED, CPT, 16>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    case 32: a = mid_b1_occ<F16, GATED, CPT, 32>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    case 64: a = mid_b1_occ<F16, GATED, CPT, 64>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    case 128: a = mid_b1_occ<F16, GATED, CPT, 128>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    default:
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_fused_mid<F16, GATED, CPT, 1>, TPB, lds) != hipSuccess) a = 0;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_fused_mid<F16, GATED, CPT, 4>, TPB, lds) != hipSuccess) b = 0;
+  return B == 1 ? a : std::min(a, b);
+}
+
+template <bool F16, bool GATED>
+int mid_occupancy(const LayerDev& L, int B) {
+  switch (pick_cpt(row_chunks(L))) {
+    case 1: return mid_occupancy_cpt<F16, GATED, 1>(L, B);
+    case 2: return mid_occupancy_cpt<F16, GATED, 2>(L, B);
+    case 4: return mid_occupancy_cpt<F16, GATED, 4>(L, B);
+    default: return mid_occupancy_cpt<F16, GATED, 8>(L, B);
+  }
 }
 
 template <bool F16, bool GATED>
@@ -888,6 +1295,19 @@ void mid_dispatch(const LayerDev& L, const float* x, int B, float* scores, hipSt
 }
 
 }  // namespace
+
+int mid_resident_groups(const LayerDev& L, int max_batch) {
+  if (pick_cpt(row_chunks(L)) == 0 || L.w_f16 != L.p_f16) return 0;
+  int occ1, occb;
+  if (L.w_f16) {
+    occ1 = L.gated ? mid_occupancy<true, true>(L, 1) : mid_occupancy<true, false>(L, 1);
+    occb = L.gated ? mid_occupancy<true, true>(L, max_batch) : mid_occupancy<true, false>(L, max_batch);
+  } else {
+    occ1 = L.gated ? mid_occupancy<false, true>(L, 1) : mid_occupancy<false, false>(L, 1);
+    occb = L.gated ? mid_occupancy<false, true>(L, max_batch) : mid_occupancy<false, false>(L, max_batch);
+  }
+  return std::min(occ1, occb) * L.n_cus;
+}
 
 bool shape_supported(const LayerDev& L, bool fused) {
   if (pick_cpt(row_chunks(L)) == 0) return false;
@@ -931,20 +1351,27 @@ hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_
 }
 
 hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
-                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s) {
+                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
+                         hipEvent_t* ev) {
+  if (ev) (void)hipEventRecord(ev[0], s);
   if (L.p_f16)
     stage1_launch<true>(L, x, B, s);
   else
     stage1_launch<false>(L, x, B, s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   if (L.w_f16) {
     if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s);
     else mid_dispatch<true, false>(L, x, B, scores, s);
-    down_launch<true, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
   } else {
     if (L.gated) mid_dispatch<false, true>(L, x, B, scores, s);
     else mid_dispatch<false, false>(L, x, B, scores, s);
-    down_launch<false, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
   }
+  if (ev) (void)hipEventRecord(ev[2], s);
+  if (L.w_f16)
+    down_launch<true, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
+  else
+    down_launch<false, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
+  if (ev) (void)hipEventRecord(ev[3], s);
   return hipGetLastError();
 }
 

@@ -140,6 +140,14 @@ int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t*
 int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                       int32_t* count, uint64_t* tokmask, float* scores, void* stream);
 
+/* Measurement hook. events: NULL (off) or an array of four hipEvent_t (passed as void*)
+ * created by the caller. While set, every sparse_ffn_decode on this handle records
+ * events[0] before its predictor stage-1 kernel, events[1] before the fused middle kernel
+ * (stage 2, threshold, compaction, gather), events[2] before the down projection and
+ * events[3] after it, all on the call's stream, so hipEventElapsedTime gives each
+ * kernel's duration. The events are borrowed; the handle only stores the four values. */
+int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events);
+
 /* Human-readable text for a status code (static storage). */
 const char* sparse_ffn_status_string(int status);
 
