@@ -112,8 +112,8 @@ def sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
 
 
 def sparse_ffn_set_timing_events(h, events) -> None:
-    """events: None or four hipEvent_t handles (ints)."""
-    arr = None if events is None else (C.c_void_p * 4)(*events)
+    """events: None or six hipEvent_t handles (ints): a start/end pair per decode kernel."""
+    arr = None if events is None else (C.c_void_p * 6)(*events)
     _ck(_lib.sparse_ffn_set_timing_events(h, arr), "sparse_ffn_set_timing_events")
 
 

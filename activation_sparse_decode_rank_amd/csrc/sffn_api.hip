@@ -17,7 +17,7 @@ struct sparse_ffn_s {
   sffn_desc desc;
   sffn::LayerDev L;
   int max_batch;
-  hipEvent_t ev[4];
+  hipEvent_t ev[6];
   bool timing;
 };
 
@@ -220,9 +220,9 @@ int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events) {
     h->timing = false;
     return SFFN_OK;
   }
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 6; ++k)
     if (!events[k]) return SFFN_ERR_INVALID;
-  for (int k = 0; k < 4; ++k) h->ev[k] = static_cast<hipEvent_t>(events[k]);
+  for (int k = 0; k < 6; ++k) h->ev[k] = static_cast<hipEvent_t>(events[k]);
   h->timing = true;
   return SFFN_OK;
 }

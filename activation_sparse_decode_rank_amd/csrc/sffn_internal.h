@@ -54,10 +54,10 @@ hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t
                           int32_t* count, uint64_t* tokmask, hipStream_t s);
 hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
                           const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s);
-// ev: optional four events recorded around the three kernels (see sparse_ffn_set_timing_events)
+// ev: optional six events, a start/end pair stamped by each of the three kernel dispatches
 hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
                          int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
-                         hipEvent_t* ev);
+                         const hipEvent_t* ev);
 hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const float* b_act,
                                  int d, int n, const float* x, int N, int64_t* counts,
                                  hipStream_t s);

@@ -19,6 +19,8 @@
 // every reduction has a fixed order, so results are bit-reproducible.
 #include "sffn_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 namespace sffn {
@@ -1143,12 +1145,26 @@ void pick_group(int nchp, int& Lw, int& cplp) {
 }
 bool x_in_lds(int B, int d) { return (size_t)B * d * 4 <= (size_t)X_LDS_MAX; }
 
-template <bool F16>
-void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s) {
-  if (B == 1)
-    hipLaunchKernelGGL((k_pred_stage1<F16, 1>), dim3(L.r), dim3(TPB), 0, s, L.p1, x, L.d, L.r, B, L.q);
+// Launch a kernel. With a timing pair (tev != nullptr) the launch goes through
+// hipExtLaunchKernelGGL, which stamps tev[0] and tev[1] with the dispatch's own start and
+// end times (the timestamps a kernel-trace profiler reports), not with marker packets
+// queued around it.
+template <typename K, typename... A>
+void launch(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const hipEvent_t* tev,
+            A... a) {
+  if (tev)
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, tev[0], tev[1], 0u, a...);
   else
-    hipLaunchKernelGGL((k_pred_stage1<F16, 4>), dim3(L.r), dim3(TPB), 0, s, L.p1, x, L.d, L.r, B, L.q);
+    kern<<<grid, block, lds, s>>>(a...);
+}
+
+template <bool F16>
+void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
+                   const hipEvent_t* tev = nullptr) {
+  if (B == 1)
+    launch(k_pred_stage1<F16, 1>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q);
+  else
+    launch(k_pred_stage1<F16, 4>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q);
 }
 
 template <bool F16>
@@ -1200,52 +1216,55 @@ void gather_dispatch(const LayerDev& L, const float* x, int B, const int32_t* id
 template <bool F16, bool FROM_WG>
 void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                  int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
-                 hipStream_t s) {
+                 hipStream_t s, const hipEvent_t* tev = nullptr) {
   constexpr int EPC = F16 ? 8 : 4;
   const int grid = (L.d / EPC) / 2;
   const size_t lds = FROM_WG ? (size_t)LIST_CAP * 4 : 0;
   if (B == 1)
-    hipLaunchKernelGGL((k_down<F16, FROM_WG, 1>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
+    launch(k_down<F16, FROM_WG, 1>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
                        L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
                        L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
   else
-    hipLaunchKernelGGL((k_down<F16, FROM_WG, 4>), dim3(grid), dim3(TPB), lds, s, L.w_down_t,
+    launch(k_down<F16, FROM_WG, 4>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
                        L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
                        L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
-void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s) {
+void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                   const hipEvent_t* tev) {
   const bool xl = x_in_lds(1, L.d);
   const size_t lds = xl ? (size_t)L.d * 4 : 0;
-  hipLaunchKernelGGL((k_mid_b1<F16, GATED, CPT, NCHP>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+  launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
                      L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs, L.cnt_g, L.list_g,
                      L.tok_g, L.h_buf, scores, xl ? 1 : 0);
 }
 
 template <bool F16, bool GATED, int CPT>
-bool mid_b1_dispatch(const LayerDev& L, const float* x, float* scores, hipStream_t s) {
+bool mid_b1_dispatch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                     const hipEvent_t* tev) {
   switch (L.r / (F16 ? 8 : 4)) {
-    case 8: mid_b1_launch<F16, GATED, CPT, 8>(L, x, scores, s); return true;
-    case 16: mid_b1_launch<F16, GATED, CPT, 16>(L, x, scores, s); return true;
-    case 32: mid_b1_launch<F16, GATED, CPT, 32>(L, x, scores, s); return true;
-    case 64: mid_b1_launch<F16, GATED, CPT, 64>(L, x, scores, s); return true;
-    case 128: mid_b1_launch<F16, GATED, CPT, 128>(L, x, scores, s); return true;
+    case 8: mid_b1_launch<F16, GATED, CPT, 8>(L, x, scores, s, tev); return true;
+    case 16: mid_b1_launch<F16, GATED, CPT, 16>(L, x, scores, s, tev); return true;
+    case 32: mid_b1_launch<F16, GATED, CPT, 32>(L, x, scores, s, tev); return true;
+    case 64: mid_b1_launch<F16, GATED, CPT, 64>(L, x, scores, s, tev); return true;
+    case 128: mid_b1_launch<F16, GATED, CPT, 128>(L, x, scores, s, tev); return true;
     default: return false;
   }
 }
 
 template <bool F16, bool GATED, int CPT>
-void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
-  if (B == 1 && mid_b1_dispatch<F16, GATED, CPT>(L, x, scores, s)) return;
+void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s,
+                    const hipEvent_t* tev) {
+  if (B == 1 && mid_b1_dispatch<F16, GATED, CPT>(L, x, scores, s, tev)) return;
   const bool xl = x_in_lds(B, L.d);
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
   if (B == 1)
-    hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 1>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+    launch(k_fused_mid<F16, GATED, CPT, 1>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
                        L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
                        L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
   else
-    hipLaunchKernelGGL((k_fused_mid<F16, GATED, CPT, 4>), dim3(L.g_mid), dim3(TPB), lds, s, L.p2,
+    launch(k_fused_mid<F16, GATED, CPT, 4>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
                        L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
                        L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
 }
@@ -1285,12 +1304,13 @@ int mid_occupancy(const LayerDev& L, int B) {
 }
 
 template <bool F16, bool GATED>
-void mid_dispatch(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+void mid_dispatch(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s,
+                  const hipEvent_t* tev) {
   switch (pick_cpt(row_chunks(L))) {
-    case 1: mid_launch_cpt<F16, GATED, 1>(L, x, B, scores, s); break;
-    case 2: mid_launch_cpt<F16, GATED, 2>(L, x, B, scores, s); break;
-    case 4: mid_launch_cpt<F16, GATED, 4>(L, x, B, scores, s); break;
-    default: mid_launch_cpt<F16, GATED, 8>(L, x, B, scores, s); break;
+    case 1: mid_launch_cpt<F16, GATED, 1>(L, x, B, scores, s, tev); break;
+    case 2: mid_launch_cpt<F16, GATED, 2>(L, x, B, scores, s, tev); break;
+    case 4: mid_launch_cpt<F16, GATED, 4>(L, x, B, scores, s, tev); break;
+    default: mid_launch_cpt<F16, GATED, 8>(L, x, B, scores, s, tev); break;
   }
 }
 
@@ -1352,26 +1372,25 @@ hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_
 
 hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
                          int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
-                         hipEvent_t* ev) {
-  if (ev) (void)hipEventRecord(ev[0], s);
+                         const hipEvent_t* ev) {
+  const hipEvent_t* t1 = ev ? ev + 0 : nullptr;
+  const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
+  const hipEvent_t* t3 = ev ? ev + 4 : nullptr;
   if (L.p_f16)
-    stage1_launch<true>(L, x, B, s);
+    stage1_launch<true>(L, x, B, s, t1);
   else
-    stage1_launch<false>(L, x, B, s);
-  if (ev) (void)hipEventRecord(ev[1], s);
+    stage1_launch<false>(L, x, B, s, t1);
   if (L.w_f16) {
-    if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s);
-    else mid_dispatch<true, false>(L, x, B, scores, s);
+    if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s, t2);
+    else mid_dispatch<true, false>(L, x, B, scores, s, t2);
   } else {
-    if (L.gated) mid_dispatch<false, true>(L, x, B, scores, s);
-    else mid_dispatch<false, false>(L, x, B, scores, s);
+    if (L.gated) mid_dispatch<false, true>(L, x, B, scores, s, t2);
+    else mid_dispatch<false, false>(L, x, B, scores, s, t2);
   }
-  if (ev) (void)hipEventRecord(ev[2], s);
   if (L.w_f16)
-    down_launch<true, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
+    down_launch<true, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s, t3);
   else
-    down_launch<false, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s);
-  if (ev) (void)hipEventRecord(ev[3], s);
+    down_launch<false, true>(L, B, nullptr, nullptr, idx, count, tokmask, y, s, t3);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ replayed from HIP graphs (one per group of tokens) with inputs resident in HBM; 
 region is bracketed by device synchronizations.
 
 Also measured, beside the headline number:
-  - per-kernel durations from HIP events the library records on its own stream;
+  - per-kernel durations from HIP events that each kernel dispatch stamps itself
+    (start and end of execution, on the library's stream);
   - the dense FFN of the same shapes on the same (unpacked) fp16 weights, through torch
     (hipBLASLt), graph-captured and timed the same way;
   - the fp64 CPU oracle on a bounded sample of the same workload, on the host cores.
@@ -73,6 +74,29 @@ class HipEvents:
         self.ev = []
 
 
+def measured_traffic(kernel_file, workload):
+    """HBM bytes per dispatch of the dominant kernel from the committed counter summary
+    profiles/<kernel>_<workload>_pmc.md (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of
+    known size), or None when there is none or the kernel source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_file}_{workload}_pmc.md")
+    src = os.path.join(ROOT, "activation_sparse_decode_rank_amd", "csrc", "sffn_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel source sha256") != digest:
+        return None
+    try:
+        return float(fields["traffic bytes per dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def kernel_bytes(cfg, n_act):
     """Algorithmic bytes per launch of each decode kernel for one token."""
     sw, sp = cfg.w_bytes, cfg.p_bytes
@@ -98,6 +122,12 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every decode eagerly instead of replaying captured graphs "
+                         "(for per-dispatch counter collection; the timing is then not the metric)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB 4 times (the known-size "
+                         "kernel that scales HBM counter readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,6 +151,15 @@ def main():
     steps = max(G, ((args.steps + G - 1) // G) * G)
     warmup = ((args.warmup + G - 1) // G) * G
     t_setup = time.time()
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 4 x {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
 
     # ------------------------------------------------------------------ offline: layers
     Xprof = make_tokens(cfg, args.profile_tokens, 100, "cuda")
@@ -156,16 +195,21 @@ def main():
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
     graphs = []
-    for gi in range(T // G):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            for t in range(gi * G, (gi + 1) * G):
-                decode_token(t)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    log(f"captured {len(graphs)} graphs of {G * L * 3} kernels")
+    if not args.no_graph:
+        for gi in range(T // G):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for t in range(gi * G, (gi + 1) * G):
+                    decode_token(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} graphs of {G * L * 3} kernels")
 
     def replay(graph_list, ntok):
+        if not graph_list:
+            for i in range(ntok):
+                decode_token(i % T)
+            return
         for i in range(ntok // G):
             graph_list[i % len(graph_list)].replay()
 
@@ -193,11 +237,11 @@ def main():
 
     # ------------------------------------------------------------------ per-kernel event pass
     KT = min(args.kernel_tokens, T)
-    hev = HipEvents(4 * KT * L)
+    hev = HipEvents(6 * KT * L)
     for t in range(KT):
         for l in range(L):
-            base = 4 * (t * L + l)
-            NAT.sparse_ffn_set_timing_events(layers[l].handle, hev.ev[base:base + 4])
+            base = 6 * (t * L + l)
+            NAT.sparse_ffn_set_timing_events(layers[l].handle, hev.ev[base:base + 6])
             layers[l].decode(X[t, l:l + 1], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
                              tokmask=tok_buf[l])
     torch.cuda.synchronize()
@@ -207,10 +251,9 @@ def main():
     kbytes = {"stage1": [], "mid": [], "down": []}
     for t in range(KT):
         for l in range(L):
-            base = 4 * (t * L + l)
-            kus["stage1"].append(1000.0 * hev.elapsed_ms(base, base + 1))
-            kus["mid"].append(1000.0 * hev.elapsed_ms(base + 1, base + 2))
-            kus["down"].append(1000.0 * hev.elapsed_ms(base + 2, base + 3))
+            base = 6 * (t * L + l)
+            for j, k in enumerate(("stage1", "mid", "down")):
+                kus[k].append(1000.0 * hev.elapsed_ms(base + 2 * j, base + 2 * j + 1))
             kb = kernel_bytes(cfg, int(cnt[t, l]))
             for k in kb:
                 kbytes[k].append(kb[k])
@@ -222,7 +265,7 @@ def main():
         kernels[k] = {"avg_us": round(us, 3), "algorithmic_bytes": int(np.mean(kbytes[k])),
                       "gbps": round(gb, 1)}
     dom = max(("mid", "down"), key=lambda k: kernels[k]["avg_us"])
-    kname = {"mid": "k_fused_mid (predictor stage 2 + threshold + compaction + gather-GEMV/ReLU)",
+    kname = {"mid": "k_mid_b1 (predictor stage 2 + threshold + compaction + gather-GEMV/ReLU)",
              "down": "k_down (down projection, column-owned)"}[dom]
     log("kernels:", json.dumps(kernels))
 
@@ -299,8 +342,11 @@ def main():
 
     # ------------------------------------------------------------------ report
     kd = kernels[dom]
+    traffic = measured_traffic({"mid": "k_mid_b1", "down": "k_down"}[dom], cfg.name)
     roof = {"bound": "hbm", "kernel": kname, "achieved": kd["gbps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(kd["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+            "unit": "GB/s", "frac": round(kd["gbps"] / HBM_PEAK_GBPS, 4),
+            "traffic": (int(traffic) if traffic is not None else None),
+            "algorithmic_bytes": kd["algorithmic_bytes"]}
     act_lo, act_hi = min(cfg.activity), max(cfg.activity)
     out = {
         "metric": METRIC,

@@ -140,12 +140,15 @@ int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t*
 int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                       int32_t* count, uint64_t* tokmask, float* scores, void* stream);
 
-/* Measurement hook. events: NULL (off) or an array of four hipEvent_t (passed as void*)
- * created by the caller. While set, every sparse_ffn_decode on this handle records
- * events[0] before its predictor stage-1 kernel, events[1] before the fused middle kernel
- * (stage 2, threshold, compaction, gather), events[2] before the down projection and
- * events[3] after it, all on the call's stream, so hipEventElapsedTime gives each
- * kernel's duration. The events are borrowed; the handle only stores the four values. */
+/* Measurement hook. events: NULL (off) or an array of six hipEvent_t (passed as void*)
+ * created by the caller. While set, every sparse_ffn_decode on this handle launches its
+ * three kernels so that each dispatch stamps a pair of events with its own start and end
+ * time: events[0..1] the predictor stage-1 kernel, events[2..3] the fused middle kernel
+ * (stage 2, threshold, compaction, gather), events[4..5] the down projection. Then
+ * hipEventElapsedTime(events[2k], events[2k+1]) is that kernel's execution time, the same
+ * interval a kernel-trace profiler reports. Use it outside graph capture. The events are
+ * borrowed; the handle only stores the six values. Returns SFFN_ERR_INVALID for a NULL
+ * handle or a NULL entry. */
 int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events);
 
 /* Human-readable text for a status code (static storage). */
