@@ -24,6 +24,7 @@ class SffnDesc(C.Structure):
         ("b_out", C.c_void_p), ("p1", C.c_void_p), ("p2", C.c_void_p), ("p_bias", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
         ("neuron_freq", C.c_void_p),
+        ("deterministic", C.c_int32),
     ]
 
 

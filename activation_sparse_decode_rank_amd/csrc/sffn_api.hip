@@ -135,6 +135,7 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
       return SFFN_ERR_HIP;
     L.n_cus = cus;
     L.g_gather = std::max(1, 2 * cus);
+    L.ks_down = sffn::down_split(L, desc->deterministic != 0);
 
     // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
     // of the active ones; as many ranges as can be resident at once, at most G_MID_MAX

@@ -35,6 +35,8 @@ struct LayerDev {
   int n_tiles;   // compaction tiles of 256 neurons
   int g_gather;  // workgroups of the balanced gather
   int n_cus;     // compute units on the device
+  int ks_down;   // row splits of the down projection (1 = plain stores; 2 keeps y bitwise
+                 // reproducible; more adds float atomics in a varying order)
 };
 
 constexpr int G_MID_MAX = 1024;    // most workgroups the fused middle kernel may use
@@ -43,6 +45,9 @@ constexpr int MID_RANGE_MAX = 256;  // most neurons one middle workgroup may own
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
 size_t workspace_bytes(int d, int n, int r, int max_batch);
 void carve_workspace(LayerDev& L, void* ws, int max_batch);
+// 128-byte column blocks of the down projection, and the row split it should use
+int down_blocks(const LayerDev& L);
+int down_split(const LayerDev& L, bool deterministic);
 // whether kernels exist for this shape (fused = the single-call decode path)
 bool shape_supported(const LayerDev& L, bool fused);
 // middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch

@@ -139,6 +139,11 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 __host__ __device__ constexpr int group_leader(int L) { return L <= 16 ? 0 : L - 1; }
 
+// y[0..ny) = 0 over the whole grid: the down projection adds its split-k sums into y.
+__device__ __forceinline__ void zero_grid(float* __restrict__ y, int ny) {
+  for (int i = blockIdx.x * TPB + threadIdx.x; i < ny; i += gridDim.x * TPB) y[i] = 0.f;
+}
+
 // Cooperative copy of x [B][d] fp32 into LDS.
 __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats) {
   const float4_t* src = reinterpret_cast<const float4_t*>(x);
@@ -152,9 +157,11 @@ __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats
 template <bool PF16, int TBG>
 __global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
                                                      const float* __restrict__ x, int d, int r,
-                                                     int B, float* __restrict__ q) {
+                                                     int B, float* __restrict__ q,
+                                                     float* __restrict__ y0, int ny) {
   constexpr int EPC = Elt<PF16>::EPC;
   constexpr int MAXC = 8;
+  zero_grid(y0, ny);
   const int j = blockIdx.x, tid = threadIdx.x;
   const int nch = d / EPC;
   const size_t row0 = (size_t)j * nch;
@@ -430,8 +437,10 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
                                                 const int32_t* __restrict__ idx,
                                                 const int32_t* __restrict__ count,
                                                 const uint64_t* __restrict__ tokmask,
-                                                float* __restrict__ h_pos, int x_lds) {
+                                                float* __restrict__ h_pos, int x_lds,
+                                                float* __restrict__ y0, int ny) {
   using G = Gather<WF16, GATED, CPT, TBG>;
+  zero_grid(y0, ny);
   constexpr int RCAP = 512;
   extern __shared__ float4_t s_dyn4[];
   float* s_x = reinterpret_cast<float*>(s_dyn4);
@@ -823,41 +832,56 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
 }
 
 // ============================================================================ down
-// Down projection with column ownership: workgroup w owns 2 chunks (32 bytes) of every
-// row of W_down^T, i.e. 16 fp16 / 8 fp32 output columns, and sums over the whole active
-// list, so no cross-workgroup reduction exists. The four workgroups that share a 128-byte
-// line are placed on the same XCD (workgroups are dealt to the 8 XCDs round-robin), so
-// each line is fetched into one L2 once. Thread t handles chunk t&1 and list positions
-// k = t>>1 + 128j; per batch, the row ids and activations are loaded first, then the
-// weight chunks (LOADS rows in flight), then the FMAs. Partial sums are reduced by a
-// fixed shuffle tree across the row lanes of a wave, then across the four waves in order.
-// FROM_WG: the list is the middle kernel's: workgroup u's active neurons sit at slots
-// rs[u] .. rs[u] + cnt_g[u]; concatenated in u order they are ascending. This kernel also
-// writes idx, count and tokmask (if non-null) for that list. Otherwise the list is
-// idx_in[0..*count) and activations are indexed by list position.
+// Down projection y_b = sum_k h_{k,b} W_down^T[idx_k] + b_out, split two ways:
+//  - columns: workgroup (cb, kq) owns the 128-byte column block cb (8 chunks = 8*EPC output
+//    columns), so every weight read is a whole 128-byte line of a row;
+//  - rows (split-k): it owns list positions [kq*per, min(total, (kq+1)*per)),
+//    per = ceil(total / KS).
+// Inside the workgroup, thread t handles chunk t&7 of the block and row slot t>>3 (32
+// slots); per batch the row ids and activations are loaded first, then LOADS_D weight
+// chunks per thread, then the FMAs. The 32 slots are reduced in a fixed order (DPP within
+// 16-lane rows, then LDS across rows and waves). The workgroup's sums are added into y,
+// which an earlier kernel of the same call has zeroed: a plain store when KS == 1, else a
+// float atomic add, b_out riding on kq == 0's sum. With KS == 2 the result is still
+// bitwise reproducible (two addends onto +0 commute exactly); KS > 2 trades that for
+// speed. The KS workgroups of one block are dealt to the same XCD (block ids cb + kq*ncb
+// with ncb a multiple of 8; workgroups go to the 8 XCDs round-robin), so their atomics
+// meet in one L2.
+// FROM_WG: the list is the middle kernel's: range u's active neurons sit at slots
+// rs[u] .. rs[u] + cnt_g[u]; concatenated in u order they are ascending. This kernel then
+// also writes idx, count and tokmask (if non-null) for that list, each workgroup of split
+// kq a share of kq's positions. Otherwise the list is idx_in[0..*count) and activations
+// are indexed by list position.
+constexpr int CB_LANES = 8;               // 16-byte chunks per column block (128 bytes)
+constexpr int RSD = TPB / CB_LANES;       // row slots per workgroup
+template <int TB>
+struct DownCfg {
+  static constexpr int LOADS_D = TB == 1 ? 16 : 8;  // weight rows a thread keeps in flight
+};
+
 template <bool WF16, bool FROM_WG, int TB>
 __global__ __launch_bounds__(TPB) void k_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, int B, const int32_t* __restrict__ idx_in,
     const int32_t* __restrict__ count_in, const int32_t* __restrict__ cnt_g,
     const int32_t* __restrict__ rs, const int32_t* __restrict__ list_g,
-    const uint64_t* __restrict__ tok_g, int g_mid, int32_t* __restrict__ idx_out,
+    const uint64_t* __restrict__ tok_g, int g_mid, int KS, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
   constexpr int EPC = Elt<WF16>::EPC;
-  constexpr int NRL = TPB / 2;  // row lanes
-  constexpr int UPT = G_MID_MAX / TPB;  // middle workgroups per thread in the scan
+  constexpr int COLS = CB_LANES * EPC;
+  constexpr int LD = DownCfg<TB>::LOADS_D;
+  constexpr int UPT = G_MID_MAX / TPB;  // middle ranges per thread in the scan
   extern __shared__ float4_t s_dyn4[];
   int32_t* s_slot = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
   __shared__ int s_wsum[TPB / 64];
-  __shared__ float s_red[TPB / 64][4][2][TB * EPC];  // [wave][row][chunk parity][value]
+  __shared__ float s_red[TPB / 64][4][CB_LANES][TB * EPC];  // [wave][16-lane row][chunk][value]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = d / EPC;
-  const int G = gridDim.x;
-  int s = blockIdx.x;
-  if ((G & 7) == 0) s = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int ch = tid & 1, rl = tid >> 1;
-  const int chunk = 2 * s + ch;
+  const int ncb = gridDim.x / KS;
+  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
+  const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
+  const int chunk = min(cb * CB_LANES + li, nch - 1);  // a partial last block re-reads; unused
 
   int total;
   int cu[UPT], ru[UPT], offu[UPT];
@@ -882,24 +906,26 @@ __global__ __launch_bounds__(TPB) void k_down(
       offu[v] = run;
       run += cu[v];
     }
-    if (blockIdx.x == 0 && tid == 0) *count_out = total;
+    if (blockIdx.x == 0 && tid == 0 && count_out) *count_out = total;
   } else {
     total = min(max(*count_in, 0), n);  // a count beyond the list is clamped
   }
+  const int per = (total + KS - 1) / KS;
+  const int p0 = min(total, kq * per), p1 = min(total, p0 + per);
+  // this workgroup's share of split kq's positions for publishing the list
+  const int pubq = (p1 - p0 + ncb - 1) / ncb;
+  const int pub0 = p0 + cb * pubq, pub1 = min(p1, pub0 + pubq);
 
   float acc[TB][EPC];
   const int ntg = (B + TB - 1) / TB;
-  const int wcap = FROM_WG ? LIST_CAP : (total > 0 ? total : 1);
-  const int pub = (total + G - 1) / G;
-  const int pub0 = blockIdx.x * pub, pub1 = pub0 + pub;
   for (int tg = 0; tg < ntg; ++tg) {
     const int b0 = tg * TB;
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
-    for (int wb = 0; wb < total; wb += wcap) {
-      const int wl = min(wcap, total - wb);
+    for (int wb = p0; wb < p1; wb += LIST_CAP) {
+      const int wl = min(LIST_CAP, p1 - wb);
       if (FROM_WG) {
         __syncthreads();
 #pragma unroll
@@ -909,51 +935,49 @@ __global__ __launch_bounds__(TPB) void k_down(
         }
         __syncthreads();
       }
-      // Per batch: every row id and activation load first, then every weight-chunk load,
-      // then stores, then the FMAs. All slots are executed; a slot past the end of the
-      // list reads the last listed position again and contributes 0. Straight-line code
-      // keeps the compiler's wait counts exact, so no weight load waits on another.
-      for (int kb0 = 0; kb0 < wl; kb0 += NRL * LOADS) {
-        int hp[LOADS];
+      // Per batch: every row id and activation load first, then every weight load, then
+      // stores, then the FMAs. Slots past the end re-read the last position and add 0.
+      for (int kb0 = 0; kb0 < wl; kb0 += RSD * LD) {
+        int hp[LD];
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-          const int kc = min(kb0 + u * NRL + rl, wl - 1);
+        for (int u = 0; u < LD; ++u) {
+          const int kc = min(kb0 + u * RSD + rsl, wl - 1);
           hp[u] = FROM_WG ? s_slot[kc] : wb + kc;
         }
-        int ii[LOADS];
-        float hv[LOADS][TB];
+        int ii[LD];
+        float hv[LD][TB];
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
+        for (int u = 0; u < LD; ++u) {
           ii[u] = FROM_WG ? list_g[hp[u]] : idx_in[hp[u]];
 #pragma unroll
           for (int b = 0; b < TB; ++b) hv[u][b] = h_in[(size_t)hp[u] * B + min(b0 + b, B - 1)];
         }
-        uint64_t tb[LOADS];
-        const bool publish = FROM_WG && tg == 0;
-        if (publish && tokmask_out) {
+        const bool publish = FROM_WG && tg == 0 && idx_out;
+        uint64_t tb[LD];
+        if (TB > 1 && publish && tokmask_out) {
 #pragma unroll
-          for (int u = 0; u < LOADS; ++u) tb[u] = tok_g[hp[u]];
+          for (int u = 0; u < LD; ++u) tb[u] = tok_g[hp[u]];
         }
-        u32x4 wv[LOADS];
+        u32x4 wv[LD];
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
+        for (int u = 0; u < LD; ++u) {
           const int ic = (ii[u] >= 0 && ii[u] < n) ? ii[u] : 0;  // out-of-range entries add 0
           wv[u] = ld_chunk(w_down_t, (size_t)ic * nch + chunk);
         }
-        if (publish && ch == 0) {
-          // the ascending list with token bits: workgroup g owns positions [g*pub, (g+1)*pub)
+        if (publish && li == 0) {
 #pragma unroll
-          for (int u = 0; u < LOADS; ++u) {
-            const int k = kb0 + u * NRL + rl;
+          for (int u = 0; u < LD; ++u) {
+            const int k = kb0 + u * RSD + rsl;
             if (k < wl && wb + k >= pub0 && wb + k < pub1) {
               idx_out[wb + k] = ii[u];
-              if (tokmask_out) tokmask_out[wb + k] = tb[u];
+              // TB == 1 is launched only for one token: every listed neuron carries bit 0
+              if (tokmask_out) tokmask_out[wb + k] = TB == 1 ? (uint64_t)1 : tb[u];
             }
           }
         }
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-          const int k = kb0 + u * NRL + rl;
+        for (int u = 0; u < LD; ++u) {
+          const int k = kb0 + u * RSD + rsl;
           const bool ok = k < wl && ii[u] >= 0 && ii[u] < n;
           float f[EPC];
           unpack<WF16>(wv[u], f);
@@ -966,33 +990,35 @@ __global__ __launch_bounds__(TPB) void k_down(
         }
       }
     }
-    // fixed-order reduction: within each 16-lane row over lanes of equal chunk parity
-    // (DPP: lanes l^2, l-4, l-8; complete in lanes 12 and 13), then rows and waves in order
+    // fixed-order reduction of the 32 row slots: lanes l and l+8 of each 16-lane row
+    // (DPP, complete in lanes 8..15), then the 4 rows of each wave and the 4 waves in order
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        float v = dpp_add<DPP_QP_XOR2>(acc[b][e]);
-        v = dpp_add<dpp_shr(4)>(v);
-        acc[b][e] = dpp_add<dpp_shr(8)>(v);
-      }
-    if ((lane & 15) == 12 || (lane & 15) == 13) {
+      for (int e = 0; e < EPC; ++e) acc[b][e] = dpp_add<dpp_shr(8)>(acc[b][e]);
+    if ((lane & 15) >= 8) {
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s_red[wave][lane >> 4][lane & 1][b * EPC + e] = acc[b][e];
+        for (int e = 0; e < EPC; ++e) s_red[wave][(lane >> 4)][li][b * EPC + e] = acc[b][e];
     }
     __syncthreads();
-    if (tid < TB * EPC * 2) {
-      const int c2 = tid & 1, be = tid >> 1, b = be / EPC, e = be % EPC;
-      if (b0 + b < B) {
+    if (tid < TB * COLS) {
+      const int b = tid / COLS, cc = tid % COLS;
+      const int c_li = cc / EPC, e = cc % EPC;
+      const int col = (cb * CB_LANES + c_li) * EPC + e;
+      if (b0 + b < B && col < d && (kq == 0 || p1 > p0)) {
         float sum = 0.f;
 #pragma unroll
-        for (int wv2 = 0; wv2 < TPB / 64; ++wv2)
+        for (int w2 = 0; w2 < TPB / 64; ++w2)
 #pragma unroll
-          for (int row = 0; row < 4; ++row) sum += s_red[wv2][row][c2][be];
-        const int col = (2 * s + c2) * EPC + e;
-        y[(size_t)(b0 + b) * d + col] = sum + (b_out ? b_out[col] : 0.f);
+          for (int row = 0; row < 4; ++row) sum += s_red[w2][row][c_li][b * EPC + e];
+        if (kq == 0 && b_out) sum += b_out[col];
+        float* dst = y + (size_t)(b0 + b) * d + col;
+        if (KS == 1)
+          *dst = sum;
+        else
+          atomicAdd(dst, sum);
       }
     }
     __syncthreads();
@@ -1158,13 +1184,15 @@ void launch(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const hipE
     kern<<<grid, block, lds, s>>>(a...);
 }
 
+// y0: output the down projection will add into (zeroed here when it splits rows), or null
 template <bool F16>
 void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                   const hipEvent_t* tev = nullptr) {
+                   const hipEvent_t* tev = nullptr, float* y0 = nullptr) {
+  const int ny = (y0 && L.ks_down > 1) ? B * L.d : 0;
   if (B == 1)
-    launch(k_pred_stage1<F16, 1>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q);
+    launch(k_pred_stage1<F16, 1>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q, y0, ny);
   else
-    launch(k_pred_stage1<F16, 4>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q);
+    launch(k_pred_stage1<F16, 4>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q, y0, ny);
 }
 
 template <bool F16>
@@ -1191,25 +1219,28 @@ hipError_t predict_t(const LayerDev& L, const float* x, int B, float* scores, hi
 
 template <bool F16, bool GATED, int CPT>
 void gather_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                   const int32_t* count, const uint64_t* tokmask, hipStream_t s) {
+                   const int32_t* count, const uint64_t* tokmask, float* y0, hipStream_t s) {
   const bool xl = x_in_lds(B, L.d);
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
+  const int ny = L.ks_down > 1 ? B * L.d : 0;
   if (B == 1)
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 1>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0);
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
+                       y0, ny);
   else
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 4>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0);
+                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
+                       y0, ny);
 }
 
 template <bool F16, bool GATED>
 void gather_dispatch(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                     const int32_t* count, const uint64_t* tokmask, hipStream_t s) {
+                     const int32_t* count, const uint64_t* tokmask, float* y0, hipStream_t s) {
   switch (pick_cpt(row_chunks(L))) {
-    case 1: gather_launch<F16, GATED, 1>(L, x, B, idx, count, tokmask, s); break;
-    case 2: gather_launch<F16, GATED, 2>(L, x, B, idx, count, tokmask, s); break;
-    case 4: gather_launch<F16, GATED, 4>(L, x, B, idx, count, tokmask, s); break;
-    default: gather_launch<F16, GATED, 8>(L, x, B, idx, count, tokmask, s); break;
+    case 1: gather_launch<F16, GATED, 1>(L, x, B, idx, count, tokmask, y0, s); break;
+    case 2: gather_launch<F16, GATED, 2>(L, x, B, idx, count, tokmask, y0, s); break;
+    case 4: gather_launch<F16, GATED, 4>(L, x, B, idx, count, tokmask, y0, s); break;
+    default: gather_launch<F16, GATED, 8>(L, x, B, idx, count, tokmask, y0, s); break;
   }
 }
 
@@ -1217,17 +1248,16 @@ template <bool F16, bool FROM_WG>
 void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                  int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
                  hipStream_t s, const hipEvent_t* tev = nullptr) {
-  constexpr int EPC = F16 ? 8 : 4;
-  const int grid = (L.d / EPC) / 2;
+  const int grid = down_blocks(L) * L.ks_down;
   const size_t lds = FROM_WG ? (size_t)LIST_CAP * 4 : 0;
   if (B == 1)
     launch(k_down<F16, FROM_WG, 1>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
                        L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
-                       L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
+                       L.tok_g, L.g_mid, L.ks_down, idx_out, count_out, tok_out, y);
   else
     launch(k_down<F16, FROM_WG, 4>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
                        L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
-                       L.tok_g, L.g_mid, idx_out, count_out, tok_out, y);
+                       L.tok_g, L.g_mid, L.ks_down, idx_out, count_out, tok_out, y);
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
@@ -1316,6 +1346,18 @@ void mid_dispatch(const LayerDev& L, const float* x, int B, float* scores, hipSt
 
 }  // namespace
 
+int down_blocks(const LayerDev& L) {
+  const int nch = L.d / (L.w_f16 ? 8 : 4);
+  return (nch + CB_LANES - 1) / CB_LANES;
+}
+
+int down_split(const LayerDev& L, bool deterministic) {
+  const int ncb = down_blocks(L);
+  int ks = std::max(1, std::min(8, (L.n_cus + ncb / 2) / ncb));
+  if (deterministic) ks = std::min(ks, 2);
+  return ks;
+}
+
 int mid_resident_groups(const LayerDev& L, int max_batch) {
   if (pick_cpt(row_chunks(L)) == 0 || L.w_f16 != L.p_f16) return 0;
   int occ1, occb;
@@ -1359,12 +1401,12 @@ hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t
 hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
                           const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s) {
   if (L.w_f16) {
-    if (L.gated) gather_dispatch<true, true>(L, x, B, idx, count, tokmask, s);
-    else gather_dispatch<true, false>(L, x, B, idx, count, tokmask, s);
+    if (L.gated) gather_dispatch<true, true>(L, x, B, idx, count, tokmask, y, s);
+    else gather_dispatch<true, false>(L, x, B, idx, count, tokmask, y, s);
     down_launch<true, false>(L, B, idx, count, nullptr, nullptr, nullptr, y, s);
   } else {
-    if (L.gated) gather_dispatch<false, true>(L, x, B, idx, count, tokmask, s);
-    else gather_dispatch<false, false>(L, x, B, idx, count, tokmask, s);
+    if (L.gated) gather_dispatch<false, true>(L, x, B, idx, count, tokmask, y, s);
+    else gather_dispatch<false, false>(L, x, B, idx, count, tokmask, y, s);
     down_launch<false, false>(L, B, idx, count, nullptr, nullptr, nullptr, y, s);
   }
   return hipGetLastError();
@@ -1377,9 +1419,9 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
   const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
   const hipEvent_t* t3 = ev ? ev + 4 : nullptr;
   if (L.p_f16)
-    stage1_launch<true>(L, x, B, s, t1);
+    stage1_launch<true>(L, x, B, s, t1, y);
   else
-    stage1_launch<false>(L, x, B, s, t1);
+    stage1_launch<false>(L, x, B, s, t1, y);
   if (L.w_f16) {
     if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s, t2);
     else mid_dispatch<true, false>(L, x, B, scores, s, t2);

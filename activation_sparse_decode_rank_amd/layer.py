@@ -72,12 +72,14 @@ class SparseFFN:
     w_down_t: [n, d] W_down transposed; p1: [r, d]; p2: [n, r]; biases fp32.
     profile_x: [N, d] fp32 profiling tokens; when given, neurons are profiled and the
     hottest ceil(hot_frac * n) packed first, and their frequencies balance the work split.
+    deterministic: keep y bitwise reproducible from run to run (slightly slower down
+    projection); otherwise the fastest split, whose y may vary in the last bits.
     """
 
     def __init__(self, *, w_act, w_down_t, p1, p2, b_act=None, b_out=None, p_bias=None,
                  w_up=None, threshold: float = 0.0, max_batch: int = 1,
                  profile_x: Optional[torch.Tensor] = None, hot_frac: float = 0.2,
-                 perm: Optional[np.ndarray] = None, stream=None):
+                 perm: Optional[np.ndarray] = None, deterministic: bool = False, stream=None):
         dev = w_act.device
         if dev.type != "cuda":
             raise ValueError("SparseFFN needs device tensors")
@@ -126,6 +128,8 @@ class SparseFFN:
         D.gated = int(self.gated)
         D.w_dtype, D.p_dtype = _DT[w_act.dtype], _DT[p1.dtype]
         D.threshold = self.threshold
+        D.deterministic = int(bool(deterministic))
+        self.deterministic = bool(deterministic)
         D.w_act, D.w_down_t = _ptr(self.w_act), _ptr(self.w_down_t)
         D.b_act, D.b_out = _ptr(self.b_act), _ptr(self.b_out)
         D.p1, D.p2, D.p_bias = _ptr(self.p1), _ptr(self.p2), _ptr(self.p_bias)

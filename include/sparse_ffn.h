@@ -95,6 +95,11 @@ typedef struct {
                                neuron (e.g. profile counts / profile tokens). Read only by
                                sparse_ffn_create, to cut the neurons into contiguous ranges
                                of about equal expected work. NULL = every neuron equal. */
+  int32_t deterministic;    /* 1: y is bitwise reproducible from run to run (the down
+                               projection splits the active rows at most two ways);
+                               0: fastest (its row splits add into y with float atomics,
+                               so the last bits of y can vary between runs). Index lists,
+                               counts and token bits are bit-exact either way. */
 } sffn_desc;
 
 /* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The

@@ -56,9 +56,9 @@ def test_desc_layout_matches_header(N):
 #include <stdio.h>
 #include "sparse_ffn.h"
 int main(void){
- printf("%zu %zu %zu %zu %zu %zu\n", sizeof(sffn_desc), offsetof(sffn_desc, threshold),
+ printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(sffn_desc), offsetof(sffn_desc, threshold),
   offsetof(sffn_desc, w_act), offsetof(sffn_desc, workspace), offsetof(sffn_desc, workspace_bytes),
-  offsetof(sffn_desc, neuron_freq));
+  offsetof(sffn_desc, neuron_freq), offsetof(sffn_desc, deterministic));
  return 0; }
 '''
     exe = os.path.join(ROOT, "_build", "desc_layout")
@@ -69,7 +69,7 @@ int main(void){
     got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     D = N.SffnDesc
     assert got == [C.sizeof(D), D.threshold.offset, D.w_act.offset, D.workspace.offset,
-                   D.workspace_bytes.offset, D.neuron_freq.offset]
+                   D.workspace_bytes.offset, D.neuron_freq.offset, D.deterministic.offset]
 
 
 def _valid_desc(N, **over):
