@@ -136,6 +136,8 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.n_cus = cus;
     L.g_gather = std::max(1, 2 * cus);
     L.ks_down = sffn::down_split(L, desc->deterministic != 0);
+    L.ks_tile = sffn::tile_split(L, desc->deterministic != 0);
+    L.g_up = std::max(1, std::min((desc->d_ffn + 15) / 16, 4 * cus));
 
     // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
     // of the active ones; as many ranges as can be resident at once, at most G_MID_MAX

@@ -37,6 +37,9 @@ struct LayerDev {
   int n_cus;     // compute units on the device
   int ks_down;   // row splits of the down projection (1 = plain stores; 2 keeps y bitwise
                  // reproducible; more adds float atomics in a varying order)
+  int ks_tile;   // the same for the batch (matrix-core) down projection
+  int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64)
+  int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
 };
 
 constexpr int G_MID_MAX = 1024;    // most workgroups the fused middle kernel may use
@@ -48,6 +51,7 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch);
 // 128-byte column blocks of the down projection, and the row split it should use
 int down_blocks(const LayerDev& L);
 int down_split(const LayerDev& L, bool deterministic);
+int tile_split(const LayerDev& L, bool deterministic);
 // whether kernels exist for this shape (fused = the single-call decode path)
 bool shape_supported(const LayerDev& L, bool fused);
 // middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch

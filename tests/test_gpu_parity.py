@@ -116,6 +116,12 @@ SHAPES = [
     ("C3", 512, 1100, 64, 4),
     ("C5", 1024, 2100, 256, 1),
     ("C2", 4096, 1500, 256, 2),
+    # batches of 16 and more take the matrix-core tile path (fp16, d a multiple of 128)
+    ("C3", 512, 1100, 64, 16),
+    ("C2", 1024, 3000, 128, 32),
+    ("C3", 256, 777, 64, 20),       # ragged token tile
+    ("C2", 512, 2000, 64, 64),
+    ("C3", 520, 900, 64, 16),       # d not a multiple of 128: the vector path at batch 16
 ]
 
 
@@ -265,13 +271,14 @@ def test_all_active_and_true_sign_equal_dense(gated):
 
 
 @pytest.mark.parametrize("gated", [False, True])
-@pytest.mark.parametrize("B", [1, 5])
-def test_integer_fixture_bit_exact(gated, B):
-    """Integer weights and tokens: every partial sum is exact in fp32, so the HIP path must
-    reproduce the oracle bit for bit, scores, list and output."""
+@pytest.mark.parametrize("B,d", [(1, 64), (5, 64), (16, 128), (24, 128)])
+def test_integer_fixture_bit_exact(gated, B, d):
+    """Integer weights and tokens: every partial sum is exact in fp32 (and each activation
+    is exactly hi + lo in fp16), so the HIP path must reproduce the oracle bit for bit,
+    scores, list and output, on the vector path and on the matrix-core tile path."""
     from activation_sparse_decode_rank_amd import SparseFFN
     from synth import integer_layer
-    d, n, r = 64, 1000, 16
+    n, r = 1000, 16
     say(f"integer fixture gated={gated} B={B}")
     lo, hi = (-1, 1) if gated else (-2, 2)
     L = integer_layer(d, n, r, gated=gated, seed=77 + B, B=B, lo=lo, hi=hi)
@@ -372,3 +379,38 @@ def test_full_size_layer_decode(name, layer):
     errs = rel_err_rows(to_np(y), Y)
     say(f"  count={k} ({k / c.n:.3f}) band={nband} err={max(errs):.2e}")
     assert max(errs) <= REL_TOL
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_full_size_batch_decode(B):
+    """The batch sweep's shape (Llama-7B-shaped gated layer, d=4096, d_ffn=11008) at 16 and
+    32 tokens with independent per-token masks: the matrix-core tile path, checked per token
+    against the oracle under the GPU's own (band-checked) masks."""
+    c = cfg("C4")
+    say(f"full size batch {B}")
+    s, L, Lt = build(c, 0, max_batch=B, profile_tokens=1024)
+    del Lt
+    X = tokens(c, B, c.d)
+    Xh = to_np(X)
+    y, idx, count, tok = s.decode(X)
+    torch.cuda.synchronize()
+    k = int(count.item())
+    S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
+    Mg = gpu_mask_orig(s.perm, to_np(idx), k, to_np(tok), B, c.n)
+    M, nband = check_mask(Mg, S)
+    ri, rk, rt = oracle.compact(M)
+    Y = oracle.forward(Xh, L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    errs = rel_err_rows(to_np(y), Y)
+    say(f"  union={k} ({k / c.n:.3f}) band={nband} err={max(errs):.2e}")
+    assert max(errs) <= REL_TOL
+
+
+def test_batch_tiles_deterministic():
+    """deterministic=1 on the tile path: bitwise-identical outputs across runs."""
+    c = cfg("C3")
+    say("tile path determinism")
+    s, _, _ = build(c, 0, d=512, n=1100, rank=64, max_batch=32, deterministic=True)
+    X = tokens(c, 32, 512)
+    outs = [to_np(s.decode(X)[0]).copy() for _ in range(3)]
+    for y in outs[1:]:
+        assert np.array_equal(y, outs[0])
