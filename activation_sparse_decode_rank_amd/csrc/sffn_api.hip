@@ -82,6 +82,38 @@ std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_byt
   return {};
 }
 
+// Cut the ranges into ks contiguous splits of about equal expected active neurons (the
+// sum of the neurons' frequencies; every neuron counts 1 without frequencies), for the
+// decode down projection. upt = ranges per thread the largest split needs (256 threads).
+void split_ranges(const std::vector<int32_t>& rs, const float* freq, int ks, sffn::SplitArg& sa,
+                  int& upt) {
+  const int g = (int)rs.size() - 1;
+  std::vector<double> cum(g + 1, 0.0);
+  for (int u = 0; u < g; ++u) {
+    double e = 0.0;
+    for (int i = rs[u]; i < rs[u + 1]; ++i) {
+      double f = freq ? (double)freq[i] : 1.0;
+      if (!(f >= 0.0)) f = 0.0;
+      if (f > 1.0) f = 1.0;
+      e += f;
+    }
+    cum[u + 1] = cum[u] + e;
+  }
+  sa = sffn::SplitArg{};
+  sa.s[0] = 0;
+  int u = 0;
+  for (int k = 1; k < ks; ++k) {
+    const double goal = cum[g] * k / ks;
+    while (u < g && cum[u] < goal) ++u;
+    sa.s[k] = u;
+  }
+  sa.s[ks] = g;
+  int widest = 0;
+  for (int k = 0; k < ks; ++k) widest = std::max(widest, sa.s[k + 1] - sa.s[k]);
+  upt = 1;
+  while (upt * 256 < widest && upt < 16) upt *= 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,7 +178,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     const double act_row = wb * desc->d * (desc->gated ? 2.0 : 1.0);
     int target = sffn::mid_resident_groups(L, desc->max_batch);
     if (target <= 0) target = 2 * cus;
-    target = std::min(target, sffn::G_MID_MAX);
+    // beyond ~4 per CU the per-range overheads dominate; up to RS_ARG_MAX ranges travel in
+    // the kernel arguments
+    target = std::min(target, sffn::RS_ARG_MAX);
     const int min_groups = (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX;
     if (target < min_groups) target = min_groups;
     std::vector<int32_t> rs = balanced_ranges(desc->d_ffn, desc->neuron_freq, pb * desc->rank,
@@ -156,6 +190,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
       if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
           hipSuccess)
         return SFFN_ERR_HIP;
+      L.rs_in_arg = L.g_mid <= sffn::RS_ARG_MAX;
+      if (L.rs_in_arg) std::copy(rs.begin(), rs.end(), L.ra.r);
+      split_ranges(rs, desc->neuron_freq, L.ks_down, L.sa, L.split_upt);
     }
     sparse_ffn_s* h = new (std::nothrow) sparse_ffn_s;
     if (!h) return SFFN_ERR_HIP;

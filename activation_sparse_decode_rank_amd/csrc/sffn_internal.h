@@ -7,6 +7,23 @@
 
 namespace sffn {
 
+constexpr int G_MID_MAX = 2048;   // most workgroups the fused middle kernel may use
+constexpr int MID_RANGE_MAX = 64;  // most neurons one middle workgroup may own (one 64-bit
+                                   // activity word per range)
+// Neuron ranges of the middle kernel passed by value in the kernel arguments, so that a
+// workgroup's first weight loads do not wait on a table load (the table and the other
+// arguments fit the 4 KB argument block).
+constexpr int RS_ARG_MAX = 952;
+struct RangeArg {
+  int32_t r[RS_ARG_MAX + 1];
+};
+// Row splits of the decode down projection: split k covers middle-kernel ranges
+// [s[k], s[k+1]), cut so that the splits expect about equal numbers of active neurons.
+constexpr int KS_MAX = 16;
+struct SplitArg {
+  int32_t s[KS_MAX + 1];
+};
+
 // Device-side view of one layer plus the workspace carve-up.
 struct LayerDev {
   int d, n, r;
@@ -22,14 +39,12 @@ struct LayerDev {
   const float* p_bias;
   // workspace regions
   float* q;            // [max_batch][r] predictor stage-1 output
-  float* h_buf;        // [n][B] activations: by list position (forward) or slot (decode)
-  uint64_t* tok_full;  // [n] token bits by neuron (compaction)
-  uint64_t* tok_g;     // [n] token bits by slot (decode)
-  int32_t* list_g;     // [n] neuron id by slot (decode)
+  float* h_buf;        // [n][B] activations: by list position (forward) or neuron (decode)
+  uint64_t* tok_full;  // [n] token bits by neuron (compaction, decode)
   int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
-  int32_t* cnt_g;      // [g_mid] active count per middle workgroup
   int32_t* tile_cnt;   // [n_tiles] compaction tile counts
   uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
+  uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
   // launch geometry fixed at create time
   int g_mid;     // workgroups of the fused middle kernel (<= G_MID_MAX)
   int n_tiles;   // compaction tiles of 256 neurons
@@ -40,10 +55,11 @@ struct LayerDev {
   int ks_tile;   // the same for the batch (matrix-core) down projection
   int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64)
   int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
+  bool rs_in_arg;  // the range table travels in the middle kernel's arguments (ra)
+  RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)
+  SplitArg sa;     // decode down projection: range splits, ks_down of them
+  int split_upt;   // most ranges of one split per thread of the down kernel (1, 2, 4, 8)
 };
-
-constexpr int G_MID_MAX = 1024;    // most workgroups the fused middle kernel may use
-constexpr int MID_RANGE_MAX = 256;  // most neurons one middle workgroup may own
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
 size_t workspace_bytes(int d, int n, int r, int max_batch);

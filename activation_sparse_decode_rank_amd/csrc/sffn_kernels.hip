@@ -15,8 +15,11 @@
 //    section 工程影響).
 // How it is computed here is specific to this chip: kernel boundaries are the only
 // grid-wide synchronization (they cost about a microsecond and a half inside a HIP graph,
-// far less than any in-kernel grid barrier on this part), no atomics are used at all, and
-// every reduction has a fixed order, so results are bit-reproducible.
+// far less than any in-kernel grid barrier on this part). Global atomics are few: the
+// middle kernel ORs each wave's active bits into a union bitmask (at most two 64-bit ORs
+// per wave, order-independent), and the down projection may add up to KS split-k sums
+// per output element (bitwise reproducible for KS <= 2). Every other reduction has a
+// fixed order.
 #include "sffn_internal.h"
 
 #include <hip/hip_ext.h>
@@ -28,8 +31,6 @@ namespace {
 
 constexpr int TPB = 256;        // threads per workgroup for every kernel here
 constexpr int MAXB = 64;        // tokens per call (one bit each in a 64-bit word)
-constexpr int LOADS = 16;       // 16-byte loads a thread keeps in flight in the row loops
-constexpr int LIST_CAP = 8192;  // active-list window held in LDS by the down kernel
 constexpr int X_LDS_MAX = 48 * 1024;  // tokens are staged in LDS when they fit in this
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -44,6 +45,12 @@ struct Elt {
 
 __device__ __forceinline__ u32x4 ld_chunk(const void* base, size_t chunk) {
   return reinterpret_cast<const u32x4*>(base)[chunk];
+}
+// Weight rows read once per step: non-temporal, so that streaming them does not evict
+// what the step reuses from the caches (kernel code, the token, predictor outputs,
+// activations, and rows the previous kernel prefetched).
+__device__ __forceinline__ u32x4 ld_stream(const void* base, size_t chunk) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + chunk);
 }
 
 template <bool F16>
@@ -143,7 +150,6 @@ __host__ __device__ constexpr int group_leader(int L) { return L <= 16 ? 0 : L -
 __device__ __forceinline__ void zero_grid(float* __restrict__ y, int ny) {
   for (int i = blockIdx.x * TPB + threadIdx.x; i < ny; i += gridDim.x * TPB) y[i] = 0.f;
 }
-
 // Cooperative copy of x [B][d] fp32 into LDS.
 __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats) {
   const float4_t* src = reinterpret_cast<const float4_t*>(x);
@@ -152,32 +158,64 @@ __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats
 }
 
 // ============================================================================ predictor
-// Stage 1: q[b][j] = P1[j] . x_b. One workgroup per predictor row; each thread holds up
-// to MAXC chunks of the row in registers and reuses them for every token group of TBG.
-template <bool PF16, int TBG>
+// Stage 1: q[b][j] = P1[j] . x_b. Workgroup j < r owns predictor row j; each thread holds
+// NCPT chunks of the row in registers and reuses them for every token group of TBG. In the
+// decode step these workgroups also clear y (ny floats), which the down projection later
+// adds its split-k sums into.
+// Workgroups r .. r + g_pf - 1 only prefetch: workgroup r + w reads middle-kernel range w's
+// rows of the predictor's second-stage matrix p2 (NCHP chunks per row) and its two bias
+// entries per neuron, so that the middle kernel's first loads hit cache instead of HBM.
+// Those addresses are static, so their latency overlaps this kernel's own. Workgroups are
+// dealt to the XCDs round-robin by id, and r is a multiple of 8, so workgroup r + w shares
+// an XCD (and its L2) with middle workgroup w. Every prefetch load is issued before any
+// wait; the values are folded into a register that an empty asm consumes, so the loads
+// stay and nothing is stored.
+constexpr int PF_PER_THREAD = 8;
+template <bool PF16, int TBG, int NCPT>
 __global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
                                                      const float* __restrict__ x, int d, int r,
                                                      int B, float* __restrict__ q,
-                                                     float* __restrict__ y0, int ny) {
+                                                     float* __restrict__ y0, int ny,
+                                                     const void* __restrict__ p2, int nchp,
+                                                     const RangeArg ra,
+                                                     const float* __restrict__ pfb0,
+                                                     const float* __restrict__ pfb1) {
   constexpr int EPC = Elt<PF16>::EPC;
-  constexpr int MAXC = 8;
-  zero_grid(y0, ny);
   const int j = blockIdx.x, tid = threadIdx.x;
+  if (j >= r) {
+    const int w = j - r;
+    const int r0 = ra.r[w], r1 = ra.r[w + 1];
+    const int c0 = r0 * nchp, nc = (r1 - r0) * nchp;
+    u32x4 pv[PF_PER_THREAD];
+#pragma unroll
+    for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = ld_chunk(p2, c0 + min(tid + v * TPB, nc - 1));
+    float b0 = 0.f, b1 = 0.f;
+    if (tid < r1 - r0) {
+      if (pfb0) b0 = pfb0[r0 + tid];
+      if (pfb1) b1 = pfb1[r0 + tid];
+    }
+    unsigned sink = __float_as_uint(b0) ^ __float_as_uint(b1);
+#pragma unroll
+    for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v].x;
+    asm volatile("" ::"v"(sink));
+    return;
+  }
+  for (int i = j * TPB + tid; i < ny; i += r * TPB) y0[i] = 0.f;
   const int nch = d / EPC;
   const size_t row0 = (size_t)j * nch;
   __shared__ float red[TPB / 64][MAXB];
-  u32x4 wv[MAXC];
+  u32x4 wv[NCPT];
 #pragma unroll
-  for (int m = 0; m < MAXC; ++m) {
+  for (int m = 0; m < NCPT; ++m) {
     const int c = tid + m * TPB;
-    if (c < nch) wv[m] = ld_chunk(p1, row0 + c);
+    if (c < nch) wv[m] = ld_stream(p1, row0 + c);
   }
   for (int b0 = 0; b0 < B; b0 += TBG) {
     float acc[TBG];
 #pragma unroll
     for (int b = 0; b < TBG; ++b) acc[b] = 0.f;
 #pragma unroll
-    for (int m = 0; m < MAXC; ++m) {
+    for (int m = 0; m < NCPT; ++m) {
       const int c = tid + m * TPB;
       if (c < nch) {
         float f[EPC];
@@ -479,15 +517,17 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
 // t+256, ...); with NCHP = chunks per P2 row a power of two, a row's chunks sit in NCHP
 // consecutive lanes (above 64, in consecutive waves). Every load that does not depend on
 // the scores (P2 block, q, biases, x) is issued before the first wait.
-// Outputs, for its k-th active neuron i (k ascending with i), at slot rs[w] + k:
-// list_g = i, tok_g = token bits, h_g[slot*B + b] = activation. cnt_g[w] = active count.
-// scores is written when non-null.
+// Outputs: wbits[w], the range's activity word (bit j = neuron rs[w] + j is active for at
+// least one token; ranges hold at most 64 neurons), written every call with a plain store;
+// and for each active neuron i its token bits tok_full[i] and activations h_g[i*B + b] (0
+// for tokens whose bit is clear). Other neurons' entries are not written. scores is
+// written when non-null.
 template <bool F16, bool GATED, int CPT, int TBG>
 __global__ __launch_bounds__(TPB) void k_fused_mid(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
     int r, const void* __restrict__ w_act, const float* __restrict__ b_act,
     const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
-    int32_t* __restrict__ cnt_g, int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_g,
+    const RangeArg ra, uint64_t* __restrict__ wbits, uint64_t* __restrict__ tok_full,
     float* __restrict__ h_g, float* __restrict__ scores, int x_lds) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int PL = 16;  // P2 chunks a thread keeps in flight
@@ -507,7 +547,7 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
   __shared__ float s_red[G::RED_FLOATS];
 
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = rs[w], r1 = rs[w + 1];
+  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
   const int nown = r1 - r0;  // 1..RMAX
   const int nchp = r / EPC;  // power of two, <= 128
   const int lg = 31 - __clz(nchp);
@@ -531,7 +571,7 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
     pb = pbias ? pbias[r0 + tid] : 0.f;
     ba = b_act ? b_act[r0 + tid] : 0.f;
   }
-  s_tok[tid] = 0;
+  if (tid < RMAX) s_tok[tid] = 0;
   if (x_lds) stage_x(s_x, x, B * d);
   if (tid < nown) {
     s_pb[tid] = pb;
@@ -626,27 +666,29 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
     s_rows[k] = i;
     s_bits[k] = bits;
     s_bias[k] = s_ba[tid];
-    s_pos[k] = r0 + k;
-    list_g[r0 + k] = i;
-    tok_g[r0 + k] = bits;
+    s_pos[k] = i;
   }
-  if (tid == 0) cnt_g[w] = nact;
   __syncthreads();
   // ---- gather + ReLU over the owned active rows
   G::run(w_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_bias, s_pos, nact, h_g, s_red);
+  // token bits and the range's activity word (the range fits in wave 0's 64 lanes) are
+  // stored last: the wait that follows a store and a barrier would hold back the gather
+  if (tid < nact) tok_full[s_rows[tid]] = s_bits[tid];
+  if (tid == 0) wbits[w] = word;
 }
 
 // ---------------------------------------------------------------------------- B = 1
 // The single-token form of the middle kernel, specialized on NCHP (chunks per predictor
 // row) so that the lane-group reductions are straight-line DPP code. Addresses of unused
-// slots are clamped into the owned block instead of branching per lane.
+// slots are clamped into the owned block instead of branching per lane. Outputs as in
+// k_fused_mid with B = 1: the range's activity word and h_g[i] for every active neuron i
+// (no token bits: with one token every listed neuron is active for it).
 template <bool F16, bool GATED, int CPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_mid_b1(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
     const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int n, float tau, const int32_t* __restrict__ rs, int32_t* __restrict__ cnt_g,
-    int32_t* __restrict__ list_g, uint64_t* __restrict__ tok_g, float* __restrict__ h_g,
-    float* __restrict__ scores, int x_lds) {
+    int d, int n, float tau, const int32_t* __restrict__ rs, const RangeArg ra,
+    uint64_t* __restrict__ wbits, float* __restrict__ h_g, float* __restrict__ scores) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int GRP = NCHP < 64 ? NCHP : 64;   // lanes holding one predictor row in a wave
   constexpr int WPR = NCHP > 64 ? NCHP / 64 : 1;  // waves per predictor row
@@ -656,8 +698,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
   constexpr int RB = (16 / CPT) > 0 ? (16 / CPT) : 1;  // gathered rows in flight
   constexpr int NV = GATED ? 2 : 1;
   static_assert(NCHP >= 1 && NCHP <= 128 && (NCHP & (NCHP - 1)) == 0, "NCHP");
-  extern __shared__ float4_t s_dyn4[];
-  float* s_x = reinterpret_cast<float*>(s_dyn4);
+  
   __shared__ uint8_t s_act[RMAX];
   __shared__ int32_t s_rows[RMAX];
   __shared__ float s_bias[RMAX];
@@ -668,15 +709,18 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
   __shared__ float s_red[4 * RB * NV];
 
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = rs[w], r1 = rs[w + 1];
+  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
   const int nown = r1 - r0;  // 1..RMAX
   const int pos = tid & (NCHP - 1);
   const int rsub = tid / NCHP;
   const int nslots = (nown + RPP - 1) / RPP;
   const size_t blk0 = (size_t)r0 * NCHP;
 
-  // ---- every score-independent load first: P2 (first PL slots), q, biases, x
+  // ---- every score-independent load first: P2 (first PL slots), q, biases, x. Slots
+  // beyond the range (m >= mlim, uniform) re-read its last row and are not computed.
+  // (Guarding these loads instead makes the compiler keep far more registers live.)
   u32x4 wv[PL];
+  int mlim = min(PL, nslots);
 #pragma unroll
   for (int m = 0; m < PL; ++m) {
     const int j = min(m * RPP + rsub, nown - 1);
@@ -689,8 +733,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
     pb = pbias ? pbias[r0 + tid] : 0.f;
     ba = b_act ? b_act[r0 + tid] : 0.f;
   }
-  s_act[tid] = 0;
-  if (x_lds) stage_x(s_x, x, d);
+  if (tid < RMAX) s_act[tid] = 0;
   if (tid < nown) {
     s_pb[tid] = pb;
     s_ba[tid] = ba;
@@ -700,6 +743,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
   // ---- predictor stage 2 and threshold
   for (int s0 = 0; s0 < nslots; s0 += PL) {
     if (s0 > 0) {
+      mlim = min(PL, nslots - s0);
 #pragma unroll
       for (int m = 0; m < PL; ++m) {
         const int j = min((s0 + m) * RPP + rsub, nown - 1);
@@ -708,9 +752,10 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
     }
     float acc[PL];
 #pragma unroll
-    for (int m = 0; m < PL; ++m) acc[m] = dot_chunk<F16>(wv[m], qs, 0.f);
+    for (int m = 0; m < PL; ++m) acc[m] = m < mlim ? dot_chunk<F16>(wv[m], qs, 0.f) : 0.f;
 #pragma unroll
-    for (int m = 0; m < PL; ++m) acc[m] = group_sum<GRP>(acc[m]);
+    for (int m = 0; m < PL; ++m)
+      if (m < mlim) acc[m] = group_sum<GRP>(acc[m]);
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
       const int j = (s0 + m) * RPP + rsub;
@@ -753,16 +798,22 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
     const int k = before + __popcll(lower);
     s_rows[k] = r0 + tid;
     s_bias[k] = s_ba[tid];
-    list_g[r0 + k] = r0 + tid;
-    tok_g[r0 + k] = 1;
   }
-  if (tid == 0) cnt_g[w] = nact;
   __syncthreads();
 
-  // ---- gather-GEMV + ReLU over the active rows, RB rows in flight
-  const float* xsrc = x_lds ? s_x : x;
+  // ---- gather-GEMV + ReLU over the active rows, RB rows in flight. The input chunks this
+  // thread multiplies are loaded into registers once, with the first rows' loads.
   const int nch = d / EPC;
   const int rowch = GATED ? 2 * nch : nch;
+  float xs[CPT][EPC];
+  if (nact > 0) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * TPB;
+      const bool up = GATED && c >= nch;
+      load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
+    }
+  }
   for (int base = 0; base < nact; base += RB) {
     const int nb = min(RB, nact - base);  // uniform
     u32x4 gv[RB][CPT];
@@ -771,9 +822,10 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
       if (rr < nb) {
         const size_t row0 = (size_t)s_rows[base + rr] * rowch;
 #pragma unroll
-        for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_chunk(w_act, row0 + min(tid + m * TPB, rowch - 1));
+        for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_stream(w_act, row0 + min(tid + m * TPB, rowch - 1));
       }
     }
+
     float acc[RB][NV];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr)
@@ -784,13 +836,10 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
       const int c = tid + m * TPB;
       const bool cv = c < rowch;
       const bool up = GATED && c >= nch;
-      const int xc = min(up ? c - nch : c, nch - 1);
-      float xs[EPC];
-      load_x<EPC>(xsrc + (size_t)xc * EPC, xs);
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
         if (rr < nb) {
-          const float dv = dot_chunk<F16>(gv[rr][m], xs, 0.f);
+          const float dv = dot_chunk<F16>(gv[rr][m], xs[m], 0.f);
           const float add = cv ? dv : 0.f;
           if (GATED && up) acc[rr][NV - 1] += add;
           else acc[rr][0] += add;
@@ -825,18 +874,20 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
         u += s_red[(3 * RB + rr) * NV + 1];
         h = h * u;
       }
-      h_g[r0 + base + rr] = h;
+      h_g[s_rows[base + rr]] = h;
     }
     __syncthreads();
   }
+  // The range's activity word (the range fits in wave 0's 64 lanes) is stored last: the
+  // wait that follows a store and a barrier would hold back the gather's loads.
+  if (tid == 0) wbits[w] = word;
 }
 
 // ============================================================================ down
 // Down projection y_b = sum_k h_{k,b} W_down^T[idx_k] + b_out, split two ways:
 //  - columns: workgroup (cb, kq) owns the 128-byte column block cb (8 chunks = 8*EPC output
 //    columns), so every weight read is a whole 128-byte line of a row;
-//  - rows (split-k): it owns list positions [kq*per, min(total, (kq+1)*per)),
-//    per = ceil(total / KS).
+//  - rows (split-k): it owns split kq of the active rows.
 // Inside the workgroup, thread t handles chunk t&7 of the block and row slot t>>3 (32
 // slots); per batch the row ids and activations are loaded first, then LOADS_D weight
 // chunks per thread, then the FMAs. The 32 slots are reduced in a fixed order (DPP within
@@ -844,14 +895,19 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
 // which an earlier kernel of the same call has zeroed: a plain store when KS == 1, else a
 // float atomic add, b_out riding on kq == 0's sum. With KS == 2 the result is still
 // bitwise reproducible (two addends onto +0 commute exactly); KS > 2 trades that for
-// speed. The KS workgroups of one block are dealt to the same XCD (block ids cb + kq*ncb
-// with ncb a multiple of 8; workgroups go to the 8 XCDs round-robin), so their atomics
-// meet in one L2.
-// FROM_WG: the list is the middle kernel's: range u's active neurons sit at slots
-// rs[u] .. rs[u] + cnt_g[u]; concatenated in u order they are ascending. This kernel then
-// also writes idx, count and tokmask (if non-null) for that list, each workgroup of split
-// kq a share of kq's positions. Otherwise the list is idx_in[0..*count) and activations
-// are indexed by list position.
+// speed.
+// BITS (decode): the active rows come from the middle kernel's per-range activity words
+// (bit j of wbits[u] = neuron rs[u] + j; ranges ascending and contiguous) and activations
+// are indexed by neuron, h_in[i*B + b]. Split kq owns the ranges [sa.s[kq], sa.s[kq+1])
+// (cut offline for equal expected activity). In one round of loads each thread reads its
+// UPT ranges' words and starts and the words of every earlier range (their popcount is
+// the split's first list position); a workgroup-local scan then places the split's set
+// bits into an LDS list, so each thread expands only its own few bits. The kernel also
+// writes idx, count and tokmask (if non-null) for the whole list, each workgroup a share
+// of its split's positions, after its sums (a store followed by a barrier would stall).
+// Otherwise (list mode) the list is idx_in[0..*count), split by position, with
+// activations indexed by list position, h_in[k*B + b].
+constexpr int LIST_CAP = 8192;            // split-list window held in LDS (BITS)
 constexpr int CB_LANES = 8;               // 16-byte chunks per column block (128 bytes)
 constexpr int RSD = TPB / CB_LANES;       // row slots per workgroup
 template <int TB>
@@ -859,21 +915,23 @@ struct DownCfg {
   static constexpr int LOADS_D = TB == 1 ? 16 : 8;  // weight rows a thread keeps in flight
 };
 
-template <bool WF16, bool FROM_WG, int TB>
+template <bool WF16, bool BITS, int TB, int UPT>
 __global__ __launch_bounds__(TPB) void k_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, int B, const int32_t* __restrict__ idx_in,
-    const int32_t* __restrict__ count_in, const int32_t* __restrict__ cnt_g,
-    const int32_t* __restrict__ rs, const int32_t* __restrict__ list_g,
-    const uint64_t* __restrict__ tok_g, int g_mid, int KS, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
+    const int32_t* __restrict__ count_in, const uint64_t* __restrict__ wbits,
+    const int32_t* __restrict__ rs, const SplitArg sa, const uint64_t* __restrict__ tok_full,
+    int KS, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
+    uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int COLS = CB_LANES * EPC;
   constexpr int LD = DownCfg<TB>::LOADS_D;
-  constexpr int UPT = G_MID_MAX / TPB;  // middle ranges per thread in the scan
+  constexpr int PFX = G_MID_MAX / TPB;  // earlier-range words per thread
+  static_assert(UPT >= 1 && UPT * TPB <= G_MID_MAX, "UPT");
   extern __shared__ float4_t s_dyn4[];
-  int32_t* s_slot = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
+  int32_t* s_list = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries (BITS)
   __shared__ int s_wsum[TPB / 64];
+  __shared__ int s_psum[TPB / 64];
   __shared__ float s_red[TPB / 64][4][CB_LANES][TB * EPC];  // [wave][16-lane row][chunk][value]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -883,38 +941,48 @@ __global__ __launch_bounds__(TPB) void k_down(
   const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
   const int chunk = min(cb * CB_LANES + li, nch - 1);  // a partial last block re-reads; unused
 
-  int total;
-  int cu[UPT], ru[UPT], offu[UPT];
-  if (FROM_WG) {
-    int tsum = 0;
+  // p0..p1: this workgroup's positions (BITS: local to the split); gbase: global position
+  // of local position 0
+  int p0, p1, gbase = 0;
+  uint64_t wd[UPT];
+  int rb[UPT];
+  int woff = 0;  // BITS: local position of this thread's first set bit
+  if (BITS) {
+    const int u0 = sa.s[kq], u1 = sa.s[kq + 1];
+    int c = 0;
 #pragma unroll
     for (int v = 0; v < UPT; ++v) {
-      const int u = tid * UPT + v;
-      cu[v] = u < g_mid ? cnt_g[u] : 0;
-      ru[v] = u < g_mid ? rs[u] : 0;
-      tsum += cu[v];
+      const int u = u0 + tid * UPT + v;
+      wd[v] = u < u1 ? wbits[u] : 0;
+      rb[v] = u < u1 ? rs[u] : 0;
+      c += __popcll(wd[v]);
     }
-    const int incl = wave_incl_scan(tsum);
-    if (lane == 63) s_wsum[wave] = incl;
+    int pc = 0;
+#pragma unroll
+    for (int v = 0; v < PFX; ++v) {
+      const int u = tid + v * TPB;
+      if (u < u0) pc += __popcll(wbits[u]);
+    }
+    const int incl = wave_incl_scan(c);
+    const int pincl = wave_incl_scan(pc);
+    if (lane == 63) {
+      s_wsum[wave] = incl;
+      s_psum[wave] = pincl;
+    }
     __syncthreads();
-    int woff = 0;
-    for (int v = 0; v < wave; ++v) woff += s_wsum[v];
-    total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    int run = woff + incl - tsum;
+    int before = 0;
 #pragma unroll
-    for (int v = 0; v < UPT; ++v) {
-      offu[v] = run;
-      run += cu[v];
-    }
-    if (blockIdx.x == 0 && tid == 0 && count_out) *count_out = total;
+    for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wsum[v] : 0;
+    p0 = 0;
+    p1 = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    gbase = s_psum[0] + s_psum[1] + s_psum[2] + s_psum[3];
+    woff = before + incl - c;
   } else {
-    total = min(max(*count_in, 0), n);  // a count beyond the list is clamped
+    const int total = min(max(*count_in, 0), n);  // a count beyond the list is clamped
+    const int per = (total + KS - 1) / KS;
+    p0 = min(total, kq * per);
+    p1 = min(total, p0 + per);
   }
-  const int per = (total + KS - 1) / KS;
-  const int p0 = min(total, kq * per), p1 = min(total, p0 + per);
-  // this workgroup's share of split kq's positions for publishing the list
-  const int pubq = (p1 - p0 + ncb - 1) / ncb;
-  const int pub0 = p0 + cb * pubq, pub1 = min(p1, pub0 + pubq);
 
   float acc[TB][EPC];
   const int ntg = (B + TB - 1) / TB;
@@ -926,54 +994,59 @@ __global__ __launch_bounds__(TPB) void k_down(
       for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
     for (int wb = p0; wb < p1; wb += LIST_CAP) {
       const int wl = min(LIST_CAP, p1 - wb);
-      if (FROM_WG) {
+      // BITS: expand the split's set bits at local positions [wb, wb + wl) into s_list
+      // (once, when the whole split fits one window)
+      if (BITS && (tg == 0 || p1 - p0 > LIST_CAP)) {
         __syncthreads();
+        int pos = woff;
 #pragma unroll
         for (int v = 0; v < UPT; ++v) {
-          const int lo = max(offu[v], wb), hi = min(offu[v] + cu[v], wb + wl);
-          for (int k = lo; k < hi; ++k) s_slot[k - wb] = ru[v] + (k - offu[v]);
+          uint64_t m = wd[v];
+          const int c = __popcll(m);
+          if (pos < wb + wl && pos + c > wb) {
+            while (m) {
+              const int bit = __ffsll((unsigned long long)m) - 1;
+              m &= m - 1;
+              if (pos >= wb && pos < wb + wl) s_list[pos - wb] = rb[v] + bit;
+              ++pos;
+            }
+          } else {
+            pos += c;
+          }
         }
         __syncthreads();
+        // a list longer than one window is published window by window, here
+        if (p1 - p0 > LIST_CAP && tg == 0 && idx_out) {
+          for (int k = tid; k < wl; k += TPB) {
+            if (k % ncb != cb) continue;
+            const int i = s_list[k];
+            idx_out[gbase + wb + k] = i;
+            if (tokmask_out) tokmask_out[gbase + wb + k] = B == 1 ? (uint64_t)1 : tok_full[i];
+          }
+        }
       }
       // Per batch: every row id and activation load first, then every weight load, then
-      // stores, then the FMAs. Slots past the end re-read the last position and add 0.
+      // the FMAs. Slots past the end re-read the last position and add 0.
       for (int kb0 = 0; kb0 < wl; kb0 += RSD * LD) {
-        int hp[LD];
+        int ii[LD];
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
           const int kc = min(kb0 + u * RSD + rsl, wl - 1);
-          hp[u] = FROM_WG ? s_slot[kc] : wb + kc;
+          ii[u] = BITS ? s_list[kc] : idx_in[wb + kc];
         }
-        int ii[LD];
         float hv[LD][TB];
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
-          ii[u] = FROM_WG ? list_g[hp[u]] : idx_in[hp[u]];
+          const int kc = min(kb0 + u * RSD + rsl, wl - 1);
+          const int hr = BITS ? ((ii[u] >= 0 && ii[u] < n) ? ii[u] : 0) : wb + kc;
 #pragma unroll
-          for (int b = 0; b < TB; ++b) hv[u][b] = h_in[(size_t)hp[u] * B + min(b0 + b, B - 1)];
-        }
-        const bool publish = FROM_WG && tg == 0 && idx_out;
-        uint64_t tb[LD];
-        if (TB > 1 && publish && tokmask_out) {
-#pragma unroll
-          for (int u = 0; u < LD; ++u) tb[u] = tok_g[hp[u]];
+          for (int b = 0; b < TB; ++b) hv[u][b] = h_in[(size_t)hr * B + min(b0 + b, B - 1)];
         }
         u32x4 wv[LD];
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
           const int ic = (ii[u] >= 0 && ii[u] < n) ? ii[u] : 0;  // out-of-range entries add 0
-          wv[u] = ld_chunk(w_down_t, (size_t)ic * nch + chunk);
-        }
-        if (publish && li == 0) {
-#pragma unroll
-          for (int u = 0; u < LD; ++u) {
-            const int k = kb0 + u * RSD + rsl;
-            if (k < wl && wb + k >= pub0 && wb + k < pub1) {
-              idx_out[wb + k] = ii[u];
-              // TB == 1 is launched only for one token: every listed neuron carries bit 0
-              if (tokmask_out) tokmask_out[wb + k] = TB == 1 ? (uint64_t)1 : tb[u];
-            }
-          }
+          wv[u] = ld_stream(w_down_t, (size_t)ic * nch + chunk);
         }
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
@@ -1022,6 +1095,19 @@ __global__ __launch_bounds__(TPB) void k_down(
       }
     }
     __syncthreads();
+  }
+  if (BITS) {
+    // the list of this split (held whole in s_list when it fits one window): workgroup cb
+    // publishes local positions k with k % ncb == cb; the last split's workgroup 0 knows
+    // the total
+    if (idx_out && p1 - p0 <= LIST_CAP) {
+      for (int k = cb + tid * ncb; k < p1; k += TPB * ncb) {
+        const int i = s_list[k];
+        idx_out[gbase + k] = i;
+        if (tokmask_out) tokmask_out[gbase + k] = B == 1 ? (uint64_t)1 : tok_full[i];
+      }
+    }
+    if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + p1;
   }
 }
 
@@ -1393,12 +1479,10 @@ size_t workspace_bytes(int d, int n, int r, int max_batch) {
   b += align256((size_t)max_batch * r * 4);      // q
   b += align256((size_t)((n + 63) / 64 * 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
   b += align256((size_t)n * 8);                  // tok_full
-  b += align256((size_t)n * 8);                  // tok_g
-  b += align256((size_t)n * 4);                  // list_g
   b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
-  b += align256((size_t)G_MID_MAX * 4);          // cnt_g
   b += align256((size_t)n_tiles * 4);            // tile_cnt
   b += align256((size_t)((n + 63) / 64) * 8);    // words
+  b += align256((size_t)G_MID_MAX * 8);          // wbits
   return b;
 }
 
@@ -1411,12 +1495,10 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   L.ldh = (n + 63) / 64 * 64;
   L.h_buf = reinterpret_cast<float*>(take((size_t)L.ldh * max_batch * 4));
   L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
-  L.tok_g = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
-  L.list_g = reinterpret_cast<int32_t*>(take((size_t)n * 4));
   L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
-  L.cnt_g = reinterpret_cast<int32_t*>(take((size_t)G_MID_MAX * 4));
   L.tile_cnt = reinterpret_cast<int32_t*>(take((size_t)n_tiles * 4));
   L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
+  L.wbits = reinterpret_cast<uint64_t*>(take((size_t)G_MID_MAX * 8));
   L.n_tiles = n_tiles;
 }
 
@@ -1456,15 +1538,41 @@ void launch(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const hipE
     kern<<<grid, block, lds, s>>>(a...);
 }
 
-// y0: output the down projection will add into (zeroed here when it splits rows), or null
+// y0: output of ny floats the down projection will add into (zeroed here), or null;
+// prefetch: extra workgroups pull the middle kernel's predictor rows and biases into cache
+template <bool F16, int NCPT>
+void stage1_launch_t(const LayerDev& L, const float* x, int B, hipStream_t s,
+                     const hipEvent_t* tev, float* y0, int ny, int g_pf) {
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  const dim3 grid(L.r + g_pf);
+  if (B == 1)
+    launch(k_pred_stage1<F16, 1, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
+           y0, ny, L.p2, nchp, L.ra, L.p_bias, L.b_act);
+  else
+    launch(k_pred_stage1<F16, 4, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
+           y0, ny, L.p2, nchp, L.ra, L.p_bias, L.b_act);
+}
+
+// prefetch workgroups are used when the ranges travel in the kernel arguments, a range's
+// predictor rows fit PF_PER_THREAD chunks per thread, and r keeps them on their consumer's
+// XCD
+int stage1_prefetch_groups(const LayerDev& L) {
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  if (!L.rs_in_arg || L.r % 8 != 0 || MID_RANGE_MAX * nchp > TPB * PF_PER_THREAD) return 0;
+  return L.g_mid;
+}
+
 template <bool F16>
 void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                   const hipEvent_t* tev = nullptr, float* y0 = nullptr) {
-  const int ny = (y0 && L.ks_down > 1) ? B * L.d : 0;
-  if (B == 1)
-    launch(k_pred_stage1<F16, 1>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q, y0, ny);
-  else
-    launch(k_pred_stage1<F16, 4>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q, y0, ny);
+                   const hipEvent_t* tev = nullptr, float* y0 = nullptr, int ny = 0,
+                   bool prefetch = false) {
+  if (!y0) ny = 0;
+  const int g_pf = prefetch ? stage1_prefetch_groups(L) : 0;
+  const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
+  if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny, g_pf);
+  else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny, g_pf);
+  else if (ncpt <= 4) stage1_launch_t<F16, 4>(L, x, B, s, tev, y0, ny, g_pf);
+  else stage1_launch_t<F16, 8>(L, x, B, s, tev, y0, ny, g_pf);
 }
 
 template <bool F16>
@@ -1521,30 +1629,49 @@ void gather_dispatch(const LayerDev& L, const float* x, int B, const int32_t* id
   }
 }
 
-template <bool F16, bool FROM_WG>
+template <bool F16, bool BITS, int TB, int UPT>
+void down_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                   int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
+                   hipStream_t s, const hipEvent_t* tev) {
+  const int grid = down_blocks(L) * L.ks_down;
+  const size_t lds = BITS ? (size_t)LIST_CAP * 4 : 0;
+  launch(k_down<F16, BITS, TB, UPT>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t, L.b_out,
+         L.h_buf, L.d, L.n, B, idx, count, L.wbits, L.rs, L.sa, L.tok_full, L.ks_down,
+         idx_out, count_out, tok_out, y);
+}
+
+// BITS: decode (list from the union bitmask, activations by neuron); otherwise the given
+// list idx/count with activations by list position
+template <bool F16, bool BITS>
 void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                  int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
                  hipStream_t s, const hipEvent_t* tev = nullptr) {
-  const int grid = down_blocks(L) * L.ks_down;
-  const size_t lds = FROM_WG ? (size_t)LIST_CAP * 4 : 0;
-  if (B == 1)
-    launch(k_down<F16, FROM_WG, 1>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
-                       L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
-                       L.tok_g, L.g_mid, L.ks_down, idx_out, count_out, tok_out, y);
-  else
-    launch(k_down<F16, FROM_WG, 4>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t,
-                       L.b_out, L.h_buf, L.d, L.n, B, idx, count, L.cnt_g, L.rs, L.list_g,
-                       L.tok_g, L.g_mid, L.ks_down, idx_out, count_out, tok_out, y);
+  if (!BITS) {
+    if (B == 1) down_launch_t<F16, false, 1, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev);
+    else down_launch_t<F16, false, 4, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev);
+    return;
+  }
+#define DOWN_BITS(TB)                                                                          \
+  switch (L.split_upt) {                                                                       \
+    case 1: down_launch_t<F16, true, TB, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
+    case 2: down_launch_t<F16, true, TB, 2>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
+    case 4: down_launch_t<F16, true, TB, 4>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
+    default: down_launch_t<F16, true, TB, 8>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
+  }
+  if (B == 1) {
+    DOWN_BITS(1)
+  } else {
+    DOWN_BITS(4)
+  }
+#undef DOWN_BITS
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
 void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                    const hipEvent_t* tev) {
-  const bool xl = x_in_lds(1, L.d);
-  const size_t lds = xl ? (size_t)L.d * 4 : 0;
-  launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
-                     L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs, L.cnt_g, L.list_g,
-                     L.tok_g, L.h_buf, scores, xl ? 1 : 0);
+  launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), 0, s, tev, L.p2,
+         L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs, L.ra,
+         L.wbits, L.h_buf, scores);
 }
 
 template <bool F16, bool GATED, int CPT>
@@ -1568,12 +1695,12 @@ void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hip
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
   if (B == 1)
     launch(k_fused_mid<F16, GATED, CPT, 1>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
-                       L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
-                       L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
+           L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
+           L.rs_in_arg ? nullptr : L.rs, L.ra, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0);
   else
     launch(k_fused_mid<F16, GATED, CPT, 4>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
-                       L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs, L.cnt_g,
-                       L.list_g, L.tok_g, L.h_buf, scores, xl ? 1 : 0);
+           L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
+           L.rs_in_arg ? nullptr : L.rs, L.ra, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0);
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
@@ -1588,11 +1715,11 @@ int mid_occupancy_cpt(const LayerDev& L, int B) {
   const size_t lds = x_in_lds(B, L.d) ? (size_t)B * L.d * 4 : 0;
   int a = 0, b = 0;
   switch (L.r / (F16 ? 8 : 4)) {
-    case 8: a = mid_b1_occ<F16, GATED, CPT, 8>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
-    case 16: a = mid_b1_occ<F16, GATED, CPT, 16>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
-    case 32: a = mid_b1_occ<F16, GATED, CPT, 32>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
-    case 64: a = mid_b1_occ<F16, GATED, CPT, 64>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
-    case 128: a = mid_b1_occ<F16, GATED, CPT, 128>(x_in_lds(1, L.d) ? (size_t)L.d * 4 : 0); break;
+    case 8: a = mid_b1_occ<F16, GATED, CPT, 8>(0); break;
+    case 16: a = mid_b1_occ<F16, GATED, CPT, 16>(0); break;
+    case 32: a = mid_b1_occ<F16, GATED, CPT, 32>(0); break;
+    case 64: a = mid_b1_occ<F16, GATED, CPT, 64>(0); break;
+    case 128: a = mid_b1_occ<F16, GATED, CPT, 128>(0); break;
     default:
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_fused_mid<F16, GATED, CPT, 1>, TPB, lds) != hipSuccess) a = 0;
   }
@@ -1707,6 +1834,8 @@ bool shape_supported(const LayerDev& L, bool fused) {
     if (L.w_f16 != L.p_f16) return false;
     if (nchp > 128 || (nchp & (nchp - 1)) != 0) return false;  // P2 row = power-of-two chunks
     if (L.g_mid < 1 || L.g_mid > G_MID_MAX) return false;
+    if (L.split_upt < 1 || L.split_upt > 8) return false;  // the down kernel's word registers
+    if (L.ks_down < 1 || L.ks_down > KS_MAX) return false;
   }
   return true;
 }
@@ -1753,11 +1882,11 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     // scores go to the caller's buffer or, when none is given, to the activation buffer,
     // which the up projection only overwrites after compaction has read them
     float* sc = scores ? scores : L.h_buf;
-    if (L.p_f16) {
-      stage1_launch<true>(L, x, B, s, t1, y);
-    } else {
-      stage1_launch<false>(L, x, B, s, t1, y);
-    }
+    const int ny = L.ks_tile > 1 ? B * L.d : 0;
+    if (L.p_f16)
+      stage1_launch<true>(L, x, B, s, t1, y, ny);
+    else
+      stage1_launch<false>(L, x, B, s, t1, y, ny);
     hipError_t e = L.p_f16 ? scores_launch<true>(L, B, sc, s) : scores_launch<false>(L, B, sc, s);
     if (e != hipSuccess) return e;
     e = launch_compact(L, sc, B, idx, count, tokmask, s);
@@ -1765,10 +1894,11 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     forward_tiles(L, x, B, idx, count, tokmask, y, false, s, t2, t3);
     return hipGetLastError();
   }
+  const int ny = L.ks_down > 1 ? B * L.d : 0;
   if (L.p_f16)
-    stage1_launch<true>(L, x, B, s, t1, y);
+    stage1_launch<true>(L, x, B, s, t1, y, ny, true);
   else
-    stage1_launch<false>(L, x, B, s, t1, y);
+    stage1_launch<false>(L, x, B, s, t1, y, ny, true);
   if (L.w_f16) {
     if (L.gated) mid_dispatch<true, true>(L, x, B, scores, s, t2);
     else mid_dispatch<true, false>(L, x, B, scores, s, t2);

@@ -43,8 +43,10 @@
  *      x:               [B][d] fp32       tokens;  y: [B][d] fp32
  *      scores:          [B][d_ffn] fp32
  *  - Arithmetic: weights are read as stored (fp16 or fp32) and widened to fp32; every
- *    accumulation is fp32. Results are deterministic: the same inputs give bit-identical
- *    outputs (no floating-point atomics anywhere).
+ *    accumulation is fp32. Index lists, counts and token bits are always bit-identical
+ *    from run to run; y is too when the descriptor asks for it (`deterministic`),
+ *    otherwise the down projection's row splits add into y with float atomics and its
+ *    last bits may vary between runs.
  */
 #ifndef SPARSE_FFN_H
 #define SPARSE_FFN_H
