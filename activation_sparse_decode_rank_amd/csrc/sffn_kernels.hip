@@ -89,6 +89,23 @@ __device__ __forceinline__ void load_x(const float* p, float* xs) {
   }
 }
 
+// Read one word of each of the first LINES 64-byte lines of this kernel's explicit
+// arguments at entry, all loads issued before one wait. The compiler otherwise loads
+// arguments next to their first use, spread through the kernel, and each argument line
+// touched for the first time costs a memory round trip; after this every such load hits
+// the scalar cache. Large by-value tables go last in the argument list, past LINES.
+template <int LINES>
+__device__ __forceinline__ void touch_kernargs() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef const uint32_t __attribute__((address_space(4)))* karg_ptr;
+  const karg_ptr ka = (karg_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t v = 0;
+#pragma unroll
+  for (int l = 0; l < LINES; ++l) v ^= ka[16 * l];
+  asm volatile("" ::"s"(v));
+#endif
+}
+
 // Cross-lane adds through DPP: VALU operations that read a neighbouring lane's register
 // directly, with no LDS round trip. Lanes whose source is outside the pattern, or whose
 // 16-lane row is masked off, add 0. Patterns used (each adds the value of lane src(l)):
@@ -177,10 +194,11 @@ __global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1
                                                      int B, float* __restrict__ q,
                                                      float* __restrict__ y0, int ny,
                                                      const void* __restrict__ p2, int nchp,
-                                                     const RangeArg ra,
                                                      const float* __restrict__ pfb0,
-                                                     const float* __restrict__ pfb1) {
+                                                     const float* __restrict__ pfb1,
+                                                     const RangeArg ra) {
   constexpr int EPC = Elt<PF16>::EPC;
+  touch_kernargs<2>();
   const int j = blockIdx.x, tid = threadIdx.x;
   if (j >= r) {
     const int w = j - r;
@@ -527,8 +545,8 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
     int r, const void* __restrict__ w_act, const float* __restrict__ b_act,
     const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
-    const RangeArg ra, uint64_t* __restrict__ wbits, uint64_t* __restrict__ tok_full,
-    float* __restrict__ h_g, float* __restrict__ scores, int x_lds) {
+    uint64_t* __restrict__ wbits, uint64_t* __restrict__ tok_full, float* __restrict__ h_g,
+    float* __restrict__ scores, int x_lds, const RangeArg ra) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int PL = 16;  // P2 chunks a thread keeps in flight
   constexpr int RMAX = MID_RANGE_MAX;
@@ -546,6 +564,7 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
   __shared__ int s_wcnt[TPB / 64];
   __shared__ float s_red[G::RED_FLOATS];
 
+  touch_kernargs<2>();
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
   const int nown = r1 - r0;  // 1..RMAX
@@ -687,8 +706,8 @@ template <bool F16, bool GATED, int CPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_mid_b1(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
     const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int n, float tau, const int32_t* __restrict__ rs, const RangeArg ra,
-    uint64_t* __restrict__ wbits, float* __restrict__ h_g, float* __restrict__ scores) {
+    int d, int n, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
+    float* __restrict__ h_g, float* __restrict__ scores, const RangeArg ra) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int GRP = NCHP < 64 ? NCHP : 64;   // lanes holding one predictor row in a wave
   constexpr int WPR = NCHP > 64 ? NCHP / 64 : 1;  // waves per predictor row
@@ -708,6 +727,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
   __shared__ int s_wcnt[TPB / 64];
   __shared__ float s_red[4 * RB * NV];
 
+  touch_kernargs<2>();
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
   const int nown = r1 - r0;  // 1..RMAX
@@ -921,7 +941,7 @@ __global__ __launch_bounds__(TPB) void k_down(
     const float* __restrict__ h_in, int d, int n, int B, const int32_t* __restrict__ idx_in,
     const int32_t* __restrict__ count_in, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, const SplitArg sa, const uint64_t* __restrict__ tok_full,
-    int KS, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
+    int KS, int ncb, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
     uint64_t* __restrict__ tokmask_out, float* __restrict__ y) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int COLS = CB_LANES * EPC;
@@ -934,9 +954,9 @@ __global__ __launch_bounds__(TPB) void k_down(
   __shared__ int s_psum[TPB / 64];
   __shared__ float s_red[TPB / 64][4][CB_LANES][TB * EPC];  // [wave][16-lane row][chunk][value]
 
+  touch_kernargs<4>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = d / EPC;
-  const int ncb = gridDim.x / KS;
   const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
   const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
   const int chunk = min(cb * CB_LANES + li, nch - 1);  // a partial last block re-reads; unused
@@ -1547,10 +1567,10 @@ void stage1_launch_t(const LayerDev& L, const float* x, int B, hipStream_t s,
   const dim3 grid(L.r + g_pf);
   if (B == 1)
     launch(k_pred_stage1<F16, 1, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
-           y0, ny, L.p2, nchp, L.ra, L.p_bias, L.b_act);
+           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
   else
     launch(k_pred_stage1<F16, 4, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
-           y0, ny, L.p2, nchp, L.ra, L.p_bias, L.b_act);
+           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
 }
 
 // prefetch workgroups are used when the ranges travel in the kernel arguments, a range's
@@ -1637,7 +1657,7 @@ void down_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* 
   const size_t lds = BITS ? (size_t)LIST_CAP * 4 : 0;
   launch(k_down<F16, BITS, TB, UPT>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t, L.b_out,
          L.h_buf, L.d, L.n, B, idx, count, L.wbits, L.rs, L.sa, L.tok_full, L.ks_down,
-         idx_out, count_out, tok_out, y);
+         down_blocks(L), idx_out, count_out, tok_out, y);
 }
 
 // BITS: decode (list from the union bitmask, activations by neuron); otherwise the given
@@ -1670,8 +1690,8 @@ template <bool F16, bool GATED, int CPT, int NCHP>
 void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                    const hipEvent_t* tev) {
   launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), 0, s, tev, L.p2,
-         L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs, L.ra,
-         L.wbits, L.h_buf, scores);
+         L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs,
+         L.wbits, L.h_buf, scores, L.ra);
 }
 
 template <bool F16, bool GATED, int CPT>
@@ -1696,11 +1716,11 @@ void mid_launch_cpt(const LayerDev& L, const float* x, int B, float* scores, hip
   if (B == 1)
     launch(k_fused_mid<F16, GATED, CPT, 1>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
            L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
-           L.rs_in_arg ? nullptr : L.rs, L.ra, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0);
+           L.rs_in_arg ? nullptr : L.rs, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0, L.ra);
   else
     launch(k_fused_mid<F16, GATED, CPT, 4>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
            L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
-           L.rs_in_arg ? nullptr : L.rs, L.ra, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0);
+           L.rs_in_arg ? nullptr : L.rs, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0, L.ra);
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
