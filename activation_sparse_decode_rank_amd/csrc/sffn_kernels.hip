@@ -1131,6 +1131,182 @@ __global__ __launch_bounds__(TPB) void k_down(
   }
 }
 
+// Single-token decode form of the down projection (list from the middle kernel's activity
+// words, one token). Same column blocks, range splits and fixed-order reduction as k_down,
+// written for a short dependent chain of instructions: these workgroups run one wave per
+// SIMD, so every instruction on the path to the weight loads adds its full latency. The
+// split's own words are scanned first; the words of earlier ranges (needed only for the
+// list's global positions, which are published last) are loaded in the same round but
+// summed after the sums have been issued. Neuron ids expand into LDS without bound checks
+// when the split fits one window (the usual case), and no barrier precedes that window.
+template <bool WF16>
+__device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
+                                             const float* __restrict__ h_in, int n,
+                                             unsigned nch, unsigned chunk, int rsl,
+                                             const int32_t* s_list, int wl,
+                                             float (&acc)[Elt<WF16>::EPC]) {
+  constexpr int EPC = Elt<WF16>::EPC;
+  constexpr int LD = 16;
+  for (int kb0 = 0; kb0 < wl; kb0 += RSD * LD) {
+    int ii[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) ii[u] = min(s_list[min(kb0 + u * RSD + rsl, wl - 1)], n - 1);
+    float hv[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) hv[u] = h_in[ii[u]];
+    u32x4 wv[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) wv[u] = ld_stream(w_down_t, (unsigned)ii[u] * nch + chunk);
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const float h = kb0 + u * RSD + rsl < wl ? hv[u] : 0.f;
+      float f[EPC];
+      unpack<WF16>(wv[u], f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] = fmaf(h, f[e], acc[e]);
+    }
+  }
+}
+
+template <bool WF16, int UPT>
+__global__ __launch_bounds__(TPB) void k_down_b1(
+    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
+    const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
+    float* __restrict__ y, const SplitArg sa) {
+  constexpr int EPC = Elt<WF16>::EPC;
+  constexpr int COLS = CB_LANES * EPC;
+  constexpr int PFX = G_MID_MAX / TPB;  // earlier-range words per thread
+  static_assert(UPT >= 1 && UPT * TPB <= G_MID_MAX, "UPT");
+  extern __shared__ float4_t s_dyn4[];
+  int32_t* s_list = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
+  __shared__ int s_wsum[TPB / 64];
+  __shared__ int s_psum[TPB / 64];
+  __shared__ float s_red[TPB / 64][4][CB_LANES][EPC];  // [wave][16-lane row][chunk][value]
+  touch_kernargs<2>();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned nch = d / EPC;
+  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
+  const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
+  const unsigned chunk = min((unsigned)(cb * CB_LANES + li), nch - 1);  // partial last block
+  const int u0 = sa.s[kq], u1 = sa.s[kq + 1];
+
+  uint64_t wd[UPT];
+  int rb[UPT];
+  int c = 0;
+#pragma unroll
+  for (int v = 0; v < UPT; ++v) {
+    const int u = u0 + tid * UPT + v;
+    wd[v] = u < u1 ? wbits[u] : 0;
+    rb[v] = u < u1 ? rs[u] : 0;
+  }
+  uint64_t pw[PFX];
+#pragma unroll
+  for (int v = 0; v < PFX; ++v) pw[v] = tid + v * TPB < u0 ? wbits[tid + v * TPB] : 0;
+#pragma unroll
+  for (int v = 0; v < UPT; ++v) c += __popcll(wd[v]);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wsum[v] : 0;
+  const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];  // rows of this split
+  const int off = before + incl - c;  // local position of this thread's first set bit
+
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  int gbase = -1;  // global list position of the split's first row, once known
+  if (total <= LIST_CAP) {
+    int pos = off;
+#pragma unroll
+    for (int v = 0; v < UPT; ++v) {
+      uint64_t m = wd[v];
+      while (m) {
+        s_list[pos++] = rb[v] + (__ffsll((unsigned long long)m) - 1);
+        m &= m - 1;
+      }
+    }
+    __syncthreads();
+    down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, total, acc);
+  } else {
+    // long split: windows of LIST_CAP, each published as it is expanded (global offset first)
+    int pc = 0;
+#pragma unroll
+    for (int v = 0; v < PFX; ++v) pc += __popcll(pw[v]);
+    const int pincl = wave_incl_scan(pc);
+    if (lane == 63) s_psum[wave] = pincl;
+    for (int wb = 0; wb < total; wb += LIST_CAP) {
+      const int wl = min(LIST_CAP, total - wb);
+      __syncthreads();
+      gbase = s_psum[0] + s_psum[1] + s_psum[2] + s_psum[3];
+      int pos = off;
+#pragma unroll
+      for (int v = 0; v < UPT; ++v) {
+        uint64_t m = wd[v];
+        while (m) {
+          if (pos >= wb && pos < wb + wl) s_list[pos - wb] = rb[v] + (__ffsll((unsigned long long)m) - 1);
+          m &= m - 1;
+          ++pos;
+        }
+      }
+      __syncthreads();
+      if (idx_out) {
+        for (int k = cb + tid * ncb; k < wl; k += TPB * ncb) {
+          idx_out[gbase + wb + k] = s_list[k];
+          if (tokmask_out) tokmask_out[gbase + wb + k] = 1;
+        }
+      }
+      down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, wl, acc);
+    }
+  }
+  // fixed-order reduction of the 32 row slots: lanes l and l+8 of each 16-lane row (DPP,
+  // complete in lanes 8..15), then the 4 rows of each wave and the 4 waves in order
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = dpp_add<dpp_shr(8)>(acc[e]);
+  if ((lane & 15) >= 8) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s_red[wave][lane >> 4][li][e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < COLS) {
+    const int c_li = tid / EPC, e = tid % EPC;
+    const int col = (cb * CB_LANES + c_li) * EPC + e;
+    if (col < d && (kq == 0 || total > 0)) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < TPB / 64; ++w2)
+#pragma unroll
+        for (int row = 0; row < 4; ++row) sum += s_red[w2][row][c_li][e];
+      if (kq == 0 && b_out) sum += b_out[col];
+      if (KS == 1)
+        y[col] = sum;
+      else
+        atomicAdd(y + col, sum);
+    }
+  }
+  // the list: this split's rows sit at global positions gbase + k (gbase = active neurons
+  // of all earlier ranges); workgroup cb publishes the positions k with k % ncb == cb
+  if (gbase < 0) {
+    int pc = 0;
+#pragma unroll
+    for (int v = 0; v < PFX; ++v) pc += __popcll(pw[v]);
+    const int pincl = wave_incl_scan(pc);
+    if (lane == 63) s_psum[wave] = pincl;
+    __syncthreads();
+    gbase = s_psum[0] + s_psum[1] + s_psum[2] + s_psum[3];
+    if (idx_out) {
+      for (int k = cb + tid * ncb; k < total; k += TPB * ncb) {
+        idx_out[gbase + k] = s_list[k];
+        if (tokmask_out) tokmask_out[gbase + k] = 1;
+      }
+    }
+  }
+  if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + total;
+}
+
 // ============================================================================ batch tiles
 // From TILE_MIN_B tokens on, the union rows form dense tiles and the products go to the
 // matrix cores: v_mfma_f32_16x16x32_f16 multiplies a 16x32 fp16 tile by a 32x16 fp16 tile
@@ -1671,6 +1847,10 @@ void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* co
     else down_launch_t<F16, false, 4, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev);
     return;
   }
+#define DOWN_B1(UPT)                                                                           \
+  launch(k_down_b1<F16, UPT>, dim3(down_blocks(L) * L.ks_down), dim3(TPB), (size_t)LIST_CAP * 4, \
+         s, tev, L.w_down_t, L.b_out, L.h_buf, L.d, L.n, L.wbits, L.rs, L.ks_down,              \
+         down_blocks(L), idx_out, count_out, tok_out, y, L.sa)
 #define DOWN_BITS(TB)                                                                          \
   switch (L.split_upt) {                                                                       \
     case 1: down_launch_t<F16, true, TB, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
@@ -1679,11 +1859,17 @@ void down_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* co
     default: down_launch_t<F16, true, TB, 8>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
   }
   if (B == 1) {
-    DOWN_BITS(1)
+    switch (L.split_upt) {
+      case 1: DOWN_B1(1); break;
+      case 2: DOWN_B1(2); break;
+      case 4: DOWN_B1(4); break;
+      default: DOWN_B1(8); break;
+    }
   } else {
     DOWN_BITS(4)
   }
 #undef DOWN_BITS
+#undef DOWN_B1
 }
 
 template <bool F16, bool GATED, int CPT, int NCHP>
