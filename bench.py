@@ -3,19 +3,22 @@
 
 Workload (default): the OPT-6.7B-shaped ReLU FFN stack, 32 layers, d=4096, d_ffn=16384,
 fp16 weights, predictor rank 256, batch 1, per-layer activity 5% -> 10% (Zipf 1.1), hot
-20% of neurons packed first. Every weight, token and profile token is seeded synthetic
-data (no model checkpoint, no dataset).
+20% of neurons packed first. `--config` selects another workload shape (C1 OPT-125m layer,
+C3 Llama-7B-shaped gated stack, C4 its batch sweep with `--batch`, C5 OPT-175B-shaped
+slice); every weight, token and profile token is seeded synthetic data (no model
+checkpoint, no dataset).
 
-A step is one decode token through every layer of the stack: for each layer, the predictor
-(both stages), threshold, compaction, gather-GEMV + ReLU and down projection, all through
-the library's single-call decode entry point. Each (token, layer) reads its own pre-drawn
-x, so the calibrated activity holds; y is not chained into the next layer. Steps are
-replayed from HIP graphs (one per group of tokens) with inputs resident in HBM; the timed
-region is bracketed by device synchronizations.
+A step is one decode token (or one batch of `--batch` tokens) through every layer of the
+stack: for each layer, the predictor (both stages), threshold, compaction, gather-GEMV +
+ReLU and down projection, all through the library's single-call decode entry point. Each
+(token, layer) reads its own pre-drawn x, so the calibrated activity holds; y is not
+chained into the next layer. Steps are replayed from HIP graphs (one per group of steps)
+with inputs resident in HBM; the timed region is bracketed by device synchronizations.
 
 Also measured, beside the headline number:
   - per-kernel durations from HIP events that each kernel dispatch stamps itself
-    (start and end of execution, on the library's stream);
+    (start and end of execution, on the library's stream), with each kernel's algorithmic
+    bytes (and, for the matrix-core kernels, flops) per launch;
   - the dense FFN of the same shapes on the same (unpacked) fp16 weights, through torch
     (hipBLASLt), graph-captured and timed the same way;
   - the fp64 CPU oracle on a bounded sample of the same workload, on the host cores.
@@ -25,8 +28,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -38,6 +41,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the part
+TILE_MIN_B = 16                # from this batch on the decode step runs the matrix-core kernels
 METRIC = "sparse FFN decode µs/layer + active-weight HBM GB/s vs peak, 10% activity"
 
 
@@ -74,13 +79,16 @@ class HipEvents:
         self.ev = []
 
 
+def kernel_source_sha():
+    src = os.path.join(ROOT, "activation_sparse_decode_rank_amd", "csrc", "sffn_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
 def measured_traffic(kernel_file, workload):
     """HBM bytes per dispatch of the dominant kernel from the committed counter summary
     profiles/<kernel>_<workload>_pmc.md (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of
     known size), or None when there is none or the kernel source has changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel_file}_{workload}_pmc.md")
-    src = os.path.join(ROOT, "activation_sparse_decode_rank_amd", "csrc", "sffn_kernels.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -88,8 +96,7 @@ def measured_traffic(kernel_file, workload):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("kernel source sha256") != digest:
+    if fields.get("kernel source sha256") != kernel_source_sha():
         return None
     try:
         return float(fields["traffic bytes per dispatch"])
@@ -97,27 +104,55 @@ def measured_traffic(kernel_file, workload):
         return None
 
 
-def kernel_bytes(cfg, n_act):
-    """Algorithmic bytes per launch of each decode kernel for one token."""
+def kernel_names(cfg, B):
+    """The three kernels the decode step's timing events cover, by path."""
+    if B >= TILE_MIN_B and cfg.w_dtype == "f16" and cfg.d % 128 == 0:
+        return ("stage1", "up_tiles", "down_tiles"), {
+            "stage1": "k_pred_stage1 (predictor stage 1, q = P1 x)",
+            "up_tiles": "k_up_mfma (gathered-tile up projection on the matrix cores)",
+            "down_tiles": "k_down_mfma (gathered-tile down projection on the matrix cores)"}
+    return ("stage1", "mid", "down"), {
+        "stage1": "k_pred_stage1 (predictor stage 1, q = P1 x)",
+        "mid": ("k_mid_b1" if B == 1 else "k_fused_mid")
+        + " (predictor stage 2 + threshold + compaction + gather-GEMV/ReLU)",
+        "down": ("k_down_b1" if B == 1 else "k_down") + " (down projection over the active rows)"}
+
+
+def kernel_cost(cfg, B, n_union):
+    """Algorithmic bytes and flops per launch of each timed decode kernel for one step
+    (n_union: rows in the union list)."""
     sw, sp = cfg.w_bytes, cfg.p_bytes
     d, n, r = cfg.d, cfg.n, cfg.rank
     ma = 2 if cfg.gated else 1
-    stage1 = r * d * sp + 4 * d + 4 * r
-    mid = n * r * sp + 4 * n + 4 * r + 4 * d + n_act * (ma * d * sw + 4 + 4 + 8 + 4)
-    down = n_act * (d * sw + 4 + 4 + 8 + 4 + 8) + 4 * d + 4 * d
-    return {"stage1": stage1, "mid": mid, "down": down}
+    names, _ = kernel_names(cfg, B)
+    stage1 = r * d * sp + 4 * B * d + 4 * B * r
+    if names[1] == "mid":
+        # P2, biases, q and x; the union's activation rows; activity words, bits and
+        # activations out
+        mid = n * r * sp + 8 * n + 4 * B * r + 4 * B * d + n_union * (ma * d * sw + 8 + 4 * B)
+        # activation rows, activations, list and bits out, y
+        down = n_union * (d * sw + 4 + 4 * B + 8) + 4 * B * d * 2
+        return {"stage1": (stage1, 0.0), "mid": (mid, 0.0), "down": (down, 0.0)}
+    up = n_union * (ma * d * sw + 4 + 8 + 4 + 4 * B) + 4 * B * d
+    down = n_union * (d * sw + 4 + 4 * B) + 4 * B * d * 2
+    # flops of the products as defined (every token against the union rows); the kernels
+    # issue each product twice (hi and lo halves of the fp32 activations)
+    up_fl = 2.0 * ma * d * n_union * B
+    down_fl = 2.0 * d * n_union * B
+    return {"stage1": (stage1, 0.0), "up_tiles": (up, up_fl), "down_tiles": (down, down_fl)}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256, help="timed decode tokens (each = all layers)")
+    ap.add_argument("--steps", type=int, default=256, help="timed decode steps (each = all layers)")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--config", default="C2")
-    ap.add_argument("--tokens", type=int, default=256, help="distinct pre-drawn tokens")
-    ap.add_argument("--group", type=int, default=8, help="tokens per captured graph")
+    ap.add_argument("--batch", type=int, default=1, help="tokens decoded together per step")
+    ap.add_argument("--tokens", type=int, default=256, help="distinct pre-drawn steps")
+    ap.add_argument("--group", type=int, default=8, help="steps per captured graph")
     ap.add_argument("--profile-tokens", type=int, default=4096)
-    ap.add_argument("--kernel-tokens", type=int, default=32, help="tokens in the per-kernel event pass")
+    ap.add_argument("--kernel-tokens", type=int, default=32, help="steps in the per-kernel event pass")
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -144,12 +179,16 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
+    B = int(args.batch)
+    if not 1 <= B <= NAT.SFFN_MAX_BATCH:
+        raise SystemExit(f"--batch must be in 1..{NAT.SFFN_MAX_BATCH}")
     L = args.layers or (cfg.rotate_copies if cfg.rotate_copies > 1 else cfg.layers)
     d, n, r = cfg.d, cfg.n, cfg.rank
     G = max(1, args.group)
     T = max(G, (args.tokens // G) * G)
     steps = max(G, ((args.steps + G - 1) // G) * G)
     warmup = ((args.warmup + G - 1) // G) * G
+    names, knames = kernel_names(cfg, B)
     t_setup = time.time()
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
@@ -168,30 +207,41 @@ def main():
         src_layer = 0 if cfg.rotate_copies > 1 else l
         Lt = make_layer(cfg, src_layer, "cuda")
         s = SparseFFN(w_act=Lt.w_a, w_up=Lt.w_u, w_down_t=Lt.w_o, p1=Lt.p1, p2=Lt.p2,
-                      b_act=Lt.b_a, b_out=Lt.b_o, p_bias=Lt.c, max_batch=1, profile_x=Xprof,
+                      b_act=Lt.b_a, b_out=Lt.b_o, p_bias=Lt.c, max_batch=B, profile_x=Xprof,
                       hot_frac=cfg.hot_frac)
         layers.append(s)
-        originals.append(Lt)
+        keep = not args.no_dense or (not args.no_cpu and l < 2)
+        originals.append(Lt if keep else None)
+        del Lt
         if l % 8 == 0 or l == L - 1:
             log(f"layer {l + 1}/{L} generated, profiled and packed")
     del Xprof
-    X = make_tokens(cfg, T * L, 200, "cuda").view(T, L, d).contiguous()
+    X = make_tokens(cfg, T * L * B, 200, "cuda").view(T, L, B, d).contiguous()
     torch.cuda.synchronize()
-    log(f"setup {time.time() - t_setup:.1f}s; {T} tokens x {L} layers")
+    log(f"setup {time.time() - t_setup:.1f}s; {T} steps x {L} layers x {B} token(s)")
 
     # ------------------------------------------------------------------ sparse decode graphs
-    y_buf = torch.empty((L, 1, d), dtype=torch.float32, device="cuda")
+    y_buf = torch.empty((L, B, d), dtype=torch.float32, device="cuda")
     idx_buf = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(L)]
     tok_buf = [torch.empty(n, dtype=torch.int64, device="cuda") for _ in range(L)]
     counts = torch.zeros((T, L), dtype=torch.int32, device="cuda")
+    per_tok = np.zeros((T, L), np.int64)  # sum over tokens of each token's own actives
 
-    def decode_token(t):
+    def decode_step(t):
         for l in range(L):
-            layers[l].decode(X[t, l:l + 1], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
+            layers[l].decode(X[t, l], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
                              tokmask=tok_buf[l])
 
-    for t in range(min(T, 2)):
-        decode_token(t)
+    # one eager pass over every step: union sizes and, for batches, each token's actives
+    for t in range(T):
+        decode_step(t)
+        if B > 1:
+            torch.cuda.synchronize()
+            for l in range(L):
+                k = int(counts[t, l].item())
+                bits = tok_buf[l][:k].cpu().numpy().view(np.uint64)
+                per_tok[t, l] = int(sum(int(((bits >> np.uint64(b)) & np.uint64(1)).sum())
+                                        for b in range(B)))
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
     graphs = []
@@ -200,38 +250,39 @@ def main():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 for t in range(gi * G, (gi + 1) * G):
-                    decode_token(t)
+                    decode_step(t)
             graphs.append(g)
         torch.cuda.synchronize()
-        log(f"captured {len(graphs)} graphs of {G * L * 3} kernels")
+        log(f"captured {len(graphs)} graphs of {G * L} layer steps")
 
-    def replay(graph_list, ntok):
+    def replay(graph_list, nsteps, eager_fn):
         if not graph_list:
-            for i in range(ntok):
-                decode_token(i % T)
+            for i in range(nsteps):
+                eager_fn(i % T)
             return
-        for i in range(ntok // G):
+        for i in range(nsteps // G):
             graph_list[i % len(graph_list)].replay()
 
-    replay(graphs, warmup)
+    replay(graphs, warmup, decode_step)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    replay(graphs, steps)
+    replay(graphs, steps, decode_step)
     e1.record()
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / steps
     us_per_layer = ms_per_step * 1000.0 / L
-    log(f"sparse decode: {ms_per_step:.4f} ms/token, {us_per_layer:.3f} us/layer")
+    log(f"sparse decode: {ms_per_step:.4f} ms/step, {us_per_layer:.3f} us/layer")
 
-    cnt = counts.cpu().numpy().astype(np.int64)  # actual active neurons per (token, layer)
+    cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
+    if B == 1:
+        per_tok = cnt
     used = [t % T for t in range(steps)]
-    n_act_used = cnt[used].astype(np.float64)
-    n_act_mean = float(n_act_used.mean())
-    m = cfg.m
-    b_active = n_act_mean * m * d * cfg.w_bytes
+    n_union_mean = float(cnt[used].mean())
+    n_tok_mean = float(per_tok[used].mean()) / B
+    b_active = n_union_mean * cfg.m * d * cfg.w_bytes  # weight bytes the step must move
     b_pred = (r * d + n * r) * cfg.p_bytes + 4 * n
     active_gbps = b_active / (us_per_layer * 1e-6) / 1e9
 
@@ -242,64 +293,69 @@ def main():
         for l in range(L):
             base = 6 * (t * L + l)
             NAT.sparse_ffn_set_timing_events(layers[l].handle, hev.ev[base:base + 6])
-            layers[l].decode(X[t, l:l + 1], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
+            layers[l].decode(X[t, l], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
                              tokmask=tok_buf[l])
     torch.cuda.synchronize()
     for l in range(L):
         NAT.sparse_ffn_set_timing_events(layers[l].handle, None)
-    kus = {"stage1": [], "mid": [], "down": []}
-    kbytes = {"stage1": [], "mid": [], "down": []}
+    kus = {k: [] for k in names}
+    kbytes = {k: [] for k in names}
+    kflops = {k: [] for k in names}
     for t in range(KT):
         for l in range(L):
             base = 6 * (t * L + l)
-            for j, k in enumerate(("stage1", "mid", "down")):
+            cost = kernel_cost(cfg, B, int(cnt[t, l]))
+            for j, k in enumerate(names):
                 kus[k].append(1000.0 * hev.elapsed_ms(base + 2 * j, base + 2 * j + 1))
-            kb = kernel_bytes(cfg, int(cnt[t, l]))
-            for k in kb:
-                kbytes[k].append(kb[k])
+                kbytes[k].append(cost[k][0])
+                kflops[k].append(cost[k][1])
     hev.close()
     kernels = {}
-    for k in kus:
+    for k in names:
         us = float(np.mean(kus[k]))
         gb = float(np.mean(kbytes[k])) / (us * 1e-6) / 1e9
         kernels[k] = {"avg_us": round(us, 3), "algorithmic_bytes": int(np.mean(kbytes[k])),
                       "gbps": round(gb, 1)}
-    dom = max(("mid", "down"), key=lambda k: kernels[k]["avg_us"])
-    kname = {"mid": "k_mid_b1 (predictor stage 2 + threshold + compaction + gather-GEMV/ReLU)",
-             "down": "k_down (down projection, column-owned)"}[dom]
+        if np.mean(kflops[k]) > 0:
+            tf = float(np.mean(kflops[k])) / (us * 1e-6) / 1e12
+            kernels[k]["algorithmic_flops"] = int(np.mean(kflops[k]))
+            kernels[k]["tflops"] = round(tf, 2)
+            kernels[k]["mfma_util"] = round(tf / MFMA_F16_PEAK_TFLOPS, 5)
+    dom = max(names[1:], key=lambda k: kernels[k]["avg_us"])
     log("kernels:", json.dumps(kernels))
 
     # ------------------------------------------------------------------ dense baseline
     dense = None
     if not args.no_dense:
-        X16 = X.half()
-        b16 = [o.b_a.half() for o in originals]
-        bo16 = [o.b_o.half() for o in originals]
+        wdt = originals[0].w_a.dtype  # the dense chain computes in the weights' dtype
+        Xw = X.to(wdt)
+        bw = [o.b_a.to(wdt) for o in originals]
+        bow = [o.b_o.to(wdt) for o in originals]
 
-        def dense_token(t):
+        def dense_step(t):
             for l in range(L):
                 o = originals[l]
-                x = X16[t, l:l + 1]
-                a = F.linear(x, o.w_a, b16[l])
+                x = Xw[t, l]
+                a = F.linear(x, o.w_a, bw[l])
                 h = F.relu(a)
                 if o.w_u is not None:
                     h = h * F.linear(x, o.w_u)
-                _ = torch.matmul(h, o.w_o) + bo16[l]
+                _ = torch.matmul(h, o.w_o) + bow[l]
 
         for t in range(2):
-            dense_token(t)
+            dense_step(t)
         torch.cuda.synchronize()
         dgraphs = []
         for gi in range(T // G):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 for t in range(gi * G, (gi + 1) * G):
-                    dense_token(t)
+                    dense_step(t)
             dgraphs.append(g)
-        replay(dgraphs, warmup)
+        replay(dgraphs, warmup, dense_step)
         torch.cuda.synchronize()
         e0.record()
-        replay(dgraphs, steps)
+        replay(dgraphs, steps, dense_step)
         e1.record()
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / steps
@@ -307,7 +363,8 @@ def main():
         dense_bytes = (n * d * (3 if cfg.gated else 2)) * cfg.w_bytes
         dense = {"us_per_layer": round(dense_us, 3),
                  "gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
-                 "impl": "torch F.linear/matmul (hipBLASLt), fp16, graph-captured"}
+                 "impl": f"torch F.linear/matmul (hipBLASLt/rocBLAS), {cfg.w_dtype}, {B} token(s), "
+                         f"graph-captured"}
         log(f"dense: {dense_us:.3f} us/layer ({dense['gbps']} GB/s)")
         del dgraphs
 
@@ -325,7 +382,7 @@ def main():
         while time.time() - t_start < args.cpu_seconds and done < T * n_cpu_layers:
             t, l = done // n_cpu_layers, done % n_cpu_layers
             Lh = host[l]
-            x = np.ascontiguousarray(Xh[t, l:l + 1])
+            x = np.ascontiguousarray(Xh[t, l])
             c0 = time.perf_counter()
             S = oracle.predict(x, Lh["p1"], Lh["p2"], Lh["c"])
             idx, k, tok = oracle.compact(oracle.threshold(S, 0.0))
@@ -335,18 +392,24 @@ def main():
             done += 1
         cpu = {"value": round(float(np.median(times)), 1), "unit": "us/layer", "cores": 1,
                "kind": "oracle",
-               "sample": f"{len(times)} (token, layer) decodes of layers 0..{n_cpu_layers - 1}, "
-                         f"tokens 0..{(len(times) - 1) // n_cpu_layers}: predict + threshold + "
-                         f"compact + forward in fp64, single thread, median"}
+               "sample": f"{len(times)} (step, layer) decodes of {B} token(s), layers "
+                         f"0..{n_cpu_layers - 1}, steps 0..{(len(times) - 1) // n_cpu_layers}: "
+                         f"predict + threshold + compact + forward in fp64, single thread, median"}
         log(f"cpu oracle: {cpu['value']} us/layer over {len(times)} samples")
 
     # ------------------------------------------------------------------ report
     kd = kernels[dom]
-    traffic = measured_traffic({"mid": "k_mid_b1", "down": "k_down"}[dom], cfg.name)
-    roof = {"bound": "hbm", "kernel": kname, "achieved": kd["gbps"], "peak": HBM_PEAK_GBPS,
+    kfile = knames[dom].split(" ")[0]
+    traffic = measured_traffic(kfile, f"{cfg.name}_b{B}")
+    roof = {"bound": "hbm", "kernel": knames[dom], "achieved": kd["gbps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(kd["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": (int(traffic) if traffic is not None else None),
             "algorithmic_bytes": kd["algorithmic_bytes"]}
+    if "mfma_util" in kd:
+        # the matrix-core kernels stay bound by HBM at these arithmetic intensities; their
+        # flops rate against the fp16 matrix-core peak rides along
+        roof["mfma"] = {"achieved_tflops": kd["tflops"], "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                        "util": kd["mfma_util"]}
     act_lo, act_hi = min(cfg.activity), max(cfg.activity)
     out = {
         "metric": METRIC,
@@ -363,13 +426,15 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.description}",
-            "layers": L, "d": d, "d_ffn": n, "rank": r, "batch": 1,
+            "layers": L, "d": d, "d_ffn": n, "rank": r, "batch": B,
             "weights": cfg.w_dtype, "predictor": cfg.p_dtype,
             "activity_target": (f"{act_lo:.3f}-{act_hi:.3f}" if act_lo != act_hi else f"{act_lo:.3f}"),
-            "tokens": T, "graph_tokens": G,
+            "tokens": T, "graph_steps": G,
         },
-        "n_act_mean": round(n_act_mean, 1),
-        "activity_measured": round(n_act_mean / n, 4),
+        "n_act_mean": round(n_tok_mean, 1),
+        "n_union_mean": round(n_union_mean, 1),
+        "activity_measured": round(n_tok_mean / n, 4),
+        "union_fraction": round(n_union_mean / n, 4),
         "active_weight_bytes_per_layer": int(b_active),
         "predictor_bytes_per_layer": int(b_pred),
         "active_weight_gbps": round(active_gbps, 1),
@@ -380,6 +445,7 @@ def main():
         "speedup_vs_dense": (round(dense["us_per_layer"] / us_per_layer, 3) if dense else None),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "kernel_source_sha256": kernel_source_sha(),
     }
     print(json.dumps(out), flush=True)
 
