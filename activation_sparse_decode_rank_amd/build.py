@@ -18,7 +18,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_ffn.so")
-SOURCES = ["sffn_api.hip", "sffn_kernels.hip"]
+SOURCES = ["sffn_api.hip", "sffn_dispatch.hip", "sffn_decode_b1.hip", "sffn_batch.hip",
+           "sffn_mid_bt_h4.hip", "sffn_mid_bt_h8.hip", "sffn_mid_bt_f4.hip", "sffn_mid_bt_f8.hip",
+           "sffn_tiles.hip", "sffn_offline.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 FLAGS = [
@@ -43,7 +45,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

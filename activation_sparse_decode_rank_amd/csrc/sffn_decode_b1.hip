@@ -1,0 +1,628 @@
+// Batch-1 decode kernels (gfx950): predictor stage 1 with the prefetch of the middle
+// kernel's first loads, the fused middle kernel (predictor stage 2, threshold, per-range
+// compaction, gather-GEMV + ReLU) and the single-token down projection. The method is
+// described at the top of sffn_device.h.
+#include "sffn_device.h"
+
+namespace sffn {
+namespace {
+
+// ============================================================================ predictor
+// Stage 1: q[b][j] = P1[j] . x_b. Workgroup j < r owns predictor row j; each thread holds
+// NCPT chunks of the row in registers and reuses them for every token group of TBG. In the
+// decode step these workgroups also clear y (ny floats), which the down projection later
+// adds its split-k sums into.
+// Workgroups r .. r + g_pf - 1 only prefetch: workgroup r + w reads middle-kernel range w's
+// rows of the predictor's second-stage matrix p2 (NCHP chunks per row) and its two bias
+// entries per neuron, so that the middle kernel's first loads hit cache instead of HBM.
+// Those addresses are static, so their latency overlaps this kernel's own. Workgroups are
+// dealt to the XCDs round-robin by id, and r is a multiple of 8, so workgroup r + w shares
+// an XCD (and its L2) with middle workgroup w. Every prefetch load is issued before any
+// wait; the values are folded into a register that an empty asm consumes, so the loads
+// stay and nothing is stored.
+constexpr int PF_PER_THREAD = 8;
+template <bool PF16, int TBG, int NCPT>
+__global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
+                                                     const float* __restrict__ x, int d, int r,
+                                                     int B, float* __restrict__ q,
+                                                     float* __restrict__ y0, int ny,
+                                                     const void* __restrict__ p2, int nchp,
+                                                     const float* __restrict__ pfb0,
+                                                     const float* __restrict__ pfb1,
+                                                     const RangeArg ra) {
+  constexpr int EPC = Elt<PF16>::EPC;
+  touch_kernargs<2>();
+  const int j = blockIdx.x, tid = threadIdx.x;
+  if (j >= r) {
+    const int w = j - r;
+    const int r0 = ra.r[w], r1 = ra.r[w + 1];
+    const int c0 = r0 * nchp, nc = (r1 - r0) * nchp;
+    u32x4 pv[PF_PER_THREAD];
+#pragma unroll
+    for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = ld_chunk(p2, c0 + min(tid + v * TPB, nc - 1));
+    float b0 = 0.f, b1 = 0.f;
+    if (tid < r1 - r0) {
+      if (pfb0) b0 = pfb0[r0 + tid];
+      if (pfb1) b1 = pfb1[r0 + tid];
+    }
+    unsigned sink = __float_as_uint(b0) ^ __float_as_uint(b1);
+#pragma unroll
+    for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v].x;
+    asm volatile("" ::"v"(sink));
+    return;
+  }
+  for (int i = j * TPB + tid; i < ny; i += r * TPB) y0[i] = 0.f;
+  const int nch = d / EPC;
+  const size_t row0 = (size_t)j * nch;
+  __shared__ float red[TPB / 64][MAXB];
+  u32x4 wv[NCPT];
+#pragma unroll
+  for (int m = 0; m < NCPT; ++m) {
+    const int c = tid + m * TPB;
+    if (c < nch) wv[m] = ld_stream(p1, row0 + c);
+  }
+  for (int b0 = 0; b0 < B; b0 += TBG) {
+    float acc[TBG];
+#pragma unroll
+    for (int b = 0; b < TBG; ++b) acc[b] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NCPT; ++m) {
+      const int c = tid + m * TPB;
+      if (c < nch) {
+        float f[EPC];
+        unpack<PF16>(wv[m], f);
+#pragma unroll
+        for (int b = 0; b < TBG; ++b) {
+          if (b0 + b < B) {
+            float xs[EPC];
+            load_x<EPC>(x + (size_t)(b0 + b) * d + (size_t)c * EPC, xs);
+#pragma unroll
+            for (int e2 = 0; e2 < EPC; ++e2) acc[b] = fmaf(f[e2], xs[e2], acc[b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < TBG; ++b) acc[b] = wave_sum(acc[b]);
+#pragma unroll
+    for (int b = 0; b < TBG; ++b)
+      if ((tid & 63) == WAVE_SUM_LANE && b0 + b < B) red[tid >> 6][b0 + b] = acc[b];
+  }
+  __syncthreads();
+  if (tid < B) q[(size_t)tid * r + j] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+// ---------------------------------------------------------------------------- B = 1
+// The single-token form of the middle kernel, specialized on NCHP (chunks per predictor
+// row) so that the lane-group reductions are straight-line DPP code. Addresses of unused
+// slots are clamped into the owned block instead of branching per lane. Outputs as in
+// k_fused_mid with B = 1: the range's activity word and h_g[i] for every active neuron i
+// (no token bits: with one token every listed neuron is active for it).
+template <bool F16, bool GATED, int CPT, int NCHP>
+__global__ __launch_bounds__(TPB) void k_mid_b1(
+    const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
+    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
+    int d, int n, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
+    float* __restrict__ h_g, float* __restrict__ scores, const RangeArg ra) {
+  constexpr int EPC = Elt<F16>::EPC;
+  constexpr int GRP = NCHP < 64 ? NCHP : 64;   // lanes holding one predictor row in a wave
+  constexpr int WPR = NCHP > 64 ? NCHP / 64 : 1;  // waves per predictor row
+  constexpr int RPP = TPB / NCHP;              // predictor rows per slot of the workgroup
+  constexpr int PL = 8;                        // slots in flight per thread
+  constexpr int RMAX = MID_RANGE_MAX;
+  constexpr int RB = (16 / CPT) > 0 ? (16 / CPT) : 1;  // gathered rows in flight
+  constexpr int NV = GATED ? 2 : 1;
+  static_assert(NCHP >= 1 && NCHP <= 128 && (NCHP & (NCHP - 1)) == 0, "NCHP");
+  
+  __shared__ uint8_t s_act[RMAX];
+  __shared__ int32_t s_rows[RMAX];
+  __shared__ float s_bias[RMAX];
+  __shared__ float s_part[WPR > 1 ? RMAX * WPR : 1];
+  __shared__ float s_pb[RMAX];
+  __shared__ float s_ba[RMAX];
+  __shared__ int s_wcnt[TPB / 64];
+  __shared__ float s_red[4 * RB * NV];
+
+  touch_kernargs<2>();
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
+  const int nown = r1 - r0;  // 1..RMAX
+  const int pos = tid & (NCHP - 1);
+  const int rsub = tid / NCHP;
+  const int nslots = (nown + RPP - 1) / RPP;
+  const size_t blk0 = (size_t)r0 * NCHP;
+
+  // ---- every score-independent load first: P2 (first PL slots), q, biases, x. Slots
+  // beyond the range (m >= mlim, uniform) re-read its last row and are not computed.
+  // (Guarding these loads instead makes the compiler keep far more registers live.)
+  u32x4 wv[PL];
+  int mlim = min(PL, nslots);
+#pragma unroll
+  for (int m = 0; m < PL; ++m) {
+    const int j = min(m * RPP + rsub, nown - 1);
+    wv[m] = ld_chunk(p2, blk0 + (size_t)j * NCHP + pos);
+  }
+  float qs[EPC];
+  load_x<EPC>(q + (size_t)pos * EPC, qs);
+  float pb = 0.f, ba = 0.f;
+  if (tid < nown) {
+    pb = pbias ? pbias[r0 + tid] : 0.f;
+    ba = b_act ? b_act[r0 + tid] : 0.f;
+  }
+  if (tid < RMAX) s_act[tid] = 0;
+  if (tid < nown) {
+    s_pb[tid] = pb;
+    s_ba[tid] = ba;
+  }
+  __syncthreads();
+
+  // ---- predictor stage 2 and threshold
+  for (int s0 = 0; s0 < nslots; s0 += PL) {
+    if (s0 > 0) {
+      mlim = min(PL, nslots - s0);
+#pragma unroll
+      for (int m = 0; m < PL; ++m) {
+        const int j = min((s0 + m) * RPP + rsub, nown - 1);
+        wv[m] = ld_chunk(p2, blk0 + (size_t)j * NCHP + pos);
+      }
+    }
+    float acc[PL];
+#pragma unroll
+    for (int m = 0; m < PL; ++m) acc[m] = m < mlim ? dot_chunk<F16>(wv[m], qs, 0.f) : 0.f;
+#pragma unroll
+    for (int m = 0; m < PL; ++m)
+      if (m < mlim) acc[m] = group_sum<GRP>(acc[m]);
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
+      const int j = (s0 + m) * RPP + rsub;
+      if (j < nown && (lane & (GRP - 1)) == group_leader(GRP)) {
+        if (WPR == 1) {
+          const float sc = acc[m] + s_pb[j];
+          if (scores) scores[r0 + j] = sc;
+          s_act[j] = sc > tau ? 1 : 0;
+        } else {
+          s_part[j * WPR + (wave & (WPR - 1))] = acc[m];
+        }
+      }
+    }
+    if (WPR > 1) {
+      __syncthreads();
+      const int jlo = s0 * RPP, jhi = min(nown, (s0 + PL) * RPP);
+      if (tid >= jlo && tid < jhi) {
+        float sc = s_part[tid * WPR];
+#pragma unroll
+        for (int u = 1; u < WPR; ++u) sc += s_part[tid * WPR + u];
+        sc += s_pb[tid];
+        if (scores) scores[r0 + tid] = sc;
+        s_act[tid] = sc > tau ? 1 : 0;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // ---- compaction of the owned range: ballot per wave, prefix over the four waves
+  const bool act = tid < nown && s_act[tid];
+  const uint64_t word = __ballot(act);
+  if (lane == 0) s_wcnt[wave] = __popcll(word);
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wcnt[v] : 0;
+  const int nact = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  if (act) {
+    const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+    const int k = before + __popcll(lower);
+    s_rows[k] = r0 + tid;
+    s_bias[k] = s_ba[tid];
+  }
+  __syncthreads();
+
+  // ---- gather-GEMV + ReLU over the active rows, RB rows in flight. The input chunks this
+  // thread multiplies are loaded into registers once, with the first rows' loads.
+  const int nch = d / EPC;
+  const int rowch = GATED ? 2 * nch : nch;
+  float xs[CPT][EPC];
+  if (nact > 0) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * TPB;
+      const bool up = GATED && c >= nch;
+      load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
+    }
+  }
+  for (int base = 0; base < nact; base += RB) {
+    const int nb = min(RB, nact - base);  // uniform
+    u32x4 gv[RB][CPT];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      if (rr < nb) {
+        const size_t row0 = (size_t)s_rows[base + rr] * rowch;
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_stream(w_act, row0 + min(tid + m * TPB, rowch - 1));
+      }
+    }
+
+    float acc[RB][NV];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[rr][v] = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * TPB;
+      const bool cv = c < rowch;
+      const bool up = GATED && c >= nch;
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        if (rr < nb) {
+          const float dv = dot_chunk<F16>(gv[rr][m], xs[m], 0.f);
+          const float add = cv ? dv : 0.f;
+          if (GATED && up) acc[rr][NV - 1] += add;
+          else acc[rr][0] += add;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if (rr < nb) acc[rr][v] = wave_sum(acc[rr][v]);
+    if (lane == WAVE_SUM_LANE) {
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (rr < nb) s_red[(wave * RB + rr) * NV + v] = acc[rr][v];
+    }
+    __syncthreads();
+    if (tid < nb) {
+      const int rr = tid;
+      float a = s_red[(0 * RB + rr) * NV];
+      a += s_red[(1 * RB + rr) * NV];
+      a += s_red[(2 * RB + rr) * NV];
+      a += s_red[(3 * RB + rr) * NV];
+      a += s_bias[base + rr];
+      float h = a > 0.f ? a : 0.f;
+      if (GATED) {
+        float u = s_red[(0 * RB + rr) * NV + 1];
+        u += s_red[(1 * RB + rr) * NV + 1];
+        u += s_red[(2 * RB + rr) * NV + 1];
+        u += s_red[(3 * RB + rr) * NV + 1];
+        h = h * u;
+      }
+      h_g[s_rows[base + rr]] = h;
+    }
+    __syncthreads();
+  }
+  // The range's activity word (the range fits in wave 0's 64 lanes) is stored last: the
+  // wait that follows a store and a barrier would hold back the gather's loads.
+  if (tid == 0) wbits[w] = word;
+}
+
+// Single-token decode form of the down projection (list from the middle kernel's activity
+// words, one token). Same column blocks, range splits and fixed-order reduction as k_down,
+// written for a short dependent chain of instructions: these workgroups run one wave per
+// SIMD, so every instruction on the path to the weight loads adds its full latency. The
+// split's own words are scanned first; the words of earlier ranges (needed only for the
+// list's global positions, which are published last) are loaded in the same round but
+// summed after the sums have been issued. Neuron ids expand into LDS without bound checks
+// when the split fits one window (the usual case), and no barrier precedes that window.
+template <bool WF16>
+__device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
+                                             const float* __restrict__ h_in, int n,
+                                             unsigned nch, unsigned chunk, int rsl,
+                                             const int32_t* s_list, int wl,
+                                             float (&acc)[Elt<WF16>::EPC]) {
+  constexpr int EPC = Elt<WF16>::EPC;
+  constexpr int LD = 16;
+  for (int kb0 = 0; kb0 < wl; kb0 += RSD * LD) {
+    int ii[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) ii[u] = min(s_list[min(kb0 + u * RSD + rsl, wl - 1)], n - 1);
+    float hv[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) hv[u] = h_in[ii[u]];
+    u32x4 wv[LD];
+#pragma unroll
+    for (int u = 0; u < LD; ++u) wv[u] = ld_stream(w_down_t, (unsigned)ii[u] * nch + chunk);
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const float h = kb0 + u * RSD + rsl < wl ? hv[u] : 0.f;
+      float f[EPC];
+      unpack<WF16>(wv[u], f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] = fmaf(h, f[e], acc[e]);
+    }
+  }
+}
+
+template <bool WF16, int UPT>
+__global__ __launch_bounds__(TPB) void k_down_b1(
+    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
+    const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
+    float* __restrict__ y, const SplitArg sa) {
+  constexpr int EPC = Elt<WF16>::EPC;
+  constexpr int COLS = CB_LANES * EPC;
+  constexpr int PFX = G_MID_MAX / TPB;  // earlier-range words per thread
+  static_assert(UPT >= 1 && UPT * TPB <= G_MID_MAX, "UPT");
+  extern __shared__ float4_t s_dyn4[];
+  int32_t* s_list = reinterpret_cast<int32_t*>(s_dyn4);  // LIST_CAP entries
+  __shared__ int s_wsum[TPB / 64];
+  __shared__ int s_psum[TPB / 64];
+  __shared__ float s_red[TPB / 64][4][CB_LANES][EPC];  // [wave][16-lane row][chunk][value]
+  touch_kernargs<2>();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned nch = d / EPC;
+  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
+  const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
+  const unsigned chunk = min((unsigned)(cb * CB_LANES + li), nch - 1);  // partial last block
+  const int u0 = sa.s[kq], u1 = sa.s[kq + 1];
+
+  uint64_t wd[UPT];
+  int rb[UPT];
+  int c = 0;
+#pragma unroll
+  for (int v = 0; v < UPT; ++v) {
+    const int u = u0 + tid * UPT + v;
+    wd[v] = u < u1 ? wbits[u] : 0;
+    rb[v] = u < u1 ? rs[u] : 0;
+  }
+  uint64_t pw[PFX];
+#pragma unroll
+  for (int v = 0; v < PFX; ++v) pw[v] = tid + v * TPB < u0 ? wbits[tid + v * TPB] : 0;
+#pragma unroll
+  for (int v = 0; v < UPT; ++v) c += __popcll(wd[v]);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wsum[v] : 0;
+  const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];  // rows of this split
+  const int off = before + incl - c;  // local position of this thread's first set bit
+
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  int gbase = -1;  // global list position of the split's first row, once known
+  if (total <= LIST_CAP) {
+    int pos = off;
+#pragma unroll
+    for (int v = 0; v < UPT; ++v) {
+      uint64_t m = wd[v];
+      while (m) {
+        s_list[pos++] = rb[v] + (__ffsll((unsigned long long)m) - 1);
+        m &= m - 1;
+      }
+    }
+    __syncthreads();
+    down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, total, acc);
+  } else {
+    // long split: windows of LIST_CAP, each published as it is expanded (global offset first)
+    int pc = 0;
+#pragma unroll
+    for (int v = 0; v < PFX; ++v) pc += __popcll(pw[v]);
+    const int pincl = wave_incl_scan(pc);
+    if (lane == 63) s_psum[wave] = pincl;
+    for (int wb = 0; wb < total; wb += LIST_CAP) {
+      const int wl = min(LIST_CAP, total - wb);
+      __syncthreads();
+      gbase = s_psum[0] + s_psum[1] + s_psum[2] + s_psum[3];
+      int pos = off;
+#pragma unroll
+      for (int v = 0; v < UPT; ++v) {
+        uint64_t m = wd[v];
+        while (m) {
+          if (pos >= wb && pos < wb + wl) s_list[pos - wb] = rb[v] + (__ffsll((unsigned long long)m) - 1);
+          m &= m - 1;
+          ++pos;
+        }
+      }
+      __syncthreads();
+      if (idx_out) {
+        for (int k = cb + tid * ncb; k < wl; k += TPB * ncb) {
+          idx_out[gbase + wb + k] = s_list[k];
+          if (tokmask_out) tokmask_out[gbase + wb + k] = 1;
+        }
+      }
+      down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, wl, acc);
+    }
+  }
+  // fixed-order reduction of the 32 row slots: lanes l and l+8 of each 16-lane row (DPP,
+  // complete in lanes 8..15), then the 4 rows of each wave and the 4 waves in order
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = dpp_add<dpp_shr(8)>(acc[e]);
+  if ((lane & 15) >= 8) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s_red[wave][lane >> 4][li][e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < COLS) {
+    const int c_li = tid / EPC, e = tid % EPC;
+    const int col = (cb * CB_LANES + c_li) * EPC + e;
+    if (col < d && (kq == 0 || total > 0)) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < TPB / 64; ++w2)
+#pragma unroll
+        for (int row = 0; row < 4; ++row) sum += s_red[w2][row][c_li][e];
+      if (kq == 0 && b_out) sum += b_out[col];
+      if (KS == 1)
+        y[col] = sum;
+      else
+        atomicAdd(y + col, sum);
+    }
+  }
+  // the list: this split's rows sit at global positions gbase + k (gbase = active neurons
+  // of all earlier ranges); workgroup cb publishes the positions k with k % ncb == cb
+  if (gbase < 0) {
+    int pc = 0;
+#pragma unroll
+    for (int v = 0; v < PFX; ++v) pc += __popcll(pw[v]);
+    const int pincl = wave_incl_scan(pc);
+    if (lane == 63) s_psum[wave] = pincl;
+    __syncthreads();
+    gbase = s_psum[0] + s_psum[1] + s_psum[2] + s_psum[3];
+    if (idx_out) {
+      for (int k = cb + tid * ncb; k < total; k += TPB * ncb) {
+        idx_out[gbase + k] = s_list[k];
+        if (tokmask_out) tokmask_out[gbase + k] = 1;
+      }
+    }
+  }
+  if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + total;
+}
+
+// y0: output of ny floats the down projection will add into (zeroed here), or null;
+// prefetch: extra workgroups pull the middle kernel's predictor rows and biases into cache
+template <bool F16, int NCPT>
+void stage1_launch_t(const LayerDev& L, const float* x, int B, hipStream_t s,
+                     const hipEvent_t* tev, float* y0, int ny, int g_pf) {
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  const dim3 grid(L.r + g_pf);
+  if (B == 1)
+    launch(k_pred_stage1<F16, 1, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
+           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
+  else
+    launch(k_pred_stage1<F16, 4, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
+           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
+}
+
+// prefetch workgroups are used when the ranges travel in the kernel arguments, a range's
+// predictor rows fit PF_PER_THREAD chunks per thread, and r keeps them on their consumer's
+// XCD
+int stage1_prefetch_groups(const LayerDev& L) {
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  if (!L.rs_in_arg || L.r % 8 != 0 || MID_RANGE_MAX * nchp > TPB * PF_PER_THREAD) return 0;
+  return L.g_mid;
+}
+
+template <bool F16>
+void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
+                   const hipEvent_t* tev = nullptr, float* y0 = nullptr, int ny = 0,
+                   bool prefetch = false) {
+  if (!y0) ny = 0;
+  const int g_pf = prefetch ? stage1_prefetch_groups(L) : 0;
+  const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
+  if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny, g_pf);
+  else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny, g_pf);
+  else if (ncpt <= 4) stage1_launch_t<F16, 4>(L, x, B, s, tev, y0, ny, g_pf);
+  else stage1_launch_t<F16, 8>(L, x, B, s, tev, y0, ny, g_pf);
+}
+
+template <bool F16, bool GATED, int CPT, int NCHP>
+void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                   const hipEvent_t* tev) {
+  launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), 0, s, tev, L.p2,
+         L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs,
+         L.wbits, L.h_buf, scores, L.ra);
+}
+
+template <bool F16, bool GATED, int CPT>
+bool mid_b1_dispatch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                     const hipEvent_t* tev) {
+  switch (L.r / (F16 ? 8 : 4)) {
+    case 8: mid_b1_launch<F16, GATED, CPT, 8>(L, x, scores, s, tev); return true;
+    case 16: mid_b1_launch<F16, GATED, CPT, 16>(L, x, scores, s, tev); return true;
+    case 32: mid_b1_launch<F16, GATED, CPT, 32>(L, x, scores, s, tev); return true;
+    case 64: mid_b1_launch<F16, GATED, CPT, 64>(L, x, scores, s, tev); return true;
+    case 128: mid_b1_launch<F16, GATED, CPT, 128>(L, x, scores, s, tev); return true;
+    default: return false;
+  }
+}
+
+template <bool F16, bool GATED, int CPT, int NCHP>
+int mid_b1_occ(size_t lds) {
+  int a = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, k_mid_b1<F16, GATED, CPT, NCHP>, TPB, lds) != hipSuccess) a = 0;
+  return a;
+}
+
+template <bool F16, bool GATED>
+bool mid_b1_any(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                const hipEvent_t* tev) {
+  switch (pick_cpt(row_chunks(L))) {
+    case 1: return mid_b1_dispatch<F16, GATED, 1>(L, x, scores, s, tev);
+    case 2: return mid_b1_dispatch<F16, GATED, 2>(L, x, scores, s, tev);
+    case 4: return mid_b1_dispatch<F16, GATED, 4>(L, x, scores, s, tev);
+    case 8: return mid_b1_dispatch<F16, GATED, 8>(L, x, scores, s, tev);
+    default: return false;
+  }
+}
+
+template <bool F16, bool GATED, int CPT>
+int mid_b1_occ_nchp(const LayerDev& L) {
+  switch (L.r / (F16 ? 8 : 4)) {
+    case 8: return mid_b1_occ<F16, GATED, CPT, 8>(0);
+    case 16: return mid_b1_occ<F16, GATED, CPT, 16>(0);
+    case 32: return mid_b1_occ<F16, GATED, CPT, 32>(0);
+    case 64: return mid_b1_occ<F16, GATED, CPT, 64>(0);
+    case 128: return mid_b1_occ<F16, GATED, CPT, 128>(0);
+    default: return -1;
+  }
+}
+
+template <bool F16, bool GATED>
+int mid_b1_occ_any(const LayerDev& L) {
+  switch (pick_cpt(row_chunks(L))) {
+    case 1: return mid_b1_occ_nchp<F16, GATED, 1>(L);
+    case 2: return mid_b1_occ_nchp<F16, GATED, 2>(L);
+    case 4: return mid_b1_occ_nchp<F16, GATED, 4>(L);
+    case 8: return mid_b1_occ_nchp<F16, GATED, 8>(L);
+    default: return -1;
+  }
+}
+
+template <bool F16, int UPT>
+void down_b1_launch(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
+                    float* y, hipStream_t s, const hipEvent_t* tev) {
+  launch(k_down_b1<F16, UPT>, dim3(down_blocks(L) * L.ks_down), dim3(TPB), (size_t)LIST_CAP * 4,
+         s, tev, L.w_down_t, L.b_out, L.h_buf, L.d, L.n, L.wbits, L.rs, L.ks_down,
+         down_blocks(L), idx_out, count_out, tok_out, y, L.sa);
+}
+
+template <bool F16>
+void down_b1_any(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
+                 float* y, hipStream_t s, const hipEvent_t* tev) {
+  switch (L.split_upt) {
+    case 1: down_b1_launch<F16, 1>(L, idx_out, count_out, tok_out, y, s, tev); break;
+    case 2: down_b1_launch<F16, 2>(L, idx_out, count_out, tok_out, y, s, tev); break;
+    case 4: down_b1_launch<F16, 4>(L, idx_out, count_out, tok_out, y, s, tev); break;
+    default: down_b1_launch<F16, 8>(L, idx_out, count_out, tok_out, y, s, tev); break;
+  }
+}
+
+}  // namespace
+
+void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
+                float* y0, int ny, bool prefetch) {
+  if (L.p_f16)
+    stage1_launch<true>(L, x, B, s, tev, y0, ny, prefetch);
+  else
+    stage1_launch<false>(L, x, B, s, tev, y0, ny, prefetch);
+}
+
+bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                const hipEvent_t* tev) {
+  if (L.w_f16 != L.p_f16) return false;
+  if (L.w_f16) return L.gated ? mid_b1_any<true, true>(L, x, scores, s, tev) : mid_b1_any<true, false>(L, x, scores, s, tev);
+  return L.gated ? mid_b1_any<false, true>(L, x, scores, s, tev) : mid_b1_any<false, false>(L, x, scores, s, tev);
+}
+
+int occ_mid_b1(const LayerDev& L) {
+  if (L.w_f16 != L.p_f16) return -1;
+  if (L.w_f16) return L.gated ? mid_b1_occ_any<true, true>(L) : mid_b1_occ_any<true, false>(L);
+  return L.gated ? mid_b1_occ_any<false, true>(L) : mid_b1_occ_any<false, false>(L);
+}
+
+void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
+                 float* y, hipStream_t s, const hipEvent_t* tev) {
+  if (L.w_f16)
+    down_b1_any<true>(L, idx_out, count_out, tok_out, y, s, tev);
+  else
+    down_b1_any<false>(L, idx_out, count_out, tok_out, y, s, tev);
+}
+
+}  // namespace sffn

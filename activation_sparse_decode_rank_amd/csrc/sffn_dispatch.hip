@@ -1,0 +1,135 @@
+// Host dispatch of the activation-sparse FFN decode library: workspace carve-up, launch
+// geometry, and which kernels run for each entry point and batch size.
+#include "sffn_device.h"
+
+namespace sffn {
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int d, int n, int r, int max_batch) {
+  (void)d;
+  const int n_tiles = (n + TPB - 1) / TPB;
+  size_t b = 0;
+  b += align256((size_t)max_batch * r * 4);      // q
+  b += align256((size_t)((n + 63) / 64 * 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
+  b += align256((size_t)n * 8);                  // tok_full
+  b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
+  b += align256((size_t)n_tiles * 4);            // tile_cnt
+  b += align256((size_t)((n + 63) / 64) * 8);    // words
+  b += align256((size_t)G_MID_MAX * 8);          // wbits
+  return b;
+}
+
+void carve_workspace(LayerDev& L, void* ws, int max_batch) {
+  char* p = static_cast<char*>(ws);
+  const int n = L.n;
+  const int n_tiles = (n + TPB - 1) / TPB;
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  L.q = reinterpret_cast<float*>(take((size_t)max_batch * L.r * 4));
+  L.ldh = (n + 63) / 64 * 64;
+  L.h_buf = reinterpret_cast<float*>(take((size_t)L.ldh * max_batch * 4));
+  L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
+  L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
+  L.tile_cnt = reinterpret_cast<int32_t*>(take((size_t)n_tiles * 4));
+  L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
+  L.wbits = reinterpret_cast<uint64_t*>(take((size_t)G_MID_MAX * 8));
+  L.n_tiles = n_tiles;
+}
+
+namespace {
+
+// the batch path needs fp16 weights and quarters of the input width in whole k-steps
+bool tile_ok(const LayerDev& L, int B) {
+  return B >= TILE_MIN_B && L.w_f16 && L.d % 128 == 0 && B <= MAXB;
+}
+
+}  // namespace
+
+int down_blocks(const LayerDev& L) {
+  const int nch = L.d / (L.w_f16 ? 8 : 4);
+  return (nch + CB_LANES - 1) / CB_LANES;
+}
+
+int tile_split(const LayerDev& L, bool deterministic) {
+  const int ncb = (L.d + 63) / 64;
+  int ks = std::max(1, std::min(8, (L.n_cus + ncb / 2) / ncb));
+  if (deterministic) ks = std::min(ks, 2);
+  return ks;
+}
+
+int down_split(const LayerDev& L, bool deterministic) {
+  const int ncb = down_blocks(L);
+  int ks = std::max(1, std::min(8, (L.n_cus + ncb / 2) / ncb));
+  if (deterministic) ks = std::min(ks, 2);
+  return ks;
+}
+
+int mid_resident_groups(const LayerDev& L, int max_batch) {
+  if (pick_cpt(row_chunks(L)) == 0 || L.w_f16 != L.p_f16) return 0;
+  int occ1 = occ_mid_b1(L);
+  if (occ1 < 0) occ1 = occ_mid_batch(L, 1);
+  const int occb = max_batch > 1 ? occ_mid_batch(L, std::min(max_batch, TILE_MIN_B - 1)) : occ1;
+  return std::min(occ1, occb) * L.n_cus;
+}
+
+bool shape_supported(const LayerDev& L, bool fused) {
+  if (pick_cpt(row_chunks(L)) == 0) return false;
+  const int nchp = L.r / (L.p_f16 ? 8 : 4);
+  if (nchp > 256) return false;
+  const int epc_p = L.p_f16 ? 8 : 4;
+  if (L.d / epc_p > 8 * TPB) return false;  // stage 1 register budget
+  if (fused) {
+    if (L.w_f16 != L.p_f16) return false;
+    if (nchp > 128 || (nchp & (nchp - 1)) != 0) return false;  // P2 row = power-of-two chunks
+    if (L.g_mid < 1 || L.g_mid > G_MID_MAX) return false;
+    if (L.split_upt < 1 || L.split_upt > 8) return false;  // the down kernel's word registers
+    if (L.ks_down < 1 || L.ks_down > KS_MAX) return false;
+  }
+  return true;
+}
+
+hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
+  run_stage1(L, x, B, s, nullptr, nullptr, 0, false);
+  return run_scores(L, B, scores, s);
+}
+
+hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                          const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s) {
+  if (tile_ok(L, B)) {
+    run_forward_tiles(L, x, B, idx, count, tokmask, y, true, s, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  run_gather(L, x, B, idx, count, tokmask, y, s);
+  run_down(L, B, false, idx, count, nullptr, nullptr, nullptr, y, s, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
+                         int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
+                         const hipEvent_t* ev) {
+  const hipEvent_t* t1 = ev ? ev + 0 : nullptr;
+  const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
+  const hipEvent_t* t3 = ev ? ev + 4 : nullptr;
+  if (tile_ok(L, B)) {
+    // predictor, threshold and union compaction as separate kernels, then the tiles; the
+    // scores go to the caller's buffer or, when none is given, to the activation buffer,
+    // which the up projection only overwrites after compaction has read them
+    float* sc = scores ? scores : L.h_buf;
+    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false);
+    hipError_t e = run_scores(L, B, sc, s);
+    if (e != hipSuccess) return e;
+    e = launch_compact(L, sc, B, idx, count, tokmask, s);
+    if (e != hipSuccess) return e;
+    run_forward_tiles(L, x, B, idx, count, tokmask, y, false, s, t2, t3);
+    return hipGetLastError();
+  }
+  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true);
+  if (B == 1 && run_mid_b1(L, x, scores, s, t2)) {
+    run_down_b1(L, idx, count, tokmask, y, s, t3);
+    return hipGetLastError();
+  }
+  run_mid_batch(L, x, B, scores, s, t2);
+  run_down(L, B, true, nullptr, nullptr, idx, count, tokmask, y, s, t3);
+  return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -1,5 +1,6 @@
-// Internal interface between the C-ABI host code (sffn_api.hip) and the kernels
-// (sffn_kernels.hip). Not installed; the public interface is include/sparse_ffn.h.
+// Internal interface between the C-ABI host code (sffn_api.hip), the host dispatch
+// (sffn_dispatch.hip) and the kernel translation units. Not installed; the public
+// interface is include/sparse_ffn.h.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -72,6 +73,50 @@ int tile_split(const LayerDev& L, bool deterministic);
 bool shape_supported(const LayerDev& L, bool fused);
 // middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch
 int mid_resident_groups(const LayerDev& L, int max_batch);
+
+// From this many tokens on (fp16 weights, d a multiple of 128) the decode and forward
+// entry points run the gathered-tile matrix-core kernels.
+constexpr int TILE_MIN_B = 9;
+
+// Kernel-family entry points (one translation unit each; tev: an optional start/end event
+// pair stamped by the dispatch).
+// sffn_decode_b1.hip: predictor stage 1 (y0/ny: output zeroed for the split-k down
+// projection; prefetch: also pull the middle kernel's first loads into cache), the batch-1
+// middle kernel (false when no kernel exists for the shape) and down projection.
+void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
+                float* y0, int ny, bool prefetch);
+bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
+                const hipEvent_t* tev);
+int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 kernel applies
+void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
+                 float* y, hipStream_t s, const hipEvent_t* tev);
+// sffn_batch.hip: the middle kernel for any batch (small-batch kernel for 2..8 tokens,
+// otherwise the general fused one), the down projection (bits: the decode step's list from
+// the range activity words; otherwise the given idx/count), and the forward's gather.
+void run_mid_batch(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s,
+                   const hipEvent_t* tev);
+int occ_mid_batch(const LayerDev& L, int B);
+void run_down(const LayerDev& L, int B, bool bits, const int32_t* idx, const int32_t* count,
+              int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y, hipStream_t s,
+              const hipEvent_t* tev);
+void run_gather(const LayerDev& L, const float* x, int B, const int32_t* idx, const int32_t* count,
+                const uint64_t* tokmask, float* y0, hipStream_t s);
+// sffn_mid_bt_{h,f}{4,8}.hip: the small-batch middle kernel for fp16 (h) or fp32 (f)
+// weights and up to 4 or 8 tokens (false / -1 when no kernel exists for the shape)
+bool run_mid_bt_h4(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s, const hipEvent_t* tev);
+bool run_mid_bt_h8(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s, const hipEvent_t* tev);
+bool run_mid_bt_f4(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s, const hipEvent_t* tev);
+bool run_mid_bt_f8(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s, const hipEvent_t* tev);
+int occ_mid_bt_h4(const LayerDev& L);
+int occ_mid_bt_h8(const LayerDev& L);
+int occ_mid_bt_f4(const LayerDev& L);
+int occ_mid_bt_f8(const LayerDev& L);
+// sffn_tiles.hip: predictor stage 2 scores, and the matrix-core forward (zero_y: clear y
+// first when the down projection splits rows)
+hipError_t run_scores(const LayerDev& L, int B, float* scores, hipStream_t s);
+void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                       const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
+                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down);
 
 // launchers; each returns hipGetLastError() after enqueueing
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s);

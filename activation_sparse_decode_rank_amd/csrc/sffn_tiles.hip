@@ -1,0 +1,460 @@
+// Predictor scores, threshold and compaction as separate kernels (the standalone entry
+// points and the batch path), and the gathered-tile up and down projections on the matrix
+// cores for batches of 9 or more tokens (gfx950).
+#include "sffn_device.h"
+
+namespace sffn {
+namespace {
+
+// scores[b][i] = P2[i] . q_b + c_i for rows [row_begin, row_end) of this workgroup.
+template <bool PF16, int L, int CPLP, int PASSES>
+__global__ __launch_bounds__(TPB) void k_pred_scores(const void* __restrict__ p2,
+                                                     const float* __restrict__ pbias,
+                                                     const float* __restrict__ q, int n, int r,
+                                                     int B, float* __restrict__ scores) {
+  constexpr int EPC = Elt<PF16>::EPC;
+  constexpr int RPP = TPB / L;
+  const int tid = threadIdx.x;
+  const int g = tid / L, gl = tid % L;
+  const int nchp = r / EPC;
+  const int row_base = blockIdx.x * RPP * PASSES;
+  u32x4 wv[PASSES][CPLP];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = row_base + p * RPP + g;
+#pragma unroll
+    for (int m = 0; m < CPLP; ++m) {
+      const int c = gl + m * L;
+      if (row < n && c < nchp) wv[p][m] = ld_chunk(p2, (size_t)row * nchp + c);
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    float qs[CPLP][EPC];
+#pragma unroll
+    for (int m = 0; m < CPLP; ++m) {
+      const int c = gl + m * L;
+      if (c < nchp) load_x<EPC>(q + (size_t)b * r + (size_t)c * EPC, qs[m]);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = row_base + p * RPP + g;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < CPLP; ++m) {
+        const int c = gl + m * L;
+        if (c < nchp && row < n) acc = dot_chunk<PF16>(wv[p][m], qs[m], acc);
+      }
+      acc = group_sum<L>(acc);
+      if (gl == group_leader(L) && row < n) scores[(size_t)b * n + row] = acc + (pbias ? pbias[row] : 0.f);
+    }
+  }
+}
+
+// ============================================================================ compaction
+// Pass 1, one thread per neuron, 256-neuron tiles: token bits, union ballot words, and
+// the tile's active count.
+__global__ __launch_bounds__(TPB) void k_cmp_tiles(const float* __restrict__ scores, int n,
+                                                   int B, float tau,
+                                                   uint64_t* __restrict__ tok_full,
+                                                   uint64_t* __restrict__ words,
+                                                   int32_t* __restrict__ tile_cnt) {
+  __shared__ int s_cnt[TPB / 64];
+  const int i = blockIdx.x * TPB + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t bits = 0;
+  if (i < n)
+    for (int b = 0; b < B; ++b)
+      if (scores[(size_t)b * n + i] > tau) bits |= (uint64_t)1 << b;  // NaN compares false
+  const uint64_t word = __ballot(bits != 0);
+  if (i < n) tok_full[i] = bits;
+  if (lane == 0) {
+    if (i < n) words[i >> 6] = word;
+    s_cnt[wave] = __popcll(word);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) tile_cnt[blockIdx.x] = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+}
+
+// Pass 2, same tiling: exclusive prefix of the tile counts, then every active neuron
+// writes itself at its ascending position. The last tile writes the total.
+__global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict__ tok_full,
+                                                     const uint64_t* __restrict__ words,
+                                                     const int32_t* __restrict__ tile_cnt, int n,
+                                                     int n_tiles, int32_t* __restrict__ idx,
+                                                     int32_t* __restrict__ count,
+                                                     uint64_t* __restrict__ tokmask) {
+  __shared__ int s_off;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < 64) {
+    int acc = 0;
+    for (int u = lane; u < t; u += 64) acc += tile_cnt[u];
+    acc = wave_incl_scan(acc);
+    if (lane == 63) s_off = acc;
+  }
+  __syncthreads();
+  const int i = t * TPB + threadIdx.x;
+  if (i < n) {
+    const uint64_t word = words[i >> 6];
+    if ((word >> lane) & 1) {
+      int before = 0;
+      for (int v = 0; v < wave; ++v) before += __popcll(words[t * 4 + v]);
+      const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+      const int k = s_off + before + __popcll(lower);
+      idx[k] = i;
+      if (tokmask) tokmask[k] = tok_full[i];
+    }
+  }
+  if (t == n_tiles - 1 && threadIdx.x == 0) *count = s_off + tile_cnt[t];
+}
+
+// ============================================================================ batch tiles
+// From TILE_MIN_B tokens on, the union rows form dense tiles and the products go to the
+// matrix cores: v_mfma_f32_16x16x32_f16 multiplies a 16x32 fp16 tile by a 32x16 fp16 tile
+// into 16x16 fp32 accumulators (lane l holds row l%16, k 8*(l/16)..+7 of the left operand,
+// column l%16 and the same k of the right one; the result lands as column l%16, rows
+// 4*(l/16)..+3). Weights are fp16 as stored; fp32 activations enter as a hi + lo pair of
+// fp16 values (v = hi + lo to about 22 significant bits), two products per tile.
+
+__device__ __forceinline__ void split_hi_lo(const float4_t& a, const float4_t& b, half8_t& hi,
+                                            half8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 ha = (_Float16)a[e], hb = (_Float16)b[e];
+    hi[e] = ha;
+    hi[4 + e] = hb;
+    lo[e] = (_Float16)(a[e] - (float)ha);
+    lo[4 + e] = (_Float16)(b[e] - (float)hb);
+  }
+}
+
+__device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Up projection over the union list, one tile of 16 listed neurons x all B tokens per
+// workgroup iteration: wave w sums input columns [w*d/4, (w+1)*d/4), the four partial
+// tiles are added in wave order through LDS, then wave 0 applies bias, ReLU (gated: times
+// the up tile), the token bits, and writes hT[b*ldh + p] (token-major, for the down
+// projection's left operand). Loads for KB k-steps are issued before their products.
+template <bool GATED, int NT>
+__global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
+                                                 const float* __restrict__ b_act,
+                                                 const float* __restrict__ x, int d, int n, int B,
+                                                 const int32_t* __restrict__ idx,
+                                                 const int32_t* __restrict__ count,
+                                                 const uint64_t* __restrict__ tokmask,
+                                                 float* __restrict__ hT, int ldh,
+                                                 float* __restrict__ y0, int ny) {
+  constexpr int KB = NT <= 2 ? 4 : 2;  // k-steps per load batch
+  constexpr int NM = GATED ? 2 : 1;
+  __shared__ float4_t s_acc[TPB / 64][NM][NT][64];
+  zero_grid(y0, ny);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int cnt = min(max(*count, 0), n);
+  const int nch = d / 8;
+  const int rowch = GATED ? 2 * nch : nch;
+  const int kq_len = d / 4;
+  const int ksteps = kq_len / 32;
+  const int kbase = wave * kq_len + 8 * g;
+  const float* xr[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) xr[tt] = x + (size_t)min(tt * 16 + r16, B - 1) * d;
+  for (int t = blockIdx.x; t * 16 < cnt; t += gridDim.x) {
+    const int i = idx[min(t * 16 + r16, cnt - 1)];
+    const u32x4* wrow =
+        reinterpret_cast<const u32x4*>(w_act) + (size_t)((i >= 0 && i < n) ? i : 0) * rowch;
+    float4_t acc[NM][NT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ksteps; s0 += KB) {
+      u32x4 a[KB][NM];
+      float4_t xv[KB][NT][2];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int k = kbase + min(s0 + u, ksteps - 1) * 32;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) a[u][m] = wrow[m * nch + k / 8];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          xv[u][tt][0] = *reinterpret_cast<const float4_t*>(xr[tt] + k);
+          xv[u][tt][1] = *reinterpret_cast<const float4_t*>(xr[tt] + k + 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (s0 + u < ksteps) {
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            half8_t hi, lo;
+            split_hi_lo(xv[u][tt][0], xv[u][tt][1], hi, lo);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              const half8_t w8 = __builtin_bit_cast(half8_t, a[u][m]);
+              acc[m][tt] = mfma16(w8, hi, acc[m][tt]);
+              acc[m][tt] = mfma16(w8, lo, acc[m][tt]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) s_acc[wave][m][tt][lane] = acc[m][tt];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        float4_t v[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+          v[m] = ((s_acc[0][m][tt][lane] + s_acc[1][m][tt][lane]) + s_acc[2][m][tt][lane]) +
+                 s_acc[3][m][tt][lane];
+        const int b = tt * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = t * 16 + 4 * g + j;
+          if (p < cnt && b < B) {
+            const int ij = idx[p];
+            const bool ok = ij >= 0 && ij < n;
+            const float a0 = v[0][j] + ((ok && b_act) ? b_act[ij] : 0.f);
+            float h = a0 > 0.f ? a0 : 0.f;
+            if (GATED) h *= v[NM - 1][j];
+            const bool on = !tokmask || ((tokmask[p] >> b) & 1);
+            hT[(size_t)b * ldh + p] = (ok && on) ? h : 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Down projection at batch: Y[b][c] += sum_p hT[b][p] * W_down^T[idx_p][c]. Workgroup
+// (cb, kq) owns the 64-column block cb and positions [p0, p1) (a multiple of DCH per split,
+// so hT chunks stay 16-byte aligned). Per chunk of DCH positions the 256 threads load the
+// weight tile (16-byte row pieces) and the activation tile into registers, then write the
+// weights transposed into LDS (column-major: the right operand wants 8 consecutive
+// positions of one column per lane) and the activations as hi/lo fp16; wave w multiplies
+// its 16 columns for every 16-token tile. Loads run PF chunks ahead through a register
+// ring. Sums leave as in k_down: plain store for KS == 1, else float atomics onto y zeroed
+// earlier in the call, b_out riding on kq == 0.
+constexpr int DCH = 64;
+constexpr int DCH_P = DCH + 8;  // LDS row pitch in halfs (keeps 16-byte alignment)
+constexpr int IDX_CAP = 4096;   // list window held in LDS (a multiple of DCH)
+
+template <int NT, int PF>
+__global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_down_t,
+                                                   const float* __restrict__ b_out,
+                                                   const float* __restrict__ hT, int ldh, int d,
+                                                   int n, int B, const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ count, int KS,
+                                                   float* __restrict__ y) {
+  constexpr int AV = NT;  // float4 activation loads per thread per chunk (NT*16 tokens x 64 positions)
+  __shared__ __attribute__((aligned(16))) _Float16 s_w[64][DCH_P];
+  __shared__ __attribute__((aligned(16))) _Float16 s_a[2][NT * 16][DCH_P];
+  __shared__ int32_t s_idx[IDX_CAP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nch = d / 8;
+  const int ncb = gridDim.x / KS;
+  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
+  const int cnt = min(max(*count, 0), n);
+  const int per = (((cnt + KS - 1) / KS) + DCH - 1) / DCH * DCH;
+  const int p0 = min(cnt, kq * per), p1 = min(cnt, p0 + per);
+  // this thread's pieces of a chunk
+  const int wrow = tid >> 3, wcc = tid & 7;  // weight rows wrow and wrow + 32, chunk wcc
+  const int wchunk = min(cb * 8 + wcc, nch - 1);
+  int atok[AV], aq[AV];
+#pragma unroll
+  for (int u = 0; u < AV; ++u) {
+    const int e = tid + u * TPB;
+    atok[u] = e >> 4;
+    aq[u] = e & 15;
+  }
+
+  u32x4 wr[PF][2];
+  float4_t ar[PF][AV];
+  int wi[PF][2];
+  // list ids come from the LDS window (position slot_pc - wb), so no weight load waits on
+  // a global index load
+  int wb = p0, wl = 0, last_pc = p0;
+  auto issue = [&](int slot_pc, u32x4* wslot, float4_t* aslot, int* islot) {
+    slot_pc = min(slot_pc, last_pc);  // chunks past the end re-read the last one (zeroed later)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = s_idx[min(slot_pc - wb + wrow + 32 * u, wl - 1)];
+      islot[u] = i;
+      wslot[u] = ld_chunk(w_down_t, (size_t)((i >= 0 && i < n) ? i : 0) * nch + wchunk);
+    }
+#pragma unroll
+    for (int u = 0; u < AV; ++u) {
+      const int b = min(atok[u], B - 1);
+      aslot[u] = *reinterpret_cast<const float4_t*>(hT + (size_t)b * ldh + slot_pc + 4 * aq[u]);
+    }
+  };
+  auto stash = [&](int slot_pc, const u32x4* wslot, const float4_t* aslot, const int* islot) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = wrow + 32 * u;
+      const bool ok = slot_pc + r < p1 && islot[u] >= 0 && islot[u] < n && cb * 8 + wcc < nch;
+      const half8_t h = __builtin_bit_cast(half8_t, wslot[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_w[wcc * 8 + e][r] = ok ? h[e] : (_Float16)0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < AV; ++u) {
+      const int b = atok[u], q = aq[u];
+      float4_t v = aslot[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (b >= B || slot_pc + 4 * q + e >= p1) v[e] = 0.f;
+      half8_t hi, lo;
+      split_hi_lo(v, v, hi, lo);
+      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<half4_t*>(&s_a[0][b][4 * q]) = half4_t{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<half4_t*>(&s_a[1][b][4 * q]) = half4_t{lo[0], lo[1], lo[2], lo[3]};
+    }
+  };
+
+  float4_t acc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (wb = p0; wb < p1; wb += IDX_CAP) {
+    wl = min(IDX_CAP, p1 - wb);
+    __syncthreads();
+    for (int k = tid; k < wl; k += TPB) s_idx[k] = idx[wb + k];
+    __syncthreads();
+    const int nchunks = (wl + DCH - 1) / DCH;
+    last_pc = wb + (nchunks - 1) * DCH;
+    // branch-free ring: rounds of PF chunks; chunks past the end contribute zeros
+#pragma unroll
+    for (int sl = 0; sl < PF; ++sl) issue(wb + sl * DCH, wr[sl], ar[sl], wi[sl]);
+    for (int c0 = 0; c0 < nchunks; c0 += PF) {
+#pragma unroll
+      for (int sl = 0; sl < PF; ++sl) {
+        const int c = c0 + sl;
+        {
+          __syncthreads();
+          stash(wb + c * DCH, wr[sl], ar[sl], wi[sl]);
+          __syncthreads();
+          issue(wb + (c + PF) * DCH, wr[sl], ar[sl], wi[sl]);
+#pragma unroll
+        for (int ks = 0; ks < DCH / 32; ++ks) {
+          const half8_t bw = *reinterpret_cast<const half8_t*>(&s_w[16 * wave + r16][32 * ks + 8 * g]);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            const half8_t ah = *reinterpret_cast<const half8_t*>(&s_a[0][16 * tt + r16][32 * ks + 8 * g]);
+            const half8_t al = *reinterpret_cast<const half8_t*>(&s_a[1][16 * tt + r16][32 * ks + 8 * g]);
+            acc[tt] = mfma16(ah, bw, acc[tt]);
+            acc[tt] = mfma16(al, bw, acc[tt]);
+          }
+        }
+        }
+      }
+    }
+  }
+  const int col = cb * 64 + 16 * wave + r16;
+  if (col < d && (kq == 0 || p1 > p0)) {
+    const float bo = (kq == 0 && b_out) ? b_out[col] : 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = tt * 16 + 4 * g + j;
+        if (b < B) {
+          const float v = acc[tt][j] + bo;
+          float* dst = y + (size_t)b * d + col;
+          if (KS == 1)
+            *dst = v;
+          else
+            atomicAdd(dst, v);
+        }
+      }
+  }
+}
+
+template <bool F16>
+hipError_t scores_launch(const LayerDev& L, int B, float* scores, hipStream_t s) {
+  const int nchp = L.r / (F16 ? 8 : 4);
+  int Lw, cplp;
+  pick_group(nchp, Lw, cplp);
+  constexpr int PASSES = 4;
+  const int rows_per_wg = (TPB / Lw) * PASSES;
+  const dim3 grid((L.n + rows_per_wg - 1) / rows_per_wg);
+#define SCORES(LL, CC)                                                                       \
+  hipLaunchKernelGGL((k_pred_scores<F16, LL, CC, PASSES>), grid, dim3(TPB), 0, s, L.p2,      \
+                     L.p_bias, L.q, L.n, L.r, B, scores)
+  if (Lw == 8) SCORES(8, 1);
+  else if (Lw == 16) SCORES(16, 1);
+  else if (Lw == 32) SCORES(32, 1);
+  else if (cplp == 1) SCORES(64, 1);
+  else if (cplp == 2) SCORES(64, 2);
+  else SCORES(64, 4);
+#undef SCORES
+  return hipGetLastError();
+}
+
+template <bool GATED>
+void up_tile_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                    const int32_t* count, const uint64_t* tokmask, float* y0, int ny,
+                    hipStream_t s, const hipEvent_t* tev) {
+  const dim3 grid(L.g_up);
+  switch ((B + 15) / 16) {
+    case 1: launch(k_up_mfma<GATED, 1>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    case 2: launch(k_up_mfma<GATED, 2>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    case 3: launch(k_up_mfma<GATED, 3>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    default: launch(k_up_mfma<GATED, 4>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+  }
+}
+
+void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                      float* y, hipStream_t s, const hipEvent_t* tev) {
+  const dim3 grid(((L.d + 63) / 64) * L.ks_tile);
+  switch ((B + 15) / 16) {
+    case 1: launch(k_down_mfma<1, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 2: launch(k_down_mfma<2, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 3: launch(k_down_mfma<3, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    default: launch(k_down_mfma<4, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+  }
+}
+
+// union-list forward on the matrix cores; y is zeroed by the up kernel when the down
+// projection splits rows
+void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                   const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
+                   hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
+  const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
+  if (L.gated)
+    up_tile_launch<true>(L, x, B, idx, count, tokmask, y, ny, s, t_up);
+  else
+    up_tile_launch<false>(L, x, B, idx, count, tokmask, y, ny, s, t_up);
+  down_tile_launch(L, B, idx, count, y, s, t_down);
+}
+
+}  // namespace
+
+hipError_t run_scores(const LayerDev& L, int B, float* scores, hipStream_t s) {
+  return L.p_f16 ? scores_launch<true>(L, B, scores, s) : scores_launch<false>(L, B, scores, s);
+}
+
+hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t* idx,
+                          int32_t* count, uint64_t* tokmask, hipStream_t s) {
+  hipLaunchKernelGGL(k_cmp_tiles, dim3(L.n_tiles), dim3(TPB), 0, s, scores, L.n, B, L.tau,
+                     L.tok_full, L.words, L.tile_cnt);
+  hipLaunchKernelGGL(k_cmp_scatter, dim3(L.n_tiles), dim3(TPB), 0, s, L.tok_full, L.words,
+                     L.tile_cnt, L.n, L.n_tiles, idx, count, tokmask);
+  return hipGetLastError();
+}
+
+void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
+                       const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
+                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
+  forward_tiles(L, x, B, idx, count, tokmask, y, zero_y, s, t_up, t_down);
+}
+
+}  // namespace sffn

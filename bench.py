@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the part
-TILE_MIN_B = 16                # from this batch on the decode step runs the matrix-core kernels
+TILE_MIN_B = 9                 # from this batch on the decode step runs the matrix-core kernels
 METRIC = "sparse FFN decode µs/layer + active-weight HBM GB/s vs peak, 10% activity"
 
 
@@ -80,8 +80,14 @@ class HipEvents:
 
 
 def kernel_source_sha():
-    src = os.path.join(ROOT, "activation_sparse_decode_rank_amd", "csrc", "sffn_kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    """sha256 over the library's device and host sources (sorted by name)."""
+    csrc = os.path.join(ROOT, "activation_sparse_decode_rank_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel_file, workload):

@@ -116,12 +116,18 @@ SHAPES = [
     ("C3", 512, 1100, 64, 4),
     ("C5", 1024, 2100, 256, 1),
     ("C2", 4096, 1500, 256, 2),
-    # batches of 16 and more take the matrix-core tile path (fp16, d a multiple of 128)
+    # 5..8 tokens: the small-batch middle kernel's 8-token form and 8-token down projection
+    ("C3", 512, 1100, 64, 6),
+    ("C2", 1024, 2000, 128, 8),
+    ("C1", 768, 3072, 64, 5),       # fp32 weights
+    # batches of 9 and more take the matrix-core tile path (fp16, d a multiple of 128)
+    ("C2", 512, 1000, 64, 9),
     ("C3", 512, 1100, 64, 16),
     ("C2", 1024, 3000, 128, 32),
     ("C3", 256, 777, 64, 20),       # ragged token tile
     ("C2", 512, 2000, 64, 64),
     ("C3", 520, 900, 64, 16),       # d not a multiple of 128: the vector path at batch 16
+    ("C2", 264, 700, 64, 12),       # the vector path at 12 tokens (two 8-token groups)
 ]
 
 
