@@ -119,7 +119,7 @@ def kernel_names(cfg, B):
             "down_tiles": "k_down_mfma (gathered-tile down projection on the matrix cores)"}
     return ("stage1", "mid", "down"), {
         "stage1": "k_pred_stage1 (predictor stage 1, q = P1 x)",
-        "mid": ("k_mid_b1" if B == 1 else "k_fused_mid")
+        "mid": ("k_mid_b1" if B == 1 else "k_mid_bt" if B <= 8 else "k_fused_mid")
         + " (predictor stage 2 + threshold + compaction + gather-GEMV/ReLU)",
         "down": ("k_down_b1" if B == 1 else "k_down") + " (down projection over the active rows)"}
 
