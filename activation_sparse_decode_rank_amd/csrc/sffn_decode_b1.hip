@@ -1,96 +1,10 @@
-// Batch-1 decode kernels (gfx950): predictor stage 1 with the prefetch of the middle
-// kernel's first loads, the fused middle kernel (predictor stage 2, threshold, per-range
-// compaction, gather-GEMV + ReLU) and the single-token down projection. The method is
+// Batch-1 decode kernels (gfx950): the fused middle kernel (predictor stage 2, threshold,
+// per-range compaction, gather-GEMV + ReLU) and the single-token down projection. The method is
 // described at the top of sffn_device.h.
 #include "sffn_device.h"
 
 namespace sffn {
 namespace {
-
-// ============================================================================ predictor
-// Stage 1: q[b][j] = P1[j] . x_b. Workgroup j < r owns predictor row j; each thread holds
-// NCPT chunks of the row in registers and reuses them for every token group of TBG. In the
-// decode step these workgroups also clear y (ny floats), which the down projection later
-// adds its split-k sums into.
-// Workgroups r .. r + g_pf - 1 only prefetch: workgroup r + w reads middle-kernel range w's
-// rows of the predictor's second-stage matrix p2 (NCHP chunks per row) and its two bias
-// entries per neuron, so that the middle kernel's first loads hit cache instead of HBM.
-// Those addresses are static, so their latency overlaps this kernel's own. Workgroups are
-// dealt to the XCDs round-robin by id, and r is a multiple of 8, so workgroup r + w shares
-// an XCD (and its L2) with middle workgroup w. Every prefetch load is issued before any
-// wait; the values are folded into a register that an empty asm consumes, so the loads
-// stay and nothing is stored.
-constexpr int PF_PER_THREAD = 8;
-template <bool PF16, int TBG, int NCPT>
-__global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
-                                                     const float* __restrict__ x, int d, int r,
-                                                     int B, float* __restrict__ q,
-                                                     float* __restrict__ y0, int ny,
-                                                     const void* __restrict__ p2, int nchp,
-                                                     const float* __restrict__ pfb0,
-                                                     const float* __restrict__ pfb1,
-                                                     const RangeArg ra) {
-  constexpr int EPC = Elt<PF16>::EPC;
-  touch_kernargs<2>();
-  const int j = blockIdx.x, tid = threadIdx.x;
-  if (j >= r) {
-    const int w = j - r;
-    const int r0 = ra.r[w], r1 = ra.r[w + 1];
-    const int c0 = r0 * nchp, nc = (r1 - r0) * nchp;
-    u32x4 pv[PF_PER_THREAD];
-#pragma unroll
-    for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = ld_chunk(p2, c0 + min(tid + v * TPB, nc - 1));
-    float b0 = 0.f, b1 = 0.f;
-    if (tid < r1 - r0) {
-      if (pfb0) b0 = pfb0[r0 + tid];
-      if (pfb1) b1 = pfb1[r0 + tid];
-    }
-    unsigned sink = __float_as_uint(b0) ^ __float_as_uint(b1);
-#pragma unroll
-    for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v].x;
-    asm volatile("" ::"v"(sink));
-    return;
-  }
-  for (int i = j * TPB + tid; i < ny; i += r * TPB) y0[i] = 0.f;
-  const int nch = d / EPC;
-  const size_t row0 = (size_t)j * nch;
-  __shared__ float red[TPB / 64][MAXB];
-  u32x4 wv[NCPT];
-#pragma unroll
-  for (int m = 0; m < NCPT; ++m) {
-    const int c = tid + m * TPB;
-    if (c < nch) wv[m] = ld_stream(p1, row0 + c);
-  }
-  for (int b0 = 0; b0 < B; b0 += TBG) {
-    float acc[TBG];
-#pragma unroll
-    for (int b = 0; b < TBG; ++b) acc[b] = 0.f;
-#pragma unroll
-    for (int m = 0; m < NCPT; ++m) {
-      const int c = tid + m * TPB;
-      if (c < nch) {
-        float f[EPC];
-        unpack<PF16>(wv[m], f);
-#pragma unroll
-        for (int b = 0; b < TBG; ++b) {
-          if (b0 + b < B) {
-            float xs[EPC];
-            load_x<EPC>(x + (size_t)(b0 + b) * d + (size_t)c * EPC, xs);
-#pragma unroll
-            for (int e2 = 0; e2 < EPC; ++e2) acc[b] = fmaf(f[e2], xs[e2], acc[b]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < TBG; ++b) acc[b] = wave_sum(acc[b]);
-#pragma unroll
-    for (int b = 0; b < TBG; ++b)
-      if ((tid & 63) == WAVE_SUM_LANE && b0 + b < B) red[tid >> 6][b0 + b] = acc[b];
-  }
-  __syncthreads();
-  if (tid < B) q[(size_t)tid * r + j] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-}
 
 // ---------------------------------------------------------------------------- B = 1
 // The single-token form of the middle kernel, specialized on NCHP (chunks per predictor
@@ -475,42 +389,6 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
   if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + total;
 }
 
-// y0: output of ny floats the down projection will add into (zeroed here), or null;
-// prefetch: extra workgroups pull the middle kernel's predictor rows and biases into cache
-template <bool F16, int NCPT>
-void stage1_launch_t(const LayerDev& L, const float* x, int B, hipStream_t s,
-                     const hipEvent_t* tev, float* y0, int ny, int g_pf) {
-  const int nchp = L.r / (L.p_f16 ? 8 : 4);
-  const dim3 grid(L.r + g_pf);
-  if (B == 1)
-    launch(k_pred_stage1<F16, 1, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
-           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
-  else
-    launch(k_pred_stage1<F16, 4, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
-           y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
-}
-
-// prefetch workgroups are used when the ranges travel in the kernel arguments, a range's
-// predictor rows fit PF_PER_THREAD chunks per thread, and r keeps them on their consumer's
-// XCD
-int stage1_prefetch_groups(const LayerDev& L) {
-  const int nchp = L.r / (L.p_f16 ? 8 : 4);
-  if (!L.rs_in_arg || L.r % 8 != 0 || MID_RANGE_MAX * nchp > TPB * PF_PER_THREAD) return 0;
-  return L.g_mid;
-}
-
-template <bool F16>
-void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                   const hipEvent_t* tev = nullptr, float* y0 = nullptr, int ny = 0,
-                   bool prefetch = false) {
-  if (!y0) ny = 0;
-  const int g_pf = prefetch ? stage1_prefetch_groups(L) : 0;
-  const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
-  if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny, g_pf);
-  else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny, g_pf);
-  else if (ncpt <= 4) stage1_launch_t<F16, 4>(L, x, B, s, tev, y0, ny, g_pf);
-  else stage1_launch_t<F16, 8>(L, x, B, s, tev, y0, ny, g_pf);
-}
 
 template <bool F16, bool GATED, int CPT, int NCHP>
 void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
@@ -596,13 +474,6 @@ void down_b1_any(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
 
 }  // namespace
 
-void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                float* y0, int ny, bool prefetch) {
-  if (L.p_f16)
-    stage1_launch<true>(L, x, B, s, tev, y0, ny, prefetch);
-  else
-    stage1_launch<false>(L, x, B, s, tev, y0, ny, prefetch);
-}
 
 bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev) {

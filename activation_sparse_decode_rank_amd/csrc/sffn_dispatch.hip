@@ -7,13 +7,11 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(int d, int n, int r, int max_batch) {
   (void)d;
-  const int n_tiles = (n + TPB - 1) / TPB;
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
   b += align256((size_t)((n + 63) / 64 * 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
   b += align256((size_t)n * 8);                  // tok_full
   b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
-  b += align256((size_t)n_tiles * 4);            // tile_cnt
   b += align256((size_t)((n + 63) / 64) * 8);    // words
   b += align256((size_t)G_MID_MAX * 8);          // wbits
   return b;
@@ -29,7 +27,6 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   L.h_buf = reinterpret_cast<float*>(take((size_t)L.ldh * max_batch * 4));
   L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
   L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
-  L.tile_cnt = reinterpret_cast<int32_t*>(take((size_t)n_tiles * 4));
   L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
   L.wbits = reinterpret_cast<uint64_t*>(take((size_t)G_MID_MAX * 8));
   L.n_tiles = n_tiles;
@@ -89,6 +86,8 @@ bool shape_supported(const LayerDev& L, bool fused) {
 
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
   run_stage1(L, x, B, s, nullptr, nullptr, 0, false);
+  // the same scores kernel the decode step runs at this batch, so both give equal scores
+  if (tile_ok(L, B) && score_tiles_ok(L, B)) return run_score_tiles(L, B, scores, s);
   return run_scores(L, B, scores, s);
 }
 
@@ -110,14 +109,22 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
   const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
   const hipEvent_t* t3 = ev ? ev + 4 : nullptr;
   if (tile_ok(L, B)) {
-    // predictor, threshold and union compaction as separate kernels, then the tiles; the
-    // scores go to the caller's buffer or, when none is given, to the activation buffer,
-    // which the up projection only overwrites after compaction has read them
-    float* sc = scores ? scores : L.h_buf;
+    // stage 1; scores, threshold and union words in one matrix-core kernel (else scores
+    // and two compaction passes, the scores going to the caller's buffer or, when none is
+    // given, to the activation buffer, which the up projection only overwrites after
+    // compaction has read them); the ascending list; then the tiles
     run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false);
-    hipError_t e = run_scores(L, B, sc, s);
-    if (e != hipSuccess) return e;
-    e = launch_compact(L, sc, B, idx, count, tokmask, s);
+    hipError_t e;
+    if (score_tiles_ok(L, B)) {
+      e = run_score_tiles(L, B, scores, s);
+      if (e != hipSuccess) return e;
+      e = launch_scatter(L, idx, count, tokmask, s);
+    } else {
+      float* sc = scores ? scores : L.h_buf;
+      e = run_scores(L, B, sc, s);
+      if (e != hipSuccess) return e;
+      e = launch_compact(L, sc, B, idx, count, tokmask, s);
+    }
     if (e != hipSuccess) return e;
     run_forward_tiles(L, x, B, idx, count, tokmask, y, false, s, t2, t3);
     return hipGetLastError();

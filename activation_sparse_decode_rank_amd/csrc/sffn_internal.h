@@ -43,7 +43,6 @@ struct LayerDev {
   float* h_buf;        // [n][B] activations: by list position (forward) or neuron (decode)
   uint64_t* tok_full;  // [n] token bits by neuron (compaction, decode)
   int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
-  int32_t* tile_cnt;   // [n_tiles] compaction tile counts
   uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
   uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
   // launch geometry fixed at create time
@@ -114,6 +113,13 @@ int occ_mid_bt_f8(const LayerDev& L);
 // sffn_tiles.hip: predictor stage 2 scores, and the matrix-core forward (zero_y: clear y
 // first when the down projection splits rows)
 hipError_t run_scores(const LayerDev& L, int B, float* scores, hipStream_t s);
+// scores, threshold and the union words in one matrix-core kernel (scores may be null),
+// when q fits in LDS; then launch_scatter writes the ascending list from the words
+constexpr size_t SCORE_Q_LDS = 64 * 1024;
+bool score_tiles_ok(const LayerDev& L, int B);
+hipError_t run_score_tiles(const LayerDev& L, int B, float* scores, hipStream_t s);
+hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint64_t* tokmask,
+                          hipStream_t s);
 void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
                        hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down);

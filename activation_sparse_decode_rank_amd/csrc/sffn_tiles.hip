@@ -51,44 +51,39 @@ __global__ __launch_bounds__(TPB) void k_pred_scores(const void* __restrict__ p2
 }
 
 // ============================================================================ compaction
-// Pass 1, one thread per neuron, 256-neuron tiles: token bits, union ballot words, and
-// the tile's active count.
+// Pass 1, one thread per neuron: token bits and the union ballot word of every 64 neurons.
 __global__ __launch_bounds__(TPB) void k_cmp_tiles(const float* __restrict__ scores, int n,
                                                    int B, float tau,
                                                    uint64_t* __restrict__ tok_full,
-                                                   uint64_t* __restrict__ words,
-                                                   int32_t* __restrict__ tile_cnt) {
-  __shared__ int s_cnt[TPB / 64];
+                                                   uint64_t* __restrict__ words) {
   const int i = blockIdx.x * TPB + threadIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   uint64_t bits = 0;
   if (i < n)
     for (int b = 0; b < B; ++b)
       if (scores[(size_t)b * n + i] > tau) bits |= (uint64_t)1 << b;  // NaN compares false
   const uint64_t word = __ballot(bits != 0);
-  if (i < n) tok_full[i] = bits;
-  if (lane == 0) {
-    if (i < n) words[i >> 6] = word;
-    s_cnt[wave] = __popcll(word);
+  if (i < n) {
+    tok_full[i] = bits;
+    if (lane == 0) words[i >> 6] = word;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) tile_cnt[blockIdx.x] = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
 }
 
-// Pass 2, same tiling: exclusive prefix of the tile counts, then every active neuron
-// writes itself at its ascending position. The last tile writes the total.
+// Pass 2, 256-neuron tiles: the exclusive prefix of the union words' popcounts before the
+// tile, then every active neuron writes itself at its ascending position. The last tile
+// writes the total.
 __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict__ tok_full,
-                                                     const uint64_t* __restrict__ words,
-                                                     const int32_t* __restrict__ tile_cnt, int n,
+                                                     const uint64_t* __restrict__ words, int n,
                                                      int n_tiles, int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ count,
                                                      uint64_t* __restrict__ tokmask) {
   __shared__ int s_off;
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = (n + 63) / 64;
   if (threadIdx.x < 64) {
     int acc = 0;
-    for (int u = lane; u < t; u += 64) acc += tile_cnt[u];
+    for (int u = lane; u < 4 * t; u += 64) acc += __popcll(words[u]);
     acc = wave_incl_scan(acc);
     if (lane == 63) s_off = acc;
   }
@@ -105,7 +100,103 @@ __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict_
       if (tokmask) tokmask[k] = tok_full[i];
     }
   }
-  if (t == n_tiles - 1 && threadIdx.x == 0) *count = s_off + tile_cnt[t];
+  if (t == n_tiles - 1 && threadIdx.x == 0) {
+    int tot = s_off;
+    for (int v = 0; v < 4; ++v)
+      if (4 * t + v < nw) tot += __popcll(words[4 * t + v]);
+    *count = tot;
+  }
+}
+
+// Predictor stage 2, threshold and the union words at batch, on the matrix cores (the
+// first compaction pass fused in). Workgroup w owns neurons [64w, 64w + 64), wave v the 16
+// from 64w + 16v. With v_mfma_f32_16x16x4_f32 (lane l: A[l%16][l/16], B[l/16][l%16];
+// result column l%16, rows 4*(l/16)..+3), lane group g = l/16 walks k in [g*r/4,
+// (g+1)*r/4): its P2 row piece is contiguous, q comes from LDS, and each product takes one
+// k of each group. Products and sums are fp32. A ballot of every thresholded result
+// register gives 16 tokens x 4 neurons of bits at once. Writes tok_full and the union word
+// (as k_cmp_tiles does) and, if asked, the scores.
+template <bool PF16, int NT>
+__global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2,
+                                                     const float* __restrict__ pbias,
+                                                     const float* __restrict__ q, int n, int r,
+                                                     int B, float tau,
+                                                     uint64_t* __restrict__ tok_full,
+                                                     uint64_t* __restrict__ words,
+                                                     float* __restrict__ scores) {
+  constexpr int EPC = Elt<PF16>::EPC;
+  constexpr int CU = 8;  // P2 chunks per lane in flight
+  extern __shared__ float s_q[];  // [B][r]
+  __shared__ uint64_t s_tok[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  for (int u = tid; u < B * r / 4; u += TPB)
+    reinterpret_cast<float4_t*>(s_q)[u] = reinterpret_cast<const float4_t*>(q)[u];
+  const int base = blockIdx.x * 64 + wave * 16;
+  const int row = min(base + r16, n - 1);
+  const int kg = r / 4;           // k values per lane group
+  const int nck = kg / EPC;       // P2 chunks per lane
+  const size_t c0 = (size_t)row * (r / EPC) + (size_t)g * nck;
+  const float* qrow[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) qrow[tt] = s_q + (size_t)min(16 * tt + r16, B - 1) * r + g * kg;
+  __syncthreads();
+  float4_t acc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < nck; cb += CU) {
+    u32x4 wv[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + min(cb + u, nck - 1));
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (cb + u < nck) {  // uniform
+        float f[EPC];
+        unpack<PF16>(wv[u], f);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const float* qp = qrow[tt] + (cb + u) * EPC;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], qp[e], acc[tt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // scores and threshold: lane holds tokens 16tt + l%16, neurons base + 4g + v
+  float pb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i = base + 4 * g + v;
+    pb[v] = (pbias && i < n) ? pbias[i] : 0.f;
+  }
+  uint64_t bits = 0;  // lanes 0..15: token bits of neuron base + lane
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int b = 16 * tt + r16;
+    uint64_t m[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = base + 4 * g + v;
+      const float sc = acc[tt][v] + pb[v];
+      if (scores && b < B && i < n) scores[(size_t)b * n + i] = sc;
+      m[v] = __ballot(b < B && i < n && sc > tau);  // NaN compares false
+    }
+    // neuron base + lane (lane < 16) = 4G + v with G = lane / 4: its 16 token bits sit at
+    // bits 16G .. 16G + 15 of ballot v
+    const int v = lane & 3, G = (lane >> 2) & 3;
+    const uint64_t mv = v == 0 ? m[0] : v == 1 ? m[1] : v == 2 ? m[2] : m[3];
+    bits |= ((mv >> (16 * G)) & 0xFFFFull) << (16 * tt);
+  }
+  if (lane < 16) s_tok[wave * 16 + lane] = bits;
+  __syncthreads();
+  if (wave == 0) {
+    const int i = blockIdx.x * 64 + lane;
+    const uint64_t tb = i < n ? s_tok[lane] : 0;
+    const uint64_t word = __ballot(tb != 0);
+    if (i < n) tok_full[i] = tb;
+    if (lane == 0) words[blockIdx.x] = word;
+  }
 }
 
 // ============================================================================ batch tiles
@@ -445,9 +536,39 @@ hipError_t run_scores(const LayerDev& L, int B, float* scores, hipStream_t s) {
 hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t* idx,
                           int32_t* count, uint64_t* tokmask, hipStream_t s) {
   hipLaunchKernelGGL(k_cmp_tiles, dim3(L.n_tiles), dim3(TPB), 0, s, scores, L.n, B, L.tau,
-                     L.tok_full, L.words, L.tile_cnt);
-  hipLaunchKernelGGL(k_cmp_scatter, dim3(L.n_tiles), dim3(TPB), 0, s, L.tok_full, L.words,
-                     L.tile_cnt, L.n, L.n_tiles, idx, count, tokmask);
+                     L.tok_full, L.words);
+  hipLaunchKernelGGL(k_cmp_scatter, dim3(L.n_tiles), dim3(TPB), 0, s, L.tok_full, L.words, L.n,
+                     L.n_tiles, idx, count, tokmask);
+  return hipGetLastError();
+}
+
+bool score_tiles_ok(const LayerDev& L, int B) {
+  const int epc = L.p_f16 ? 8 : 4;
+  return B >= 1 && B <= MAXB && L.r % (4 * epc) == 0 && (size_t)B * L.r * 4 <= SCORE_Q_LDS;
+}
+
+hipError_t run_score_tiles(const LayerDev& L, int B, float* scores, hipStream_t s) {
+  const dim3 grid((L.n + 63) / 64);
+  const size_t lds = (size_t)B * L.r * 4;
+#define SFFN_ST(F16, NT)                                                                     \
+  hipLaunchKernelGGL((k_score_tiles<F16, NT>), grid, dim3(TPB), lds, s, L.p2, L.p_bias, L.q, \
+                     L.n, L.r, B, L.tau, L.tok_full, L.words, scores)
+  const int nt = (B + 15) / 16;
+  if (L.p_f16) {
+    if (nt == 1) SFFN_ST(true, 1); else if (nt == 2) SFFN_ST(true, 2);
+    else if (nt == 3) SFFN_ST(true, 3); else SFFN_ST(true, 4);
+  } else {
+    if (nt == 1) SFFN_ST(false, 1); else if (nt == 2) SFFN_ST(false, 2);
+    else if (nt == 3) SFFN_ST(false, 3); else SFFN_ST(false, 4);
+  }
+#undef SFFN_ST
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint64_t* tokmask,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_cmp_scatter, dim3(L.n_tiles), dim3(TPB), 0, s, L.tok_full, L.words, L.n,
+                     L.n_tiles, idx, count, tokmask);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -160,6 +161,9 @@ def main():
     ap.add_argument("--profile-tokens", type=int, default=4096)
     ap.add_argument("--kernel-tokens", type=int, default=32, help="steps in the per-kernel event pass")
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers")
+    ap.add_argument("--activity", type=float, default=0.0,
+                    help="override every layer's target activity (e.g. 0.10 for the OPT-6.7B "
+                         "stack at a flat 10%%)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -185,6 +189,11 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
+    if args.activity > 0:
+        cfg = dataclasses.replace(cfg, activity=tuple([args.activity] * cfg.layers),
+                                  name=f"{cfg.name}_act{args.activity:g}",
+                                  description=f"{cfg.description}; every layer at "
+                                              f"{100 * args.activity:g}% target activity")
     B = int(args.batch)
     if not 1 <= B <= NAT.SFFN_MAX_BATCH:
         raise SystemExit(f"--batch must be in 1..{NAT.SFFN_MAX_BATCH}")

@@ -89,7 +89,10 @@ def test_compact_boundaries(n, B):
 # --------------------------------------------------------------------------- predictor
 @pytest.mark.parametrize("name,d,n,r,B", [("C1", 768, 3072, 64, 1), ("C2", 512, 1000, 64, 1),
                                           ("C2", 256, 777, 128, 4), ("C3", 256, 555, 64, 2),
-                                          ("C5", 1024, 2100, 256, 1)])
+                                          ("C5", 1024, 2100, 256, 1),
+                                          # the matrix-core score kernel (9+ tokens)
+                                          ("C2", 512, 1000, 64, 16), ("C3", 1024, 2000, 256, 33),
+                                          ("C2", 1024, 3000, 256, 64), ("C5", 1024, 2100, 1024, 12)])
 def test_predict_scores_and_mask(name, d, n, r, B):
     c = cfg(name)
     say(f"predict {name} d={d} n={n} r={r} B={B}")
@@ -128,6 +131,7 @@ SHAPES = [
     ("C2", 512, 2000, 64, 64),
     ("C3", 520, 900, 64, 16),       # d not a multiple of 128: the vector path at batch 16
     ("C2", 264, 700, 64, 12),       # the vector path at 12 tokens (two 8-token groups)
+    ("C2", 1024, 3000, 256, 64),    # 64 tokens x rank 256: the largest q the score kernel stages
 ]
 
 
