@@ -176,6 +176,53 @@ __device__ __forceinline__ void stage_x(float* s_x, const float* x, int n_floats
   for (int u = threadIdx.x; u < n_floats / 4; u += TPB) dst[u] = src[u];
 }
 
+// fp32 -> (hi, lo) fp16 pair with v = hi + lo to about 22 significant bits: the matrix-core
+// kernels multiply fp16 weights by both halves of an fp32 activation.
+__device__ __forceinline__ void split_hi_lo(const float4_t& a, const float4_t& b, half8_t& hi,
+                                            half8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 ha = (_Float16)a[e], hb = (_Float16)b[e];
+    hi[e] = ha;
+    hi[4 + e] = hb;
+    lo[e] = (_Float16)(a[e] - (float)ha);
+    lo[4 + e] = (_Float16)(b[e] - (float)hb);
+  }
+}
+
+// Token split for the matrix-core up projection. x_hl holds, for every 8-input chunk c of
+// the d inputs and every token slot b < tbp (tbp = the batch rounded up to 16), the hi
+// halves of x_b[8c .. 8c+7] at x_hl[c * tbp + b] and the lo halves at
+// x_hl[(d/8 + c) * tbp + b] (16 bytes each; slots b >= B hold zeros). With the token
+// fastest, 16 tokens x 4 consecutive chunks are one contiguous kilobyte. Item u in
+// [u0, nitems) step ustride is the pair (c = u / tbp, b = u % tbp).
+__device__ __forceinline__ void split_x_items(const float* __restrict__ x, int B, int d, int tbp,
+                                              u32x4* __restrict__ x_hl, int u0, int ustride) {
+  const int nch = d / 8;
+  for (int u = u0; u < nch * tbp; u += ustride) {
+    const int c = u / tbp, b = u % tbp;
+    float4_t a = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
+    if (b < B) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(x + (size_t)b * d + (size_t)c * 8);
+      a = p[0];
+      e = p[1];
+    }
+    half8_t hi, lo;
+    split_hi_lo(a, e, hi, lo);
+    x_hl[(size_t)c * tbp + b] = __builtin_bit_cast(u32x4, hi);
+    x_hl[(size_t)(nch + c) * tbp + b] = __builtin_bit_cast(u32x4, lo);
+  }
+}
+
+// Orders LDS accesses of one wave: stores before it are visible to the wave's loads after
+// it (a wave's LDS operations execute in order; the fences keep the compiler from moving
+// them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 constexpr int LIST_CAP = 8192;            // split-list window held in LDS (BITS)
 constexpr int CB_LANES = 8;               // 16-byte chunks per column block (128 bytes)
 constexpr int RSD = TPB / CB_LANES;       // row slots per workgroup

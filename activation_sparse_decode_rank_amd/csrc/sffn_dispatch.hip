@@ -5,8 +5,11 @@
 namespace sffn {
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+static size_t x_hl_bytes(int d, int max_batch) {
+  return (size_t)2 * (d / 8) * ((max_batch + 15) / 16 * 16) * 16;
+}
+
 size_t workspace_bytes(int d, int n, int r, int max_batch) {
-  (void)d;
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
   b += align256((size_t)((n + 63) / 64 * 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
@@ -14,6 +17,7 @@ size_t workspace_bytes(int d, int n, int r, int max_batch) {
   b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
   b += align256((size_t)((n + 63) / 64) * 8);    // words
   b += align256((size_t)G_MID_MAX * 8);          // wbits
+  b += align256(x_hl_bytes(d, max_batch));       // x_hl
   return b;
 }
 
@@ -29,14 +33,16 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));
   L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
   L.wbits = reinterpret_cast<uint64_t*>(take((size_t)G_MID_MAX * 8));
+  L.x_hl = take(x_hl_bytes(L.d, max_batch));
   L.n_tiles = n_tiles;
 }
 
 namespace {
 
-// the batch path needs fp16 weights and quarters of the input width in whole k-steps
+// the matrix-core path: fp16 weights, and each quarter of the input width a whole number
+// of 64-input step pairs
 bool tile_ok(const LayerDev& L, int B) {
-  return B >= TILE_MIN_B && L.w_f16 && L.d % 128 == 0 && B <= MAXB;
+  return B >= TILE_MIN_B && L.w_f16 && L.d % 256 == 0 && B <= MAXB;
 }
 
 }  // namespace
@@ -85,7 +91,7 @@ bool shape_supported(const LayerDev& L, bool fused) {
 }
 
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
-  run_stage1(L, x, B, s, nullptr, nullptr, 0, false);
+  run_stage1(L, x, B, s, nullptr, nullptr, 0, false, false);
   // the same scores kernel the decode step runs at this batch, so both give equal scores
   if (tile_ok(L, B) && score_tiles_ok(L, B)) return run_score_tiles(L, B, scores, s);
   return run_scores(L, B, scores, s);
@@ -113,7 +119,7 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     // and two compaction passes, the scores going to the caller's buffer or, when none is
     // given, to the activation buffer, which the up projection only overwrites after
     // compaction has read them); the ascending list; then the tiles
-    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false);
+    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false, true);
     hipError_t e;
     if (score_tiles_ok(L, B)) {
       e = run_score_tiles(L, B, scores, s);
@@ -129,7 +135,7 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     run_forward_tiles(L, x, B, idx, count, tokmask, y, false, s, t2, t3);
     return hipGetLastError();
   }
-  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true);
+  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true, false);
   if (B == 1 && run_mid_b1(L, x, scores, s, t2)) {
     run_down_b1(L, idx, count, tokmask, y, s, t3);
     return hipGetLastError();

@@ -44,6 +44,8 @@ struct LayerDev {
   uint64_t* tok_full;  // [n] token bits by neuron (compaction, decode)
   int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
   uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
+  void* x_hl;          // tokens split into fp16 hi/lo for the matrix-core up projection:
+                       // 2 x [d/8 chunks][max_batch rounded up to 16] x 16 bytes
   uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
   // launch geometry fixed at create time
   int g_mid;     // workgroups of the fused middle kernel (<= G_MID_MAX)
@@ -82,8 +84,10 @@ constexpr int TILE_MIN_B = 9;
 // sffn_decode_b1.hip: predictor stage 1 (y0/ny: output zeroed for the split-k down
 // projection; prefetch: also pull the middle kernel's first loads into cache), the batch-1
 // middle kernel (false when no kernel exists for the shape) and down projection.
+// prefetch: extra workgroups warm the middle kernel's first loads; split_x (2+ tokens):
+// extra workgroups write the tokens' fp16 hi/lo split into x_hl for the up tile kernel
 void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                float* y0, int ny, bool prefetch);
+                float* y0, int ny, bool prefetch, bool split_x);
 bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev);
 int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 kernel applies

@@ -143,18 +143,24 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&a)[V]) {
 // a few tokens on). Row tile = id mod (rows / MT): with rows / MT a multiple of 8 a row
 // tile stays on one XCD, whose L2 then serves its rows to every token group. Workgroups
 // from nmain on prefetch the middle kernel's ranges as in the single-token form (nmain is
-// a multiple of 8). The first nmain workgroups also clear y0[0..ny).
+// a multiple of 8), npf of them. The nsplit workgroups after those split the tokens into
+// x_hl for the matrix-core up projection (see split_x_items; tbp token slots). The first
+// nmain workgroups also clear y0[0..ny).
 template <bool PF16, int MT, int BT>
 __global__ __launch_bounds__(TPB) void k_pred_stage1_mt(
     const void* __restrict__ p1, const float* __restrict__ x, int d, int r, int B,
-    float* __restrict__ q, float* __restrict__ y0, int ny, int nrt, int nmain,
-    const void* __restrict__ p2, int nchp, const float* __restrict__ pfb0,
-    const float* __restrict__ pfb1, const RangeArg ra) {
+    float* __restrict__ q, float* __restrict__ y0, int ny, int nrt, int nmain, int npf,
+    u32x4* __restrict__ x_hl, int tbp, int nsplit, const void* __restrict__ p2, int nchp,
+    const float* __restrict__ pfb0, const float* __restrict__ pfb1, const RangeArg ra) {
   constexpr int EPC = Elt<PF16>::EPC;
   constexpr int V = MT * BT;
   constexpr int SPAN = 64 / V;  // lanes holding each reduced value
   touch_kernargs<2>();
   const int g = blockIdx.x, tid = threadIdx.x;
+  if (g >= nmain + npf) {
+    split_x_items(x, B, d, tbp, x_hl, (g - nmain - npf) * TPB + tid, nsplit * TPB);
+    return;
+  }
   if (g >= nmain) {
     prefetch_mid_range(g - nmain, p2, nchp, pfb0, pfb1, ra);
     return;
@@ -219,25 +225,28 @@ int stage1_prefetch_groups(const LayerDev& L) {
 
 template <bool F16, int MT, int BT>
 void stage1_mt_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                      const hipEvent_t* tev, float* y0, int ny, int g_pf) {
+                      const hipEvent_t* tev, float* y0, int ny, int g_pf, bool split_x) {
   const int nchp = L.r / (F16 ? 8 : 4);
   const int nrt = (L.r + MT - 1) / MT;
   const int nmain = (nrt * ((B + BT - 1) / BT) + 7) / 8 * 8;
-  launch(k_pred_stage1_mt<F16, MT, BT>, dim3(nmain + g_pf), dim3(TPB), 0, s, tev, L.p1, x, L.d,
-         L.r, B, L.q, y0, ny, nrt, nmain, L.p2, nchp, L.p_bias, L.b_act, L.ra);
+  const int tbp = (B + 15) / 16 * 16;
+  const int nsplit = split_x ? (L.d / 8 * tbp + 4 * TPB - 1) / (4 * TPB) : 0;  // 4 items a thread
+  launch(k_pred_stage1_mt<F16, MT, BT>, dim3(nmain + g_pf + nsplit), dim3(TPB), 0, s, tev, L.p1,
+         x, L.d, L.r, B, L.q, y0, ny, nrt, nmain, g_pf, static_cast<u32x4*>(L.x_hl), tbp, nsplit,
+         L.p2, nchp, L.p_bias, L.b_act, L.ra);
 }
 
 // Several tokens: BT = 2 tokens per workgroup up to 8 tokens, 4 beyond; MT the largest row
 // tile that still leaves at least 256 workgroups (one per compute unit).
 template <bool F16>
 void stage1_mt_dispatch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                        const hipEvent_t* tev, float* y0, int ny, int g_pf) {
+                        const hipEvent_t* tev, float* y0, int ny, int g_pf, bool split_x) {
   const int bt = B <= 8 ? 2 : 4;
   const int ntg = (B + bt - 1) / bt;
   int mt = 1;
   for (int m = 8; m >= 2; m /= 2)
     if ((L.r / m) * ntg >= 256) { mt = m; break; }
-#define SFFN_S1(M, T) stage1_mt_launch<F16, M, T>(L, x, B, s, tev, y0, ny, g_pf)
+#define SFFN_S1(M, T) stage1_mt_launch<F16, M, T>(L, x, B, s, tev, y0, ny, g_pf, split_x)
   if (bt == 2) {
     if (mt == 8) SFFN_S1(8, 2); else if (mt == 4) SFFN_S1(4, 2); else if (mt == 2) SFFN_S1(2, 2); else SFFN_S1(1, 2);
   } else {
@@ -247,13 +256,12 @@ void stage1_mt_dispatch(const LayerDev& L, const float* x, int B, hipStream_t s,
 }
 
 template <bool F16>
-void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                   const hipEvent_t* tev = nullptr, float* y0 = nullptr, int ny = 0,
-                   bool prefetch = false) {
+void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
+                   float* y0, int ny, bool prefetch, bool split_x) {
   if (!y0) ny = 0;
   const int g_pf = prefetch ? stage1_prefetch_groups(L) : 0;
   if (B > 1) {
-    stage1_mt_dispatch<F16>(L, x, B, s, tev, y0, ny, g_pf);
+    stage1_mt_dispatch<F16>(L, x, B, s, tev, y0, ny, g_pf, split_x);
     return;
   }
   const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
@@ -266,11 +274,11 @@ void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
 }  // namespace
 
 void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                float* y0, int ny, bool prefetch) {
+                float* y0, int ny, bool prefetch, bool split_x) {
   if (L.p_f16)
-    stage1_launch<true>(L, x, B, s, tev, y0, ny, prefetch);
+    stage1_launch<true>(L, x, B, s, tev, y0, ny, prefetch, split_x);
   else
-    stage1_launch<false>(L, x, B, s, tev, y0, ny, prefetch);
+    stage1_launch<false>(L, x, B, s, tev, y0, ny, prefetch, split_x);
 }
 
 }  // namespace sffn

@@ -112,10 +112,12 @@ __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict_
 // first compaction pass fused in). Workgroup w owns neurons [64w, 64w + 64), wave v the 16
 // from 64w + 16v. With v_mfma_f32_16x16x4_f32 (lane l: A[l%16][l/16], B[l/16][l%16];
 // result column l%16, rows 4*(l/16)..+3), lane group g = l/16 walks k in [g*r/4,
-// (g+1)*r/4): its P2 row piece is contiguous, q comes from LDS, and each product takes one
-// k of each group. Products and sums are fp32. A ballot of every thresholded result
-// register gives 16 tokens x 4 neurons of bits at once. Writes tok_full and the union word
-// (as k_cmp_tiles does) and, if asked, the scores.
+// (g+1)*r/4): its P2 row piece is contiguous, and each product takes one k of each group.
+// q sits in LDS k-major, token pitch TP = 16 NT rounded up to 32, token b of row k at column
+// b ^ (16 * (group of k & 1)): a wave's 64 reads of one step then fall two to a bank.
+// Products and sums are fp32. A ballot of every thresholded result register gives 16
+// tokens x 4 neurons of bits at once. Writes tok_full and the union word (as k_cmp_tiles
+// does) and, if asked, the scores.
 template <bool PF16, int NT>
 __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2,
                                                      const float* __restrict__ pbias,
@@ -126,20 +128,29 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
                                                      float* __restrict__ scores) {
   constexpr int EPC = Elt<PF16>::EPC;
   constexpr int CU = 8;  // P2 chunks per lane in flight
-  extern __shared__ float s_q[];  // [B][r]
+  constexpr int TP = (16 * NT + 31) / 32 * 32;  // a multiple of 32, so b ^ 16 stays in the row
+  extern __shared__ float s_q[];  // [r][TP]
   __shared__ uint64_t s_tok[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  for (int u = tid; u < B * r / 4; u += TPB)
-    reinterpret_cast<float4_t*>(s_q)[u] = reinterpret_cast<const float4_t*>(q)[u];
+  const int kg = r / 4;           // k values per lane group
+  // stage q: thread item (k4, b) = 4 consecutive k of token b (clamped to B - 1)
+  for (int u = tid; u < (r / 4) * TP; u += TPB) {
+    const int b = u % TP, k4 = u / TP;
+    const float4_t v = *reinterpret_cast<const float4_t*>(q + (size_t)min(b, B - 1) * r + 4 * k4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * k4 + e;
+      s_q[k * TP + (b ^ (16 * ((k / kg) & 1)))] = v[e];
+    }
+  }
   const int base = blockIdx.x * 64 + wave * 16;
   const int row = min(base + r16, n - 1);
-  const int kg = r / 4;           // k values per lane group
   const int nck = kg / EPC;       // P2 chunks per lane
   const size_t c0 = (size_t)row * (r / EPC) + (size_t)g * nck;
-  const float* qrow[NT];
+  const float* qb[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) qrow[tt] = s_q + (size_t)min(16 * tt + r16, B - 1) * r + g * kg;
+  for (int tt = 0; tt < NT; ++tt) qb[tt] = s_q + (size_t)g * kg * TP + ((16 * tt + r16) ^ (16 * (g & 1)));
   __syncthreads();
   float4_t acc[NT];
 #pragma unroll
@@ -155,10 +166,10 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
         unpack<PF16>(wv[u], f);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          const float* qp = qrow[tt] + (cb + u) * EPC;
+          const float* qp = qb[tt] + (size_t)(cb + u) * EPC * TP;
 #pragma unroll
           for (int e = 0; e < EPC; ++e)
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], qp[e], acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], qp[e * TP], acc[tt], 0, 0, 0);
         }
       }
     }
@@ -207,18 +218,6 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
 // 4*(l/16)..+3). Weights are fp16 as stored; fp32 activations enter as a hi + lo pair of
 // fp16 values (v = hi + lo to about 22 significant bits), two products per tile.
 
-__device__ __forceinline__ void split_hi_lo(const float4_t& a, const float4_t& b, half8_t& hi,
-                                            half8_t& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const _Float16 ha = (_Float16)a[e], hb = (_Float16)b[e];
-    hi[e] = ha;
-    hi[4 + e] = hb;
-    lo[e] = (_Float16)(a[e] - (float)ha);
-    lo[4 + e] = (_Float16)(b[e] - (float)hb);
-  }
-}
-
 __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -227,70 +226,113 @@ __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, c
 // workgroup iteration: wave w sums input columns [w*d/4, (w+1)*d/4), the four partial
 // tiles are added in wave order through LDS, then wave 0 applies bias, ReLU (gated: times
 // the up tile), the token bits, and writes hT[b*ldh + p] (token-major, for the down
-// projection's left operand). Loads for KB k-steps are issued before their products.
+// projection's left operand).
+// Weights are read whole lines at a time (lane l: row l/8 of an 8-row half tile, 16-byte
+// chunk l%8 of each 128-byte piece): the operand layout itself (lane l: row l%16, chunk
+// l/16) would read 16 rows x 64 bytes per instruction, which streams gathered rows at about
+// two thirds of the rate. Each 64-input step pair passes through a small wave-private LDS
+// buffer into operand order. The activations come split in x_hl (the token fastest), so a
+// wave's operand load for one k-step is a contiguous kilobyte. Loads run one batch of KP
+// step pairs ahead of the products.
 template <bool GATED, int NT>
 __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
                                                  const float* __restrict__ b_act,
-                                                 const float* __restrict__ x, int d, int n, int B,
-                                                 const int32_t* __restrict__ idx,
+                                                 const u32x4* __restrict__ x_hl, int d, int n,
+                                                 int B, const int32_t* __restrict__ idx,
                                                  const int32_t* __restrict__ count,
                                                  const uint64_t* __restrict__ tokmask,
                                                  float* __restrict__ hT, int ldh,
                                                  float* __restrict__ y0, int ny) {
-  constexpr int KB = NT <= 2 ? 4 : 2;  // k-steps per load batch
   constexpr int NM = GATED ? 2 : 1;
+  constexpr int TBP = 16 * NT;                 // token slots in x_hl
+  constexpr int KP = NT == 1 ? 2 : 1;          // 64-input step pairs per load batch
+  constexpr int PITCH = 9;                     // transpose buffer row pitch in chunks
+  __shared__ u32x4 s_w[TPB / 64][KP][NM][16 * PITCH];
   __shared__ float4_t s_acc[TPB / 64][NM][NT][64];
   zero_grid(y0, ny);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;
   const int cnt = min(max(*count, 0), n);
-  const int nch = d / 8;
-  const int rowch = GATED ? 2 * nch : nch;
-  const int kq_len = d / 4;
-  const int ksteps = kq_len / 32;
-  const int kbase = wave * kq_len + 8 * g;
-  const float* xr[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) xr[tt] = x + (size_t)min(tt * 16 + r16, B - 1) * d;
+  const int nch = d / 8;                 // chunks per matrix row
+  const int rowch = NM * nch;
+  const int qch = nch / 4;               // this wave's chunks of each row
+  const int npairs = qch / 8;            // its 64-input step pairs
+  const int c0 = wave * qch;
+  const u32x4* wbase = reinterpret_cast<const u32x4*>(w_act);
+  const u32x4* xh = x_hl + r16;
+  const u32x4* xl = x_hl + (size_t)nch * TBP + r16;
+  u32x4* sw = &s_w[wave][0][0][0];
   for (int t = blockIdx.x; t * 16 < cnt; t += gridDim.x) {
-    const int i = idx[min(t * 16 + r16, cnt - 1)];
-    const u32x4* wrow =
-        reinterpret_cast<const u32x4*>(w_act) + (size_t)((i >= 0 && i < n) ? i : 0) * rowch;
+    const int ia = idx[min(t * 16 + lr, cnt - 1)], ib = idx[min(t * 16 + 8 + lr, cnt - 1)];
+    const u32x4* pa = wbase + (size_t)((ia >= 0 && ia < n) ? ia : 0) * rowch + c0 + lc;
+    const u32x4* pb = wbase + (size_t)((ib >= 0 && ib < n) ? ib : 0) * rowch + c0 + lc;
     float4_t acc[NM][NT];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ksteps; s0 += KB) {
-      u32x4 a[KB][NM];
-      float4_t xv[KB][NT][2];
+    u32x4 wa[2][KP][NM], wb[2][KP][NM], xv[2][KP][2][NT][2];
+    // every load unconditional (pair index clamped); pairs past the end multiply zeros
+    auto load = [&](int p0, int bb) {
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int k = kbase + min(s0 + u, ksteps - 1) * 32;
+      for (int kp = 0; kp < KP; ++kp) {
+        const int p = min(p0 + kp, npairs - 1);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) a[u][m] = wrow[m * nch + k / 8];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          xv[u][tt][0] = *reinterpret_cast<const float4_t*>(xr[tt] + k);
-          xv[u][tt][1] = *reinterpret_cast<const float4_t*>(xr[tt] + k + 4);
+        for (int m = 0; m < NM; ++m) {
+          wa[bb][kp][m] = ld_stream(pa, (size_t)m * nch + 8 * p);
+          wb[bb][kp][m] = ld_stream(pb, (size_t)m * nch + 8 * p);
         }
-      }
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        if (s0 + u < ksteps) {
+        for (int st = 0; st < 2; ++st) {
+          const size_t c = (size_t)(c0 + 8 * p + 4 * st + g) * TBP;
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
-            half8_t hi, lo;
-            split_hi_lo(xv[u][tt][0], xv[u][tt][1], hi, lo);
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const half8_t w8 = __builtin_bit_cast(half8_t, a[u][m]);
-              acc[m][tt] = mfma16(w8, hi, acc[m][tt]);
-              acc[m][tt] = mfma16(w8, lo, acc[m][tt]);
-            }
+            xv[bb][kp][st][tt][0] = xh[c + 16 * tt];
+            xv[bb][kp][st][tt][1] = xl[c + 16 * tt];
           }
         }
       }
+    };
+    auto mult = [&](int p0, int bb) {
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          sw[(kp * NM + m) * 16 * PITCH + lr * PITCH + lc] = wa[bb][kp][m];
+          sw[(kp * NM + m) * 16 * PITCH + (8 + lr) * PITCH + lc] = wb[bb][kp][m];
+        }
+      wave_lds_sync();
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp) {
+        const bool live = p0 + kp < npairs;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const u32x4 a = sw[(kp * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g];
+            const half8_t w8 = __builtin_bit_cast(half8_t, live ? a : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+              acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][0]), acc[m][tt]);
+              acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][1]), acc[m][tt]);
+            }
+          }
+      }
+      wave_lds_sync();
+    };
+    // the scheduling barriers keep each batch's loads ahead of the products before their
+    // use (the scheduler would otherwise sink them to their first use)
+    load(0, 0);
+    for (int p0 = 0; p0 < npairs; p0 += 2 * KP) {
+      load(p0 + KP, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(p0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(p0 + 2 * KP, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(p0 + KP, 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -323,6 +365,12 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
     }
     __syncthreads();
   }
+}
+
+// Standalone token split (the forward entry point has no stage 1 to do it).
+__global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, int B, int d,
+                                                 int tbp, u32x4* __restrict__ x_hl) {
+  split_x_items(x, B, d, tbp, x_hl, blockIdx.x * TPB + threadIdx.x, gridDim.x * TPB);
 }
 
 // Down projection at batch: Y[b][c] += sum_p hT[b][p] * W_down^T[idx_p][c]. Workgroup
@@ -496,10 +544,10 @@ void up_tile_launch(const LayerDev& L, const float* x, int B, const int32_t* idx
                     hipStream_t s, const hipEvent_t* tev) {
   const dim3 grid(L.g_up);
   switch ((B + 15) / 16) {
-    case 1: launch(k_up_mfma<GATED, 1>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    case 2: launch(k_up_mfma<GATED, 2>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    case 3: launch(k_up_mfma<GATED, 3>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    default: launch(k_up_mfma<GATED, 4>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    case 1: launch(k_up_mfma<GATED, 1>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    case 2: launch(k_up_mfma<GATED, 2>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    case 3: launch(k_up_mfma<GATED, 3>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+    default: launch(k_up_mfma<GATED, 4>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
   }
 }
 
@@ -515,11 +563,18 @@ void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_
 }
 
 // union-list forward on the matrix cores; y is zeroed by the up kernel when the down
-// projection splits rows
+// projection splits rows. Standalone (zero_y) the tokens are split here; in the decode
+// step stage 1 has split them.
 void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                    const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
                    hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
   const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
+  if (zero_y) {
+    const int tbp = (B + 15) / 16 * 16;
+    const int items = L.d / 8 * tbp;
+    hipLaunchKernelGGL(k_split_x, dim3((items + TPB - 1) / TPB), dim3(TPB), 0, s, x, B, L.d, tbp,
+                       static_cast<u32x4*>(L.x_hl));
+  }
   if (L.gated)
     up_tile_launch<true>(L, x, B, idx, count, tokmask, y, ny, s, t_up);
   else
@@ -542,14 +597,19 @@ hipError_t launch_compact(const LayerDev& L, const float* scores, int B, int32_t
   return hipGetLastError();
 }
 
+static size_t score_tiles_lds(const LayerDev& L, int B) {
+  const int nt = (B + 15) / 16;
+  return (size_t)L.r * ((16 * nt + 31) / 32 * 32) * 4;
+}
+
 bool score_tiles_ok(const LayerDev& L, int B) {
   const int epc = L.p_f16 ? 8 : 4;
-  return B >= 1 && B <= MAXB && L.r % (4 * epc) == 0 && (size_t)B * L.r * 4 <= SCORE_Q_LDS;
+  return B >= 1 && B <= MAXB && L.r % (4 * epc) == 0 && score_tiles_lds(L, B) <= SCORE_Q_LDS;
 }
 
 hipError_t run_score_tiles(const LayerDev& L, int B, float* scores, hipStream_t s) {
   const dim3 grid((L.n + 63) / 64);
-  const size_t lds = (size_t)B * L.r * 4;
+  const size_t lds = score_tiles_lds(L, B);
 #define SFFN_ST(F16, NT)                                                                     \
   hipLaunchKernelGGL((k_score_tiles<F16, NT>), grid, dim3(TPB), lds, s, L.p2, L.p_bias, L.q, \
                      L.n, L.r, B, L.tau, L.tok_full, L.words, scores)
