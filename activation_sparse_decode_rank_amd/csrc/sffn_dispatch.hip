@@ -12,7 +12,7 @@ static size_t x_hl_bytes(int d, int max_batch) {
 size_t workspace_bytes(int d, int n, int r, int max_batch) {
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
-  b += align256((size_t)((n + 63) / 64 * 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
+  b += align256((size_t)((n + 63) / 64 * 64 + 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
   b += align256((size_t)n * 8);                  // tok_full
   b += align256((size_t)(G_MID_MAX + 1) * 4);    // rs (range table, written at create)
   b += align256((size_t)((n + 63) / 64) * 8);    // words
@@ -27,7 +27,7 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   const int n_tiles = (n + TPB - 1) / TPB;
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
   L.q = reinterpret_cast<float*>(take((size_t)max_batch * L.r * 4));
-  L.ldh = (n + 63) / 64 * 64;
+  L.ldh = (n + 63) / 64 * 64 + 64;  // 64 spare slots: the down tile kernel reads past the list end
   L.h_buf = reinterpret_cast<float*>(take((size_t)L.ldh * max_batch * 4));
   L.tok_full = reinterpret_cast<uint64_t*>(take((size_t)n * 8));
   L.rs = reinterpret_cast<int32_t*>(take((size_t)(G_MID_MAX + 1) * 4));

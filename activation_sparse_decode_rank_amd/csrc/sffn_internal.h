@@ -55,7 +55,7 @@ struct LayerDev {
   int ks_down;   // row splits of the down projection (1 = plain stores; 2 keeps y bitwise
                  // reproducible; more adds float atomics in a varying order)
   int ks_tile;   // the same for the batch (matrix-core) down projection
-  int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64)
+  int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64, plus 64)
   int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
   bool rs_in_arg;  // the range table travels in the middle kernel's arguments (ra)
   RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)

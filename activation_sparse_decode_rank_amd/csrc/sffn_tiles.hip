@@ -374,146 +374,175 @@ __global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, in
 }
 
 // Down projection at batch: Y[b][c] += sum_p hT[b][p] * W_down^T[idx_p][c]. Workgroup
-// (cb, kq) owns the 64-column block cb and positions [p0, p1) (a multiple of DCH per split,
-// so hT chunks stay 16-byte aligned). Per chunk of DCH positions the 256 threads load the
-// weight tile (16-byte row pieces) and the activation tile into registers, then write the
-// weights transposed into LDS (column-major: the right operand wants 8 consecutive
-// positions of one column per lane) and the activations as hi/lo fp16; wave w multiplies
-// its 16 columns for every 16-token tile. Loads run PF chunks ahead through a register
-// ring. Sums leave as in k_down: plain store for KS == 1, else float atomics onto y zeroed
-// earlier in the call, b_out riding on kq == 0.
-constexpr int DCH = 64;
-constexpr int DCH_P = DCH + 8;  // LDS row pitch in halfs (keeps 16-byte alignment)
+// (cb, kq) owns the 64-column block cb and list positions [p0, p1) (split kq of KS, a
+// multiple of 32 positions each). Each wave streams its own 32-position chunks (chunk k of
+// the split goes to wave k % 4): lane l reads row l/8 + 8j (j < 4) of the chunk, 16-byte
+// piece l%8 of the block (whole 128-byte lines), stores the piece as is in the wave's own
+// LDS buffer, and gathers 8 consecutive positions of one column as the right operand of
+// v_mfma_f32_16x16x32_f16; the activations (token l%16, positions
+// 8*(l/16)..+7) are the left one, as a hi + lo fp16 pair. No workgroup barrier in the
+// loop; loads run one batch of KB chunks ahead. At the end the four waves' sums are added
+// in wave order through LDS and leave as in k_down: plain stores for KS == 1, else float
+// atomics onto y zeroed earlier in the call, b_out riding on kq == 0.
+constexpr int DCH = 32;         // positions per chunk (one k-step)
 constexpr int IDX_CAP = 4096;   // list window held in LDS (a multiple of DCH)
-
-template <int NT, int PF>
+template <int NT>
 __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_down_t,
                                                    const float* __restrict__ b_out,
                                                    const float* __restrict__ hT, int ldh, int d,
                                                    int n, int B, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ count, int KS,
                                                    float* __restrict__ y) {
-  constexpr int AV = NT;  // float4 activation loads per thread per chunk (NT*16 tokens x 64 positions)
-  __shared__ __attribute__((aligned(16))) _Float16 s_w[64][DCH_P];
-  __shared__ __attribute__((aligned(16))) _Float16 s_a[2][NT * 16][DCH_P];
+  constexpr int KB = NT <= 2 ? 2 : 1;   // chunks per load batch
+  // chunk buffer: [32 positions][64 columns] fp16 at a pitch of 33 words, so a wave's gather
+  // of one position row per lane group (8 rows apart) touches all 32 banks
+  constexpr int WP = 66;
+  __shared__ __attribute__((aligned(16))) _Float16 s_wt[TPB / 64][KB][DCH * WP];
+  __shared__ float4_t s_acc[TPB / 64][4][NT][64];
   __shared__ int32_t s_idx[IDX_CAP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;
   const int nch = d / 8;
   const int ncb = gridDim.x / KS;
   const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
   const int cnt = min(max(*count, 0), n);
   const int per = (((cnt + KS - 1) / KS) + DCH - 1) / DCH * DCH;
   const int p0 = min(cnt, kq * per), p1 = min(cnt, p0 + per);
-  // this thread's pieces of a chunk
-  const int wrow = tid >> 3, wcc = tid & 7;  // weight rows wrow and wrow + 32, chunk wcc
-  const int wchunk = min(cb * 8 + wcc, nch - 1);
-  int atok[AV], aq[AV];
+  const bool col_ok = cb * 8 + lc < nch;
+  const u32x4* wcol = reinterpret_cast<const u32x4*>(w_down_t) + min(cb * 8 + lc, nch - 1);
+  const float* hrow[NT];
 #pragma unroll
-  for (int u = 0; u < AV; ++u) {
-    const int e = tid + u * TPB;
-    atok[u] = e >> 4;
-    aq[u] = e & 15;
-  }
+  for (int tt = 0; tt < NT; ++tt) hrow[tt] = hT + (size_t)min(16 * tt + r16, B - 1) * ldh;
+  _Float16* swt = &s_wt[wave][0][0];
 
-  u32x4 wr[PF][2];
-  float4_t ar[PF][AV];
-  int wi[PF][2];
-  // list ids come from the LDS window (position slot_pc - wb), so no weight load waits on
-  // a global index load
-  int wb = p0, wl = 0, last_pc = p0;
-  auto issue = [&](int slot_pc, u32x4* wslot, float4_t* aslot, int* islot) {
-    slot_pc = min(slot_pc, last_pc);  // chunks past the end re-read the last one (zeroed later)
+  float4_t acc[4][NT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = s_idx[min(slot_pc - wb + wrow + 32 * u, wl - 1)];
-      islot[u] = i;
-      wslot[u] = ld_chunk(w_down_t, (size_t)((i >= 0 && i < n) ? i : 0) * nch + wchunk);
-    }
+  for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
-    for (int u = 0; u < AV; ++u) {
-      const int b = min(atok[u], B - 1);
-      aslot[u] = *reinterpret_cast<const float4_t*>(hT + (size_t)b * ldh + slot_pc + 4 * aq[u]);
-    }
-  };
-  auto stash = [&](int slot_pc, const u32x4* wslot, const float4_t* aslot, const int* islot) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = wrow + 32 * u;
-      const bool ok = slot_pc + r < p1 && islot[u] >= 0 && islot[u] < n && cb * 8 + wcc < nch;
-      const half8_t h = __builtin_bit_cast(half8_t, wslot[u]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_w[wcc * 8 + e][r] = ok ? h[e] : (_Float16)0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < AV; ++u) {
-      const int b = atok[u], q = aq[u];
-      float4_t v = aslot[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (b >= B || slot_pc + 4 * q + e >= p1) v[e] = 0.f;
-      half8_t hi, lo;
-      split_hi_lo(v, v, hi, lo);
-      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<half4_t*>(&s_a[0][b][4 * q]) = half4_t{hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<half4_t*>(&s_a[1][b][4 * q]) = half4_t{lo[0], lo[1], lo[2], lo[3]};
-    }
-  };
-
-  float4_t acc[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) acc[tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NT; ++tt) acc[cg][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4 wv[2][KB][4];
+  float4_t av[2][KB][NT][2];
+  int wb = p0, wl = 0;
   for (wb = p0; wb < p1; wb += IDX_CAP) {
     wl = min(IDX_CAP, p1 - wb);
     __syncthreads();
     for (int k = tid; k < wl; k += TPB) s_idx[k] = idx[wb + k];
     __syncthreads();
-    const int nchunks = (wl + DCH - 1) / DCH;
-    last_pc = wb + (nchunks - 1) * DCH;
-    // branch-free ring: rounds of PF chunks; chunks past the end contribute zeros
+    const int nck = (wl + DCH - 1) / DCH;        // chunks in this window
+    const int mine = (nck - wave + 3) / 4;       // this wave's chunks: wave, wave + 4, ...
+    // window offset of this wave's chunk number i, clamped to its last chunk (a wave with
+    // none reads chunk 0): every load stays within positions < wl + 31, inside the
+    // activation row (rows are padded by 64 past the list's largest size) and the window's
+    // indices; products of chunks past the end are skipped
+    auto chunk_at = [&](int i) { return mine > 0 ? (wave + 4 * min(i, mine - 1)) * DCH : 0; };
+    auto load = [&](int i0, int bb) {
 #pragma unroll
-    for (int sl = 0; sl < PF; ++sl) issue(wb + sl * DCH, wr[sl], ar[sl], wi[sl]);
-    for (int c0 = 0; c0 < nchunks; c0 += PF) {
+      for (int kb = 0; kb < KB; ++kb) {
+        const int pc = chunk_at(i0 + kb);
 #pragma unroll
-      for (int sl = 0; sl < PF; ++sl) {
-        const int c = c0 + sl;
-        {
-          __syncthreads();
-          stash(wb + c * DCH, wr[sl], ar[sl], wi[sl]);
-          __syncthreads();
-          issue(wb + (c + PF) * DCH, wr[sl], ar[sl], wi[sl]);
+        for (int j = 0; j < 4; ++j) {
+          const int i = s_idx[min(pc + lr + 8 * j, wl - 1)];
+          wv[bb][kb][j] = ld_stream(wcol, (size_t)((i >= 0 && i < n) ? i : 0) * nch);
+        }
 #pragma unroll
-        for (int ks = 0; ks < DCH / 32; ++ks) {
-          const half8_t bw = *reinterpret_cast<const half8_t*>(&s_w[16 * wave + r16][32 * ks + 8 * g]);
+        for (int tt = 0; tt < NT; ++tt) {
+          const float* hp = hrow[tt] + wb + pc + 8 * g;
+          av[bb][kb][tt][0] = *reinterpret_cast<const float4_t*>(hp);
+          av[bb][kb][tt][1] = *reinterpret_cast<const float4_t*>(hp + 4);
+        }
+      }
+    };
+    auto mult = [&](int i0, int bb) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int pc = chunk_at(i0 + kb);
+        _Float16* bufk = swt + kb * DCH * WP;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pos = pc + lr + 8 * j;
+          const int i = s_idx[min(pos, wl - 1)];
+          const bool ok = pos < wl && i >= 0 && i < n && col_ok;
+          const u32x4 v = ok ? wv[bb][kb][j] : u32x4{0u, 0u, 0u, 0u};
+          uint32_t* dst = reinterpret_cast<uint32_t*>(bufk + (lr + 8 * j) * WP + 8 * lc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = v[e];
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (i0 + kb < mine) {  // uniform within the wave
+          const int pc = (wave + 4 * (i0 + kb)) * DCH;
+          const _Float16* bufk = swt + kb * DCH * WP;
+          half8_t ah[NT], al[NT];
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
-            const half8_t ah = *reinterpret_cast<const half8_t*>(&s_a[0][16 * tt + r16][32 * ks + 8 * g]);
-            const half8_t al = *reinterpret_cast<const half8_t*>(&s_a[1][16 * tt + r16][32 * ks + 8 * g]);
-            acc[tt] = mfma16(ah, bw, acc[tt]);
-            acc[tt] = mfma16(al, bw, acc[tt]);
+            float4_t v0 = av[bb][kb][tt][0], v1 = av[bb][kb][tt][1];
+            const int q0 = pc + 8 * g;
+            const bool tok = 16 * tt + r16 < B;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (!tok || q0 + e >= wl) v0[e] = 0.f;
+              if (!tok || q0 + 4 + e >= wl) v1[e] = 0.f;
+            }
+            split_hi_lo(v0, v1, ah[tt], al[tt]);
+          }
+#pragma unroll
+          for (int cg = 0; cg < 4; ++cg) {
+            half8_t bw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bw[e] = bufk[(8 * g + e) * WP + 16 * cg + r16];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+              acc[cg][tt] = mfma16(ah[tt], bw, acc[cg][tt]);
+              acc[cg][tt] = mfma16(al[tt], bw, acc[cg][tt]);
+            }
           }
         }
+      }
+      wave_lds_sync();
+    };
+    load(0, 0);
+    for (int i0 = 0; i0 < mine; i0 += 2 * KB) {
+      load(i0 + KB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(i0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(i0 + 2 * KB, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(i0 + KB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // fixed-order sum of the four waves, then out (lane l holds column 16cg + l%16 of the
+  // block, tokens 16tt + 4*(l/16) + j)
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) s_acc[wave][cg][tt][lane] = acc[cg][tt];
+  __syncthreads();
+  if (kq == 0 || p1 > p0) {
+    for (int o = tid; o < 4 * NT * 64; o += TPB) {
+      const int cg = o / (NT * 64), tt = (o / 64) % NT, l = o % 64;
+      const float4_t v = ((s_acc[0][cg][tt][l] + s_acc[1][cg][tt][l]) + s_acc[2][cg][tt][l]) +
+                         s_acc[3][cg][tt][l];
+      const int col = cb * 64 + 16 * cg + (l & 15);
+      if (col < d) {
+        const float bo = (kq == 0 && b_out) ? b_out[col] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = 16 * tt + 4 * (l >> 4) + j;
+          if (b < B) {
+            float* dst = y + (size_t)b * d + col;
+            if (KS == 1)
+              *dst = v[j] + bo;
+            else
+              atomicAdd(dst, v[j] + bo);
+          }
         }
       }
     }
-  }
-  const int col = cb * 64 + 16 * wave + r16;
-  if (col < d && (kq == 0 || p1 > p0)) {
-    const float bo = (kq == 0 && b_out) ? b_out[col] : 0.f;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int b = tt * 16 + 4 * g + j;
-        if (b < B) {
-          const float v = acc[tt][j] + bo;
-          float* dst = y + (size_t)b * d + col;
-          if (KS == 1)
-            *dst = v;
-          else
-            atomicAdd(dst, v);
-        }
-      }
   }
 }
 
@@ -555,10 +584,10 @@ void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_
                       float* y, hipStream_t s, const hipEvent_t* tev) {
   const dim3 grid(((L.d + 63) / 64) * L.ks_tile);
   switch ((B + 15) / 16) {
-    case 1: launch(k_down_mfma<1, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 2: launch(k_down_mfma<2, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 3: launch(k_down_mfma<3, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    default: launch(k_down_mfma<4, 4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 1: launch(k_down_mfma<1>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 2: launch(k_down_mfma<2>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 3: launch(k_down_mfma<3>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    default: launch(k_down_mfma<4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
   }
 }
 
