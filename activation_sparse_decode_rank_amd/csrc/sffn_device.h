@@ -25,6 +25,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "sffn_internal.h"
 

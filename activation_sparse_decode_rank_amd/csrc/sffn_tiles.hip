@@ -111,10 +111,11 @@ __global__ __launch_bounds__(TPB) void k_cmp_scatter(const uint64_t* __restrict_
 // Predictor stage 2, threshold and the union words at batch, on the matrix cores (the
 // first compaction pass fused in). Workgroup w owns neurons [64w, 64w + 64), wave v the 16
 // from 64w + 16v. With v_mfma_f32_16x16x4_f32 (lane l: A[l%16][l/16], B[l/16][l%16];
-// result column l%16, rows 4*(l/16)..+3), lane group g = l/16 walks k in [g*r/4,
-// (g+1)*r/4): its P2 row piece is contiguous, and each product takes one k of each group.
-// q sits in LDS k-major, token pitch TP = 16 NT rounded up to 32, token b of row k at column
-// b ^ (16 * (group of k & 1)): a wave's 64 reads of one step then fall two to a bank.
+// result column l%16, rows 4*(l/16)..+3), lane group g = l/16 takes the 16-byte P2 chunks
+// 4u + g (u = 0, 1, ...) of its row, so each load instruction reads 64 contiguous bytes of
+// each of the wave's 16 rows, and each product takes one k from each group. q sits in LDS
+// k-major, token pitch TP = 16 NT rounded up to 32, token b of row k at column
+// b ^ (16 * (chunk of k & 1)): a wave's 64 reads of one step then fall two to a bank.
 // Products and sums are fp32. A ballot of every thresholded result register gives 16
 // tokens x 4 neurons of bits at once. Writes tok_full and the union word (as k_cmp_tiles
 // does) and, if asked, the scores.
@@ -141,16 +142,16 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int k = 4 * k4 + e;
-      s_q[k * TP + (b ^ (16 * ((k / kg) & 1)))] = v[e];
+      s_q[k * TP + (b ^ (16 * ((k / EPC) & 1)))] = v[e];
     }
   }
   const int base = blockIdx.x * 64 + wave * 16;
   const int row = min(base + r16, n - 1);
   const int nck = kg / EPC;       // P2 chunks per lane
-  const size_t c0 = (size_t)row * (r / EPC) + (size_t)g * nck;
+  const size_t c0 = (size_t)row * (r / EPC) + g;   // chunk 4u + g of the row
   const float* qb[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) qb[tt] = s_q + (size_t)g * kg * TP + ((16 * tt + r16) ^ (16 * (g & 1)));
+  for (int tt = 0; tt < NT; ++tt) qb[tt] = s_q + (size_t)g * EPC * TP + ((16 * tt + r16) ^ (16 * (g & 1)));
   __syncthreads();
   float4_t acc[NT];
 #pragma unroll
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
   for (int cb = 0; cb < nck; cb += CU) {
     u32x4 wv[CU];
 #pragma unroll
-    for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + min(cb + u, nck - 1));
+    for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + 4 * (size_t)min(cb + u, nck - 1));
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       if (cb + u < nck) {  // uniform
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
         unpack<PF16>(wv[u], f);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          const float* qp = qb[tt] + (size_t)(cb + u) * EPC * TP;
+          const float* qp = qb[tt] + (size_t)(cb + u) * 4 * EPC * TP;
 #pragma unroll
           for (int e = 0; e < EPC; ++e)
             acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], qp[e * TP], acc[tt], 0, 0, 0);
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
     u32x4 wa[2][KP][NM], wb[2][KP][NM], xv[2][KP][2][NT][2];
-    // every load unconditional (pair index clamped); pairs past the end multiply zeros
+    // KP pairs into buffer bb; every load unconditional (pair index clamped)
     auto load = [&](int p0, int bb) {
 #pragma unroll
       for (int kp = 0; kp < KP; ++kp) {
@@ -294,9 +295,11 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
         }
       }
     };
-    auto mult = [&](int p0, int bb) {
+    // products of the first KPN pairs held in buffer bb (all of them live: no selects)
+    auto mult = [&](int bb, auto kpn) {
+      constexpr int KPN = decltype(kpn)::value;
 #pragma unroll
-      for (int kp = 0; kp < KP; ++kp)
+      for (int kp = 0; kp < KPN; ++kp)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           sw[(kp * NM + m) * 16 * PITCH + lr * PITCH + lc] = wa[bb][kp][m];
@@ -304,35 +307,41 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
         }
       wave_lds_sync();
 #pragma unroll
-      for (int kp = 0; kp < KP; ++kp) {
-        const bool live = p0 + kp < npairs;
+      for (int kp = 0; kp < KPN; ++kp)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            const u32x4 a = sw[(kp * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g];
-            const half8_t w8 = __builtin_bit_cast(half8_t, live ? a : u32x4{0u, 0u, 0u, 0u});
+            const half8_t w8 = __builtin_bit_cast(
+                half8_t, sw[(kp * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g]);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
               acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][0]), acc[m][tt]);
               acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][1]), acc[m][tt]);
             }
           }
-      }
       wave_lds_sync();
     };
-    // the scheduling barriers keep each batch's loads ahead of the products before their
-    // use (the scheduler would otherwise sink them to their first use)
-    load(0, 0);
-    for (int p0 = 0; p0 < npairs; p0 += 2 * KP) {
-      load(p0 + KP, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mult(p0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(p0 + 2 * KP, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mult(p0 + KP, 1);
-      __builtin_amdgcn_sched_barrier(0);
+    // whole iterations of 2 KP pairs, pipelined (the scheduling barriers keep each batch's
+    // loads ahead of the products before their use; the scheduler would otherwise sink
+    // them to their first use); then the leftover pairs one at a time
+    const int nfull = npairs / (2 * KP) * (2 * KP);
+    if (nfull > 0) {
+      load(0, 0);
+      for (int p0 = 0; p0 < nfull; p0 += 2 * KP) {
+        load(p0 + KP, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mult(0, std::integral_constant<int, KP>{});
+        __builtin_amdgcn_sched_barrier(0);
+        load(p0 + 2 * KP, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mult(1, std::integral_constant<int, KP>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    for (int p = nfull; p < npairs; ++p) {
+      load(p, 0);
+      mult(0, std::integral_constant<int, 1>{});
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -409,7 +418,6 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
   const int cnt = min(max(*count, 0), n);
   const int per = (((cnt + KS - 1) / KS) + DCH - 1) / DCH * DCH;
   const int p0 = min(cnt, kq * per), p1 = min(cnt, p0 + per);
-  const bool col_ok = cb * 8 + lc < nch;
   const u32x4* wcol = reinterpret_cast<const u32x4*>(w_down_t) + min(cb * 8 + lc, nch - 1);
   const float* hrow[NT];
 #pragma unroll
@@ -458,15 +466,14 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
       for (int kb = 0; kb < KB; ++kb) {
         const int pc = chunk_at(i0 + kb);
         _Float16* bufk = swt + kb * DCH * WP;
+        // stored as loaded: positions past the window end and invalid list entries meet
+        // zero activations (the up projection writes 0 for invalid entries), columns past
+        // d are never stored, so with finite weights they add nothing
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int pos = pc + lr + 8 * j;
-          const int i = s_idx[min(pos, wl - 1)];
-          const bool ok = pos < wl && i >= 0 && i < n && col_ok;
-          const u32x4 v = ok ? wv[bb][kb][j] : u32x4{0u, 0u, 0u, 0u};
           uint32_t* dst = reinterpret_cast<uint32_t*>(bufk + (lr + 8 * j) * WP + 8 * lc);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = v[e];
+          for (int e = 0; e < 4; ++e) dst[e] = wv[bb][kb][j][e];
         }
       }
       wave_lds_sync();

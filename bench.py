@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the part
-TILE_MIN_B = 9                 # from this batch on the decode step runs the matrix-core kernels
+TILE_MIN_B = 4                 # from this batch on the decode step runs the matrix-core kernels
 METRIC = "sparse FFN decode µs/layer + active-weight HBM GB/s vs peak, 10% activity"
 
 
@@ -113,7 +113,7 @@ def measured_traffic(kernel_file, workload):
 
 def kernel_names(cfg, B):
     """The three kernels the decode step's timing events cover, by path."""
-    if B >= TILE_MIN_B and cfg.w_dtype == "f16" and cfg.d % 128 == 0:
+    if B >= TILE_MIN_B and cfg.w_dtype == "f16" and cfg.d % 256 == 0:
         return ("stage1", "up_tiles", "down_tiles"), {
             "stage1": "k_pred_stage1 (predictor stage 1, q = P1 x)",
             "up_tiles": "k_up_mfma (gathered-tile up projection on the matrix cores)",

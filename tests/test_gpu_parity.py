@@ -119,17 +119,22 @@ SHAPES = [
     ("C3", 512, 1100, 64, 4),
     ("C5", 1024, 2100, 256, 1),
     ("C2", 4096, 1500, 256, 2),
-    # 5..8 tokens: the small-batch middle kernel's 8-token form and 8-token down projection
+    # the vector small-batch path (2-3 tokens, or weights the tile path does not take):
+    # its 4- and 8-token middle kernel forms and down projections
+    ("C1", 768, 3072, 64, 5),       # fp32 weights
+    ("C2", 640, 1000, 64, 4),       # d not a multiple of 256
+    ("C3", 384, 900, 64, 7),
+    # 4 tokens and more take the matrix-core tile path (fp16, d a multiple of 256)
     ("C3", 512, 1100, 64, 6),
     ("C2", 1024, 2000, 128, 8),
-    ("C1", 768, 3072, 64, 5),       # fp32 weights
-    # batches of 9 and more take the matrix-core tile path (fp16, d a multiple of 128)
+    ("C2", 1280, 2000, 128, 8),     # the up kernel's pipelined pairs plus a leftover pair
+    ("C2", 2048, 1500, 128, 12),
     ("C2", 512, 1000, 64, 9),
     ("C3", 512, 1100, 64, 16),
     ("C2", 1024, 3000, 128, 32),
     ("C3", 256, 777, 64, 20),       # ragged token tile
     ("C2", 512, 2000, 64, 64),
-    ("C3", 520, 900, 64, 16),       # d not a multiple of 128: the vector path at batch 16
+    ("C3", 520, 900, 64, 16),       # d not a multiple of 256: the vector path at batch 16
     ("C2", 264, 700, 64, 12),       # the vector path at 12 tokens (two 8-token groups)
     ("C2", 1024, 3000, 256, 64),    # 64 tokens x rank 256: the largest q the score kernel stages
 ]
@@ -281,14 +286,15 @@ def test_all_active_and_true_sign_equal_dense(gated):
 
 
 @pytest.mark.parametrize("gated", [False, True])
-@pytest.mark.parametrize("B,d", [(1, 64), (5, 64), (16, 128), (24, 128)])
+@pytest.mark.parametrize("B,d", [(1, 64), (5, 64), (16, 128), (6, 256), (16, 256), (24, 256)])
 def test_integer_fixture_bit_exact(gated, B, d):
     """Integer weights and tokens: every partial sum is exact in fp32 (and each activation
     is exactly hi + lo in fp16), so the HIP path must reproduce the oracle bit for bit,
-    scores, list and output, on the vector path and on the matrix-core tile path."""
+    scores, list and output, on the vector path (d = 64, 128) and on the matrix-core tile
+    path with its matrix-core score kernel (d = 256, rank 32)."""
     from activation_sparse_decode_rank_amd import SparseFFN
     from synth import integer_layer
-    n, r = 1000, 16
+    n, r = 1000, (32 if d % 256 == 0 else 16)
     say(f"integer fixture gated={gated} B={B}")
     lo, hi = (-1, 1) if gated else (-2, 2)
     L = integer_layer(d, n, r, gated=gated, seed=77 + B, B=B, lo=lo, hi=hi)
