@@ -85,6 +85,24 @@ std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_byt
 // Cut the ranges into ks contiguous splits of about equal expected active neurons (the
 // sum of the neurons' frequencies; every neuron counts 1 without frequencies), for the
 // decode down projection. upt = ranges per thread the largest split needs (256 threads).
+// the largest expected cost (bytes) of one range: its predictor rows plus each neuron's
+// ReLU-input row(s) weighted by its activation frequency
+double max_range_cost(const std::vector<int32_t>& rs, const float* freq, double p2_row_bytes,
+                      double act_row_bytes) {
+  double worst = 0.0;
+  for (size_t u = 0; u + 1 < rs.size(); ++u) {
+    double c = 0.0;
+    for (int i = rs[u]; i < rs[u + 1]; ++i) {
+      double f = freq ? (double)freq[i] : 0.0;
+      if (!(f >= 0.0)) f = 0.0;
+      if (f > 1.0) f = 1.0;
+      c += p2_row_bytes + f * act_row_bytes;
+    }
+    worst = std::max(worst, c);
+  }
+  return worst;
+}
+
 void split_ranges(const std::vector<int32_t>& rs, const float* freq, int ks, sffn::SplitArg& sa,
                   int& upt) {
   const int g = (int)rs.size() - 1;
@@ -176,15 +194,27 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     const double wb = desc->w_dtype == SFFN_F16 ? 2.0 : 4.0;
     const double pb = desc->p_dtype == SFFN_F16 ? 2.0 : 4.0;
     const double act_row = wb * desc->d * (desc->gated ? 2.0 : 1.0);
-    int target = sffn::mid_resident_groups(L, desc->max_batch);
-    if (target <= 0) target = 2 * cus;
-    // beyond ~4 per CU the per-range overheads dominate; up to RS_ARG_MAX ranges travel in
-    // the kernel arguments
-    target = std::min(target, sffn::RS_ARG_MAX);
+    int resident = sffn::mid_resident_groups(L, desc->max_batch);
+    if (resident <= 0) resident = 2 * cus;
+    // up to RS_ARG_MAX ranges travel in the kernel arguments
     const int min_groups = (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX;
-    if (target < min_groups) target = min_groups;
+    const int target = std::max(std::min(resident, sffn::RS_ARG_MAX), min_groups);
     std::vector<int32_t> rs = balanced_ranges(desc->d_ffn, desc->neuron_freq, pb * desc->rank,
                                               act_row, target);
+    // When the 64-neuron cap alone fixes the layout (a wide layer whose resident workgroups
+    // number about n/64), the hot prefix lands in a few full ranges whose gathers run long.
+    // More ranges than are resident at once then pay off: up to RS_ARG_MAX in the kernel
+    // arguments, or twice the minimum (table in memory) when even that is not more. Kept
+    // when the costliest range's expected bytes at least halve.
+    const int wide = min_groups < sffn::RS_ARG_MAX ? sffn::RS_ARG_MAX
+                                                   : std::min(2 * min_groups, sffn::G_MID_MAX);
+    if (!rs.empty() && target == min_groups && wide > (int)rs.size() - 1) {
+      std::vector<int32_t> rs2 = balanced_ranges(desc->d_ffn, desc->neuron_freq,
+                                                 pb * desc->rank, act_row, wide);
+      if (!rs2.empty() && max_range_cost(rs2, desc->neuron_freq, pb * desc->rank, act_row) <
+                              0.5 * max_range_cost(rs, desc->neuron_freq, pb * desc->rank, act_row))
+        rs.swap(rs2);
+    }
     L.g_mid = rs.empty() ? 0 : (int)rs.size() - 1;
     if (L.g_mid > 0) {
       if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=

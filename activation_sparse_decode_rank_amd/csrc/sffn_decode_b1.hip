@@ -418,13 +418,22 @@ int mid_b1_occ(size_t lds) {
   return a;
 }
 
+// chunks per thread of a gathered row: as pick_cpt, plus 6 for rows of 1281-1536 chunks
+// (the OPT-175B width), which saves the registers of two unused chunks per row and input
+// and keeps four workgroups resident per compute unit
+inline int pick_cpt_b1(int rowch) {
+  const int c = pick_cpt(rowch);
+  return c == 8 && rowch <= 6 * TPB ? 6 : c;
+}
+
 template <bool F16, bool GATED>
 bool mid_b1_any(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev) {
-  switch (pick_cpt(row_chunks(L))) {
+  switch (pick_cpt_b1(row_chunks(L))) {
     case 1: return mid_b1_dispatch<F16, GATED, 1>(L, x, scores, s, tev);
     case 2: return mid_b1_dispatch<F16, GATED, 2>(L, x, scores, s, tev);
     case 4: return mid_b1_dispatch<F16, GATED, 4>(L, x, scores, s, tev);
+    case 6: return mid_b1_dispatch<F16, GATED, 6>(L, x, scores, s, tev);
     case 8: return mid_b1_dispatch<F16, GATED, 8>(L, x, scores, s, tev);
     default: return false;
   }
@@ -444,10 +453,11 @@ int mid_b1_occ_nchp(const LayerDev& L) {
 
 template <bool F16, bool GATED>
 int mid_b1_occ_any(const LayerDev& L) {
-  switch (pick_cpt(row_chunks(L))) {
+  switch (pick_cpt_b1(row_chunks(L))) {
     case 1: return mid_b1_occ_nchp<F16, GATED, 1>(L);
     case 2: return mid_b1_occ_nchp<F16, GATED, 2>(L);
     case 4: return mid_b1_occ_nchp<F16, GATED, 4>(L);
+    case 6: return mid_b1_occ_nchp<F16, GATED, 6>(L);
     case 8: return mid_b1_occ_nchp<F16, GATED, 8>(L);
     default: return -1;
   }

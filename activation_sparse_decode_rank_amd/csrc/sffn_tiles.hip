@@ -464,7 +464,6 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
     auto mult = [&](int i0, int bb) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int pc = chunk_at(i0 + kb);
         _Float16* bufk = swt + kb * DCH * WP;
         // stored as loaded: positions past the window end and invalid list entries meet
         // zero activations (the up projection writes 0 for invalid entries), columns past
