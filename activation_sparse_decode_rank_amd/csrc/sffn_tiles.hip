@@ -135,6 +135,14 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int kg = r / 4;           // k values per lane group
+  const int base = blockIdx.x * 64 + wave * 16;
+  const int row = min(base + r16, n - 1);
+  const int nck = kg / EPC;       // P2 chunks per lane
+  const size_t c0 = (size_t)row * (r / EPC) + g;   // chunk 4u + g of the row
+  // the first batch of P2 loads goes out before q is staged (they do not depend on it)
+  u32x4 wv[CU];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + 4 * (size_t)min(u, nck - 1));
   // stage q: thread item (k4, b) = 4 consecutive k of token b (clamped to B - 1)
   for (int u = tid; u < (r / 4) * TP; u += TPB) {
     const int b = u % TP, k4 = u / TP;
@@ -145,10 +153,6 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
       s_q[k * TP + (b ^ (16 * ((k / EPC) & 1)))] = v[e];
     }
   }
-  const int base = blockIdx.x * 64 + wave * 16;
-  const int row = min(base + r16, n - 1);
-  const int nck = kg / EPC;       // P2 chunks per lane
-  const size_t c0 = (size_t)row * (r / EPC) + g;   // chunk 4u + g of the row
   const float* qb[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) qb[tt] = s_q + (size_t)g * EPC * TP + ((16 * tt + r16) ^ (16 * (g & 1)));
@@ -157,9 +161,10 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = float4_t{0.f, 0.f, 0.f, 0.f};
   for (int cb = 0; cb < nck; cb += CU) {
-    u32x4 wv[CU];
+    if (cb > 0) {
 #pragma unroll
-    for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + 4 * (size_t)min(cb + u, nck - 1));
+      for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + 4 * (size_t)min(cb + u, nck - 1));
+    }
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       if (cb + u < nck) {  // uniform
@@ -254,7 +259,12 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int lr = lane >> 3, lc = lane & 7;
-  const int cnt = min(max(*count, 0), n);
+  // the count and the first tile's list entries load together: entries past the count
+  // are stale but clamped to a valid row below, and their results are never stored
+  const int cnt_raw = *count;
+  int ia = idx[min((int)blockIdx.x * 16 + lr, n - 1)];
+  int ib = idx[min((int)blockIdx.x * 16 + 8 + lr, n - 1)];
+  const int cnt = min(max(cnt_raw, 0), n);
   const int nch = d / 8;                 // chunks per matrix row
   const int rowch = NM * nch;
   const int qch = nch / 4;               // this wave's chunks of each row
@@ -265,7 +275,10 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
   const u32x4* xl = x_hl + (size_t)nch * TBP + r16;
   u32x4* sw = &s_w[wave][0][0][0];
   for (int t = blockIdx.x; t * 16 < cnt; t += gridDim.x) {
-    const int ia = idx[min(t * 16 + lr, cnt - 1)], ib = idx[min(t * 16 + 8 + lr, cnt - 1)];
+    if (t != (int)blockIdx.x) {
+      ia = idx[min(t * 16 + lr, cnt - 1)];
+      ib = idx[min(t * 16 + 8 + lr, cnt - 1)];
+    }
     const u32x4* pa = wbase + (size_t)((ia >= 0 && ia < n) ? ia : 0) * rowch + c0 + lc;
     const u32x4* pb = wbase + (size_t)((ib >= 0 && ib < n) ? ib : 0) * rowch + c0 + lc;
     float4_t acc[NM][NT];
@@ -326,8 +339,21 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
     // loads ahead of the products before their use; the scheduler would otherwise sink
     // them to their first use); then the leftover pairs one at a time
     const int nfull = npairs / (2 * KP) * (2 * KP);
+    // the epilogue's list entries and token bits (lane: positions t*16 + 4g + j) go out
+    // behind the first weight batch; by the time they are used they have long landed
+    int ej[4];
+    uint64_t em[4];
+    auto load_epilogue = [&]() {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pc = min(t * 16 + 4 * g + j, cnt - 1);
+        ej[j] = idx[pc];
+        em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
+      }
+    };
     if (nfull > 0) {
       load(0, 0);
+      load_epilogue();
       for (int p0 = 0; p0 < nfull; p0 += 2 * KP) {
         load(p0 + KP, 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -339,10 +365,14 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (nfull == 0) load_epilogue();
     for (int p = nfull; p < npairs; ++p) {
       load(p, 0);
       mult(0, std::integral_constant<int, 1>{});
     }
+    float eb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eb[j] = (b_act && ej[j] >= 0 && ej[j] < n) ? b_act[ej[j]] : 0.f;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -361,12 +391,11 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
         for (int j = 0; j < 4; ++j) {
           const int p = t * 16 + 4 * g + j;
           if (p < cnt && b < B) {
-            const int ij = idx[p];
-            const bool ok = ij >= 0 && ij < n;
-            const float a0 = v[0][j] + ((ok && b_act) ? b_act[ij] : 0.f);
+            const bool ok = ej[j] >= 0 && ej[j] < n;
+            const float a0 = v[0][j] + eb[j];
             float h = a0 > 0.f ? a0 : 0.f;
             if (GATED) h *= v[NM - 1][j];
-            const bool on = !tokmask || ((tokmask[p] >> b) & 1);
+            const bool on = (em[j] >> b) & 1;
             hT[(size_t)b * ldh + p] = (ok && on) ? h : 0.f;
           }
         }
