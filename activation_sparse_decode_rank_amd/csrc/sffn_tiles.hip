@@ -228,11 +228,12 @@ __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Up projection over the union list, one tile of 16 listed neurons x all B tokens per
-// workgroup iteration: wave w sums input columns [w*d/4, (w+1)*d/4), the four partial
-// tiles are added in wave order through LDS, then wave 0 applies bias, ReLU (gated: times
-// the up tile), the token bits, and writes hT[b*ldh + p] (token-major, for the down
-// projection's left operand).
+// Up projection over the union list. Workgroup iteration u takes the TR tiles of 16 listed
+// neurons from u*TR on, for all B tokens: wave w of its W sums input columns
+// [w*d/W, (w+1)*d/W) for all TR tiles (each activation fragment serves TR tiles), the W
+// partial tiles are added in wave order through LDS, then wave i < TR applies bias, ReLU
+// (gated: times the up tile) and the token bits to tile i and writes hT[b*ldh + p]
+// (token-major, for the down projection's left operand).
 // Weights are read whole lines at a time (lane l: row l/8 of an 8-row half tile, 16-byte
 // chunk l%8 of each 128-byte piece): the operand layout itself (lane l: row l%16, chunk
 // l/16) would read 16 rows x 64 bytes per instruction, which streams gathered rows at about
@@ -240,63 +241,82 @@ __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, c
 // buffer into operand order. The activations come split in x_hl (the token fastest), so a
 // wave's operand load for one k-step is a contiguous kilobyte. Loads run one batch of KP
 // step pairs ahead of the products.
-template <bool GATED, int NT>
-__global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
-                                                 const float* __restrict__ b_act,
-                                                 const u32x4* __restrict__ x_hl, int d, int n,
-                                                 int B, const int32_t* __restrict__ idx,
-                                                 const int32_t* __restrict__ count,
-                                                 const uint64_t* __restrict__ tokmask,
-                                                 float* __restrict__ hT, int ldh,
-                                                 float* __restrict__ y0, int ny) {
+template <bool GATED, int NT, int TR, int W>
+__global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_act,
+                                                    const float* __restrict__ b_act,
+                                                    const u32x4* __restrict__ x_hl, int d,
+                                                    int n, int B,
+                                                    const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ count,
+                                                    const uint64_t* __restrict__ tokmask,
+                                                    float* __restrict__ hT, int ldh,
+                                                    float* __restrict__ y0, int ny) {
   constexpr int NM = GATED ? 2 : 1;
-  constexpr int TBP = 16 * NT;                 // token slots in x_hl
-  constexpr int KP = NT == 1 ? 2 : 1;          // 64-input step pairs per load batch
-  constexpr int PITCH = 9;                     // transpose buffer row pitch in chunks
-  __shared__ u32x4 s_w[TPB / 64][KP][NM][16 * PITCH];
-  __shared__ float4_t s_acc[TPB / 64][NM][NT][64];
-  zero_grid(y0, ny);
+  constexpr int TBP = 16 * NT;                        // token slots in x_hl
+  constexpr int KP = (NT == 1 && TR == 1) ? 2 : 1;    // 64-input step pairs per load batch
+  constexpr int PITCH = 9;                            // transpose buffer row pitch in chunks
+  constexpr int RT = 16 * TR;                         // rows per workgroup iteration
+  __shared__ u32x4 s_w[W][KP][TR][NM][16 * PITCH];
+  __shared__ float4_t s_acc[W][TR][NM][NT][64];
+  for (int i = blockIdx.x * 64 * W + threadIdx.x; i < ny; i += gridDim.x * 64 * W) y0[i] = 0.f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int lr = lane >> 3, lc = lane & 7;
-  // the count and the first tile's list entries load together: entries past the count
-  // are stale but clamped to a valid row below, and their results are never stored
+  // the count and the first iteration's list entries load together: entries past the
+  // count are stale but clamped to a valid row below, and their results are never stored
   const int cnt_raw = *count;
-  int ia = idx[min((int)blockIdx.x * 16 + lr, n - 1)];
-  int ib = idx[min((int)blockIdx.x * 16 + 8 + lr, n - 1)];
+  int ia[TR], ib[TR];
+#pragma unroll
+  for (int i = 0; i < TR; ++i) {
+    ia[i] = idx[min((int)blockIdx.x * RT + 16 * i + lr, n - 1)];
+    ib[i] = idx[min((int)blockIdx.x * RT + 16 * i + 8 + lr, n - 1)];
+  }
   const int cnt = min(max(cnt_raw, 0), n);
   const int nch = d / 8;                 // chunks per matrix row
   const int rowch = NM * nch;
-  const int qch = nch / 4;               // this wave's chunks of each row
+  const int qch = nch / W;               // this wave's chunks of each row
   const int npairs = qch / 8;            // its 64-input step pairs
   const int c0 = wave * qch;
   const u32x4* wbase = reinterpret_cast<const u32x4*>(w_act);
   const u32x4* xh = x_hl + r16;
   const u32x4* xl = x_hl + (size_t)nch * TBP + r16;
-  u32x4* sw = &s_w[wave][0][0][0];
-  for (int t = blockIdx.x; t * 16 < cnt; t += gridDim.x) {
-    if (t != (int)blockIdx.x) {
-      ia = idx[min(t * 16 + lr, cnt - 1)];
-      ib = idx[min(t * 16 + 8 + lr, cnt - 1)];
+  u32x4* sw = &s_w[wave][0][0][0][0];
+  const int et = wave < TR ? wave : 0;   // the tile whose epilogue this wave finishes
+  for (int u = blockIdx.x; u * RT < cnt; u += gridDim.x) {
+    if (u != (int)blockIdx.x) {
+#pragma unroll
+      for (int i = 0; i < TR; ++i) {
+        ia[i] = idx[min(u * RT + 16 * i + lr, cnt - 1)];
+        ib[i] = idx[min(u * RT + 16 * i + 8 + lr, cnt - 1)];
+      }
     }
-    const u32x4* pa = wbase + (size_t)((ia >= 0 && ia < n) ? ia : 0) * rowch + c0 + lc;
-    const u32x4* pb = wbase + (size_t)((ib >= 0 && ib < n) ? ib : 0) * rowch + c0 + lc;
-    float4_t acc[NM][NT];
+    const u32x4* pa[TR];
+    const u32x4* pb[TR];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < TR; ++i) {
+      pa[i] = wbase + (size_t)((ia[i] >= 0 && ia[i] < n) ? ia[i] : 0) * rowch + c0 + lc;
+      pb[i] = wbase + (size_t)((ib[i] >= 0 && ib[i] < n) ? ib[i] : 0) * rowch + c0 + lc;
+    }
+    float4_t acc[TR][NM][NT];
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4 wa[2][KP][NM], wb[2][KP][NM], xv[2][KP][2][NT][2];
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[i][m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4 wa[2][KP][TR][NM], wb[2][KP][TR][NM], xv[2][KP][2][NT][2];
     // KP pairs into buffer bb; every load unconditional (pair index clamped)
     auto load = [&](int p0, int bb) {
 #pragma unroll
       for (int kp = 0; kp < KP; ++kp) {
         const int p = min(p0 + kp, npairs - 1);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          wa[bb][kp][m] = ld_stream(pa, (size_t)m * nch + 8 * p);
-          wb[bb][kp][m] = ld_stream(pb, (size_t)m * nch + 8 * p);
-        }
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            wa[bb][kp][i][m] = ld_stream(pa[i], (size_t)m * nch + 8 * p);
+            wb[bb][kp][i][m] = ld_stream(pb[i], (size_t)m * nch + 8 * p);
+          }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const size_t c = (size_t)(c0 + 8 * p + 4 * st + g) * TBP;
@@ -314,39 +334,44 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
 #pragma unroll
       for (int kp = 0; kp < KPN; ++kp)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          sw[(kp * NM + m) * 16 * PITCH + lr * PITCH + lc] = wa[bb][kp][m];
-          sw[(kp * NM + m) * 16 * PITCH + (8 + lr) * PITCH + lc] = wb[bb][kp][m];
-        }
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            u32x4* bw = sw + ((kp * TR + i) * NM + m) * 16 * PITCH;
+            bw[lr * PITCH + lc] = wa[bb][kp][i][m];
+            bw[(8 + lr) * PITCH + lc] = wb[bb][kp][i][m];
+          }
       wave_lds_sync();
 #pragma unroll
       for (int kp = 0; kp < KPN; ++kp)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const half8_t w8 = __builtin_bit_cast(
-                half8_t, sw[(kp * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g]);
+          for (int i = 0; i < TR; ++i)
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-              acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][0]), acc[m][tt]);
-              acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][1]), acc[m][tt]);
+            for (int m = 0; m < NM; ++m) {
+              const half8_t w8 = __builtin_bit_cast(
+                  half8_t, sw[((kp * TR + i) * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g]);
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt) {
+                acc[i][m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][0]), acc[i][m][tt]);
+                acc[i][m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][kp][st][tt][1]), acc[i][m][tt]);
+              }
             }
-          }
       wave_lds_sync();
     };
     // whole iterations of 2 KP pairs, pipelined (the scheduling barriers keep each batch's
     // loads ahead of the products before their use; the scheduler would otherwise sink
     // them to their first use); then the leftover pairs one at a time
     const int nfull = npairs / (2 * KP) * (2 * KP);
-    // the epilogue's list entries and token bits (lane: positions t*16 + 4g + j) go out
-    // behind the first weight batch; by the time they are used they have long landed
+    // the epilogue's list entries and token bits (lane: positions 4g + j of tile et) go
+    // out behind the first weight batch; by the time they are used they have long landed
     int ej[4];
     uint64_t em[4];
     auto load_epilogue = [&]() {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pc = min(t * 16 + 4 * g + j, cnt - 1);
+        const int pc = min(u * RT + 16 * et + 4 * g + j, cnt - 1);
         ej[j] = idx[pc];
         em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
       }
@@ -374,22 +399,26 @@ __global__ __launch_bounds__(TPB) void k_up_mfma(const void* __restrict__ w_act,
 #pragma unroll
     for (int j = 0; j < 4; ++j) eb[j] = (b_act && ej[j] >= 0 && ej[j] < n) ? b_act[ej[j]] : 0.f;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < TR; ++i)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) s_acc[wave][m][tt][lane] = acc[m][tt];
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) s_acc[wave][i][m][tt][lane] = acc[i][m][tt];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < TR) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         float4_t v[NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-          v[m] = ((s_acc[0][m][tt][lane] + s_acc[1][m][tt][lane]) + s_acc[2][m][tt][lane]) +
-                 s_acc[3][m][tt][lane];
+        for (int m = 0; m < NM; ++m) {
+          v[m] = s_acc[0][et][m][tt][lane];
+#pragma unroll
+          for (int ww = 1; ww < W; ++ww) v[m] += s_acc[ww][et][m][tt][lane];
+        }
         const int b = tt * 16 + r16;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int p = t * 16 + 4 * g + j;
+          const int p = u * RT + 16 * et + 4 * g + j;
           if (p < cnt && b < B) {
             const bool ok = ej[j] >= 0 && ej[j] < n;
             const float a0 = v[0][j] + eb[j];
@@ -602,16 +631,34 @@ hipError_t scores_launch(const LayerDev& L, int B, float* scores, hipStream_t s)
   return hipGetLastError();
 }
 
+template <bool GATED, int NT, int TR, int W>
+void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                      const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
+                      const hipEvent_t* tev) {
+  launch(k_up_mfma<GATED, NT, TR, W>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.b_act,
+         static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0,
+         ny);
+}
+
+// At 16 tokens (one token tile) each workgroup takes two row tiles with eight waves
+// splitting d, so each activation fragment serves both tiles and the pairs stay about as
+// many as the compute units. Otherwise one row tile and four waves: with two token tiles a
+// paired workgroup needs more registers than let two of them share a compute unit, and
+// the pairs then outnumber the compute units (measured no faster at 32 tokens).
 template <bool GATED>
-void up_tile_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                    const int32_t* count, const uint64_t* tokmask, float* y0, int ny,
-                    hipStream_t s, const hipEvent_t* tev) {
-  const dim3 grid(L.g_up);
-  switch ((B + 15) / 16) {
-    case 1: launch(k_up_mfma<GATED, 1>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    case 2: launch(k_up_mfma<GATED, 2>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    case 3: launch(k_up_mfma<GATED, 3>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
-    default: launch(k_up_mfma<GATED, 4>, grid, dim3(TPB), 0, s, tev, L.w_act, L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0, ny); break;
+void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                    const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
+                    const hipEvent_t* tev) {
+  const int nt = (B + 15) / 16;
+  if (B >= 16 && nt == 1 && L.d % 512 == 0) {
+    up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, y0, ny, s, tev);
+    return;
+  }
+  switch (nt) {
+    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
+    case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
+    case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
+    default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
   }
 }
 
@@ -640,9 +687,9 @@ void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        static_cast<u32x4*>(L.x_hl));
   }
   if (L.gated)
-    up_tile_launch<true>(L, x, B, idx, count, tokmask, y, ny, s, t_up);
+    up_tile_launch<true>(L, B, idx, count, tokmask, y, ny, s, t_up);
   else
-    up_tile_launch<false>(L, x, B, idx, count, tokmask, y, ny, s, t_up);
+    up_tile_launch<false>(L, B, idx, count, tokmask, y, ny, s, t_up);
   down_tile_launch(L, B, idx, count, y, s, t_down);
 }
 

@@ -129,6 +129,9 @@ SHAPES = [
     ("C2", 1024, 2000, 128, 8),
     ("C2", 1280, 2000, 128, 8),     # the up kernel's pipelined pairs plus a leftover pair
     ("C2", 2048, 1500, 128, 12),
+    ("C2", 1536, 1200, 128, 16),    # two row tiles per workgroup, eight waves, a leftover pair
+    ("C3", 1536, 1500, 128, 16),
+    ("C3", 1536, 1500, 128, 24),
     ("C2", 512, 1000, 64, 9),
     ("C3", 512, 1100, 64, 16),
     ("C2", 1024, 3000, 128, 32),
