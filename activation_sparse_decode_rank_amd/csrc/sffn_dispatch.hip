@@ -100,7 +100,7 @@ hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* score
 hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
                           const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s) {
   if (tile_ok(L, B)) {
-    run_forward_tiles(L, x, B, idx, count, tokmask, y, true, s, nullptr, nullptr);
+    run_forward_tiles(L, x, B, idx, count, tokmask, y, true, false, s, nullptr, nullptr);
     return hipGetLastError();
   }
   run_gather(L, x, B, idx, count, tokmask, y, s);
@@ -115,16 +115,19 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
   const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
   const hipEvent_t* t3 = ev ? ev + 4 : nullptr;
   if (tile_ok(L, B)) {
-    // stage 1; scores, threshold and union words in one matrix-core kernel (else scores
-    // and two compaction passes, the scores going to the caller's buffer or, when none is
-    // given, to the activation buffer, which the up projection only overwrites after
-    // compaction has read them); the ascending list; then the tiles
+    // stage 1; scores, threshold and union words in one matrix-core kernel, with the up
+    // tile kernel listing the union itself from those words (or a scatter pass when the
+    // words do not fit its LDS); else scores and two compaction passes, the scores going
+    // to the caller's buffer or, when none is given, to the activation buffer, which the
+    // up projection only overwrites after compaction has read them; then the tiles
     run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false, true);
     hipError_t e;
+    bool fw = false;
     if (score_tiles_ok(L, B)) {
       e = run_score_tiles(L, B, scores, s);
       if (e != hipSuccess) return e;
-      e = launch_scatter(L, idx, count, tokmask, s);
+      fw = union_in_up_ok(L);
+      if (!fw) e = launch_scatter(L, idx, count, tokmask, s);
     } else {
       float* sc = scores ? scores : L.h_buf;
       e = run_scores(L, B, sc, s);
@@ -132,7 +135,7 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
       e = launch_compact(L, sc, B, idx, count, tokmask, s);
     }
     if (e != hipSuccess) return e;
-    run_forward_tiles(L, x, B, idx, count, tokmask, y, false, s, t2, t3);
+    run_forward_tiles(L, x, B, idx, count, tokmask, y, false, fw, s, t2, t3);
     return hipGetLastError();
   }
   run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true, false);

@@ -124,9 +124,14 @@ bool score_tiles_ok(const LayerDev& L, int B);
 hipError_t run_score_tiles(const LayerDev& L, int B, float* scores, hipStream_t s);
 hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint64_t* tokmask,
                           hipStream_t s);
+// from_words: the up kernel lists the union itself from the words and token bits of
+// run_score_tiles (writing idx, count and tokmask; needs union_in_up_ok) instead of
+// reading them
+bool union_in_up_ok(const LayerDev& L);
 void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down);
+                       bool from_words, hipStream_t s, const hipEvent_t* t_up,
+                       const hipEvent_t* t_down);
 
 // launchers; each returns hipGetLastError() after enqueueing
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s);

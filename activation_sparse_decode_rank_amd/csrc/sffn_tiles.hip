@@ -241,14 +241,22 @@ __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, c
 // buffer into operand order. The activations come split in x_hl (the token fastest), so a
 // wave's operand load for one k-step is a contiguous kilobyte. Loads run one batch of KP
 // step pairs ahead of the products.
-template <bool GATED, int NT, int TR, int W>
+constexpr int FW_WORDS_MAX = 1024;  // union words the up kernel can list itself (n <= 65536)
+
+// The list from the union words (FW): each workgroup prefix-sums the popcounts of the
+// words in LDS, and list position p is the k-th set bit of the word w with
+// pref[w] <= p < pref[w + 1] (found by binary search over the prefixes; empty words share
+// their successor's prefix and are never chosen). The positions of its own tiles are
+// written to idx, with their token bits; workgroup 0 writes the count.
+template <bool GATED, int NT, int TR, int W, bool FW>
 __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_act,
                                                     const float* __restrict__ b_act,
                                                     const u32x4* __restrict__ x_hl, int d,
-                                                    int n, int B,
-                                                    const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ count,
-                                                    const uint64_t* __restrict__ tokmask,
+                                                    int n, int B, int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ count,
+                                                    uint64_t* __restrict__ tokmask,
+                                                    const uint64_t* __restrict__ words,
+                                                    const uint64_t* __restrict__ tok_full,
                                                     float* __restrict__ hT, int ldh,
                                                     float* __restrict__ y0, int ny) {
   constexpr int NM = GATED ? 2 : 1;
@@ -262,16 +270,55 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int lr = lane >> 3, lc = lane & 7;
-  // the count and the first iteration's list entries load together: entries past the
-  // count are stale but clamped to a valid row below, and their results are never stored
-  const int cnt_raw = *count;
+  constexpr int NTH = 64 * W;
+  constexpr int PE = FW ? (FW_WORDS_MAX + NTH - 1) / NTH : 1;  // words per thread in the scan
+  __shared__ int32_t s_pref[FW ? FW_WORDS_MAX + 1 : 1];
+  __shared__ uint64_t s_word[FW ? FW_WORDS_MAX : 1];
+  __shared__ int32_t s_rows[FW ? RT : 1];
+  __shared__ int32_t s_wsum[W];
+  const int nw = (n + 63) / 64;
   int ia[TR], ib[TR];
+  int cnt;
+  if constexpr (FW) {
+    for (int w = tid; w < nw; w += NTH) s_word[w] = words[w];
+    __syncthreads();
+    int loc[PE], sum = 0;
 #pragma unroll
-  for (int i = 0; i < TR; ++i) {
-    ia[i] = idx[min((int)blockIdx.x * RT + 16 * i + lr, n - 1)];
-    ib[i] = idx[min((int)blockIdx.x * RT + 16 * i + 8 + lr, n - 1)];
+    for (int e = 0; e < PE; ++e) {
+      const int w = tid * PE + e;
+      loc[e] = w < nw ? __popcll(s_word[w]) : 0;
+      sum += loc[e];
+    }
+    const int incl = wave_incl_scan(sum);
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum, total = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      run += v < wave ? s_wsum[v] : 0;
+      total += s_wsum[v];
+    }
+#pragma unroll
+    for (int e = 0; e < PE; ++e) {
+      const int w = tid * PE + e;
+      if (w < nw) s_pref[w] = run;
+      run += loc[e];
+    }
+    if (tid == 0) s_pref[nw] = total;
+    if (blockIdx.x == 0 && tid == 0) *count = total;
+    cnt = min(total, n);
+    __syncthreads();
+  } else {
+    // the count and the first iteration's list entries load together: entries past the
+    // count are stale but clamped to a valid row below, and their results are never stored
+    const int cnt_raw = *count;
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      ia[i] = idx[min((int)blockIdx.x * RT + 16 * i + lr, n - 1)];
+      ib[i] = idx[min((int)blockIdx.x * RT + 16 * i + 8 + lr, n - 1)];
+    }
+    cnt = min(max(cnt_raw, 0), n);
   }
-  const int cnt = min(max(cnt_raw, 0), n);
   const int nch = d / 8;                 // chunks per matrix row
   const int rowch = NM * nch;
   const int qch = nch / W;               // this wave's chunks of each row
@@ -283,7 +330,43 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   u32x4* sw = &s_w[wave][0][0][0][0];
   const int et = wave < TR ? wave : 0;   // the tile whose epilogue this wave finishes
   for (int u = blockIdx.x; u * RT < cnt; u += gridDim.x) {
-    if (u != (int)blockIdx.x) {
+    if constexpr (FW) {
+      if (tid < RT) {
+        const int p = min(u * RT + tid, cnt - 1);
+        int lo = 0, hi = nw - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pref[mid] <= p) lo = mid;
+          else hi = mid - 1;
+        }
+        uint64_t v = s_word[lo];
+        int k = p - s_pref[lo], bit = 0;
+#pragma unroll
+        for (int sft = 32; sft >= 1; sft >>= 1) {
+          const uint64_t low = (((uint64_t)1) << sft) - 1;
+          const int c = __popcll(v & low);
+          if (k >= c) {
+            k -= c;
+            v >>= sft;
+            bit += sft;
+          } else {
+            v &= low;
+          }
+        }
+        const int row = lo * 64 + bit;
+        s_rows[tid] = row;
+        if (u * RT + tid < cnt) {
+          idx[u * RT + tid] = row;
+          if (tokmask) tokmask[u * RT + tid] = tok_full[row];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TR; ++i) {
+        ia[i] = s_rows[16 * i + lr];
+        ib[i] = s_rows[16 * i + 8 + lr];
+      }
+    } else if (u != (int)blockIdx.x) {
 #pragma unroll
       for (int i = 0; i < TR; ++i) {
         ia[i] = idx[min(u * RT + 16 * i + lr, cnt - 1)];
@@ -371,9 +454,14 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     auto load_epilogue = [&]() {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pc = min(u * RT + 16 * et + 4 * g + j, cnt - 1);
-        ej[j] = idx[pc];
-        em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
+        if constexpr (FW) {
+          ej[j] = s_rows[16 * et + 4 * g + j];
+          em[j] = tok_full[ej[j]];
+        } else {
+          const int pc = min(u * RT + 16 * et + 4 * g + j, cnt - 1);
+          ej[j] = idx[pc];
+          em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
+        }
       }
     };
     if (nfull > 0) {
@@ -631,13 +719,23 @@ hipError_t scores_launch(const LayerDev& L, int B, float* scores, hipStream_t s)
   return hipGetLastError();
 }
 
+// fw: the up kernel lists the union itself from the words and token bits the score kernel
+// left in the workspace, writing idx, count and tokmask; otherwise it reads them
 template <bool GATED, int NT, int TR, int W>
 void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                       const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
-                      const hipEvent_t* tev) {
-  launch(k_up_mfma<GATED, NT, TR, W>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.b_act,
-         static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask, L.h_buf, L.ldh, y0,
-         ny);
+                      const hipEvent_t* tev, bool fw) {
+  int32_t* idx_w = const_cast<int32_t*>(idx);
+  int32_t* cnt_w = const_cast<int32_t*>(count);
+  uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
+  if (fw)
+    launch(k_up_mfma<GATED, NT, TR, W, true>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act,
+           L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
+           (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny);
+  else
+    launch(k_up_mfma<GATED, NT, TR, W, false>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act,
+           L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
+           (const uint64_t*)nullptr, (const uint64_t*)nullptr, L.h_buf, L.ldh, y0, ny);
 }
 
 // At 16 tokens (one token tile) each workgroup takes two row tiles with eight waves
@@ -648,17 +746,17 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
 template <bool GATED>
 void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                     const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
-                    const hipEvent_t* tev) {
+                    const hipEvent_t* tev, bool fw) {
   const int nt = (B + 15) / 16;
   if (B >= 16 && nt == 1 && L.d % 512 == 0) {
-    up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, y0, ny, s, tev);
+    up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, y0, ny, s, tev, fw);
     return;
   }
   switch (nt) {
-    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
-    case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
-    case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
-    default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev); break;
+    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
+    case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
+    case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
+    default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
   }
 }
 
@@ -678,7 +776,7 @@ void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_
 // step stage 1 has split them.
 void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                    const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                   hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
+                   bool fw, hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
   const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
   if (zero_y) {
     const int tbp = (B + 15) / 16 * 16;
@@ -687,9 +785,9 @@ void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        static_cast<u32x4*>(L.x_hl));
   }
   if (L.gated)
-    up_tile_launch<true>(L, B, idx, count, tokmask, y, ny, s, t_up);
+    up_tile_launch<true>(L, B, idx, count, tokmask, y, ny, s, t_up, fw);
   else
-    up_tile_launch<false>(L, B, idx, count, tokmask, y, ny, s, t_up);
+    up_tile_launch<false>(L, B, idx, count, tokmask, y, ny, s, t_up, fw);
   down_tile_launch(L, B, idx, count, y, s, t_down);
 }
 
@@ -743,10 +841,13 @@ hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint6
   return hipGetLastError();
 }
 
+bool union_in_up_ok(const LayerDev& L) { return (L.n + 63) / 64 <= FW_WORDS_MAX; }
+
 void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
-  forward_tiles(L, x, B, idx, count, tokmask, y, zero_y, s, t_up, t_down);
+                       bool from_words, hipStream_t s, const hipEvent_t* t_up,
+                       const hipEvent_t* t_down) {
+  forward_tiles(L, x, B, idx, count, tokmask, y, zero_y, from_words, s, t_up, t_down);
 }
 
 }  // namespace sffn
