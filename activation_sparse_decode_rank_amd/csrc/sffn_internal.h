@@ -77,7 +77,7 @@ int mid_resident_groups(const LayerDev& L, int max_batch);
 
 // From this many tokens on (fp16 weights, d a multiple of 128) the decode and forward
 // entry points run the gathered-tile matrix-core kernels.
-constexpr int TILE_MIN_B = 4;
+constexpr int TILE_MIN_B = 2;
 
 // Kernel-family entry points (one translation unit each; tev: an optional start/end event
 // pair stamped by the dispatch).

@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the part
-TILE_MIN_B = 4                 # from this batch on the decode step runs the matrix-core kernels
+TILE_MIN_B = 2                 # from this batch on the decode step runs the matrix-core kernels
 METRIC = "sparse FFN decode µs/layer + active-weight HBM GB/s vs peak, 10% activity"
 
 

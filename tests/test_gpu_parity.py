@@ -119,12 +119,13 @@ SHAPES = [
     ("C3", 512, 1100, 64, 4),
     ("C5", 1024, 2100, 256, 1),
     ("C2", 4096, 1500, 256, 2),
-    # the vector small-batch path (2-3 tokens, or weights the tile path does not take):
-    # its 4- and 8-token middle kernel forms and down projections
+    # the vector small-batch path (weights the tile path does not take): its 4- and
+    # 8-token middle kernel forms and down projections
     ("C1", 768, 3072, 64, 5),       # fp32 weights
     ("C2", 640, 1000, 64, 4),       # d not a multiple of 256
+    ("C3", 384, 900, 64, 2),
     ("C3", 384, 900, 64, 7),
-    # 4 tokens and more take the matrix-core tile path (fp16, d a multiple of 256)
+    # 2 tokens and more take the matrix-core tile path (fp16, d a multiple of 256)
     ("C3", 512, 1100, 64, 6),
     ("C2", 1024, 2000, 128, 8),
     ("C2", 1280, 2000, 128, 8),     # the up kernel's pipelined pairs plus a leftover pair
