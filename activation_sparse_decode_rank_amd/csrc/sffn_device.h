@@ -192,10 +192,10 @@ __device__ __forceinline__ void split_hi_lo(const float4_t& a, const float4_t& b
 }
 
 // Token split for the matrix-core up projection. x_hl holds, for every 8-input chunk c of
-// the d inputs and every token slot b < tbp (tbp = the batch rounded up to 16), the hi
+// the d inputs and every token slot b < tbp (tbp >= B; the library uses tbp = B), the hi
 // halves of x_b[8c .. 8c+7] at x_hl[c * tbp + b] and the lo halves at
 // x_hl[(d/8 + c) * tbp + b] (16 bytes each; slots b >= B hold zeros). With the token
-// fastest, 16 tokens x 4 consecutive chunks are one contiguous kilobyte. Item u in
+// fastest, all tokens of 4 consecutive chunks are one contiguous run. Item u in
 // [u0, nitems) step ustride is the pair (c = u / tbp, b = u % tbp).
 __device__ __forceinline__ void split_x_items(const float* __restrict__ x, int B, int d, int tbp,
                                               u32x4* __restrict__ x_hl, int u0, int ustride) {

@@ -5,9 +5,7 @@
 namespace sffn {
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-static size_t x_hl_bytes(int d, int max_batch) {
-  return (size_t)2 * (d / 8) * ((max_batch + 15) / 16 * 16) * 16;
-}
+static size_t x_hl_bytes(int d, int max_batch) { return (size_t)2 * (d / 8) * max_batch * 16; }
 
 size_t workspace_bytes(int d, int n, int r, int max_batch) {
   size_t b = 0;

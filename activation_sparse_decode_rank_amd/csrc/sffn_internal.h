@@ -45,7 +45,7 @@ struct LayerDev {
   int32_t* rs;         // [g_mid + 1] neuron ranges of the fused middle kernel (set at create)
   uint64_t* words;     // [ceil(n/64)] union bit words (compaction)
   void* x_hl;          // tokens split into fp16 hi/lo for the matrix-core up projection:
-                       // 2 x [d/8 chunks][max_batch rounded up to 16] x 16 bytes
+                       // 2 x [d/8 chunks][B token slots] x 16 bytes (sized for max_batch)
   uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
   // launch geometry fixed at create time
   int g_mid;     // workgroups of the fused middle kernel (<= G_MID_MAX)

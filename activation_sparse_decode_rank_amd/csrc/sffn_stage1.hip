@@ -229,7 +229,7 @@ void stage1_mt_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
   const int nchp = L.r / (F16 ? 8 : 4);
   const int nrt = (L.r + MT - 1) / MT;
   const int nmain = (nrt * ((B + BT - 1) / BT) + 7) / 8 * 8;
-  const int tbp = (B + 15) / 16 * 16;
+  const int tbp = B;  // token slots per chunk in x_hl
   const int nsplit = split_x ? (L.d / 8 * tbp + 4 * TPB - 1) / (4 * TPB) : 0;  // 4 items a thread
   launch(k_pred_stage1_mt<F16, MT, BT>, dim3(nmain + g_pf + nsplit), dim3(TPB), 0, s, tev, L.p1,
          x, L.d, L.r, B, L.q, y0, ny, nrt, nmain, g_pf, static_cast<u32x4*>(L.x_hl), tbp, nsplit,

@@ -239,7 +239,7 @@ __device__ __forceinline__ float4_t mfma16(const half8_t& a, const half8_t& b, c
 // l/16) would read 16 rows x 64 bytes per instruction, which streams gathered rows at about
 // two thirds of the rate. Each 64-input step pair passes through a small wave-private LDS
 // buffer into operand order. The activations come split in x_hl (the token fastest), so a
-// wave's operand load for one k-step is a contiguous kilobyte. Loads run one batch of KP
+// wave's operand load for one k-step is one contiguous run of B x 64 bytes. Loads run one batch of KP
 // step pairs ahead of the products.
 constexpr int FW_WORDS_MAX = 1024;  // union words the up kernel can list itself (n <= 65536)
 
@@ -260,7 +260,6 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
                                                     float* __restrict__ hT, int ldh,
                                                     float* __restrict__ y0, int ny) {
   constexpr int NM = GATED ? 2 : 1;
-  constexpr int TBP = 16 * NT;                        // token slots in x_hl
   constexpr int KP = (NT == 1 && TR == 1) ? 2 : 1;    // 64-input step pairs per load batch
   constexpr int PITCH = 9;                            // transpose buffer row pitch in chunks
   constexpr int RT = 16 * TR;                         // rows per workgroup iteration
@@ -325,8 +324,14 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   const int npairs = qch / 8;            // its 64-input step pairs
   const int c0 = wave * qch;
   const u32x4* wbase = reinterpret_cast<const u32x4*>(w_act);
-  const u32x4* xh = x_hl + r16;
-  const u32x4* xl = x_hl + (size_t)nch * TBP + r16;
+  // x_hl holds exactly B token slots per chunk; lanes of token tile columns past the batch
+  // re-read the last token's chunk (their products are never stored), so at a few tokens
+  // an operand load touches one or two cache lines, not a padded kilobyte
+  const u32x4* xh = x_hl;
+  const u32x4* xl = x_hl + (size_t)nch * B;
+  int tok[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) tok[tt] = min(16 * tt + r16, B - 1);
   u32x4* sw = &s_w[wave][0][0][0][0];
   const int et = wave < TR ? wave : 0;   // the tile whose epilogue this wave finishes
   for (int u = blockIdx.x; u * RT < cnt; u += gridDim.x) {
@@ -402,11 +407,11 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
           }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const size_t c = (size_t)(c0 + 8 * p + 4 * st + g) * TBP;
+          const size_t c = (size_t)(c0 + 8 * p + 4 * st + g) * B;
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
-            xv[bb][kp][st][tt][0] = xh[c + 16 * tt];
-            xv[bb][kp][st][tt][1] = xl[c + 16 * tt];
+            xv[bb][kp][st][tt][0] = xh[c + tok[tt]];
+            xv[bb][kp][st][tt][1] = xl[c + tok[tt]];
           }
         }
       }
@@ -781,9 +786,8 @@ void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                    bool fw, hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
   const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
   if (zero_y) {
-    const int tbp = (B + 15) / 16 * 16;
-    const int items = L.d / 8 * tbp;
-    hipLaunchKernelGGL(k_split_x, dim3((items + TPB - 1) / TPB), dim3(TPB), 0, s, x, B, L.d, tbp,
+    const int items = L.d / 8 * B;
+    hipLaunchKernelGGL(k_split_x, dim3((items + TPB - 1) / TPB), dim3(TPB), 0, s, x, B, L.d, B,
                        static_cast<u32x4*>(L.x_hl));
   }
   if (L.gated)
