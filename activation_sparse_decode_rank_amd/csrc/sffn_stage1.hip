@@ -264,6 +264,13 @@ void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s, cons
     stage1_mt_dispatch<F16>(L, x, B, s, tev, y0, ny, g_pf, split_x);
     return;
   }
+  // one token, rank 512 and up (e.g. the OPT-175B slice: 1024 rows of 12288): four rows per
+  // workgroup, so the token is read from L2 a quarter as often (every single-row workgroup
+  // reads all of it, twice the bytes of its own row)
+  if (L.r >= 512) {
+    stage1_mt_launch<F16, 4, 1>(L, x, B, s, tev, y0, ny, g_pf, split_x);
+    return;
+  }
   const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
   if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny, g_pf);
   else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny, g_pf);
