@@ -59,7 +59,9 @@ int tile_split(const LayerDev& L, bool deterministic) {
 
 int down_split(const LayerDev& L, bool deterministic) {
   const int ncb = down_blocks(L);
-  int ks = std::max(1, std::min(8, (L.n_cus + ncb / 2) / ncb));
+  // at least one workgroup per compute unit (a wide layer has more column blocks than
+  // half the compute units but fewer than all of them)
+  int ks = std::max(1, std::min(8, (L.n_cus + ncb - 1) / ncb));
   if (deterministic) ks = std::min(ks, 2);
   return ks;
 }
