@@ -139,19 +139,43 @@ __global__ __launch_bounds__(TPB) void k_score_tiles(const void* __restrict__ p2
   const int row = min(base + r16, n - 1);
   const int nck = kg / EPC;       // P2 chunks per lane
   const size_t c0 = (size_t)row * (r / EPC) + g;   // chunk 4u + g of the row
-  // the first batch of P2 loads goes out before q is staged (they do not depend on it)
+  // q comes from the previous kernel through the last-level cache. Its first batch of QB
+  // items per thread (item (k4, b) = 4 consecutive k of token b, clamped to B - 1) and the
+  // first batch of P2 loads all go out before anything waits; then q is stored to LDS
+  constexpr int QB = 8;
+  const int nq = (r / 4) * TP;
+  float4_t qv[QB];
+  auto q_load = [&](int u0) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int u = min(u0 + j * TPB + tid, nq - 1);
+      const int b = u % TP, k4 = u / TP;
+      qv[j] = *reinterpret_cast<const float4_t*>(q + (size_t)min(b, B - 1) * r + 4 * k4);
+    }
+  };
+  // items past the end repeat the last item (same value to the same place), so the
+  // stores carry no branch that the compiler could sink a load into
+  auto q_store = [&](int u0) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int u = min(u0 + j * TPB + tid, nq - 1);
+      const int b = u % TP, k4 = u / TP;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * k4 + e;
+        s_q[k * TP + (b ^ (16 * ((k / EPC) & 1)))] = qv[j][e];
+      }
+    }
+  };
+  q_load(0);
   u32x4 wv[CU];
 #pragma unroll
   for (int u = 0; u < CU; ++u) wv[u] = ld_stream(p2, c0 + 4 * (size_t)min(u, nck - 1));
-  // stage q: thread item (k4, b) = 4 consecutive k of token b (clamped to B - 1)
-  for (int u = tid; u < (r / 4) * TP; u += TPB) {
-    const int b = u % TP, k4 = u / TP;
-    const float4_t v = *reinterpret_cast<const float4_t*>(q + (size_t)min(b, B - 1) * r + 4 * k4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = 4 * k4 + e;
-      s_q[k * TP + (b ^ (16 * ((k / EPC) & 1)))] = v[e];
-    }
+  __builtin_amdgcn_sched_barrier(0);
+  q_store(0);
+  for (int u0 = QB * TPB; u0 < nq; u0 += QB * TPB) {
+    q_load(u0);
+    q_store(u0);
   }
   const float* qb[NT];
 #pragma unroll
@@ -586,7 +610,16 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
   for (wb = p0; wb < p1; wb += IDX_CAP) {
     wl = min(IDX_CAP, p1 - wb);
     __syncthreads();
-    for (int k = tid; k < wl; k += TPB) s_idx[k] = idx[wb + k];
+    // the list comes from the up kernel through the last-level cache: a batch of 8 entries
+    // per thread is loaded before any is stored (entries past the window repeat its last
+    // one, same value to the same place, so no store is conditional)
+    for (int k0 = 0; k0 < wl; k0 += 8 * TPB) {
+      int iv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) iv[j] = idx[wb + min(k0 + j * TPB + tid, wl - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_idx[min(k0 + j * TPB + tid, wl - 1)] = iv[j];
+    }
     __syncthreads();
     const int nck = (wl + DCH - 1) / DCH;        // chunks in this window
     const int mine = (nck - wave + 3) / 4;       // this wave's chunks: wave, wave + 4, ...
