@@ -303,13 +303,14 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   int ia[TR], ib[TR];
   int cnt;
   if constexpr (FW) {
-    for (int w = tid; w < nw; w += NTH) s_word[w] = words[w];
-    __syncthreads();
+    // thread t loads words t*PE .. t*PE + PE - 1 together (one round trip, any n)
     int loc[PE], sum = 0;
 #pragma unroll
     for (int e = 0; e < PE; ++e) {
       const int w = tid * PE + e;
-      loc[e] = w < nw ? __popcll(s_word[w]) : 0;
+      const uint64_t v = words[min(w, nw - 1)];
+      s_word[w] = v;
+      loc[e] = w < nw ? __popcll(v) : 0;
       sum += loc[e];
     }
     const int incl = wave_incl_scan(sum);

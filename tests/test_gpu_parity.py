@@ -141,12 +141,13 @@ SHAPES = [
     ("C3", 520, 900, 64, 16),       # d not a multiple of 256: the vector path at batch 16
     ("C2", 264, 700, 64, 12),       # the vector path at 12 tokens (two 8-token groups)
     ("C2", 1024, 3000, 256, 64),    # 64 tokens x rank 256: the largest q the score kernel stages
-    # input splits of the up tile kernel (few tiles: every tile split, parts summed in order)
-    ("C3", 4096, 1100, 128, 4),     # gated, four parts
-    ("C2", 4096, 1300, 128, 16),    # two row tiles per workgroup, four parts
-    ("C2", 2048, 1200, 128, 24),    # two token tiles, four parts
+    # wide inputs on the tile path
+    ("C3", 4096, 1100, 128, 4),     # gated, full model width
+    ("C2", 4096, 1300, 128, 16),    # two row tiles per workgroup
+    ("C2", 2048, 1200, 128, 24),    # two token tiles
     ("C3", 2048, 1500, 128, 64),    # four token tiles
-    ("C5", 12288, 900, 128, 3),     # eight parts
+    ("C5", 12288, 900, 128, 3),     # the OPT-175B width
+    ("C2", 256, 20000, 64, 4),      # more union words than the up kernel has threads
 ]
 
 
