@@ -477,10 +477,12 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     // loads ahead of the products before their use; the scheduler would otherwise sink
     // them to their first use); then the leftover pairs one at a time
     const int nfull = npairs / (2 * KP) * (2 * KP);
-    // the epilogue's list entries and token bits (lane: positions 4g + j of tile et) go
-    // out behind the first weight batch; by the time they are used they have long landed
+    // the epilogue's list entries, token bits and biases (lane: positions 4g + j of tile
+    // et) go out behind the first weight batch; by the time they are used they have long
+    // landed
     int ej[4];
     uint64_t em[4];
+    float eb[4];
     auto load_epilogue = [&]() {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -492,6 +494,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
           ej[j] = idx[pc];
           em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
         }
+        eb[j] = (b_act && ej[j] >= 0 && ej[j] < n) ? b_act[ej[j]] : 0.f;
       }
     };
     if (nfull > 0) {
@@ -513,9 +516,6 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
       load(p, 0);
       mult(0, std::integral_constant<int, 1>{});
     }
-    float eb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) eb[j] = (b_act && ej[j] >= 0 && ej[j] < n) ? b_act[ej[j]] : 0.f;
 #pragma unroll
     for (int i = 0; i < TR; ++i)
 #pragma unroll
@@ -714,22 +714,33 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
     for (int tt = 0; tt < NT; ++tt) s_acc[wave][cg][tt][lane] = acc[cg][tt];
   __syncthreads();
   if (kq == 0 || p1 > p0) {
-    for (int o = tid; o < 4 * NT * 64; o += TPB) {
+    // 4 * NT * 64 outputs, NT per thread: a fixed trip count, so the b_out loads of all
+    // of them go out together
+    static_assert(4 * 64 == TPB, "one output per thread and token tile");
+    float bo[NT];
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int o = it * TPB + tid;
+      const int col = cb * 64 + 16 * (o / (NT * 64)) + (o & 15);
+      bo[it] = (kq == 0 && b_out && col < d) ? b_out[col] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int o = it * TPB + tid;
       const int cg = o / (NT * 64), tt = (o / 64) % NT, l = o % 64;
       const float4_t v = ((s_acc[0][cg][tt][l] + s_acc[1][cg][tt][l]) + s_acc[2][cg][tt][l]) +
                          s_acc[3][cg][tt][l];
       const int col = cb * 64 + 16 * cg + (l & 15);
       if (col < d) {
-        const float bo = (kq == 0 && b_out) ? b_out[col] : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int b = 16 * tt + 4 * (l >> 4) + j;
           if (b < B) {
             float* dst = y + (size_t)b * d + col;
             if (KS == 1)
-              *dst = v[j] + bo;
+              *dst = v[j] + bo[it];
             else
-              atomicAdd(dst, v[j] + bo);
+              atomicAdd(dst, v[j] + bo[it]);
           }
         }
       }
