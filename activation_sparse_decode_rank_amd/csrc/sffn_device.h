@@ -196,22 +196,34 @@ __device__ __forceinline__ void split_hi_lo(const float4_t& a, const float4_t& b
 // halves of x_b[8c .. 8c+7] at x_hl[c * tbp + b] and the lo halves at
 // x_hl[(d/8 + c) * tbp + b] (16 bytes each; slots b >= B hold zeros). With the token
 // fastest, all tokens of 4 consecutive chunks are one contiguous run. Item u in
-// [u0, nitems) step ustride is the pair (c = u / tbp, b = u % tbp).
+// [u0, nitems) step ustride is the pair (c = u / tbp, b = u % tbp). A thread's items go in
+// batches of 4 whose loads are all issued before any is used (the tokens come cold from
+// HBM; one round trip per batch, not per item). Items past the end repeat the last item,
+// the same value to the same place, so no store is conditional.
 __device__ __forceinline__ void split_x_items(const float* __restrict__ x, int B, int d, int tbp,
                                               u32x4* __restrict__ x_hl, int u0, int ustride) {
-  const int nch = d / 8;
-  for (int u = u0; u < nch * tbp; u += ustride) {
-    const int c = u / tbp, b = u % tbp;
-    float4_t a = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
-    if (b < B) {
+  constexpr int IPT = 4;
+  const int nch = d / 8, nitems = nch * tbp;
+  for (int ub = u0; ub < nitems; ub += IPT * ustride) {
+    float4_t a[IPT], e[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = min(ub + i * ustride, nitems - 1);
+      const int c = u / tbp, b = min(u % tbp, B - 1);
       const float4_t* p = reinterpret_cast<const float4_t*>(x + (size_t)b * d + (size_t)c * 8);
-      a = p[0];
-      e = p[1];
+      a[i] = p[0];
+      e[i] = p[1];
     }
-    half8_t hi, lo;
-    split_hi_lo(a, e, hi, lo);
-    x_hl[(size_t)c * tbp + b] = __builtin_bit_cast(u32x4, hi);
-    x_hl[(size_t)(nch + c) * tbp + b] = __builtin_bit_cast(u32x4, lo);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = min(ub + i * ustride, nitems - 1);
+      const int c = u / tbp, b = u % tbp;
+      if (b >= B) a[i] = e[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+      half8_t hi, lo;
+      split_hi_lo(a[i], e[i], hi, lo);
+      x_hl[(size_t)c * tbp + b] = __builtin_bit_cast(u32x4, hi);
+      x_hl[(size_t)(nch + c) * tbp + b] = __builtin_bit_cast(u32x4, lo);
+    }
   }
 }
 

@@ -33,9 +33,14 @@ __device__ __forceinline__ void prefetch_mid_range(int w, const void* __restrict
   const int tid = threadIdx.x;
   const int r0 = ra.r[w], r1 = ra.r[w + 1];
   const int c0 = r0 * nchp, nc = (r1 - r0) * nchp;
-  u32x4 pv[PF_PER_THREAD];
+  // one 4-byte load per 16-byte chunk: every 128-byte line of the range is still touched
+  // (8 lanes per line), and the loads have distinct destination registers, so none waits
+  // for another (a 16-byte load of which only a quarter is used let the compiler overlap
+  // destinations and wait between loads)
+  const uint32_t* p2w = reinterpret_cast<const uint32_t*>(p2);
+  uint32_t pv[PF_PER_THREAD];
 #pragma unroll
-  for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = ld_chunk(p2, c0 + min(tid + v * TPB, nc - 1));
+  for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = p2w[4 * (size_t)(c0 + min(tid + v * TPB, nc - 1))];
   float b0 = 0.f, b1 = 0.f;
   if (tid < r1 - r0) {
     if (pfb0) b0 = pfb0[r0 + tid];
@@ -43,7 +48,7 @@ __device__ __forceinline__ void prefetch_mid_range(int w, const void* __restrict
   }
   unsigned sink = __float_as_uint(b0) ^ __float_as_uint(b1);
 #pragma unroll
-  for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v].x;
+  for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v];
   asm volatile("" ::"v"(sink));
 }
 template <bool PF16, int TBG, int NCPT>
