@@ -188,6 +188,15 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.ks_down = sffn::down_split(L, desc->deterministic != 0);
     L.ks_tile = sffn::tile_split(L, desc->deterministic != 0);
     L.g_up = std::max(1, std::min((desc->d_ffn + 15) / 16, 4 * cus));
+    // stream-K up projection: two workgroups per compute unit, and enough that one
+    // range touches at most 13 tiles of the largest list
+    L.g_sk = std::min(sffn::SK_G_MAX, std::max(2 * cus, ((desc->d_ffn + 15) / 16 + 12) / 13));
+    if (L.sk_part) {
+      // its arrival counters start at zero; every call leaves them zero
+      if (hipMemset(L.sk_cnt, 0, (size_t)((desc->d_ffn + 15) / 16 + 1) * 4) != hipSuccess ||
+          hipStreamSynchronize(nullptr) != hipSuccess)
+        return SFFN_ERR_HIP;
+    }
 
     // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
     // of the active ones; as many ranges as can be resident at once, at most G_MID_MAX

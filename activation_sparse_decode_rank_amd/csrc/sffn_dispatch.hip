@@ -6,6 +6,8 @@ namespace sffn {
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static size_t x_hl_bytes(int d, int max_batch) { return (size_t)2 * (d / 8) * max_batch * 16; }
+static size_t sk_part_bytes(int max_batch) { return max_batch >= TILE_MIN_B ? SK_PART_BYTES : 0; }
+static size_t sk_cnt_bytes(int n) { return (size_t)((n + 15) / 16 + 1) * 4; }
 
 size_t workspace_bytes(int d, int n, int r, int max_batch) {
   size_t b = 0;
@@ -16,6 +18,8 @@ size_t workspace_bytes(int d, int n, int r, int max_batch) {
   b += align256((size_t)((n + 63) / 64) * 8);    // words
   b += align256((size_t)G_MID_MAX * 8);          // wbits
   b += align256(x_hl_bytes(d, max_batch));       // x_hl
+  b += align256(sk_part_bytes(max_batch));       // sk_part
+  b += align256(sk_cnt_bytes(n));                // sk_cnt
   return b;
 }
 
@@ -32,6 +36,8 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   L.words = reinterpret_cast<uint64_t*>(take((size_t)((n + 63) / 64) * 8));
   L.wbits = reinterpret_cast<uint64_t*>(take((size_t)G_MID_MAX * 8));
   L.x_hl = take(x_hl_bytes(L.d, max_batch));
+  L.sk_part = sk_part_bytes(max_batch) ? reinterpret_cast<float*>(take(sk_part_bytes(max_batch))) : nullptr;
+  L.sk_cnt = reinterpret_cast<int32_t*>(take(sk_cnt_bytes(n)));
   L.n_tiles = n_tiles;
 }
 

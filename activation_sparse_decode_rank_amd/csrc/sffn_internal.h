@@ -47,6 +47,8 @@ struct LayerDev {
   void* x_hl;          // tokens split into fp16 hi/lo for the matrix-core up projection:
                        // 2 x [d/8 chunks][B token slots] x 16 bytes (sized for max_batch)
   uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
+  float* sk_part;      // stream-K up projection: two part slots per workgroup (null: unused)
+  int32_t* sk_cnt;     // [ceil(n/16) + 1] arrival counters of its tiles (zero between calls)
   // launch geometry fixed at create time
   int g_mid;     // workgroups of the fused middle kernel (<= G_MID_MAX)
   int n_tiles;   // compaction tiles of 256 neurons
@@ -57,6 +59,7 @@ struct LayerDev {
   int ks_tile;   // the same for the batch (matrix-core) down projection
   int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64, plus 64)
   int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
+  int g_sk;      // workgroups of its stream-K form (at most SK_G_MAX)
   bool rs_in_arg;  // the range table travels in the middle kernel's arguments (ra)
   RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)
   SplitArg sa;     // decode down projection: range splits, ks_down of them
@@ -74,6 +77,11 @@ int tile_split(const LayerDev& L, bool deterministic);
 bool shape_supported(const LayerDev& L, bool fused);
 // middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch
 int mid_resident_groups(const LayerDev& L, int max_batch);
+
+// Stream-K up projection: most workgroups, and the bytes of their part slots (two slots of
+// 2 matrices x 2 token tiles x 64 lanes x 4 floats each)
+constexpr int SK_G_MAX = 512;
+constexpr size_t SK_PART_BYTES = (size_t)2 * SK_G_MAX * 2 * 2 * 64 * 4 * 4;
 
 // From this many tokens on (fp16 weights, d a multiple of 128) the decode and forward
 // entry points run the gathered-tile matrix-core kernels.

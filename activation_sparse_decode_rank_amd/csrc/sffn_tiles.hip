@@ -552,6 +552,330 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   }
 }
 
+// Stream-K form of the up projection in the decode step (union listed from the words,
+// two token tiles). The work is the list's 16-row tiles times their KBT input blocks
+// (block kb of a tile: wave w sums its pairs 2 (kb W + w) and 2 (kb W + w) + 1 of 64
+// inputs each), flattened tile-major. Workgroup g of the G' = min(G, 2 x tiles) that take
+// part gets the equal contiguous range [g T / G', (g + 1) T / G') of the T blocks, so every
+// compute unit streams about the same bytes whatever the union's size: whole tiles per
+// workgroup leave compute units idle when there are fewer tiles than workgroups, and give
+// a few a second round when there are slightly more. Loads run one pair ahead across
+// block and tile boundaries.
+// A range is at least half a tile long, so a tile has at most 3 parts. A tile inside one
+// range is finished there. A part of a split tile (at most two per workgroup: the tile
+// its range starts in and the one it ends in) has its W-wave sum published with
+// device-coherent stores in slot 2g (the range's first tile) or 2g + 1 (its last); the
+// part that arrives last at the tile's counter adds the parts in workgroup order (the sum
+// does not depend on arrival order), finishes the epilogue, writes the tile's list
+// entries and resets the counter to zero for the next call.
+constexpr int SK_TMAX = 16;   // tiles one range may touch (listed in LDS at once)
+constexpr int SK_PMAX = 3;    // parts of one tile
+template <bool GATED, int NT, int W>
+__global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act,
+                                                  const float* __restrict__ b_act,
+                                                  const u32x4* __restrict__ x_hl, int d,
+                                                  int n, int B, int32_t* __restrict__ idx,
+                                                  int32_t* __restrict__ count,
+                                                  uint64_t* __restrict__ tokmask,
+                                                  const uint64_t* __restrict__ words,
+                                                  const uint64_t* __restrict__ tok_full,
+                                                  float* __restrict__ hT, int ldh,
+                                                  float* __restrict__ y0, int ny,
+                                                  float* __restrict__ part,
+                                                  int32_t* __restrict__ tcnt) {
+  constexpr int NM = GATED ? 2 : 1;
+  constexpr int PITCH = 9;
+  constexpr int NTH = 64 * W;
+  constexpr int PE = (FW_WORDS_MAX + NTH - 1) / NTH;
+  constexpr int NO = NM * NT * 4 * 64;   // floats of one part
+  static_assert(SK_TMAX * 16 <= NTH, "one listing pass");
+  __shared__ u32x4 s_w[W][NM][16 * PITCH];
+  __shared__ float4_t s_acc[W][NM][NT][64];
+  __shared__ int32_t s_pref[FW_WORDS_MAX + 1];
+  __shared__ uint64_t s_word[FW_WORDS_MAX];
+  __shared__ int32_t s_rows[SK_TMAX * 16];
+  __shared__ int32_t s_wsum[W];
+  for (int i = blockIdx.x * NTH + threadIdx.x; i < ny; i += gridDim.x * NTH) y0[i] = 0.f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;
+  const int nw = (n + 63) / 64;
+  // ---- prefix sums of the union words (each thread loads its PE words in one batch)
+  int loc[PE], sum = 0;
+#pragma unroll
+  for (int e = 0; e < PE; ++e) {
+    const int w = tid * PE + e;
+    const uint64_t v = words[min(w, nw - 1)];
+    s_word[w] = v;
+    loc[e] = w < nw ? __popcll(v) : 0;
+    sum += loc[e];
+  }
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    run += v < wave ? s_wsum[v] : 0;
+    total += s_wsum[v];
+  }
+#pragma unroll
+  for (int e = 0; e < PE; ++e) {
+    const int w = tid * PE + e;
+    if (w < nw) s_pref[w] = run;
+    run += loc[e];
+  }
+  if (tid == 0) s_pref[nw] = total;
+  if (blockIdx.x == 0 && tid == 0) *count = total;
+  const int cnt = min(total, n);
+  __syncthreads();
+  // ---- this workgroup's range of blocks
+  const int nch = d / 8, rowch = NM * nch;
+  const int KBT = nch / (16 * W);
+  const int ntiles = (cnt + 15) / 16;
+  const long long T = (long long)ntiles * KBT;
+  const int G = min((int)gridDim.x, 2 * ntiles);
+  const int gi = blockIdx.x;
+  if (gi >= G) return;  // uniform; also covers an empty list
+  auto start_of = [&](long long gg) { return gg * T / G; };
+  auto owner_of = [&](long long j) { return (int)(((j + 1) * G - 1) / T); };
+  const long long j0 = start_of(gi), j1 = start_of(gi + 1);
+  const int t_first = (int)(j0 / KBT), t_last = (int)((j1 - 1) / KBT);
+  // ---- rows of tiles t_first .. t_last: list position p is the k-th set bit of the word
+  // w with pref[w] <= p < pref[w + 1] (binary search over the prefixes)
+  if (tid < (t_last - t_first + 1) * 16) {
+    const int p = min(t_first * 16 + tid, cnt - 1);
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    uint64_t v = s_word[lo];
+    int k = p - s_pref[lo], bit = 0;
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) {
+      const uint64_t low = (((uint64_t)1) << sft) - 1;
+      const int c = __popcll(v & low);
+      if (k >= c) {
+        k -= c;
+        v >>= sft;
+        bit += sft;
+      } else {
+        v &= low;
+      }
+    }
+    s_rows[tid] = lo * 64 + bit;
+  }
+  __syncthreads();
+  // ---- the stream
+  const u32x4* wbase = reinterpret_cast<const u32x4*>(w_act);
+  const u32x4* xh = x_hl;
+  const u32x4* xl = x_hl + (size_t)nch * B;
+  int tok[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) tok[tt] = min(16 * tt + r16, B - 1);
+  u32x4* sw = &s_w[wave][0][0];
+  const u32x4* pa;
+  const u32x4* pb;
+  auto set_rows = [&](int t) {
+    const int ra = s_rows[(t - t_first) * 16 + lr], rb = s_rows[(t - t_first) * 16 + 8 + lr];
+    pa = wbase + (size_t)((ra >= 0 && ra < n) ? ra : 0) * rowch + lc;
+    pb = wbase + (size_t)((rb >= 0 && rb < n) ? rb : 0) * rowch + lc;
+  };
+  u32x4 wa[2][NM], wb[2][NM], xv[2][2][NT][2];
+  // pair q (of the row's d / 64) of the current rows into buffer bb
+  auto load = [&](int q, int bb) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      wa[bb][m] = ld_stream(pa, (size_t)m * nch + 8 * q);
+      wb[bb][m] = ld_stream(pb, (size_t)m * nch + 8 * q);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const size_t c = (size_t)(8 * q + 4 * st + g) * B;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        xv[bb][st][tt][0] = xh[c + tok[tt]];
+        xv[bb][st][tt][1] = xl[c + tok[tt]];
+      }
+    }
+  };
+  float4_t acc[NM][NT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  auto mult = [&](int bb) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      u32x4* bw = sw + m * 16 * PITCH;
+      bw[lr * PITCH + lc] = wa[bb][m];
+      bw[(8 + lr) * PITCH + lc] = wb[bb][m];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const half8_t w8 =
+            __builtin_bit_cast(half8_t, sw[m * 16 * PITCH + r16 * PITCH + 4 * st + g]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][0]), acc[m][tt]);
+          acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][1]), acc[m][tt]);
+        }
+      }
+    wave_lds_sync();
+  };
+  // epilogue inputs of tile t (positions 4g + j): rows, token bits, biases
+  int ej[4];
+  uint64_t em[4];
+  float eb[4];
+  auto load_ep = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ej[j] = s_rows[(t - t_first) * 16 + 4 * g + j];
+      em[j] = tok_full[ej[j]];
+      eb[j] = b_act ? b_act[ej[j]] : 0.f;
+    }
+  };
+  // the end of tile t's segment [seg0, jend]: the W-wave sum, then the tile's epilogue
+  // here or a published part
+  auto flush = [&](int t, long long seg0, long long jend) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) s_acc[wave][m][tt][lane] = acc[m][tt];
+    __syncthreads();
+    if (wave == 0) {
+      float4_t v[NM][NT];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          v[m][tt] = s_acc[0][m][tt][lane];
+#pragma unroll
+          for (int ww = 1; ww < W; ++ww) v[m][tt] += s_acc[ww][m][tt][lane];
+        }
+      const long long tb = (long long)t * KBT;
+      bool fin = true;
+      if (!(seg0 == tb && jend == tb + KBT - 1)) {
+        float* pt = part + (size_t)(2 * gi + (j0 >= tb ? 0 : 1)) * NO;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              __hip_atomic_store(pt + ((m * NT + tt) * 4 + c) * 64 + lane, v[m][tt][c],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int glo = owner_of(tb), np = owner_of(tb + KBT - 1) - glo + 1;
+        int old = 0;
+        if (lane == 0)
+          old = __hip_atomic_fetch_add(tcnt + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0);
+        fin = old == np - 1;
+        if (fin) {
+          asm volatile("" ::: "memory");
+          // every part's loads first (parts past np repeat the last), then the sum in
+          // workgroup order
+          float pv[SK_PMAX][NM][NT][4];
+#pragma unroll
+          for (int q = 0; q < SK_PMAX; ++q) {
+            const int gg = glo + min(q, np - 1);
+            const float* pq = part + (size_t)(2 * gg + (start_of(gg) >= tb ? 0 : 1)) * NO;
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  pv[q][m][tt][c] = __hip_atomic_load(pq + ((m * NT + tt) * 4 + c) * 64 + lane,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                float a = pv[0][m][tt][c];
+#pragma unroll
+                for (int q = 1; q < SK_PMAX; ++q) a += q < np ? pv[q][m][tt][c] : 0.f;
+                v[m][tt][c] = a;
+              }
+          if (lane == 0) __hip_atomic_store(tcnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (fin) {
+        if (r16 == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int p = t * 16 + 4 * g + j;
+            if (p < cnt) {
+              idx[p] = ej[j];
+              if (tokmask) tokmask[p] = em[j];
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const int b = tt * 16 + r16;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int p = t * 16 + 4 * g + j;
+            if (p < cnt && b < B) {
+              const float a0 = v[0][tt][j] + eb[j];
+              float h = a0 > 0.f ? a0 : 0.f;
+              if (GATED) h *= v[NM - 1][tt][j];
+              hT[(size_t)b * ldh + p] = ((em[j] >> b) & 1) ? h : 0.f;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  long long j = j0, seg0 = j0;
+  int t = t_first, kb = (int)(j0 - (long long)t_first * KBT);
+  set_rows(t);
+  load(2 * (kb * W + wave), 0);
+  load_ep(t);
+  while (true) {
+    // block j: its first pair sits in buffer 0, its second goes to buffer 1
+    load(2 * (kb * W + wave) + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mult(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const long long jn = j + 1;
+    const bool more = jn < j1;
+    const bool next_tile = kb + 1 == KBT;
+    const int kbn = next_tile ? 0 : kb + 1;
+    if (more) {
+      if (next_tile) set_rows(t + 1);
+      load(2 * (kbn * W + wave), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mult(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more || next_tile) {
+      flush(t, seg0, j);
+      if (!more) break;
+      t = t + 1;
+      seg0 = jn;
+      load_ep(t);
+    }
+    j = jn;
+    kb = kbn;
+  }
+}
+
 // Standalone token split (the forward entry point has no stage 1 to do it).
 __global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, int B, int d,
                                                  int tbp, u32x4* __restrict__ x_hl) {
@@ -795,11 +1119,39 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
 // the pairs then outnumber the compute units (measured no faster at 32 tokens); below 16
 // tokens eight waves on one row tile measured slower (2 tokens 18.3 vs 17.5 us, 8 tokens
 // 30.9 vs 26.7 us on the Llama-7B shape).
+template <bool GATED, int NT>
+void up_sk_launch(const LayerDev& L, int B, int32_t* idx, int32_t* count, uint64_t* tokmask,
+                  float* y0, int ny, hipStream_t s, const hipEvent_t* tev) {
+  launch(k_up_sk<GATED, NT, 4>, dim3(L.g_sk), dim3(256), 0, s, tev, L.w_act, L.b_act,
+         static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask,
+         (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny,
+         L.sk_part, L.sk_cnt);
+}
+
+// the stream-K form: the decode step's list from the words, two token tiles, d a
+// multiple of 512 with at least two input blocks per tile, and ranges that touch at most
+// SK_TMAX tiles (g_sk >= tiles / 13). Measured on the Llama-7B-shaped gated stack it
+// gains at 32 tokens (82.9 vs 84.4 us a layer) and loses below 17: at 16 tokens the
+// two-tile eight-wave form, whose activation fragments serve two row tiles, is faster
+// (51.0 vs 55.2 us), and at 4 tokens every tile is split and the hand-offs cost more than
+// the balance gains (35.3 vs 33.1 us).
+bool up_sk_ok(const LayerDev& L, int B, bool fw) {
+  return fw && L.sk_part && B > 16 && B <= 32 && L.d % 512 == 0 && L.d >= 1024 &&
+         L.g_sk * 13 >= (L.n + 15) / 16;
+}
+
 template <bool GATED>
 void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                     const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
                     const hipEvent_t* tev, bool fw) {
   const int nt = (B + 15) / 16;
+  if (up_sk_ok(L, B, fw)) {
+    int32_t* idx_w = const_cast<int32_t*>(idx);
+    int32_t* cnt_w = const_cast<int32_t*>(count);
+    uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
+    up_sk_launch<GATED, 2>(L, B, idx_w, cnt_w, tok_w, y0, ny, s, tev);
+    return;
+  }
   if (B >= 16 && nt == 1 && L.d % 512 == 0) {
     up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, y0, ny, s, tev, fw);
     return;
