@@ -229,6 +229,7 @@ __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
                                              float (&acc)[Elt<WF16>::EPC]) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int LD = 16;
+  static_assert(RSD * LD == DOWN_B1_BATCH, "batch size the split count is chosen for");
   for (int kb0 = 0; kb0 < wl; kb0 += RSD * LD) {
     int ii[LD];
 #pragma unroll

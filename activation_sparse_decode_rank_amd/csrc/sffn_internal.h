@@ -21,6 +21,9 @@ struct RangeArg {
 // Row splits of the decode down projection: split k covers middle-kernel ranges
 // [s[k], s[k+1]), cut so that the splits expect about equal numbers of active neurons.
 constexpr int KS_MAX = 16;
+// rows one workgroup of the single-token down projection gathers in one batch (32 row
+// slots x 16 rows in flight each)
+constexpr int DOWN_B1_BATCH = 512;
 struct SplitArg {
   int32_t s[KS_MAX + 1];
 };
