@@ -552,10 +552,10 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   }
 }
 
-// Stream-K form of the up projection in the decode step (union listed from the words,
-// two token tiles). The work is the list's 16-row tiles times their KBT input blocks
-// (block kb of a tile: wave w sums its pairs 2 (kb W + w) and 2 (kb W + w) + 1 of 64
-// inputs each), flattened tile-major. Workgroup g of the G' = min(G, 2 x tiles) that take
+// Stream-K form of the up projection in the decode step (union listed from the words).
+// The work is the list's tiles of TR 16-row tiles times their KBT input blocks (block kb
+// of a tile: wave w sums its pairs 2 (kb W + w) and 2 (kb W + w) + 1 of 64 inputs each,
+// each activation fragment serving the TR row tiles), flattened tile-major. Workgroup g of the G' = min(G, 2 x tiles) that take
 // part gets the equal contiguous range [g T / G', (g + 1) T / G') of the T blocks, so every
 // compute unit streams about the same bytes whatever the union's size: whole tiles per
 // workgroup leave compute units idle when there are fewer tiles than workgroups, and give
@@ -564,13 +564,14 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 // A range is at least half a tile long, so a tile has at most 3 parts. A tile inside one
 // range is finished there. A part of a split tile (at most two per workgroup: the tile
 // its range starts in and the one it ends in) has its W-wave sum published with
-// device-coherent stores in slot 2g (the range's first tile) or 2g + 1 (its last); the
-// part that arrives last at the tile's counter adds the parts in workgroup order (the sum
+// device-coherent stores in slot 2g (the range's first tile) or 2g + 1 (its last), one
+// sub-slot per row tile; the part that arrives last at the row tile's counter (wave i
+// finishes row tile i) adds the parts in workgroup order (the sum
 // does not depend on arrival order), finishes the epilogue, writes the tile's list
 // entries and resets the counter to zero for the next call.
 constexpr int SK_TMAX = 16;   // tiles one range may touch (listed in LDS at once)
 constexpr int SK_PMAX = 3;    // parts of one tile
-template <bool GATED, int NT, int W>
+template <bool GATED, int NT, int TR, int W>
 __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act,
                                                   const float* __restrict__ b_act,
                                                   const u32x4* __restrict__ x_hl, int d,
@@ -587,13 +588,14 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   constexpr int PITCH = 9;
   constexpr int NTH = 64 * W;
   constexpr int PE = (FW_WORDS_MAX + NTH - 1) / NTH;
-  constexpr int NO = NM * NT * 4 * 64;   // floats of one part
-  static_assert(SK_TMAX * 16 <= NTH, "one listing pass");
-  __shared__ u32x4 s_w[W][NM][16 * PITCH];
-  __shared__ float4_t s_acc[W][NM][NT][64];
+  constexpr int RT = 16 * TR;            // rows per tile (TR row tiles of 16)
+  constexpr int NO = NM * NT * 4 * 64;   // floats of one part of one row tile
+  static_assert(SK_TMAX * RT <= NTH, "one listing pass");
+  __shared__ u32x4 s_w[W][TR][NM][16 * PITCH];
+  __shared__ float4_t s_acc[W][TR][NM][NT][64];
   __shared__ int32_t s_pref[FW_WORDS_MAX + 1];
   __shared__ uint64_t s_word[FW_WORDS_MAX];
-  __shared__ int32_t s_rows[SK_TMAX * 16];
+  __shared__ int32_t s_rows[SK_TMAX * RT];
   __shared__ int32_t s_wsum[W];
   for (int i = blockIdx.x * NTH + threadIdx.x; i < ny; i += gridDim.x * NTH) y0[i] = 0.f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   // ---- this workgroup's range of blocks
   const int nch = d / 8, rowch = NM * nch;
   const int KBT = nch / (16 * W);
-  const int ntiles = (cnt + 15) / 16;
+  const int ntiles = (cnt + RT - 1) / RT;
   const long long T = (long long)ntiles * KBT;
   const int G = min((int)gridDim.x, 2 * ntiles);
   const int gi = blockIdx.x;
@@ -643,8 +645,8 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   const int t_first = (int)(j0 / KBT), t_last = (int)((j1 - 1) / KBT);
   // ---- rows of tiles t_first .. t_last: list position p is the k-th set bit of the word
   // w with pref[w] <= p < pref[w + 1] (binary search over the prefixes)
-  if (tid < (t_last - t_first + 1) * 16) {
-    const int p = min(t_first * 16 + tid, cnt - 1);
+  if (tid < (t_last - t_first + 1) * RT) {
+    const int p = min(t_first * RT + tid, cnt - 1);
     int lo = 0, hi = nw - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -675,22 +677,28 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   int tok[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) tok[tt] = min(16 * tt + r16, B - 1);
-  u32x4* sw = &s_w[wave][0][0];
-  const u32x4* pa;
-  const u32x4* pb;
+  u32x4* sw = &s_w[wave][0][0][0];
+  const u32x4* pa[TR];
+  const u32x4* pb[TR];
   auto set_rows = [&](int t) {
-    const int ra = s_rows[(t - t_first) * 16 + lr], rb = s_rows[(t - t_first) * 16 + 8 + lr];
-    pa = wbase + (size_t)((ra >= 0 && ra < n) ? ra : 0) * rowch + lc;
-    pb = wbase + (size_t)((rb >= 0 && rb < n) ? rb : 0) * rowch + lc;
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      const int ra = s_rows[(t - t_first) * RT + 16 * i + lr];
+      const int rb = s_rows[(t - t_first) * RT + 16 * i + 8 + lr];
+      pa[i] = wbase + (size_t)((ra >= 0 && ra < n) ? ra : 0) * rowch + lc;
+      pb[i] = wbase + (size_t)((rb >= 0 && rb < n) ? rb : 0) * rowch + lc;
+    }
   };
-  u32x4 wa[2][NM], wb[2][NM], xv[2][2][NT][2];
+  u32x4 wa[2][TR][NM], wb[2][TR][NM], xv[2][2][NT][2];
   // pair q (of the row's d / 64) of the current rows into buffer bb
   auto load = [&](int q, int bb) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      wa[bb][m] = ld_stream(pa, (size_t)m * nch + 8 * q);
-      wb[bb][m] = ld_stream(pb, (size_t)m * nch + 8 * q);
-    }
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        wa[bb][i][m] = ld_stream(pa[i], (size_t)m * nch + 8 * q);
+        wb[bb][i][m] = ld_stream(pb[i], (size_t)m * nch + 8 * q);
+      }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const size_t c = (size_t)(8 * q + 4 * st + g) * B;
@@ -701,41 +709,49 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
       }
     }
   };
-  float4_t acc[NM][NT];
+  float4_t acc[TR][NM][NT];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+  for (int i = 0; i < TR; ++i)
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[i][m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
   auto mult = [&](int bb) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      u32x4* bw = sw + m * 16 * PITCH;
-      bw[lr * PITCH + lc] = wa[bb][m];
-      bw[(8 + lr) * PITCH + lc] = wb[bb][m];
-    }
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        u32x4* bw = sw + (i * NM + m) * 16 * PITCH;
+        bw[lr * PITCH + lc] = wa[bb][i][m];
+        bw[(8 + lr) * PITCH + lc] = wb[bb][i][m];
+      }
     wave_lds_sync();
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const half8_t w8 =
-            __builtin_bit_cast(half8_t, sw[m * 16 * PITCH + r16 * PITCH + 4 * st + g]);
+      for (int i = 0; i < TR; ++i)
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][0]), acc[m][tt]);
-          acc[m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][1]), acc[m][tt]);
+        for (int m = 0; m < NM; ++m) {
+          const half8_t w8 = __builtin_bit_cast(
+              half8_t, sw[(i * NM + m) * 16 * PITCH + r16 * PITCH + 4 * st + g]);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            acc[i][m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][0]), acc[i][m][tt]);
+            acc[i][m][tt] = mfma16(w8, __builtin_bit_cast(half8_t, xv[bb][st][tt][1]), acc[i][m][tt]);
+          }
         }
-      }
     wave_lds_sync();
   };
-  // epilogue inputs of tile t (positions 4g + j): rows, token bits, biases
+  // epilogue inputs of row tile et of tile t (positions 4g + j): rows, token bits, biases;
+  // wave et < TR finishes row tile et
+  const int et = wave < TR ? wave : 0;
   int ej[4];
   uint64_t em[4];
   float eb[4];
   auto load_ep = [&](int t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ej[j] = s_rows[(t - t_first) * 16 + 4 * g + j];
+      ej[j] = s_rows[(t - t_first) * RT + 16 * et + 4 * g + j];
       em[j] = tok_full[ej[j]];
       eb[j] = b_act ? b_act[ej[j]] : 0.f;
     }
@@ -744,24 +760,26 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   // here or a published part
   auto flush = [&](int t, long long seg0, long long jend) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < TR; ++i)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) s_acc[wave][m][tt][lane] = acc[m][tt];
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) s_acc[wave][i][m][tt][lane] = acc[i][m][tt];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < TR) {
       float4_t v[NM][NT];
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          v[m][tt] = s_acc[0][m][tt][lane];
+          v[m][tt] = s_acc[0][et][m][tt][lane];
 #pragma unroll
-          for (int ww = 1; ww < W; ++ww) v[m][tt] += s_acc[ww][m][tt][lane];
+          for (int ww = 1; ww < W; ++ww) v[m][tt] += s_acc[ww][et][m][tt][lane];
         }
       const long long tb = (long long)t * KBT;
       bool fin = true;
       if (!(seg0 == tb && jend == tb + KBT - 1)) {
-        float* pt = part + (size_t)(2 * gi + (j0 >= tb ? 0 : 1)) * NO;
+        float* pt = part + ((size_t)(2 * gi + (j0 >= tb ? 0 : 1)) * TR + et) * NO;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -774,7 +792,7 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
         const int glo = owner_of(tb), np = owner_of(tb + KBT - 1) - glo + 1;
         int old = 0;
         if (lane == 0)
-          old = __hip_atomic_fetch_add(tcnt + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          old = __hip_atomic_fetch_add(tcnt + t * TR + et, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
         fin = old == np - 1;
         if (fin) {
@@ -785,7 +803,7 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
 #pragma unroll
           for (int q = 0; q < SK_PMAX; ++q) {
             const int gg = glo + min(q, np - 1);
-            const float* pq = part + (size_t)(2 * gg + (start_of(gg) >= tb ? 0 : 1)) * NO;
+            const float* pq = part + ((size_t)(2 * gg + (start_of(gg) >= tb ? 0 : 1)) * TR + et) * NO;
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -806,14 +824,14 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
                 for (int q = 1; q < SK_PMAX; ++q) a += q < np ? pv[q][m][tt][c] : 0.f;
                 v[m][tt][c] = a;
               }
-          if (lane == 0) __hip_atomic_store(tcnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) __hip_atomic_store(tcnt + t * TR + et, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       if (fin) {
         if (r16 == 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int p = t * 16 + 4 * g + j;
+            const int p = t * RT + 16 * et + 4 * g + j;
             if (p < cnt) {
               idx[p] = ej[j];
               if (tokmask) tokmask[p] = em[j];
@@ -825,7 +843,7 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
           const int b = tt * 16 + r16;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int p = t * 16 + 4 * g + j;
+            const int p = t * RT + 16 * et + 4 * g + j;
             if (p < cnt && b < B) {
               const float a0 = v[0][tt][j] + eb[j];
               float h = a0 > 0.f ? a0 : 0.f;
@@ -838,9 +856,11 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < TR; ++i)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) acc[m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[i][m][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
   };
   long long j = j0, seg0 = j0;
   int t = t_first, kb = (int)(j0 - (long long)t_first * KBT);
@@ -1119,25 +1139,31 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
 // the pairs then outnumber the compute units (measured no faster at 32 tokens); below 16
 // tokens eight waves on one row tile measured slower (2 tokens 18.3 vs 17.5 us, 8 tokens
 // 30.9 vs 26.7 us on the Llama-7B shape).
-template <bool GATED, int NT>
+template <bool GATED, int NT, int TR, int W>
 void up_sk_launch(const LayerDev& L, int B, int32_t* idx, int32_t* count, uint64_t* tokmask,
-                  float* y0, int ny, hipStream_t s, const hipEvent_t* tev) {
-  launch(k_up_sk<GATED, NT, 4>, dim3(L.g_sk), dim3(256), 0, s, tev, L.w_act, L.b_act,
+                  float* y0, int ny, hipStream_t s, const hipEvent_t* tev, int grid) {
+  launch(k_up_sk<GATED, NT, TR, W>, dim3(grid), dim3(64 * W), 0, s, tev, L.w_act, L.b_act,
          static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask,
          (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny,
          L.sk_part, L.sk_cnt);
 }
 
-// the stream-K form: the decode step's list from the words, two token tiles, d a
-// multiple of 512 with at least two input blocks per tile, and ranges that touch at most
-// SK_TMAX tiles (g_sk >= tiles / 13). Measured on the Llama-7B-shaped gated stack it
-// gains at 32 tokens (82.9 vs 84.4 us a layer) and loses below 17: at 16 tokens the
-// two-tile eight-wave form, whose activation fragments serve two row tiles, is faster
-// (51.0 vs 55.2 us), and at 4 tokens every tile is split and the hand-offs cost more than
-// the balance gains (35.3 vs 33.1 us).
-bool up_sk_ok(const LayerDev& L, int B, bool fw) {
-  return fw && L.sk_part && B > 16 && B <= 32 && L.d % 512 == 0 && L.d >= 1024 &&
-         L.g_sk * 13 >= (L.n + 15) / 16;
+// The stream-K form runs at 17-32 tokens (the decode step's list from the words): one row
+// tile, four waves, two workgroups per compute unit (g_sk); d a multiple of 512 with at
+// least two input blocks per tile, and ranges that touch at most SK_TMAX tiles (g_sk >=
+// tiles / 13). Measured on the Llama-7B-shaped gated stack it gains at 32 tokens (82.9 vs
+// 84.4 us a layer); wherever the ranges are only a few blocks long the hand-offs (about a
+// coherent round trip each) cost more than the balance gains:
+//  - 4 tokens, one row tile: 35.3 vs 33.1 us (every tile split);
+//  - 16 tokens, one row tile: 55.2 vs 51.0 us (the two-row-tile eight-wave kernel shares
+//    each activation fragment between two row tiles);
+//  - 16 tokens, two row tiles and eight waves on all 256 compute units instead of 197:
+//    54.0 vs 51.4 us (about 3 blocks per range, so almost every tile is split).
+int up_sk_form(const LayerDev& L, int B, bool fw) {
+  if (!fw || !L.sk_part) return 0;
+  if (B > 16 && B <= 32 && L.d % 512 == 0 && L.d >= 1024 && L.g_sk * 13 >= (L.n + 15) / 16)
+    return 1;
+  return 0;
 }
 
 template <bool GATED>
@@ -1145,11 +1171,11 @@ void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t*
                     const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
                     const hipEvent_t* tev, bool fw) {
   const int nt = (B + 15) / 16;
-  if (up_sk_ok(L, B, fw)) {
+  if (const int form = up_sk_form(L, B, fw)) {
     int32_t* idx_w = const_cast<int32_t*>(idx);
     int32_t* cnt_w = const_cast<int32_t*>(count);
     uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
-    up_sk_launch<GATED, 2>(L, B, idx_w, cnt_w, tok_w, y0, ny, s, tev);
+    up_sk_launch<GATED, 2, 1, 4>(L, B, idx_w, cnt_w, tok_w, y0, ny, s, tev, L.g_sk);
     return;
   }
   if (B >= 16 && nt == 1 && L.d % 512 == 0) {

@@ -298,13 +298,14 @@ def test_all_active_and_true_sign_equal_dense(gated):
 
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("B,d", [(1, 64), (5, 64), (16, 128), (6, 256), (16, 256), (24, 256),
-                                 (24, 1024)])
+                                 (24, 1024), (16, 2048)])
 def test_integer_fixture_bit_exact(gated, B, d):
     """Integer weights and tokens: every partial sum is exact in fp32 (and each activation
     is exactly hi + lo in fp16), so the HIP path must reproduce the oracle bit for bit,
     scores, list and output, on the vector path (d = 64, 128) and on the matrix-core tile
-    path with its matrix-core score kernel (d = 256, rank 32), including the stream-K up
-    projection with its split tiles (24 tokens, d = 1024)."""
+    path with its matrix-core score kernel (d = 256, rank 32), the two-row-tile up kernel
+    (16 tokens, d = 2048) and the stream-K up projection with its split tiles (24 tokens,
+    d = 1024)."""
     from activation_sparse_decode_rank_amd import SparseFFN
     from synth import integer_layer
     n, r = 1000, (32 if d % 256 == 0 else 16)
