@@ -475,7 +475,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     };
     // whole iterations of 2 KP pairs, pipelined (the scheduling barriers keep each batch's
     // loads ahead of the products before their use; the scheduler would otherwise sink
-    // them to their first use); then the leftover pairs one at a time
+    // them to their first use), the last one peeled; then the leftover pairs one at a time
     const int nfull = npairs / (2 * KP) * (2 * KP);
     // the epilogue's list entries, token bits and biases (lane: positions 4g + j of tile
     // et) go out behind the first weight batch; by the time they are used they have long
@@ -500,7 +500,8 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     if (nfull > 0) {
       load(0, 0);
       load_epilogue();
-      for (int p0 = 0; p0 < nfull; p0 += 2 * KP) {
+      int p0 = 0;
+      for (; p0 + 2 * KP < nfull; p0 += 2 * KP) {
         load(p0 + KP, 1);
         __builtin_amdgcn_sched_barrier(0);
         mult(0, std::integral_constant<int, KP>{});
@@ -510,6 +511,14 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
         mult(1, std::integral_constant<int, KP>{});
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the last whole iteration fetches nothing ahead (a wave retires only when its loads
+      // have landed)
+      load(p0 + KP, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(0, std::integral_constant<int, KP>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mult(1, std::integral_constant<int, KP>{});
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (nfull == 0) load_epilogue();
     for (int p = nfull; p < npairs; ++p) {
@@ -1038,8 +1047,12 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
       }
       wave_lds_sync();
     };
+    // whole iterations while chunks remain past the next two batches; then the last one
+    // or two batches with nothing fetched beyond the wave's own chunks (a wave retires only
+    // when its loads have landed)
     load(0, 0);
-    for (int i0 = 0; i0 < mine; i0 += 2 * KB) {
+    int i0 = 0;
+    for (; i0 + 2 * KB < mine; i0 += 2 * KB) {
       load(i0 + KB, 1);
       __builtin_amdgcn_sched_barrier(0);
       mult(i0, 0);
@@ -1048,6 +1061,15 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
       __builtin_amdgcn_sched_barrier(0);
       mult(i0 + KB, 1);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i0 + KB < mine) {  // uniform within the wave
+      load(i0 + KB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(i0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mult(i0 + KB, 1);
+    } else {
+      mult(i0, 0);
     }
   }
   // fixed-order sum of the four waves, then out (lane l holds column 16cg + l%16 of the
