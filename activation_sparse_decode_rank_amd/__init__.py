@@ -11,4 +11,6 @@ from ._native import (  # noqa: F401
     sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts, sparse_ffn_set_timing_events,
     sparse_ffn_status_string, sparse_ffn_workspace_bytes,
 )
-from .layer import SparseFFN, n_hot_for, pack_rows, permutation, profile_counts  # noqa: F401
+from .layer import (  # noqa: F401
+    LookaheadBuffers, SparseFFN, decode_lookahead, n_hot_for, pack_rows, permutation, profile_counts,
+)

@@ -201,3 +201,63 @@ class SparseFFN:
             self.close()
         except Exception:
             pass
+
+
+class LookaheadBuffers:
+    """Per-layer device buffers of a look-ahead decode: scores [B, n], the active list
+    (idx, count, tokmask) and the output y [B, d] of every layer."""
+
+    def __init__(self, layers, B: int, device="cuda"):
+        self.B = int(B)
+        self.scores = [torch.empty((B, s.n), dtype=torch.float32, device=device) for s in layers]
+        self.idx = [torch.empty(s.n, dtype=torch.int32, device=device) for s in layers]
+        self.count = torch.zeros(len(layers), dtype=torch.int32, device=device)
+        self.tokmask = [torch.empty(s.n, dtype=torch.int64, device=device) for s in layers]
+        self.y = [torch.empty((B, s.d), dtype=torch.float32, device=device) for s in layers]
+
+
+def decode_lookahead(layers, xs, bufs: LookaheadBuffers, stream=None, side_stream=None):
+    """Look-ahead ("asynchronous") decode through a stack of layers (novita.ai
+    activation-sparsity article, section 上下文稀疏性: the next layer's sparsity is
+    predicted ahead of time, off the critical path).
+
+    Layer 0's active set comes from its own input xs[0]; layer l >= 1's from the previous
+    layer's input xs[l - 1], through layer l's own predictor. Its predict and compact run
+    on side_stream while layer l - 1's forward runs on stream, so the critical path of a
+    layer is its forward alone (once the side stream keeps up). Output: bufs.y[l] =
+    forward of layer l on xs[l] over that active set. Only host scheduling happens here:
+    every step is a C-ABI call (predict, compact, forward) on the given streams, ordered
+    with events:
+      - the side stream starts layer l + 1's prediction once the stream has reached layer
+        l's forward (xs[l] is ready there; in a model it is the previous layer's output);
+      - the stream waits for layer l + 1's list before layer l + 1's forward, so the side
+        work of a call ends inside it (graph capture sees a fork and a join).
+    A layer's handle is used by one stream at a time, and a call reuses its buffers only
+    after the previous call's stream work on them."""
+    main = stream if stream is not None else torch.cuda.current_stream()
+    side = side_stream
+    if side is None:
+        raise ValueError("decode_lookahead needs a side stream")
+    L = len(layers)
+    if len(xs) != L:
+        raise ValueError("one input per layer")
+
+    def predict_list(l, x, s):
+        layers[l].predict(x, scores=bufs.scores[l], stream=s)
+        layers[l].compact(bufs.scores[l], idx=bufs.idx[l], count=bufs.count[l:l + 1],
+                          tokmask=bufs.tokmask[l], stream=s)
+
+    predict_list(0, xs[0], main)
+    for l in range(L):
+        if l + 1 < L:
+            ready = torch.cuda.Event()
+            ready.record(main)
+            side.wait_event(ready)
+            predict_list(l + 1, xs[l], side)
+            listed = torch.cuda.Event()
+            listed.record(side)
+        layers[l].forward(xs[l], bufs.idx[l], bufs.count[l:l + 1], tokmask=bufs.tokmask[l],
+                          y=bufs.y[l], stream=main)
+        if l + 1 < L:
+            main.wait_event(listed)
+    return bufs.y

@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every decode eagerly instead of replaying captured graphs "
                          "(for per-dispatch counter collection; the timing is then not the metric)")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="also time the look-ahead schedule (next layer's mask predicted from "
+                         "the current layer's input on a second stream), reported beside the metric")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 4 times (the known-size "
                          "kernel that scales HBM counter readings)")
@@ -183,7 +186,7 @@ def main():
     import torch
     import torch.nn.functional as F
 
-    from activation_sparse_decode_rank_amd import SparseFFN
+    from activation_sparse_decode_rank_amd import LookaheadBuffers, SparseFFN, decode_lookahead
     from activation_sparse_decode_rank_amd import _native as NAT
     from synth import get_config, make_layer, make_tokens
 
@@ -290,6 +293,47 @@ def main():
     ms_per_step = ms_total / steps
     us_per_layer = ms_per_step * 1000.0 / L
     log(f"sparse decode: {ms_per_step:.4f} ms/step, {us_per_layer:.3f} us/layer")
+
+    # ------------------------------------------------------------------ look-ahead schedule
+    # The same layers and tokens through decode_lookahead: layer l >= 1 takes its active set
+    # from layer l - 1's input (its own predictor), predicted on a second stream while layer
+    # l - 1's forward runs. A different mask than the metric's (each layer's own input), so
+    # it is reported beside the metric, not as it.
+    lookahead = None
+    if args.lookahead:
+        side = torch.cuda.Stream()
+        la_bufs = LookaheadBuffers(layers, B)
+
+        def la_step(t, stream=None):
+            decode_lookahead(layers, [X[t, l] for l in range(L)], la_bufs,
+                             stream=stream if stream is not None else torch.cuda.current_stream(),
+                             side_stream=side)
+
+        la_step(0)
+        torch.cuda.synchronize()
+        la_graphs = []
+        if not args.no_graph:
+            for gi in range(T // G):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for t in range(gi * G, (gi + 1) * G):
+                        la_step(t, cap)
+                la_graphs.append(g)
+            torch.cuda.synchronize()
+        replay(la_graphs, warmup, la_step)
+        torch.cuda.synchronize()
+        e0.record()
+        replay(la_graphs, steps, la_step)
+        e1.record()
+        torch.cuda.synchronize()
+        la_ms = e0.elapsed_time(e1) / steps
+        la_us = la_ms * 1000.0 / L
+        lookahead = {"us_per_layer": round(la_us, 3), "ms_per_step": round(la_ms, 5),
+                     "speedup_vs_metric_path": round(us_per_layer / la_us, 3),
+                     "mask": "layer l >= 1 from layer l-1's input (layer l's predictor, second "
+                             "stream beside layer l-1's forward); layer 0 from its own input"}
+        log(f"look-ahead decode: {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
+        del la_graphs, la_bufs
 
     cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
     if B == 1:
@@ -460,6 +504,7 @@ def main():
         "speedup_vs_dense": (round(dense["us_per_layer"] / us_per_layer, 3) if dense else None),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "lookahead": lookahead,
         "kernel_source_sha256": kernel_source_sha(),
     }
     print(json.dumps(out), flush=True)

@@ -211,6 +211,53 @@ def test_decode_pipeline(name, d, n, r, B):
     say(f"  count={k} band={nband} err={max(errs):.2e}")
 
 
+@pytest.mark.parametrize("name,d,n,r,B", [("C2", 512, 1000, 64, 1), ("C2", 512, 1000, 64, 4),
+                                          ("C3", 512, 1100, 64, 2)])
+def test_lookahead_stack(name, d, n, r, B):
+    """Look-ahead schedule over a 3-layer stack: layer l >= 1 takes its active set from layer
+    l - 1's input through its own predictor (layer 0 from its own input), predicted on a side
+    stream beside the previous forward. Each mask is checked against the oracle outside the
+    band, each output against the oracle under the GPU's own list, and the two-stream run
+    equals the same calls issued on one stream, bit for bit (deterministic handles)."""
+    from activation_sparse_decode_rank_amd import LookaheadBuffers, decode_lookahead
+    c = cfg(name)
+    say(f"look-ahead {name} d={d} n={n} r={r} B={B}")
+    stack = [build(c, l, d=d, n=n, rank=r, max_batch=B, deterministic=True) for l in range(3)]
+    layers = [s for s, _, _ in stack]
+    xs = [tokens(c, B, d, tag=300 + l) for l in range(3)]
+    side = torch.cuda.Stream()
+    main = torch.cuda.Stream()
+    bufs = LookaheadBuffers(layers, B)
+    with torch.cuda.stream(main):
+        for _ in range(2):  # the second call reuses the buffers
+            decode_lookahead(layers, xs, bufs, stream=main, side_stream=side)
+    torch.cuda.synchronize()
+    for l, (s, L, _) in enumerate(stack):
+        k = int(bufs.count[l].item())
+        idx_h, tok_h = to_np(bufs.idx[l]), to_np(bufs.tokmask[l])
+        Xsrc = to_np(xs[0] if l == 0 else xs[l - 1])
+        S = oracle.predict(Xsrc, L["p1"], L["p2"], L["c"])
+        Mg = gpu_mask_orig(s.perm, idx_h, k, tok_h, B, n)
+        M, nband = check_mask(Mg, S)
+        ri, rk, rt = oracle.compact(M)
+        Y = oracle.forward(to_np(xs[l]), L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"],
+                           b_o=L["b_o"])
+        errs = rel_err_rows(to_np(bufs.y[l]), Y)
+        assert max(errs) <= REL_TOL, (l, errs)
+        say(f"  layer {l}: count={k} band={nband} err={max(errs):.2e}")
+    # the same calls on one stream
+    for l, s in enumerate(layers):
+        src = xs[0] if l == 0 else xs[l - 1]
+        sc = s.predict(src)
+        i2, c2, t2 = s.compact(sc)
+        y2 = s.forward(xs[l], i2, c2, t2)
+        torch.cuda.synchronize()
+        k = int(c2.item())
+        assert k == int(bufs.count[l].item())
+        assert np.array_equal(to_np(i2)[:k], to_np(bufs.idx[l])[:k])
+        assert np.array_equal(to_np(y2), to_np(bufs.y[l]))
+
+
 def test_decode_deterministic():
     """deterministic=1: repeated decodes give bitwise-identical y and lists, and match the
     oracle (the down projection splits rows at most two ways)."""
