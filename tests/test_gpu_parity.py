@@ -385,15 +385,50 @@ def test_integer_fixture_bit_exact(gated, B, d):
     assert np.array_equal(to_np(y).astype(np.float64), Y)
 
 
-def test_empty_mask_gives_output_bias():
+@pytest.mark.parametrize("B,d", [(1, 256), (2, 256), (24, 1024)])
+def test_empty_mask_gives_output_bias(B, d):
+    """No active neuron: y = b_out, on the single-token path, the tile path and the
+    stream-K up kernel (24 tokens)."""
     c = cfg("C2")
-    say("empty mask")
-    s, L, _ = build(c, 0, d=256, n=700, rank=64, max_batch=2, threshold=float("inf"))
-    X = tokens(c, 2, 256)
-    y, idx, count, tok = s.decode(X)
-    torch.cuda.synchronize()
-    assert int(count.item()) == 0
-    assert np.array_equal(to_np(y), np.tile(L["b_o"], (2, 1)))
+    say(f"empty mask B={B} d={d}")
+    s, L, _ = build(c, 0, d=d, n=700, rank=64, max_batch=B, threshold=float("inf"))
+    X = tokens(c, B, d)
+    for _ in range(2):  # the second call sees the counters the first left
+        y, idx, count, tok = s.decode(X)
+        torch.cuda.synchronize()
+        assert int(count.item()) == 0
+        assert np.array_equal(to_np(y), np.tile(L["b_o"], (B, 1)))
+
+
+@pytest.mark.parametrize("tau", [0.2, 0.5, 1.0])
+def test_stream_k_small_unions(tau):
+    """Stream-K up kernel (24 tokens, d = 1024) on unions of a few tiles down to a handful of
+    rows (raised thresholds): list bit-exact with the oracle on the GPU's own scores, output
+    within tolerance under that list, and the same result on a second call (the tiles'
+    arrival counters are back at zero)."""
+    c = cfg("C2")
+    B, d, n = 24, 1024, 1500
+    say(f"stream-K small union tau={tau}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=128, max_batch=B, threshold=tau, deterministic=True)
+    X = tokens(c, B, d)
+    scores = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        y, idx, count, tok = s.decode(X, scores=scores)
+        torch.cuda.synchronize()
+        outs.append((to_np(y).copy(), int(count.item()), to_np(idx).copy(), to_np(tok).copy()))
+    (y1, k, idx_h, tok_h), (y2, k2, idx2, tok2) = outs
+    assert k == k2 and np.array_equal(y1, y2) and np.array_equal(idx_h[:k], idx2[:k])
+    ri, rk, rt = oracle.compact(oracle.threshold(to_np(scores).astype(np.float32), tau))
+    assert rk == k
+    assert np.array_equal(idx_h[:k], ri)
+    assert np.array_equal(tok_h[:k].astype(np.uint64), rt)
+    Mg = gpu_mask_orig(s.perm, idx_h, k, tok_h, B, n)
+    ro, rko, rto = oracle.compact(Mg)
+    Y = oracle.forward(to_np(X), L["w_a"], L["w_o"], ro, rto, Wu=L["w_u"], b_a=L["b_a"],
+                       b_o=L["b_o"])
+    assert max(rel_err_rows(y1, Y)) <= REL_TOL
+    say(f"  count={k}")
 
 
 # --------------------------------------------------------------------------- offline steps
