@@ -148,6 +148,7 @@ SHAPES = [
     ("C3", 2048, 1500, 128, 64),    # four token tiles
     ("C5", 12288, 900, 128, 3),     # the OPT-175B width
     ("C2", 256, 20000, 64, 4),      # more union words than the up kernel has threads
+    ("C5", 8192, 1500, 512, 1),     # one token at rank 512: the four-row stage 1
 ]
 
 
