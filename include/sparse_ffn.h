@@ -105,9 +105,12 @@ typedef struct {
 } sffn_desc;
 
 /* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The
- * workspace holds predictor intermediates, per-neuron activations, compaction state and a
- * small table of neuron ranges that sparse_ffn_create writes (synchronously) and every
- * later call reads. Give each handle its own workspace. */
+ * workspace holds predictor intermediates, per-neuron activations, compaction state,
+ * partial sums of tiles split between workgroups, a small table of neuron ranges that
+ * sparse_ffn_create writes and every later call reads, and tile counters that
+ * sparse_ffn_create zeroes and every call leaves at zero (both synchronously, at create).
+ * Give each handle its own workspace, and order the calls on one handle (a call that
+ * overlaps another on the same workspace races with it). */
 size_t sparse_ffn_workspace_bytes(const sffn_desc* desc);
 
 /* Validate `desc` and create a handle (host metadata only). Queries the current HIP device
