@@ -49,6 +49,8 @@ def _load():
         "sparse_ffn_compact": (C.c_int, [P, P, I32, P, P, P, P]),
         "sparse_ffn_forward": (C.c_int, [P, P, I32, P, P, P, P, P]),
         "sparse_ffn_decode": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
+        "sparse_ffn_lookahead_begin": (C.c_int, [P, P, P]),
+        "sparse_ffn_decode_lookahead": (C.c_int, [P, P, P, P, P, P, P, P]),
         "sparse_ffn_status_string": (C.c_char_p, [C.c_int]),
         "sparse_ffn_set_timing_events": (C.c_int, [P, C.POINTER(P)]),
         "sparse_ffn_profile_counts": (C.c_int, [P, I32, I32, P, I32, I32, P, I32, P, P]),
@@ -65,6 +67,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destroy",
             "sparse_ffn_predict", "sparse_ffn_compact", "sparse_ffn_forward", "sparse_ffn_decode",
+            "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows")
 
@@ -110,6 +113,15 @@ def sparse_ffn_forward(h, x, B, idx, count, tokmask, y, stream) -> None:
 
 def sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
     _ck(_lib.sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream), "sparse_ffn_decode")
+
+
+def sparse_ffn_lookahead_begin(h, x, stream) -> None:
+    _ck(_lib.sparse_ffn_lookahead_begin(h, x, stream), "sparse_ffn_lookahead_begin")
+
+
+def sparse_ffn_decode_lookahead(cur, nxt, x, y, idx, count, tokmask, stream) -> None:
+    _ck(_lib.sparse_ffn_decode_lookahead(cur, nxt, x, y, idx, count, tokmask, stream),
+        "sparse_ffn_decode_lookahead")
 
 
 def sparse_ffn_set_timing_events(h, events) -> None:

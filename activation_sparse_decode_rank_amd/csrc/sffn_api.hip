@@ -193,10 +193,14 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.g_sk = std::min(sffn::SK_G_MAX, std::max(2 * cus, ((desc->d_ffn + 15) / 16 + 12) / 13));
     if (L.sk_part) {
       // its arrival counters start at zero; every call leaves them zero
-      if (hipMemset(L.sk_cnt, 0, (size_t)((desc->d_ffn + 15) / 16 + 1) * 4) != hipSuccess ||
-          hipStreamSynchronize(nullptr) != hipSuccess)
+      if (hipMemset(L.sk_cnt, 0, (size_t)((desc->d_ffn + 15) / 16 + 1) * 4) != hipSuccess)
         return SFFN_ERR_HIP;
     }
+    // range activity words start empty, so a look-ahead decode run before any prediction
+    // sees an empty set
+    if (hipMemset(L.wbits, 0, (size_t)sffn::G_MID_MAX * 8) != hipSuccess ||
+        hipStreamSynchronize(nullptr) != hipSuccess)
+      return SFFN_ERR_HIP;
 
     // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
     // of the active ones; as many ranges as can be resident at once, at most G_MID_MAX
@@ -303,6 +307,39 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
   if (!sffn::shape_supported(h->L, true)) return SFFN_ERR_UNSUPPORTED;
   return sffn::launch_decode(h->L, x, B, y, idx, count, tokmask, scores,
                              static_cast<hipStream_t>(stream), h->timing ? h->ev : nullptr) ==
+                 hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+namespace {
+bool lookahead_ok(sparse_ffn_t h) {
+  return sffn::shape_supported(h->L, true) && sffn::lookahead_layer_ok(h->L);
+}
+bool overlap(const sffn_desc& a, const sffn_desc& b) {
+  const char* a0 = static_cast<const char*>(a.workspace);
+  const char* b0 = static_cast<const char*>(b.workspace);
+  return a0 < b0 + b.workspace_bytes && b0 < a0 + a.workspace_bytes;
+}
+}  // namespace
+
+int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream) {
+  if (!first || !x || !aligned16(x)) return SFFN_ERR_INVALID;
+  if (!lookahead_ok(first)) return SFFN_ERR_UNSUPPORTED;
+  return sffn::run_lookahead_begin(first->L, x, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
+                                int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream) {
+  if (!cur || !x || !y || !idx || !count || cur == next) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
+  if (next && (next->L.d != cur->L.d || overlap(cur->desc, next->desc))) return SFFN_ERR_INVALID;
+  if (!lookahead_ok(cur) || (next && !lookahead_ok(next))) return SFFN_ERR_UNSUPPORTED;
+  if (next && cur->L.g_mid < next->L.r) return SFFN_ERR_UNSUPPORTED;  // one stage-1 row a workgroup
+  return sffn::run_lookahead(cur->L, next ? &next->L : nullptr, x, y, idx, count, tokmask,
+                             static_cast<hipStream_t>(stream), cur->timing ? cur->ev : nullptr) ==
                  hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;

@@ -7,47 +7,38 @@ namespace sffn {
 namespace {
 
 // ---------------------------------------------------------------------------- B = 1
-// The single-token form of the middle kernel, specialized on NCHP (chunks per predictor
-// row) so that the lane-group reductions are straight-line DPP code. Addresses of unused
-// slots are clamped into the owned block instead of branching per lane. Outputs as in
-// k_fused_mid with B = 1: the range's activity word and h_g[i] for every active neuron i
-// (no token bits: with one token every listed neuron is active for it).
-template <bool F16, bool GATED, int CPT, int NCHP>
-__global__ __launch_bounds__(TPB) void k_mid_b1(
-    const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
-    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int n, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
-    float* __restrict__ h_g, float* __restrict__ scores, const RangeArg ra) {
+// The two halves of the single-token middle kernel, as device functions: the fused kernel
+// runs both in one workgroup, the look-ahead decode runs them in different launches.
+
+// Predictor stage 2 and threshold over one range's neurons [r0, r0 + nown) (1 <= nown <=
+// MID_RANGE_MAX): s_act[j] = (P2[r0 + j] . q + c[r0 + j] > tau), the score also stored when
+// scores is given. Specialized on NCHP (chunks per predictor row) so that the lane-group
+// reductions are straight-line DPP code; addresses of unused slots are clamped into the
+// owned block instead of branching per lane. extra() runs after the predictor loads are
+// issued and before the first barrier. Returns after a barrier, with s_act complete.
+template <bool F16, int NCHP, typename Extra>
+__device__ __forceinline__ void mid_scores_b1(const void* __restrict__ p2,
+                                              const float* __restrict__ pbias,
+                                              const float* __restrict__ q, int r0, int nown,
+                                              float tau, float* __restrict__ scores,
+                                              uint8_t* s_act, Extra extra) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int GRP = NCHP < 64 ? NCHP : 64;   // lanes holding one predictor row in a wave
   constexpr int WPR = NCHP > 64 ? NCHP / 64 : 1;  // waves per predictor row
   constexpr int RPP = TPB / NCHP;              // predictor rows per slot of the workgroup
   constexpr int PL = 8;                        // slots in flight per thread
   constexpr int RMAX = MID_RANGE_MAX;
-  constexpr int RB = (16 / CPT) > 0 ? (16 / CPT) : 1;  // gathered rows in flight
-  constexpr int NV = GATED ? 2 : 1;
   static_assert(NCHP >= 1 && NCHP <= 128 && (NCHP & (NCHP - 1)) == 0, "NCHP");
-  
-  __shared__ uint8_t s_act[RMAX];
-  __shared__ int32_t s_rows[RMAX];
-  __shared__ float s_bias[RMAX];
   __shared__ float s_part[WPR > 1 ? RMAX * WPR : 1];
   __shared__ float s_pb[RMAX];
-  __shared__ float s_ba[RMAX];
-  __shared__ int s_wcnt[TPB / 64];
-  __shared__ float s_red[4 * RB * NV];
-
-  touch_kernargs<2>();
-  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
-  const int nown = r1 - r0;  // 1..RMAX
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos = tid & (NCHP - 1);
   const int rsub = tid / NCHP;
   const int nslots = (nown + RPP - 1) / RPP;
   const size_t blk0 = (size_t)r0 * NCHP;
 
-  // ---- every score-independent load first: P2 (first PL slots), q, biases, x. Slots
-  // beyond the range (m >= mlim, uniform) re-read its last row and are not computed.
+  // every score-independent load first: P2 (first PL slots), q, the predictor biases.
+  // Slots beyond the range (m >= mlim, uniform) re-read its last row and are not computed.
   // (Guarding these loads instead makes the compiler keep far more registers live.)
   u32x4 wv[PL];
   int mlim = min(PL, nslots);
@@ -58,19 +49,12 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
   }
   float qs[EPC];
   load_x<EPC>(q + (size_t)pos * EPC, qs);
-  float pb = 0.f, ba = 0.f;
-  if (tid < nown) {
-    pb = pbias ? pbias[r0 + tid] : 0.f;
-    ba = b_act ? b_act[r0 + tid] : 0.f;
-  }
+  const float pb = (tid < nown && pbias) ? pbias[r0 + tid] : 0.f;
+  extra();
   if (tid < RMAX) s_act[tid] = 0;
-  if (tid < nown) {
-    s_pb[tid] = pb;
-    s_ba[tid] = ba;
-  }
+  if (tid < nown) s_pb[tid] = pb;
   __syncthreads();
 
-  // ---- predictor stage 2 and threshold
   for (int s0 = 0; s0 < nslots; s0 += PL) {
     if (s0 > 0) {
       mlim = min(PL, nslots - s0);
@@ -114,36 +98,26 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
     }
   }
   __syncthreads();
-  // ---- compaction of the owned range: ballot per wave, prefix over the four waves
-  const bool act = tid < nown && s_act[tid];
-  const uint64_t word = __ballot(act);
-  if (lane == 0) s_wcnt[wave] = __popcll(word);
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wcnt[v] : 0;
-  const int nact = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-  if (act) {
-    const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
-    const int k = before + __popcll(lower);
-    s_rows[k] = r0 + tid;
-    s_bias[k] = s_ba[tid];
-  }
-  __syncthreads();
+}
 
-  // ---- gather-GEMV + ReLU over the active rows, RB rows in flight. The input chunks this
-  // thread multiplies are loaded into registers once, with the first rows' loads.
+// Gather-GEMV + ReLU over the nact active rows listed in s_rows (their activation biases in
+// s_bias), RB rows in flight, against the input chunks xs the caller loaded (chunk tid + m
+// TPB of the row; for the gated bundle the second half maps onto the same input):
+// h_g[row] = ReLU(W_a[row] . x + b), gated: times W_u[row] . x. first() runs exactly once:
+// after the first rows' loads are issued, or at once when no row is active.
+template <bool F16, bool GATED, int CPT, typename First>
+__device__ __forceinline__ void mid_gather_b1(const void* __restrict__ w_act, int d, int nact,
+                                              const int32_t* s_rows, const float* s_bias,
+                                              const float (&xs)[CPT][Elt<F16>::EPC],
+                                              float* __restrict__ h_g, First first) {
+  constexpr int EPC = Elt<F16>::EPC;
+  constexpr int RB = (16 / CPT) > 0 ? (16 / CPT) : 1;  // gathered rows in flight
+  constexpr int NV = GATED ? 2 : 1;
+  __shared__ float s_red[4 * RB * NV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = d / EPC;
   const int rowch = GATED ? 2 * nch : nch;
-  float xs[CPT][EPC];
-  if (nact > 0) {
-#pragma unroll
-    for (int m = 0; m < CPT; ++m) {
-      const int c = tid + m * TPB;
-      const bool up = GATED && c >= nch;
-      load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
-    }
-  }
+  if (nact == 0) first();
   for (int base = 0; base < nact; base += RB) {
     const int nb = min(RB, nact - base);  // uniform
     u32x4 gv[RB][CPT];
@@ -155,6 +129,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
         for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_stream(w_act, row0 + min(tid + m * TPB, rowch - 1));
       }
     }
+    if (base == 0) first();
 
     float acc[RB][NV];
 #pragma unroll
@@ -208,6 +183,65 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
     }
     __syncthreads();
   }
+}
+
+// The single-token middle kernel: predictor stage 2, threshold, compaction of the owned
+// range and the gather over its active rows, in one workgroup per range. Outputs as in
+// k_fused_mid with B = 1: the range's activity word and h_g[i] for every active neuron i
+// (no token bits: with one token every listed neuron is active for it).
+template <bool F16, bool GATED, int CPT, int NCHP>
+__global__ __launch_bounds__(TPB) void k_mid_b1(
+    const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
+    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
+    int d, int n, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
+    float* __restrict__ h_g, float* __restrict__ scores, const RangeArg ra) {
+  constexpr int EPC = Elt<F16>::EPC;
+  constexpr int RMAX = MID_RANGE_MAX;
+  __shared__ uint8_t s_act[RMAX];
+  __shared__ int32_t s_rows[RMAX];
+  __shared__ float s_bias[RMAX];
+  __shared__ float s_ba[RMAX];
+  __shared__ int s_wcnt[TPB / 64];
+
+  touch_kernargs<2>();
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
+  const int nown = r1 - r0;  // 1..RMAX
+
+  mid_scores_b1<F16, NCHP>(p2, pbias, q, r0, nown, tau, scores, s_act, [&]() {
+    const float ba = (tid < nown && b_act) ? b_act[r0 + tid] : 0.f;
+    if (tid < nown) s_ba[tid] = ba;
+  });
+  // ---- compaction of the owned range: ballot per wave, prefix over the four waves
+  const bool act = tid < nown && s_act[tid];
+  const uint64_t word = __ballot(act);
+  if (lane == 0) s_wcnt[wave] = __popcll(word);
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < TPB / 64; ++v) before += v < wave ? s_wcnt[v] : 0;
+  const int nact = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  if (act) {
+    const uint64_t lower = lane ? (word & ((~(uint64_t)0) >> (64 - lane))) : 0;
+    const int k = before + __popcll(lower);
+    s_rows[k] = r0 + tid;
+    s_bias[k] = s_ba[tid];
+  }
+  __syncthreads();
+
+  // ---- gather-GEMV + ReLU over the active rows. The input chunks this thread multiplies
+  // are loaded into registers once, with the first rows' loads.
+  const int nch = d / EPC;
+  float xs[CPT][EPC];
+  if (nact > 0) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * TPB;
+      const bool up = GATED && c >= nch;
+      load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
+    }
+  }
+  mid_gather_b1<F16, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, []() {});
   // The range's activity word (the range fits in wave 0's 64 lanes) is stored last: the
   // wait that follows a store and a barrier would hold back the gather's loads.
   if (tid == 0) wbits[w] = word;
@@ -251,13 +285,16 @@ __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
   }
 }
 
+// The body of one workgroup (index bid) of the single-token down projection; the kernel
+// below runs it on every workgroup, and the look-ahead decode on the first ones of a launch
+// it shares with the next layer's scores.
 template <bool WF16, int UPT>
-__global__ __launch_bounds__(TPB) void k_down_b1(
-    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+__device__ __forceinline__ void down_b1_body(
+    int bid, const void* __restrict__ w_down_t, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
-    float* __restrict__ y, const SplitArg sa) {
+    float* __restrict__ y, const SplitArg& sa) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int COLS = CB_LANES * EPC;
   constexpr int PFX = G_MID_MAX / TPB;  // earlier-range words per thread
@@ -267,10 +304,9 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
   __shared__ int s_wsum[TPB / 64];
   __shared__ int s_psum[TPB / 64];
   __shared__ float s_red[TPB / 64][4][CB_LANES][EPC];  // [wave][16-lane row][chunk][value]
-  touch_kernargs<2>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const unsigned nch = d / EPC;
-  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
+  const int cb = bid % ncb, kq = bid / ncb;
   const int li = tid & (CB_LANES - 1), rsl = tid / CB_LANES;
   const unsigned chunk = min((unsigned)(cb * CB_LANES + li), nch - 1);  // partial last block
   const int u0 = sa.s[kq], u1 = sa.s[kq + 1];
@@ -390,6 +426,131 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
   if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + total;
 }
 
+template <bool WF16, int UPT>
+__global__ __launch_bounds__(TPB) void k_down_b1(
+    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
+    const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
+    float* __restrict__ y, const SplitArg sa) {
+  touch_kernargs<2>();
+  down_b1_body<WF16, UPT>(blockIdx.x, w_down_t, b_out, h_in, d, n, wbits, rs, KS, ncb, idx_out,
+                          count_out, tokmask_out, y, sa);
+}
+
+
+// ------------------------------------------------------------ look-ahead decode (B = 1)
+// The asynchronous predictor of the novita.ai activation-sparsity article (section
+// 上下文稀疏性): the next layer's active set is predicted from the current layer's input,
+// so that its prediction runs beside the current layer's weight streams instead of before
+// them. A layer then takes two launches, each holding two independent roles (no wait
+// between workgroups inside a launch):
+//   k_la_gather: this layer's gather-GEMV + ReLU over the set chosen earlier (its range
+//                activity words), and stage 1 of the next layer's predictor on this input;
+//   k_la_down:   this layer's down projection, and the next layer's stage 2 + threshold,
+//                which leave that layer's range activity words.
+// Both roles run the same code, in the same summation order, as the single-token decode
+// kernels, so a layer's list equals the one its own decode step would make from the
+// previous layer's input, and y equals that step's output under that list.
+
+// Workgroup w gathers middle range w of this layer and, for w < rn, computes row w of the
+// next layer's stage 1 (qn[w] = P1n[w] . x, as k_pred_stage1 does for one token) between
+// issuing its first weight loads and using them. The first workgroups also clear y (ny
+// floats) for the down projection's split sums. fp16 weights and predictor.
+template <bool GATED, int CPT, int NCPT>
+__global__ __launch_bounds__(TPB) void k_la_gather(
+    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
+    int d, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
+    float* __restrict__ h_g, float* __restrict__ y0, int ny, const void* __restrict__ p1n,
+    int rn, float* __restrict__ qn, const RangeArg ra) {
+  constexpr int EPC = Elt<true>::EPC;
+  constexpr int RMAX = MID_RANGE_MAX;
+  __shared__ int32_t s_rows[RMAX];
+  __shared__ float s_bias[RMAX];
+  __shared__ float s_q[TPB / 64];
+  touch_kernargs<2>();
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
+  const int nown = r1 - r0;  // 1..RMAX
+  const uint64_t word = wbits[w] & (nown >= 64 ? ~(uint64_t)0 : (((uint64_t)1) << nown) - 1);
+  const float ba = (tid < nown && b_act) ? b_act[r0 + tid] : 0.f;
+  const int nch = d / EPC;
+  const bool s1 = w < rn;  // uniform
+  u32x4 pv[NCPT];
+  float x1[NCPT][EPC];
+  if (s1) {
+#pragma unroll
+    for (int m = 0; m < NCPT; ++m) {
+      const int c = tid + m * TPB;
+      if (c < nch) {
+        pv[m] = ld_stream(p1n, (size_t)w * nch + c);
+        load_x<EPC>(x + (size_t)c * EPC, x1[m]);
+      }
+    }
+  }
+  float xs[CPT][EPC];
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int c = tid + m * TPB;
+    const bool up = GATED && c >= nch;
+    load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
+  }
+  for (int i = w * TPB + tid; i < ny; i += gridDim.x * TPB) y0[i] = 0.f;
+  // the range's active rows in ascending order, from its word (the range fits in 64 lanes)
+  const int nact = __popcll(word);
+  if (tid < nown && ((word >> tid) & 1)) {
+    const int k = __popcll(word & ((((uint64_t)1) << tid) - 1));
+    s_rows[k] = r0 + tid;
+    s_bias[k] = ba;
+  }
+  __syncthreads();
+  mid_gather_b1<true, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, [&]() {
+    if (!s1) return;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < NCPT; ++m) {
+      const int c = tid + m * TPB;
+      if (c < nch) {
+        float f[EPC];
+        unpack<true>(pv[m], f);
+#pragma unroll
+        for (int e2 = 0; e2 < EPC; ++e2) acc = fmaf(f[e2], x1[m][e2], acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == WAVE_SUM_LANE) s_q[wave] = acc;
+    __syncthreads();
+    if (tid == 0) qn[w] = ((s_q[0] + s_q[1]) + s_q[2]) + s_q[3];
+  });
+}
+
+// Workgroups below ndown run this layer's down projection (as k_down_b1, which also
+// publishes the list, count and token bits); workgroup ndown + w scores the next layer's
+// range w (bounds from its range table rsn) against qn and stores the range's activity
+// word in wbits_n. fp16 weights and predictor.
+template <int UPT, int NCHP>
+__global__ __launch_bounds__(TPB) void k_la_down(
+    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
+    const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y,
+    int ndown, const void* __restrict__ p2n, const float* __restrict__ pbn,
+    const float* __restrict__ qn, float taun, const int32_t* __restrict__ rsn,
+    uint64_t* __restrict__ wbits_n, const SplitArg sa) {
+  __shared__ uint8_t s_act[MID_RANGE_MAX];
+  touch_kernargs<2>();
+  if ((int)blockIdx.x < ndown) {
+    down_b1_body<true, UPT>(blockIdx.x, w_down_t, b_out, h_in, d, n, wbits, rs, KS, ncb,
+                            idx_out, count_out, tokmask_out, y, sa);
+    return;
+  }
+  const int w = blockIdx.x - ndown, tid = threadIdx.x;
+  const int r0 = rsn[w], nown = rsn[w + 1] - r0;
+  mid_scores_b1<true, NCHP>(p2n, pbn, qn, r0, nown, taun, nullptr, s_act, []() {});
+  const uint64_t word = __ballot(tid < nown && s_act[tid]);
+  if (tid == 0) wbits_n[w] = word;
+}
+
 
 template <bool F16, bool GATED, int CPT, int NCHP>
 void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
@@ -483,6 +644,79 @@ void down_b1_any(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
   }
 }
 
+
+// ---- look-ahead launches
+// chunks per thread of the folded stage-1 row (d / 8 chunks of fp16): 1, 2 or 4, else 0
+inline int la_ncpt(int d) {
+  const int nch = d / 8;
+  return nch <= TPB ? 1 : nch <= 2 * TPB ? 2 : nch <= 4 * TPB ? 4 : 0;
+}
+
+template <bool GATED, int CPT, int NCPT>
+void la_gather_launch(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
+                      hipStream_t s, const hipEvent_t* tev) {
+  const int ny = C.ks_down > 1 ? C.d : 0;
+  launch(k_la_gather<GATED, CPT, NCPT>, dim3(C.g_mid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
+         x, C.d, C.rs_in_arg ? nullptr : C.rs, C.wbits, C.h_buf, y, ny,
+         Nx ? Nx->p1 : nullptr, Nx ? Nx->r : 0, Nx ? Nx->q : nullptr, C.ra);
+}
+
+// the (gated, chunks per gathered row, chunks per stage-1 row) forms that occur for
+// d <= 8192: both counts follow from d
+template <bool GATED>
+bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
+                   hipStream_t s, const hipEvent_t* tev) {
+  const int cpt = pick_cpt_b1(row_chunks(C)), ncpt = la_ncpt(C.d);
+#define SFFN_LA(CP, NC)                                           \
+  if (cpt == CP && ncpt == NC) {                                  \
+    la_gather_launch<GATED, CP, NC>(C, Nx, x, y, s, tev);         \
+    return true;                                                  \
+  }
+  if (GATED) {
+    SFFN_LA(1, 1) SFFN_LA(2, 1) SFFN_LA(4, 2) SFFN_LA(6, 4) SFFN_LA(8, 4)
+  } else {
+    SFFN_LA(1, 1) SFFN_LA(2, 2) SFFN_LA(4, 4)
+  }
+#undef SFFN_LA
+  return false;
+}
+
+template <int UPT, int NCHP>
+void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
+                    uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
+  const int ncb = C ? down_blocks(*C) : 1;
+  const int ndown = C ? ncb * C->ks_down : 0;
+  const int nscore = Nx ? Nx->g_mid : 0;
+  SplitArg none{};
+  launch(k_la_down<UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
+         C ? C->w_down_t : nullptr, C ? C->b_out : nullptr, C ? C->h_buf : nullptr,
+         C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
+         C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
+         Nx ? Nx->p_bias : nullptr, Nx ? Nx->q : nullptr, Nx ? Nx->tau : 0.f,
+         Nx ? Nx->rs : nullptr, Nx ? Nx->wbits : nullptr, C ? C->sa : none);
+}
+
+template <int UPT>
+bool la_down_nchp(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
+                  uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
+  switch (Nx ? Nx->r / 8 : 32) {
+    case 8: la_down_launch<UPT, 8>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 16: la_down_launch<UPT, 16>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 32: la_down_launch<UPT, 32>(C, Nx, idx, count, tok, y, s, tev); return true;
+    default: return false;
+  }
+}
+
+bool la_down_any(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
+                 uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
+  switch (C ? C->split_upt : 1) {
+    case 1: return la_down_nchp<1>(C, Nx, idx, count, tok, y, s, tev);
+    case 2: return la_down_nchp<2>(C, Nx, idx, count, tok, y, s, tev);
+    case 4: return la_down_nchp<4>(C, Nx, idx, count, tok, y, s, tev);
+    default: return la_down_nchp<8>(C, Nx, idx, count, tok, y, s, tev);
+  }
+}
+
 }  // namespace
 
 
@@ -505,6 +739,41 @@ void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
     down_b1_any<true>(L, idx_out, count_out, tok_out, y, s, tev);
   else
     down_b1_any<false>(L, idx_out, count_out, tok_out, y, s, tev);
+}
+
+// A layer the look-ahead kernels cover: fp16 weights and predictor, one-row stage 1
+// (rank below 512, 8 to 32 chunks a predictor row), d <= 8192, and the single-token
+// decode's own conditions.
+bool lookahead_layer_ok(const LayerDev& L) {
+  if (!L.w_f16 || !L.p_f16 || L.r >= 512) return false;
+  const int nchp = L.r / 8;
+  if (nchp != 8 && nchp != 16 && nchp != 32) return false;
+  if (la_ncpt(L.d) == 0 || L.d % 8 != 0) return false;
+  const int cpt = pick_cpt_b1(row_chunks(L)), ncpt = la_ncpt(L.d);
+  const bool form = L.gated ? ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 1) ||
+                               (cpt == 4 && ncpt == 2) || (cpt == 6 && ncpt == 4) ||
+                               (cpt == 8 && ncpt == 4))
+                            : ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 2) ||
+                               (cpt == 4 && ncpt == 4));
+  return form && occ_mid_b1(L) > 0;
+}
+
+hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s) {
+  run_stage1(Nx, x, 1, s, nullptr, nullptr, 0, false, false);
+  if (!la_down_any(nullptr, &Nx, nullptr, nullptr, nullptr, nullptr, s, nullptr))
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t run_lookahead(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
+                         int32_t* idx, int32_t* count, uint64_t* tok, hipStream_t s,
+                         const hipEvent_t* ev) {
+  const bool ok = C.gated ? la_gather_any<true>(C, Nx, x, y, s, ev ? ev + 2 : nullptr)
+                          : la_gather_any<false>(C, Nx, x, y, s, ev ? ev + 2 : nullptr);
+  if (!ok) return hipErrorInvalidValue;
+  if (!la_down_any(&C, Nx, idx, count, tok, y, s, ev ? ev + 4 : nullptr))
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace sffn

@@ -102,6 +102,15 @@ void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const h
 bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev);
 int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 kernel applies
+// look-ahead decode (one token): which layers its kernels cover; begin (stage 1 and the
+// scores of layer Nx on x, leaving Nx's range words); one layer C on x over its held set,
+// predicting Nx's set from x when Nx is given (ev: optional six timing events, of which
+// pairs 1 and 2 stamp the two launches)
+bool lookahead_layer_ok(const LayerDev& L);
+hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s);
+hipError_t run_lookahead(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
+                         int32_t* idx, int32_t* count, uint64_t* tok, hipStream_t s,
+                         const hipEvent_t* ev);
 void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
                  float* y, hipStream_t s, const hipEvent_t* tev);
 // sffn_batch.hip: the middle kernel for any batch (small-batch kernel for 2..8 tokens,

@@ -191,6 +191,28 @@ class SparseFFN:
                             count.data_ptr(), tokmask.data_ptr(), _ptr(scores), _stream(stream))
         return y, idx, count, tokmask
 
+    def lookahead_begin(self, x, stream=None):
+        """Predict this layer's active set from x ([1, d] fp32) and hold it for
+        decode_ahead (sparse_ffn_lookahead_begin)."""
+        if self._check_x(x) != 1:
+            raise ValueError("the look-ahead decode takes one token")
+        N.sparse_ffn_lookahead_begin(self.handle, x.data_ptr(), _stream(stream))
+
+    def decode_ahead(self, x, nxt=None, y=None, idx=None, count=None, tokmask=None, stream=None):
+        """This layer on x ([1, d] fp32) over the set held from lookahead_begin or from the
+        previous layer's decode_ahead, predicting nxt's set from x when nxt (the next
+        SparseFFN) is given (sparse_ffn_decode_lookahead). Returns y, idx, count, tokmask."""
+        if self._check_x(x) != 1:
+            raise ValueError("the look-ahead decode takes one token")
+        dev = x.device
+        y = torch.empty((1, self.d), dtype=torch.float32, device=dev) if y is None else y
+        idx = torch.empty(self.n, dtype=torch.int32, device=dev) if idx is None else idx
+        count = torch.empty(1, dtype=torch.int32, device=dev) if count is None else count
+        N.sparse_ffn_decode_lookahead(self.handle, nxt.handle if nxt is not None else None,
+                                      x.data_ptr(), y.data_ptr(), idx.data_ptr(),
+                                      count.data_ptr(), _ptr(tokmask), _stream(stream))
+        return y, idx, count, tokmask
+
     def close(self):
         if getattr(self, "handle", None):
             N.sparse_ffn_destroy(self.handle)
@@ -260,4 +282,25 @@ def decode_lookahead(layers, xs, bufs: LookaheadBuffers, stream=None, side_strea
                           y=bufs.y[l], stream=main)
         if l + 1 < L:
             main.wait_event(listed)
+    return bufs.y
+
+
+def decode_lookahead_fused(layers, xs, bufs: LookaheadBuffers, stream=None):
+    """The look-ahead decode of decode_lookahead for one token, in two launches a layer on
+    one stream (sparse_ffn_lookahead_begin, then sparse_ffn_decode_lookahead per layer):
+    the next layer's prediction shares the launches of the current layer's gather and
+    down projection instead of running on a second stream. Same sets and outputs:
+    bufs.y[l] = layer l on xs[l] over the set its predictor gives for xs[l - 1] (layer 0:
+    xs[0]); bufs.idx / count / tokmask hold each layer's list."""
+    main = stream if stream is not None else torch.cuda.current_stream()
+    L = len(layers)
+    if len(xs) != L:
+        raise ValueError("one input per layer")
+    if bufs.B != 1:
+        raise ValueError("the fused look-ahead decode takes one token")
+    layers[0].lookahead_begin(xs[0], stream=main)
+    for l in range(L):
+        layers[l].decode_ahead(xs[l], layers[l + 1] if l + 1 < L else None, y=bufs.y[l],
+                               idx=bufs.idx[l], count=bufs.count[l:l + 1],
+                               tokmask=bufs.tokmask[l], stream=main)
     return bufs.y

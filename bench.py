@@ -171,8 +171,9 @@ def main():
                     help="launch every decode eagerly instead of replaying captured graphs "
                          "(for per-dispatch counter collection; the timing is then not the metric)")
     ap.add_argument("--lookahead", action="store_true",
-                    help="also time the look-ahead schedule (next layer's mask predicted from "
-                         "the current layer's input on a second stream), reported beside the metric")
+                    help="also time the look-ahead decode (next layer's mask predicted from the "
+                         "current layer's input: on a second stream, and at one token also fused "
+                         "into the current layer's two launches), reported beside the metric")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 4 times (the known-size "
                          "kernel that scales HBM counter readings)")
@@ -186,7 +187,8 @@ def main():
     import torch
     import torch.nn.functional as F
 
-    from activation_sparse_decode_rank_amd import LookaheadBuffers, SparseFFN, decode_lookahead
+    from activation_sparse_decode_rank_amd import (LookaheadBuffers, SparseFFN, decode_lookahead,
+                                                   decode_lookahead_fused)
     from activation_sparse_decode_rank_amd import _native as NAT
     from synth import get_config, make_layer, make_tokens
 
@@ -309,31 +311,50 @@ def main():
                              stream=stream if stream is not None else torch.cuda.current_stream(),
                              side_stream=side)
 
-        la_step(0)
-        torch.cuda.synchronize()
-        la_graphs = []
-        if not args.no_graph:
-            for gi in range(T // G):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    for t in range(gi * G, (gi + 1) * G):
-                        la_step(t, cap)
-                la_graphs.append(g)
+        def la_fused_step(t, stream=None):
+            decode_lookahead_fused(layers, [X[t, l] for l in range(L)], la_bufs, stream=stream)
+
+        def time_schedule(step_fn):
+            step_fn(0)
             torch.cuda.synchronize()
-        replay(la_graphs, warmup, la_step)
-        torch.cuda.synchronize()
-        e0.record()
-        replay(la_graphs, steps, la_step)
-        e1.record()
-        torch.cuda.synchronize()
-        la_ms = e0.elapsed_time(e1) / steps
+            gl = []
+            if not args.no_graph:
+                for gi in range(T // G):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap):
+                        for t in range(gi * G, (gi + 1) * G):
+                            step_fn(t, cap)
+                    gl.append(g)
+                torch.cuda.synchronize()
+            replay(gl, warmup, step_fn)
+            torch.cuda.synchronize()
+            e0.record()
+            replay(gl, steps, step_fn)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        la_ms = time_schedule(la_step)
         la_us = la_ms * 1000.0 / L
         lookahead = {"us_per_layer": round(la_us, 3), "ms_per_step": round(la_ms, 5),
                      "speedup_vs_metric_path": round(us_per_layer / la_us, 3),
                      "mask": "layer l >= 1 from layer l-1's input (layer l's predictor, second "
                              "stream beside layer l-1's forward); layer 0 from its own input"}
-        log(f"look-ahead decode: {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
-        del la_graphs, la_bufs
+        log(f"look-ahead decode (two streams): {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
+        if B == 1:
+            try:
+                fu_ms = time_schedule(la_fused_step)
+            except Exception as e:  # shapes the fused kernels do not cover
+                log(f"fused look-ahead not run: {e}")
+            else:
+                fu_us = fu_ms * 1000.0 / L
+                lookahead.update({
+                    "fused_us_per_layer": round(fu_us, 3), "fused_ms_per_step": round(fu_ms, 5),
+                    "fused_speedup_vs_metric_path": round(us_per_layer / fu_us, 3),
+                    "fused": "two launches a layer: gather + next layer's stage 1, then down "
+                             "projection + next layer's scores"})
+                log(f"look-ahead decode (fused): {fu_ms:.4f} ms/step, {fu_us:.3f} us/layer")
+        del la_bufs
 
     cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
     if B == 1:

@@ -150,6 +150,30 @@ int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t*
 int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                       int32_t* count, uint64_t* tokmask, float* scores, void* stream);
 
+/* Look-ahead decode, one token (the asynchronous predictor of the novita.ai
+ * activation-sparsity article, section 上下文稀疏性: the next layer's active neurons are
+ * predicted from the current layer's input, beside the current layer's weight reads).
+ *
+ * sparse_ffn_lookahead_begin(first, x) predicts first's active set from x (first's own
+ * input, as sparse_ffn_decode would) and keeps it in first's workspace.
+ * sparse_ffn_decode_lookahead(cur, next, x) then runs layer cur on its input x over the
+ * set held in cur's workspace (from begin, or from the previous call, which named cur as
+ * its next), writing y, idx, count and, if non-NULL, tokmask as sparse_ffn_decode does at
+ * B = 1; and, when next is non-NULL, predicts next's set from this same x and keeps it in
+ * next's workspace. A stack of layers 0..L-1 is: begin(h0, x0); then for each l,
+ * decode_lookahead(h_l, h_{l+1} or NULL for the last, x_l). Layer l >= 1 thus uses the set
+ * its own predictor gives for x_{l-1}; its list is bit-exact with sparse_ffn_decode's on
+ * x_{l-1}, and y is sparse_ffn_forward's on x_l over that list (bitwise so in the
+ * deterministic mode).
+ * Two launches per layer, and no wait between the launches' workgroups. x: device [1][d]
+ * fp32; y: device [1][d] fp32. Both layers need fp16 weights and predictor, rank below
+ * 512, d <= 8192, the same d, and workspaces that do not overlap (SFFN_ERR_UNSUPPORTED /
+ * SFFN_ERR_INVALID otherwise). Calls on the layers involved must be ordered on one
+ * stream. */
+int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream);
+int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
+                                int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream);
+
 /* Measurement hook. events: NULL (off) or an array of six hipEvent_t (passed as void*)
  * created by the caller. While set, every sparse_ffn_decode on this handle launches its
  * three kernels so that each dispatch stamps a pair of events with its own start and end

@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -119,6 +119,9 @@ def test_calls_reject_null_handle_and_bad_batch(N):
     assert L.sparse_ffn_decode(None, 0x10000, 1, 0x10000, 0x10000, 0x10000, None, None, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_destroy(None) == N.SFFN_OK
     assert L.sparse_ffn_set_timing_events(None, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_lookahead_begin(None, 0x10000, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_decode_lookahead(None, None, 0x10000, 0x10000, 0x10000, 0x10000, None,
+                                         None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_pack_rows(0x10000, 0x10000, 0x10000, 4, 6, 0, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_pack_rows(0x10000, 0x10000, 0x10000, 4, 8, 4, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_profile_counts(None, 1, 0, None, 8, 8, 0x10000, 4, 0x10000, None) == N.SFFN_ERR_INVALID

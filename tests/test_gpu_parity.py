@@ -259,6 +259,84 @@ def test_lookahead_stack(name, d, n, r, B):
         assert np.array_equal(to_np(y2), to_np(bufs.y[l]))
 
 
+
+@pytest.mark.parametrize("name,d,n,r,nl,det", [
+    ("C2", 512, 1000, 64, 3, True), ("C3", 512, 1100, 64, 3, True),
+    ("C2", 1024, 3000, 128, 3, False), ("C3", 2048, 2500, 128, 3, True),
+    ("C2", 4096, 16384, 256, 2, False), ("C3", 4096, 11008, 256, 2, False)])
+def test_lookahead_fused(name, d, n, r, nl, det):
+    """Fused look-ahead decode (two launches a layer): layer l >= 1 takes its active set from
+    layer l - 1's input through its own predictor, layer 0 from its own input. Each mask
+    against the oracle outside the band, each output against the oracle under the GPU's own
+    list; each list bit-exact with the single-token decode step's on the input it was
+    predicted from; with the same token fed to every layer, y equals the decode step's
+    (bitwise in the deterministic mode). Run twice: the held sets and buffers are reused."""
+    from activation_sparse_decode_rank_amd import LookaheadBuffers, decode_lookahead_fused
+    c = cfg(name)
+    say(f"fused look-ahead {name} d={d} n={n} r={r} layers={nl} det={det}")
+    stack = [build(c, l, d=d, n=n, rank=r, deterministic=det) for l in range(nl)]
+    layers = [s for s, _, _ in stack]
+    xs = [tokens(c, 1, d, tag=310 + l) for l in range(nl)]
+    bufs = LookaheadBuffers(layers, 1)
+    for _ in range(2):
+        decode_lookahead_fused(layers, xs, bufs)
+    torch.cuda.synchronize()
+    for l, (s, L, _) in enumerate(stack):
+        k = int(bufs.count[l].item())
+        idx_h, tok_h = to_np(bufs.idx[l]), to_np(bufs.tokmask[l])
+        assert np.all(np.diff(idx_h[:k]) > 0)
+        assert np.all(tok_h[:k] == 1)
+        src = xs[0] if l == 0 else xs[l - 1]
+        S = oracle.predict(to_np(src), L["p1"], L["p2"], L["c"])
+        M, nband = check_mask(gpu_mask_orig(s.perm, idx_h, k, tok_h, 1, n), S)
+        ri, rk, rt = oracle.compact(M)
+        Y = oracle.forward(to_np(xs[l]), L["w_a"], L["w_o"], ri, rt, Wu=L["w_u"], b_a=L["b_a"],
+                           b_o=L["b_o"])
+        errs = rel_err_rows(to_np(bufs.y[l]), Y)
+        assert max(errs) <= REL_TOL, (l, errs)
+        # the decode step on the input the set was predicted from makes the same list
+        _, i2, c2, _ = s.decode(src)
+        torch.cuda.synchronize()
+        assert int(c2.item()) == k
+        assert np.array_equal(to_np(i2)[:k], idx_h[:k])
+        say(f"  layer {l}: count={k} band={nband} err={max(errs):.2e}")
+    # one token for every layer: the held set is the layer's own, so y is the decode step's
+    same = [xs[0]] * nl
+    decode_lookahead_fused(layers, same, bufs)
+    torch.cuda.synchronize()
+    for l, s in enumerate(layers):
+        y2, i2, c2, _ = s.decode(xs[0])
+        torch.cuda.synchronize()
+        k = int(c2.item())
+        assert k == int(bufs.count[l].item())
+        assert np.array_equal(to_np(i2)[:k], to_np(bufs.idx[l])[:k])
+        if det:
+            assert np.array_equal(to_np(y2), to_np(bufs.y[l]))
+        else:
+            scale = float(np.abs(to_np(y2)).max())
+            assert float(np.abs(to_np(y2) - to_np(bufs.y[l])).max()) <= 1e-5 * scale
+
+
+def test_lookahead_fused_rejects():
+    """The fused look-ahead entry points reject a layer paired with itself and shapes their
+    kernels do not cover (fp32 weights), before anything is enqueued."""
+    from activation_sparse_decode_rank_amd import _native as N
+    say("fused look-ahead argument checks")
+    a, _, _ = build(cfg("C2"), 0, d=512, n=1000, rank=64)
+    f32, _, _ = build(cfg("C1"), 0, d=256, n=600, rank=64)
+    x = tokens(cfg("C2"), 1, 512)
+    y = torch.empty((1, 512), dtype=torch.float32, device="cuda")
+    idx = torch.empty(1000, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    L = N.lib()
+    assert L.sparse_ffn_decode_lookahead(a.handle, a.handle, x.data_ptr(), y.data_ptr(),
+                                         idx.data_ptr(), cnt.data_ptr(), None, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_decode_lookahead(a.handle, f32.handle, x.data_ptr(), y.data_ptr(),
+                                         idx.data_ptr(), cnt.data_ptr(), None, None) == N.SFFN_ERR_INVALID
+    x1 = tokens(cfg("C1"), 1, 256)
+    assert L.sparse_ffn_lookahead_begin(f32.handle, x1.data_ptr(), None) == N.SFFN_ERR_UNSUPPORTED
+
+
 def test_decode_deterministic():
     """deterministic=1: repeated decodes give bitwise-identical y and lists, and match the
     oracle (the down projection splits rows at most two ways)."""
