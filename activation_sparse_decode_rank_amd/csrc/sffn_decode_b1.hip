@@ -457,8 +457,11 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
 // next layer's stage 1 (qn[w] = P1n[w] . x, as k_pred_stage1 does for one token) between
 // issuing its first weight loads and using them. The first workgroups also clear y (ny
 // floats) for the down projection's split sums. fp16 weights and predictor.
+// Up to four chunks a gathered row, the registers are capped so that four workgroups fit a
+// compute unit: every range is then resident at once, as in the single-token middle kernel.
 template <bool GATED, int CPT, int NCPT>
-__global__ __launch_bounds__(TPB) void k_la_gather(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
+                          amdgpu_waves_per_eu(CPT <= 4 ? 4 : 1))) void k_la_gather(
     const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
     int d, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
     float* __restrict__ h_g, float* __restrict__ y0, int ny, const void* __restrict__ p1n,
@@ -476,16 +479,15 @@ __global__ __launch_bounds__(TPB) void k_la_gather(
   const float ba = (tid < nown && b_act) ? b_act[r0 + tid] : 0.f;
   const int nch = d / EPC;
   const bool s1 = w < rn;  // uniform
+  // the stage-1 row's chunks are chunks tid + m TPB (m < NCPT <= CPT) of x, which the
+  // gather's input registers xs[m] already hold wherever the chunk exists
+  static_assert(NCPT <= CPT, "stage-1 chunks within the gather's input chunks");
   u32x4 pv[NCPT];
-  float x1[NCPT][EPC];
   if (s1) {
 #pragma unroll
     for (int m = 0; m < NCPT; ++m) {
       const int c = tid + m * TPB;
-      if (c < nch) {
-        pv[m] = ld_stream(p1n, (size_t)w * nch + c);
-        load_x<EPC>(x + (size_t)c * EPC, x1[m]);
-      }
+      if (c < nch) pv[m] = ld_stream(p1n, (size_t)w * nch + c);
     }
   }
   float xs[CPT][EPC];
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(TPB) void k_la_gather(
         float f[EPC];
         unpack<true>(pv[m], f);
 #pragma unroll
-        for (int e2 = 0; e2 < EPC; ++e2) acc = fmaf(f[e2], x1[m][e2], acc);
+        for (int e2 = 0; e2 < EPC; ++e2) acc = fmaf(f[e2], xs[m][e2], acc);
       }
     }
     acc = wave_sum(acc);
@@ -525,9 +527,12 @@ __global__ __launch_bounds__(TPB) void k_la_gather(
 }
 
 // Workgroups below ndown run this layer's down projection (as k_down_b1, which also
-// publishes the list, count and token bits); workgroup ndown + w scores the next layer's
-// range w (bounds from its range table rsn) against qn and stores the range's activity
-// word in wbits_n. fp16 weights and predictor.
+// publishes the list, count and token bits); workgroup ndown + i scores the next layer's
+// ranges 2i and 2i + 1 (of gn; bounds from its range table rsn) against qn and stores each
+// range's activity word in wbits_n. Two ranges a workgroup keep every workgroup of the
+// launch resident at once; the second range's predictor rows are pulled into cache while
+// the first is scored (one load per 128-byte line, values discarded). fp16 weights and
+// predictor.
 template <int UPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_la_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y,
     int ndown, const void* __restrict__ p2n, const float* __restrict__ pbn,
-    const float* __restrict__ qn, float taun, const int32_t* __restrict__ rsn,
+    const float* __restrict__ qn, float taun, const int32_t* __restrict__ rsn, int gn,
     uint64_t* __restrict__ wbits_n, const SplitArg sa) {
   __shared__ uint8_t s_act[MID_RANGE_MAX];
   touch_kernargs<2>();
@@ -544,11 +549,32 @@ __global__ __launch_bounds__(TPB) void k_la_down(
                             idx_out, count_out, tokmask_out, y, sa);
     return;
   }
-  const int w = blockIdx.x - ndown, tid = threadIdx.x;
-  const int r0 = rsn[w], nown = rsn[w + 1] - r0;
-  mid_scores_b1<true, NCHP>(p2n, pbn, qn, r0, nown, taun, nullptr, s_act, []() {});
-  const uint64_t word = __ballot(tid < nown && s_act[tid]);
-  if (tid == 0) wbits_n[w] = word;
+  constexpr int ROW_BYTES = NCHP * 16;
+  constexpr int PF_ITERS = (MID_RANGE_MAX * ROW_BYTES + TPB * 128 - 1) / (TPB * 128);
+  const int w0 = 2 * ((int)blockIdx.x - ndown), tid = threadIdx.x;
+  const bool two = w0 + 1 < gn;  // uniform
+  const int ra0 = rsn[w0], n0 = rsn[w0 + 1] - ra0;
+  const int ra1 = two ? rsn[w0 + 1] : 0, n1 = two ? rsn[w0 + 2] - ra1 : 0;
+  uint32_t sink = 0;
+  mid_scores_b1<true, NCHP>(p2n, pbn, qn, ra0, n0, taun, nullptr, s_act, [&]() {
+    if (!two) return;
+    const char* base = static_cast<const char*>(p2n) + (size_t)ra1 * ROW_BYTES;
+    const int bytes = n1 * ROW_BYTES;
+#pragma unroll
+    for (int v = 0; v < PF_ITERS; ++v) {
+      const int off = min((tid + v * TPB) * 128, bytes - 4);
+      sink ^= *reinterpret_cast<const uint32_t*>(base + off);
+    }
+    if (tid < n1 && pbn) sink ^= __float_as_uint(pbn[ra1 + tid]);
+  });
+  const uint64_t word0 = __ballot(tid < n0 && s_act[tid]);
+  if (tid == 0) wbits_n[w0] = word0;
+  if (two) {
+    mid_scores_b1<true, NCHP>(p2n, pbn, qn, ra1, n1, taun, nullptr, s_act, []() {});
+    const uint64_t word1 = __ballot(tid < n1 && s_act[tid]);
+    if (tid == 0) wbits_n[w0 + 1] = word1;
+  }
+  asm volatile("" ::"v"(sink));
 }
 
 
@@ -672,7 +698,7 @@ bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float*
     la_gather_launch<GATED, CP, NC>(C, Nx, x, y, s, tev);         \
     return true;                                                  \
   }
-  if (GATED) {
+  if constexpr (GATED) {
     SFFN_LA(1, 1) SFFN_LA(2, 1) SFFN_LA(4, 2) SFFN_LA(6, 4) SFFN_LA(8, 4)
   } else {
     SFFN_LA(1, 1) SFFN_LA(2, 2) SFFN_LA(4, 4)
@@ -686,14 +712,14 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
                     uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   const int ncb = C ? down_blocks(*C) : 1;
   const int ndown = C ? ncb * C->ks_down : 0;
-  const int nscore = Nx ? Nx->g_mid : 0;
+  const int nscore = Nx ? (Nx->g_mid + 1) / 2 : 0;
   SplitArg none{};
   launch(k_la_down<UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
          C ? C->w_down_t : nullptr, C ? C->b_out : nullptr, C ? C->h_buf : nullptr,
          C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
          C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
          Nx ? Nx->p_bias : nullptr, Nx ? Nx->q : nullptr, Nx ? Nx->tau : 0.f,
-         Nx ? Nx->rs : nullptr, Nx ? Nx->wbits : nullptr, C ? C->sa : none);
+         Nx ? Nx->rs : nullptr, Nx ? Nx->g_mid : 0, Nx ? Nx->wbits : nullptr, C ? C->sa : none);
 }
 
 template <int UPT>

@@ -19,6 +19,11 @@ Also measured, beside the headline number:
   - per-kernel durations from HIP events that each kernel dispatch stamps itself
     (start and end of execution, on the library's stream), with each kernel's algorithmic
     bytes (and, for the matrix-core kernels, flops) per launch;
+  - at one token, the look-ahead decode (`lookahead`): each layer's active set predicted
+    from the previous layer's input and that prediction fused into the previous layer's
+    two launches; a different mask than the headline's (each layer's own input), so it is
+    reported beside it, graph-replayed and timed the same way, with each launch's own
+    event-stamped duration;
   - the dense FFN of the same shapes on the same (unpacked) fp16 weights, through torch
     (hipBLASLt), graph-captured and timed the same way;
   - the fp64 CPU oracle on a bounded sample of the same workload, on the host cores.
@@ -170,10 +175,12 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every decode eagerly instead of replaying captured graphs "
                          "(for per-dispatch counter collection; the timing is then not the metric)")
-    ap.add_argument("--lookahead", action="store_true",
-                    help="also time the look-ahead decode (next layer's mask predicted from the "
-                         "current layer's input: on a second stream, and at one token also fused "
-                         "into the current layer's two launches), reported beside the metric")
+    ap.add_argument("--no-lookahead", action="store_true",
+                    help="skip the look-ahead decode (next layer's mask predicted from the current "
+                         "layer's input, fused into the current layer's two launches; one token), "
+                         "which is otherwise timed and reported beside the metric")
+    ap.add_argument("--lookahead-streams", action="store_true",
+                    help="also time the look-ahead schedule on two streams (separate calls)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 4 times (the known-size "
                          "kernel that scales HBM counter readings)")
@@ -302,7 +309,9 @@ def main():
     # l - 1's forward runs. A different mask than the metric's (each layer's own input), so
     # it is reported beside the metric, not as it.
     lookahead = None
-    if args.lookahead:
+    if args.lookahead_streams or (B == 1 and not args.no_lookahead):
+        lookahead = {"mask": "layer l >= 1 from layer l-1's input (layer l's predictor); layer 0 "
+                             "from its own input"}
         side = torch.cuda.Stream()
         la_bufs = LookaheadBuffers(layers, B)
 
@@ -334,26 +343,50 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / steps
 
-        la_ms = time_schedule(la_step)
-        la_us = la_ms * 1000.0 / L
-        lookahead = {"us_per_layer": round(la_us, 3), "ms_per_step": round(la_ms, 5),
-                     "speedup_vs_metric_path": round(us_per_layer / la_us, 3),
-                     "mask": "layer l >= 1 from layer l-1's input (layer l's predictor, second "
-                             "stream beside layer l-1's forward); layer 0 from its own input"}
-        log(f"look-ahead decode (two streams): {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
-        if B == 1:
+        if args.lookahead_streams:
+            la_ms = time_schedule(la_step)
+            la_us = la_ms * 1000.0 / L
+            lookahead.update({"streams_us_per_layer": round(la_us, 3),
+                              "streams_speedup_vs_metric_path": round(us_per_layer / la_us, 3),
+                              "streams": "separate predict + compact calls on a second stream "
+                                         "beside the previous layer's forward"})
+            log(f"look-ahead decode (two streams): {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
+        if B == 1 and not args.no_lookahead:
             try:
                 fu_ms = time_schedule(la_fused_step)
             except Exception as e:  # shapes the fused kernels do not cover
                 log(f"fused look-ahead not run: {e}")
             else:
                 fu_us = fu_ms * 1000.0 / L
+                la_cnt = la_bufs.count.cpu().numpy().astype(np.int64)  # last step's lists
+                fu_gbps = float(la_cnt.mean()) * cfg.m * d * cfg.w_bytes / (fu_us * 1e-6) / 1e9
                 lookahead.update({
-                    "fused_us_per_layer": round(fu_us, 3), "fused_ms_per_step": round(fu_ms, 5),
-                    "fused_speedup_vs_metric_path": round(us_per_layer / fu_us, 3),
-                    "fused": "two launches a layer: gather + next layer's stage 1, then down "
-                             "projection + next layer's scores"})
+                    "us_per_layer": round(fu_us, 3), "ms_per_step": round(fu_ms, 5),
+                    "speedup_vs_metric_path": round(us_per_layer / fu_us, 3),
+                    "active_weight_gbps": round(fu_gbps, 1),
+                    "active_weight_frac_of_peak": round(fu_gbps / HBM_PEAK_GBPS, 4),
+                    "launches": "two a layer: gather + next layer's stage 1, then down "
+                                "projection + next layer's scores"})
                 log(f"look-ahead decode (fused): {fu_ms:.4f} ms/step, {fu_us:.3f} us/layer")
+                # each launch timed by its own dispatch (events pairs 1 and 2 of a handle)
+                KT = min(args.kernel_tokens, T)
+                fev = HipEvents(6 * KT * L)
+                for t in range(KT):
+                    layers[0].lookahead_begin(X[t, 0])
+                    for l in range(L):
+                        base = 6 * (t * L + l)
+                        NAT.sparse_ffn_set_timing_events(layers[l].handle, fev.ev[base:base + 6])
+                        layers[l].decode_ahead(X[t, l], layers[l + 1] if l + 1 < L else None,
+                                               y=la_bufs.y[l], idx=la_bufs.idx[l],
+                                               count=la_bufs.count[l:l + 1],
+                                               tokmask=la_bufs.tokmask[l])
+                        NAT.sparse_ffn_set_timing_events(layers[l].handle, None)
+                torch.cuda.synchronize()
+                fa = [1000.0 * fev.elapsed_ms(6 * i + 2, 6 * i + 3) for i in range(KT * L)]
+                fb = [1000.0 * fev.elapsed_ms(6 * i + 4, 6 * i + 5) for i in range(KT * L)]
+                fev.close()
+                lookahead["launch_us"] = {"gather_and_next_stage1": round(float(np.mean(fa)), 3),
+                                                "down_and_next_scores": round(float(np.mean(fb)), 3)}
         del la_bufs
 
     cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
@@ -528,6 +561,8 @@ def main():
         "lookahead": lookahead,
         "kernel_source_sha256": kernel_source_sha(),
     }
+    if lookahead and dense and "us_per_layer" in lookahead:
+        lookahead["speedup_vs_dense"] = round(dense["us_per_layer"] / lookahead["us_per_layer"], 3)
     print(json.dumps(out), flush=True)
 
 
