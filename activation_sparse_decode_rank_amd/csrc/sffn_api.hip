@@ -252,6 +252,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
       }
       split_ranges(rs, desc->neuron_freq, L.ks_down, L.sa, L.split_upt);
     }
+    // workgroups per compute unit of this layer's look-ahead down launch (set once here:
+    // the launch order depends on it, and graph capture may be running at call time)
+    L.la_occ = sffn::lookahead_layer_ok(L) ? sffn::lookahead_down_occ(L) : 0;
     sparse_ffn_s* h = new (std::nothrow) sparse_ffn_s;
     if (!h) return SFFN_ERR_HIP;
     h->desc = *desc;
@@ -337,7 +340,6 @@ int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (next && (next->L.d != cur->L.d || overlap(cur->desc, next->desc))) return SFFN_ERR_INVALID;
   if (!lookahead_ok(cur) || (next && !lookahead_ok(next))) return SFFN_ERR_UNSUPPORTED;
-  if (next && cur->L.g_mid < next->L.r) return SFFN_ERR_UNSUPPORTED;  // one stage-1 row a workgroup
   return sffn::run_lookahead(cur->L, next ? &next->L : nullptr, x, y, idx, count, tokmask,
                              static_cast<hipStream_t>(stream), cur->timing ? cur->ev : nullptr) ==
                  hipSuccess

@@ -453,17 +453,18 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
 // kernels, so a layer's list equals the one its own decode step would make from the
 // previous layer's input, and y equals that step's output under that list.
 
-// Workgroup w gathers middle range w of this layer and, for w < rn, computes row w of the
-// next layer's stage 1 (qn[w] = P1n[w] . x, as k_pred_stage1 does for one token) between
-// issuing its first weight loads and using them. The first workgroups also clear y (ny
-// floats) for the down projection's split sums. fp16 weights and predictor.
+// Workgroup w gathers middle range w of this layer (w < gm) and, for w < rn, computes row w
+// of the next layer's stage 1 (qn[w] = P1n[w] . x, in k_pred_stage1's order for one token)
+// between issuing its first weight loads and using them; the grid is max(gm, rn), and
+// workgroups past the ranges compute their stage-1 row only. The first workgroups also
+// clear y (ny floats) for the down projection's split sums. fp16 weights and predictor.
 // Up to four chunks a gathered row, the registers are capped so that four workgroups fit a
 // compute unit: every range is then resident at once, as in the single-token middle kernel.
 template <bool GATED, int CPT, int NCPT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
                           amdgpu_waves_per_eu(CPT <= 4 ? 4 : 1))) void k_la_gather(
     const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
+    int d, int gm, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
     float* __restrict__ h_g, float* __restrict__ y0, int ny, const void* __restrict__ p1n,
     int rn, float* __restrict__ qn, const RangeArg ra) {
   constexpr int EPC = Elt<true>::EPC;
@@ -473,9 +474,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
   __shared__ float s_q[TPB / 64];
   touch_kernargs<2>();
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = rs ? rs[w] : ra.r[w], r1 = rs ? rs[w + 1] : ra.r[w + 1];
-  const int nown = r1 - r0;  // 1..RMAX
-  const uint64_t word = wbits[w] & (nown >= 64 ? ~(uint64_t)0 : (((uint64_t)1) << nown) - 1);
+  const bool owns = w < gm;  // uniform
+  const int r0 = owns ? (rs ? rs[w] : ra.r[w]) : 0;
+  const int nown = owns ? (rs ? rs[w + 1] : ra.r[w + 1]) - r0 : 0;  // 1..RMAX, or 0
+  const uint64_t word =
+      owns ? wbits[w] & (nown >= 64 ? ~(uint64_t)0 : (((uint64_t)1) << nown) - 1) : 0;
   const float ba = (tid < nown && b_act) ? b_act[r0 + tid] : 0.f;
   const int nch = d / EPC;
   const bool s1 = w < rn;  // uniform
@@ -506,7 +509,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
     s_bias[k] = ba;
   }
   __syncthreads();
-  mid_gather_b1<true, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, [&]() {
+  auto stage1 = [&]() {
     if (!s1) return;
     float acc = 0.f;
 #pragma unroll
@@ -523,13 +526,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
     if (lane == WAVE_SUM_LANE) s_q[wave] = acc;
     __syncthreads();
     if (tid == 0) qn[w] = ((s_q[0] + s_q[1]) + s_q[2]) + s_q[3];
-  });
+  };
+  mid_gather_b1<true, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, stage1);
 }
 
-// Workgroups below ndown run this layer's down projection (as k_down_b1, which also
-// publishes the list, count and token bits); workgroup ndown + i scores the next layer's
-// ranges 2i and 2i + 1 (of gn; bounds from its range table rsn) against qn and stores each
-// range's activity word in wbits_n. Two ranges a workgroup keep every workgroup of the
+// ndown workgroups run this layer's down projection (as k_down_b1, which also publishes the
+// list, count and token bits); scoring workgroup i scores the next layer's ranges 2i and
+// 2i + 1 (of gn; bounds from its range table rsn) against qn and stores each range's
+// activity word in wbits_n. The down workgroups come first, unless sfirst: when the launch
+// does not fit the GPU at once, the scoring workgroups go first so that the next layer's
+// predictor stream starts with the down projection's instead of after it. Two ranges a workgroup keep every workgroup of the
 // launch resident at once; the second range's predictor rows are pulled into cache while
 // the first is scored (one load per 128-byte line, values discarded). fp16 weights and
 // predictor.
@@ -541,17 +547,18 @@ __global__ __launch_bounds__(TPB) void k_la_down(
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y,
     int ndown, const void* __restrict__ p2n, const float* __restrict__ pbn,
     const float* __restrict__ qn, float taun, const int32_t* __restrict__ rsn, int gn,
-    uint64_t* __restrict__ wbits_n, const SplitArg sa) {
+    uint64_t* __restrict__ wbits_n, int sfirst, const SplitArg sa) {
   __shared__ uint8_t s_act[MID_RANGE_MAX];
   touch_kernargs<2>();
-  if ((int)blockIdx.x < ndown) {
-    down_b1_body<true, UPT>(blockIdx.x, w_down_t, b_out, h_in, d, n, wbits, rs, KS, ncb,
-                            idx_out, count_out, tokmask_out, y, sa);
+  const int nsc = (gn + 1) / 2, bid = blockIdx.x;
+  if (sfirst ? bid >= nsc : bid < ndown) {
+    down_b1_body<true, UPT>(sfirst ? bid - nsc : bid, w_down_t, b_out, h_in, d, n, wbits, rs,
+                            KS, ncb, idx_out, count_out, tokmask_out, y, sa);
     return;
   }
   constexpr int ROW_BYTES = NCHP * 16;
   constexpr int PF_ITERS = (MID_RANGE_MAX * ROW_BYTES + TPB * 128 - 1) / (TPB * 128);
-  const int w0 = 2 * ((int)blockIdx.x - ndown), tid = threadIdx.x;
+  const int w0 = 2 * (sfirst ? bid : bid - ndown), tid = threadIdx.x;
   const bool two = w0 + 1 < gn;  // uniform
   const int ra0 = rsn[w0], n0 = rsn[w0 + 1] - ra0;
   const int ra1 = two ? rsn[w0 + 1] : 0, n1 = two ? rsn[w0 + 2] - ra1 : 0;
@@ -672,23 +679,24 @@ void down_b1_any(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
 
 
 // ---- look-ahead launches
-// chunks per thread of the folded stage-1 row (d / 8 chunks of fp16): 1, 2 or 4, else 0
+// chunks per thread of the folded stage-1 row (d / 8 chunks of fp16): 1, 2, 4 or 6, else 0
 inline int la_ncpt(int d) {
   const int nch = d / 8;
-  return nch <= TPB ? 1 : nch <= 2 * TPB ? 2 : nch <= 4 * TPB ? 4 : 0;
+  return nch <= TPB ? 1 : nch <= 2 * TPB ? 2 : nch <= 4 * TPB ? 4 : nch <= 6 * TPB ? 6 : 0;
 }
 
 template <bool GATED, int CPT, int NCPT>
 void la_gather_launch(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                       hipStream_t s, const hipEvent_t* tev) {
   const int ny = C.ks_down > 1 ? C.d : 0;
-  launch(k_la_gather<GATED, CPT, NCPT>, dim3(C.g_mid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
-         x, C.d, C.rs_in_arg ? nullptr : C.rs, C.wbits, C.h_buf, y, ny,
+  const int grid = std::max(C.g_mid, Nx ? Nx->r : 0);
+  launch(k_la_gather<GATED, CPT, NCPT>, dim3(grid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
+         x, C.d, C.g_mid, C.rs_in_arg ? nullptr : C.rs, C.wbits, C.h_buf, y, ny,
          Nx ? Nx->p1 : nullptr, Nx ? Nx->r : 0, Nx ? Nx->q : nullptr, C.ra);
 }
 
 // the (gated, chunks per gathered row, chunks per stage-1 row) forms that occur for
-// d <= 8192: both counts follow from d
+// d <= 8192, and plain layers up to d = 12288: both counts follow from d
 template <bool GATED>
 bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                    hipStream_t s, const hipEvent_t* tev) {
@@ -701,7 +709,7 @@ bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float*
   if constexpr (GATED) {
     SFFN_LA(1, 1) SFFN_LA(2, 1) SFFN_LA(4, 2) SFFN_LA(6, 4) SFFN_LA(8, 4)
   } else {
-    SFFN_LA(1, 1) SFFN_LA(2, 2) SFFN_LA(4, 4)
+    SFFN_LA(1, 1) SFFN_LA(2, 2) SFFN_LA(4, 4) SFFN_LA(6, 6)
   }
 #undef SFFN_LA
   return false;
@@ -714,12 +722,14 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
   const int ndown = C ? ncb * C->ks_down : 0;
   const int nscore = Nx ? (Nx->g_mid + 1) / 2 : 0;
   SplitArg none{};
+  const int sfirst = C && nscore > 0 && ndown + nscore > C->la_occ * C->n_cus ? 1 : 0;
   launch(k_la_down<UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
          C ? C->w_down_t : nullptr, C ? C->b_out : nullptr, C ? C->h_buf : nullptr,
          C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
          C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
          Nx ? Nx->p_bias : nullptr, Nx ? Nx->q : nullptr, Nx ? Nx->tau : 0.f,
-         Nx ? Nx->rs : nullptr, Nx ? Nx->g_mid : 0, Nx ? Nx->wbits : nullptr, C ? C->sa : none);
+         Nx ? Nx->rs : nullptr, Nx ? Nx->g_mid : 0, Nx ? Nx->wbits : nullptr, sfirst,
+         C ? C->sa : none);
 }
 
 template <int UPT>
@@ -729,7 +739,29 @@ bool la_down_nchp(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* 
     case 8: la_down_launch<UPT, 8>(C, Nx, idx, count, tok, y, s, tev); return true;
     case 16: la_down_launch<UPT, 16>(C, Nx, idx, count, tok, y, s, tev); return true;
     case 32: la_down_launch<UPT, 32>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 64: la_down_launch<UPT, 64>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 128: la_down_launch<UPT, 128>(C, Nx, idx, count, tok, y, s, tev); return true;
     default: return false;
+  }
+}
+
+template <int UPT, int NCHP>
+int la_down_occ() {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_la_down<UPT, NCHP>, TPB,
+                                                   (size_t)LIST_CAP * 4) != hipSuccess)
+    occ = 0;
+  return occ;
+}
+
+template <int UPT>
+int la_down_occ_nchp(int nchp) {
+  switch (nchp) {
+    case 8: return la_down_occ<UPT, 8>();
+    case 16: return la_down_occ<UPT, 16>();
+    case 32: return la_down_occ<UPT, 32>();
+    case 64: return la_down_occ<UPT, 64>();
+    default: return la_down_occ<UPT, 128>();
   }
 }
 
@@ -767,20 +799,20 @@ void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
     down_b1_any<false>(L, idx_out, count_out, tok_out, y, s, tev);
 }
 
-// A layer the look-ahead kernels cover: fp16 weights and predictor, one-row stage 1
-// (rank below 512, 8 to 32 chunks a predictor row), d <= 8192, and the single-token
-// decode's own conditions.
+// A layer the look-ahead kernels cover: fp16 weights and predictor, rank 64 to 1024 (8 to
+// 128 chunks a predictor row, a power of two), d <= 8192 (plain layers: 12288), and the
+// single-token decode's own conditions.
 bool lookahead_layer_ok(const LayerDev& L) {
-  if (!L.w_f16 || !L.p_f16 || L.r >= 512) return false;
+  if (!L.w_f16 || !L.p_f16) return false;
   const int nchp = L.r / 8;
-  if (nchp != 8 && nchp != 16 && nchp != 32) return false;
+  if (L.r % 8 != 0 || nchp < 8 || nchp > 128 || (nchp & (nchp - 1)) != 0) return false;
   if (la_ncpt(L.d) == 0 || L.d % 8 != 0) return false;
   const int cpt = pick_cpt_b1(row_chunks(L)), ncpt = la_ncpt(L.d);
   const bool form = L.gated ? ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 1) ||
                                (cpt == 4 && ncpt == 2) || (cpt == 6 && ncpt == 4) ||
                                (cpt == 8 && ncpt == 4))
                             : ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 2) ||
-                               (cpt == 4 && ncpt == 4));
+                               (cpt == 4 && ncpt == 4) || (cpt == 6 && ncpt == 6));
   return form && occ_mid_b1(L) > 0;
 }
 
@@ -800,6 +832,16 @@ hipError_t run_lookahead(const LayerDev& C, const LayerDev* Nx, const float* x, 
   if (!la_down_any(&C, Nx, idx, count, tok, y, s, ev ? ev + 4 : nullptr))
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+int lookahead_down_occ(const LayerDev& L) {
+  const int nchp = L.r / 8;
+  switch (L.split_upt) {
+    case 1: return la_down_occ_nchp<1>(nchp);
+    case 2: return la_down_occ_nchp<2>(nchp);
+    case 4: return la_down_occ_nchp<4>(nchp);
+    default: return la_down_occ_nchp<8>(nchp);
+  }
 }
 
 }  // namespace sffn

@@ -67,6 +67,7 @@ struct LayerDev {
   RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)
   SplitArg sa;     // decode down projection: range splits, ks_down of them
   int split_upt;   // most ranges of one split per thread of the down kernel (1, 2, 4, 8)
+  int la_occ;      // workgroups per compute unit of the look-ahead down launch (0: unknown)
 };
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
@@ -107,6 +108,7 @@ int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 ker
 // predicting Nx's set from x when Nx is given (ev: optional six timing events, of which
 // pairs 1 and 2 stamp the two launches)
 bool lookahead_layer_ok(const LayerDev& L);
+int lookahead_down_occ(const LayerDev& L);  // for the launch with this layer as both roles' shape
 hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s);
 hipError_t run_lookahead(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                          int32_t* idx, int32_t* count, uint64_t* tok, hipStream_t s,

@@ -162,14 +162,16 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
  * B = 1; and, when next is non-NULL, predicts next's set from this same x and keeps it in
  * next's workspace. A stack of layers 0..L-1 is: begin(h0, x0); then for each l,
  * decode_lookahead(h_l, h_{l+1} or NULL for the last, x_l). Layer l >= 1 thus uses the set
- * its own predictor gives for x_{l-1}; its list is bit-exact with sparse_ffn_decode's on
- * x_{l-1}, and y is sparse_ffn_forward's on x_l over that list (bitwise so in the
- * deterministic mode).
+ * its own predictor gives for x_{l-1}. Below rank 512 its list is bit-exact with
+ * sparse_ffn_decode's on x_{l-1} (same summation order); from rank 512 sparse_ffn_decode
+ * sums stage 1 in another order, so the lists may differ for scores within rounding of the
+ * threshold. y is the single-token decode's output on x_l over that list (bitwise so in
+ * the deterministic mode).
  * Two launches per layer, and no wait between the launches' workgroups. x: device [1][d]
- * fp32; y: device [1][d] fp32. Both layers need fp16 weights and predictor, rank below
- * 512, d <= 8192, the same d, and workspaces that do not overlap (SFFN_ERR_UNSUPPORTED /
- * SFFN_ERR_INVALID otherwise). Calls on the layers involved must be ordered on one
- * stream. */
+ * fp32; y: device [1][d] fp32. Both layers need fp16 weights and predictor, a rank of 8
+ * times a power of two from 64 to 1024, d <= 8192 (plain layers: 12288), the same d, and
+ * workspaces that do not overlap (SFFN_ERR_UNSUPPORTED / SFFN_ERR_INVALID otherwise).
+ * Calls on the layers involved must be ordered on one stream. */
 int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream);
 int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
                                 int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream);
