@@ -172,8 +172,8 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
  * times a power of two from 64 to 1024, d <= 8192 (plain layers: 12288), the same d, and
  * workspaces that do not overlap (SFFN_ERR_UNSUPPORTED / SFFN_ERR_INVALID otherwise).
  * Calls on the layers involved must be ordered on one stream. The held set lives in the
- * layer's workspace: a sparse_ffn_decode on that layer replaces it with the set of its own
- * input (a layer never predicted holds the empty set). */
+ * layer's workspace: other calls on that layer may overwrite it (sparse_ffn_decode at one
+ * token leaves the set of its own input); a layer never predicted holds the empty set. */
 int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream);
 int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
                                 int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream);
