@@ -348,6 +348,76 @@ def test_lookahead_fused_rejects():
     assert L.sparse_ffn_lookahead_begin(f32.handle, x1.data_ptr(), None) == N.SFFN_ERR_UNSUPPORTED
 
 
+
+@pytest.mark.parametrize("name,d,n,r,B", [("C2", 1024, 3000, 128, 1), ("C3", 1024, 2500, 128, 4),
+                                          ("C3", 1024, 2500, 128, 24)])
+def test_graph_replay_matches_eager(name, d, n, r, B):
+    """The decode step captured in a HIP graph and replayed several times, with eager decodes
+    of other tokens in between, gives each time exactly the eager result for its token
+    (lists bitwise; y bitwise in the deterministic mode). At 24 tokens this runs the
+    stream-K up kernel, whose tile counters must come back to zero after every replay."""
+    c = cfg(name)
+    say(f"graph replay {name} d={d} n={n} r={r} B={B}")
+    s, _, _ = build(c, 0, d=d, n=n, rank=r, max_batch=B, deterministic=True)
+    X = tokens(c, B, d, tag=320)
+    other = tokens(c, B, d, tag=321)
+    y_e, i_e, c_e, t_e = [t.clone() for t in s.decode(X)]
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_e)
+    idx = torch.empty_like(i_e)
+    cnt = torch.empty_like(c_e)
+    tok = torch.empty_like(t_e)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        s.decode(X, y=y, idx=idx, count=cnt, tokmask=tok, stream=side)
+    k = int(c_e.item())
+    for rep in range(3):
+        y.zero_()
+        idx.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == k, rep
+        assert np.array_equal(to_np(idx)[:k], to_np(i_e)[:k]), rep
+        if B > 1:
+            assert np.array_equal(to_np(tok)[:k], to_np(t_e)[:k]), rep
+        assert np.array_equal(to_np(y), to_np(y_e)), rep
+        s.decode(other)  # eager work on the same handle between replays
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_lookahead():
+    """The fused look-ahead decode of a 3-layer stack captured in a HIP graph and replayed
+    three times, with eager decodes in between, equals the eager look-ahead run bitwise
+    (deterministic handles)."""
+    from activation_sparse_decode_rank_amd import LookaheadBuffers, decode_lookahead_fused
+    c = cfg("C2")
+    say("graph replay of the fused look-ahead")
+    layers = [build(c, l, d=1024, n=3000, rank=128, deterministic=True)[0] for l in range(3)]
+    xs = [tokens(c, 1, 1024, tag=330 + l) for l in range(3)]
+    ref = LookaheadBuffers(layers, 1)
+    decode_lookahead_fused(layers, xs, ref)
+    torch.cuda.synchronize()
+    bufs = LookaheadBuffers(layers, 1)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        decode_lookahead_fused(layers, xs, bufs, stream=side)
+    for rep in range(3):
+        for yb in bufs.y:
+            yb.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(bufs.count), to_np(ref.count)), rep
+        for l in range(3):
+            k = int(ref.count[l].item())
+            assert np.array_equal(to_np(bufs.idx[l])[:k], to_np(ref.idx[l])[:k]), (rep, l)
+            assert np.array_equal(to_np(bufs.y[l]), to_np(ref.y[l])), (rep, l)
+        for l, s in enumerate(layers):
+            s.decode(xs[(l + 1) % 3])  # eager work that also overwrites the held sets
+        torch.cuda.synchronize()
+
+
 def test_decode_deterministic():
     """deterministic=1: repeated decodes give bitwise-identical y and lists, and match the
     oracle (the down projection splits rows at most two ways)."""
