@@ -340,6 +340,7 @@ int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (next && (next->L.d != cur->L.d || overlap(cur->desc, next->desc))) return SFFN_ERR_INVALID;
   if (!lookahead_ok(cur) || (next && !lookahead_ok(next))) return SFFN_ERR_UNSUPPORTED;
+  if (next && next->L.w_f16 != cur->L.w_f16) return SFFN_ERR_UNSUPPORTED;  // one launch, one type
   return sffn::run_lookahead(cur->L, next ? &next->L : nullptr, x, y, idx, count, tokmask,
                              static_cast<hipStream_t>(stream), cur->timing ? cur->ev : nullptr) ==
                  hipSuccess

@@ -460,14 +460,14 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
 // clear y (ny floats) for the down projection's split sums. fp16 weights and predictor.
 // Up to four chunks a gathered row, the registers are capped so that four workgroups fit a
 // compute unit: every range is then resident at once, as in the single-token middle kernel.
-template <bool GATED, int CPT, int NCPT>
+template <bool F16, bool GATED, int CPT, int NCPT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
                           amdgpu_waves_per_eu(CPT <= 4 ? 4 : 1))) void k_la_gather(
     const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
     int d, int gm, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
     float* __restrict__ h_g, float* __restrict__ y0, int ny, const void* __restrict__ p1n,
     int rn, float* __restrict__ qn, const RangeArg ra) {
-  constexpr int EPC = Elt<true>::EPC;
+  constexpr int EPC = Elt<F16>::EPC;
   constexpr int RMAX = MID_RANGE_MAX;
   __shared__ int32_t s_rows[RMAX];
   __shared__ float s_bias[RMAX];
@@ -517,7 +517,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
       const int c = tid + m * TPB;
       if (c < nch) {
         float f[EPC];
-        unpack<true>(pv[m], f);
+        unpack<F16>(pv[m], f);
 #pragma unroll
         for (int e2 = 0; e2 < EPC; ++e2) acc = fmaf(f[e2], xs[m][e2], acc);
       }
@@ -527,7 +527,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
     __syncthreads();
     if (tid == 0) qn[w] = ((s_q[0] + s_q[1]) + s_q[2]) + s_q[3];
   };
-  mid_gather_b1<true, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, stage1);
+  mid_gather_b1<F16, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, stage1);
 }
 
 // ndown workgroups run this layer's down projection (as k_down_b1, which also publishes the
@@ -539,7 +539,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
 // launch resident at once; the second range's predictor rows are pulled into cache while
 // the first is scored (one load per 128-byte line, values discarded). fp16 weights and
 // predictor.
-template <int UPT, int NCHP>
+template <bool F16, int UPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_la_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
   touch_kernargs<2>();
   const int nsc = (gn + 1) / 2, bid = blockIdx.x;
   if (sfirst ? bid >= nsc : bid < ndown) {
-    down_b1_body<true, UPT>(sfirst ? bid - nsc : bid, w_down_t, b_out, h_in, d, n, wbits, rs,
+    down_b1_body<F16, UPT>(sfirst ? bid - nsc : bid, w_down_t, b_out, h_in, d, n, wbits, rs,
                             KS, ncb, idx_out, count_out, tokmask_out, y, sa);
     return;
   }
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
   const int ra0 = rsn[w0], n0 = rsn[w0 + 1] - ra0;
   const int ra1 = two ? rsn[w0 + 1] : 0, n1 = two ? rsn[w0 + 2] - ra1 : 0;
   uint32_t sink = 0;
-  mid_scores_b1<true, NCHP>(p2n, pbn, qn, ra0, n0, taun, nullptr, s_act, [&]() {
+  mid_scores_b1<F16, NCHP>(p2n, pbn, qn, ra0, n0, taun, nullptr, s_act, [&]() {
     if (!two) return;
     const char* base = static_cast<const char*>(p2n) + (size_t)ra1 * ROW_BYTES;
     const int bytes = n1 * ROW_BYTES;
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
   const uint64_t word0 = __ballot(tid < n0 && s_act[tid]);
   if (tid == 0) wbits_n[w0] = word0;
   if (two) {
-    mid_scores_b1<true, NCHP>(p2n, pbn, qn, ra1, n1, taun, nullptr, s_act, []() {});
+    mid_scores_b1<F16, NCHP>(p2n, pbn, qn, ra1, n1, taun, nullptr, s_act, []() {});
     const uint64_t word1 = __ballot(tid < n1 && s_act[tid]);
     if (tid == 0) wbits_n[w0 + 1] = word1;
   }
@@ -679,31 +679,32 @@ void down_b1_any(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
 
 
 // ---- look-ahead launches
-// chunks per thread of the folded stage-1 row (d / 8 chunks of fp16): 1, 2, 4 or 6, else 0
-inline int la_ncpt(int d) {
-  const int nch = d / 8;
+// chunks per thread of the folded stage-1 row (d / 8 chunks of fp16, d / 4 of fp32): 1, 2,
+// 4 or 6, else 0
+inline int la_ncpt(int d, bool f16) {
+  const int nch = d / (f16 ? 8 : 4);
   return nch <= TPB ? 1 : nch <= 2 * TPB ? 2 : nch <= 4 * TPB ? 4 : nch <= 6 * TPB ? 6 : 0;
 }
 
-template <bool GATED, int CPT, int NCPT>
+template <bool F16, bool GATED, int CPT, int NCPT>
 void la_gather_launch(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                       hipStream_t s, const hipEvent_t* tev) {
   const int ny = C.ks_down > 1 ? C.d : 0;
   const int grid = std::max(C.g_mid, Nx ? Nx->r : 0);
-  launch(k_la_gather<GATED, CPT, NCPT>, dim3(grid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
+  launch(k_la_gather<F16, GATED, CPT, NCPT>, dim3(grid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
          x, C.d, C.g_mid, C.rs_in_arg ? nullptr : C.rs, C.wbits, C.h_buf, y, ny,
          Nx ? Nx->p1 : nullptr, Nx ? Nx->r : 0, Nx ? Nx->q : nullptr, C.ra);
 }
 
 // the (gated, chunks per gathered row, chunks per stage-1 row) forms that occur for
 // d <= 8192, and plain layers up to d = 12288: both counts follow from d
-template <bool GATED>
+template <bool F16, bool GATED>
 bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                    hipStream_t s, const hipEvent_t* tev) {
-  const int cpt = pick_cpt_b1(row_chunks(C)), ncpt = la_ncpt(C.d);
+  const int cpt = pick_cpt_b1(row_chunks(C)), ncpt = la_ncpt(C.d, F16);
 #define SFFN_LA(CP, NC)                                           \
   if (cpt == CP && ncpt == NC) {                                  \
-    la_gather_launch<GATED, CP, NC>(C, Nx, x, y, s, tev);         \
+    la_gather_launch<F16, GATED, CP, NC>(C, Nx, x, y, s, tev);    \
     return true;                                                  \
   }
   if constexpr (GATED) {
@@ -715,7 +716,7 @@ bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float*
   return false;
 }
 
-template <int UPT, int NCHP>
+template <bool F16, int UPT, int NCHP>
 void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                     uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   const int ncb = C ? down_blocks(*C) : 1;
@@ -723,7 +724,7 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
   const int nscore = Nx ? (Nx->g_mid + 1) / 2 : 0;
   SplitArg none{};
   const int sfirst = C && nscore > 0 && ndown + nscore > C->la_occ * C->n_cus ? 1 : 0;
-  launch(k_la_down<UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
+  launch(k_la_down<F16, UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
          C ? C->w_down_t : nullptr, C ? C->b_out : nullptr, C ? C->h_buf : nullptr,
          C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
          C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
@@ -732,47 +733,56 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
          C ? C->sa : none);
 }
 
-template <int UPT>
+template <bool F16, int UPT>
 bool la_down_nchp(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                   uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
-  switch (Nx ? Nx->r / 8 : 32) {
-    case 8: la_down_launch<UPT, 8>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 16: la_down_launch<UPT, 16>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 32: la_down_launch<UPT, 32>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 64: la_down_launch<UPT, 64>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 128: la_down_launch<UPT, 128>(C, Nx, idx, count, tok, y, s, tev); return true;
+  switch (Nx ? Nx->r / (F16 ? 8 : 4) : 32) {
+    case 8: la_down_launch<F16, UPT, 8>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 16: la_down_launch<F16, UPT, 16>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 32: la_down_launch<F16, UPT, 32>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 64: la_down_launch<F16, UPT, 64>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 128: la_down_launch<F16, UPT, 128>(C, Nx, idx, count, tok, y, s, tev); return true;
     default: return false;
   }
 }
 
-template <int UPT, int NCHP>
+template <bool F16, int UPT, int NCHP>
 int la_down_occ() {
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_la_down<UPT, NCHP>, TPB,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_la_down<F16, UPT, NCHP>, TPB,
                                                    (size_t)LIST_CAP * 4) != hipSuccess)
     occ = 0;
   return occ;
 }
 
-template <int UPT>
+template <bool F16, int UPT>
 int la_down_occ_nchp(int nchp) {
   switch (nchp) {
-    case 8: return la_down_occ<UPT, 8>();
-    case 16: return la_down_occ<UPT, 16>();
-    case 32: return la_down_occ<UPT, 32>();
-    case 64: return la_down_occ<UPT, 64>();
-    default: return la_down_occ<UPT, 128>();
+    case 8: return la_down_occ<F16, UPT, 8>();
+    case 16: return la_down_occ<F16, UPT, 16>();
+    case 32: return la_down_occ<F16, UPT, 32>();
+    case 64: return la_down_occ<F16, UPT, 64>();
+    default: return la_down_occ<F16, UPT, 128>();
   }
 }
 
-bool la_down_any(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
+template <bool F16>
+bool la_down_upt(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                  uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   switch (C ? C->split_upt : 1) {
-    case 1: return la_down_nchp<1>(C, Nx, idx, count, tok, y, s, tev);
-    case 2: return la_down_nchp<2>(C, Nx, idx, count, tok, y, s, tev);
-    case 4: return la_down_nchp<4>(C, Nx, idx, count, tok, y, s, tev);
-    default: return la_down_nchp<8>(C, Nx, idx, count, tok, y, s, tev);
+    case 1: return la_down_nchp<F16, 1>(C, Nx, idx, count, tok, y, s, tev);
+    case 2: return la_down_nchp<F16, 2>(C, Nx, idx, count, tok, y, s, tev);
+    case 4: return la_down_nchp<F16, 4>(C, Nx, idx, count, tok, y, s, tev);
+    default: return la_down_nchp<F16, 8>(C, Nx, idx, count, tok, y, s, tev);
   }
+}
+
+// both roles share the weight type (checked by the caller)
+bool la_down_any(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
+                 uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
+  const bool f16 = C ? C->w_f16 : Nx->w_f16;
+  return f16 ? la_down_upt<true>(C, Nx, idx, count, tok, y, s, tev)
+             : la_down_upt<false>(C, Nx, idx, count, tok, y, s, tev);
 }
 
 }  // namespace
@@ -799,15 +809,17 @@ void run_down_b1(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64
     down_b1_any<false>(L, idx_out, count_out, tok_out, y, s, tev);
 }
 
-// A layer the look-ahead kernels cover: fp16 weights and predictor, rank 64 to 1024 (8 to
-// 128 chunks a predictor row, a power of two), d <= 8192 (plain layers: 12288), and the
-// single-token decode's own conditions.
+// A layer the look-ahead kernels cover: weights and predictor of one type (fp16 or fp32),
+// 8 to 128 chunks a predictor row (a power of two: rank 64 to 1024 in fp16, 32 to 512 in
+// fp32), at most 1024 chunks a row of the input (1536 for plain layers: d <= 8192 and
+// 12288 in fp16), and the single-token decode's own conditions.
 bool lookahead_layer_ok(const LayerDev& L) {
-  if (!L.w_f16 || !L.p_f16) return false;
-  const int nchp = L.r / 8;
-  if (L.r % 8 != 0 || nchp < 8 || nchp > 128 || (nchp & (nchp - 1)) != 0) return false;
-  if (la_ncpt(L.d) == 0 || L.d % 8 != 0) return false;
-  const int cpt = pick_cpt_b1(row_chunks(L)), ncpt = la_ncpt(L.d);
+  if (L.w_f16 != L.p_f16) return false;
+  const int epc = L.w_f16 ? 8 : 4;
+  const int nchp = L.r / epc;
+  if (L.r % epc != 0 || nchp < 8 || nchp > 128 || (nchp & (nchp - 1)) != 0) return false;
+  if (la_ncpt(L.d, L.w_f16) == 0 || L.d % epc != 0) return false;
+  const int cpt = pick_cpt_b1(row_chunks(L)), ncpt = la_ncpt(L.d, L.w_f16);
   const bool form = L.gated ? ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 1) ||
                                (cpt == 4 && ncpt == 2) || (cpt == 6 && ncpt == 4) ||
                                (cpt == 8 && ncpt == 4))
@@ -826,22 +838,30 @@ hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s
 hipError_t run_lookahead(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                          int32_t* idx, int32_t* count, uint64_t* tok, hipStream_t s,
                          const hipEvent_t* ev) {
-  const bool ok = C.gated ? la_gather_any<true>(C, Nx, x, y, s, ev ? ev + 2 : nullptr)
-                          : la_gather_any<false>(C, Nx, x, y, s, ev ? ev + 2 : nullptr);
+  const hipEvent_t* t1 = ev ? ev + 2 : nullptr;
+  const bool ok = C.w_f16 ? (C.gated ? la_gather_any<true, true>(C, Nx, x, y, s, t1)
+                                     : la_gather_any<true, false>(C, Nx, x, y, s, t1))
+                          : (C.gated ? la_gather_any<false, true>(C, Nx, x, y, s, t1)
+                                     : la_gather_any<false, false>(C, Nx, x, y, s, t1));
   if (!ok) return hipErrorInvalidValue;
   if (!la_down_any(&C, Nx, idx, count, tok, y, s, ev ? ev + 4 : nullptr))
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-int lookahead_down_occ(const LayerDev& L) {
-  const int nchp = L.r / 8;
+template <bool F16>
+int lookahead_down_occ_t(const LayerDev& L) {
+  const int nchp = L.r / (F16 ? 8 : 4);
   switch (L.split_upt) {
-    case 1: return la_down_occ_nchp<1>(nchp);
-    case 2: return la_down_occ_nchp<2>(nchp);
-    case 4: return la_down_occ_nchp<4>(nchp);
-    default: return la_down_occ_nchp<8>(nchp);
+    case 1: return la_down_occ_nchp<F16, 1>(nchp);
+    case 2: return la_down_occ_nchp<F16, 2>(nchp);
+    case 4: return la_down_occ_nchp<F16, 4>(nchp);
+    default: return la_down_occ_nchp<F16, 8>(nchp);
   }
+}
+
+int lookahead_down_occ(const LayerDev& L) {
+  return L.w_f16 ? lookahead_down_occ_t<true>(L) : lookahead_down_occ_t<false>(L);
 }
 
 }  // namespace sffn

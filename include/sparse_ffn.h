@@ -168,9 +168,11 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
  * threshold. y is the single-token decode's output on x_l over that list (bitwise so in
  * the deterministic mode).
  * Two launches per layer, and no wait between the launches' workgroups. x: device [1][d]
- * fp32; y: device [1][d] fp32. Both layers need fp16 weights and predictor, a rank of 8
- * times a power of two from 64 to 1024, d <= 8192 (plain layers: 12288), the same d, and
- * workspaces that do not overlap (SFFN_ERR_UNSUPPORTED / SFFN_ERR_INVALID otherwise).
+ * fp32; y: device [1][d] fp32. Both layers need weights and predictor of one type (both
+ * fp16 or both fp32, the same in both layers), a predictor row of 8 to 128 16-byte chunks
+ * (a power of two: rank 64 to 1024 in fp16, 32 to 512 in fp32), an input row of at most
+ * 1024 chunks (plain layers: 1536; d <= 8192 or 12288 in fp16), the same d, and workspaces
+ * that do not overlap (SFFN_ERR_UNSUPPORTED / SFFN_ERR_INVALID otherwise).
  * Calls on the layers involved must be ordered on one stream. The held set lives in the
  * layer's workspace: other calls on that layer may overwrite it (sparse_ffn_decode at one
  * token leaves the set of its own input); a layer never predicted holds the empty set. */

@@ -264,7 +264,8 @@ def test_lookahead_stack(name, d, n, r, B):
     ("C2", 512, 1000, 64, 3, True), ("C3", 512, 1100, 64, 3, True),
     ("C2", 1024, 3000, 128, 3, False), ("C3", 2048, 2500, 128, 3, True),
     ("C2", 4096, 16384, 256, 2, False), ("C3", 4096, 11008, 256, 2, False),
-    ("C5", 12288, 6144, 1024, 2, False), ("C5", 2048, 3000, 512, 3, True)])
+    ("C5", 12288, 6144, 1024, 2, False), ("C5", 2048, 3000, 512, 3, True),
+    ("C1", 768, 3072, 64, 3, True), ("C1", 1024, 2000, 128, 3, False)])
 def test_lookahead_fused(name, d, n, r, nl, det):
     """Fused look-ahead decode (two launches a layer): layer l >= 1 takes its active set from
     layer l - 1's input through its own predictor, layer 0 from its own input. Each mask
@@ -329,12 +330,15 @@ def test_lookahead_fused(name, d, n, r, nl, det):
 
 
 def test_lookahead_fused_rejects():
-    """The fused look-ahead entry points reject a layer paired with itself and shapes their
-    kernels do not cover (fp32 weights), before anything is enqueued."""
+    """The fused look-ahead entry points reject a layer paired with itself or with a layer
+    of another width, a pair of different weight types, and shapes their kernels do not
+    cover (an input row of 2048 fp16 chunks), before anything is enqueued."""
     from activation_sparse_decode_rank_amd import _native as N
     say("fused look-ahead argument checks")
     a, _, _ = build(cfg("C2"), 0, d=512, n=1000, rank=64)
     f32, _, _ = build(cfg("C1"), 0, d=256, n=600, rank=64)
+    f32w, _, _ = build(cfg("C1"), 0, d=512, n=600, rank=64)
+    wide, _, _ = build(cfg("C2"), 0, d=16384, n=300, rank=64)
     x = tokens(cfg("C2"), 1, 512)
     y = torch.empty((1, 512), dtype=torch.float32, device="cuda")
     idx = torch.empty(1000, dtype=torch.int32, device="cuda")
@@ -344,8 +348,10 @@ def test_lookahead_fused_rejects():
                                          idx.data_ptr(), cnt.data_ptr(), None, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_decode_lookahead(a.handle, f32.handle, x.data_ptr(), y.data_ptr(),
                                          idx.data_ptr(), cnt.data_ptr(), None, None) == N.SFFN_ERR_INVALID
-    x1 = tokens(cfg("C1"), 1, 256)
-    assert L.sparse_ffn_lookahead_begin(f32.handle, x1.data_ptr(), None) == N.SFFN_ERR_UNSUPPORTED
+    assert L.sparse_ffn_decode_lookahead(a.handle, f32w.handle, x.data_ptr(), y.data_ptr(),
+                                         idx.data_ptr(), cnt.data_ptr(), None, None) == N.SFFN_ERR_UNSUPPORTED
+    xw = tokens(cfg("C2"), 1, 16384)
+    assert L.sparse_ffn_lookahead_begin(wide.handle, xw.data_ptr(), None) == N.SFFN_ERR_UNSUPPORTED
 
 
 
