@@ -457,7 +457,8 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
 // of the next layer's stage 1 (qn[w] = P1n[w] . x, in k_pred_stage1's order for one token)
 // between issuing its first weight loads and using them; the grid is max(gm, rn), and
 // workgroups past the ranges compute their stage-1 row only. The first workgroups also
-// clear y (ny floats) for the down projection's split sums. fp16 weights and predictor.
+// clear y (ny floats) for the down projection's split sums. F16: fp16 weights and predictor
+// (else fp32).
 // Up to four chunks a gathered row, the registers are capped so that four workgroups fit a
 // compute unit: every range is then resident at once, as in the single-token middle kernel.
 template <bool F16, bool GATED, int CPT, int NCPT>
@@ -535,10 +536,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
 // 2i + 1 (of gn; bounds from its range table rsn) against qn and stores each range's
 // activity word in wbits_n. The down workgroups come first, unless sfirst: when the launch
 // does not fit the GPU at once, the scoring workgroups go first so that the next layer's
-// predictor stream starts with the down projection's instead of after it. Two ranges a workgroup keep every workgroup of the
-// launch resident at once; the second range's predictor rows are pulled into cache while
-// the first is scored (one load per 128-byte line, values discarded). fp16 weights and
-// predictor.
+// predictor stream starts with the down projection's instead of after it. Two ranges a
+// workgroup keep every workgroup of the launch resident at once where it fits; the second
+// range's predictor rows are pulled into cache while the first is scored (one load per
+// 128-byte line, values discarded). F16: fp16 weights and predictor (else fp32).
 template <bool F16, int UPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_la_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
