@@ -697,8 +697,17 @@ void la_gather_launch(const LayerDev& C, const LayerDev* Nx, const float* x, flo
          Nx ? Nx->p1 : nullptr, Nx ? Nx->r : 0, Nx ? Nx->q : nullptr, C.ra);
 }
 
-// the (gated, chunks per gathered row, chunks per stage-1 row) forms that occur for
-// d <= 8192, and plain layers up to d = 12288: both counts follow from d
+// the (gated, chunks per gathered row, chunks per stage-1 row) forms instantiated below:
+// those that occur up to 1024 input chunks (d <= 8192 in fp16), and plain layers up to 1536
+// (d = 12288); both counts follow from d
+inline bool la_form_ok(bool gated, int cpt, int ncpt) {
+  if (gated)
+    return (cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 1) || (cpt == 4 && ncpt == 2) ||
+           (cpt == 6 && ncpt == 4) || (cpt == 8 && ncpt == 4);
+  return (cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 2) || (cpt == 4 && ncpt == 4) ||
+         (cpt == 6 && ncpt == 6);
+}
+
 template <bool F16, bool GATED>
 bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float* y,
                    hipStream_t s, const hipEvent_t* tev) {
@@ -821,12 +830,7 @@ bool lookahead_layer_ok(const LayerDev& L) {
   if (L.r % epc != 0 || nchp < 8 || nchp > 128 || (nchp & (nchp - 1)) != 0) return false;
   if (la_ncpt(L.d, L.w_f16) == 0 || L.d % epc != 0) return false;
   const int cpt = pick_cpt_b1(row_chunks(L)), ncpt = la_ncpt(L.d, L.w_f16);
-  const bool form = L.gated ? ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 1) ||
-                               (cpt == 4 && ncpt == 2) || (cpt == 6 && ncpt == 4) ||
-                               (cpt == 8 && ncpt == 4))
-                            : ((cpt == 1 && ncpt == 1) || (cpt == 2 && ncpt == 2) ||
-                               (cpt == 4 && ncpt == 4) || (cpt == 6 && ncpt == 6));
-  return form && occ_mid_b1(L) > 0;
+  return la_form_ok(L.gated, cpt, ncpt) && occ_mid_b1(L) > 0;
 }
 
 hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s) {

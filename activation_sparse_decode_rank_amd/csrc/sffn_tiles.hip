@@ -1193,7 +1193,7 @@ void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t*
                     const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
                     const hipEvent_t* tev, bool fw) {
   const int nt = (B + 15) / 16;
-  if (const int form = up_sk_form(L, B, fw)) {
+  if (up_sk_form(L, B, fw) != 0) {
     int32_t* idx_w = const_cast<int32_t*>(idx);
     int32_t* cnt_w = const_cast<int32_t*>(count);
     uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
