@@ -532,14 +532,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
 }
 
 // ndown workgroups run this layer's down projection (as k_down_b1, which also publishes the
-// list, count and token bits); scoring workgroup i scores the next layer's ranges 2i and
-// 2i + 1 (of gn; bounds from its range table rsn) against qn and stores each range's
+// list, count and token bits); scoring workgroup i scores the next layer's ranges LA_RPW i
+// onwards (of gn; bounds from its range table rsn) against qn and stores each range's
 // activity word in wbits_n. The down workgroups come first, unless sfirst: when the launch
 // does not fit the GPU at once, the scoring workgroups go first so that the next layer's
 // predictor stream starts with the down projection's instead of after it. Two ranges a
 // workgroup keep every workgroup of the launch resident at once where it fits; the second
 // range's predictor rows are pulled into cache while the first is scored (one load per
 // 128-byte line, values discarded). F16: fp16 weights and predictor (else fp32).
+// next-layer ranges scored per workgroup: two halve the scoring workgroups at the cost of
+// one more serial score pass; three or four make that serial tail the longer role
+constexpr int LA_RPW = 2;
 template <bool F16, int UPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_la_down(
     const void* __restrict__ w_down_t, const float* __restrict__ b_out,
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
     uint64_t* __restrict__ wbits_n, int sfirst, const SplitArg sa) {
   __shared__ uint8_t s_act[MID_RANGE_MAX];
   touch_kernargs<2>();
-  const int nsc = (gn + 1) / 2, bid = blockIdx.x;
+  const int nsc = (gn + LA_RPW - 1) / LA_RPW, bid = blockIdx.x;
   if (sfirst ? bid >= nsc : bid < ndown) {
     down_b1_body<F16, UPT>(sfirst ? bid - nsc : bid, w_down_t, b_out, h_in, d, n, wbits, rs,
                             KS, ncb, idx_out, count_out, tokmask_out, y, sa);
@@ -559,28 +562,37 @@ __global__ __launch_bounds__(TPB) void k_la_down(
   }
   constexpr int ROW_BYTES = NCHP * 16;
   constexpr int PF_ITERS = (MID_RANGE_MAX * ROW_BYTES + TPB * 128 - 1) / (TPB * 128);
-  const int w0 = 2 * (sfirst ? bid : bid - ndown), tid = threadIdx.x;
-  const bool two = w0 + 1 < gn;  // uniform
-  const int ra0 = rsn[w0], n0 = rsn[w0 + 1] - ra0;
-  const int ra1 = two ? rsn[w0 + 1] : 0, n1 = two ? rsn[w0 + 2] - ra1 : 0;
-  uint32_t sink = 0;
-  mid_scores_b1<F16, NCHP>(p2n, pbn, qn, ra0, n0, taun, nullptr, s_act, [&]() {
-    if (!two) return;
-    const char* base = static_cast<const char*>(p2n) + (size_t)ra1 * ROW_BYTES;
-    const int bytes = n1 * ROW_BYTES;
+  const int w0 = LA_RPW * (sfirst ? bid : bid - ndown), tid = threadIdx.x;
+  const int nr = min(LA_RPW, gn - w0);  // uniform, >= 1
+  int rb[LA_RPW + 1];
 #pragma unroll
-    for (int v = 0; v < PF_ITERS; ++v) {
-      const int off = min((tid + v * TPB) * 128, bytes - 4);
-      sink ^= *reinterpret_cast<const uint32_t*>(base + off);
+  for (int k = 0; k <= LA_RPW; ++k) rb[k] = rsn[w0 + min(k, nr)];
+  uint32_t sink = 0;
+  mid_scores_b1<F16, NCHP>(p2n, pbn, qn, rb[0], rb[1] - rb[0], taun, nullptr, s_act, [&]() {
+#pragma unroll
+    for (int k = 1; k < LA_RPW; ++k) {
+      if (k >= nr) break;
+      const char* base = static_cast<const char*>(p2n) + (size_t)rb[k] * ROW_BYTES;
+      const int bytes = (rb[k + 1] - rb[k]) * ROW_BYTES;
+#pragma unroll
+      for (int v = 0; v < PF_ITERS; ++v) {
+        const int off = min((tid + v * TPB) * 128, bytes - 4);
+        sink ^= *reinterpret_cast<const uint32_t*>(base + off);
+      }
+      if (tid < rb[k + 1] - rb[k] && pbn) sink ^= __float_as_uint(pbn[rb[k] + tid]);
     }
-    if (tid < n1 && pbn) sink ^= __float_as_uint(pbn[ra1 + tid]);
   });
-  const uint64_t word0 = __ballot(tid < n0 && s_act[tid]);
-  if (tid == 0) wbits_n[w0] = word0;
-  if (two) {
-    mid_scores_b1<F16, NCHP>(p2n, pbn, qn, ra1, n1, taun, nullptr, s_act, []() {});
-    const uint64_t word1 = __ballot(tid < n1 && s_act[tid]);
-    if (tid == 0) wbits_n[w0 + 1] = word1;
+  {
+    const uint64_t word = __ballot(tid < rb[1] - rb[0] && s_act[tid]);
+    if (tid == 0) wbits_n[w0] = word;
+  }
+#pragma unroll
+  for (int k = 1; k < LA_RPW; ++k) {
+    if (k >= nr) break;
+    const int nk = rb[k + 1] - rb[k];
+    mid_scores_b1<F16, NCHP>(p2n, pbn, qn, rb[k], nk, taun, nullptr, s_act, []() {});
+    const uint64_t word = __ballot(tid < nk && s_act[tid]);
+    if (tid == 0) wbits_n[w0 + k] = word;
   }
   asm volatile("" ::"v"(sink));
 }
@@ -731,7 +743,7 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
                     uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   const int ncb = C ? down_blocks(*C) : 1;
   const int ndown = C ? ncb * C->ks_down : 0;
-  const int nscore = Nx ? (Nx->g_mid + 1) / 2 : 0;
+  const int nscore = Nx ? (Nx->g_mid + LA_RPW - 1) / LA_RPW : 0;
   SplitArg none{};
   const int sfirst = C && nscore > 0 && ndown + nscore > C->la_occ * C->n_cus ? 1 : 0;
   launch(k_la_down<F16, UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
