@@ -424,6 +424,28 @@ def test_graph_replay_lookahead():
         torch.cuda.synchronize()
 
 
+
+def test_lookahead_never_predicted_is_empty():
+    """A layer that no look-ahead call has predicted holds the empty set (its range words are
+    cleared at create): decode_ahead then lists nothing and writes y = b_out, twice in a row,
+    while predicting the next layer, whose set then matches the decode step's."""
+    c = cfg("C2")
+    say("look-ahead on a never-predicted layer")
+    (a, La, _), (b, Lb, _) = [build(c, l, d=512, n=1000, rank=64, deterministic=True)
+                              for l in range(2)]
+    x = tokens(c, 1, 512, tag=340)
+    for _ in range(2):
+        y, idx, cnt, _ = a.decode_ahead(x, b)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == 0
+        assert np.array_equal(to_np(y)[0], La["b_o"].astype(np.float32))
+    y2, i2, c2, _ = b.decode_ahead(x, None)
+    _, i3, c3, _ = b.decode(x)
+    torch.cuda.synchronize()
+    k = int(c3.item())
+    assert int(c2.item()) == k and np.array_equal(to_np(i2)[:k], to_np(i3)[:k])
+
+
 def test_decode_deterministic():
     """deterministic=1: repeated decodes give bitwise-identical y and lists, and match the
     oracle (the down projection splits rows at most two ways)."""
