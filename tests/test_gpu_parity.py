@@ -265,7 +265,9 @@ def test_lookahead_stack(name, d, n, r, B):
     ("C2", 1024, 3000, 128, 3, False), ("C3", 2048, 2500, 128, 3, True),
     ("C2", 4096, 16384, 256, 2, False), ("C3", 4096, 11008, 256, 2, False),
     ("C5", 12288, 6144, 1024, 2, False), ("C5", 2048, 3000, 512, 3, True),
-    ("C1", 768, 3072, 64, 3, True), ("C1", 1024, 2000, 128, 3, False)])
+    ("C1", 768, 3072, 64, 3, True), ("C1", 1024, 2000, 128, 3, False),
+    ("C3", 6144, 1500, 128, 2, True), ("C3", 8192, 1200, 128, 2, False),
+    ("C2", 8192, 2000, 128, 2, False)])
 def test_lookahead_fused(name, d, n, r, nl, det):
     """Fused look-ahead decode (two launches a layer): layer l >= 1 takes its active set from
     layer l - 1's input through its own predictor, layer 0 from its own input. Each mask
