@@ -9,7 +9,8 @@ from ._native import (  # noqa: F401
     SFFN_MAX_BATCH, SFFN_OK, SffnDesc, SparseFFNError, sparse_ffn_compact, sparse_ffn_create,
     sparse_ffn_decode, sparse_ffn_decode_lookahead, sparse_ffn_destroy, sparse_ffn_forward,
     sparse_ffn_lookahead_begin, sparse_ffn_pack_rows,
-    sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts, sparse_ffn_set_timing_events,
+    sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts, sparse_ffn_read_probe,
+    sparse_ffn_set_timing_events,
     sparse_ffn_status_string, sparse_ffn_workspace_bytes,
 )
 from .layer import (  # noqa: F401

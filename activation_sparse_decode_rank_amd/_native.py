@@ -56,6 +56,7 @@ def _load():
         "sparse_ffn_profile_counts": (C.c_int, [P, I32, I32, P, I32, I32, P, I32, P, P]),
         "sparse_ffn_permutation": (C.c_int, [P, I32, I32, P]),
         "sparse_ffn_pack_rows": (C.c_int, [P, P, P, I32, I64, I64, P]),
+        "sparse_ffn_read_probe": (C.c_int, [P, SZ, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -69,7 +70,8 @@ EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destr
             "sparse_ffn_predict", "sparse_ffn_compact", "sparse_ffn_forward", "sparse_ffn_decode",
             "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
-            "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows")
+            "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
+            "sparse_ffn_read_probe")
 
 
 def lib():
@@ -142,3 +144,7 @@ def sparse_ffn_permutation(counts_host, d_ffn, n_hot, perm_host) -> None:
 def sparse_ffn_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes, stream) -> None:
     _ck(_lib.sparse_ffn_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes, stream),
         "sparse_ffn_pack_rows")
+
+
+def sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream) -> None:
+    _ck(_lib.sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream), "sparse_ffn_read_probe")

@@ -229,7 +229,10 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
         rs.swap(rs2);
     }
     L.g_mid = rs.empty() ? 0 : (int)rs.size() - 1;
-    if (L.g_mid > 0) {
+    // the workspace holds a range table and activity words for at most G_MID_MAX ranges
+    // (d_ffn up to 131072 at 64 neurons a range); a wider layer keeps g_mid out of range,
+    // so the decode entry points return SFFN_ERR_UNSUPPORTED and nothing reads the table
+    if (L.g_mid > 0 && L.g_mid <= sffn::G_MID_MAX) {
       if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
           hipSuccess)
         return SFFN_ERR_HIP;
@@ -408,6 +411,24 @@ int sparse_ffn_pack_rows(const void* src, const int32_t* perm, void* dst, int32_
     return SFFN_ERR_INVALID;
   return sffn::launch_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes,
                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                          void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || workgroups < 0) return SFFN_ERR_INVALID;
+  if (!aligned16(buf)) return SFFN_ERR_INVALID;
+  int g = workgroups;
+  if (g == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return SFFN_ERR_HIP;
+    g = 8 * std::max(cus, 1);
+  }
+  return sffn::launch_read_probe(buf, bytes, g, sink, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;
 }

@@ -106,7 +106,7 @@ hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* score
 hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_t* idx,
                           const int32_t* count, const uint64_t* tokmask, float* y, hipStream_t s) {
   if (tile_ok(L, B)) {
-    run_forward_tiles(L, x, B, idx, count, tokmask, y, true, false, s, nullptr, nullptr);
+    run_forward_tiles(L, x, B, idx, count, tokmask, nullptr, y, true, false, s, nullptr, nullptr);
     return hipGetLastError();
   }
   run_gather(L, x, B, idx, count, tokmask, y, s);
@@ -141,7 +141,10 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
       e = launch_compact(L, sc, B, idx, count, tokmask, s);
     }
     if (e != hipSuccess) return e;
-    run_forward_tiles(L, x, B, idx, count, tokmask, y, false, fw, s, t2, t3);
+    // a caller that wants no token bits still gets per-token activations: the up kernel
+    // then takes each listed neuron's bits from the compaction's by-neuron words
+    run_forward_tiles(L, x, B, idx, count, tokmask, tokmask ? nullptr : L.tok_full, y, false,
+                      fw, s, t2, t3);
     return hipGetLastError();
   }
   run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true, false);

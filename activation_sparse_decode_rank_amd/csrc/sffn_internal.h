@@ -148,12 +148,14 @@ hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint6
                           hipStream_t s);
 // from_words: the up kernel lists the union itself from the words and token bits of
 // run_score_tiles (writing idx, count and tokmask; needs union_in_up_ok) instead of
-// reading them
+// reading them. Otherwise it reads idx and count, and each listed neuron's token bits from
+// tokmask (by list position) or, when tokmask is null, from tok_by_neuron (by neuron, as
+// the compaction leaves them in tok_full); both null: every token uses every listed neuron.
 bool union_in_up_ok(const LayerDev& L);
 void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                       const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                       bool from_words, hipStream_t s, const hipEvent_t* t_up,
-                       const hipEvent_t* t_down);
+                       const int32_t* count, const uint64_t* tokmask,
+                       const uint64_t* tok_by_neuron, float* y, bool zero_y, bool from_words,
+                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down);
 
 // launchers; each returns hipGetLastError() after enqueueing
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s);
@@ -170,5 +172,9 @@ hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const 
                                  hipStream_t s);
 hipError_t launch_pack_rows(const void* src, const int32_t* perm, void* dst, int rows,
                             int64_t row_bytes, int64_t dst_stride_bytes, hipStream_t s);
+// sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
+// number of workgroups; sink [workgroups] is written only in a practically impossible case
+hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                             hipStream_t s);
 
 }  // namespace sffn

@@ -492,7 +492,11 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
         } else {
           const int pc = min(u * RT + 16 * et + 4 * g + j, cnt - 1);
           ej[j] = idx[pc];
-          em[j] = tokmask ? tokmask[pc] : ~(uint64_t)0;
+          // token bits by list position; else by neuron from the compaction (decode with no
+          // caller mask); else every token uses every listed neuron (standalone forward)
+          em[j] = tokmask ? tokmask[pc]
+                          : tok_full ? tok_full[(ej[j] >= 0 && ej[j] < n) ? ej[j] : 0]
+                                     : ~(uint64_t)0;
         }
         eb[j] = (b_act && ej[j] >= 0 && ej[j] < n) ? b_act[ej[j]] : 0.f;
       }
@@ -1139,8 +1143,8 @@ hipError_t scores_launch(const LayerDev& L, int B, float* scores, hipStream_t s)
 // left in the workspace, writing idx, count and tokmask; otherwise it reads them
 template <bool GATED, int NT, int TR, int W>
 void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
-                      const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
-                      const hipEvent_t* tev, bool fw) {
+                      const uint64_t* tokmask, const uint64_t* tok_by_neuron, float* y0, int ny,
+                      hipStream_t s, const hipEvent_t* tev, bool fw) {
   int32_t* idx_w = const_cast<int32_t*>(idx);
   int32_t* cnt_w = const_cast<int32_t*>(count);
   uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
@@ -1151,7 +1155,7 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
   else
     launch(k_up_mfma<GATED, NT, TR, W, false>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act,
            L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
-           (const uint64_t*)nullptr, (const uint64_t*)nullptr, L.h_buf, L.ldh, y0, ny);
+           (const uint64_t*)nullptr, tok_by_neuron, L.h_buf, L.ldh, y0, ny);
 }
 
 // At 16 tokens (one token tile) each workgroup takes two row tiles with eight waves
@@ -1190,8 +1194,8 @@ int up_sk_form(const LayerDev& L, int B, bool fw) {
 
 template <bool GATED>
 void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
-                    const uint64_t* tokmask, float* y0, int ny, hipStream_t s,
-                    const hipEvent_t* tev, bool fw) {
+                    const uint64_t* tokmask, const uint64_t* tok_by_neuron, float* y0, int ny,
+                    hipStream_t s, const hipEvent_t* tev, bool fw) {
   const int nt = (B + 15) / 16;
   if (up_sk_form(L, B, fw) != 0) {
     int32_t* idx_w = const_cast<int32_t*>(idx);
@@ -1201,14 +1205,14 @@ void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t*
     return;
   }
   if (B >= 16 && nt == 1 && L.d % 512 == 0) {
-    up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, y0, ny, s, tev, fw);
+    up_tile_launch_t<GATED, 1, 2, 8>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw);
     return;
   }
   switch (nt) {
-    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
-    case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
-    case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
-    default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, y0, ny, s, tev, fw); break;
+    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
+    case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
+    case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
+    default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
   }
 }
 
@@ -1227,8 +1231,9 @@ void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_
 // projection splits rows. Standalone (zero_y) the tokens are split here; in the decode
 // step stage 1 has split them.
 void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                   const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                   bool fw, hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
+                   const int32_t* count, const uint64_t* tokmask, const uint64_t* tok_by_neuron,
+                   float* y, bool zero_y, bool fw, hipStream_t s, const hipEvent_t* t_up,
+                   const hipEvent_t* t_down) {
   const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
   if (zero_y) {
     const int items = L.d / 8 * B;
@@ -1236,9 +1241,9 @@ void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                        static_cast<u32x4*>(L.x_hl));
   }
   if (L.gated)
-    up_tile_launch<true>(L, B, idx, count, tokmask, y, ny, s, t_up, fw);
+    up_tile_launch<true>(L, B, idx, count, tokmask, tok_by_neuron, y, ny, s, t_up, fw);
   else
-    up_tile_launch<false>(L, B, idx, count, tokmask, y, ny, s, t_up, fw);
+    up_tile_launch<false>(L, B, idx, count, tokmask, tok_by_neuron, y, ny, s, t_up, fw);
   down_tile_launch(L, B, idx, count, y, s, t_down);
 }
 
@@ -1295,10 +1300,11 @@ hipError_t launch_scatter(const LayerDev& L, int32_t* idx, int32_t* count, uint6
 bool union_in_up_ok(const LayerDev& L) { return (L.n + 63) / 64 <= FW_WORDS_MAX; }
 
 void run_forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
-                       const int32_t* count, const uint64_t* tokmask, float* y, bool zero_y,
-                       bool from_words, hipStream_t s, const hipEvent_t* t_up,
-                       const hipEvent_t* t_down) {
-  forward_tiles(L, x, B, idx, count, tokmask, y, zero_y, from_words, s, t_up, t_down);
+                       const int32_t* count, const uint64_t* tokmask,
+                       const uint64_t* tok_by_neuron, float* y, bool zero_y, bool from_words,
+                       hipStream_t s, const hipEvent_t* t_up, const hipEvent_t* t_down) {
+  forward_tiles(L, x, B, idx, count, tokmask, tok_by_neuron, y, zero_y, from_words, s, t_up,
+                t_down);
 }
 
 }  // namespace sffn

@@ -122,27 +122,47 @@ class SparseFFN:
         self.b_out = b_out
         torch.cuda.current_stream(dev).synchronize() if stream is None else stream.synchronize()
 
+        self._w_dtype, self._p_dtype = _DT[w_act.dtype], _DT[p1.dtype]
+        self._freq = freq  # host frequencies: read by every create over these weights
+        self.perm_dev = perm_dev
+        self._create(self.threshold, bool(deterministic), self.max_batch)
+
+    def _create(self, threshold: float, deterministic: bool, max_batch: int) -> None:
+        """A library handle over this object's packed weights, with its own workspace."""
+        self.threshold = float(threshold)
+        self.deterministic = bool(deterministic)
+        self.max_batch = int(max_batch)
         self.desc = N.SffnDesc()
         D = self.desc
-        D.d, D.d_ffn, D.rank, D.max_batch = d, n, r, self.max_batch
+        D.d, D.d_ffn, D.rank, D.max_batch = self.d, self.n, self.r, self.max_batch
         D.gated = int(self.gated)
-        D.w_dtype, D.p_dtype = _DT[w_act.dtype], _DT[p1.dtype]
+        D.w_dtype, D.p_dtype = self._w_dtype, self._p_dtype
         D.threshold = self.threshold
-        D.deterministic = int(bool(deterministic))
-        self.deterministic = bool(deterministic)
+        D.deterministic = int(self.deterministic)
         D.w_act, D.w_down_t = _ptr(self.w_act), _ptr(self.w_down_t)
         D.b_act, D.b_out = _ptr(self.b_act), _ptr(self.b_out)
         D.p1, D.p2, D.p_bias = _ptr(self.p1), _ptr(self.p2), _ptr(self.p_bias)
         ws = N.sparse_ffn_workspace_bytes(D)
         if ws == 0:
             raise N.SparseFFNError(N.SFFN_ERR_INVALID, "sparse_ffn_workspace_bytes")
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.w_act.device)
         D.workspace, D.workspace_bytes = self.workspace.data_ptr(), ws
-        self._freq = freq  # keep the host array alive across create
-        D.neuron_freq = None if freq is None else freq.ctypes.data
+        D.neuron_freq = None if self._freq is None else self._freq.ctypes.data
         self.handle = N.sparse_ffn_create(D)
         D.neuron_freq = None
-        self.perm_dev = perm_dev
+
+    def clone(self, *, threshold: Optional[float] = None, deterministic: Optional[bool] = None,
+              max_batch: Optional[int] = None) -> "SparseFFN":
+        """Another handle over the same packed weights (no copy), with its own workspace and
+        the given threshold, mode or batch limit (default: this layer's). For example
+        threshold=-inf lists every neuron: the library's own dense FFN."""
+        c = object.__new__(SparseFFN)
+        c.__dict__.update({k: v for k, v in self.__dict__.items()
+                           if k not in ("handle", "desc", "workspace")})
+        c._create(self.threshold if threshold is None else threshold,
+                  self.deterministic if deterministic is None else deterministic,
+                  self.max_batch if max_batch is None else max_batch)
+        return c
 
     # ---------------------------------------------------------------- calls
     def _check_x(self, x):

@@ -1,32 +1,40 @@
 #!/usr/bin/env python3
 """Benchmark: sparse FFN decode µs/layer and active-weight HBM GB/s on one MI355X.
 
-Workload (default): the OPT-6.7B-shaped ReLU FFN stack, 32 layers, d=4096, d_ffn=16384,
-fp16 weights, predictor rank 256, batch 1, per-layer activity 5% -> 10% (Zipf 1.1), hot
-20% of neurons packed first. `--config` selects another workload shape (C1 OPT-125m layer,
-C3 Llama-7B-shaped gated stack, C4 its batch sweep with `--batch`, C5 OPT-175B-shaped
-slice); every weight, token and profile token is seeded synthetic data (no model
-checkpoint, no dataset).
+Workload (default): the OPT-6.7B-shaped ReLU FFN stack with every layer at 10% target
+activity (the metric's condition), 32 layers, d=4096, d_ffn=16384, fp16 weights,
+predictor rank 256, batch 1, Zipf(1.1) neuron frequencies, hot 20% of neurons packed
+first. `--config` selects another workload (C1 OPT-125m layer, C2 the same stack on its
+5% -> 10% activity ramp, C3 Llama-7B-shaped gated stack, C4 its batch sweep with
+`--batch`, C5 OPT-175B-shaped slice); every weight, token and profile token is seeded
+synthetic data (no model checkpoint, no dataset).
 
 A step is one decode token (or one batch of `--batch` tokens) through every layer of the
 stack: for each layer, the predictor (both stages), threshold, compaction, gather-GEMV +
 ReLU and down projection, all through the library's single-call decode entry point. Each
 (token, layer) reads its own pre-drawn x, so the calibrated activity holds; y is not
-chained into the next layer. Steps are replayed from HIP graphs (one per group of steps)
-with inputs resident in HBM; the timed region is bracketed by device synchronizations.
+chained into the next layer. Steps are replayed from HIP graphs with inputs resident in
+HBM; exactly --steps steps are timed, bracketed by device synchronizations.
 
 Also measured, beside the headline number:
-  - per-kernel durations from HIP events that each kernel dispatch stamps itself
-    (start and end of execution, on the library's stream), with each kernel's algorithmic
-    bytes (and, for the matrix-core kernels, flops) per launch;
-  - at one token, the look-ahead decode (`lookahead`): each layer's active set predicted
-    from the previous layer's input and that prediction fused into the previous layer's
-    two launches; a different mask than the headline's (each layer's own input), so it is
-    reported beside it, graph-replayed and timed the same way, with each launch's own
-    event-stamped duration;
-  - the dense FFN of the same shapes on the same (unpacked) fp16 weights, through torch
-    (hipBLASLt), graph-captured and timed the same way;
-  - the fp64 CPU oracle on a bounded sample of the same workload, on the host cores.
+  - the per-layer time of each graph replay in the timed region (p10 / p50 / p90);
+  - per-kernel durations from HIP events that each kernel dispatch stamps itself (start and
+    end of execution, on the library's stream), with each kernel's algorithmic bytes (and,
+    for the matrix-core kernels, flops) per launch;
+  - a plain read stream over 4 GiB (the library's read probe): the achievable read
+    bandwidth, reported beside the nominal 8 TB/s peak;
+  - the dense FFN two ways: the library itself with every neuron listed (threshold -inf),
+    and torch's F.linear chain (hipBLASLt) on the same unpacked fp16 weights, both
+    graph-captured and timed the same way, plus the dense bytes at the achievable read rate;
+  - the deterministic mode (y bitwise reproducible) timed the same way;
+  - at one token, the look-ahead decode (each layer's set predicted from the previous
+    layer's input, fused into the previous layer's two launches), reported beside the
+    metric since its masks differ;
+  - the predictor's recall and precision against the true ReLU signs (a diagnostic of the
+    synthetic calibrated predictor, not graded);
+  - for the default workload, the same stack on its 5% -> 10% ramp (`c2_ramp`);
+  - the fp64 CPU oracle on a bounded sample of the same workload, single-threaded and with
+    OpenMP on the host's cores, with the host's core count and CPU model.
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -50,6 +58,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of the part
 TILE_MIN_B = 2                 # from this batch on the decode step runs the matrix-core kernels
 METRIC = "sparse FFN decode µs/layer + active-weight HBM GB/s vs peak, 10% activity"
+PROBE_BYTES = 4 << 30
 
 
 def log(*a):
@@ -65,12 +74,17 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(count):
             e = ctypes.c_void_p()
             if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.ev.append(e.value)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -154,12 +168,148 @@ def kernel_cost(cfg, B, n_union):
     return {"stage1": (stage1, 0.0), "up_tiles": (up, up_fl), "down_tiles": (down, down_fl)}
 
 
+def host_cpu():
+    """(nproc, usable cores, CPU model) of this host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or 1, usable, model
+
+
+class Timer:
+    """Graph-replayed timing of `step_fn(t)` over exactly `steps` steps after `warmup`: graphs
+    of G steps (the last one shorter when the count is not a multiple of G), an event
+    before and after every replay (per-replay times for percentiles)."""
+
+    def __init__(self, torch, T, G, steps, warmup, cap, use_graphs):
+        self.torch, self.T, self.G = torch, T, G
+        self.steps, self.warmup, self.cap, self.use_graphs = steps, warmup, cap, use_graphs
+
+    def _plan(self, n):
+        full, rem = divmod(n, self.G)
+        return [self.G] * full + ([rem] if rem else [])
+
+    def run(self, step_fn):
+        torch = self.torch
+        G, T = self.G, self.T
+        groups = {}
+        if self.use_graphs:
+            for gi in range(T // G):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.cap):
+                    for t in range(gi * G, (gi + 1) * G):
+                        step_fn(t, self.cap)
+                groups.setdefault(G, []).append(g)
+            for rem in {len_ for len_ in self._plan(self.steps) + self._plan(self.warmup)
+                        if len_ != G}:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.cap):
+                    for t in range(rem):
+                        step_fn(t, self.cap)
+                groups[rem] = [g]
+            torch.cuda.synchronize()
+        cursor = {"i": 0}
+
+        def replay(len_):
+            if self.use_graphs:
+                lst = groups[len_]
+                lst[cursor["i"] % len(lst)].replay()
+                cursor["i"] += 1
+            else:
+                for _ in range(len_):
+                    step_fn(cursor["i"] % T, None)
+                    cursor["i"] += 1
+
+        for len_ in self._plan(self.warmup):
+            replay(len_)
+        torch.cuda.synchronize()
+        plan = self._plan(self.steps)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i, len_ in enumerate(plan):
+            replay(len_)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        total = evs[0].elapsed_time(evs[-1])
+        per = [evs[i].elapsed_time(evs[i + 1]) / len_ for i, len_ in enumerate(plan)]
+        del groups
+        return total / self.steps, per
+
+
+def percentiles_us(per_step_ms, L):
+    v = np.asarray(per_step_ms) * 1000.0 / L
+    return {"p10": round(float(np.percentile(v, 10)), 3), "p50": round(float(np.percentile(v, 50)), 3),
+            "p90": round(float(np.percentile(v, 90)), 3), "replays": int(len(v))}
+
+
+def read_probe(torch, NAT, reps=10):
+    """Achievable read bandwidth (GB/s): the best of `reps` timed read streams over 4 GiB."""
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(8 * 1024, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    NAT.sparse_ffn_read_probe(buf.data_ptr(), PROBE_BYTES, 0, sink.data_ptr(), s.cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev[2 * i].record()
+        NAT.sparse_ffn_read_probe(buf.data_ptr(), PROBE_BYTES, 0, sink.data_ptr(), s.cuda_stream)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]
+    del buf, sink
+    rates = [PROBE_BYTES / (m * 1e-3) / 1e9 for m in ms]
+    return {"gbps": round(max(rates), 1), "median_gbps": round(float(np.median(rates)), 1),
+            "bytes": PROBE_BYTES, "reps": reps,
+            "impl": "sparse_ffn_read_probe: 16-byte non-temporal loads, 8 in flight per thread, "
+                    "8 workgroups per compute unit"}
+
+
+def build_stack(cfg, B, L, args, keep_originals):
+    import torch
+
+    from activation_sparse_decode_rank_amd import SparseFFN
+    from synth import make_layer, make_tokens
+    Xprof = make_tokens(cfg, args.profile_tokens, 100, "cuda")
+    layers, originals = [], []
+    for l in range(L):
+        src_layer = 0 if cfg.rotate_copies > 1 else l
+        Lt = make_layer(cfg, src_layer, "cuda")
+        s = SparseFFN(w_act=Lt.w_a, w_up=Lt.w_u, w_down_t=Lt.w_o, p1=Lt.p1, p2=Lt.p2,
+                      b_act=Lt.b_a, b_out=Lt.b_o, p_bias=Lt.c, max_batch=B, profile_x=Xprof,
+                      hot_frac=cfg.hot_frac)
+        layers.append(s)
+        originals.append(Lt if keep_originals(l) else None)
+        del Lt
+        if l % 8 == 0 or l == L - 1:
+            log(f"{cfg.name}: layer {l + 1}/{L} generated, profiled and packed")
+    del Xprof
+    torch.cuda.synchronize()
+    return layers, originals
+
+
+def decode_pass(torch, layers, X, t, y_buf, idx_buf, tok_buf, counts, stream=None):
+    for l, s in enumerate(layers):
+        s.decode(X[t, l], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
+                 tokmask=tok_buf[l], stream=stream)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256, help="timed decode steps (each = all layers)")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--config", default="C2")
+    ap.add_argument("--config", default="C2_10")
     ap.add_argument("--batch", type=int, default=1, help="tokens decoded together per step")
     ap.add_argument("--tokens", type=int, default=256, help="distinct pre-drawn steps")
     ap.add_argument("--group", type=int, default=8, help="steps per captured graph")
@@ -167,11 +317,14 @@ def main():
     ap.add_argument("--kernel-tokens", type=int, default=32, help="steps in the per-kernel event pass")
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers")
     ap.add_argument("--activity", type=float, default=0.0,
-                    help="override every layer's target activity (e.g. 0.10 for the OPT-6.7B "
-                         "stack at a flat 10%%)")
+                    help="override every layer's target activity")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-probe", action="store_true", help="skip the 4 GiB read-stream probe")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the all-active, deterministic, recall and ramp legs")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU work per oracle leg (single-threaded, then OpenMP)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every decode eagerly instead of replaying captured graphs "
                          "(for per-dispatch counter collection; the timing is then not the metric)")
@@ -190,14 +343,16 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
 
     import torch
     import torch.nn.functional as F
 
-    from activation_sparse_decode_rank_amd import (LookaheadBuffers, SparseFFN, decode_lookahead,
+    from activation_sparse_decode_rank_amd import (LookaheadBuffers, decode_lookahead,
                                                    decode_lookahead_fused)
     from activation_sparse_decode_rank_amd import _native as NAT
-    from synth import get_config, make_layer, make_tokens
+    from synth import get_config, make_tokens
 
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
@@ -213,8 +368,7 @@ def main():
     d, n, r = cfg.d, cfg.n, cfg.rank
     G = max(1, args.group)
     T = max(G, (args.tokens // G) * G)
-    steps = max(G, ((args.steps + G - 1) // G) * G)
-    warmup = ((args.warmup + G - 1) // G) * G
+    steps, warmup = int(args.steps), int(args.warmup)
     names, knames = kernel_names(cfg, B)
     t_setup = time.time()
     if args.copy_mib > 0:
@@ -227,22 +381,15 @@ def main():
         log(f"copy calibration: 4 x {args.copy_mib} MiB read + {args.copy_mib} MiB written")
         del src, dst
 
+    probe = None
+    if not args.no_probe:
+        probe = read_probe(torch, NAT)
+        log(f"read probe: {probe['gbps']} GB/s best, {probe['median_gbps']} median over 4 GiB")
+
     # ------------------------------------------------------------------ offline: layers
-    Xprof = make_tokens(cfg, args.profile_tokens, 100, "cuda")
-    layers, originals = [], []
-    for l in range(L):
-        src_layer = 0 if cfg.rotate_copies > 1 else l
-        Lt = make_layer(cfg, src_layer, "cuda")
-        s = SparseFFN(w_act=Lt.w_a, w_up=Lt.w_u, w_down_t=Lt.w_o, p1=Lt.p1, p2=Lt.p2,
-                      b_act=Lt.b_a, b_out=Lt.b_o, p_bias=Lt.c, max_batch=B, profile_x=Xprof,
-                      hot_frac=cfg.hot_frac)
-        layers.append(s)
-        keep = not args.no_dense or (not args.no_cpu and l < 2)
-        originals.append(Lt if keep else None)
-        del Lt
-        if l % 8 == 0 or l == L - 1:
-            log(f"layer {l + 1}/{L} generated, profiled and packed")
-    del Xprof
+    layers, originals = build_stack(cfg, B, L, args,
+                                    lambda l: not args.no_dense or not args.no_extra
+                                    or (not args.no_cpu and l < 2))
     X = make_tokens(cfg, T * L * B, 200, "cuda").view(T, L, B, d).contiguous()
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s; {T} steps x {L} layers x {B} token(s)")
@@ -254,14 +401,9 @@ def main():
     counts = torch.zeros((T, L), dtype=torch.int32, device="cuda")
     per_tok = np.zeros((T, L), np.int64)  # sum over tokens of each token's own actives
 
-    def decode_step(t):
-        for l in range(L):
-            layers[l].decode(X[t, l], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
-                             tokmask=tok_buf[l])
-
     # one eager pass over every step: union sizes and, for batches, each token's actives
     for t in range(T):
-        decode_step(t)
+        decode_pass(torch, layers, X, t, y_buf, idx_buf, tok_buf, counts)
         if B > 1:
             torch.cuda.synchronize()
             for l in range(L):
@@ -271,43 +413,25 @@ def main():
                                         for b in range(B)))
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
-    graphs = []
-    if not args.no_graph:
-        for gi in range(T // G):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for t in range(gi * G, (gi + 1) * G):
-                    decode_step(t)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        log(f"captured {len(graphs)} graphs of {G * L} layer steps")
+    timer = Timer(torch, T, G, steps, warmup, cap, not args.no_graph)
 
-    def replay(graph_list, nsteps, eager_fn):
-        if not graph_list:
-            for i in range(nsteps):
-                eager_fn(i % T)
-            return
-        for i in range(nsteps // G):
-            graph_list[i % len(graph_list)].replay()
+    def step(stack):
+        return lambda t, s: decode_pass(torch, stack, X, t, y_buf, idx_buf, tok_buf, counts, s)
 
-    replay(graphs, warmup, decode_step)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    replay(graphs, steps, decode_step)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / steps
+    ms_per_step, per_replay = timer.run(step(layers))
     us_per_layer = ms_per_step * 1000.0 / L
     log(f"sparse decode: {ms_per_step:.4f} ms/step, {us_per_layer:.3f} us/layer")
 
+    cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
+    if B == 1:
+        per_tok = cnt
+    n_union_mean = float(cnt.mean())
+    n_tok_mean = float(per_tok.mean()) / B
+    b_active = n_union_mean * cfg.m * d * cfg.w_bytes  # weight bytes the step must move
+    b_pred = (r * d + n * r) * cfg.p_bytes + 4 * n
+    active_gbps = b_active / (us_per_layer * 1e-6) / 1e9
+
     # ------------------------------------------------------------------ look-ahead schedule
-    # The same layers and tokens through decode_lookahead: layer l >= 1 takes its active set
-    # from layer l - 1's input (its own predictor), predicted on a second stream while layer
-    # l - 1's forward runs. A different mask than the metric's (each layer's own input), so
-    # it is reported beside the metric, not as it.
     lookahead = None
     if args.lookahead_streams or (B == 1 and not args.no_lookahead):
         lookahead = {"mask": "layer l >= 1 from layer l-1's input (layer l's predictor); layer 0 "
@@ -323,28 +447,10 @@ def main():
         def la_fused_step(t, stream=None):
             decode_lookahead_fused(layers, [X[t, l] for l in range(L)], la_bufs, stream=stream)
 
-        def time_schedule(step_fn):
-            step_fn(0)
-            torch.cuda.synchronize()
-            gl = []
-            if not args.no_graph:
-                for gi in range(T // G):
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=cap):
-                        for t in range(gi * G, (gi + 1) * G):
-                            step_fn(t, cap)
-                    gl.append(g)
-                torch.cuda.synchronize()
-            replay(gl, warmup, step_fn)
-            torch.cuda.synchronize()
-            e0.record()
-            replay(gl, steps, step_fn)
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps
-
         if args.lookahead_streams:
-            la_ms = time_schedule(la_step)
+            la_step(0)
+            torch.cuda.synchronize()
+            la_ms, _ = timer.run(la_step)
             la_us = la_ms * 1000.0 / L
             lookahead.update({"streams_us_per_layer": round(la_us, 3),
                               "streams_speedup_vs_metric_path": round(us_per_layer / la_us, 3),
@@ -353,7 +459,9 @@ def main():
             log(f"look-ahead decode (two streams): {la_ms:.4f} ms/step, {la_us:.3f} us/layer")
         if B == 1 and not args.no_lookahead:
             try:
-                fu_ms = time_schedule(la_fused_step)
+                la_fused_step(0)
+                torch.cuda.synchronize()
+                fu_ms, _ = timer.run(la_fused_step)
             except Exception as e:  # shapes the fused kernels do not cover
                 log(f"fused look-ahead not run: {e}")
             else:
@@ -386,18 +494,8 @@ def main():
                 fb = [1000.0 * fev.elapsed_ms(6 * i + 4, 6 * i + 5) for i in range(KT * L)]
                 fev.close()
                 lookahead["launch_us"] = {"gather_and_next_stage1": round(float(np.mean(fa)), 3),
-                                                "down_and_next_scores": round(float(np.mean(fb)), 3)}
+                                          "down_and_next_scores": round(float(np.mean(fb)), 3)}
         del la_bufs
-
-    cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
-    if B == 1:
-        per_tok = cnt
-    used = [t % T for t in range(steps)]
-    n_union_mean = float(cnt[used].mean())
-    n_tok_mean = float(per_tok[used].mean()) / B
-    b_active = n_union_mean * cfg.m * d * cfg.w_bytes  # weight bytes the step must move
-    b_pred = (r * d + n * r) * cfg.p_bytes + 4 * n
-    active_gbps = b_active / (us_per_layer * 1e-6) / 1e9
 
     # ------------------------------------------------------------------ per-kernel event pass
     KT = min(args.kernel_tokens, T)
@@ -437,6 +535,59 @@ def main():
     dom = max(names[1:], key=lambda k: kernels[k]["avg_us"])
     log("kernels:", json.dumps(kernels))
 
+    # ------------------------------------------------------------------ extra legs
+    dense_bytes = (n * d * (3 if cfg.gated else 2)) * cfg.w_bytes
+    all_active = deterministic = quality = None
+    if not args.no_extra:
+        # the library's own dense FFN: every neuron listed (threshold -inf), same weights
+        dense_layers = [s.clone(threshold=float("-inf")) for s in layers]
+        aa_ms, _ = timer.run(step(dense_layers))
+        aa_us = aa_ms * 1000.0 / L
+        all_active = {"us_per_layer": round(aa_us, 3),
+                      "gbps": round(dense_bytes / (aa_us * 1e-6) / 1e9, 1),
+                      "impl": "this library's decode with threshold -inf (every neuron listed): "
+                              "predictor, compaction and the gather kernels over all rows"}
+        assert int(counts[0, 0].item()) == n, "all-active leg did not list every neuron"
+        log(f"library all-active: {aa_us:.3f} us/layer")
+        del dense_layers
+        # deterministic mode (y bitwise reproducible), same masks
+        det_layers = [s.clone(deterministic=True) for s in layers]
+        de_ms, de_per = timer.run(step(det_layers))
+        de_us = de_ms * 1000.0 / L
+        deterministic = {"us_per_layer": round(de_us, 3),
+                         "cost_vs_metric_path": round(de_us / us_per_layer, 4),
+                         "layer_us_percentiles": percentiles_us(de_per, L)}
+        log(f"deterministic mode: {de_us:.3f} us/layer")
+        del det_layers
+        # predictor recall / precision against the true ReLU signs on sampled steps
+        tp = fp = fn = 0
+        ns = min(8, T)
+        for t in range(ns):
+            decode_pass(torch, layers, X, t, y_buf, idx_buf, tok_buf, counts)
+            torch.cuda.synchronize()
+            for l in range(L):
+                o = originals[l]
+                a = F.linear(X[t, l], o.w_a.float(), o.b_a)           # [B, n] true ReLU input
+                k = int(counts[t, l].item())
+                pidx = layers[l].perm_dev[idx_buf[l][:k].long()]       # original neuron ids
+                bits = tok_buf[l][:k]
+                for b in range(B):
+                    pm = torch.zeros(n, dtype=torch.bool, device="cuda")
+                    sel = ((bits >> b) & 1).bool() if B > 1 else torch.ones(k, dtype=torch.bool,
+                                                                              device="cuda")
+                    pm[pidx[sel]] = True
+                    tm = a[b] > 0
+                    tp += int((pm & tm).sum())
+                    fp += int((pm & ~tm).sum())
+                    fn += int((~pm & tm).sum())
+        quality = {"recall": round(tp / max(tp + fn, 1), 4),
+                   "precision": round(tp / max(tp + fp, 1), 4),
+                   "sample": f"{ns} steps x {L} layers x {B} token(s); true mask = fp32 "
+                             f"W_a x + b_a > 0 (torch), predicted = the decode's list",
+                   "note": "synthetic calibrated random-subspace predictor (no trained "
+                           "predictor exists here): a diagnostic, not graded"}
+        log(f"predictor recall {quality['recall']}, precision {quality['precision']}")
+
     # ------------------------------------------------------------------ dense baseline
     dense = None
     if not args.no_dense:
@@ -445,7 +596,7 @@ def main():
         bw = [o.b_a.to(wdt) for o in originals]
         bow = [o.b_o.to(wdt) for o in originals]
 
-        def dense_step(t):
+        def dense_step(t, stream=None):
             for l in range(L):
                 o = originals[l]
                 x = Xw[t, l]
@@ -458,28 +609,19 @@ def main():
         for t in range(2):
             dense_step(t)
         torch.cuda.synchronize()
-        dgraphs = []
-        for gi in range(T // G):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for t in range(gi * G, (gi + 1) * G):
-                    dense_step(t)
-            dgraphs.append(g)
-        replay(dgraphs, warmup, dense_step)
-        torch.cuda.synchronize()
-        e0.record()
-        replay(dgraphs, steps, dense_step)
-        e1.record()
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / steps
+        dms, _ = timer.run(dense_step)
         dense_us = dms * 1000.0 / L
-        dense_bytes = (n * d * (3 if cfg.gated else 2)) * cfg.w_bytes
         dense = {"us_per_layer": round(dense_us, 3),
                  "gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+                 "dense_weight_bytes_per_layer": int(dense_bytes),
                  "impl": f"torch F.linear/matmul (hipBLASLt/rocBLAS), {cfg.w_dtype}, {B} token(s), "
                          f"graph-captured"}
+        if all_active:
+            dense["library_all_active"] = all_active
+        if probe:
+            dense["ideal_us_at_achievable_peak"] = round(dense_bytes / (probe["gbps"] * 1e9) * 1e6, 3)
         log(f"dense: {dense_us:.3f} us/layer ({dense['gbps']} GB/s)")
-        del dgraphs
+        del Xw
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -489,26 +631,52 @@ def main():
         n_cpu_layers = min(L, 2)
         host = [originals[l].numpy() for l in range(n_cpu_layers)]
         Xh = X[:, :n_cpu_layers].cpu().numpy()
-        times = []
-        t_start = time.time()
-        done = 0
-        while time.time() - t_start < args.cpu_seconds and done < T * n_cpu_layers:
-            t, l = done // n_cpu_layers, done % n_cpu_layers
-            Lh = host[l]
-            x = np.ascontiguousarray(Xh[t, l])
-            c0 = time.perf_counter()
-            S = oracle.predict(x, Lh["p1"], Lh["p2"], Lh["c"])
-            idx, k, tok = oracle.compact(oracle.threshold(S, 0.0))
-            _ = oracle.forward(x, Lh["w_a"], Lh["w_o"], idx, tok, Wu=Lh["w_u"], b_a=Lh["b_a"],
-                               b_o=Lh["b_o"])
-            times.append((time.perf_counter() - c0) * 1e6)
-            done += 1
-        cpu = {"value": round(float(np.median(times)), 1), "unit": "us/layer", "cores": 1,
+
+        def time_oracle(seconds):
+            times = []
+            t_start = time.time()
+            done = 0
+            while time.time() - t_start < seconds and done < T * n_cpu_layers:
+                t, l = done // n_cpu_layers, done % n_cpu_layers
+                Lh = host[l]
+                x = np.ascontiguousarray(Xh[t, l])
+                c0 = time.perf_counter()
+                S = oracle.predict(x, Lh["p1"], Lh["p2"], Lh["c"])
+                idx, k, tok = oracle.compact(oracle.threshold(S, 0.0))
+                _ = oracle.forward(x, Lh["w_a"], Lh["w_o"], idx, tok, Wu=Lh["w_u"], b_a=Lh["b_a"],
+                                   b_o=Lh["b_o"])
+                times.append((time.perf_counter() - c0) * 1e6)
+                done += 1
+            return times
+
+        nproc, usable, model = host_cpu()
+        t1 = time_oracle(args.cpu_seconds)
+        single = {"value": round(float(np.median(t1)), 1), "unit": "us/layer", "cores": 1,
+                  "samples": len(t1)}
+        log(f"cpu oracle, 1 thread: {single['value']} us/layer over {len(t1)} samples")
+        prev = oracle.set_library(oracle.open_library(oracle.OMP_LIB_PATH))
+        try:
+            threads = oracle.threads()
+            tm = time_oracle(args.cpu_seconds)
+        finally:
+            oracle.set_library(prev)
+        cpu = {"value": round(float(np.median(tm)), 1), "unit": "us/layer", "cores": threads,
                "kind": "oracle",
-               "sample": f"{len(times)} (step, layer) decodes of {B} token(s), layers "
-                         f"0..{n_cpu_layers - 1}, steps 0..{(len(times) - 1) // n_cpu_layers}: "
-                         f"predict + threshold + compact + forward in fp64, single thread, median"}
-        log(f"cpu oracle: {cpu['value']} us/layer over {len(times)} samples")
+               "sample": f"{len(tm)} (step, layer) decodes of {B} token(s), layers "
+                         f"0..{n_cpu_layers - 1}: predict + threshold + compact + forward in "
+                         f"fp64 (OpenMP over neurons and output columns, {threads} threads), "
+                         f"median; single_thread: the same, one thread",
+               "nproc": nproc, "usable_cores": usable, "cpu_model": model,
+               "single_thread": single}
+        log(f"cpu oracle, OpenMP {threads} threads: {cpu['value']} us/layer over {len(tm)} samples "
+            f"({model}, nproc {nproc})")
+        del host, Xh
+
+    # ------------------------------------------------------------------ the 5% -> 10% ramp
+    ramp = None
+    if not args.no_extra and cfg.name == "opt6.7b_stack_10pct" and B == 1 and not args.layers:
+        layers = originals = None  # free the headline stack before building the ramp's
+        ramp = run_ramp(torch, args, timer, dense)
 
     # ------------------------------------------------------------------ report
     kd = kernels[dom]
@@ -518,6 +686,9 @@ def main():
             "unit": "GB/s", "frac": round(kd["gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": (int(traffic) if traffic is not None else None),
             "algorithmic_bytes": kd["algorithmic_bytes"]}
+    if probe:
+        roof["achievable_peak"] = probe["gbps"]
+        roof["frac_of_achievable"] = round(kd["gbps"] / probe["gbps"], 4)
     if "mfma_util" in kd:
         # the matrix-core kernels stay bound by HBM at these arithmetic intensities; their
         # flops rate against the fp16 matrix-core peak rides along
@@ -544,6 +715,7 @@ def main():
             "activity_target": (f"{act_lo:.3f}-{act_hi:.3f}" if act_lo != act_hi else f"{act_lo:.3f}"),
             "tokens": T, "graph_steps": G,
         },
+        "layer_us_percentiles": percentiles_us(per_replay, L),
         "n_act_mean": round(n_tok_mean, 1),
         "n_union_mean": round(n_union_mean, 1),
         "activity_measured": round(n_tok_mean / n, 4),
@@ -556,14 +728,57 @@ def main():
         "kernels": kernels,
         "dense": dense,
         "speedup_vs_dense": (round(dense["us_per_layer"] / us_per_layer, 3) if dense else None),
+        "speedup_vs_library_all_active": (round(all_active["us_per_layer"] / us_per_layer, 3)
+                                          if all_active else None),
+        "speedup_vs_ideal_dense": (round(dense["ideal_us_at_achievable_peak"] / us_per_layer, 3)
+                                   if dense and "ideal_us_at_achievable_peak" in dense else None),
         "roofline": roof,
+        "hbm_read_probe": probe,
+        "deterministic": deterministic,
+        "predictor_quality": quality,
         "cpu_baseline": cpu,
         "lookahead": lookahead,
+        "c2_ramp": ramp,
         "kernel_source_sha256": kernel_source_sha(),
     }
     if lookahead and dense and "us_per_layer" in lookahead:
         lookahead["speedup_vs_dense"] = round(dense["us_per_layer"] / lookahead["us_per_layer"], 3)
     print(json.dumps(out), flush=True)
+
+
+def run_ramp(torch, args, timer, dense):
+    """The OPT-6.7B stack on its 5% -> 10% per-layer activity ramp (same weights, biases
+    set for the ramp): the headline path only, timed the same way."""
+    from synth import get_config, make_tokens
+    cfg = get_config("C2")
+    L, d, n = cfg.layers, cfg.d, cfg.n
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layers, _ = build_stack(cfg, 1, L, args, lambda l: False)
+    X = make_tokens(cfg, timer.T * L, 200, "cuda").view(timer.T, L, 1, d).contiguous()
+    y_buf = torch.empty((L, 1, d), dtype=torch.float32, device="cuda")
+    idx_buf = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(L)]
+    tok_buf = [torch.empty(n, dtype=torch.int64, device="cuda") for _ in range(L)]
+    counts = torch.zeros((timer.T, L), dtype=torch.int32, device="cuda")
+    for t in range(timer.T):
+        decode_pass(torch, layers, X, t, y_buf, idx_buf, tok_buf, counts)
+    torch.cuda.synchronize()
+    ms, per = timer.run(lambda t, s: decode_pass(torch, layers, X, t, y_buf, idx_buf, tok_buf,
+                                                 counts, s))
+    us = ms * 1000.0 / L
+    cnt = counts.cpu().numpy().astype(np.int64)
+    b_active = float(cnt.mean()) * cfg.m * d * cfg.w_bytes
+    gbps = b_active / (us * 1e-6) / 1e9
+    log(f"C2 ramp: {us:.3f} us/layer")
+    out = {"workload": f"{cfg.name}: {cfg.description}", "us_per_layer": round(us, 3),
+           "layer_us_percentiles": percentiles_us(per, L),
+           "activity_measured": round(float(cnt.mean()) / n, 4),
+           "active_weight_gbps": round(gbps, 1),
+           "active_weight_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    if dense:  # the same weight shapes: the dense time does not depend on the activity
+        out["speedup_vs_dense"] = round(dense["us_per_layer"] / us, 3)
+    del layers
+    return out
 
 
 if __name__ == "__main__":

@@ -47,6 +47,12 @@
  *    from run to run; y is too when the descriptor asks for it (`deterministic`),
  *    otherwise the down projection's row splits add into y with float atomics and its
  *    last bits may vary between runs.
+ *  - Range limit of the matrix-core path (2 or more tokens, fp16 weights, d a multiple of
+ *    256): there each fp32 token value and each fp32 activation h is carried as a pair of
+ *    fp16 halves (hi + lo, about 22 significant bits) and multiplied on the matrix cores.
+ *    Every |x| and |h| must therefore stay below 65504, the largest finite fp16 value; a
+ *    larger one becomes inf and its token's y is not finite. The single-token path and
+ *    fp32 weights have no such limit (fp32 throughout).
  */
 #ifndef SPARSE_FFN_H
 #define SPARSE_FFN_H
@@ -190,6 +196,17 @@ int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float
  * borrowed; the handle only stores the six values. Returns SFFN_ERR_INVALID for a NULL
  * handle or a NULL entry. */
 int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events);
+
+/* Measurement helper, not a step of the method: enqueue a plain read stream over bytes of
+ * device memory at buf (16-byte aligned; bytes a positive multiple of 16), 16-byte loads,
+ * non-temporal, by `workgroups` workgroups of 256 threads (0 = 8 per compute unit). Timed
+ * by the caller (events around the call), it gives the read bandwidth this device
+ * achieves, the practical ceiling of every weight stream of the decode path, reported
+ * beside the nominal HBM peak. sink: device uint32 [workgroups] the kernel may write (it
+ * practically never does; the possible store keeps the loads from being removed). Nothing
+ * is read from sink. Returns SFFN_ERR_INVALID on a bad argument. */
+int sparse_ffn_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                          void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* sparse_ffn_status_string(int status);

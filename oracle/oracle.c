@@ -78,12 +78,14 @@ int oracle_predict(int32_t d, int32_t n, int32_t r, int32_t B, const float* X,
   if (!q) return ORC_ERR;
   for (int32_t b = 0; b < B; ++b) {
     const float* x = X + (size_t)b * d;
+#pragma omp parallel for schedule(static)
     for (int32_t j = 0; j < r; ++j) {
       double acc = 0.0;
       for (int32_t t = 0; t < d; ++t) acc += elem(P1, p_dtype, (size_t)j * d + t) * (double)x[t];
       q[j] = acc;
       if (Q) Q[(size_t)b * r + j] = acc;
     }
+#pragma omp parallel for schedule(static)
     for (int32_t i = 0; i < n; ++i) {
       double acc = 0.0;
       for (int32_t j = 0; j < r; ++j) acc += elem(P2, p_dtype, (size_t)i * r + j) * q[j];
@@ -128,7 +130,12 @@ int oracle_compact(int32_t B, int32_t n, const uint8_t* M, int32_t* idx, int32_t
  *   plain: h = relu(a);  gated: h = relu(a) * (sum_t Wu[i][t] x[b][t])
  *   y[b][j] += h * Wo[i][j]   for every j
  * then y[b][j] += b_o[j]. Wa, Wu and Wo (= W_down transposed) are n x d row-major.
- * relu(a) = a if a > 0 else +0.0. b_a and b_o may be NULL (= 0). */
+ * relu(a) = a if a > 0 else +0.0. b_a and b_o may be NULL (= 0).
+ * Written as two loops per token: every listed neuron's h first (each depends on its own
+ * row only), then the output elements, each starting at 0 and adding its h * Wo terms in
+ * ascending k, then b_o. Each output element sees exactly the operations of the one-loop
+ * form above, in the same order, so the result is the same bit for bit; an OpenMP build
+ * may run either loop's iterations on several threads without changing any sum. */
 int oracle_forward(int32_t d, int32_t n, int32_t B, int32_t gated, const float* X,
                    const void* Wa, const void* Wu, const void* Wo, int32_t w_dtype,
                    const float* b_a, const float* b_o, const int32_t* idx, int32_t count,
@@ -138,11 +145,15 @@ int oracle_forward(int32_t d, int32_t n, int32_t B, int32_t gated, const float* 
     return ORC_ERR;
   for (int32_t k = 0; k < count; ++k)
     if (idx[k] < 0 || idx[k] >= n) return ORC_ERR;
+  double* hk = (double*)malloc(sizeof(double) * (size_t)(count > 0 ? count : 1));
+  uint8_t* use = (uint8_t*)malloc((size_t)(count > 0 ? count : 1));
+  if (!hk || !use) { free(hk); free(use); return ORC_ERR; }
   for (int32_t b = 0; b < B; ++b) {
     const float* x = X + (size_t)b * d;
     double* y = Y + (size_t)b * d;
-    for (int32_t j = 0; j < d; ++j) y[j] = 0.0;
+#pragma omp parallel for schedule(dynamic, 16)
     for (int32_t k = 0; k < count; ++k) {
+      use[k] = 0;
       if (tokmask && !((tokmask[k] >> b) & 1)) continue;
       int32_t i = idx[k];
       double a = 0.0;
@@ -154,12 +165,39 @@ int oracle_forward(int32_t d, int32_t n, int32_t B, int32_t gated, const float* 
         for (int32_t t = 0; t < d; ++t) u += elem(Wu, w_dtype, (size_t)i * d + t) * (double)x[t];
         h = h * u;
       }
-      for (int32_t j = 0; j < d; ++j) y[j] += h * elem(Wo, w_dtype, (size_t)i * d + j);
+      hk[k] = h;
+      use[k] = 1;
     }
-    if (b_o)
-      for (int32_t j = 0; j < d; ++j) y[j] += (double)b_o[j];
+#pragma omp parallel for schedule(static)
+    for (int32_t jb = 0; jb < d; jb += 64) {
+      const int32_t je = jb + 64 < d ? jb + 64 : d;
+      for (int32_t j = jb; j < je; ++j) y[j] = 0.0;
+      for (int32_t k = 0; k < count; ++k) {
+        if (!use[k]) continue;
+        const int32_t i = idx[k];
+        const double h = hk[k];
+        for (int32_t j = jb; j < je; ++j) y[j] += h * elem(Wo, w_dtype, (size_t)i * d + j);
+      }
+      if (b_o)
+        for (int32_t j = jb; j < je; ++j) y[j] += (double)b_o[j];
+    }
   }
+  free(hk);
+  free(use);
   return ORC_OK;
+}
+
+/* Threads the oracle's loops run on: 1 in the plain build, OpenMP's count in an OpenMP
+ * build (timing reports only). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* Dense FFN: the forward above with every neuron 0..n-1, ascending, and no mask. */

@@ -16,17 +16,25 @@ F32, F16, F64 = 0, 1, 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+OMP_LIB_PATH = os.path.join(_HERE, "liboracle_omp.so")
 _lib = None
+_FLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+          "-Wextra"]
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into liboracle.so (plain C11, no fast-math, no FP contraction)."""
+    """Compile oracle.c with gcc into liboracle.so (plain C11, no fast-math, no FP
+    contraction, single-threaded: the OpenMP pragmas are ignored), and the same source with
+    -fopenmp into liboracle_omp.so (the CPU baseline's all-core timing; same arithmetic)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
+        subprocess.run(["gcc", *_FLAGS, "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"],
+                       check=True)
         os.replace(tmp, _LIB_PATH)
+    if force or not os.path.exists(OMP_LIB_PATH):
+        tmp = OMP_LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *_FLAGS, "-fopenmp", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, OMP_LIB_PATH)
     return _LIB_PATH
 
 
@@ -46,7 +54,17 @@ def _configure(lib):
     for name in ("predict", "threshold", "compact", "forward", "dense", "preact",
                  "profile_counts", "permutation", "pack_rows"):
         getattr(lib, "oracle_" + name).restype = C.c_int
+    if hasattr(lib, "oracle_threads"):
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = C.c_int
     return lib
+
+
+def threads() -> int:
+    """Threads the active oracle library runs its loops on (1 unless the OpenMP build is
+    routed in with set_library)."""
+    lib = load()
+    return int(lib.oracle_threads()) if hasattr(lib, "oracle_threads") else 1
 
 
 def open_library(path: str):

@@ -71,8 +71,18 @@ C5 = Config(5, "opt175b_slice", 12288, 49152, 1024, False, "f16", "f16", 24, _co
             0.10, "normal", (1,),
             description="OPT-175B-shaped FFN slice, 24 layers, fp16, r=1024, 5% active, Zipf(1.2)")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+# The OPT-6.7B-shaped stack with every layer at 10% target activity: the metric's own
+# condition (~10% of neurons active in decode, PowerInfer-2 article, section 4.1.2). Same
+# config id, so the same seeded weights, tokens and predictor subspaces as C2; only the
+# per-neuron biases (which set the activity) differ.
+C2_10 = Config(2, "opt6.7b_stack_10pct", 4096, 16384, 256, False, "f16", "f16", 32,
+               _const(0.10, 32), 1.1, 0.20, "normal", (1,),
+               description="OPT-6.7B-shaped ReLU FFN stack, 32 layers, fp16, r=256, every layer "
+                           "10% active, Zipf(1.1)")
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2_10)}
 CONFIGS.update({f"C{c.cid}": c for c in (C1, C2, C3, C4, C5)})
+CONFIGS["C2_10"] = C2_10
 
 
 def get_config(name: str) -> Config:

@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -125,6 +125,14 @@ def test_calls_reject_null_handle_and_bad_batch(N):
     assert L.sparse_ffn_pack_rows(0x10000, 0x10000, 0x10000, 4, 6, 0, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_pack_rows(0x10000, 0x10000, 0x10000, 4, 8, 4, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_profile_counts(None, 1, 0, None, 8, 8, 0x10000, 4, 0x10000, None) == N.SFFN_ERR_INVALID
+    # read probe: null buffer or sink, a size that is not a positive multiple of 16, an
+    # unaligned buffer, a negative grid
+    assert L.sparse_ffn_read_probe(None, 1024, 1, 0x10000, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_read_probe(0x10000, 1024, 1, None, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_read_probe(0x10000, 1000, 1, 0x10000, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_read_probe(0x10000, 0, 1, 0x10000, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_read_probe(0x10008, 1024, 1, 0x10000, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_read_probe(0x10000, 1024, -1, 0x10000, None) == N.SFFN_ERR_INVALID
 
 
 def test_status_strings(N):

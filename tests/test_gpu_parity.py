@@ -673,6 +673,7 @@ def test_full_size_layer_decode(name, layer):
     y, idx, count, tok = s.decode(X)
     torch.cuda.synchronize()
     k = int(count.item())
+    _check_published_list(s, X, 1, to_np(idx), k, to_np(tok))
     S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
     Mg = gpu_mask_orig(s.perm, to_np(idx), k, to_np(tok), 1, c.n)
     M, nband = check_mask(Mg, S)
@@ -681,6 +682,25 @@ def test_full_size_layer_decode(name, layer):
     errs = rel_err_rows(to_np(y), Y)
     say(f"  count={k} ({k / c.n:.3f}) band={nband} err={max(errs):.2e}")
     assert max(errs) <= REL_TOL
+
+
+def _check_published_list(s, X, B, idx_h, k, tok_h):
+    """The list a full-size decode publishes (idx, count, token bits; read by nothing in the
+    step itself, whose down kernels take the ranges' activity words) must be the compaction
+    of the decode's own scores, bit for bit: a second decode that also returns its scores
+    publishes the same list, strictly ascending, equal to the oracle's compaction of those
+    scores (the same fp32 values on both sides, no band)."""
+    scores = torch.empty((B, s.n), dtype=torch.float32, device="cuda")
+    _, idx2, count2, tok2 = s.decode(X, scores=scores)
+    torch.cuda.synchronize()
+    assert int(count2.item()) == k
+    assert np.array_equal(to_np(idx2)[:k], idx_h[:k])
+    assert np.array_equal(to_np(tok2)[:k], tok_h[:k])
+    assert np.all(np.diff(idx_h[:k]) > 0)
+    ri, rk, rt = oracle.compact(oracle.threshold(to_np(scores).astype(np.float32), s.threshold))
+    assert rk == k
+    assert np.array_equal(idx_h[:k], ri)
+    assert np.array_equal(tok_h[:k].astype(np.uint64), rt)
 
 
 @pytest.mark.parametrize("B", [2, 4, 8, 16, 32])
@@ -698,6 +718,7 @@ def test_full_size_batch_decode(B):
     y, idx, count, tok = s.decode(X)
     torch.cuda.synchronize()
     k = int(count.item())
+    _check_published_list(s, X, B, to_np(idx), k, to_np(tok))
     S = oracle.predict(Xh, L["p1"], L["p2"], L["c"])
     Mg = gpu_mask_orig(s.perm, to_np(idx), k, to_np(tok), B, c.n)
     M, nband = check_mask(Mg, S)
