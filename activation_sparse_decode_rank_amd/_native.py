@@ -10,7 +10,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_ffn.so")
 
-SFFN_OK, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_ERR_HIP = 0, -1, -2, -3
+SFFN_OK, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_ERR_HIP, SFFN_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+SFFN_STATIC_SCRATCH_BYTES = 16 << 20
 SFFN_F32, SFFN_F16 = 0, 1
 SFFN_MAX_BATCH = 64
 
@@ -49,6 +50,7 @@ def _load():
         "sparse_ffn_compact": (C.c_int, [P, P, I32, P, P, P, P]),
         "sparse_ffn_forward": (C.c_int, [P, P, I32, P, P, P, P, P]),
         "sparse_ffn_decode": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
+        "sparse_ffn_decode_static": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
         "sparse_ffn_lookahead_begin": (C.c_int, [P, P, P]),
         "sparse_ffn_decode_lookahead": (C.c_int, [P, P, P, P, P, P, P, P]),
         "sparse_ffn_status_string": (C.c_char_p, [C.c_int]),
@@ -68,6 +70,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destroy",
             "sparse_ffn_predict", "sparse_ffn_compact", "sparse_ffn_forward", "sparse_ffn_decode",
+            "sparse_ffn_decode_static",
             "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
@@ -115,6 +118,11 @@ def sparse_ffn_forward(h, x, B, idx, count, tokmask, y, stream) -> None:
 
 def sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
     _ck(_lib.sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream), "sparse_ffn_decode")
+
+
+def sparse_ffn_decode_static(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
+    _ck(_lib.sparse_ffn_decode_static(h, x, B, y, idx, count, tokmask, scores, stream),
+        "sparse_ffn_decode_static")
 
 
 def sparse_ffn_lookahead_begin(h, x, stream) -> None:

@@ -19,6 +19,9 @@ struct sparse_ffn_s {
   int max_batch;
   hipEvent_t ev[6];
   bool timing;
+  bool has_ws;                  // false: created without a workspace (static decode only)
+  int device;                   // the HIP device current at creation
+  std::vector<int32_t> rs_host;  // the range table (g_mid + 1 entries), for the static decode
 };
 
 namespace {
@@ -38,8 +41,10 @@ int check_desc(const sffn_desc* d) {
   return SFFN_OK;
 }
 
+// workspace may be NULL with workspace_bytes 0: a handle for sparse_ffn_decode_static only
 int check_ptrs(const sffn_desc* d) {
-  if (!d->w_act || !d->w_down_t || !d->p1 || !d->p2 || !d->workspace) return SFFN_ERR_INVALID;
+  if (!d->w_act || !d->w_down_t || !d->p1 || !d->p2) return SFFN_ERR_INVALID;
+  if (!d->workspace && d->workspace_bytes != 0) return SFFN_ERR_INVALID;
   if (!aligned16(d->w_act) || !aligned16(d->w_down_t) || !aligned16(d->p1) ||
       !aligned16(d->p2) || !aligned16(d->workspace))
     return SFFN_ERR_INVALID;
@@ -142,6 +147,8 @@ const char* sparse_ffn_status_string(int status) {
     case SFFN_ERR_INVALID: return "invalid argument";
     case SFFN_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case SFFN_ERR_HIP: return "HIP call failed";
+    case SFFN_ERR_TOO_LARGE:
+      return "workspace needed exceeds the static scratch buffer (SFFN_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -158,8 +165,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     if (rc != SFFN_OK) return rc;
     rc = check_ptrs(desc);
     if (rc != SFFN_OK) return rc;
+    const bool has_ws = desc->workspace != nullptr;
     const size_t need = sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch);
-    if (desc->workspace_bytes < need) return SFFN_ERR_INVALID;
+    if (has_ws && desc->workspace_bytes < need) return SFFN_ERR_INVALID;
 
     sffn::LayerDev L{};
     L.d = desc->d;
@@ -184,6 +192,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return SFFN_ERR_HIP;
     L.n_cus = cus;
+    // the static scratch array's address on this device (looked up once per device); a
+    // handle without a workspace has no other device memory to run on
+    if (!sffn::static_scratch_setup(dev) && !has_ws) return SFFN_ERR_HIP;
     L.g_gather = std::max(1, 2 * cus);
     L.ks_down = sffn::down_split(L, desc->deterministic != 0);
     L.ks_tile = sffn::tile_split(L, desc->deterministic != 0);
@@ -191,15 +202,15 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     // stream-K up projection: two workgroups per compute unit, and enough that one
     // range touches at most 13 tiles of the largest list
     L.g_sk = std::min(sffn::SK_G_MAX, std::max(2 * cus, ((desc->d_ffn + 15) / 16 + 12) / 13));
-    if (L.sk_part) {
+    if (has_ws && L.sk_part) {
       // its arrival counters start at zero; every call leaves them zero
       if (hipMemset(L.sk_cnt, 0, (size_t)((desc->d_ffn + 15) / 16 + 1) * 4) != hipSuccess)
         return SFFN_ERR_HIP;
     }
     // range activity words start empty, so a look-ahead decode run before any prediction
     // sees an empty set
-    if (hipMemset(L.wbits, 0, (size_t)sffn::G_MID_MAX * 8) != hipSuccess ||
-        hipStreamSynchronize(nullptr) != hipSuccess)
+    if (has_ws && (hipMemset(L.wbits, 0, (size_t)sffn::G_MID_MAX * 8) != hipSuccess ||
+                   hipStreamSynchronize(nullptr) != hipSuccess))
       return SFFN_ERR_HIP;
 
     // the middle kernel reads the predictor row of every neuron and the ReLU-input row(s)
@@ -233,8 +244,8 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     // (d_ffn up to 131072 at 64 neurons a range); a wider layer keeps g_mid out of range,
     // so the decode entry points return SFFN_ERR_UNSUPPORTED and nothing reads the table
     if (L.g_mid > 0 && L.g_mid <= sffn::G_MID_MAX) {
-      if (hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
-          hipSuccess)
+      if (has_ws && hipMemcpy(L.rs, rs.data(), rs.size() * sizeof(int32_t),
+                              hipMemcpyHostToDevice) != hipSuccess)
         return SFFN_ERR_HIP;
       L.rs_in_arg = L.g_mid <= sffn::RS_ARG_MAX;
       if (L.rs_in_arg) std::copy(rs.begin(), rs.end(), L.ra.r);
@@ -266,6 +277,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     h->max_batch = desc->max_batch;
     for (auto& e : h->ev) e = nullptr;
     h->timing = false;
+    h->has_ws = has_ws;
+    h->device = dev;
+    if (L.g_mid > 0 && L.g_mid <= sffn::G_MID_MAX) h->rs_host = rs;
     *out = h;
     return SFFN_OK;
   } catch (...) {
@@ -280,6 +294,7 @@ int sparse_ffn_destroy(sparse_ffn_t h) {
 
 int sparse_ffn_predict(sparse_ffn_t h, const float* x, int32_t B, float* scores, void* stream) {
   if (!h || !x || !scores || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!h->has_ws) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(scores)) return SFFN_ERR_INVALID;
   return sffn::launch_predict(h->L, x, B, scores, static_cast<hipStream_t>(stream)) == hipSuccess
              ? SFFN_OK
@@ -289,6 +304,7 @@ int sparse_ffn_predict(sparse_ffn_t h, const float* x, int32_t B, float* scores,
 int sparse_ffn_compact(sparse_ffn_t h, const float* scores, int32_t B, int32_t* idx,
                        int32_t* count, uint64_t* tokmask, void* stream) {
   if (!h || !scores || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!h->has_ws) return SFFN_ERR_INVALID;
   if (B > 1 && !tokmask) return SFFN_ERR_INVALID;
   return sffn::launch_compact(h->L, scores, B, idx, count, tokmask,
                               static_cast<hipStream_t>(stream)) == hipSuccess
@@ -299,6 +315,7 @@ int sparse_ffn_compact(sparse_ffn_t h, const float* scores, int32_t B, int32_t* 
 int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t* idx,
                        const int32_t* count, const uint64_t* tokmask, float* y, void* stream) {
   if (!h || !x || !idx || !count || !y || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!h->has_ws) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   return sffn::launch_forward(h->L, x, B, idx, count, tokmask, y,
                               static_cast<hipStream_t>(stream)) == hipSuccess
@@ -309,6 +326,7 @@ int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t*
 int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                       int32_t* count, uint64_t* tokmask, float* scores, void* stream) {
   if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!h->has_ws) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (!sffn::shape_supported(h->L, true)) return SFFN_ERR_UNSUPPORTED;
   return sffn::launch_decode(h->L, x, B, y, idx, count, tokmask, scores,
@@ -330,7 +348,7 @@ bool overlap(const sffn_desc& a, const sffn_desc& b) {
 }  // namespace
 
 int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream) {
-  if (!first || !x || !aligned16(x)) return SFFN_ERR_INVALID;
+  if (!first || !x || !aligned16(x) || !first->has_ws) return SFFN_ERR_INVALID;
   if (!lookahead_ok(first)) return SFFN_ERR_UNSUPPORTED;
   return sffn::run_lookahead_begin(first->L, x, static_cast<hipStream_t>(stream)) == hipSuccess
              ? SFFN_OK
@@ -340,6 +358,7 @@ int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream)
 int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
                                 int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream) {
   if (!cur || !x || !y || !idx || !count || cur == next) return SFFN_ERR_INVALID;
+  if (!cur->has_ws || (next && !next->has_ws)) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (next && (next->L.d != cur->L.d || overlap(cur->desc, next->desc))) return SFFN_ERR_INVALID;
   if (!lookahead_ok(cur) || (next && !lookahead_ok(next))) return SFFN_ERR_UNSUPPORTED;
@@ -347,6 +366,21 @@ int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float
   return sffn::run_lookahead(cur->L, next ? &next->L : nullptr, x, y, idx, count, tokmask,
                              static_cast<hipStream_t>(stream), cur->timing ? cur->ev : nullptr) ==
                  hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
+                             int32_t* count, uint64_t* tokmask, float* scores, void* stream) {
+  if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
+  if (!sffn::shape_supported(h->L, true) || h->rs_host.empty()) return SFFN_ERR_UNSUPPORTED;
+  if (sffn::workspace_bytes(h->L.d, h->L.n, h->L.r, B) > sffn::STATIC_SCRATCH_BYTES)
+    return SFFN_ERR_TOO_LARGE;
+  void* base = sffn::static_scratch_ptr(h->device);
+  if (!base) return SFFN_ERR_HIP;
+  return sffn::run_decode_static(h->L, h->rs_host.data(), h->L.g_mid, base, x, B, y, idx, count,
+                                 tokmask, scores, static_cast<hipStream_t>(stream)) == hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;
 }

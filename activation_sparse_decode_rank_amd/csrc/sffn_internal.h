@@ -172,6 +172,18 @@ hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const 
                                  hipStream_t s);
 hipError_t launch_pack_rows(const void* src, const int32_t* perm, void* dst, int rows,
                             int64_t row_bytes, int64_t dst_stride_bytes, hipStream_t s);
+// sffn_static.hip: the decode step over a static per-device scratch array of
+// STATIC_SCRATCH_BYTES (see sparse_ffn_decode_static). setup: look the array's address up
+// on device dev (current), once; ptr: that address (null before setup). run: carve the
+// per-call regions of H's workspace layout for B tokens out of base, write the range table
+// (g + 1 entries from the host) and zero the tile counters with a small kernel, then the
+// decode step's kernels.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
+bool static_scratch_setup(int dev);
+void* static_scratch_ptr(int dev);
+hipError_t run_decode_static(const LayerDev& H, const int32_t* rs_host, int g, void* base,
+                             const float* x, int B, float* y, int32_t* idx, int32_t* count,
+                             uint64_t* tokmask, float* scores, hipStream_t s);
 // sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
 // number of workgroups; sink [workgroups] is written only in a practically impossible case
 hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink,

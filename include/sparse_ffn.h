@@ -68,13 +68,18 @@ enum {
   SFFN_OK = 0,
   SFFN_ERR_INVALID = -1,      /* bad argument; nothing was enqueued */
   SFFN_ERR_UNSUPPORTED = -2,  /* valid but no kernel for this dtype/shape */
-  SFFN_ERR_HIP = -3           /* a HIP call failed (device query or launch) */
+  SFFN_ERR_HIP = -3,          /* a HIP call failed (device query or launch) */
+  SFFN_ERR_TOO_LARGE = -4     /* sparse_ffn_decode_static: the call needs more scratch than
+                                 SFFN_STATIC_SCRATCH_BYTES; nothing was enqueued */
 };
 
 typedef enum { SFFN_F32 = 0, SFFN_F16 = 1 } sffn_dtype;
 
 /* Largest batch: one bit per token in the 64-bit membership words. */
 #define SFFN_MAX_BATCH 64
+
+/* Size of the static per-device scratch array behind sparse_ffn_decode_static (16 MiB). */
+#define SFFN_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef struct sparse_ffn_s* sparse_ffn_t;
 
@@ -97,7 +102,10 @@ typedef struct {
   const void* p1;        /* device [rank][d] */
   const void* p2;        /* device [d_ffn][rank] */
   const float* p_bias;   /* device [d_ffn]: predictor bias c; NULL = 0 */
-  void* workspace;       /* device scratch of at least sparse_ffn_workspace_bytes() */
+  void* workspace;       /* device scratch of at least sparse_ffn_workspace_bytes(); or NULL
+                            with workspace_bytes 0: the handle then serves only
+                            sparse_ffn_decode_static (every other call on it returns
+                            SFFN_ERR_INVALID) */
   size_t workspace_bytes;
   const float* neuron_freq; /* host [d_ffn], optional: expected activation frequency of each
                                neuron (e.g. profile counts / profile tokens). Read only by
@@ -185,6 +193,27 @@ int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32
 int sparse_ffn_lookahead_begin(sparse_ffn_t first, const float* x, void* stream);
 int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float* x, float* y,
                                 int32_t* idx, int32_t* count, uint64_t* tokmask, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sparse_ffn_decode with the same
+ * arguments, results and kernels, but every per-call intermediate (predictor output,
+ * activations, token bits, union and range words, split tokens, tile partial sums and
+ * counters, and a copy of the handle's range table) lives in a static array of
+ * SFFN_STATIC_SCRATCH_BYTES that the library holds on each device it runs on until the
+ * process ends; the handle's workspace is not touched (it may be NULL, see sffn_desc).
+ * It allocates nothing: no hipMalloc, no hipFree, no memset; one small kernel writes the
+ * range table and zeroes the counters at the start of every call.
+ * Limits: the scratch the call needs is sparse_ffn_workspace_bytes() of the descriptor
+ * with max_batch = B; above SFFN_STATIC_SCRATCH_BYTES it returns SFFN_ERR_TOO_LARGE and
+ * enqueues nothing (16 MiB covers d_ffn = 16384, rank 256, d = 4096 up to 64 tokens, and
+ * d_ffn = 49152, rank 1024, d = 12288 up to 32). The handle must have been created on the
+ * device whose stream is passed. Every call on a device shares that device's one array
+ * and leaves its contents behind: two calls on one device that overlap in time (on
+ * different streams, or from different threads, on any handles) race with each other and
+ * give wrong results; order them on one stream. The look-ahead entry points keep their
+ * state in the workspace and have no static form. */
+int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
+                             int32_t* count, uint64_t* tokmask, float* scores, void* stream);
 
 /* Measurement hook. events: NULL (off) or an array of six hipEvent_t (passed as void*)
  * created by the caller. While set, every sparse_ffn_decode on this handle launches its

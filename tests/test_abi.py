@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -117,6 +117,8 @@ def test_calls_reject_null_handle_and_bad_batch(N):
     assert L.sparse_ffn_compact(None, 0x10000, 1, 0x10000, 0x10000, None, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_forward(None, 0x10000, 1, 0x10000, 0x10000, None, 0x10000, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_decode(None, 0x10000, 1, 0x10000, 0x10000, 0x10000, None, None, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_decode_static(None, 0x10000, 1, 0x10000, 0x10000, 0x10000, None, None,
+                                      None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_destroy(None) == N.SFFN_OK
     assert L.sparse_ffn_set_timing_events(None, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_lookahead_begin(None, 0x10000, None) == N.SFFN_ERR_INVALID
@@ -140,6 +142,7 @@ def test_status_strings(N):
     assert "invalid" in N.sparse_ffn_status_string(-1)
     assert "unsupported" in N.sparse_ffn_status_string(-2)
     assert "HIP" in N.sparse_ffn_status_string(-3)
+    assert "static scratch" in N.sparse_ffn_status_string(-4)
 
 
 def test_permutation_hand_fixture(N):
