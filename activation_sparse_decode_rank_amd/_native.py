@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_ffn.so")
 SFFN_OK, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_ERR_HIP, SFFN_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 SFFN_STATIC_SCRATCH_BYTES = 16 << 20
 SFFN_F32, SFFN_F16 = 0, 1
+SFFN_LAYOUT_SPLIT, SFFN_LAYOUT_BUNDLE = 0, 1
 SFFN_MAX_BATCH = 64
 
 
@@ -26,6 +27,7 @@ class SffnDesc(C.Structure):
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
         ("neuron_freq", C.c_void_p),
         ("deterministic", C.c_int32),
+        ("layout", C.c_int32), ("single_pass", C.c_int32),
     ]
 
 

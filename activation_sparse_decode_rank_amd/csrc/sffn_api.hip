@@ -38,12 +38,16 @@ int check_desc(const sffn_desc* d) {
   if (!dtype_ok(d->w_dtype) || !dtype_ok(d->p_dtype)) return SFFN_ERR_INVALID;
   if (d->d % 8 != 0 || d->rank % 8 != 0) return SFFN_ERR_INVALID;
   if (d->d_ffn > (1 << 24)) return SFFN_ERR_UNSUPPORTED;
+  if (d->layout != SFFN_LAYOUT_SPLIT && d->layout != SFFN_LAYOUT_BUNDLE) return SFFN_ERR_INVALID;
+  if (d->single_pass != 0 && d->single_pass != 1) return SFFN_ERR_INVALID;
   return SFFN_OK;
 }
 
 // workspace may be NULL with workspace_bytes 0: a handle for sparse_ffn_decode_static only
+// bundle layout: the down rows sit inside w_act's bundles and w_down_t must be NULL
 int check_ptrs(const sffn_desc* d) {
-  if (!d->w_act || !d->w_down_t || !d->p1 || !d->p2) return SFFN_ERR_INVALID;
+  if (!d->w_act || !d->p1 || !d->p2) return SFFN_ERR_INVALID;
+  if ((d->layout == SFFN_LAYOUT_BUNDLE) != (d->w_down_t == nullptr)) return SFFN_ERR_INVALID;
   if (!d->workspace && d->workspace_bytes != 0) return SFFN_ERR_INVALID;
   if (!aligned16(d->w_act) || !aligned16(d->w_down_t) || !aligned16(d->p1) ||
       !aligned16(d->p2) || !aligned16(d->workspace))
@@ -155,7 +159,8 @@ const char* sparse_ffn_status_string(int status) {
 
 size_t sparse_ffn_workspace_bytes(const sffn_desc* desc) {
   if (check_desc(desc) != SFFN_OK) return 0;
-  return sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch);
+  return sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch,
+                               desc->single_pass != 0);
 }
 
 int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
@@ -166,7 +171,8 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     rc = check_ptrs(desc);
     if (rc != SFFN_OK) return rc;
     const bool has_ws = desc->workspace != nullptr;
-    const size_t need = sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch);
+    const size_t need = sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch,
+                                              desc->single_pass != 0);
     if (has_ws && desc->workspace_bytes < need) return SFFN_ERR_INVALID;
 
     sffn::LayerDev L{};
@@ -179,12 +185,26 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.tau = desc->threshold;
     L.w_act = desc->w_act;
     L.w_down_t = desc->w_down_t;
+    {
+      // row strides in 16-byte chunks; in the bundle layout neuron i's rows (gate,) up and
+      // down follow each other, and the down rows start after the first bundle's input rows
+      const int nch = desc->d / (desc->w_dtype == SFFN_F16 ? 8 : 4);
+      const int m_in = desc->gated ? 2 : 1;
+      if (desc->layout == SFFN_LAYOUT_BUNDLE) {
+        L.act_ld = L.down_ld = (m_in + 1) * nch;
+        L.w_down_t = static_cast<const char*>(desc->w_act) + (size_t)m_in * nch * 16;
+      } else {
+        L.act_ld = m_in * nch;
+        L.down_ld = nch;
+      }
+    }
+    L.single_pass = desc->single_pass != 0;
     L.b_act = desc->b_act;
     L.b_out = desc->b_out;
     L.p1 = desc->p1;
     L.p2 = desc->p2;
     L.p_bias = desc->p_bias;
-    sffn::carve_workspace(L, desc->workspace, desc->max_batch);
+    sffn::carve_workspace(L, desc->workspace, desc->max_batch, L.single_pass);
     if (!sffn::shape_supported(L, false)) return SFFN_ERR_UNSUPPORTED;
 
     int dev = 0, cus = 0;
@@ -375,7 +395,7 @@ int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y
   if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (!sffn::shape_supported(h->L, true) || h->rs_host.empty()) return SFFN_ERR_UNSUPPORTED;
-  if (sffn::workspace_bytes(h->L.d, h->L.n, h->L.r, B) > sffn::STATIC_SCRATCH_BYTES)
+  if (sffn::workspace_bytes(h->L.d, h->L.n, h->L.r, B, h->L.single_pass) > sffn::STATIC_SCRATCH_BYTES)
     return SFFN_ERR_TOO_LARGE;
   void* base = sffn::static_scratch_ptr(h->device);
   if (!base) return SFFN_ERR_HIP;

@@ -24,7 +24,7 @@ struct Gather {
   static constexpr int NV = GATED ? 2 : 1;
   static constexpr int RED_FLOATS = 4 * RB * TBG * NV;
 
-  __device__ static void run(const void* __restrict__ w_act, const float* xsrc, int d, int n,
+  __device__ static void run(const void* __restrict__ w_act, int ld, const float* xsrc, int d, int n,
                              int B, const int32_t* rows, const uint64_t* bits, const float* bias,
                              const int32_t* outpos, int nrows, float* __restrict__ h_out,
                              float* s_red) {
@@ -38,7 +38,7 @@ struct Gather {
       for (int rr = 0; rr < RB; ++rr) {
         const int ri = rr < nb ? rows[base + rr] : -1;
         if (ri >= 0 && ri < n) {
-          const size_t row0 = (size_t)ri * rowch;
+          const size_t row0 = (size_t)ri * ld;
 #pragma unroll
           for (int m = 0; m < CPT; ++m) {
             const int c = tid + m * TPB;
@@ -132,7 +132,7 @@ struct Gather {
 // [w*per, (w+1)*per) of the given list (per = ceil(count / grid)); h of list position k
 // goes to h_pos[k*B + b].
 template <bool WF16, bool GATED, int CPT, int TBG>
-__global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
+__global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act, int ld_act,
                                                 const float* __restrict__ b_act,
                                                 const float* __restrict__ x, int d, int n, int B,
                                                 const int32_t* __restrict__ idx,
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
       s_pos[u] = kb + u;
     }
     __syncthreads();
-    G::run(w_act, xsrc, d, n, B, s_rows, s_bits, s_bias, s_pos, nr, h_pos, s_red);
+    G::run(w_act, ld_act, xsrc, d, n, B, s_rows, s_bits, s_bias, s_pos, nr, h_pos, s_red);
   }
 }
 
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(TPB) void k_gather(const void* __restrict__ w_act,
 template <bool F16, bool GATED, int CPT, int TBG>
 __global__ __launch_bounds__(TPB) void k_fused_mid(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
-    int r, const void* __restrict__ w_act, const float* __restrict__ b_act,
+    int r, const void* __restrict__ w_act, int ld_act, const float* __restrict__ b_act,
     const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
     uint64_t* __restrict__ wbits, uint64_t* __restrict__ tok_full, float* __restrict__ h_g,
     float* __restrict__ scores, int x_lds, const RangeArg ra) {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(TPB) void k_fused_mid(
   }
   __syncthreads();
   // ---- gather + ReLU over the owned active rows
-  G::run(w_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_bias, s_pos, nact, h_g, s_red);
+  G::run(w_act, ld_act, x_lds ? s_x : x, d, n, B, s_rows, s_bits, s_bias, s_pos, nact, h_g, s_red);
   // token bits and the range's activity word (the range fits in wave 0's 64 lanes) are
   // stored last: the wait that follows a store and a barrier would hold back the gather
   if (tid < nact) tok_full[s_rows[tid]] = s_bits[tid];
@@ -372,7 +372,7 @@ struct DownCfg {
 
 template <bool WF16, bool BITS, int TB, int UPT>
 __global__ __launch_bounds__(TPB) void k_down(
-    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, int B, const int32_t* __restrict__ idx_in,
     const int32_t* __restrict__ count_in, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, const SplitArg sa, const uint64_t* __restrict__ tok_full,
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(TPB) void k_down(
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
           const int ic = (ii[u] >= 0 && ii[u] < n) ? ii[u] : 0;  // out-of-range entries add 0
-          wv[u] = ld_stream(w_down_t, (size_t)ic * nch + chunk);
+          wv[u] = ld_stream(w_down_t, (size_t)ic * ld_down + chunk);
         }
 #pragma unroll
         for (int u = 0; u < LD; ++u) {
@@ -574,11 +574,11 @@ void gather_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
   const int ny = L.ks_down > 1 ? B * L.d : 0;
   if (B == 1)
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 1>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
+                       L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
                        y0, ny);
   else
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 4>), dim3(L.g_gather), dim3(TPB), lds, s,
-                       L.w_act, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
+                       L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
                        y0, ny);
 }
 
@@ -599,7 +599,7 @@ void down_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* 
                    hipStream_t s, const hipEvent_t* tev) {
   const int grid = down_blocks(L) * L.ks_down;
   const size_t lds = BITS ? (size_t)LIST_CAP * 4 : 0;
-  launch(k_down<F16, BITS, TB, UPT>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t, L.b_out,
+  launch(k_down<F16, BITS, TB, UPT>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t, L.down_ld, L.b_out,
          L.h_buf, L.d, L.n, B, idx, count, L.wbits, L.rs, L.sa, L.tok_full, L.ks_down,
          down_blocks(L), idx_out, count_out, tok_out, y);
 }
@@ -612,11 +612,11 @@ void fused_launch(const LayerDev& L, const float* x, int B, float* scores, hipSt
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
   if (B == 1)
     launch(k_fused_mid<F16, GATED, CPT, 1>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
-           L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
+           L.p_bias, L.q, L.r, L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, L.tau,
            L.rs_in_arg ? nullptr : L.rs, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0, L.ra);
   else
     launch(k_fused_mid<F16, GATED, CPT, 4>, dim3(L.g_mid), dim3(TPB), lds, s, tev, L.p2,
-           L.p_bias, L.q, L.r, L.w_act, L.b_act, x, L.d, L.n, B, L.tau,
+           L.p_bias, L.q, L.r, L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, L.tau,
            L.rs_in_arg ? nullptr : L.rs, L.wbits, L.tok_full, L.h_buf, scores, xl ? 1 : 0, L.ra);
 }
 

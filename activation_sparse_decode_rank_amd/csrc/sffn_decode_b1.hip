@@ -106,7 +106,7 @@ __device__ __forceinline__ void mid_scores_b1(const void* __restrict__ p2,
 // h_g[row] = ReLU(W_a[row] . x + b), gated: times W_u[row] . x. first() runs exactly once:
 // after the first rows' loads are issued, or at once when no row is active.
 template <bool F16, bool GATED, int CPT, typename First>
-__device__ __forceinline__ void mid_gather_b1(const void* __restrict__ w_act, int d, int nact,
+__device__ __forceinline__ void mid_gather_b1(const void* __restrict__ w_act, int ld, int d, int nact,
                                               const int32_t* s_rows, const float* s_bias,
                                               const float (&xs)[CPT][Elt<F16>::EPC],
                                               float* __restrict__ h_g, First first) {
@@ -124,7 +124,7 @@ __device__ __forceinline__ void mid_gather_b1(const void* __restrict__ w_act, in
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       if (rr < nb) {
-        const size_t row0 = (size_t)s_rows[base + rr] * rowch;
+        const size_t row0 = (size_t)s_rows[base + rr] * ld;
 #pragma unroll
         for (int m = 0; m < CPT; ++m) gv[rr][m] = ld_stream(w_act, row0 + min(tid + m * TPB, rowch - 1));
       }
@@ -192,9 +192,10 @@ __device__ __forceinline__ void mid_gather_b1(const void* __restrict__ w_act, in
 template <bool F16, bool GATED, int CPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_mid_b1(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
-    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int n, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
-    float* __restrict__ h_g, float* __restrict__ scores, const RangeArg ra) {
+    const void* __restrict__ w_act, int ld_act, const float* __restrict__ b_act,
+    const float* __restrict__ x, int d, int n, float tau, const int32_t* __restrict__ rs,
+    uint64_t* __restrict__ wbits, float* __restrict__ h_g, float* __restrict__ scores,
+    const RangeArg ra) {
   constexpr int EPC = Elt<F16>::EPC;
   constexpr int RMAX = MID_RANGE_MAX;
   __shared__ uint8_t s_act[RMAX];
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
       load_x<EPC>(x + (size_t)min(up ? c - nch : c, nch - 1) * EPC, xs[m]);
     }
   }
-  mid_gather_b1<F16, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, []() {});
+  mid_gather_b1<F16, GATED, CPT>(w_act, ld_act, d, nact, s_rows, s_bias, xs, h_g, []() {});
   // The range's activity word (the range fits in wave 0's 64 lanes) is stored last: the
   // wait that follows a store and a barrier would hold back the gather's loads.
   if (tid == 0) wbits[w] = word;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(TPB) void k_mid_b1(
 template <bool WF16>
 __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
                                              const float* __restrict__ h_in, int n,
-                                             unsigned nch, unsigned chunk, int rsl,
+                                             unsigned ld, unsigned chunk, int rsl,
                                              const int32_t* s_list, int wl,
                                              float (&acc)[Elt<WF16>::EPC]) {
   constexpr int EPC = Elt<WF16>::EPC;
@@ -273,7 +274,7 @@ __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
     for (int u = 0; u < LD; ++u) hv[u] = h_in[ii[u]];
     u32x4 wv[LD];
 #pragma unroll
-    for (int u = 0; u < LD; ++u) wv[u] = ld_stream(w_down_t, (unsigned)ii[u] * nch + chunk);
+    for (int u = 0; u < LD; ++u) wv[u] = ld_stream(w_down_t, (size_t)ii[u] * ld + chunk);
 #pragma unroll
     for (int u = 0; u < LD; ++u) {
       const float h = kb0 + u * RSD + rsl < wl ? hv[u] : 0.f;
@@ -290,7 +291,7 @@ __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
 // it shares with the next layer's scores.
 template <bool WF16, int UPT>
 __device__ __forceinline__ void down_b1_body(
-    int bid, const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    int bid, const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
@@ -349,7 +350,7 @@ __device__ __forceinline__ void down_b1_body(
       }
     }
     __syncthreads();
-    down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, total, acc);
+    down_rows_b1<WF16>(w_down_t, h_in, n, ld_down, chunk, rsl, s_list, total, acc);
   } else {
     // long split: windows of LIST_CAP, each published as it is expanded (global offset first)
     int pc = 0;
@@ -378,7 +379,7 @@ __device__ __forceinline__ void down_b1_body(
           if (tokmask_out) tokmask_out[gbase + wb + k] = 1;
         }
       }
-      down_rows_b1<WF16>(w_down_t, h_in, n, nch, chunk, rsl, s_list, wl, acc);
+      down_rows_b1<WF16>(w_down_t, h_in, n, ld_down, chunk, rsl, s_list, wl, acc);
     }
   }
   // fixed-order reduction of the 32 row slots: lanes l and l+8 of each 16-lane row (DPP,
@@ -428,13 +429,13 @@ __device__ __forceinline__ void down_b1_body(
 
 template <bool WF16, int UPT>
 __global__ __launch_bounds__(TPB) void k_down_b1(
-    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
     float* __restrict__ y, const SplitArg sa) {
   touch_kernargs<2>();
-  down_b1_body<WF16, UPT>(blockIdx.x, w_down_t, b_out, h_in, d, n, wbits, rs, KS, ncb, idx_out,
+  down_b1_body<WF16, UPT>(blockIdx.x, w_down_t, ld_down, b_out, h_in, d, n, wbits, rs, KS, ncb, idx_out,
                           count_out, tokmask_out, y, sa);
 }
 
@@ -464,8 +465,9 @@ __global__ __launch_bounds__(TPB) void k_down_b1(
 template <bool F16, bool GATED, int CPT, int NCPT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
                           amdgpu_waves_per_eu(CPT <= 4 ? 4 : 1))) void k_la_gather(
-    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int gm, const int32_t* __restrict__ rs, const uint64_t* __restrict__ wbits,
+    const void* __restrict__ w_act, int ld_act, const float* __restrict__ b_act,
+    const float* __restrict__ x, int d, int gm, const int32_t* __restrict__ rs,
+    const uint64_t* __restrict__ wbits,
     float* __restrict__ h_g, float* __restrict__ y0, int ny, const void* __restrict__ p1n,
     int rn, float* __restrict__ qn, const RangeArg ra) {
   constexpr int EPC = Elt<F16>::EPC;
@@ -528,7 +530,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
     __syncthreads();
     if (tid == 0) qn[w] = ((s_q[0] + s_q[1]) + s_q[2]) + s_q[3];
   };
-  mid_gather_b1<F16, GATED, CPT>(w_act, d, nact, s_rows, s_bias, xs, h_g, stage1);
+  mid_gather_b1<F16, GATED, CPT>(w_act, ld_act, d, nact, s_rows, s_bias, xs, h_g, stage1);
 }
 
 // ndown workgroups run this layer's down projection (as k_down_b1, which also publishes the
@@ -545,7 +547,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
 constexpr int LA_RPW = 2;
 template <bool F16, int UPT, int NCHP>
 __global__ __launch_bounds__(TPB) void k_la_down(
-    const void* __restrict__ w_down_t, const float* __restrict__ b_out,
+    const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y,
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(TPB) void k_la_down(
   touch_kernargs<2>();
   const int nsc = (gn + LA_RPW - 1) / LA_RPW, bid = blockIdx.x;
   if (sfirst ? bid >= nsc : bid < ndown) {
-    down_b1_body<F16, UPT>(sfirst ? bid - nsc : bid, w_down_t, b_out, h_in, d, n, wbits, rs,
+    down_b1_body<F16, UPT>(sfirst ? bid - nsc : bid, w_down_t, ld_down, b_out, h_in, d, n, wbits, rs,
                             KS, ncb, idx_out, count_out, tokmask_out, y, sa);
     return;
   }
@@ -602,7 +604,7 @@ template <bool F16, bool GATED, int CPT, int NCHP>
 void mid_b1_launch(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                    const hipEvent_t* tev) {
   launch(k_mid_b1<F16, GATED, CPT, NCHP>, dim3(L.g_mid), dim3(TPB), 0, s, tev, L.p2,
-         L.p_bias, L.q, L.w_act, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs,
+         L.p_bias, L.q, L.w_act, L.act_ld, L.b_act, x, L.d, L.n, L.tau, L.rs_in_arg ? nullptr : L.rs,
          L.wbits, L.h_buf, scores, L.ra);
 }
 
@@ -675,7 +677,7 @@ template <bool F16, int UPT>
 void down_b1_launch(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
                     float* y, hipStream_t s, const hipEvent_t* tev) {
   launch(k_down_b1<F16, UPT>, dim3(down_blocks(L) * L.ks_down), dim3(TPB), (size_t)LIST_CAP * 4,
-         s, tev, L.w_down_t, L.b_out, L.h_buf, L.d, L.n, L.wbits, L.rs, L.ks_down,
+         s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.d, L.n, L.wbits, L.rs, L.ks_down,
          down_blocks(L), idx_out, count_out, tok_out, y, L.sa);
 }
 
@@ -704,7 +706,7 @@ void la_gather_launch(const LayerDev& C, const LayerDev* Nx, const float* x, flo
                       hipStream_t s, const hipEvent_t* tev) {
   const int ny = C.ks_down > 1 ? C.d : 0;
   const int grid = std::max(C.g_mid, Nx ? Nx->r : 0);
-  launch(k_la_gather<F16, GATED, CPT, NCPT>, dim3(grid), dim3(TPB), 0, s, tev, C.w_act, C.b_act,
+  launch(k_la_gather<F16, GATED, CPT, NCPT>, dim3(grid), dim3(TPB), 0, s, tev, C.w_act, C.act_ld, C.b_act,
          x, C.d, C.g_mid, C.rs_in_arg ? nullptr : C.rs, C.wbits, C.h_buf, y, ny,
          Nx ? Nx->p1 : nullptr, Nx ? Nx->r : 0, Nx ? Nx->q : nullptr, C.ra);
 }
@@ -747,7 +749,8 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
   SplitArg none{};
   const int sfirst = C && nscore > 0 && ndown + nscore > C->la_occ * C->n_cus ? 1 : 0;
   launch(k_la_down<F16, UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
-         C ? C->w_down_t : nullptr, C ? C->b_out : nullptr, C ? C->h_buf : nullptr,
+         C ? C->w_down_t : nullptr, C ? C->down_ld : 0, C ? C->b_out : nullptr,
+         C ? C->h_buf : nullptr,
          C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
          C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
          Nx ? Nx->p_bias : nullptr, Nx ? Nx->q : nullptr, Nx ? Nx->tau : 0.f,

@@ -9,7 +9,7 @@ static size_t x_hl_bytes(int d, int max_batch) { return (size_t)2 * (d / 8) * ma
 static size_t sk_part_bytes(int max_batch) { return max_batch >= TILE_MIN_B ? SK_PART_BYTES : 0; }
 static size_t sk_cnt_bytes(int n) { return (size_t)((n + 15) / 16 + 1) * 4; }
 
-size_t workspace_bytes(int d, int n, int r, int max_batch) {
+size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass) {
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
   b += align256((size_t)((n + 63) / 64 * 64 + 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
@@ -20,10 +20,11 @@ size_t workspace_bytes(int d, int n, int r, int max_batch) {
   b += align256(x_hl_bytes(d, max_batch));       // x_hl
   b += align256(sk_part_bytes(max_batch));       // sk_part
   b += align256(sk_cnt_bytes(n));                // sk_cnt
+  if (single_pass) b += align256(bundle_part_bytes(d, n));  // part
   return b;
 }
 
-void carve_workspace(LayerDev& L, void* ws, int max_batch) {
+void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass) {
   char* p = static_cast<char*>(ws);
   const int n = L.n;
   const int n_tiles = (n + TPB - 1) / TPB;
@@ -38,6 +39,7 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch) {
   L.x_hl = take(x_hl_bytes(L.d, max_batch));
   L.sk_part = sk_part_bytes(max_batch) ? reinterpret_cast<float*>(take(sk_part_bytes(max_batch))) : nullptr;
   L.sk_cnt = reinterpret_cast<int32_t*>(take(sk_cnt_bytes(n)));
+  L.part = single_pass ? reinterpret_cast<float*>(take(bundle_part_bytes(L.d, n))) : nullptr;
   L.n_tiles = n_tiles;
 }
 
@@ -146,6 +148,12 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     run_forward_tiles(L, x, B, idx, count, tokmask, tokmask ? nullptr : L.tok_full, y, false,
                       fw, s, t2, t3);
     return hipGetLastError();
+  }
+  if (B == 1 && L.single_pass && bundle_ok(L)) {
+    // one pass over the active neurons' bundles writes partial outputs; the reduction
+    // writes all of y, so stage 1 clears nothing
+    run_stage1(L, x, 1, s, t1, nullptr, 0, true, false);
+    if (run_bundle_b1(L, x, y, idx, count, tokmask, scores, s, t2, t3)) return hipGetLastError();
   }
   run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true, false);
   if (B == 1 && run_mid_b1(L, x, scores, s, t2)) {

@@ -36,6 +36,8 @@ struct LayerDev {
   float tau;
   const void* w_act;
   const void* w_down_t;
+  int act_ld;   // 16-byte chunks from one neuron's ReLU-input row(s) to the next neuron's
+  int down_ld;  // the same for the rows of w_down_t (both larger in the bundle layout)
   const float* b_act;
   const float* b_out;
   const void* p1;
@@ -50,6 +52,7 @@ struct LayerDev {
   void* x_hl;          // tokens split into fp16 hi/lo for the matrix-core up projection:
                        // 2 x [d/8 chunks][B token slots] x 16 bytes (sized for max_batch)
   uint64_t* wbits;     // [G_MID_MAX] activity word of each middle-kernel range (decode)
+  float* part;         // single-pass decode: partial outputs of its workgroups (null: unused)
   float* sk_part;      // stream-K up projection: two part slots per workgroup (null: unused)
   int32_t* sk_cnt;     // [ceil(n/16) + 1] arrival counters of its tiles (zero between calls)
   // launch geometry fixed at create time
@@ -68,11 +71,13 @@ struct LayerDev {
   SplitArg sa;     // decode down projection: range splits, ks_down of them
   int split_upt;   // most ranges of one split per thread of the down kernel (1, 2, 4, 8)
   int la_occ;      // workgroups per compute unit of the look-ahead down launch (0: unknown)
+  bool single_pass;  // single-token decode through the bundle pass (sffn_bundle.hip)
 };
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
-size_t workspace_bytes(int d, int n, int r, int max_batch);
-void carve_workspace(LayerDev& L, void* ws, int max_batch);
+// (single_pass: also the partial outputs of the single-pass decode)
+size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass);
+void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass);
 // 128-byte column blocks of the down projection, and the row split it should use
 int down_blocks(const LayerDev& L);
 int down_split(const LayerDev& L, bool deterministic);
@@ -184,6 +189,16 @@ void* static_scratch_ptr(int dev);
 hipError_t run_decode_static(const LayerDev& H, const int32_t* rs_host, int g, void* base,
                              const float* x, int B, float* y, int32_t* idx, int32_t* count,
                              uint64_t* tokmask, float* scores, hipStream_t s);
+// sffn_bundle.hip: the single-token decode in one pass over each active neuron's bundle
+// (input rows and down row together), then a fixed-order reduction of the workgroups'
+// partial outputs that also publishes the list. ok: kernels exist for the shape; run:
+// after stage 1, false when they do not (t_pass, t_reduce: optional event pairs).
+constexpr int BUNDLE_RANGES_PER_GROUP = 4;
+bool bundle_ok(const LayerDev& L);
+bool run_bundle_b1(const LayerDev& L, const float* x, float* y, int32_t* idx, int32_t* count,
+                   uint64_t* tok, float* scores, hipStream_t s, const hipEvent_t* t_pass,
+                   const hipEvent_t* t_reduce);
+size_t bundle_part_bytes(int d, int n);
 // sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
 // number of workgroups; sink [workgroups] is written only in a practically impossible case
 hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink,

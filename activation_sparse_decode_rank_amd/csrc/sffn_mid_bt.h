@@ -19,8 +19,9 @@ namespace {
 template <bool F16, bool GATED, int CX, int NCHP, int BT>
 __global__ __launch_bounds__(TPB) void k_mid_bt(
     const void* __restrict__ p2, const float* __restrict__ pbias, const float* __restrict__ q,
-    const void* __restrict__ w_act, const float* __restrict__ b_act, const float* __restrict__ x,
-    int d, int n, int B, float tau, const int32_t* __restrict__ rs, uint64_t* __restrict__ wbits,
+    const void* __restrict__ w_act, int ld_act, const float* __restrict__ b_act,
+    const float* __restrict__ x, int d, int n, int B, float tau, const int32_t* __restrict__ rs,
+    uint64_t* __restrict__ wbits,
     uint64_t* __restrict__ tok_full, float* __restrict__ h_g, float* __restrict__ scores,
     const RangeArg ra) {
   constexpr int EPC = Elt<F16>::EPC;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(TPB) void k_mid_bt(
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       if (rr < nb) {
-        const size_t row0 = (size_t)s_rows[base + rr] * (NV * nch);
+        const size_t row0 = (size_t)s_rows[base + rr] * ld_act;
 #pragma unroll
         for (int m = 0; m < CX; ++m) {
           const int c = min(tid + m * TPB, nch - 1);
@@ -208,7 +209,7 @@ template <bool F16, bool GATED, int CX, int NCHP, int BT>
 void mid_bt_launch(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s,
                    const hipEvent_t* tev) {
   launch(k_mid_bt<F16, GATED, CX, NCHP, BT>, dim3(L.g_mid), dim3(TPB), 0, s, tev, L.p2, L.p_bias,
-         L.q, L.w_act, L.b_act, x, L.d, L.n, B, L.tau, L.rs_in_arg ? nullptr : L.rs, L.wbits,
+         L.q, L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, L.tau, L.rs_in_arg ? nullptr : L.rs, L.wbits,
          L.tok_full, L.h_buf, scores, L.ra);
 }
 

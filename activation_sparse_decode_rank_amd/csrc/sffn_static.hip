@@ -55,7 +55,7 @@ hipError_t run_decode_static(const LayerDev& H, const int32_t* rs_host, int g, v
                              const float* x, int B, float* y, int32_t* idx, int32_t* count,
                              uint64_t* tokmask, float* scores, hipStream_t s) {
   LayerDev L = H;
-  carve_workspace(L, base, B);
+  carve_workspace(L, base, B, H.single_pass);
   const int ncnt = (L.n + 15) / 16 + 1;
   for (int off = 0; off <= g; off += RS_ARG_MAX + 1) {
     const int cnt = std::min(RS_ARG_MAX + 1, g + 1 - off);

@@ -273,7 +273,7 @@ constexpr int FW_WORDS_MAX = 1024;  // union words the up kernel can list itself
 // their successor's prefix and are never chosen). The positions of its own tiles are
 // written to idx, with their token bits; workgroup 0 writes the count.
 template <bool GATED, int NT, int TR, int W, bool FW>
-__global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_act,
+__global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_act, int ld_act,
                                                     const float* __restrict__ b_act,
                                                     const u32x4* __restrict__ x_hl, int d,
                                                     int n, int B, int32_t* __restrict__ idx,
@@ -344,7 +344,6 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     cnt = min(max(cnt_raw, 0), n);
   }
   const int nch = d / 8;                 // chunks per matrix row
-  const int rowch = NM * nch;
   const int qch = nch / W;               // this wave's chunks of each row
   const int npairs = qch / 8;            // its 64-input step pairs
   const int c0 = wave * qch;
@@ -407,8 +406,8 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
     const u32x4* pb[TR];
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
-      pa[i] = wbase + (size_t)((ia[i] >= 0 && ia[i] < n) ? ia[i] : 0) * rowch + c0 + lc;
-      pb[i] = wbase + (size_t)((ib[i] >= 0 && ib[i] < n) ? ib[i] : 0) * rowch + c0 + lc;
+      pa[i] = wbase + (size_t)((ia[i] >= 0 && ia[i] < n) ? ia[i] : 0) * ld_act + c0 + lc;
+      pb[i] = wbase + (size_t)((ib[i] >= 0 && ib[i] < n) ? ib[i] : 0) * ld_act + c0 + lc;
     }
     float4_t acc[TR][NM][NT];
 #pragma unroll
@@ -585,7 +584,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 constexpr int SK_TMAX = 16;   // tiles one range may touch (listed in LDS at once)
 constexpr int SK_PMAX = 3;    // parts of one tile
 template <bool GATED, int NT, int TR, int W>
-__global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act,
+__global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act, int ld_act,
                                                   const float* __restrict__ b_act,
                                                   const u32x4* __restrict__ x_hl, int d,
                                                   int n, int B, int32_t* __restrict__ idx,
@@ -645,7 +644,7 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
   const int cnt = min(total, n);
   __syncthreads();
   // ---- this workgroup's range of blocks
-  const int nch = d / 8, rowch = NM * nch;
+  const int nch = d / 8;
   const int KBT = nch / (16 * W);
   const int ntiles = (cnt + RT - 1) / RT;
   const long long T = (long long)ntiles * KBT;
@@ -698,8 +697,8 @@ __global__ __launch_bounds__(64 * W) void k_up_sk(const void* __restrict__ w_act
     for (int i = 0; i < TR; ++i) {
       const int ra = s_rows[(t - t_first) * RT + 16 * i + lr];
       const int rb = s_rows[(t - t_first) * RT + 16 * i + 8 + lr];
-      pa[i] = wbase + (size_t)((ra >= 0 && ra < n) ? ra : 0) * rowch + lc;
-      pb[i] = wbase + (size_t)((rb >= 0 && rb < n) ? rb : 0) * rowch + lc;
+      pa[i] = wbase + (size_t)((ra >= 0 && ra < n) ? ra : 0) * ld_act + lc;
+      pb[i] = wbase + (size_t)((rb >= 0 && rb < n) ? rb : 0) * ld_act + lc;
     }
   };
   u32x4 wa[2][TR][NM], wb[2][TR][NM], xv[2][2][NT][2];
@@ -929,7 +928,7 @@ __global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, in
 constexpr int DCH = 32;         // positions per chunk (one k-step)
 constexpr int IDX_CAP = 4096;   // list window held in LDS (a multiple of DCH)
 template <int NT>
-__global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_down_t,
+__global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_down_t, int ld_down,
                                                    const float* __restrict__ b_out,
                                                    const float* __restrict__ hT, int ldh, int d,
                                                    int n, int B, const int32_t* __restrict__ idx,
@@ -993,7 +992,7 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = s_idx[min(pc + lr + 8 * j, wl - 1)];
-          wv[bb][kb][j] = ld_stream(wcol, (size_t)((i >= 0 && i < n) ? i : 0) * nch);
+          wv[bb][kb][j] = ld_stream(wcol, (size_t)((i >= 0 && i < n) ? i : 0) * ld_down);
         }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -1149,11 +1148,11 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
   int32_t* cnt_w = const_cast<int32_t*>(count);
   uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
   if (fw)
-    launch(k_up_mfma<GATED, NT, TR, W, true>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act,
+    launch(k_up_mfma<GATED, NT, TR, W, true>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
            L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
            (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny);
   else
-    launch(k_up_mfma<GATED, NT, TR, W, false>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act,
+    launch(k_up_mfma<GATED, NT, TR, W, false>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
            L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
            (const uint64_t*)nullptr, tok_by_neuron, L.h_buf, L.ldh, y0, ny);
 }
@@ -1168,7 +1167,7 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
 template <bool GATED, int NT, int TR, int W>
 void up_sk_launch(const LayerDev& L, int B, int32_t* idx, int32_t* count, uint64_t* tokmask,
                   float* y0, int ny, hipStream_t s, const hipEvent_t* tev, int grid) {
-  launch(k_up_sk<GATED, NT, TR, W>, dim3(grid), dim3(64 * W), 0, s, tev, L.w_act, L.b_act,
+  launch(k_up_sk<GATED, NT, TR, W>, dim3(grid), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld, L.b_act,
          static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx, count, tokmask,
          (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny,
          L.sk_part, L.sk_cnt);
@@ -1220,10 +1219,10 @@ void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_
                       float* y, hipStream_t s, const hipEvent_t* tev) {
   const dim3 grid(((L.d + 63) / 64) * L.ks_tile);
   switch ((B + 15) / 16) {
-    case 1: launch(k_down_mfma<1>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 2: launch(k_down_mfma<2>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 3: launch(k_down_mfma<3>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    default: launch(k_down_mfma<4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 1: launch(k_down_mfma<1>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 2: launch(k_down_mfma<2>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 3: launch(k_down_mfma<3>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    default: launch(k_down_mfma<4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
   }
 }
 

@@ -74,12 +74,18 @@ class SparseFFN:
     hottest ceil(hot_frac * n) packed first, and their frequencies balance the work split.
     deterministic: keep y bitwise reproducible from run to run (slightly slower down
     projection); otherwise the fastest split, whose y may vary in the last bits.
+    bundle: store each neuron's rows together ([gate,] up, down: one [n, m, d] tensor, the
+    PowerInfer-2 neuron bundle) instead of separate matrices.
+    single_pass: the single-token decode gathers each active neuron's input and down rows in
+    one pass and adds the workgroups' partial outputs in a fixed order (y bitwise
+    reproducible); shapes it does not cover fall back to the three-launch path.
     """
 
     def __init__(self, *, w_act, w_down_t, p1, p2, b_act=None, b_out=None, p_bias=None,
                  w_up=None, threshold: float = 0.0, max_batch: int = 1,
                  profile_x: Optional[torch.Tensor] = None, hot_frac: float = 0.2,
-                 perm: Optional[np.ndarray] = None, deterministic: bool = False, stream=None):
+                 perm: Optional[np.ndarray] = None, deterministic: bool = False,
+                 bundle: bool = False, single_pass: bool = False, stream=None):
         dev = w_act.device
         if dev.type != "cuda":
             raise ValueError("SparseFFN needs device tensors")
@@ -107,14 +113,25 @@ class SparseFFN:
         perm_dev = torch.from_numpy(self.perm).to(dev)
 
         # packed copies, made by the library's row-gather kernel
-        if self.gated:
-            eb = w_act.element_size()
-            self.w_act = torch.empty((n, 2, d), dtype=w_act.dtype, device=dev)
-            pack_rows(w_act, perm_dev, self.w_act, 0, 2 * d * eb, stream)
-            pack_rows(w_up, perm_dev, self.w_act, d * eb, 2 * d * eb, stream)
+        eb = w_act.element_size()
+        self.bundle = bool(bundle)
+        if self.bundle:
+            # neuron i's rows side by side: [gate,] up, down
+            rows = [w_act, w_up, w_down_t] if self.gated else [w_act, w_down_t]
+            m = len(rows)
+            self.w_act = torch.empty((n, m, d), dtype=w_act.dtype, device=dev)
+            for k, src in enumerate(rows):
+                pack_rows(src, perm_dev, self.w_act, k * d * eb, m * d * eb, stream)
+            self.w_down_t = None
         else:
-            self.w_act = pack_rows(w_act, perm_dev, stream=stream)
-        self.w_down_t = pack_rows(w_down_t, perm_dev, stream=stream)
+            if self.gated:
+                self.w_act = torch.empty((n, 2, d), dtype=w_act.dtype, device=dev)
+                pack_rows(w_act, perm_dev, self.w_act, 0, 2 * d * eb, stream)
+                pack_rows(w_up, perm_dev, self.w_act, d * eb, 2 * d * eb, stream)
+            else:
+                self.w_act = pack_rows(w_act, perm_dev, stream=stream)
+            self.w_down_t = pack_rows(w_down_t, perm_dev, stream=stream)
+        self.single_pass = bool(single_pass)
         self.p2 = pack_rows(p2, perm_dev, stream=stream)
         self.b_act = None if b_act is None else pack_rows(b_act.contiguous(), perm_dev, stream=stream)
         self.p_bias = None if p_bias is None else pack_rows(p_bias.contiguous(), perm_dev, stream=stream)
@@ -139,6 +156,8 @@ class SparseFFN:
         D.w_dtype, D.p_dtype = self._w_dtype, self._p_dtype
         D.threshold = self.threshold
         D.deterministic = int(self.deterministic)
+        D.layout = N.SFFN_LAYOUT_BUNDLE if self.bundle else N.SFFN_LAYOUT_SPLIT
+        D.single_pass = int(self.single_pass)
         D.w_act, D.w_down_t = _ptr(self.w_act), _ptr(self.w_down_t)
         D.b_act, D.b_out = _ptr(self.b_act), _ptr(self.b_out)
         D.p1, D.p2, D.p_bias = _ptr(self.p1), _ptr(self.p2), _ptr(self.p_bias)
@@ -152,13 +171,15 @@ class SparseFFN:
         D.neuron_freq = None
 
     def clone(self, *, threshold: Optional[float] = None, deterministic: Optional[bool] = None,
-              max_batch: Optional[int] = None) -> "SparseFFN":
+              max_batch: Optional[int] = None, single_pass: Optional[bool] = None) -> "SparseFFN":
         """Another handle over the same packed weights (no copy), with its own workspace and
         the given threshold, mode or batch limit (default: this layer's). For example
         threshold=-inf lists every neuron: the library's own dense FFN."""
         c = object.__new__(SparseFFN)
         c.__dict__.update({k: v for k, v in self.__dict__.items()
                            if k not in ("handle", "desc", "workspace")})
+        if single_pass is not None:
+            c.single_pass = bool(single_pass)
         c._create(self.threshold if threshold is None else threshold,
                   self.deterministic if deterministic is None else deterministic,
                   self.max_batch if max_batch is None else max_batch)

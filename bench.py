@@ -275,7 +275,7 @@ def read_probe(torch, NAT, reps=10):
                     "8 workgroups per compute unit"}
 
 
-def build_stack(cfg, B, L, args, keep_originals):
+def build_stack(cfg, B, L, args, keep_originals, **kw):
     import torch
 
     from activation_sparse_decode_rank_amd import SparseFFN
@@ -287,7 +287,7 @@ def build_stack(cfg, B, L, args, keep_originals):
         Lt = make_layer(cfg, src_layer, "cuda")
         s = SparseFFN(w_act=Lt.w_a, w_up=Lt.w_u, w_down_t=Lt.w_o, p1=Lt.p1, p2=Lt.p2,
                       b_act=Lt.b_a, b_out=Lt.b_o, p_bias=Lt.c, max_batch=B, profile_x=Xprof,
-                      hot_frac=cfg.hot_frac)
+                      hot_frac=cfg.hot_frac, **kw)
         layers.append(s)
         originals.append(Lt if keep_originals(l) else None)
         del Lt
@@ -537,7 +537,7 @@ def main():
 
     # ------------------------------------------------------------------ extra legs
     dense_bytes = (n * d * (3 if cfg.gated else 2)) * cfg.w_bytes
-    all_active = deterministic = quality = None
+    all_active = deterministic = quality = single_pass = None
     if not args.no_extra:
         # the library's own dense FFN: every neuron listed (threshold -inf), same weights
         dense_layers = [s.clone(threshold=float("-inf")) for s in layers]
@@ -559,6 +559,15 @@ def main():
                          "layer_us_percentiles": percentiles_us(de_per, L)}
         log(f"deterministic mode: {de_us:.3f} us/layer")
         del det_layers
+        # the single-pass decode (gather and down rows in one pass, fixed-order reduction)
+        if B == 1:
+            sp_layers = [s.clone(single_pass=True) for s in layers]
+            sp_ms, sp_per = timer.run(step(sp_layers))
+            sp_us = sp_ms * 1000.0 / L
+            single_pass = {"split_layout_us_per_layer": round(sp_us, 3),
+                           "speedup_vs_metric_path": round(us_per_layer / sp_us, 4)}
+            log(f"single pass (split layout): {sp_us:.3f} us/layer")
+            del sp_layers
         # predictor recall / precision against the true ReLU signs on sampled steps
         tp = fp = fn = 0
         ns = min(8, T)
@@ -587,6 +596,43 @@ def main():
                    "note": "synthetic calibrated random-subspace predictor (no trained "
                            "predictor exists here): a diagnostic, not graded"}
         log(f"predictor recall {quality['recall']}, precision {quality['precision']}")
+
+    # the single-pass decode over neuron bundles: its own packed copy of the stack
+    if single_pass is not None:
+        bl, _ = build_stack(cfg, B, L, args, lambda l: False, bundle=True, single_pass=True)
+        bu_ms, bu_per = timer.run(step(bl))
+        bu_us = bu_ms * 1000.0 / L
+        KT2 = min(args.kernel_tokens, T)
+        bev = HipEvents(6 * KT2 * L)
+        for t in range(KT2):
+            for l in range(L):
+                base = 6 * (t * L + l)
+                NAT.sparse_ffn_set_timing_events(bl[l].handle, bev.ev[base:base + 6])
+                bl[l].decode(X[t, l], y=y_buf[l], idx=idx_buf[l], count=counts[t, l:l + 1],
+                             tokmask=tok_buf[l])
+                NAT.sparse_ffn_set_timing_events(bl[l].handle, None)
+        torch.cuda.synchronize()
+        bk = {}
+        for j, k in enumerate(("stage1", "bundle_pass", "reduce")):
+            bk[k] = round(float(np.mean([1000.0 * bev.elapsed_ms(6 * i + 2 * j, 6 * i + 2 * j + 1)
+                                         for i in range(KT2 * L)])), 3)
+        bev.close()
+        pass_bytes = [n * r * cfg.p_bytes + 8 * n + 4 * r + 4 * d
+                      + int(cnt[t, l]) * (cfg.m * d * cfg.w_bytes + 8) for t in range(KT2)
+                      for l in range(L)]
+        pb_mean = float(np.mean(pass_bytes))
+        single_pass.update({
+            "bundle_layout_us_per_layer": round(bu_us, 3),
+            "bundle_speedup_vs_metric_path": round(us_per_layer / bu_us, 4),
+            "bundle_layer_us_percentiles": percentiles_us(bu_per, L),
+            "kernel_us": bk,
+            "bundle_pass_algorithmic_bytes": int(pb_mean),
+            "bundle_pass_gbps": round(pb_mean / (bk["bundle_pass"] * 1e-6) / 1e9, 1),
+            "impl": "stage 1, then k_bundle_b1 (scores, threshold, compaction, and each active "
+                    "neuron's input and down rows in one batch of loads; partial outputs of four "
+                    "ranges per workgroup), then k_bundle_reduce (fixed-order sum + list)"})
+        log(f"single pass (bundle layout): {bu_us:.3f} us/layer; kernels {bk}")
+        del bl
 
     # ------------------------------------------------------------------ dense baseline
     dense = None
@@ -735,6 +781,7 @@ def main():
         "roofline": roof,
         "hbm_read_probe": probe,
         "deterministic": deterministic,
+        "single_pass": single_pass,
         "predictor_quality": quality,
         "cpu_baseline": cpu,
         "lookahead": lookahead,

@@ -75,6 +75,17 @@ enum {
 
 typedef enum { SFFN_F32 = 0, SFFN_F16 = 1 } sffn_dtype;
 
+/* Weight layouts (sffn_desc.layout).
+ * SFFN_LAYOUT_SPLIT:  w_act and w_down_t are separate arrays, as described above.
+ * SFFN_LAYOUT_BUNDLE: each neuron's rows are stored together, as one bundle: w_act is
+ *   [d_ffn][m][d] with m = 2 (plain: up row, down row) or 3 (gated: gate row, up row, down
+ *   row), and w_down_t is NULL. Gate, up and down rows of a neuron are used together, so
+ *   PowerInfer-2 stores them together and reads them in one I/O (PowerInfer-2 article,
+ *   section 4.4 Neuron-Cluster-Level Pipeline). Every entry point accepts either layout
+ *   with the same results; the single-pass decode (sffn_desc.single_pass) reads a neuron's
+ *   bundle in one batch of loads. */
+typedef enum { SFFN_LAYOUT_SPLIT = 0, SFFN_LAYOUT_BUNDLE = 1 } sffn_layout;
+
 /* Largest batch: one bit per token in the 64-bit membership words. */
 #define SFFN_MAX_BATCH 64
 
@@ -96,7 +107,7 @@ typedef struct {
   int32_t p_dtype;    /* sffn_dtype of p1 and p2 */
   float threshold;    /* tau: neuron i is active for a token iff its score > tau (strict; NaN inactive) */
   const void* w_act;     /* device, see layout above */
-  const void* w_down_t;  /* device, [d_ffn][d] */
+  const void* w_down_t;  /* device, [d_ffn][d]; NULL in the bundle layout */
   const float* b_act;    /* device [d_ffn]: bias inside the ReLU (b_up, or b_gate); NULL = 0 */
   const float* b_out;    /* device [d]: output bias; NULL = 0 */
   const void* p1;        /* device [rank][d] */
@@ -116,6 +127,21 @@ typedef struct {
                                0: fastest (its row splits add into y with float atomics,
                                so the last bits of y can vary between runs). Index lists,
                                counts and token bits are bit-exact either way. */
+  int32_t layout;           /* sffn_layout: SFFN_LAYOUT_SPLIT (0) or SFFN_LAYOUT_BUNDLE (1) */
+  int32_t single_pass;      /* 1: the single-token decode (sparse_ffn_decode at B = 1, and its
+                               static form) gathers each active neuron's input rows and down
+                               row in one pass, keeps a partial output per workgroup and adds
+                               the partials in a fixed order in a second launch (no float
+                               atomics: y is bitwise reproducible whatever `deterministic`
+                               says), where the layer's shape allows (weights and predictor
+                               of one type, rank 64 to 512 in fp16 or 32 to 256 in fp32,
+                               d <= 4096 in fp16 or 2048 in fp32; otherwise the three-launch
+                               path runs). The workspace then also holds the partials (about
+                               d * 4 bytes per four neuron ranges). 0: the three-launch path
+                               (middle kernel, then a down projection that finds the active
+                               rows again). Lists, counts, token bits and scores are the same
+                               either way; y agrees to rounding. Operator fusion: novita.ai
+                               activation-sparsity article, section 工程影響. */
 } sffn_desc;
 
 /* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The

@@ -32,7 +32,7 @@ def rel_err_rows(y, ref):
 
 def build(cfg, layer=0, *, d=None, n=None, rank=None, activity=None, max_batch=1,
           nonzero_b_o=True, profile_tokens=256, hot_frac=None, threshold=0.0, pack=True,
-          gen_device="cuda", deterministic=False):
+          gen_device="cuda", deterministic=False, bundle=False, single_pass=False):
     """Generate a layer (original order) and a SparseFFN over it; returns (sffn, L_np, Lt)."""
     from activation_sparse_decode_rank_amd import SparseFFN
     from synth import make_layer, make_tokens
@@ -43,7 +43,7 @@ def build(cfg, layer=0, *, d=None, n=None, rank=None, activity=None, max_batch=1
     s = SparseFFN(w_act=Lt.w_a, w_up=Lt.w_u, w_down_t=Lt.w_o, p1=Lt.p1, p2=Lt.p2, b_act=Lt.b_a,
                   b_out=Lt.b_o, p_bias=Lt.c, threshold=threshold, max_batch=max_batch,
                   profile_x=Xp, hot_frac=cfg.hot_frac if hot_frac is None else hot_frac,
-                  deterministic=deterministic)
+                  deterministic=deterministic, bundle=bundle, single_pass=single_pass)
     torch.cuda.synchronize()
     return s, Lt.numpy(), Lt
 
