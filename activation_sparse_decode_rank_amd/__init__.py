@@ -7,7 +7,7 @@ from . import _native  # noqa: F401  (raises ImportError when the library is mis
 from ._native import (  # noqa: F401
     EXPORTED, SFFN_ERR_HIP, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_F16, SFFN_F32,
     SFFN_MAX_BATCH, SFFN_OK, SffnDesc, SparseFFNError, sparse_ffn_compact, sparse_ffn_create,
-    sparse_ffn_decode, sparse_ffn_decode_lookahead, sparse_ffn_destroy, sparse_ffn_forward,
+    sparse_ffn_decode, sparse_ffn_decode_lookahead, sparse_ffn_decode_static, sparse_ffn_dense, sparse_ffn_destroy, sparse_ffn_forward,
     sparse_ffn_lookahead_begin, sparse_ffn_pack_rows,
     sparse_ffn_permutation, sparse_ffn_predict, sparse_ffn_profile_counts, sparse_ffn_read_probe,
     sparse_ffn_set_timing_events,

@@ -27,7 +27,7 @@ class SffnDesc(C.Structure):
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
         ("neuron_freq", C.c_void_p),
         ("deterministic", C.c_int32),
-        ("layout", C.c_int32), ("single_pass", C.c_int32),
+        ("layout", C.c_int32), ("single_pass", C.c_int32), ("dense_union", C.c_float),
     ]
 
 
@@ -53,6 +53,7 @@ def _load():
         "sparse_ffn_forward": (C.c_int, [P, P, I32, P, P, P, P, P]),
         "sparse_ffn_decode": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
         "sparse_ffn_decode_static": (C.c_int, [P, P, I32, P, P, P, P, P, P]),
+        "sparse_ffn_dense": (C.c_int, [P, P, I32, P, P]),
         "sparse_ffn_lookahead_begin": (C.c_int, [P, P, P]),
         "sparse_ffn_decode_lookahead": (C.c_int, [P, P, P, P, P, P, P, P]),
         "sparse_ffn_status_string": (C.c_char_p, [C.c_int]),
@@ -72,7 +73,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destroy",
             "sparse_ffn_predict", "sparse_ffn_compact", "sparse_ffn_forward", "sparse_ffn_decode",
-            "sparse_ffn_decode_static",
+            "sparse_ffn_decode_static", "sparse_ffn_dense",
             "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
@@ -120,6 +121,10 @@ def sparse_ffn_forward(h, x, B, idx, count, tokmask, y, stream) -> None:
 
 def sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream) -> None:
     _ck(_lib.sparse_ffn_decode(h, x, B, y, idx, count, tokmask, scores, stream), "sparse_ffn_decode")
+
+
+def sparse_ffn_dense(h, x, B, y, stream) -> None:
+    _ck(_lib.sparse_ffn_dense(h, x, B, y, stream), "sparse_ffn_dense")
 
 
 def sparse_ffn_decode_static(h, x, B, y, idx, count, tokmask, scores, stream) -> None:

@@ -40,6 +40,7 @@ int check_desc(const sffn_desc* d) {
   if (d->d_ffn > (1 << 24)) return SFFN_ERR_UNSUPPORTED;
   if (d->layout != SFFN_LAYOUT_SPLIT && d->layout != SFFN_LAYOUT_BUNDLE) return SFFN_ERR_INVALID;
   if (d->single_pass != 0 && d->single_pass != 1) return SFFN_ERR_INVALID;
+  if (!(d->dense_union >= 0.f && d->dense_union <= 1.f)) return SFFN_ERR_INVALID;
   return SFFN_OK;
 }
 
@@ -199,6 +200,25 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
       }
     }
     L.single_pass = desc->single_pass != 0;
+    L.max_batch = desc->max_batch;
+    // the dense route from the smallest batch whose expected union of predicted sets (the
+    // neurons' profile frequencies f_i, tokens independent: 1 - mean_i (1 - f_i)^B) exceeds
+    // dense_union; 0 (or no frequencies) = never
+    L.dense_from_b = SFFN_MAX_BATCH + 1;
+    if (desc->dense_union > 0.f && desc->neuron_freq) {
+      for (int b = 1; b <= desc->max_batch; ++b) {
+        double u = 0.0;
+        for (int i = 0; i < desc->d_ffn; ++i) {
+          double f = desc->neuron_freq[i];
+          f = f > 0.0 ? (f < 1.0 ? f : 1.0) : 0.0;
+          u += 1.0 - std::pow(1.0 - f, (double)b);
+        }
+        if (u / desc->d_ffn > (double)desc->dense_union) {
+          L.dense_from_b = b;
+          break;
+        }
+      }
+    }
     L.b_act = desc->b_act;
     L.b_out = desc->b_out;
     L.p1 = desc->p1;
@@ -386,6 +406,15 @@ int sparse_ffn_decode_lookahead(sparse_ffn_t cur, sparse_ffn_t next, const float
   return sffn::run_lookahead(cur->L, next ? &next->L : nullptr, x, y, idx, count, tokmask,
                              static_cast<hipStream_t>(stream), cur->timing ? cur->ev : nullptr) ==
                  hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_dense(sparse_ffn_t h, const float* x, int32_t B, float* y, void* stream) {
+  if (!h || !x || !y || B < 1) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
+  if (!h->has_ws) return SFFN_ERR_INVALID;
+  return sffn::launch_dense(h->L, x, B, y, static_cast<hipStream_t>(stream)) == hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;
 }

@@ -21,6 +21,7 @@ size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass) {
   b += align256(sk_part_bytes(max_batch));       // sk_part
   b += align256(sk_cnt_bytes(n));                // sk_cnt
   if (single_pass) b += align256(bundle_part_bytes(d, n));  // part
+  b += align256((size_t)(n + 1) * 4);            // dense_idx
   return b;
 }
 
@@ -40,6 +41,7 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass) {
   L.sk_part = sk_part_bytes(max_batch) ? reinterpret_cast<float*>(take(sk_part_bytes(max_batch))) : nullptr;
   L.sk_cnt = reinterpret_cast<int32_t*>(take(sk_cnt_bytes(n)));
   L.part = single_pass ? reinterpret_cast<float*>(take(bundle_part_bytes(L.d, n))) : nullptr;
+  L.dense_idx = reinterpret_cast<int32_t*>(take((size_t)(n + 1) * 4));
   L.n_tiles = n_tiles;
 }
 
@@ -116,9 +118,35 @@ hipError_t launch_forward(const LayerDev& L, const float* x, int B, const int32_
   return hipGetLastError();
 }
 
+// Every neuron of the layer for B tokens (any B): the identity list, then the forward
+// entry point's kernels over it, in chunks of the tokens the workspace holds.
+hipError_t launch_dense(const LayerDev& L, const float* x, int B, float* y, hipStream_t s) {
+  hipError_t e = launch_fill_list(L, 0, L.dense_idx, L.dense_idx + L.n, nullptr, s);
+  if (e != hipSuccess) return e;
+  const int chunk = std::min(L.max_batch, MAXB);
+  for (int b0 = 0; b0 < B; b0 += chunk) {
+    const int bc = std::min(chunk, B - b0);
+    e = launch_forward(L, x + (size_t)b0 * L.d, bc, L.dense_idx, L.dense_idx + L.n, nullptr,
+                       y + (size_t)b0 * L.d, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int32_t* idx,
                          int32_t* count, uint64_t* tokmask, float* scores, hipStream_t s,
                          const hipEvent_t* ev) {
+  if (B >= L.dense_from_b) {
+    // above the crossover: every neuron for every token (the published list says so); the
+    // predictor runs only when its scores are asked for
+    if (scores) {
+      hipError_t e = launch_predict(L, x, B, scores, s);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_fill_list(L, B, idx, count, tokmask, s);
+    if (e != hipSuccess) return e;
+    return launch_forward(L, x, B, idx, count, tokmask, y, s);
+  }
   const hipEvent_t* t1 = ev ? ev + 0 : nullptr;
   const hipEvent_t* t2 = ev ? ev + 2 : nullptr;
   const hipEvent_t* t3 = ev ? ev + 4 : nullptr;

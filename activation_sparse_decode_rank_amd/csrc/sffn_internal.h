@@ -72,6 +72,9 @@ struct LayerDev {
   int split_upt;   // most ranges of one split per thread of the down kernel (1, 2, 4, 8)
   int la_occ;      // workgroups per compute unit of the look-ahead down launch (0: unknown)
   bool single_pass;  // single-token decode through the bundle pass (sffn_bundle.hip)
+  int max_batch;     // tokens the workspace is sized for
+  int dense_from_b;  // decode computes every neuron from this many tokens on (65: never)
+  int32_t* dense_idx;  // [n + 1]: the identity list and its count, for the dense route
 };
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
@@ -199,6 +202,12 @@ bool run_bundle_b1(const LayerDev& L, const float* x, float* y, int32_t* idx, in
                    uint64_t* tok, float* scores, hipStream_t s, const hipEvent_t* t_pass,
                    const hipEvent_t* t_reduce);
 size_t bundle_part_bytes(int d, int n);
+// the dense route (sparse_ffn_dense, and decode above its union crossover): every neuron,
+// no predictor; tokens in chunks of at most max_batch (and 64). idx/count/tok: where the
+// identity list goes (tok may be null; B bits set per entry), or the workspace's own copy
+hipError_t launch_fill_list(const LayerDev& L, int B, int32_t* idx, int32_t* count,
+                            uint64_t* tok, hipStream_t s);
+hipError_t launch_dense(const LayerDev& L, const float* x, int B, float* y, hipStream_t s);
 // sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
 // number of workgroups; sink [workgroups] is written only in a practically impossible case
 hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink,

@@ -90,7 +90,27 @@ __global__ __launch_bounds__(TPB) void k_pack_rows(const uint32_t* __restrict__ 
   }
 }
 
+// The identity list of the dense route: idx[k] = k, *count = n, and (tok non-null) every
+// entry's token bits set for B tokens.
+__global__ __launch_bounds__(TPB) void k_fill_list(int n, int B, int32_t* __restrict__ idx,
+                                                   int32_t* __restrict__ count,
+                                                   uint64_t* __restrict__ tok) {
+  const uint64_t bits = B >= 64 ? ~(uint64_t)0 : (((uint64_t)1) << B) - 1;
+  for (int k = blockIdx.x * TPB + threadIdx.x; k < n; k += gridDim.x * TPB) {
+    idx[k] = k;
+    if (tok) tok[k] = bits;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *count = n;
+}
+
 }  // namespace
+
+hipError_t launch_fill_list(const LayerDev& L, int B, int32_t* idx, int32_t* count,
+                            uint64_t* tok, hipStream_t s) {
+  const int grid = std::max(1, std::min((L.n + TPB - 1) / TPB, 4 * L.n_cus));
+  hipLaunchKernelGGL(k_fill_list, dim3(grid), dim3(TPB), 0, s, L.n, B, idx, count, tok);
+  return hipGetLastError();
+}
 
 hipError_t launch_profile_counts(const void* w_act, int w_f16, int gated, const float* b_act,
                                  int d, int n, const float* x, int N, int64_t* counts,

@@ -79,13 +79,17 @@ class SparseFFN:
     single_pass: the single-token decode gathers each active neuron's input and down rows in
     one pass and adds the workgroups' partial outputs in a fixed order (y bitwise
     reproducible); shapes it does not cover fall back to the three-launch path.
+    dense_union: decode computes every neuron (the dense FFN, no predictor) from the batch
+    size whose expected union of predicted sets exceeds this fraction (0: never; needs the
+    profile).
     """
 
     def __init__(self, *, w_act, w_down_t, p1, p2, b_act=None, b_out=None, p_bias=None,
                  w_up=None, threshold: float = 0.0, max_batch: int = 1,
                  profile_x: Optional[torch.Tensor] = None, hot_frac: float = 0.2,
                  perm: Optional[np.ndarray] = None, deterministic: bool = False,
-                 bundle: bool = False, single_pass: bool = False, stream=None):
+                 bundle: bool = False, single_pass: bool = False, dense_union: float = 0.0,
+                 stream=None):
         dev = w_act.device
         if dev.type != "cuda":
             raise ValueError("SparseFFN needs device tensors")
@@ -132,6 +136,7 @@ class SparseFFN:
                 self.w_act = pack_rows(w_act, perm_dev, stream=stream)
             self.w_down_t = pack_rows(w_down_t, perm_dev, stream=stream)
         self.single_pass = bool(single_pass)
+        self.dense_union = float(dense_union)
         self.p2 = pack_rows(p2, perm_dev, stream=stream)
         self.b_act = None if b_act is None else pack_rows(b_act.contiguous(), perm_dev, stream=stream)
         self.p_bias = None if p_bias is None else pack_rows(p_bias.contiguous(), perm_dev, stream=stream)
@@ -158,6 +163,7 @@ class SparseFFN:
         D.deterministic = int(self.deterministic)
         D.layout = N.SFFN_LAYOUT_BUNDLE if self.bundle else N.SFFN_LAYOUT_SPLIT
         D.single_pass = int(self.single_pass)
+        D.dense_union = self.dense_union
         D.w_act, D.w_down_t = _ptr(self.w_act), _ptr(self.w_down_t)
         D.b_act, D.b_out = _ptr(self.b_act), _ptr(self.b_out)
         D.p1, D.p2, D.p_bias = _ptr(self.p1), _ptr(self.p2), _ptr(self.p_bias)
@@ -171,7 +177,8 @@ class SparseFFN:
         D.neuron_freq = None
 
     def clone(self, *, threshold: Optional[float] = None, deterministic: Optional[bool] = None,
-              max_batch: Optional[int] = None, single_pass: Optional[bool] = None) -> "SparseFFN":
+              max_batch: Optional[int] = None, single_pass: Optional[bool] = None,
+              dense_union: Optional[float] = None) -> "SparseFFN":
         """Another handle over the same packed weights (no copy), with its own workspace and
         the given threshold, mode or batch limit (default: this layer's). For example
         threshold=-inf lists every neuron: the library's own dense FFN."""
@@ -180,6 +187,8 @@ class SparseFFN:
                            if k not in ("handle", "desc", "workspace")})
         if single_pass is not None:
             c.single_pass = bool(single_pass)
+        if dense_union is not None:
+            c.dense_union = float(dense_union)
         c._create(self.threshold if threshold is None else threshold,
                   self.deterministic if deterministic is None else deterministic,
                   self.max_batch if max_batch is None else max_batch)
@@ -231,6 +240,17 @@ class SparseFFN:
         N.sparse_ffn_decode(self.handle, x.data_ptr(), B, y.data_ptr(), idx.data_ptr(),
                             count.data_ptr(), tokmask.data_ptr(), _ptr(scores), _stream(stream))
         return y, idx, count, tokmask
+
+    def dense(self, x, y=None, stream=None):
+        """The dense FFN over every neuron for x ([B, d] fp32, any B: prefill), no predictor
+        (sparse_ffn_dense)."""
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous fp32 [B, d] device tensor")
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty((B, self.d), dtype=torch.float32, device=x.device)
+        N.sparse_ffn_dense(self.handle, x.data_ptr(), B, y.data_ptr(), _stream(stream))
+        return y
 
     def lookahead_begin(self, x, stream=None):
         """Predict this layer's active set from x ([1, d] fp32) and hold it for

@@ -33,6 +33,9 @@ Also measured, beside the headline number:
   - the predictor's recall and precision against the true ReLU signs (a diagnostic of the
     synthetic calibrated predictor, not graded);
   - for the default workload, the same stack on its 5% -> 10% ramp (`c2_ramp`);
+  - the sparse decode against the dense route (every neuron, no predictor) on the
+    Llama-7B-shaped gated stack at 16-64 tokens, where the union of the tokens' sets grows,
+    and the dense route as 512-token prefill against torch (`dense_crossover`);
   - the fp64 CPU oracle on a bounded sample of the same workload, single-threaded and with
     OpenMP on the host's cores, with the host's core count and CPU model.
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -322,7 +325,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the 4 GiB read-stream probe")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the all-active, deterministic, recall and ramp legs")
+                    help="skip the all-active, deterministic, single-pass, recall, ramp and "
+                         "crossover legs")
+    ap.add_argument("--no-crossover", action="store_true",
+                    help="skip the sparse-vs-dense crossover on the gated batch stack")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="CPU work per oracle leg (single-threaded, then OpenMP)")
     ap.add_argument("--no-graph", action="store_true",
@@ -724,6 +730,11 @@ def main():
         layers = originals = None  # free the headline stack before building the ramp's
         ramp = run_ramp(torch, args, timer, dense)
 
+    crossover = None
+    if not args.no_extra and not args.no_crossover and B == 1:
+        layers = originals = None
+        crossover = run_crossover(torch, args, cap)
+
     # ------------------------------------------------------------------ report
     kd = kernels[dom]
     kfile = knames[dom].split(" ")[0]
@@ -786,11 +797,96 @@ def main():
         "cpu_baseline": cpu,
         "lookahead": lookahead,
         "c2_ramp": ramp,
+        "dense_crossover": crossover,
         "kernel_source_sha256": kernel_source_sha(),
     }
     if lookahead and dense and "us_per_layer" in lookahead:
         lookahead["speedup_vs_dense"] = round(dense["us_per_layer"] / lookahead["us_per_layer"], 3)
     print(json.dumps(out), flush=True)
+
+
+def run_crossover(torch, args, cap):
+    """The sparse decode against the dense route (every neuron, no predictor) on the
+    Llama-7B-shaped gated stack with independent per-token masks, at growing batches: the
+    union of the tokens' sets grows with the batch until the sparse path stops paying. Also
+    the dense route as prefill (512 tokens) against torch's F.linear chain on the same
+    weights, on the first four layers."""
+    import torch.nn.functional as F
+    from synth import get_config, make_tokens
+    cfg = get_config("C4")
+    L, d, n = cfg.layers, cfg.d, cfg.n
+    Bmax = 64
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layers, originals = build_stack(cfg, Bmax, L, args, lambda l: l < 4)
+    T, G = 16, 4
+    X = make_tokens(cfg, T * L * Bmax, 200, "cuda").view(T, L, Bmax, d).contiguous()
+    y_buf = torch.empty((L, Bmax, d), dtype=torch.float32, device="cuda")
+    idx_buf = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(L)]
+    tok_buf = [torch.empty(n, dtype=torch.int64, device="cuda") for _ in range(L)]
+    counts = torch.zeros((T, L), dtype=torch.int32, device="cuda")
+    timer = Timer(torch, T, G, 16, 4, cap, True)
+    rows = []
+    for B in (16, 32, 48, 64):
+        Xb = X[:, :, :B].contiguous()
+        for t in range(T):
+            decode_pass(torch, layers, Xb, t, y_buf, idx_buf, tok_buf, counts)
+        torch.cuda.synchronize()
+        union = float(counts.float().mean()) / n
+        sp_ms, _ = timer.run(lambda t, st: decode_pass(torch, layers, Xb, t, y_buf, idx_buf,
+                                                       tok_buf, counts, st))
+        de_ms, _ = timer.run(lambda t, st: [layers[l].dense(Xb[t, l], y=y_buf[l, :B], stream=st)
+                                            for l in range(L)])
+        rows.append({"batch": B, "union_fraction": round(union, 4),
+                     "sparse_us_per_layer": round(sp_ms * 1000.0 / L, 3),
+                     "dense_route_us_per_layer": round(de_ms * 1000.0 / L, 3)})
+        log(f"crossover B={B}: union {union:.3f}, sparse {rows[-1]['sparse_us_per_layer']} us, "
+            f"dense route {rows[-1]['dense_route_us_per_layer']} us")
+    cross = next((r_["union_fraction"] for r_ in rows
+                  if r_["dense_route_us_per_layer"] < r_["sparse_us_per_layer"]), None)
+    # prefill: 512 tokens through the first four layers
+    P, LP = 512, 4
+    Xp = make_tokens(cfg, P * LP, 300, "cuda").view(LP, P, d).contiguous()
+    yp = torch.empty((LP, P, d), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def time_fn(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    lib_ms = time_fn(lambda: [layers[l].dense(Xp[l], y=yp[l]) for l in range(LP)])
+    Xh = Xp.half()
+
+    def torch_prefill():
+        for l in range(LP):
+            o = originals[l]
+            a = F.linear(Xh[l], o.w_a, o.b_a.half())
+            h = F.relu(a) * F.linear(Xh[l], o.w_u)
+            _ = torch.matmul(h, o.w_o) + o.b_o.half()
+
+    th_ms = time_fn(torch_prefill)
+    out = {"workload": f"{cfg.name}: {cfg.description}", "rows": rows,
+           "crossover_union_fraction": cross,
+           "note": "dense route = every neuron through the forward kernels (tile path), no "
+                   "predictor; the decode switches to it when sffn_desc.dense_union is set and "
+                   "the expected union exceeds it",
+           "prefill_512_tokens": {
+               "library_dense_tokens_per_s": round(P * LP / (lib_ms * 1e-3) / LP, 1),
+               "torch_fp16_tokens_per_s": round(P * LP / (th_ms * 1e-3) / LP, 1),
+               "library_ms_per_layer": round(lib_ms / LP, 4),
+               "torch_ms_per_layer": round(th_ms / LP, 4),
+               "note": "per layer; the library keeps fp32 activations (hi + lo fp16 on the matrix "
+                       "cores) and re-reads the weights once per 64-token chunk; torch runs fp16 "
+                       "activations through hipBLASLt"}}
+    log(f"prefill 512 tokens: library {lib_ms / LP:.3f} ms/layer, torch {th_ms / LP:.3f} ms/layer")
+    del layers, originals
+    return out
 
 
 def run_ramp(torch, args, timer, dense):

@@ -142,6 +142,17 @@ typedef struct {
                                rows again). Lists, counts, token bits and scores are the same
                                either way; y agrees to rounding. Operator fusion: novita.ai
                                activation-sparsity article, section 工程影響. */
+  float dense_union;        /* 0: never. In (0, 1]: sparse_ffn_decode computes every neuron
+                               for every token (the dense FFN; the predictor is skipped and
+                               the published list is every neuron with every token's bit)
+                               from the smallest batch size whose expected union of the
+                               tokens' predicted sets, 1 - mean_i (1 - f_i)^B over the
+                               neurons' neuron_freq values f_i (tokens independent), exceeds
+                               this fraction. The choice depends on B only and is fixed at
+                               create (needs neuron_freq). As the union grows with the batch,
+                               the sparse path stops paying (novita.ai article, section
+                               批次大小影響; PowerInfer-2 article, section 4.1.1 NPU-Centric
+                               Prefill runs prefill dense). */
 } sffn_desc;
 
 /* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The
@@ -189,6 +200,16 @@ int sparse_ffn_forward(sparse_ffn_t h, const float* x, int32_t B, const int32_t*
  * receives the predictor scores. */
 int sparse_ffn_decode(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                       int32_t* count, uint64_t* tokmask, float* scores, void* stream);
+
+/* Dense FFN over every neuron for B tokens, any B >= 1 (prefill): y_b = sum_i
+ * h_i(x_b) w_down_t[i] + b_out with h as in sparse_ffn_forward, i.e. sparse_ffn_forward over
+ * the list of all d_ffn neurons with every token's bit set. No predictor. Tokens go through
+ * in chunks of the handle's max_batch (the workspace's size), so B may exceed
+ * SFFN_MAX_BATCH. x: device [B][d] fp32; y: device [B][d] fp32, fully overwritten. The
+ * dense prefill of PowerInfer-2 (PowerInfer-2 article, section 4.1.1 NPU-Centric Prefill);
+ * the sparse path pays only while the active set is a small part of the layer (novita.ai
+ * activation-sparsity article, section 批次大小影響). */
+int sparse_ffn_dense(sparse_ffn_t h, const float* x, int32_t B, float* y, void* stream);
 
 /* Look-ahead decode, one token (the asynchronous predictor of the novita.ai
  * activation-sparsity article, section 上下文稀疏性: the next layer's active neurons are

@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -99,6 +99,8 @@ def test_workspace_bytes(N):
     dict(gated=2), dict(w_dtype=7), dict(p_dtype=-1), dict(w_act=None), dict(p2=None),
     dict(workspace=None), dict(w_act=0x10004), dict(b_out=0x10008),
     dict(workspace_bytes=16),  # too small
+    dict(dense_union=1.5), dict(dense_union=-0.1), dict(dense_union=float("nan")),
+    dict(layout=2), dict(single_pass=2), dict(layout=1),  # bundle layout with a w_down_t
 ])
 def test_create_rejects_invalid(N, over):
     D = _valid_desc(N)
