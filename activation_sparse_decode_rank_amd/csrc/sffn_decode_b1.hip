@@ -849,7 +849,7 @@ bool lookahead_layer_ok(const LayerDev& L) {
 }
 
 hipError_t run_lookahead_begin(const LayerDev& Nx, const float* x, hipStream_t s) {
-  run_stage1(Nx, x, 1, s, nullptr, nullptr, 0, false, false);
+  run_stage1(Nx, x, 1, s, nullptr, nullptr, 0, false);
   if (!la_down_any(nullptr, &Nx, nullptr, nullptr, nullptr, nullptr, s, nullptr))
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -15,12 +15,12 @@
 //  - memory is read in whole coalesced blocks and operators are fused (novita.ai article,
 //    section 工程影響).
 // How it is computed here is specific to this chip: kernel boundaries are the only
-// grid-wide synchronization (they cost about a microsecond and a half inside a HIP graph,
-// far less than any in-kernel grid barrier on this part). Global atomics are few: the
-// middle kernel ORs each wave's active bits into a union bitmask (at most two 64-bit ORs
-// per wave, order-independent), and the down projection may add up to KS split-k sums
-// per output element (bitwise reproducible for KS <= 2). Every other reduction has a
-// fixed order.
+// grid-wide synchronization (inside a HIP graph the next kernel starts as the previous one
+// drains; a hand-off between workgroups of one launch through a device-coherent counter
+// measured slower, since same-address atomics and polls serialize at the coherent level).
+// Global atomics are few: the down projections may add up to KS split-k sums per output
+// element with float atomics (bitwise reproducible for KS <= 2), and the stream-K up
+// kernel counts the parts of each split tile. Every other reduction has a fixed order.
 #pragma once
 #include <hip/hip_ext.h>
 
@@ -51,7 +51,7 @@ __device__ __forceinline__ u32x4 ld_chunk(const void* base, size_t chunk) {
 }
 // Weight rows read once per step: non-temporal, so that streaming them does not evict
 // what the step reuses from the caches (kernel code, the token, predictor outputs,
-// activations, and rows the previous kernel prefetched).
+// activations).
 __device__ __forceinline__ u32x4 ld_stream(const void* base, size_t chunk) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + chunk);
 }

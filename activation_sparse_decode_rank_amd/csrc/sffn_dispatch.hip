@@ -101,7 +101,7 @@ bool shape_supported(const LayerDev& L, bool fused) {
 }
 
 hipError_t launch_predict(const LayerDev& L, const float* x, int B, float* scores, hipStream_t s) {
-  run_stage1(L, x, B, s, nullptr, nullptr, 0, false, false);
+  run_stage1(L, x, B, s, nullptr, nullptr, 0, false);
   // the same scores kernel the decode step runs at this batch, so both give equal scores
   if (tile_ok(L, B) && score_tiles_ok(L, B)) return run_score_tiles(L, B, scores, s);
   return run_scores(L, B, scores, s);
@@ -156,7 +156,7 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     // words do not fit its LDS); else scores and two compaction passes, the scores going
     // to the caller's buffer or, when none is given, to the activation buffer, which the
     // up projection only overwrites after compaction has read them; then the tiles
-    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, false, true);
+    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, true);
     hipError_t e;
     bool fw = false;
     if (score_tiles_ok(L, B)) {
@@ -180,10 +180,10 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
   if (B == 1 && L.single_pass && bundle_ok(L)) {
     // one pass over the active neurons' bundles writes partial outputs; the reduction
     // writes all of y, so stage 1 clears nothing
-    run_stage1(L, x, 1, s, t1, nullptr, 0, true, false);
+    run_stage1(L, x, 1, s, t1, nullptr, 0, false);
     if (run_bundle_b1(L, x, y, idx, count, tokmask, scores, s, t2, t3)) return hipGetLastError();
   }
-  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, true, false);
+  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, false);
   if (B == 1 && run_mid_b1(L, x, scores, s, t2)) {
     run_down_b1(L, idx, count, tokmask, y, s, t3);
     return hipGetLastError();

@@ -101,13 +101,12 @@ constexpr int TILE_MIN_B = 2;
 
 // Kernel-family entry points (one translation unit each; tev: an optional start/end event
 // pair stamped by the dispatch).
-// sffn_decode_b1.hip: predictor stage 1 (y0/ny: output zeroed for the split-k down
-// projection; prefetch: also pull the middle kernel's first loads into cache), the batch-1
-// middle kernel (false when no kernel exists for the shape) and down projection.
-// prefetch: extra workgroups warm the middle kernel's first loads; split_x (2+ tokens):
-// extra workgroups write the tokens' fp16 hi/lo split into x_hl for the up tile kernel
+// sffn_stage1.hip: predictor stage 1 (y0/ny: output zeroed for the split-k down
+// projection; split_x (2+ tokens): extra workgroups write the tokens' fp16 hi/lo split into
+// x_hl for the up tile kernel). sffn_decode_b1.hip: the batch-1 middle kernel (false when no
+// kernel exists for the shape) and down projection.
 void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                float* y0, int ny, bool prefetch, bool split_x);
+                float* y0, int ny, bool split_x);
 bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev);
 int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 kernel applies

@@ -1,6 +1,5 @@
-// Predictor stage 1 (gfx950): q = P1 x for one token or several, plus the prefetch of the
-// middle kernel's first loads. The method is described at the top of sffn_device.h; the
-// predictor is the first half of the low-rank score map (unite.ai PowerInfer overview,
+// Predictor stage 1 (gfx950): q = P1 x for one token or several. The method is described at
+// the top of sffn_device.h; the predictor is the first half of the low-rank score map (unite.ai PowerInfer overview,
 // "Predictores de espacialidad adaptativa"; novita.ai activation-sparsity article, section
 // 自適應稀疏預測器).
 #include "sffn_device.h"
@@ -13,60 +12,14 @@ namespace {
 // NCPT chunks of the row in registers and reuses them for every token group of TBG. In the
 // decode step these workgroups also clear y (ny floats), which the down projection later
 // adds its split-k sums into.
-// Workgroups r .. r + g_pf - 1 only prefetch: workgroup r + w reads middle-kernel range w's
-// rows of the predictor's second-stage matrix p2 (NCHP chunks per row) and its two bias
-// entries per neuron, so that the middle kernel's first loads hit cache instead of HBM.
-// Those addresses are static, so their latency overlaps this kernel's own. Workgroups are
-// dealt to the XCDs round-robin by id, and r is a multiple of 8, so workgroup r + w shares
-// an XCD (and its L2) with middle workgroup w. Every prefetch load is issued before any
-// wait; the values are folded into a register that an empty asm consumes, so the loads
-// stay and nothing is stored.
-constexpr int PF_PER_THREAD = 8;
-// The body of a prefetch workgroup: read middle-kernel range w's predictor rows (NCHP
-// chunks each) and its two bias entries per neuron. Every load is issued before any wait;
-// the values are folded into a register that an empty asm consumes, so the loads stay and
-// nothing is stored.
-__device__ __forceinline__ void prefetch_mid_range(int w, const void* __restrict__ p2, int nchp,
-                                                   const float* __restrict__ pfb0,
-                                                   const float* __restrict__ pfb1,
-                                                   const RangeArg& ra) {
-  const int tid = threadIdx.x;
-  const int r0 = ra.r[w], r1 = ra.r[w + 1];
-  const int c0 = r0 * nchp, nc = (r1 - r0) * nchp;
-  // one 4-byte load per 16-byte chunk: every 128-byte line of the range is still touched
-  // (8 lanes per line), and the loads have distinct destination registers, so none waits
-  // for another (a 16-byte load of which only a quarter is used let the compiler overlap
-  // destinations and wait between loads)
-  const uint32_t* p2w = reinterpret_cast<const uint32_t*>(p2);
-  uint32_t pv[PF_PER_THREAD];
-#pragma unroll
-  for (int v = 0; v < PF_PER_THREAD; ++v) pv[v] = p2w[4 * (size_t)(c0 + min(tid + v * TPB, nc - 1))];
-  float b0 = 0.f, b1 = 0.f;
-  if (tid < r1 - r0) {
-    if (pfb0) b0 = pfb0[r0 + tid];
-    if (pfb1) b1 = pfb1[r0 + tid];
-  }
-  unsigned sink = __float_as_uint(b0) ^ __float_as_uint(b1);
-#pragma unroll
-  for (int v = 0; v < PF_PER_THREAD; ++v) sink ^= pv[v];
-  asm volatile("" ::"v"(sink));
-}
 template <bool PF16, int TBG, int NCPT>
 __global__ __launch_bounds__(TPB) void k_pred_stage1(const void* __restrict__ p1,
                                                      const float* __restrict__ x, int d, int r,
                                                      int B, float* __restrict__ q,
-                                                     float* __restrict__ y0, int ny,
-                                                     const void* __restrict__ p2, int nchp,
-                                                     const float* __restrict__ pfb0,
-                                                     const float* __restrict__ pfb1,
-                                                     const RangeArg ra) {
+                                                     float* __restrict__ y0, int ny) {
   constexpr int EPC = Elt<PF16>::EPC;
-  touch_kernargs<2>();
+  touch_kernargs<1>();
   const int j = blockIdx.x, tid = threadIdx.x;
-  if (j >= r) {
-    prefetch_mid_range(j - r, p2, nchp, pfb0, pfb1, ra);
-    return;
-  }
   for (int i = j * TPB + tid; i < ny; i += r * TPB) y0[i] = 0.f;
   const int nch = d / EPC;
   const size_t row0 = (size_t)j * nch;
@@ -146,28 +99,21 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&a)[V]) {
 // all MT rows and BT tokens, so every P1 row is read ceil(B / BT) times in all and every
 // token r / MT times (the single-row form reads each token r times, which dominates from
 // a few tokens on). Row tile = id mod (rows / MT): with rows / MT a multiple of 8 a row
-// tile stays on one XCD, whose L2 then serves its rows to every token group. Workgroups
-// from nmain on prefetch the middle kernel's ranges as in the single-token form (nmain is
-// a multiple of 8), npf of them. The nsplit workgroups after those split the tokens into
-// x_hl for the matrix-core up projection (see split_x_items; tbp token slots). The first
-// nmain workgroups also clear y0[0..ny).
+// tile stays on one XCD, whose L2 then serves its rows to every token group. The nsplit
+// workgroups from nmain on split the tokens into x_hl for the matrix-core up projection
+// (see split_x_items; tbp token slots). The first nmain workgroups also clear y0[0..ny).
 template <bool PF16, int MT, int BT>
 __global__ __launch_bounds__(TPB) void k_pred_stage1_mt(
     const void* __restrict__ p1, const float* __restrict__ x, int d, int r, int B,
-    float* __restrict__ q, float* __restrict__ y0, int ny, int nrt, int nmain, int npf,
-    u32x4* __restrict__ x_hl, int tbp, int nsplit, const void* __restrict__ p2, int nchp,
-    const float* __restrict__ pfb0, const float* __restrict__ pfb1, const RangeArg ra) {
+    float* __restrict__ q, float* __restrict__ y0, int ny, int nrt, int nmain,
+    u32x4* __restrict__ x_hl, int tbp, int nsplit) {
   constexpr int EPC = Elt<PF16>::EPC;
   constexpr int V = MT * BT;
   constexpr int SPAN = 64 / V;  // lanes holding each reduced value
   touch_kernargs<2>();
   const int g = blockIdx.x, tid = threadIdx.x;
-  if (g >= nmain + npf) {
-    split_x_items(x, B, d, tbp, x_hl, (g - nmain - npf) * TPB + tid, nsplit * TPB);
-    return;
-  }
   if (g >= nmain) {
-    prefetch_mid_range(g - nmain, p2, nchp, pfb0, pfb1, ra);
+    split_x_items(x, B, d, tbp, x_hl, (g - nmain) * TPB + tid, nsplit * TPB);
     return;
   }
   for (int i = g * TPB + tid; i < ny; i += nmain * TPB) y0[i] = 0.f;
@@ -208,50 +154,36 @@ __global__ __launch_bounds__(TPB) void k_pred_stage1_mt(
   }
 }
 
-// y0: output of ny floats the down projection will add into (zeroed here), or null;
-// prefetch: extra workgroups pull the middle kernel's predictor rows and biases into cache
+// y0: output of ny floats the down projection will add into (zeroed here), or null
 template <bool F16, int NCPT>
 void stage1_launch_t(const LayerDev& L, const float* x, int B, hipStream_t s,
-                     const hipEvent_t* tev, float* y0, int ny, int g_pf) {
-  const int nchp = L.r / (L.p_f16 ? 8 : 4);
-  const dim3 grid(L.r + g_pf);
-  launch(k_pred_stage1<F16, 1, NCPT>, grid, dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
-         y0, ny, L.p2, nchp, L.p_bias, L.b_act, L.ra);
-}
-
-// prefetch workgroups are used when the ranges travel in the kernel arguments, a range's
-// predictor rows fit PF_PER_THREAD chunks per thread, and r keeps them on their consumer's
-// XCD
-int stage1_prefetch_groups(const LayerDev& L) {
-  const int nchp = L.r / (L.p_f16 ? 8 : 4);
-  if (!L.rs_in_arg || L.r % 8 != 0 || MID_RANGE_MAX * nchp > TPB * PF_PER_THREAD) return 0;
-  return L.g_mid;
+                     const hipEvent_t* tev, float* y0, int ny) {
+  launch(k_pred_stage1<F16, 1, NCPT>, dim3(L.r), dim3(TPB), 0, s, tev, L.p1, x, L.d, L.r, B, L.q,
+         y0, ny);
 }
 
 template <bool F16, int MT, int BT>
 void stage1_mt_launch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                      const hipEvent_t* tev, float* y0, int ny, int g_pf, bool split_x) {
-  const int nchp = L.r / (F16 ? 8 : 4);
+                      const hipEvent_t* tev, float* y0, int ny, bool split_x) {
   const int nrt = (L.r + MT - 1) / MT;
   const int nmain = (nrt * ((B + BT - 1) / BT) + 7) / 8 * 8;
   const int tbp = B;  // token slots per chunk in x_hl
   const int nsplit = split_x ? (L.d / 8 * tbp + 4 * TPB - 1) / (4 * TPB) : 0;  // 4 items a thread
-  launch(k_pred_stage1_mt<F16, MT, BT>, dim3(nmain + g_pf + nsplit), dim3(TPB), 0, s, tev, L.p1,
-         x, L.d, L.r, B, L.q, y0, ny, nrt, nmain, g_pf, static_cast<u32x4*>(L.x_hl), tbp, nsplit,
-         L.p2, nchp, L.p_bias, L.b_act, L.ra);
+  launch(k_pred_stage1_mt<F16, MT, BT>, dim3(nmain + nsplit), dim3(TPB), 0, s, tev, L.p1, x, L.d,
+         L.r, B, L.q, y0, ny, nrt, nmain, static_cast<u32x4*>(L.x_hl), tbp, nsplit);
 }
 
 // Several tokens: BT = 2 tokens per workgroup up to 8 tokens, 4 beyond; MT the largest row
 // tile that still leaves at least 256 workgroups (one per compute unit).
 template <bool F16>
 void stage1_mt_dispatch(const LayerDev& L, const float* x, int B, hipStream_t s,
-                        const hipEvent_t* tev, float* y0, int ny, int g_pf, bool split_x) {
+                        const hipEvent_t* tev, float* y0, int ny, bool split_x) {
   const int bt = B <= 8 ? 2 : 4;
   const int ntg = (B + bt - 1) / bt;
   int mt = 1;
   for (int m = 8; m >= 2; m /= 2)
     if ((L.r / m) * ntg >= 256) { mt = m; break; }
-#define SFFN_S1(M, T) stage1_mt_launch<F16, M, T>(L, x, B, s, tev, y0, ny, g_pf, split_x)
+#define SFFN_S1(M, T) stage1_mt_launch<F16, M, T>(L, x, B, s, tev, y0, ny, split_x)
   if (bt == 2) {
     if (mt == 8) SFFN_S1(8, 2); else if (mt == 4) SFFN_S1(4, 2); else if (mt == 2) SFFN_S1(2, 2); else SFFN_S1(1, 2);
   } else {
@@ -262,35 +194,34 @@ void stage1_mt_dispatch(const LayerDev& L, const float* x, int B, hipStream_t s,
 
 template <bool F16>
 void stage1_launch(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                   float* y0, int ny, bool prefetch, bool split_x) {
+                   float* y0, int ny, bool split_x) {
   if (!y0) ny = 0;
-  const int g_pf = prefetch ? stage1_prefetch_groups(L) : 0;
   if (B > 1) {
-    stage1_mt_dispatch<F16>(L, x, B, s, tev, y0, ny, g_pf, split_x);
+    stage1_mt_dispatch<F16>(L, x, B, s, tev, y0, ny, split_x);
     return;
   }
   // one token, rank 512 and up (e.g. the OPT-175B slice: 1024 rows of 12288): four rows per
   // workgroup, so the token is read from L2 a quarter as often (every single-row workgroup
   // reads all of it, twice the bytes of its own row)
   if (L.r >= 512) {
-    stage1_mt_launch<F16, 4, 1>(L, x, B, s, tev, y0, ny, g_pf, split_x);
+    stage1_mt_launch<F16, 4, 1>(L, x, B, s, tev, y0, ny, split_x);
     return;
   }
   const int ncpt = (L.d / (F16 ? 8 : 4) + TPB - 1) / TPB;
-  if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny, g_pf);
-  else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny, g_pf);
-  else if (ncpt <= 4) stage1_launch_t<F16, 4>(L, x, B, s, tev, y0, ny, g_pf);
-  else stage1_launch_t<F16, 8>(L, x, B, s, tev, y0, ny, g_pf);
+  if (ncpt <= 1) stage1_launch_t<F16, 1>(L, x, B, s, tev, y0, ny);
+  else if (ncpt <= 2) stage1_launch_t<F16, 2>(L, x, B, s, tev, y0, ny);
+  else if (ncpt <= 4) stage1_launch_t<F16, 4>(L, x, B, s, tev, y0, ny);
+  else stage1_launch_t<F16, 8>(L, x, B, s, tev, y0, ny);
 }
 
 }  // namespace
 
 void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const hipEvent_t* tev,
-                float* y0, int ny, bool prefetch, bool split_x) {
+                float* y0, int ny, bool split_x) {
   if (L.p_f16)
-    stage1_launch<true>(L, x, B, s, tev, y0, ny, prefetch, split_x);
+    stage1_launch<true>(L, x, B, s, tev, y0, ny, split_x);
   else
-    stage1_launch<false>(L, x, B, s, tev, y0, ny, prefetch, split_x);
+    stage1_launch<false>(L, x, B, s, tev, y0, ny, split_x);
 }
 
 }  // namespace sffn
