@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/sparse_ffn.h"
+#include "sffn_host.h"
 #include "sffn_internal.h"
 
 struct sparse_ffn_s {
@@ -57,89 +58,12 @@ int check_ptrs(const sffn_desc* d) {
   return SFFN_OK;
 }
 
-// Split neurons [0, n) into contiguous ranges of at most MID_RANGE_MAX neurons whose
-// expected costs (predictor row bytes plus expected activation frequency times the bytes
-// of the neuron's two weight rows) are about equal. With no frequencies every neuron
-// costs the same. The greedy cut is deterministic.
-std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_bytes,
-                                     double act_row_bytes, int target_groups) {
-  std::vector<double> cost(n);
-  for (int i = 0; i < n; ++i) {
-    double f = freq ? (double)freq[i] : 0.0;
-    if (!(f >= 0.0)) f = 0.0;
-    if (f > 1.0) f = 1.0;
-    cost[i] = p2_row_bytes + f * act_row_bytes;
-  }
-  const double total = std::accumulate(cost.begin(), cost.end(), 0.0);
-  double target = total / std::max(1, target_groups);
-  for (int attempt = 0; attempt < 64; ++attempt) {
-    std::vector<int32_t> rs{0};
-    double acc = 0.0;
-    int len = 0;
-    for (int i = 0; i < n; ++i) {
-      if (len > 0 && (len == sffn::MID_RANGE_MAX || acc + cost[i] > target)) {
-        rs.push_back(i);
-        acc = 0.0;
-        len = 0;
-      }
-      acc += cost[i];
-      ++len;
-    }
-    rs.push_back(n);
-    if ((int)rs.size() - 1 <= std::max(target_groups, 1)) return rs;
-    target *= 1.25;
-  }
-  return {};
-}
-
-// Cut the ranges into ks contiguous splits of about equal expected active neurons (the
-// sum of the neurons' frequencies; every neuron counts 1 without frequencies), for the
-// decode down projection. upt = ranges per thread the largest split needs (256 threads).
-// the largest expected cost (bytes) of one range: its predictor rows plus each neuron's
-// ReLU-input row(s) weighted by its activation frequency
-double max_range_cost(const std::vector<int32_t>& rs, const float* freq, double p2_row_bytes,
-                      double act_row_bytes) {
-  double worst = 0.0;
-  for (size_t u = 0; u + 1 < rs.size(); ++u) {
-    double c = 0.0;
-    for (int i = rs[u]; i < rs[u + 1]; ++i) {
-      double f = freq ? (double)freq[i] : 0.0;
-      if (!(f >= 0.0)) f = 0.0;
-      if (f > 1.0) f = 1.0;
-      c += p2_row_bytes + f * act_row_bytes;
-    }
-    worst = std::max(worst, c);
-  }
-  return worst;
-}
-
+// the down projection's splits into the kernel argument
 void split_ranges(const std::vector<int32_t>& rs, const float* freq, int ks, sffn::SplitArg& sa,
                   int& upt) {
-  const int g = (int)rs.size() - 1;
-  std::vector<double> cum(g + 1, 0.0);
-  for (int u = 0; u < g; ++u) {
-    double e = 0.0;
-    for (int i = rs[u]; i < rs[u + 1]; ++i) {
-      double f = freq ? (double)freq[i] : 1.0;
-      if (!(f >= 0.0)) f = 0.0;
-      if (f > 1.0) f = 1.0;
-      e += f;
-    }
-    cum[u + 1] = cum[u] + e;
-  }
+  const std::vector<int32_t> s = sffn::host::split_ranges(rs, freq, ks, upt);
   sa = sffn::SplitArg{};
-  sa.s[0] = 0;
-  int u = 0;
-  for (int k = 1; k < ks; ++k) {
-    const double goal = cum[g] * k / ks;
-    while (u < g && cum[u] < goal) ++u;
-    sa.s[k] = u;
-  }
-  sa.s[ks] = g;
-  int widest = 0;
-  for (int k = 0; k < ks; ++k) widest = std::max(widest, sa.s[k + 1] - sa.s[k]);
-  upt = 1;
-  while (upt * 256 < widest && upt < 16) upt *= 2;
+  std::copy(s.begin(), s.end(), sa.s);
 }
 
 }  // namespace
@@ -204,21 +128,9 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     // the dense route from the smallest batch whose expected union of predicted sets (the
     // neurons' profile frequencies f_i, tokens independent: 1 - mean_i (1 - f_i)^B) exceeds
     // dense_union; 0 (or no frequencies) = never
-    L.dense_from_b = SFFN_MAX_BATCH + 1;
-    if (desc->dense_union > 0.f && desc->neuron_freq) {
-      for (int b = 1; b <= desc->max_batch; ++b) {
-        double u = 0.0;
-        for (int i = 0; i < desc->d_ffn; ++i) {
-          double f = desc->neuron_freq[i];
-          f = f > 0.0 ? (f < 1.0 ? f : 1.0) : 0.0;
-          u += 1.0 - std::pow(1.0 - f, (double)b);
-        }
-        if (u / desc->d_ffn > (double)desc->dense_union) {
-          L.dense_from_b = b;
-          break;
-        }
-      }
-    }
+    L.dense_from_b = sffn::host::dense_from_batch(desc->neuron_freq, desc->d_ffn,
+                                                  desc->dense_union, desc->max_batch,
+                                                  SFFN_MAX_BATCH + 1);
     L.b_act = desc->b_act;
     L.b_out = desc->b_out;
     L.p1 = desc->p1;
@@ -263,8 +175,8 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     // up to RS_ARG_MAX ranges travel in the kernel arguments
     const int min_groups = (desc->d_ffn + sffn::MID_RANGE_MAX - 1) / sffn::MID_RANGE_MAX;
     const int target = std::max(std::min(resident, sffn::RS_ARG_MAX), min_groups);
-    std::vector<int32_t> rs = balanced_ranges(desc->d_ffn, desc->neuron_freq, pb * desc->rank,
-                                              act_row, target);
+    std::vector<int32_t> rs = sffn::host::balanced_ranges(
+        desc->d_ffn, desc->neuron_freq, pb * desc->rank, act_row, target, sffn::MID_RANGE_MAX);
     // When the 64-neuron cap alone fixes the layout (a wide layer whose resident workgroups
     // number about n/64), the hot prefix lands in a few full ranges whose gathers run long.
     // More ranges than are resident at once then pay off: up to RS_ARG_MAX in the kernel
@@ -273,10 +185,11 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     const int wide = min_groups < sffn::RS_ARG_MAX ? sffn::RS_ARG_MAX
                                                    : std::min(2 * min_groups, sffn::G_MID_MAX);
     if (!rs.empty() && target == min_groups && wide > (int)rs.size() - 1) {
-      std::vector<int32_t> rs2 = balanced_ranges(desc->d_ffn, desc->neuron_freq,
-                                                 pb * desc->rank, act_row, wide);
-      if (!rs2.empty() && max_range_cost(rs2, desc->neuron_freq, pb * desc->rank, act_row) <
-                              0.5 * max_range_cost(rs, desc->neuron_freq, pb * desc->rank, act_row))
+      std::vector<int32_t> rs2 = sffn::host::balanced_ranges(
+          desc->d_ffn, desc->neuron_freq, pb * desc->rank, act_row, wide, sffn::MID_RANGE_MAX);
+      if (!rs2.empty() &&
+          sffn::host::max_range_cost(rs2, desc->neuron_freq, pb * desc->rank, act_row) <
+              0.5 * sffn::host::max_range_cost(rs, desc->neuron_freq, pb * desc->rank, act_row))
         rs.swap(rs2);
     }
     L.g_mid = rs.empty() ? 0 : (int)rs.size() - 1;
@@ -463,21 +376,7 @@ int sparse_ffn_permutation(const int64_t* counts, int32_t d_ffn, int32_t n_hot,
   if (!counts || !perm_new_to_old || d_ffn <= 0 || n_hot < 0 || n_hot > d_ffn)
     return SFFN_ERR_INVALID;
   try {
-    std::vector<int32_t> order(d_ffn);
-    std::iota(order.begin(), order.end(), 0);
-    // hottest first; equal counts keep the smaller original index first
-    std::partial_sort(order.begin(), order.begin() + n_hot, order.end(),
-                      [counts](int32_t a, int32_t b) {
-                        return counts[a] != counts[b] ? counts[a] > counts[b] : a < b;
-                      });
-    std::vector<char> hot(d_ffn, 0);
-    for (int32_t k = 0; k < n_hot; ++k) {
-      perm_new_to_old[k] = order[k];
-      hot[order[k]] = 1;
-    }
-    int32_t k = n_hot;
-    for (int32_t i = 0; i < d_ffn; ++i)
-      if (!hot[i]) perm_new_to_old[k++] = i;
+    sffn::host::hot_first_permutation(counts, d_ffn, n_hot, perm_new_to_old);
     return SFFN_OK;
   } catch (...) {
     return SFFN_ERR_HIP;

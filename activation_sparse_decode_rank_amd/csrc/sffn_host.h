@@ -1,0 +1,140 @@
+// Host-side planning of the activation-sparse FFN decode library: pure C++ with no HIP
+// dependency, so that it can also be built and checked on its own (the CPU sanitizer test
+// compiles it with AddressSanitizer and UndefinedBehaviorSanitizer).
+//  - neuron ranges of the middle kernel, cut for equal expected cost from the profile
+//    frequencies, and the down projection's splits of those ranges;
+//  - the hot-first neuron permutation (unite.ai PowerInfer overview, "Fase fuera de línea"
+//    and "Colocación y gestión de neuronas": the offline profile orders neurons by how
+//    often they activate);
+//  - the batch size from which the decode step computes every neuron (the union of the
+//    tokens' active sets grows with the batch: novita.ai activation-sparsity article,
+//    section 批次大小影響).
+#pragma once
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <numeric>
+#include <vector>
+
+namespace sffn {
+namespace host {
+
+// an expected frequency clamped to [0, 1]; NaN and negatives count as 0
+inline double clamp_freq(float f) {
+  const double v = (double)f;
+  if (!(v >= 0.0)) return 0.0;
+  return v > 1.0 ? 1.0 : v;
+}
+
+// Split neurons [0, n) into contiguous ranges of at most max_len neurons whose expected
+// costs (predictor row bytes plus expected activation frequency times the bytes of the
+// neuron's ReLU-input row(s)) are about equal, at most target_groups of them (the cost per
+// range is raised until the cut fits). With no frequencies every neuron costs the same.
+// Returns the g + 1 range starts (the last = n), or an empty vector when no cut fits. The
+// greedy cut is deterministic.
+inline std::vector<int32_t> balanced_ranges(int n, const float* freq, double p2_row_bytes,
+                                            double act_row_bytes, int target_groups, int max_len) {
+  std::vector<double> cost(n > 0 ? n : 0);
+  for (int i = 0; i < n; ++i)
+    cost[i] = p2_row_bytes + (freq ? clamp_freq(freq[i]) : 0.0) * act_row_bytes;
+  const double total = std::accumulate(cost.begin(), cost.end(), 0.0);
+  double target = total / std::max(1, target_groups);
+  for (int attempt = 0; attempt < 64; ++attempt) {
+    std::vector<int32_t> rs{0};
+    double acc = 0.0;
+    int len = 0;
+    for (int i = 0; i < n; ++i) {
+      if (len > 0 && (len == max_len || acc + cost[i] > target)) {
+        rs.push_back(i);
+        acc = 0.0;
+        len = 0;
+      }
+      acc += cost[i];
+      ++len;
+    }
+    rs.push_back(n);
+    if ((int)rs.size() - 1 <= std::max(target_groups, 1)) return rs;
+    target *= 1.25;
+  }
+  return {};
+}
+
+// the largest expected cost (bytes) of one range: its predictor rows plus each neuron's
+// ReLU-input row(s) weighted by its activation frequency
+inline double max_range_cost(const std::vector<int32_t>& rs, const float* freq,
+                             double p2_row_bytes, double act_row_bytes) {
+  double worst = 0.0;
+  for (size_t u = 0; u + 1 < rs.size(); ++u) {
+    double c = 0.0;
+    for (int i = rs[u]; i < rs[u + 1]; ++i)
+      c += p2_row_bytes + (freq ? clamp_freq(freq[i]) : 0.0) * act_row_bytes;
+    worst = std::max(worst, c);
+  }
+  return worst;
+}
+
+// Cut the g ranges (starts rs, g + 1 entries) into ks contiguous splits of about equal
+// expected active neurons (the sum of the neurons' frequencies; every neuron counts 1
+// without frequencies), for the down projection. Returns the ks + 1 split bounds (range
+// indices: split k owns ranges [s[k], s[k + 1])); upt = ranges per thread the widest split
+// needs with 256 threads (1, 2, 4, 8, 16).
+inline std::vector<int32_t> split_ranges(const std::vector<int32_t>& rs, const float* freq,
+                                         int ks, int& upt) {
+  const int g = (int)rs.size() - 1;
+  std::vector<double> cum(g + 1, 0.0);
+  for (int u = 0; u < g; ++u) {
+    double e = 0.0;
+    for (int i = rs[u]; i < rs[u + 1]; ++i) e += freq ? clamp_freq(freq[i]) : 1.0;
+    cum[u + 1] = cum[u] + e;
+  }
+  std::vector<int32_t> s(ks + 1, 0);
+  int u = 0;
+  for (int k = 1; k < ks; ++k) {
+    const double goal = cum[g] * k / ks;
+    while (u < g && cum[u] < goal) ++u;
+    s[k] = u;
+  }
+  s[ks] = g;
+  int widest = 0;
+  for (int k = 0; k < ks; ++k) widest = std::max(widest, s[k + 1] - s[k]);
+  upt = 1;
+  while (upt * 256 < widest && upt < 16) upt *= 2;
+  return s;
+}
+
+// Hot-first permutation, perm[new] = old: the n_hot neurons with the largest counts first,
+// by count descending and original index ascending on ties; the rest follow in ascending
+// original index. Requires 0 <= n_hot <= n.
+inline void hot_first_permutation(const int64_t* counts, int n, int n_hot, int32_t* perm) {
+  std::vector<int32_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::partial_sort(order.begin(), order.begin() + n_hot, order.end(),
+                    [counts](int32_t a, int32_t b) {
+                      return counts[a] != counts[b] ? counts[a] > counts[b] : a < b;
+                    });
+  std::vector<char> hot(n, 0);
+  for (int k = 0; k < n_hot; ++k) {
+    perm[k] = order[k];
+    hot[order[k]] = 1;
+  }
+  int k = n_hot;
+  for (int i = 0; i < n; ++i)
+    if (!hot[i]) perm[k++] = i;
+}
+
+// The smallest batch size b <= max_batch whose expected union of the tokens' predicted
+// sets, 1 - mean_i (1 - f_i)^b with the neurons' frequencies f_i and independent tokens,
+// exceeds the fraction dense_union; `never` when there is none (or dense_union <= 0).
+inline int dense_from_batch(const float* freq, int n, double dense_union, int max_batch,
+                            int never) {
+  if (!(dense_union > 0.0) || !freq || n <= 0) return never;
+  for (int b = 1; b <= max_batch; ++b) {
+    double u = 0.0;
+    for (int i = 0; i < n; ++i) u += 1.0 - std::pow(1.0 - clamp_freq(freq[i]), (double)b);
+    if (u / n > dense_union) return b;
+  }
+  return never;
+}
+
+}  // namespace host
+}  // namespace sffn
