@@ -571,7 +571,7 @@ void gather_launch(const LayerDev& L, const float* x, int B, const int32_t* idx,
                    const int32_t* count, const uint64_t* tokmask, float* y0, hipStream_t s) {
   const bool xl = x_in_lds(B, L.d);
   const size_t lds = xl ? (size_t)B * L.d * 4 : 0;
-  const int ny = L.ks_down > 1 ? B * L.d : 0;
+  const int ny = L.ks_vec > 1 ? B * L.d : 0;
   if (B == 1)
     hipLaunchKernelGGL((k_gather<F16, GATED, CPT, 1>), dim3(L.g_gather), dim3(TPB), lds, s,
                        L.w_act, L.act_ld, L.b_act, x, L.d, L.n, B, idx, count, tokmask, L.h_buf, xl ? 1 : 0,
@@ -597,10 +597,10 @@ template <bool F16, bool BITS, int TB, int UPT>
 void down_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                    int32_t* idx_out, int32_t* count_out, uint64_t* tok_out, float* y,
                    hipStream_t s, const hipEvent_t* tev) {
-  const int grid = down_blocks(L) * L.ks_down;
+  const int grid = down_blocks(L) * L.ks_vec;
   const size_t lds = BITS ? (size_t)LIST_CAP * 4 : 0;
   launch(k_down<F16, BITS, TB, UPT>, dim3(grid), dim3(TPB), lds, s, tev, L.w_down_t, L.down_ld, L.b_out,
-         L.h_buf, L.d, L.n, B, idx, count, L.wbits, L.rs, L.sa, L.tok_full, L.ks_down,
+         L.h_buf, L.d, L.n, B, idx, count, L.wbits, L.rs, L.sa_vec, L.tok_full, L.ks_vec,
          down_blocks(L), idx_out, count_out, tok_out, y);
 }
 
@@ -667,7 +667,7 @@ void down_any(const LayerDev& L, int B, const int32_t* idx, const int32_t* count
     return;
   }
 #define DOWN_BITS(TB)                                                                          \
-  switch (L.split_upt) {                                                                       \
+  switch (L.upt_vec) {                                                                         \
     case 1: down_launch_t<F16, true, TB, 1>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
     case 2: down_launch_t<F16, true, TB, 2>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \
     case 4: down_launch_t<F16, true, TB, 4>(L, B, idx, count, idx_out, count_out, tok_out, y, s, tev); break; \

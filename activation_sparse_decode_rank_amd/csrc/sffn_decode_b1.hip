@@ -289,13 +289,14 @@ __device__ __forceinline__ void down_rows_b1(const void* __restrict__ w_down_t,
 // The body of one workgroup (index bid) of the single-token down projection; the kernel
 // below runs it on every workgroup, and the look-ahead decode on the first ones of a launch
 // it shares with the next layer's scores.
-template <bool WF16, int UPT>
+template <bool WF16, int UPT, bool JOIN>
 __device__ __forceinline__ void down_b1_body(
     int bid, const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
-    float* __restrict__ y, const SplitArg& sa) {
+    float* __restrict__ y, const SplitArg& sa, float* __restrict__ dn_part = nullptr,
+    int32_t* __restrict__ dn_cnt = nullptr) {
   constexpr int EPC = Elt<WF16>::EPC;
   constexpr int COLS = CB_LANES * EPC;
   constexpr int PFX = G_MID_MAX / TPB;  // earlier-range words per thread
@@ -391,25 +392,10 @@ __device__ __forceinline__ void down_b1_body(
     for (int e = 0; e < EPC; ++e) s_red[wave][lane >> 4][li][e] = acc[e];
   }
   __syncthreads();
-  if (tid < COLS) {
-    const int c_li = tid / EPC, e = tid % EPC;
-    const int col = (cb * CB_LANES + c_li) * EPC + e;
-    if (col < d && (kq == 0 || total > 0)) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < TPB / 64; ++w2)
-#pragma unroll
-        for (int row = 0; row < 4; ++row) sum += s_red[w2][row][c_li][e];
-      if (kq == 0 && b_out) sum += b_out[col];
-      if (KS == 1)
-        y[col] = sum;
-      else
-        atomicAdd(y + col, sum);
-    }
-  }
   // the list: this split's rows sit at global positions gbase + k (gbase = active neurons
   // of all earlier ranges); workgroup cb publishes the positions k with k % ncb == cb
-  if (gbase < 0) {
+  auto publish_list = [&]() {
+    if (gbase >= 0) return;  // published window by window above
     int pc = 0;
 #pragma unroll
     for (int v = 0; v < PFX; ++v) pc += __popcll(pw[v]);
@@ -423,20 +409,73 @@ __device__ __forceinline__ void down_b1_body(
         if (tokmask_out) tokmask_out[gbase + k] = 1;
       }
     }
+  };
+  const int c_li = tid / EPC, e_c = tid % EPC;
+  const int col = (cb * CB_LANES + c_li) * EPC + e_c;
+  float sum = 0.f;
+  if (tid < COLS) {
+#pragma unroll
+    for (int w2 = 0; w2 < TPB / 64; ++w2)
+#pragma unroll
+      for (int row = 0; row < 4; ++row) sum += s_red[w2][row][c_li][e_c];
+    if (kq == 0 && b_out && col < d) sum += b_out[col];
+  }
+  if (JOIN && KS > 1) {
+    // Fixed-order join of the KS splits of column block cb, in place of float atomics
+    // into y: every split stores its sums in its own slot with device-coherent stores,
+    // publishes its part of the list while they land, waits for them, then takes a ticket
+    // from the block's counter. The split that arrives last reads the other slots back
+    // with device-coherent loads, writes y as the sum of all slots in split order and
+    // resets the counter for the next call.
+    __shared__ int s_last;
+    float* slot = dn_part + (size_t)cb * KS * COLS + tid;
+    if (tid < COLS) __hip_atomic_store(slot + kq * COLS, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish_list();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(dn_cnt + cb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == KS - 1;
+    __syncthreads();
+    if (s_last) {
+      asm volatile("" ::: "memory");
+      if (tid < COLS) {
+        float pv[KS_JOIN_MAX];
+#pragma unroll
+        for (int q = 0; q < KS_JOIN_MAX; ++q)
+          pv[q] = q < KS && q != kq ? __hip_atomic_load(slot + q * COLS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : sum;
+        float a = pv[0];
+#pragma unroll
+        for (int q = 1; q < KS_JOIN_MAX; ++q)
+          if (q < KS) a += pv[q];
+        if (col < d) y[col] = a;
+      }
+      if (tid == 0) __hip_atomic_store(dn_cnt + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    if (tid < COLS && col < d && (kq == 0 || total > 0)) {
+      if (KS == 1)
+        y[col] = sum;
+      else
+        atomicAdd(y + col, sum);
+    }
+    publish_list();
   }
   if (kq == KS - 1 && cb == 0 && tid == 0 && count_out) *count_out = gbase + total;
 }
 
-template <bool WF16, int UPT>
+template <bool WF16, int UPT, bool JOIN>
 __global__ __launch_bounds__(TPB) void k_down_b1(
     const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
     const int32_t* __restrict__ rs, int KS, int ncb, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out,
-    float* __restrict__ y, const SplitArg sa) {
+    float* __restrict__ y, const SplitArg sa, float* __restrict__ dn_part,
+    int32_t* __restrict__ dn_cnt) {
   touch_kernargs<2>();
-  down_b1_body<WF16, UPT>(blockIdx.x, w_down_t, ld_down, b_out, h_in, d, n, wbits, rs, KS, ncb, idx_out,
-                          count_out, tokmask_out, y, sa);
+  down_b1_body<WF16, UPT, JOIN>(blockIdx.x, w_down_t, ld_down, b_out, h_in, d, n, wbits,
+                                        rs, KS, ncb, idx_out, count_out, tokmask_out, y, sa,
+                                        dn_part, dn_cnt);
 }
 
 
@@ -545,7 +584,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, TPB),
 // next-layer ranges scored per workgroup: two halve the scoring workgroups at the cost of
 // one more serial score pass; three or four make that serial tail the longer role
 constexpr int LA_RPW = 2;
-template <bool F16, int UPT, int NCHP>
+template <bool F16, int UPT, int NCHP, bool JOIN>
 __global__ __launch_bounds__(TPB) void k_la_down(
     const void* __restrict__ w_down_t, int ld_down, const float* __restrict__ b_out,
     const float* __restrict__ h_in, int d, int n, const uint64_t* __restrict__ wbits,
@@ -553,13 +592,15 @@ __global__ __launch_bounds__(TPB) void k_la_down(
     int32_t* __restrict__ count_out, uint64_t* __restrict__ tokmask_out, float* __restrict__ y,
     int ndown, const void* __restrict__ p2n, const float* __restrict__ pbn,
     const float* __restrict__ qn, float taun, const int32_t* __restrict__ rsn, int gn,
-    uint64_t* __restrict__ wbits_n, int sfirst, const SplitArg sa) {
+    uint64_t* __restrict__ wbits_n, int sfirst, const SplitArg sa, float* __restrict__ dn_part,
+    int32_t* __restrict__ dn_cnt) {
   __shared__ uint8_t s_act[MID_RANGE_MAX];
   touch_kernargs<2>();
   const int nsc = (gn + LA_RPW - 1) / LA_RPW, bid = blockIdx.x;
   if (sfirst ? bid >= nsc : bid < ndown) {
-    down_b1_body<F16, UPT>(sfirst ? bid - nsc : bid, w_down_t, ld_down, b_out, h_in, d, n, wbits, rs,
-                            KS, ncb, idx_out, count_out, tokmask_out, y, sa);
+    down_b1_body<F16, UPT, JOIN>(sfirst ? bid - nsc : bid, w_down_t, ld_down, b_out, h_in, d, n,
+                                 wbits, rs, KS, ncb, idx_out, count_out, tokmask_out, y, sa,
+                                 dn_part, dn_cnt);
     return;
   }
   constexpr int ROW_BYTES = NCHP * 16;
@@ -676,9 +717,17 @@ int mid_b1_occ_any(const LayerDev& L) {
 template <bool F16, int UPT>
 void down_b1_launch(const LayerDev& L, int32_t* idx_out, int32_t* count_out, uint64_t* tok_out,
                     float* y, hipStream_t s, const hipEvent_t* tev) {
-  launch(k_down_b1<F16, UPT>, dim3(down_blocks(L) * L.ks_down), dim3(TPB), (size_t)LIST_CAP * 4,
-         s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.d, L.n, L.wbits, L.rs, L.ks_down,
-         down_blocks(L), idx_out, count_out, tok_out, y, L.sa);
+  const int ncb = down_blocks(L);
+  if (L.join_b1)
+    launch(k_down_b1<F16, UPT, true>, dim3(ncb * L.ks_down), dim3(TPB),
+           (size_t)LIST_CAP * 4, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.d, L.n,
+           L.wbits, L.rs, L.ks_down, ncb, idx_out, count_out, tok_out, y, L.sa, L.dn_part,
+           L.dn_cnt);
+  else
+    launch(k_down_b1<F16, UPT, false>, dim3(ncb * L.ks_down), dim3(TPB),
+           (size_t)LIST_CAP * 4, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.d, L.n,
+           L.wbits, L.rs, L.ks_down, ncb, idx_out, count_out, tok_out, y, L.sa, nullptr,
+           nullptr);
 }
 
 template <bool F16>
@@ -740,7 +789,7 @@ bool la_gather_any(const LayerDev& C, const LayerDev* Nx, const float* x, float*
   return false;
 }
 
-template <bool F16, int UPT, int NCHP>
+template <bool F16, int UPT, int NCHP, bool JOIN>
 void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                     uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   const int ncb = C ? down_blocks(*C) : 1;
@@ -748,33 +797,34 @@ void la_down_launch(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t
   const int nscore = Nx ? (Nx->g_mid + LA_RPW - 1) / LA_RPW : 0;
   SplitArg none{};
   const int sfirst = C && nscore > 0 && ndown + nscore > C->la_occ * C->n_cus ? 1 : 0;
-  launch(k_la_down<F16, UPT, NCHP>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
+  launch(k_la_down<F16, UPT, NCHP, JOIN>, dim3(ndown + nscore), dim3(TPB), (size_t)LIST_CAP * 4, s, tev,
          C ? C->w_down_t : nullptr, C ? C->down_ld : 0, C ? C->b_out : nullptr,
          C ? C->h_buf : nullptr,
          C ? C->d : 0, C ? C->n : 0, C ? C->wbits : nullptr, C ? C->rs : nullptr,
          C ? C->ks_down : 1, ncb, idx, count, tok, y, ndown, Nx ? Nx->p2 : nullptr,
          Nx ? Nx->p_bias : nullptr, Nx ? Nx->q : nullptr, Nx ? Nx->tau : 0.f,
          Nx ? Nx->rs : nullptr, Nx ? Nx->g_mid : 0, Nx ? Nx->wbits : nullptr, sfirst,
-         C ? C->sa : none);
+         C ? C->sa : none, C ? C->dn_part : nullptr, C ? C->dn_cnt : nullptr);
 }
 
-template <bool F16, int UPT>
+template <bool F16, int UPT, bool JOIN>
 bool la_down_nchp(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                   uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   switch (Nx ? Nx->r / (F16 ? 8 : 4) : 32) {
-    case 8: la_down_launch<F16, UPT, 8>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 16: la_down_launch<F16, UPT, 16>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 32: la_down_launch<F16, UPT, 32>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 64: la_down_launch<F16, UPT, 64>(C, Nx, idx, count, tok, y, s, tev); return true;
-    case 128: la_down_launch<F16, UPT, 128>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 8: la_down_launch<F16, UPT, 8, JOIN>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 16: la_down_launch<F16, UPT, 16, JOIN>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 32: la_down_launch<F16, UPT, 32, JOIN>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 64: la_down_launch<F16, UPT, 64, JOIN>(C, Nx, idx, count, tok, y, s, tev); return true;
+    case 128: la_down_launch<F16, UPT, 128, JOIN>(C, Nx, idx, count, tok, y, s, tev); return true;
     default: return false;
   }
 }
 
 template <bool F16, int UPT, int NCHP>
 int la_down_occ() {
+  // the join adds no registers or LDS that change the residency
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_la_down<F16, UPT, NCHP>, TPB,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_la_down<F16, UPT, NCHP, false>, TPB,
                                                    (size_t)LIST_CAP * 4) != hipSuccess)
     occ = 0;
   return occ;
@@ -791,23 +841,28 @@ int la_down_occ_nchp(int nchp) {
   }
 }
 
-template <bool F16>
+template <bool F16, bool JOIN>
 bool la_down_upt(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                  uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
   switch (C ? C->split_upt : 1) {
-    case 1: return la_down_nchp<F16, 1>(C, Nx, idx, count, tok, y, s, tev);
-    case 2: return la_down_nchp<F16, 2>(C, Nx, idx, count, tok, y, s, tev);
-    case 4: return la_down_nchp<F16, 4>(C, Nx, idx, count, tok, y, s, tev);
-    default: return la_down_nchp<F16, 8>(C, Nx, idx, count, tok, y, s, tev);
+    case 1: return la_down_nchp<F16, 1, JOIN>(C, Nx, idx, count, tok, y, s, tev);
+    case 2: return la_down_nchp<F16, 2, JOIN>(C, Nx, idx, count, tok, y, s, tev);
+    case 4: return la_down_nchp<F16, 4, JOIN>(C, Nx, idx, count, tok, y, s, tev);
+    default: return la_down_nchp<F16, 8, JOIN>(C, Nx, idx, count, tok, y, s, tev);
   }
 }
 
 // both roles share the weight type (checked by the caller)
 bool la_down_any(const LayerDev* C, const LayerDev* Nx, int32_t* idx, int32_t* count,
                  uint64_t* tok, float* y, hipStream_t s, const hipEvent_t* tev) {
+  // the down role joins its splits as the layer's decode step does, so that its y is the
+  // decode step's
   const bool f16 = C ? C->w_f16 : Nx->w_f16;
-  return f16 ? la_down_upt<true>(C, Nx, idx, count, tok, y, s, tev)
-             : la_down_upt<false>(C, Nx, idx, count, tok, y, s, tev);
+  if (C && C->join_b1)
+    return f16 ? la_down_upt<true, true>(C, Nx, idx, count, tok, y, s, tev)
+               : la_down_upt<false, true>(C, Nx, idx, count, tok, y, s, tev);
+  return f16 ? la_down_upt<true, false>(C, Nx, idx, count, tok, y, s, tev)
+             : la_down_upt<false, false>(C, Nx, idx, count, tok, y, s, tev);
 }
 
 }  // namespace

@@ -22,6 +22,8 @@ size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass) {
   b += align256(sk_cnt_bytes(n));                // sk_cnt
   if (single_pass) b += align256(bundle_part_bytes(d, n));  // part
   b += align256((size_t)(n + 1) * 4);            // dense_idx
+  b += align256((size_t)(d / 32 + 1) * KS_JOIN_MAX * 64 * 4);  // dn_part
+  b += align256((size_t)(d / 32 + 2) * 4);       // dn_cnt
   return b;
 }
 
@@ -42,6 +44,8 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass) {
   L.sk_cnt = reinterpret_cast<int32_t*>(take(sk_cnt_bytes(n)));
   L.part = single_pass ? reinterpret_cast<float*>(take(bundle_part_bytes(L.d, n))) : nullptr;
   L.dense_idx = reinterpret_cast<int32_t*>(take((size_t)(n + 1) * 4));
+  L.dn_part = reinterpret_cast<float*>(take((size_t)(L.d / 32 + 1) * KS_JOIN_MAX * 64 * 4));
+  L.dn_cnt = reinterpret_cast<int32_t*>(take((size_t)(L.d / 32 + 2) * 4));
   L.n_tiles = n_tiles;
 }
 
@@ -96,6 +100,7 @@ bool shape_supported(const LayerDev& L, bool fused) {
     if (L.g_mid < 1 || L.g_mid > G_MID_MAX) return false;
     if (L.split_upt < 1 || L.split_upt > 8) return false;  // the down kernel's word registers
     if (L.ks_down < 1 || L.ks_down > KS_MAX) return false;
+    if (L.upt_vec < 1 || L.upt_vec > 8 || L.ks_vec < 1 || L.ks_vec > KS_MAX) return false;
   }
   return true;
 }
@@ -183,11 +188,14 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     run_stage1(L, x, 1, s, t1, nullptr, 0, false);
     if (run_bundle_b1(L, x, y, idx, count, tokmask, scores, s, t2, t3)) return hipGetLastError();
   }
-  run_stage1(L, x, B, s, t1, y, L.ks_down > 1 ? B * L.d : 0, false);
-  if (B == 1 && run_mid_b1(L, x, scores, s, t2)) {
+  // stage 1 clears y where the down projection adds its splits into it
+  if (B == 1 && L.b1_ok) {
+    run_stage1(L, x, 1, s, t1, y, L.ks_down > 1 && !L.join_b1 ? L.d : 0, false);
+    run_mid_b1(L, x, scores, s, t2);
     run_down_b1(L, idx, count, tokmask, y, s, t3);
     return hipGetLastError();
   }
+  run_stage1(L, x, B, s, t1, y, L.ks_vec > 1 ? B * L.d : 0, false);
   run_mid_batch(L, x, B, scores, s, t2);
   run_down(L, B, true, nullptr, nullptr, idx, count, tokmask, y, s, t3);
   return hipGetLastError();

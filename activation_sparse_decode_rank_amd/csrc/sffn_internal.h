@@ -24,6 +24,8 @@ constexpr int KS_MAX = 16;
 // rows one workgroup of the single-token down projection gathers in one batch (32 row
 // slots x 16 rows in flight each)
 constexpr int DOWN_B1_BATCH = 512;
+// most splits the single-token down projection's fixed-order join takes
+constexpr int KS_JOIN_MAX = 8;
 struct SplitArg {
   int32_t s[KS_MAX + 1];
 };
@@ -62,6 +64,10 @@ struct LayerDev {
   int n_cus;     // compute units on the device
   int ks_down;   // row splits of the down projection (1 = plain stores; 2 keeps y bitwise
                  // reproducible; more adds float atomics in a varying order)
+  bool join_b1;  // the single-token down projection's splits meet in a fixed-order join
+                 // (dn_part, dn_cnt) instead of float atomics
+  float* dn_part;   // [ceil(d / 32) + 1][KS_JOIN_MAX][64] split sums of that join
+  int32_t* dn_cnt;  // [ceil(d / 32) + 2] its arrival counters (zero between calls)
   int ks_tile;   // the same for the batch (matrix-core) down projection
   int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64, plus 64)
   int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
@@ -70,6 +76,11 @@ struct LayerDev {
   RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)
   SplitArg sa;     // decode down projection: range splits, ks_down of them
   int split_upt;   // most ranges of one split per thread of the down kernel (1, 2, 4, 8)
+  bool b1_ok;      // the single-token kernels cover this layer (else one token takes the
+                   // vector path)
+  int ks_vec;      // the same three for the vector down projection (batches, and one token
+  SplitArg sa_vec; // where the single-token kernels do not apply), which joins its splits
+  int upt_vec;     // with float atomics only: at most two in the deterministic mode
   int la_occ;      // workgroups per compute unit of the look-ahead down launch (0: unknown)
   bool single_pass;  // single-token decode through the bundle pass (sffn_bundle.hip)
   int max_batch;     // tokens the workspace is sized for

@@ -22,15 +22,18 @@ std::mutex g_mu;
 void* g_ptr[MAX_DEVICES] = {};
 
 // Writes entries [off, off + cnt) of the range table from the arguments (at most
-// RS_ARG_MAX + 1 per launch) and, from the first launch, zeroes the stream-K arrival
-// counters (every call leaves them zero, but the array keeps whatever the last call on
-// this device left, and nothing here may assume who that was).
+// RS_ARG_MAX + 1 per launch) and, from the first launch, zeroes the arrival counters of the
+// stream-K up projection and of the down projection's join (every call leaves them zero,
+// but the array keeps whatever the last call on this device left, and nothing here may
+// assume who that was).
 __global__ __launch_bounds__(TPB) void k_static_prologue(const RangeArg part, int off, int cnt,
                                                          int32_t* __restrict__ rs,
-                                                         int32_t* __restrict__ sk_cnt, int ncnt) {
+                                                         int32_t* __restrict__ sk_cnt, int ncnt,
+                                                         int32_t* __restrict__ dn_cnt, int ndn) {
   const int i = blockIdx.x * TPB + threadIdx.x;
   if (i < cnt) rs[off + i] = part.r[i];
   for (int j = i; j < ncnt; j += gridDim.x * TPB) sk_cnt[j] = 0;
+  for (int j = i; j < ndn; j += gridDim.x * TPB) dn_cnt[j] = 0;
 }
 
 }  // namespace
@@ -57,13 +60,15 @@ hipError_t run_decode_static(const LayerDev& H, const int32_t* rs_host, int g, v
   LayerDev L = H;
   carve_workspace(L, base, B, H.single_pass);
   const int ncnt = (L.n + 15) / 16 + 1;
+  const int ndn = L.d / 32 + 2;
   for (int off = 0; off <= g; off += RS_ARG_MAX + 1) {
     const int cnt = std::min(RS_ARG_MAX + 1, g + 1 - off);
     RangeArg part{};
     std::copy(rs_host + off, rs_host + off + cnt, part.r);
-    const int items = off == 0 ? std::max(cnt, ncnt) : cnt;
+    const int items = off == 0 ? std::max(cnt, std::max(ncnt, ndn)) : cnt;
     hipLaunchKernelGGL(k_static_prologue, dim3((items + TPB - 1) / TPB), dim3(TPB), 0, s, part,
-                       off, cnt, L.rs, L.sk_cnt, off == 0 ? ncnt : 0);
+                       off, cnt, L.rs, L.sk_cnt, off == 0 ? ncnt : 0, L.dn_cnt,
+                       off == 0 ? ndn : 0);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
