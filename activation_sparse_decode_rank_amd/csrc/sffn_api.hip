@@ -66,6 +66,15 @@ void split_ranges(const std::vector<int32_t>& rs, const float* freq, int ks, sff
   std::copy(s.begin(), s.end(), sa.s);
 }
 
+// compute units of the current device; 0 when there is none (sizes then cover any device)
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,7 +94,7 @@ const char* sparse_ffn_status_string(int status) {
 size_t sparse_ffn_workspace_bytes(const sffn_desc* desc) {
   if (check_desc(desc) != SFFN_OK) return 0;
   return sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch,
-                               desc->single_pass != 0);
+                               desc->single_pass != 0, device_cus());
 }
 
 int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
@@ -97,8 +106,12 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     if (rc != SFFN_OK) return rc;
     const bool has_ws = desc->workspace != nullptr;
     const size_t need = sffn::workspace_bytes(desc->d, desc->d_ffn, desc->rank, desc->max_batch,
-                                              desc->single_pass != 0);
+                                              desc->single_pass != 0, device_cus());
     if (has_ws && desc->workspace_bytes < need) return SFFN_ERR_INVALID;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SFFN_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return SFFN_ERR_HIP;
 
     sffn::LayerDev L{};
     L.d = desc->d;
@@ -136,20 +149,19 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     L.p1 = desc->p1;
     L.p2 = desc->p2;
     L.p_bias = desc->p_bias;
+    L.n_cus = cus;
     sffn::carve_workspace(L, desc->workspace, desc->max_batch, L.single_pass);
     if (!sffn::shape_supported(L, false)) return SFFN_ERR_UNSUPPORTED;
 
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SFFN_ERR_HIP;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return SFFN_ERR_HIP;
-    L.n_cus = cus;
     // the static scratch array's address on this device (looked up once per device); a
     // handle without a workspace has no other device memory to run on
     if (!sffn::static_scratch_setup(dev) && !has_ws) return SFFN_ERR_HIP;
     L.g_gather = std::max(1, 2 * cus);
     L.ks_down = sffn::down_split(L, desc->deterministic != 0);
-    L.ks_tile = sffn::tile_split(L, desc->deterministic != 0);
+    L.ks_tile = sffn::tile_split(L);
+    // deterministic mode: two splits add into y exactly in either order; more meet in the
+    // fixed-order join
+    L.join_tile = desc->deterministic && L.ks_tile > 2;
     L.g_up = std::max(1, std::min((desc->d_ffn + 15) / 16, 4 * cus));
     // stream-K up projection: two workgroups per compute unit, and enough that one
     // range touches at most 13 tiles of the largest list
@@ -358,7 +370,8 @@ int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y
   if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID;
   if (!sffn::shape_supported(h->L, true) || h->rs_host.empty()) return SFFN_ERR_UNSUPPORTED;
-  if (sffn::workspace_bytes(h->L.d, h->L.n, h->L.r, B, h->L.single_pass) > sffn::STATIC_SCRATCH_BYTES)
+  if (sffn::workspace_bytes(h->L.d, h->L.n, h->L.r, B, h->L.single_pass, h->L.n_cus) >
+      sffn::STATIC_SCRATCH_BYTES)
     return SFFN_ERR_TOO_LARGE;
   void* base = sffn::static_scratch_ptr(h->device);
   if (!base) return SFFN_ERR_HIP;

@@ -9,7 +9,27 @@ static size_t x_hl_bytes(int d, int max_batch) { return (size_t)2 * (d / 8) * ma
 static size_t sk_part_bytes(int max_batch) { return max_batch >= TILE_MIN_B ? SK_PART_BYTES : 0; }
 static size_t sk_cnt_bytes(int n) { return (size_t)((n + 15) / 16 + 1) * 4; }
 
-size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass) {
+int tile_split(int d, int n_cus) {
+  const int ncb = (d + 63) / 64;
+  return std::max(1, std::min(KS_JOIN_MAX, (n_cus + ncb / 2) / ncb));
+}
+
+// the down projections' join slots: up to KS_JOIN_MAX per column block of 64 outputs
+// (single token: blocks of 32 or 64 columns), and for the matrix-core down projection,
+// when it joins (more than two splits), one slot of 64 columns x 16 tokens per token tile
+// for each of its workgroups (n_cus 0: the most splits any device could take)
+size_t dn_part_bytes(int d, int max_batch, int n_cus) {
+  const size_t b1 = (size_t)(d / 32 + 1) * KS_JOIN_MAX * 64 * 4;
+  size_t tiles = 0;
+  if (max_batch >= TILE_MIN_B) {
+    const int ks = n_cus > 0 ? tile_split(d, n_cus) : KS_JOIN_MAX;
+    const size_t nt = (size_t)(std::min(max_batch, MAXB) + 15) / 16;
+    if (ks > 2) tiles = (size_t)((d + 63) / 64) * ks * nt * 1024 * 4;
+  }
+  return std::max(b1, tiles);
+}
+
+size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass, int n_cus) {
   size_t b = 0;
   b += align256((size_t)max_batch * r * 4);      // q
   b += align256((size_t)((n + 63) / 64 * 64 + 64) * max_batch * 4);  // h_buf ([n][B], or [B][ldh])
@@ -22,7 +42,7 @@ size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass) {
   b += align256(sk_cnt_bytes(n));                // sk_cnt
   if (single_pass) b += align256(bundle_part_bytes(d, n));  // part
   b += align256((size_t)(n + 1) * 4);            // dense_idx
-  b += align256((size_t)(d / 32 + 1) * KS_JOIN_MAX * 64 * 4);  // dn_part
+  b += align256(dn_part_bytes(d, max_batch, n_cus));  // dn_part
   b += align256((size_t)(d / 32 + 2) * 4);       // dn_cnt
   return b;
 }
@@ -44,7 +64,7 @@ void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass) {
   L.sk_cnt = reinterpret_cast<int32_t*>(take(sk_cnt_bytes(n)));
   L.part = single_pass ? reinterpret_cast<float*>(take(bundle_part_bytes(L.d, n))) : nullptr;
   L.dense_idx = reinterpret_cast<int32_t*>(take((size_t)(n + 1) * 4));
-  L.dn_part = reinterpret_cast<float*>(take((size_t)(L.d / 32 + 1) * KS_JOIN_MAX * 64 * 4));
+  L.dn_part = reinterpret_cast<float*>(take(dn_part_bytes(L.d, max_batch, L.n_cus)));
   L.dn_cnt = reinterpret_cast<int32_t*>(take((size_t)(L.d / 32 + 2) * 4));
   L.n_tiles = n_tiles;
 }
@@ -64,12 +84,7 @@ int down_blocks(const LayerDev& L) {
   return (nch + CB_LANES - 1) / CB_LANES;
 }
 
-int tile_split(const LayerDev& L, bool deterministic) {
-  const int ncb = (L.d + 63) / 64;
-  int ks = std::max(1, std::min(8, (L.n_cus + ncb / 2) / ncb));
-  if (deterministic) ks = std::min(ks, 2);
-  return ks;
-}
+int tile_split(const LayerDev& L) { return tile_split(L.d, L.n_cus); }
 
 int down_split(const LayerDev& L, bool deterministic) {
   const int ncb = down_blocks(L);
@@ -161,7 +176,7 @@ hipError_t launch_decode(const LayerDev& L, const float* x, int B, float* y, int
     // words do not fit its LDS); else scores and two compaction passes, the scores going
     // to the caller's buffer or, when none is given, to the activation buffer, which the
     // up projection only overwrites after compaction has read them; then the tiles
-    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 ? B * L.d : 0, true);
+    run_stage1(L, x, B, s, t1, y, L.ks_tile > 1 && !L.join_tile ? B * L.d : 0, true);
     hipError_t e;
     bool fw = false;
     if (score_tiles_ok(L, B)) {

@@ -66,9 +66,10 @@ struct LayerDev {
                  // reproducible; more adds float atomics in a varying order)
   bool join_b1;  // the single-token down projection's splits meet in a fixed-order join
                  // (dn_part, dn_cnt) instead of float atomics
-  float* dn_part;   // [ceil(d / 32) + 1][KS_JOIN_MAX][64] split sums of that join
+  float* dn_part;   // split sums of the down projections' joins (dn_part_bytes)
   int32_t* dn_cnt;  // [ceil(d / 32) + 2] its arrival counters (zero between calls)
   int ks_tile;   // the same for the batch (matrix-core) down projection
+  bool join_tile;  // its splits meet in the fixed-order join (deterministic mode, ks_tile > 2)
   int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64, plus 64)
   int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
   int g_sk;      // workgroups of its stream-K form (at most SK_G_MAX)
@@ -90,12 +91,16 @@ struct LayerDev {
 
 // workspace sizing (bytes) for a layer shape; mirrors the carve-up in carve_workspace
 // (single_pass: also the partial outputs of the single-pass decode)
-size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass);
+// (n_cus: compute units of the device, which sets the matrix-core down projection's
+// splits; 0 sizes for any device). carve_workspace reads L.n_cus.
+size_t workspace_bytes(int d, int n, int r, int max_batch, bool single_pass, int n_cus);
 void carve_workspace(LayerDev& L, void* ws, int max_batch, bool single_pass);
+// row splits of the matrix-core down projection for a width d on n_cus compute units
+int tile_split(int d, int n_cus);
 // 128-byte column blocks of the down projection, and the row split it should use
 int down_blocks(const LayerDev& L);
 int down_split(const LayerDev& L, bool deterministic);
-int tile_split(const LayerDev& L, bool deterministic);
+int tile_split(const LayerDev& L);
 // whether kernels exist for this shape (fused = the single-call decode path)
 bool shape_supported(const LayerDev& L, bool fused);
 // middle-kernel workgroups that can be resident at once (all CUs), for batches up to max_batch

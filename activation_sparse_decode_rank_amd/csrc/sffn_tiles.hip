@@ -923,17 +923,20 @@ __global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, in
 // v_mfma_f32_16x16x32_f16; the activations (token l%16, positions
 // 8*(l/16)..+7) are the left one, as a hi + lo fp16 pair. No workgroup barrier in the
 // loop; loads run one batch of KB chunks ahead. At the end the four waves' sums are added
-// in wave order through LDS and leave as in k_down: plain stores for KS == 1, else float
-// atomics onto y zeroed earlier in the call, b_out riding on kq == 0.
+// in wave order through LDS and leave as plain stores for KS == 1; else as float atomics
+// onto y zeroed earlier in the call, or (JOIN) through the fixed-order join of the splits
+// described at the single-token down projection, b_out riding on kq == 0.
 constexpr int DCH = 32;         // positions per chunk (one k-step)
 constexpr int IDX_CAP = 4096;   // list window held in LDS (a multiple of DCH)
-template <int NT>
+template <int NT, bool JOIN>
 __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_down_t, int ld_down,
                                                    const float* __restrict__ b_out,
                                                    const float* __restrict__ hT, int ldh, int d,
                                                    int n, int B, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ count, int KS,
-                                                   float* __restrict__ y) {
+                                                   float* __restrict__ y,
+                                                   float* __restrict__ dn_part,
+                                                   int32_t* __restrict__ dn_cnt) {
   constexpr int KB = NT <= 2 ? 2 : 1;   // chunks per load batch
   // chunk buffer: [32 positions][64 columns] fp16 at a pitch of 33 words, so a wave's gather
   // of one position row per lane group (8 rows apart) touches all 32 banks
@@ -1082,7 +1085,66 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) s_acc[wave][cg][tt][lane] = acc[cg][tt];
   __syncthreads();
-  if (kq == 0 || p1 > p0) {
+  if (JOIN && KS > 1) {
+    // every split takes part, an empty one with zeros; slot o of split kq holds output o
+    constexpr int NO = 4 * NT * 64;
+    __shared__ int s_last;
+    float* slot = dn_part + (size_t)cb * KS * NO * 4;
+    float4_t mine[NT];
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int o = it * TPB + tid;
+      const int cg = o / (NT * 64), tt = (o / 64) % NT, l = o % 64;
+      const int col = cb * 64 + 16 * cg + (l & 15);
+      const float bo = (kq == 0 && b_out && col < d) ? b_out[col] : 0.f;
+      mine[it] = ((s_acc[0][cg][tt][l] + s_acc[1][cg][tt][l]) + s_acc[2][cg][tt][l]) +
+                 s_acc[3][cg][tt][l];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mine[it][j] += bo;
+        __hip_atomic_store(slot + ((size_t)kq * NO + o) * 4 + j, mine[it][j], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(dn_cnt + cb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == KS - 1;
+    __syncthreads();
+    if (s_last) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        const int o = it * TPB + tid;
+        const int cg = o / (NT * 64), tt = (o / 64) % NT, l = o % 64;
+        const int col = cb * 64 + 16 * cg + (l & 15);
+        float4_t pv[KS_JOIN_MAX];
+#pragma unroll
+        for (int q = 0; q < KS_JOIN_MAX; ++q) {
+          if (q < KS && q != kq) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              pv[q][j] = __hip_atomic_load(slot + ((size_t)q * NO + o) * 4 + j, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            pv[q] = mine[it];
+          }
+        }
+        float4_t a = pv[0];
+#pragma unroll
+        for (int q = 1; q < KS_JOIN_MAX; ++q)
+          if (q < KS) a += pv[q];
+        if (col < d) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int b = 16 * tt + 4 * (l >> 4) + j;
+            if (b < B) y[(size_t)b * d + col] = a[j];
+          }
+        }
+      }
+      if (tid == 0) __hip_atomic_store(dn_cnt + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (kq == 0 || p1 > p0) {
     // 4 * NT * 64 outputs, NT per thread: a fixed trip count, so the b_out loads of all
     // of them go out together
     static_assert(4 * 64 == TPB, "one output per thread and token tile");
@@ -1215,14 +1277,25 @@ void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t*
   }
 }
 
+template <int NT>
+void down_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
+                        float* y, hipStream_t s, const hipEvent_t* tev) {
+  const dim3 grid(((L.d + 63) / 64) * L.ks_tile);
+  if (L.join_tile)
+    launch(k_down_mfma<NT, true>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out,
+           L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y, L.dn_part, L.dn_cnt);
+  else
+    launch(k_down_mfma<NT, false>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out,
+           L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y, nullptr, nullptr);
+}
+
 void down_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                       float* y, hipStream_t s, const hipEvent_t* tev) {
-  const dim3 grid(((L.d + 63) / 64) * L.ks_tile);
   switch ((B + 15) / 16) {
-    case 1: launch(k_down_mfma<1>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 2: launch(k_down_mfma<2>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    case 3: launch(k_down_mfma<3>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
-    default: launch(k_down_mfma<4>, grid, dim3(TPB), 0, s, tev, L.w_down_t, L.down_ld, L.b_out, L.h_buf, L.ldh, L.d, L.n, B, idx, count, L.ks_tile, y); break;
+    case 1: down_tile_launch_t<1>(L, B, idx, count, y, s, tev); break;
+    case 2: down_tile_launch_t<2>(L, B, idx, count, y, s, tev); break;
+    case 3: down_tile_launch_t<3>(L, B, idx, count, y, s, tev); break;
+    default: down_tile_launch_t<4>(L, B, idx, count, y, s, tev); break;
   }
 }
 
@@ -1233,7 +1306,7 @@ void forward_tiles(const LayerDev& L, const float* x, int B, const int32_t* idx,
                    const int32_t* count, const uint64_t* tokmask, const uint64_t* tok_by_neuron,
                    float* y, bool zero_y, bool fw, hipStream_t s, const hipEvent_t* t_up,
                    const hipEvent_t* t_down) {
-  const int ny = (zero_y && L.ks_tile > 1) ? B * L.d : 0;
+  const int ny = (zero_y && L.ks_tile > 1 && !L.join_tile) ? B * L.d : 0;
   if (zero_y) {
     const int items = L.d / 8 * B;
     hipLaunchKernelGGL(k_split_x, dim3((items + TPB - 1) / TPB), dim3(TPB), 0, s, x, B, L.d, B,

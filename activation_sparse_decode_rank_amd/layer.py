@@ -72,8 +72,9 @@ class SparseFFN:
     w_down_t: [n, d] W_down transposed; p1: [r, d]; p2: [n, r]; biases fp32.
     profile_x: [N, d] fp32 profiling tokens; when given, neurons are profiled and the
     hottest ceil(hot_frac * n) packed first, and their frequencies balance the work split.
-    deterministic: keep y bitwise reproducible from run to run (slightly slower down
-    projection); otherwise the fastest split, whose y may vary in the last bits.
+    deterministic: keep y bitwise reproducible from run to run (the default: the down
+    projection's splits are summed in a fixed order); False lets them add into y with float
+    atomics, a few percent faster, and y may then vary in the last bits.
     bundle: store each neuron's rows together ([gate,] up, down: one [n, m, d] tensor, the
     PowerInfer-2 neuron bundle) instead of separate matrices.
     single_pass: the single-token decode gathers each active neuron's input and down rows in
@@ -87,7 +88,7 @@ class SparseFFN:
     def __init__(self, *, w_act, w_down_t, p1, p2, b_act=None, b_out=None, p_bias=None,
                  w_up=None, threshold: float = 0.0, max_batch: int = 1,
                  profile_x: Optional[torch.Tensor] = None, hot_frac: float = 0.2,
-                 perm: Optional[np.ndarray] = None, deterministic: bool = False,
+                 perm: Optional[np.ndarray] = None, deterministic: bool = True,
                  bundle: bool = False, single_pass: bool = False, dense_union: float = 0.0,
                  stream=None):
         dev = w_act.device

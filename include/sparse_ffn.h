@@ -122,11 +122,15 @@ typedef struct {
                                neuron (e.g. profile counts / profile tokens). Read only by
                                sparse_ffn_create, to cut the neurons into contiguous ranges
                                of about equal expected work. NULL = every neuron equal. */
-  int32_t deterministic;    /* 1: y is bitwise reproducible from run to run (the down
-                               projection splits the active rows at most two ways);
-                               0: fastest (its row splits add into y with float atomics,
-                               so the last bits of y can vary between runs). Index lists,
-                               counts and token bits are bit-exact either way. */
+  int32_t deterministic;    /* 1 (recommended; the Python layer's default): y is bitwise
+                               reproducible from run to run. The down projection's row
+                               splits are summed in a fixed order: two add into a zeroed y
+                               (exact in either order), more hand their sums to the
+                               column block's last-arriving workgroup, which adds them in
+                               split order. 0: the splits add into y with float atomics
+                               (a few percent faster; the last bits of y can vary between
+                               runs). Index lists, counts and token bits are bit-exact
+                               either way. */
   int32_t layout;           /* sffn_layout: SFFN_LAYOUT_SPLIT (0) or SFFN_LAYOUT_BUNDLE (1) */
   int32_t single_pass;      /* 1: the single-token decode (sparse_ffn_decode at B = 1, and its
                                static form) gathers each active neuron's input rows and down
@@ -157,11 +161,14 @@ typedef struct {
 
 /* Bytes of device workspace a descriptor needs (0 if the descriptor is invalid). The
  * workspace holds predictor intermediates, per-neuron activations, compaction state,
- * partial sums of tiles split between workgroups, a small table of neuron ranges that
- * sparse_ffn_create writes and every later call reads, and tile counters that
- * sparse_ffn_create zeroes and every call leaves at zero (both synchronously, at create).
- * Give each handle its own workspace, and order the calls on one handle (a call that
- * overlaps another on the same workspace races with it). */
+ * partial sums of tiles and of down-projection splits that workgroups hand to each other,
+ * a small table of neuron ranges that sparse_ffn_create writes and every later call reads,
+ * and arrival counters that sparse_ffn_create zeroes and every call leaves at zero (both
+ * synchronously, at create). The size depends on the current device's compute-unit count
+ * (it sets how many splits the down projection takes): query it with the device current
+ * that the handle will be created on; with no device it covers any. Give each handle its
+ * own workspace, and order the calls on one handle (a call that overlaps another on the
+ * same workspace races with it). */
 size_t sparse_ffn_workspace_bytes(const sffn_desc* desc);
 
 /* Validate `desc` and create a handle (host metadata only). Queries the current HIP device

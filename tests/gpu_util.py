@@ -32,8 +32,9 @@ def rel_err_rows(y, ref):
 
 def build(cfg, layer=0, *, d=None, n=None, rank=None, activity=None, max_batch=1,
           nonzero_b_o=True, profile_tokens=256, hot_frac=None, threshold=0.0, pack=True,
-          gen_device="cuda", deterministic=False, bundle=False, single_pass=False):
-    """Generate a layer (original order) and a SparseFFN over it; returns (sffn, L_np, Lt)."""
+          gen_device="cuda", deterministic=True, bundle=False, single_pass=False):
+    """Generate a layer (original order) and a SparseFFN over it; returns (sffn, L_np, Lt).
+    deterministic defaults to the library's own default (True)."""
     from activation_sparse_decode_rank_amd import SparseFFN
     from synth import make_layer, make_tokens
     Lt = make_layer(cfg, layer, gen_device, nonzero_b_o=nonzero_b_o, d=d, n=n, rank=rank,

@@ -84,6 +84,14 @@ def _valid_desc(N, **over):
     return D
 
 
+def test_python_layer_defaults_to_deterministic():
+    """The Python layer's default mode keeps y bitwise reproducible (fixed-order joins of
+    the down projection's splits, no float atomics into y)."""
+    import inspect
+    from activation_sparse_decode_rank_amd import SparseFFN
+    assert inspect.signature(SparseFFN.__init__).parameters["deterministic"].default is True
+
+
 def test_workspace_bytes(N):
     D = _valid_desc(N)
     ws = N.sparse_ffn_workspace_bytes(D)
