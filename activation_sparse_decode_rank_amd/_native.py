@@ -14,6 +14,7 @@ SFFN_OK, SFFN_ERR_INVALID, SFFN_ERR_UNSUPPORTED, SFFN_ERR_HIP, SFFN_ERR_TOO_LARG
 SFFN_STATIC_SCRATCH_BYTES = 16 << 20
 SFFN_F32, SFFN_F16 = 0, 1
 SFFN_LAYOUT_SPLIT, SFFN_LAYOUT_BUNDLE = 0, 1
+SFFN_UP_ROWS, SFFN_UP_COLUMNS = 0, 1
 SFFN_MAX_BATCH = 64
 
 
@@ -62,6 +63,8 @@ def _load():
         "sparse_ffn_permutation": (C.c_int, [P, I32, I32, P]),
         "sparse_ffn_pack_rows": (C.c_int, [P, P, P, I32, I64, I64, P]),
         "sparse_ffn_read_probe": (C.c_int, [P, SZ, I32, P, P]),
+        "sparse_ffn_up_probe_work_bytes": (SZ, [I32]),
+        "sparse_ffn_up_probe": (C.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -77,7 +80,7 @@ EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destr
             "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
-            "sparse_ffn_read_probe")
+            "sparse_ffn_read_probe", "sparse_ffn_up_probe_work_bytes", "sparse_ffn_up_probe")
 
 
 def lib():
@@ -163,3 +166,13 @@ def sparse_ffn_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes, stre
 
 def sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream) -> None:
     _ck(_lib.sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream), "sparse_ffn_read_probe")
+
+
+def sparse_ffn_up_probe_work_bytes(d_ffn) -> int:
+    return int(_lib.sparse_ffn_up_probe_work_bytes(d_ffn))
+
+
+def sparse_ffn_up_probe(w_up, layout, d, d_ffn, x, idx, count, words, u, work, work_bytes,
+                        stream) -> None:
+    _ck(_lib.sparse_ffn_up_probe(w_up, layout, d, d_ffn, x, idx, count, words, u, work,
+                                 work_bytes, stream), "sparse_ffn_up_probe")

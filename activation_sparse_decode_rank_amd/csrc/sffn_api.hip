@@ -431,6 +431,30 @@ int sparse_ffn_pack_rows(const void* src, const int32_t* perm, void* dst, int32_
              : SFFN_ERR_HIP;
 }
 
+size_t sparse_ffn_up_probe_work_bytes(int32_t d_ffn) {
+  return d_ffn > 0 ? sffn::up_probe_work_bytes(d_ffn) : 0;
+}
+
+int sparse_ffn_up_probe(const void* w_up, int32_t layout, int32_t d, int32_t d_ffn,
+                        const float* x, const int32_t* idx, const int32_t* count,
+                        const uint64_t* words, float* u, void* work, size_t work_bytes,
+                        void* stream) {
+  if (!w_up || !x || !u || d <= 0 || d_ffn <= 0 || d % 8 != 0 || d > 16384) return SFFN_ERR_INVALID;
+  if (!aligned16(w_up) || !aligned16(x)) return SFFN_ERR_INVALID;
+  if (layout == SFFN_UP_ROWS) {
+    if (!idx || !count) return SFFN_ERR_INVALID;
+  } else if (layout == SFFN_UP_COLUMNS) {
+    if (!words || !work || d_ffn % 8 != 0 || work_bytes < sffn::up_probe_work_bytes(d_ffn))
+      return SFFN_ERR_INVALID;
+  } else {
+    return SFFN_ERR_INVALID;
+  }
+  return sffn::launch_up_probe(w_up, layout, d, d_ffn, x, idx, count, words, u, work,
+                               static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
 int sparse_ffn_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                           void* stream) {
   if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || workgroups < 0) return SFFN_ERR_INVALID;

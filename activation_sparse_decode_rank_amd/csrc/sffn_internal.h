@@ -225,6 +225,11 @@ hipError_t launch_fill_list(const LayerDev& L, int B, int32_t* idx, int32_t* cou
 hipError_t launch_dense(const LayerDev& L, const float* x, int B, float* y, hipStream_t s);
 // sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
 // number of workgroups; sink [workgroups] is written only in a practically impossible case
+// input-sparse up projection probe: layout 0 rows [n][d], 1 columns [d][n] (fp16)
+size_t up_probe_work_bytes(int n);
+hipError_t launch_up_probe(const void* w, int layout, int d, int n, const float* x,
+                           const int32_t* idx, const int32_t* count, const uint64_t* words,
+                           float* u, void* work, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
                              hipStream_t s);
 

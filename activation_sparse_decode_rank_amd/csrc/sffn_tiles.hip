@@ -1,6 +1,6 @@
 // Predictor scores, threshold and compaction as separate kernels (the standalone entry
 // points and the batch path), and the gathered-tile up and down projections on the matrix
-// cores for batches of 9 or more tokens (gfx950).
+// cores for batches of 2 or more tokens with fp16 weights and d a multiple of 256 (gfx950).
 #include "sffn_device.h"
 
 namespace sffn {

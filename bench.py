@@ -36,6 +36,9 @@ Also measured, beside the headline number:
   - the predictor's recall and precision against the true ReLU signs (a diagnostic of the
     synthetic calibrated predictor, not graded);
   - for the default workload, the same stack on its 5% -> 10% ramp (`c2_ramp`);
+  - the up projection of the gated Llama-7B shape, whose input is about half zeros, as
+    the decode path's row gather against a column-major W_u that skips the zero inputs
+    (`input_sparse_up`);
   - the sparse decode against the dense route (every neuron, no predictor) on the
     Llama-7B-shaped gated stack at 16-64 tokens, where the union of the tokens' sets grows,
     and the dense route as 512-token prefill against torch (`dense_crossover`);
@@ -330,6 +333,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the all-active, fast-mode, single-pass, recall, ramp and "
                          "crossover legs")
+    ap.add_argument("--no-input-sparse", action="store_true",
+                    help="skip the input-sparse up projection comparison (rows vs columns)")
     ap.add_argument("--no-crossover", action="store_true",
                     help="skip the sparse-vs-dense crossover on the gated batch stack")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -734,10 +739,13 @@ def main():
         layers = originals = None  # free the headline stack before building the ramp's
         ramp = run_ramp(torch, args, timer, dense)
 
-    crossover = None
+    crossover = input_sparse = None
     if not args.no_extra and not args.no_crossover and B == 1:
         layers = originals = None
         crossover = run_crossover(torch, args, cap)
+    if not args.no_extra and not args.no_input_sparse and B == 1:
+        layers = originals = None
+        input_sparse = run_input_sparse_up(torch, args, NAT)
 
     # ------------------------------------------------------------------ report
     kd = kernels[dom]
@@ -797,6 +805,7 @@ def main():
         "roofline": roof,
         "hbm_read_probe": probe,
         "fast_mode": fast_mode,
+        "input_sparse_up": input_sparse,
         "single_pass": single_pass,
         "predictor_quality": quality,
         "cpu_baseline": cpu,
@@ -891,6 +900,97 @@ def run_crossover(torch, args, cap):
                        "activations through hipBLASLt"}}
     log(f"prefill 512 tokens: library {lib_ms / LP:.3f} ms/layer, torch {th_ms / LP:.3f} ms/layer")
     del layers, originals
+    return out
+
+
+def run_input_sparse_up(torch, args, NAT):
+    """The up projection of the ReLU-fied gated shape, whose input x = relu(rmsnorm(z)) is
+    about half zeros (novita.ai activation-sparsity article, section 第二階段), two ways for
+    the same listed neurons: gathering their rows of W_u (the decode path's layout) and a
+    column-major copy of W_u that skips zero inputs and 16-byte pieces without a listed
+    neuron (the library's sparse_ffn_up_probe). Eight layers, packed hot-first, each with
+    the list its own decode step publishes for its token; each way captured as one graph of
+    the eight calls and replayed."""
+    from synth import get_config, make_tokens
+    cfg = get_config("C3")
+    L, d, n = 8, cfg.d, cfg.n
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layers, originals = build_stack(cfg, 1, L, args, lambda l: True)
+    X = make_tokens(cfg, L, 700, "cuda").view(L, 1, d).contiguous()
+    rows_w, cols_w, idx_l, cnt_l, words_l = [], [], [], [], []
+    row_bytes = col_bytes = col_lines = 0
+    zeros = []
+    for l in range(L):
+        _, idx, count, _ = layers[l].decode(X[l])
+        torch.cuda.synchronize()
+        k = int(count.item())
+        perm = torch.as_tensor(layers[l].perm, device="cuda").long()
+        wr = originals[l].w_u.index_select(0, perm).contiguous()
+        rows_w.append(wr)
+        cols_w.append(wr.t().contiguous())
+        idx_l.append(idx)
+        cnt_l.append(count)
+        ih = idx[:k].cpu().numpy().astype(np.int64)
+        w = np.zeros((n + 63) // 64, np.uint64)
+        np.bitwise_or.at(w, ih // 64, np.left_shift(np.uint64(1), (ih % 64).astype(np.uint64)))
+        words_l.append(torch.from_numpy(w.view(np.int64)).cuda())
+        nz = int((X[l] != 0).sum())
+        zeros.append(1.0 - nz / d)
+        live = np.zeros(n // 8, bool)
+        live[ih // 8] = True
+        lines = np.zeros((n + 63) // 64, bool)
+        lines[ih // 64] = True
+        row_bytes += k * d * 2
+        col_bytes += nz * int(live.sum()) * 16
+        col_lines += nz * int(lines.sum()) * 128
+    del layers, originals
+    u = torch.empty((L, n), dtype=torch.float32, device="cuda")
+    wb = NAT.sparse_ffn_up_probe_work_bytes(n)
+    work = torch.empty(wb // 4, dtype=torch.float32, device="cuda")
+
+    def run(layout, st):
+        for l in range(L):
+            if layout == NAT.SFFN_UP_ROWS:
+                NAT.sparse_ffn_up_probe(rows_w[l].data_ptr(), layout, d, n, X[l].data_ptr(),
+                                        idx_l[l].data_ptr(), cnt_l[l].data_ptr(), None,
+                                        u[l].data_ptr(), None, 0, st)
+            else:
+                NAT.sparse_ffn_up_probe(cols_w[l].data_ptr(), layout, d, n, X[l].data_ptr(),
+                                        None, None, words_l[l].data_ptr(), u[l].data_ptr(),
+                                        work.data_ptr(), wb, st)
+
+    side = torch.cuda.Stream()
+    out = {"workload": f"{cfg.name} shape, {L} layers, one token each",
+           "zero_input_fraction": round(float(np.mean(zeros)), 4),
+           "listed_rows_mean": round(row_bytes / (d * 2) / L, 1)}
+    reps = 32
+    for name, layout in (("rows", NAT.SFFN_UP_ROWS), ("columns", NAT.SFFN_UP_COLUMNS)):
+        run(layout, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            run(layout, side.cuda_stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        g.replay()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1000.0 / (reps * L)
+        out[name + "_us_per_layer"] = round(us, 3)
+        del g
+    out["rows_bytes_per_layer"] = int(row_bytes / L)
+    out["columns_bytes_read_per_layer"] = int(col_bytes / L)
+    out["columns_128B_lines_touched_per_layer"] = int(col_lines / L)
+    out["columns_vs_rows_time"] = round(out["columns_us_per_layer"] / out["rows_us_per_layer"], 3)
+    out["note"] = ("rows: the listed neurons' W_u rows, every input; columns: W_u transposed, "
+                   "inputs with x_j = 0 and pieces of 8 neurons with none listed skipped, plus "
+                   "a fixed-order sum of 16 input splits")
+    log(f"input-sparse up probe: rows {out['rows_us_per_layer']} us, columns "
+        f"{out['columns_us_per_layer']} us per layer")
     return out
 
 

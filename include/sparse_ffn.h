@@ -291,6 +291,31 @@ int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events);
 int sparse_ffn_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                           void* stream);
 
+/* Input-sparse up projection probe: a measurement, not a step of the decode path. The
+ * second ReLU-fication stage puts a ReLU after RMSNorm, so about half of the up
+ * projection's input x is zero (novita.ai activation-sparsity article, section 第二階段).
+ * The decode path gathers whole rows of W_u for the listed neurons, where a zero inside a
+ * row's 128-byte line saves no bytes; this probe computes the same products from a
+ * column-major copy of W_u, which can skip the zero inputs, so the two can be timed
+ * against each other. One token, fp16 weights, fp32 x and u, fp32 accumulation.
+ *   layout SFFN_UP_ROWS: w_up [d_ffn][d] (the path's row layout); idx, count: device list
+ *     of neuron ids (count <= d_ffn; ids outside [0, d_ffn) read row 0); u[k] = w_up[idx[k]]
+ *     . x for k < *count (device, at least d_ffn floats). words, work unused (may be NULL).
+ *   layout SFFN_UP_COLUMNS: w_up [d][d_ffn] (W_u transposed); words: device uint64
+ *     [ceil(d_ffn / 64)], bit i % 64 of word i / 64 = neuron i listed (d_ffn % 8 == 0); u[i]
+ *     (device [d_ffn]) = sum over j with x[j] != 0 of w_up[j][i] x[j] for each neuron i of a
+ *     16-byte piece (8 neurons) that holds a listed neuron, 0 for the others; inputs and
+ *     pieces that are skipped are not read. work: device scratch of at least
+ *     sparse_ffn_up_probe_work_bytes(d_ffn) bytes. idx, count unused.
+ * d % 8 == 0, d <= 16384; w_up and x 16-byte aligned. Returns SFFN_ERR_INVALID on a bad
+ * argument (nothing enqueued). */
+enum { SFFN_UP_ROWS = 0, SFFN_UP_COLUMNS = 1 };
+size_t sparse_ffn_up_probe_work_bytes(int32_t d_ffn);
+int sparse_ffn_up_probe(const void* w_up, int32_t layout, int32_t d, int32_t d_ffn,
+                        const float* x, const int32_t* idx, const int32_t* count,
+                        const uint64_t* words, float* u, void* work, size_t work_bytes,
+                        void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* sparse_ffn_status_string(int status);
 

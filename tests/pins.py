@@ -162,7 +162,7 @@ def pin_brute_force_masks():
             assert np.allclose(Y, Yn, rtol=1e-12, atol=1e-15), bits
 
 
-def pin_compaction_exhaustive(nmax=12):
+def pin_compaction_exhaustive(nmax=16):
     """I5: compaction of every sign pattern of n <= nmax scores is the ascending list of set
     positions, and count is the popcount."""
     for n in (1, 5, nmax):

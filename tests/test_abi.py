@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -145,6 +145,20 @@ def test_calls_reject_null_handle_and_bad_batch(N):
     assert L.sparse_ffn_read_probe(0x10000, 0, 1, 0x10000, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_read_probe(0x10008, 1024, 1, 0x10000, None) == N.SFFN_ERR_INVALID
     assert L.sparse_ffn_read_probe(0x10000, 1024, -1, 0x10000, None) == N.SFFN_ERR_INVALID
+    # the input-sparse up probe: every argument check fires before anything is enqueued
+    A = 0x10000
+    W = L.sparse_ffn_up_probe_work_bytes(1104)
+    assert W == 16 * 1104 * 4 and L.sparse_ffn_up_probe_work_bytes(0) == 0
+    up = L.sparse_ffn_up_probe
+    assert up(None, 0, 512, 1104, A, A, A, None, A, None, 0, None) == N.SFFN_ERR_INVALID
+    assert up(A, 2, 512, 1104, A, A, A, A, A, A, W, None) == N.SFFN_ERR_INVALID       # layout
+    assert up(A, 0, 500, 1104, A, A, A, None, A, None, 0, None) == N.SFFN_ERR_INVALID  # d % 8
+    assert up(A, 0, 512, 1104, A, None, A, None, A, None, 0, None) == N.SFFN_ERR_INVALID
+    assert up(A, 0, 512, 1104, A + 8, A, A, None, A, None, 0, None) == N.SFFN_ERR_INVALID
+    assert up(A, 1, 512, 1100, A, None, None, A, A, A, W, None) == N.SFFN_ERR_INVALID  # n % 8
+    assert up(A, 1, 512, 1104, A, None, None, None, A, A, W, None) == N.SFFN_ERR_INVALID
+    assert up(A, 1, 512, 1104, A, None, None, A, A, A, W - 4, None) == N.SFFN_ERR_INVALID
+    assert up(A, 1, 512, 1104, A, None, None, A, A, None, W, None) == N.SFFN_ERR_INVALID
 
 
 def test_status_strings(N):
