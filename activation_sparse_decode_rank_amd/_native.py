@@ -64,6 +64,8 @@ def _load():
         "sparse_ffn_pack_rows": (C.c_int, [P, P, P, I32, I64, I64, P]),
         "sparse_ffn_read_probe": (C.c_int, [P, SZ, I32, P, P]),
         "sparse_ffn_up_probe_work_bytes": (SZ, [I32]),
+        "sparse_ffn_prefill_work_bytes": (SZ, [P, I32]),
+        "sparse_ffn_prefill": (C.c_int, [P, P, I32, P, P, SZ, P]),
         "sparse_ffn_up_probe": (C.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -80,7 +82,8 @@ EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destr
             "sparse_ffn_lookahead_begin", "sparse_ffn_decode_lookahead",
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
-            "sparse_ffn_read_probe", "sparse_ffn_up_probe_work_bytes", "sparse_ffn_up_probe")
+            "sparse_ffn_read_probe", "sparse_ffn_up_probe_work_bytes", "sparse_ffn_up_probe",
+            "sparse_ffn_prefill_work_bytes", "sparse_ffn_prefill")
 
 
 def lib():
@@ -166,6 +169,14 @@ def sparse_ffn_pack_rows(src, perm, dst, rows, row_bytes, dst_stride_bytes, stre
 
 def sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream) -> None:
     _ck(_lib.sparse_ffn_read_probe(buf, nbytes, workgroups, sink, stream), "sparse_ffn_read_probe")
+
+
+def sparse_ffn_prefill_work_bytes(handle, chunk_tokens) -> int:
+    return int(_lib.sparse_ffn_prefill_work_bytes(handle, chunk_tokens))
+
+
+def sparse_ffn_prefill(handle, x, B, y, work, work_bytes, stream) -> None:
+    _ck(_lib.sparse_ffn_prefill(handle, x, B, y, work, work_bytes, stream), "sparse_ffn_prefill")
 
 
 def sparse_ffn_up_probe_work_bytes(d_ffn) -> int:

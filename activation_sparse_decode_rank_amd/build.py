@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_ffn.so")
 SOURCES = ["sffn_api.hip", "sffn_dispatch.hip", "sffn_stage1.hip", "sffn_decode_b1.hip", "sffn_batch.hip",
            "sffn_mid_bt_h4.hip", "sffn_mid_bt_h8.hip", "sffn_mid_bt_f4.hip", "sffn_mid_bt_f8.hip",
-           "sffn_tiles.hip", "sffn_offline.hip", "sffn_measure.hip",
+           "sffn_tiles.hip", "sffn_offline.hip", "sffn_measure.hip", "sffn_prefill.hip",
            "sffn_static.hip", "sffn_bundle.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 

@@ -365,6 +365,24 @@ int sparse_ffn_dense(sparse_ffn_t h, const float* x, int32_t B, float* y, void* 
              : SFFN_ERR_HIP;
 }
 
+size_t sparse_ffn_prefill_work_bytes(sparse_ffn_t h, int32_t chunk_tokens) {
+  if (!h || chunk_tokens < 1 || !sffn::prefill_ok(h->L)) return 0;
+  return sffn::prefill_work_bytes(h->L, chunk_tokens);
+}
+
+int sparse_ffn_prefill(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
+                       size_t work_bytes, void* stream) {
+  if (!h || !x || !y || !work || B < 1) return SFFN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(work) & 255u))
+    return SFFN_ERR_INVALID;
+  if (!sffn::prefill_ok(h->L)) return SFFN_ERR_UNSUPPORTED;
+  if (sffn::prefill_chunk(h->L, work_bytes) < 1) return SFFN_ERR_INVALID;
+  return sffn::run_prefill(h->L, x, B, y, work, work_bytes, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SFFN_OK
+             : SFFN_ERR_HIP;
+}
+
 int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,
                              int32_t* count, uint64_t* tokmask, float* scores, void* stream) {
   if (!h || !x || !y || !idx || !count || B < 1 || B > h->max_batch) return SFFN_ERR_INVALID;

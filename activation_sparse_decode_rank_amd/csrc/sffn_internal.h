@@ -225,6 +225,13 @@ hipError_t launch_fill_list(const LayerDev& L, int B, int32_t* idx, int32_t* cou
 hipError_t launch_dense(const LayerDev& L, const float* x, int B, float* y, hipStream_t s);
 // sffn_measure.hip: a plain read stream of bytes (a multiple of 16) over buf by the given
 // number of workgroups; sink [workgroups] is written only in a practically impossible case
+// dense prefill on the matrix cores (sffn_prefill.hip): fp16 weights, d a multiple of 128;
+// scratch bytes for chunks of up to `chunk` tokens, the chunk a scratch holds, and the run
+bool prefill_ok(const LayerDev& L);
+size_t prefill_work_bytes(const LayerDev& L, int chunk);
+int prefill_chunk(const LayerDev& L, size_t work_bytes);
+hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void* work,
+                       size_t work_bytes, hipStream_t s);
 // input-sparse up projection probe: layout 0 rows [n][d], 1 columns [d][n] (fp16)
 size_t up_probe_work_bytes(int n);
 hipError_t launch_up_probe(const void* w, int layout, int d, int n, const float* x,

@@ -1,0 +1,404 @@
+// Dense prefill on the matrix cores (gfx950): the FFN over every neuron for many tokens at
+// once, which the pages run dense (PowerInfer-2 article, section 4.1.1 NPU-Centric Prefill:
+// prefill takes the whole layer, no activation prediction). At hundreds of tokens the two
+// products are dense matrix products, so they are blocked for reuse: each weight tile is
+// read once per 128 tokens instead of once per 64-token chunk of the decode kernels.
+//
+// Arithmetic as on the decode path's matrix-core kernels: fp16 weights as stored, fp32
+// activations carried as fp16 hi + lo pairs (two products each, about 22 significant bits),
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+//
+// Three kernels per chunk of Bp tokens (Bp a multiple of 128; rows past the chunk's tokens
+// are zero):
+//  - k_pf_split: x [B][d] fp32 -> xh, xl [Bp][d] fp16;
+//  - k_pf_up:    h = relu(W_act x + b_act) (gated: times W_up x) for every neuron and token,
+//                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to 128; neurons past
+//                d_ffn are 0);
+//  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S = 1, 2 or 4) when the
+//                output tiles alone do not fill the GPU; the S partial sums go to scratch
+//                and k_pf_sum adds them in split order (y bitwise reproducible).
+#include "sffn_device.h"
+
+namespace sffn {
+namespace {
+
+constexpr int PF_T = 128;  // tile edge: rows (neurons or columns) and tokens per workgroup
+constexpr int PF_K = 64;   // K step: 64 fp16 = one 128-byte line of a row
+constexpr int PF_P = 72;   // LDS row pitch in halfs (64 + 8): rows start 16 bytes apart in the banks
+constexpr int PF_SMAX = 4;
+
+size_t pf_align(size_t v) { return (v + 255) & ~(size_t)255; }
+
+__device__ __forceinline__ float4_t pf_mfma(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void lds_put(_Float16* base, int row, int col8, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + row * PF_P + col8 * 8) = v;
+}
+__device__ __forceinline__ half8_t lds_get(const _Float16* base, int row, int k) {
+  return *reinterpret_cast<const half8_t*>(base + row * PF_P + k);
+}
+
+// x [B][d] fp32 -> hi, lo [Bp][d] fp16, rows B .. Bp-1 zero
+__global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, int B, int Bp, int d,
+                                                  u32x4* __restrict__ xh, u32x4* __restrict__ xl) {
+  const int nch = d / 8;
+  const size_t total = (size_t)Bp * nch;
+  for (size_t q = (size_t)blockIdx.x * TPB + threadIdx.x; q < total; q += (size_t)gridDim.x * TPB) {
+    const int b = (int)(q / nch), c = (int)(q % nch);
+    float4_t a = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
+    if (b < B) {
+      const float4_t* p = reinterpret_cast<const float4_t*>(x + (size_t)b * d + (size_t)c * 8);
+      a = p[0];
+      e = p[1];
+    }
+    half8_t hi, lo;
+    split_hi_lo(a, e, hi, lo);
+    xh[q] = __builtin_bit_cast(u32x4, hi);
+    xl[q] = __builtin_bit_cast(u32x4, lo);
+  }
+}
+
+// Up projection: workgroup (mt, bt) computes neurons [128 mt, +128) x tokens [128 bt, +128)
+// over all d inputs, K steps of 64. Wave w takes neurons 64 (w & 1) .. +64 and tokens
+// 64 (w >> 1) .. +64 (4 x 4 tiles of 16 x 16, for the gate and, gated, the up matrix).
+// The tiles of a K step sit in one of two LDS buffers (147 KB gated: one workgroup a
+// compute unit): while the matrix cores take step k from one, each thread stores step
+// k + 1 (loaded into registers during step k - 1) into the other and issues its loads for
+// step k + 2; one barrier a step. (One buffer with two workgroups a compute unit spills
+// registers in the gated form and measured 10% slower.)
+// Neuron tiles mt of the same bt are 8 apart in the grid when the neuron tile count is
+// padded to a multiple of 8, so the workgroups sharing a weight tile run on one XCD.
+template <bool GATED>
+__global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, int ld_act,
+                                               const float* __restrict__ b_act,
+                                               const u32x4* __restrict__ xh,
+                                               const u32x4* __restrict__ xl, int d, int n,
+                                               int np, int nmt, _Float16* __restrict__ hh,
+                                               _Float16* __restrict__ hl) {
+  constexpr int NM = GATED ? 2 : 1;
+  constexpr int TILE = PF_T * PF_P;
+  __shared__ __attribute__((aligned(16))) _Float16 sA[2][NM][TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 sB[2][2][TILE];
+  const int nmt_pad = (nmt + 7) / 8 * 8;
+  const int mt = blockIdx.x % nmt_pad, bt = blockIdx.x / nmt_pad;
+  if (mt >= nmt) return;  // padding workgroup (uniform)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nch = d / 8;
+  const int m0 = mt * PF_T, b0 = bt * PF_T;
+  const u32x4* w = static_cast<const u32x4*>(w_act);
+
+  // this thread's load slots: q = tid + 256 j -> row q / 8, 16-byte piece q % 8
+  size_t wrow[4];
+  int lrow[4], lseg[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + TPB * j;
+    lrow[j] = q >> 3;
+    lseg[j] = q & 7;
+    wrow[j] = (size_t)min(m0 + lrow[j], n - 1) * ld_act;
+  }
+  u32x4 ra[NM][4], rb[2][4];
+  auto fetch = [&](int k0) {
+    const int kc = k0 / 8;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ra[m][j] = ld_stream(w, wrow[j] + (size_t)m * nch + kc + lseg[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = (size_t)(b0 + lrow[j]) * nch + kc + lseg[j];
+      rb[0][j] = xh[o];
+      rb[1][j] = xl[o];
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) lds_put(sA[buf][m], lrow[j], lseg[j], ra[m][j]);
+      lds_put(sB[buf][0], lrow[j], lseg[j], rb[0][j]);
+      lds_put(sB[buf][1], lrow[j], lseg[j], rb[1][j]);
+    }
+  };
+  float4_t acc[NM][4][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[m][i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // the products of one K step from LDS buffer buf: for each 16-row tile, its hi products
+  // for the 4 token tiles, then its lo products
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < PF_K; ks += 32) {
+      const int k = ks + 8 * g;
+      half8_t bx[2][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bx[0][t] = lds_get(sB[buf][0], wn * 64 + t * 16 + r16, k);
+        bx[1][t] = lds_get(sB[buf][1], wn * 64 + t * 16 + r16, k);
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half8_t aw = lds_get(sA[buf][m], wm * 64 + i * 16 + r16, k);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(aw, bx[h][t], acc[m][i][t]);
+        }
+    }
+  };
+
+  fetch(0);
+  store(0);
+  if (PF_K < d) fetch(PF_K);
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < d; k0 += PF_K) {
+    compute(cur);
+    if (k0 + PF_K < d) {
+      store(cur ^ 1);
+      if (k0 + 2 * PF_K < d) fetch(k0 + 2 * PF_K);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  // epilogue: lane holds token 16t + r16 and neurons 16i + 4g .. +3 of the wave's block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int i0 = m0 + wm * 64 + i * 16 + 4 * g;
+    float ba[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ba[j] = (b_act && i0 + j < n) ? b_act[i0 + j] : 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = b0 + wn * 64 + t * 16 + r16;
+      _Float16 hv[4], lv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h = acc[0][i][t][j] + ba[j];
+        h = h > 0.f ? h : 0.f;
+        if (GATED) h *= acc[NM - 1][i][t][j];
+        if (i0 + j >= n) h = 0.f;
+        hv[j] = (_Float16)h;
+        lv[j] = (_Float16)(h - (float)hv[j]);
+      }
+      const size_t o = (size_t)tok * np + i0;
+      *reinterpret_cast<uint2*>(hh + o) = __builtin_bit_cast(uint2, hv);
+      *reinterpret_cast<uint2*>(hl + o) = __builtin_bit_cast(uint2, lv);
+    }
+  }
+}
+
+// Down projection: workgroup (ct, bt, s) computes columns [128 ct, +128) x tokens
+// [128 bt, +128) over neurons [s np / S, (s + 1) np / S) (whole K steps of 64). Wave w takes
+// tokens 64 (w & 1) .. +64 and columns 64 (w >> 1) .. +64. W_down^T rows are stored
+// transposed in LDS (column-major: [column][neuron]), so the right operand's 8 consecutive
+// neurons of one column are one 16-byte read: thread t loads the 16-byte pieces (8 columns)
+// cs = t / 32 and cs + 8 of neurons 2p and 2p + 1 (p = t % 32) and stores each column's
+// pair of neurons as one 32-bit word (the 32 lanes of a half wave write 32 consecutive
+// words). One LDS buffer; two workgroups fit a compute unit. S == 1 writes y (+ b_out) for
+// the chunk's real tokens; otherwise the split's sums go to part[s][Bp][d].
+__global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down_t, int ld_down,
+                                                 const float* __restrict__ b_out,
+                                                 const _Float16* __restrict__ hh,
+                                                 const _Float16* __restrict__ hl, int d, int n,
+                                                 int np, int B, int Bp, int S,
+                                                 float* __restrict__ y, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) _Float16 sH[2][PF_T * PF_P];
+  __shared__ __attribute__((aligned(16))) _Float16 sW[PF_T * PF_P];
+  const int nct = d / PF_T, nbt = Bp / PF_T;
+  const int ct = blockIdx.x % nct, bt = (blockIdx.x / nct) % nbt, s = blockIdx.x / (nct * nbt);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int c0 = ct * PF_T, b0 = bt * PF_T;
+  const int ksteps = np / PF_K;
+  const int kb = (int)((long long)ksteps * s / S), ke = (int)((long long)ksteps * (s + 1) / S);
+  const u32x4* w = static_cast<const u32x4*>(w_down_t);
+  uint32_t* sW32 = reinterpret_cast<uint32_t*>(sW);
+
+  // H slots: q = tid + 256 j -> token q / 8, piece q % 8
+  int hrow[4], hseg[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + TPB * j;
+    hrow[j] = q >> 3;
+    hseg[j] = q & 7;
+  }
+  const int wp = tid & 31, wcs = tid >> 5;  // neuron pair, 8-column piece (and + 8)
+  u32x4 rh[2][4], rw[2][2];                 // rw[piece][neuron of the pair]
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t o = (size_t)(b0 + hrow[j]) * np + k0 + hseg[j] * 8;
+      rh[0][j] = *reinterpret_cast<const u32x4*>(hh + o);
+      rh[1][j] = *reinterpret_cast<const u32x4*>(hl + o);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = min(k0 + 2 * wp + e, n - 1);  // neurons past d_ffn meet h = 0
+        rw[c][e] = ld_stream(w, (size_t)i * ld_down + c0 / 8 + wcs + 8 * c);
+      }
+  };
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kb < ke) fetch(kb * PF_K);
+  for (int kk = kb; kk < ke; ++kk) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lds_put(sH[0], hrow[j], hseg[j], rh[0][j]);
+      lds_put(sH[1], hrow[j], hseg[j], rh[1][j]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const half8_t v0 = __builtin_bit_cast(half8_t, rw[c][0]);
+      const half8_t v1 = __builtin_bit_cast(half8_t, rw[c][1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = (wcs + 8 * c) * 8 + e;
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        const half2_t pr = {v0[e], v1[e]};
+        sW32[col * (PF_P / 2) + wp] = __builtin_bit_cast(uint32_t, pr);
+      }
+    }
+    __syncthreads();
+    if (kk + 1 < ke) fetch((kk + 1) * PF_K);
+#pragma unroll
+    for (int ks = 0; ks < PF_K; ks += 32) {
+      const int k = ks + 8 * g;
+      half8_t bw[4], ah[2][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bw[t] = lds_get(sW, wn * 64 + t * 16 + r16, k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ah[0][i] = lds_get(sH[0], wm * 64 + i * 16 + r16, k);
+        ah[1][i] = lds_get(sH[1], wm * 64 + i * 16 + r16, k);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i][t] = pf_mfma(ah[h][i], bw[t], acc[i][t]);
+    }
+  }
+  // lane holds column 16t + r16 and tokens 16i + 4g .. +3 of the wave's block
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = c0 + wn * 64 + t * 16 + r16;
+    const float bo = (S == 1 && b_out) ? b_out[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = b0 + wm * 64 + i * 16 + 4 * g + j;
+        if (S == 1) {
+          if (tok < B) y[(size_t)tok * d + col] = acc[i][t][j] + bo;
+        } else {
+          part[((size_t)s * Bp + tok) * d + col] = acc[i][t][j];
+        }
+      }
+  }
+}
+
+// y[b][c] = sum over s in order of part[s][b][c], + b_out[c], for the chunk's B tokens
+__global__ __launch_bounds__(TPB) void k_pf_sum(const float* __restrict__ part, int S, int B,
+                                                int Bp, int d, const float* __restrict__ b_out,
+                                                float* __restrict__ y) {
+  const size_t total = (size_t)B * d;
+  for (size_t q = (size_t)blockIdx.x * TPB + threadIdx.x; q < total; q += (size_t)gridDim.x * TPB) {
+    float a = part[q];
+    for (int s = 1; s < S; ++s) a += part[(size_t)s * Bp * d + q];
+    y[q] = a + (b_out ? b_out[q % d] : 0.f);
+  }
+}
+
+size_t pf_np(int n) { return (size_t)(n + PF_T - 1) / PF_T * PF_T; }
+
+}  // namespace
+
+bool prefill_ok(const LayerDev& L) { return L.w_f16 && L.d % PF_T == 0 && L.d <= 65536; }
+
+// scratch for chunks of up to `chunk` tokens (rounded up to 128)
+size_t prefill_work_bytes(const LayerDev& L, int chunk) {
+  if (chunk < 1) return 0;
+  const size_t Bp = (size_t)(chunk + PF_T - 1) / PF_T * PF_T;
+  const size_t np = pf_np(L.n);
+  size_t b = 0;
+  b += 2 * pf_align(Bp * L.d * 2);           // xh, xl
+  b += 2 * pf_align(Bp * np * 2);            // hh, hl
+  b += pf_align((size_t)PF_SMAX * Bp * L.d * 4);  // split partial sums
+  return b;
+}
+
+// tokens the scratch holds per chunk (a multiple of 128; 0 when not even 128)
+int prefill_chunk(const LayerDev& L, size_t work_bytes) {
+  int c = 0;
+  for (int t = PF_T; t <= (1 << 20); t += PF_T) {
+    if (prefill_work_bytes(L, t) > work_bytes) break;
+    c = t;
+  }
+  return c;
+}
+
+hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void* work,
+                       size_t work_bytes, hipStream_t s) {
+  const int chunk = prefill_chunk(L, work_bytes);
+  if (chunk < PF_T) return hipErrorInvalidValue;
+  const int d = L.d, n = L.n, np = (int)pf_np(n);
+  const int nmt = np / PF_T, nct = d / PF_T;
+  for (int b0 = 0; b0 < B; b0 += chunk) {
+    const int bc = std::min(chunk, B - b0);
+    const int Bp = (bc + PF_T - 1) / PF_T * PF_T;
+    char* p = static_cast<char*>(work);
+    auto take = [&](size_t bytes) { char* q = p; p += pf_align(bytes); return q; };
+    u32x4* xh = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
+    u32x4* xl = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
+    _Float16* hh = reinterpret_cast<_Float16*>(take((size_t)Bp * np * 2));
+    _Float16* hl = reinterpret_cast<_Float16*>(take((size_t)Bp * np * 2));
+    float* part = reinterpret_cast<float*>(take((size_t)PF_SMAX * Bp * d * 4));
+    const float* xc = x + (size_t)b0 * d;
+    float* yc = y + (size_t)b0 * d;
+    const int items = Bp * (d / 8);
+    hipLaunchKernelGGL(k_pf_split, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)), dim3(TPB),
+                       0, s, xc, bc, Bp, d, xh, xl);
+    const int nbt = Bp / PF_T;
+    const dim3 gup((nmt + 7) / 8 * 8 * nbt);
+    if (L.gated)
+      hipLaunchKernelGGL(k_pf_up<true>, gup, dim3(TPB), 0, s, L.w_act, L.act_ld, L.b_act, xh, xl, d,
+                         n, np, nmt, hh, hl);
+    else
+      hipLaunchKernelGGL(k_pf_up<false>, gup, dim3(TPB), 0, s, L.w_act, L.act_ld, L.b_act, xh, xl, d,
+                         n, np, nmt, hh, hl);
+    // split the neurons when the output tiles alone leave compute units idle
+    int S = 1;
+    while (S < PF_SMAX && nct * nbt * S < L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
+    hipLaunchKernelGGL(k_pf_down, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
+                       L.b_out, hh, hl, d, n, np, bc, Bp, S, yc, part);
+    if (S > 1) {
+      const size_t tot = (size_t)bc * d;
+      hipLaunchKernelGGL(k_pf_sum, dim3((unsigned)std::min<size_t>((tot + TPB - 1) / TPB, 8 * L.n_cus)),
+                         dim3(TPB), 0, s, part, S, bc, Bp, d, L.b_out, yc);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace sffn

@@ -253,6 +253,33 @@ class SparseFFN:
         N.sparse_ffn_dense(self.handle, x.data_ptr(), B, y.data_ptr(), _stream(stream))
         return y
 
+    def prefill_work(self, chunk=512):
+        """Scratch for prefill in chunks of `chunk` tokens (a uint8 device tensor), or None
+        when the layer has no matrix-core prefill (fp32 weights, or d not a multiple of 128)."""
+        nb = N.sparse_ffn_prefill_work_bytes(self.handle, int(chunk))
+        if nb == 0:
+            return None
+        return torch.empty(nb, dtype=torch.uint8, device=self.w_act.device)
+
+    def prefill(self, x, y=None, work=None, stream=None):
+        """The dense FFN over every neuron for x ([B, d] fp32, any B) on the matrix cores with
+        the weights reused across 128-token tiles (sparse_ffn_prefill); layers it does not
+        cover take sparse_ffn_dense. work: scratch from prefill_work (allocated here when
+        None)."""
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous fp32 [B, d] device tensor")
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty((B, self.d), dtype=torch.float32, device=x.device)
+        if work is None:
+            work = self.prefill_work(min(max(B, 1), 512))
+        if work is None:
+            N.sparse_ffn_dense(self.handle, x.data_ptr(), B, y.data_ptr(), _stream(stream))
+            return y
+        N.sparse_ffn_prefill(self.handle, x.data_ptr(), B, y.data_ptr(), work.data_ptr(),
+                             work.numel(), _stream(stream))
+        return y
+
     def lookahead_begin(self, x, stream=None):
         """Predict this layer's active set from x ([1, d] fp32) and hold it for
         decode_ahead (sparse_ffn_lookahead_begin)."""

@@ -875,6 +875,8 @@ def run_crossover(torch, args, cap):
         return ev[0].elapsed_time(ev[1]) / reps
 
     lib_ms = time_fn(lambda: [layers[l].dense(Xp[l], y=yp[l]) for l in range(LP)])
+    pf_work = layers[0].prefill_work(P)
+    pf_ms = time_fn(lambda: [layers[l].prefill(Xp[l], y=yp[l], work=pf_work) for l in range(LP)])
     Xh = Xp.half()
 
     def torch_prefill():
@@ -885,20 +887,30 @@ def run_crossover(torch, args, cap):
             _ = torch.matmul(h, o.w_o) + o.b_o.half()
 
     th_ms = time_fn(torch_prefill)
+    # algorithmic flops of the dense FFN per layer (the products as defined, once)
+    pf_flops = 2.0 * P * n * d * (3 if cfg.gated else 2)
+    out_pf = {
+        "prefill_ms_per_layer": round(pf_ms / LP, 4),
+        "prefill_tokens_per_s": round(P / (pf_ms / LP * 1e-3), 1),
+        "prefill_tflops": round(pf_flops / (pf_ms / LP * 1e-3) / 1e12, 2),
+        "prefill_mfma_frac": round(pf_flops / (pf_ms / LP * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "dense_route_ms_per_layer": round(lib_ms / LP, 4),
+        "torch_ms_per_layer": round(th_ms / LP, 4),
+        "torch_fp16_tokens_per_s": round(P / (th_ms / LP * 1e-3), 1),
+        "note": "per layer. prefill: sparse_ffn_prefill (128 x 128 tiles on the matrix cores, each "
+                "weight tile read once per 128 tokens; fp32 activations as hi + lo fp16 pairs, so "
+                "the matrix cores run twice the algorithmic products). dense_route: "
+                "sparse_ffn_dense over the decode kernels, 64 tokens per pass. torch: fp16 "
+                "activations through hipBLASLt"}
     out = {"workload": f"{cfg.name}: {cfg.description}", "rows": rows,
            "crossover_union_fraction": cross,
            "note": "dense route = every neuron through the forward kernels (tile path), no "
                    "predictor; the decode switches to it when sffn_desc.dense_union is set and "
                    "the expected union exceeds it",
-           "prefill_512_tokens": {
-               "library_dense_tokens_per_s": round(P * LP / (lib_ms * 1e-3) / LP, 1),
-               "torch_fp16_tokens_per_s": round(P * LP / (th_ms * 1e-3) / LP, 1),
-               "library_ms_per_layer": round(lib_ms / LP, 4),
-               "torch_ms_per_layer": round(th_ms / LP, 4),
-               "note": "per layer; the library keeps fp32 activations (hi + lo fp16 on the matrix "
-                       "cores) and re-reads the weights once per 64-token chunk; torch runs fp16 "
-                       "activations through hipBLASLt"}}
-    log(f"prefill 512 tokens: library {lib_ms / LP:.3f} ms/layer, torch {th_ms / LP:.3f} ms/layer")
+           "prefill_512_tokens": out_pf}
+    log(f"prefill 512 tokens: library prefill {pf_ms / LP:.3f} ms/layer "
+        f"({out_pf['prefill_tflops']} TFLOP/s), dense route {lib_ms / LP:.3f}, torch "
+        f"{th_ms / LP:.3f} ms/layer")
     del layers, originals
     return out
 

@@ -291,6 +291,23 @@ int sparse_ffn_set_timing_events(sparse_ffn_t h, void* const* events);
 int sparse_ffn_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                           void* stream);
 
+/* Dense prefill on the matrix cores: y_b = the dense FFN of x_b over every neuron (as
+ * sparse_ffn_dense), for any number of tokens B >= 1, with the two products blocked for
+ * reuse (each weight tile is read once per 128 tokens). The pages run prefill dense
+ * (PowerInfer-2 article, section 4.1.1 NPU-Centric Prefill). Arithmetic as on the
+ * matrix-core decode path: fp16 weights, fp32 activations as fp16 hi + lo pairs (same
+ * range limit), fp32 accumulation; y is bitwise reproducible. Requires fp16 weights and d
+ * a multiple of 128 (else SFFN_ERR_UNSUPPORTED; sparse_ffn_dense covers every shape).
+ * x: device [B][d] fp32; y: device [B][d] fp32, fully overwritten. work: device scratch,
+ * 256-byte aligned, of work_bytes >= sparse_ffn_prefill_work_bytes(h, 128); the tokens are
+ * processed in chunks of the largest multiple of 128 whose scratch fits work_bytes. The
+ * handle's workspace is not used. sparse_ffn_prefill_work_bytes returns the scratch for
+ * chunks of chunk_tokens (rounded up to 128), or 0 for a NULL handle, chunk_tokens < 1 or
+ * an unsupported layer. */
+size_t sparse_ffn_prefill_work_bytes(sparse_ffn_t h, int32_t chunk_tokens);
+int sparse_ffn_prefill(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
+                       size_t work_bytes, void* stream);
+
 /* Input-sparse up projection probe: a measurement, not a step of the decode path. The
  * second ReLU-fication stage puts a ReLU after RMSNorm, so about half of the up
  * projection's input x is zero (novita.ai activation-sparsity article, section 第二階段).
