@@ -60,17 +60,20 @@ __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, i
   }
 }
 
-// Up projection: workgroup (mt, bt) computes neurons [128 mt, +128) x tokens [128 bt, +128)
-// over all d inputs, K steps of 64. Wave w takes neurons 64 (w & 1) .. +64 and tokens
-// 64 (w >> 1) .. +64 (4 x 4 tiles of 16 x 16, for the gate and, gated, the up matrix).
-// The tiles of a K step sit in one of two LDS buffers (147 KB gated: one workgroup a
-// compute unit): while the matrix cores take step k from one, each thread stores step
-// k + 1 (loaded into registers during step k - 1) into the other and issues its loads for
-// step k + 2; one barrier a step. (One buffer with two workgroups a compute unit spills
-// registers in the gated form and measured 10% slower.)
-// Neuron tiles mt of the same bt are 8 apart in the grid when the neuron tile count is
-// padded to a multiple of 8, so the workgroups sharing a weight tile run on one XCD.
-template <bool GATED>
+// Up projection: workgroup (mt, bt) computes neurons [MR mt, +MR) x tokens [128 bt, +128)
+// (MR = 32 IT: 128 or 192) over all d inputs, in stages of 32 inputs. Wave w takes neurons
+// 16 IT (w & 1) .. +16 IT and tokens 64 (w >> 1) .. +64 (IT x 4 tiles of 16 x 16, for the
+// gate and, gated, the up matrix). The operands reach LDS without passing through
+// registers (global_load_lds_dwordx4: each lane's 16 bytes land at the next 16 bytes of a
+// 1 KB block), NS stages deep, so NS - 1 stages of loads are in flight while the matrix
+// cores take one. A stage holds, per operand (each weight matrix, the tokens' hi and lo
+// halves), its rows x 64 bytes; within each 16-row group, row r's 16-byte chunk c sits at
+// position (c + r / 4) mod 4 of the row, so that a fragment read (16 rows, one chunk each)
+// touches every LDS bank once. Neuron tiles mt of the same bt are 8 apart in the grid when
+// the neuron tile count is padded to a multiple of 8, so the workgroups sharing a weight
+// tile run on one XCD.
+constexpr int PFD_K = 32;  // inputs per stage
+template <bool GATED, int IT>
 __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, int ld_act,
                                                const float* __restrict__ b_act,
                                                const u32x4* __restrict__ xh,
@@ -78,9 +81,15 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
                                                int np, int nmt, _Float16* __restrict__ hh,
                                                _Float16* __restrict__ hl) {
   constexpr int NM = GATED ? 2 : 1;
-  constexpr int TILE = PF_T * PF_P;
-  __shared__ __attribute__((aligned(16))) _Float16 sA[2][NM][TILE];
-  __shared__ __attribute__((aligned(16))) _Float16 sB[2][2][TILE];
+  constexpr int MR = 32 * IT;                  // neurons per workgroup
+  constexpr int GA = MR / 16, GB = PF_T / 16;  // 16-row groups of a weight / token operand
+  constexpr int BLK_A = MR * PFD_K, BLK_B = PF_T * PFD_K;  // halfs per operand block
+  constexpr int STAGE = NM * BLK_A + 2 * BLK_B;            // halfs per stage
+  constexpr int NS = STAGE * 2 * 4 <= 128 * 1024 ? 4 : 3;  // stages held in LDS
+  constexpr int NG = NM * GA + 2 * GB;                     // 1 KB loads a stage
+  constexpr int DPS = NG / (TPB / 64);                     // load instructions per wave a stage
+  static_assert(NG % (TPB / 64) == 0, "whole loads per wave");
+  __shared__ __attribute__((aligned(16))) _Float16 sbuf[NS * STAGE];
   const int nmt_pad = (nmt + 7) / 8 * 8;
   const int mt = blockIdx.x % nmt_pad, bt = blockIdx.x / nmt_pad;
   if (mt >= nmt) return;  // padding workgroup (uniform)
@@ -88,92 +97,87 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, g = lane >> 4;
   const int nch = d / 8;
-  const int m0 = mt * PF_T, b0 = bt * PF_T;
+  const int m0 = mt * MR, b0 = bt * PF_T;
   const u32x4* w = static_cast<const u32x4*>(w_act);
+  const int nk = d / PFD_K;
 
-  // this thread's load slots: q = tid + 256 j -> row q / 8, 16-byte piece q % 8
-  size_t wrow[4];
-  int lrow[4], lseg[4];
+  // the lane's row in a 16-row group and the global chunk its LDS position holds
+  const int lr = lane >> 2;
+  const int lc = ((lane & 3) - (lr >> 2)) & 3;
+  auto issue = [&](int st) {
+    const int kc = st * (PFD_K / 8) + lc;
+    _Float16* base = sbuf + (st % NS) * STAGE;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = tid + TPB * j;
-    lrow[j] = q >> 3;
-    lseg[j] = q & 7;
-    wrow[j] = (size_t)min(m0 + lrow[j], n - 1) * ld_act;
-  }
-  u32x4 ra[NM][4], rb[2][4];
-  auto fetch = [&](int k0) {
-    const int kc = k0 / 8;
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ra[m][j] = ld_stream(w, wrow[j] + (size_t)m * nch + kc + lseg[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t o = (size_t)(b0 + lrow[j]) * nch + kc + lseg[j];
-      rb[0][j] = xh[o];
-      rb[1][j] = xl[o];
+    for (int v = 0; v < DPS; ++v) {
+      const int u = wave + (TPB / 64) * v;  // 16-row group of some operand, wave-uniform
+      const u32x4* src;
+      int off;
+      if (u < NM * GA) {
+        const int o = u / GA, q = u % GA;
+        src = w + (size_t)min(m0 + q * 16 + lr, n - 1) * ld_act + (size_t)o * nch + kc;
+        off = o * BLK_A + q * 16 * PFD_K;
+      } else {
+        const int o = (u - NM * GA) / GB, q = (u - NM * GA) % GB;
+        src = (o == 0 ? xh : xl) + (size_t)(b0 + q * 16 + lr) * nch + kc;
+        off = NM * BLK_A + o * BLK_B + q * 16 * PFD_K;
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + off),
+                                       16, 0, 0);
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) lds_put(sA[buf][m], lrow[j], lseg[j], ra[m][j]);
-      lds_put(sB[buf][0], lrow[j], lseg[j], rb[0][j]);
-      lds_put(sB[buf][1], lrow[j], lseg[j], rb[1][j]);
-    }
+  // fragment read: rows R .. R + 15 (R a multiple of 16) of the block at off, chunk g
+  auto frag = [&](const _Float16* base, int off, int R) {
+    return *reinterpret_cast<const half8_t*>(
+        base + off + R * PFD_K + (r16 * 4 + ((g + (r16 >> 2)) & 3)) * 8);
   };
-  float4_t acc[NM][4][4];
+  float4_t acc[NM][IT][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[m][i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
-  // the products of one K step from LDS buffer buf: for each 16-row tile, its hi products
-  // for the 4 token tiles, then its lo products
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < PF_K; ks += 32) {
-      const int k = ks + 8 * g;
-      half8_t bx[2][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bx[0][t] = lds_get(sB[buf][0], wn * 64 + t * 16 + r16, k);
-        bx[1][t] = lds_get(sB[buf][1], wn * 64 + t * 16 + r16, k);
-      }
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const half8_t aw = lds_get(sA[buf][m], wm * 64 + i * 16 + r16, k);
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(aw, bx[h][t], acc[m][i][t]);
-        }
-    }
-  };
 
-  fetch(0);
-  store(0);
-  if (PF_K < d) fetch(PF_K);
-  __syncthreads();
-  int cur = 0;
-  for (int k0 = 0; k0 < d; k0 += PF_K) {
-    compute(cur);
-    if (k0 + PF_K < d) {
-      store(cur ^ 1);
-      if (k0 + 2 * PF_K < d) fetch(k0 + 2 * PF_K);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st);
+  for (int st = 0; st < nk; ++st) {
+    // this stage's loads have landed (up to NS - 2 later stages may stay in flight), in
+    // every wave
+    const int later = min(NS - 2, nk - 1 - st);
+    if (later >= 2) {
+      if (NS - 2 >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPS) : "memory");
+    } else if (later == 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();
-    cur ^= 1;
+    // a bare barrier: __syncthreads() would also wait for the stages still in flight
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nk) issue(st + NS - 1);  // into the buffer every wave has finished with
+    const _Float16* base = sbuf + (st % NS) * STAGE;
+    half8_t bx[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bx[0][t] = frag(base, NM * BLK_A, wn * 64 + t * 16);
+      bx[1][t] = frag(base, NM * BLK_A + BLK_B, wn * 64 + t * 16);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const half8_t aw = frag(base, m * BLK_A, wm * 16 * IT + i * 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(aw, bx[h][t], acc[m][i][t]);
+      }
   }
   // epilogue: lane holds token 16t + r16 and neurons 16i + 4g .. +3 of the wave's block
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int i0 = m0 + wm * 64 + i * 16 + 4 * g;
+  for (int i = 0; i < IT; ++i) {
+    const int i0 = m0 + wm * 16 * IT + i * 16 + 4 * g;
     float ba[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) ba[j] = (b_act && i0 + j < n) ? b_act[i0 + j] : 0.f;
@@ -328,7 +332,16 @@ __global__ __launch_bounds__(TPB) void k_pf_sum(const float* __restrict__ part, 
   }
 }
 
-size_t pf_np(int n) { return (size_t)(n + PF_T - 1) / PF_T * PF_T; }
+// H row length for the scratch: d_ffn rounded up to both neuron tiles (128 and 192)
+size_t pf_np(int n) { return (size_t)(n + 383) / 384 * 384; }
+
+template <bool GATED, int IT>
+void pf_up_launch(const LayerDev& L, const u32x4* xh, const u32x4* xl, int np, int nbt,
+                  _Float16* hh, _Float16* hl, hipStream_t s) {
+  const int nmt = np / (32 * IT);
+  hipLaunchKernelGGL((k_pf_up<GATED, IT>), dim3((nmt + 7) / 8 * 8 * nbt), dim3(TPB), 0, s,
+                     L.w_act, L.act_ld, L.b_act, xh, xl, L.d, L.n, np, nmt, hh, hl);
+}
 
 }  // namespace
 
@@ -360,8 +373,8 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
                        size_t work_bytes, hipStream_t s) {
   const int chunk = prefill_chunk(L, work_bytes);
   if (chunk < PF_T) return hipErrorInvalidValue;
-  const int d = L.d, n = L.n, np = (int)pf_np(n);
-  const int nmt = np / PF_T, nct = d / PF_T;
+  const int d = L.d, n = L.n;
+  const int nct = d / PF_T;
   for (int b0 = 0; b0 < B; b0 += chunk) {
     const int bc = std::min(chunk, B - b0);
     const int Bp = (bc + PF_T - 1) / PF_T * PF_T;
@@ -369,8 +382,8 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
     auto take = [&](size_t bytes) { char* q = p; p += pf_align(bytes); return q; };
     u32x4* xh = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
     u32x4* xl = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
-    _Float16* hh = reinterpret_cast<_Float16*>(take((size_t)Bp * np * 2));
-    _Float16* hl = reinterpret_cast<_Float16*>(take((size_t)Bp * np * 2));
+    _Float16* hh = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));  // rows np <= pf_np(n)
+    _Float16* hl = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));
     float* part = reinterpret_cast<float*>(take((size_t)PF_SMAX * Bp * d * 4));
     const float* xc = x + (size_t)b0 * d;
     float* yc = y + (size_t)b0 * d;
@@ -378,16 +391,25 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
     hipLaunchKernelGGL(k_pf_split, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)), dim3(TPB),
                        0, s, xc, bc, Bp, d, xh, xl);
     const int nbt = Bp / PF_T;
-    const dim3 gup((nmt + 7) / 8 * 8 * nbt);
-    if (L.gated)
-      hipLaunchKernelGGL(k_pf_up<true>, gup, dim3(TPB), 0, s, L.w_act, L.act_ld, L.b_act, xh, xl, d,
-                         n, np, nmt, hh, hl);
-    else
-      hipLaunchKernelGGL(k_pf_up<false>, gup, dim3(TPB), 0, s, L.w_act, L.act_ld, L.b_act, xh, xl, d,
-                         n, np, nmt, hh, hl);
-    // split the neurons when the output tiles alone leave compute units idle
+    // neuron tile 128 or 192, whichever finishes first with one tile a compute unit at a
+    // time: rounds of tiles x the tile's size (ties: 128)
+    auto cost = [&](int mr) {
+      const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
+      return (tiles + L.n_cus - 1) / L.n_cus * mr;
+    };
+    const int mr = cost(192) < cost(128) ? 192 : 128;
+    const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
+    if (L.gated) {
+      if (mr == 192) pf_up_launch<true, 6>(L, xh, xl, np, nbt, hh, hl, s);
+      else pf_up_launch<true, 4>(L, xh, xl, np, nbt, hh, hl, s);
+    } else {
+      if (mr == 192) pf_up_launch<false, 6>(L, xh, xl, np, nbt, hh, hl, s);
+      else pf_up_launch<false, 4>(L, xh, xl, np, nbt, hh, hl, s);
+    }
+    // split the neurons until there are two workgroups a compute unit (the down kernel
+    // keeps one LDS buffer and relies on the second workgroup to cover its loads)
     int S = 1;
-    while (S < PF_SMAX && nct * nbt * S < L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
+    while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
     hipLaunchKernelGGL(k_pf_down, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
                        L.b_out, hh, hl, d, n, np, bc, Bp, S, yc, part);
     if (S > 1) {

@@ -63,6 +63,25 @@ def test_prefill_matches_oracle(name, d, n, B, chunk, bundle):
     assert max(rel_err_rows(y, yd)) <= 1e-5
 
 
+@pytest.mark.parametrize("name,d,n,gated", [("C2", 512, 9000, False), ("C3", 512, 9000, True)])
+def test_prefill_192_neuron_tiles(name, d, n, gated):
+    """512 tokens over 9000 neurons: 192-neuron tiles finish in one round where 128-neuron
+    tiles take two, so the up kernel takes its 192-row form (plain and gated); eight sampled
+    tokens against the oracle."""
+    c = cfg(name)
+    say(f"prefill 192-neuron tiles {name} d={d} n={n}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=64, max_batch=4)
+    from synth import make_tokens
+    X = make_tokens(c, 512, 522, "cuda", d=d)
+    y = _prefill(s, X, 512)
+    sel = [0, 5, 127, 128, 300, 383, 384, 511]
+    Xh = to_np(X)[sel]
+    Y = oracle.dense(Xh, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    errs = rel_err_rows(y[sel], Y)
+    say(f"  err={max(errs):.2e}")
+    assert max(errs) <= REL_TOL, max(errs)
+
+
 def test_prefill_full_size_gated():
     """The full Llama-7B-shaped gated layer (d 4096, d_ffn 11008) at 512 tokens in one chunk:
     four sampled tokens against the oracle."""
