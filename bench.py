@@ -20,6 +20,9 @@ HBM; exactly --steps steps are timed, bracketed by device synchronizations.
 
 Also measured, beside the headline number:
   - the per-layer time of each graph replay in the timed region (p10 / p50 / p90);
+  - cache-cold layer times: one-step graphs with a 512 MiB pass over a flush buffer before
+    each replay (more than the 256 MB last-level cache), against the same graphs warm
+    (`cache_cold`);
   - per-kernel durations from HIP events that each kernel dispatch stamps itself (start and
     end of execution, on the library's stream), with each kernel's algorithmic bytes (and,
     for the matrix-core kernels, flops) per launch;
@@ -43,7 +46,9 @@ Also measured, beside the headline number:
     Llama-7B-shaped gated stack at 16-64 tokens, where the union of the tokens' sets grows,
     and the dense route as 512-token prefill against torch (`dense_crossover`);
   - the fp64 CPU oracle on a bounded sample of the same workload, single-threaded and with
-    OpenMP on the host's cores, with the host's core count and CPU model.
+    OpenMP on the host's cores, with the host's core count and CPU model, and the oracle's
+    dense FFN (every neuron, one thread);
+  - the device, its compute units and peak clocks, and the HIP / ROCm versions (`device`).
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -255,6 +260,79 @@ class Timer:
         return total / self.steps, per
 
 
+def device_env(torch):
+    """The device and software the run used: name, architecture, compute units, peak engine
+    and memory clocks (HIP device attributes), HIP, ROCm and torch versions."""
+    p = torch.cuda.get_device_properties(0)
+    env = {"device": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+           "hbm_bytes": int(p.total_memory), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version", encoding="utf-8").read().strip()
+    except OSError:
+        pass
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                              ctypes.c_int]
+
+        def attr(a):
+            v = ctypes.c_int()
+            return int(v.value) if hip.hipDeviceGetAttribute(ctypes.byref(v), a, 0) == 0 else None
+
+        # hipDeviceAttribute_t values: ClockRate 5 and MemoryClockRate 60 (kHz),
+        # MultiprocessorCount 63; the clocks are kept only when the count read the same way
+        # agrees with torch's
+        if attr(63) == p.multi_processor_count:
+            sclk, mclk = attr(5), attr(60)
+            if sclk:
+                env["sclk_peak_mhz"] = sclk / 1000.0
+            if mclk:
+                env["mclk_peak_mhz"] = mclk / 1000.0
+    except OSError:
+        pass
+    return env
+
+
+def run_cold(torch, step_fn, L, T, reps=32, flush_mib=512):
+    """Cache-cold layer times: before each replay of a one-step graph (all L layers of one
+    step), a torch add over a flush_mib MiB buffer evicts the L2 caches and the 256 MB
+    last-level cache; events around the replay alone time it. The same one-step graphs
+    replayed back to back without the flush give the warm figure beside it."""
+    cap = torch.cuda.Stream()
+    K = min(8, T)
+    graphs = []
+    for t in range(K):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step_fn(t, cap)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    flush = torch.zeros(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for mode in ("warm", "cold"):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps + K):  # the first K replays are warm-up
+            if mode == "cold":
+                flush.add_(1)
+            j = i - K
+            if j >= 0:
+                ev[2 * j].record()
+            graphs[i % K].replay()
+            if j >= 0:
+                ev[2 * j + 1].record()
+        torch.cuda.synchronize()
+        v = np.array([ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(reps)]) * 1000.0 / L
+        out[mode] = {"us_per_layer_p50": round(float(np.median(v)), 3),
+                     "p10": round(float(np.percentile(v, 10)), 3),
+                     "p90": round(float(np.percentile(v, 90)), 3)}
+    del graphs, flush
+    out["cold_over_warm"] = round(out["cold"]["us_per_layer_p50"] / out["warm"]["us_per_layer_p50"], 4)
+    out["method"] = (f"one-step graphs ({L} layers, {K} tokens in turn), {reps} timed replays "
+                     f"each way; cold: a {flush_mib} MiB read-modify-write pass before every "
+                     f"replay, outside the events")
+    return out
+
+
 def percentiles_us(per_step_ms, L):
     v = np.asarray(per_step_ms) * 1000.0 / L
     return {"p10": round(float(np.percentile(v, 10)), 3), "p50": round(float(np.percentile(v, 50)), 3),
@@ -435,6 +513,11 @@ def main():
     ms_per_step, per_replay = timer.run(step(layers))
     us_per_layer = ms_per_step * 1000.0 / L
     log(f"sparse decode: {ms_per_step:.4f} ms/step, {us_per_layer:.3f} us/layer")
+    cold = None
+    if not args.no_extra and not args.no_graph:
+        cold = run_cold(torch, step(layers), L, T)
+        log(f"cache-cold: {cold['cold']['us_per_layer_p50']} us/layer against "
+            f"{cold['warm']['us_per_layer_p50']} warm (one-step graphs)")
 
     cnt = counts.cpu().numpy().astype(np.int64)  # union rows per (step, layer)
     if B == 1:
@@ -731,6 +814,23 @@ def main():
                "single_thread": single}
         log(f"cpu oracle, OpenMP {threads} threads: {cpu['value']} us/layer over {len(tm)} samples "
             f"({model}, nproc {nproc})")
+        if B == 1:
+            # the dense FFN on the CPU: every neuron, no predictor, in the oracle's fp64
+            # arithmetic (its dense routine is single-threaded)
+            td, t_start = [], time.time()
+            while (time.time() - t_start < args.cpu_seconds / 2 and len(td) < 64) or len(td) < 3:
+                l = len(td) % n_cpu_layers
+                Lh = host[l]
+                x = np.ascontiguousarray(Xh[len(td) % T, l])
+                c0 = time.perf_counter()
+                _ = oracle.dense(x, Lh["w_a"], Lh["w_o"], Wu=Lh["w_u"], b_a=Lh["b_a"],
+                                 b_o=Lh["b_o"])
+                td.append((time.perf_counter() - c0) * 1e6)
+            cpu["dense_ffn"] = {"value": round(float(np.median(td)), 1), "unit": "us/layer",
+                                "cores": 1, "samples": len(td),
+                                "what": "the FFN over every neuron (no predictor), fp64 oracle "
+                                        "arithmetic, one thread"}
+            log(f"cpu dense FFN, 1 thread: {cpu['dense_ffn']['value']} us/layer")
         del host, Xh
 
     # ------------------------------------------------------------------ the 5% -> 10% ramp
@@ -809,6 +909,8 @@ def main():
         "single_pass": single_pass,
         "predictor_quality": quality,
         "cpu_baseline": cpu,
+        "cache_cold": cold,
+        "device": device_env(torch),
         "lookahead": lookahead,
         "c2_ramp": ramp,
         "dense_crossover": crossover,
