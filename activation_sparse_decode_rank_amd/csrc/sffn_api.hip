@@ -162,7 +162,13 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
     // deterministic mode: two splits add into y exactly in either order; more meet in the
     // fixed-order join
     L.join_tile = desc->deterministic && L.ks_tile > 2;
-    L.g_up = std::max(1, std::min((desc->d_ffn + 15) / 16, 4 * cus));
+    L.g_up = std::max(1, std::min((desc->d_ffn + 7) / 8, 4 * cus));
+    // Up tiles of 8 listed rows (twice the workgroups) while the expected union would keep
+    // at most half the compute units busy with 16-row tiles: on the gated Llama-7B shape
+    // 28.5 against 30.4 us a layer at 2 tokens (16% union); at 4 and 8 tokens (25%, 39%)
+    // they measured slower (35.9 against 34.1, 46.5 against 45.0).
+    L.up_half_b = sffn::host::union_within_batch(desc->neuron_freq, desc->d_ffn, 8.0 * cus,
+                                                 std::min(desc->max_batch, 15));
     // stream-K up projection: two workgroups per compute unit, and enough that one
     // range touches at most 13 tiles of the largest list
     L.g_sk = std::min(sffn::SK_G_MAX, std::max(2 * cus, ((desc->d_ffn + 15) / 16 + 12) / 13));

@@ -136,5 +136,24 @@ inline int dense_from_batch(const float* freq, int n, double dense_union, int ma
   return never;
 }
 
+// The largest batch size b in [2, max_b] (0: none) up to which the expected union of the
+// tokens' predicted sets, sum_i 1 - (1 - f_i)^b (independent tokens), stays within
+// max_rows; with no frequencies the union is bounded by n. The union grows with b, so
+// every smaller batch from 2 on qualifies as well.
+inline int union_within_batch(const float* freq, int n, double max_rows, int max_b) {
+  int best = 0;
+  for (int b = 2; b <= max_b; ++b) {
+    double u = 0.0;
+    if (freq) {
+      for (int i = 0; i < n; ++i) u += 1.0 - std::pow(1.0 - clamp_freq(freq[i]), (double)b);
+    } else {
+      u = (double)n;
+    }
+    if (!(u <= max_rows)) break;
+    best = b;
+  }
+  return best;
+}
+
 }  // namespace host
 }  // namespace sffn

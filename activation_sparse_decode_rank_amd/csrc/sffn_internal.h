@@ -71,7 +71,8 @@ struct LayerDev {
   int ks_tile;   // the same for the batch (matrix-core) down projection
   bool join_tile;  // its splits meet in the fixed-order join (deterministic mode, ks_tile > 2)
   int ldh;       // row stride of token-major activations hT [B][ldh] (d_ffn rounded up to 64, plus 64)
-  int g_up;      // workgroups of the batch up projection (each loops over 16-row tiles)
+  int g_up;      // workgroups of the batch up projection (each loops over row tiles)
+  int up_half_b;  // up to this batch size (0: none) its tiles take 8 listed rows, not 16
   int g_sk;      // workgroups of its stream-K form (at most SK_G_MAX)
   bool rs_in_arg;  // the range table travels in the middle kernel's arguments (ra)
   RangeArg ra;     // copy of the range table (valid entries 0..g_mid when rs_in_arg)

@@ -272,7 +272,7 @@ constexpr int FW_WORDS_MAX = 1024;  // union words the up kernel can list itself
 // pref[w] <= p < pref[w + 1] (found by binary search over the prefixes; empty words share
 // their successor's prefix and are never chosen). The positions of its own tiles are
 // written to idx, with their token bits; workgroup 0 writes the count.
-template <bool GATED, int NT, int TR, int W, bool FW>
+template <bool GATED, int NT, int TR, int W, bool FW, bool HALF>
 __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_act, int ld_act,
                                                     const float* __restrict__ b_act,
                                                     const u32x4* __restrict__ x_hl, int d,
@@ -286,7 +286,11 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
   constexpr int NM = GATED ? 2 : 1;
   constexpr int KP = (NT == 1 && TR == 1) ? 2 : 1;    // 64-input step pairs per load batch
   constexpr int PITCH = 9;                            // transpose buffer row pitch in chunks
-  constexpr int RT = 16 * TR;                         // rows per workgroup iteration
+  // rows per workgroup iteration; HALF: 8 listed rows a tile (rows 8..15 of each operand
+  // tile stay zero and their results are dropped), so a small union spreads over twice the
+  // workgroups
+  constexpr int RT = HALF ? 8 : 16 * TR;
+  static_assert(!HALF || TR == 1, "half tiles take one row tile");
   __shared__ u32x4 s_w[W][KP][TR][NM][16 * PITCH];
   __shared__ float4_t s_acc[W][TR][NM][NT][64];
   for (int i = blockIdx.x * 64 * W + threadIdx.x; i < ny; i += gridDim.x * 64 * W) y0[i] = 0.f;
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
       ia[i] = idx[min((int)blockIdx.x * RT + 16 * i + lr, n - 1)];
-      ib[i] = idx[min((int)blockIdx.x * RT + 16 * i + 8 + lr, n - 1)];
+      ib[i] = HALF ? 0 : idx[min((int)blockIdx.x * RT + 16 * i + 8 + lr, n - 1)];
     }
     cnt = min(max(cnt_raw, 0), n);
   }
@@ -357,6 +361,11 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) tok[tt] = min(16 * tt + r16, B - 1);
   u32x4* sw = &s_w[wave][0][0][0][0];
+  if constexpr (HALF) {
+    // rows 8..15 of every operand tile buffer: zero once, never written again
+    for (int q = lane; q < KP * TR * NM * 8 * PITCH; q += 64)
+      sw[(q / (8 * PITCH)) * 16 * PITCH + 8 * PITCH + q % (8 * PITCH)] = u32x4{0u, 0u, 0u, 0u};
+  }
   const int et = wave < TR ? wave : 0;   // the tile whose epilogue this wave finishes
   for (int u = blockIdx.x; u * RT < cnt; u += gridDim.x) {
     if constexpr (FW) {
@@ -393,13 +402,13 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
       for (int i = 0; i < TR; ++i) {
         ia[i] = s_rows[16 * i + lr];
-        ib[i] = s_rows[16 * i + 8 + lr];
+        ib[i] = HALF ? 0 : s_rows[16 * i + 8 + lr];
       }
     } else if (u != (int)blockIdx.x) {
 #pragma unroll
       for (int i = 0; i < TR; ++i) {
         ia[i] = idx[min(u * RT + 16 * i + lr, cnt - 1)];
-        ib[i] = idx[min(u * RT + 16 * i + 8 + lr, cnt - 1)];
+        ib[i] = HALF ? 0 : idx[min(u * RT + 16 * i + 8 + lr, cnt - 1)];
       }
     }
     const u32x4* pa[TR];
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
             wa[bb][kp][i][m] = ld_stream(pa[i], (size_t)m * nch + 8 * p);
-            wb[bb][kp][i][m] = ld_stream(pb[i], (size_t)m * nch + 8 * p);
+            if constexpr (!HALF) wb[bb][kp][i][m] = ld_stream(pb[i], (size_t)m * nch + 8 * p);
           }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
           for (int m = 0; m < NM; ++m) {
             u32x4* bw = sw + ((kp * TR + i) * NM + m) * 16 * PITCH;
             bw[lr * PITCH + lc] = wa[bb][kp][i][m];
-            bw[(8 + lr) * PITCH + lc] = wb[bb][kp][i][m];
+            if constexpr (!HALF) bw[(8 + lr) * PITCH + lc] = wb[bb][kp][i][m];
           }
       wave_lds_sync();
 #pragma unroll
@@ -486,7 +495,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (FW) {
-          ej[j] = s_rows[16 * et + 4 * g + j];
+          ej[j] = s_rows[min(16 * et + 4 * g + j, RT - 1)];
           em[j] = tok_full[ej[j]];
         } else {
           const int pc = min(u * RT + 16 * et + 4 * g + j, cnt - 1);
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(64 * W) void k_up_mfma(const void* __restrict__ w_a
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int p = u * RT + 16 * et + 4 * g + j;
-          if (p < cnt && b < B) {
+          if (p < cnt && b < B && (!HALF || g < 2)) {
             const bool ok = ej[j] >= 0 && ej[j] < n;
             const float a0 = v[0][j] + eb[j];
             float h = a0 > 0.f ? a0 : 0.f;
@@ -1202,7 +1211,7 @@ hipError_t scores_launch(const LayerDev& L, int B, float* scores, hipStream_t s)
 
 // fw: the up kernel lists the union itself from the words and token bits the score kernel
 // left in the workspace, writing idx, count and tokmask; otherwise it reads them
-template <bool GATED, int NT, int TR, int W>
+template <bool GATED, int NT, int TR, int W, bool HALF = false>
 void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_t* count,
                       const uint64_t* tokmask, const uint64_t* tok_by_neuron, float* y0, int ny,
                       hipStream_t s, const hipEvent_t* tev, bool fw) {
@@ -1210,11 +1219,11 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
   int32_t* cnt_w = const_cast<int32_t*>(count);
   uint64_t* tok_w = const_cast<uint64_t*>(tokmask);
   if (fw)
-    launch(k_up_mfma<GATED, NT, TR, W, true>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
+    launch(k_up_mfma<GATED, NT, TR, W, true, HALF>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
            L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
            (const uint64_t*)L.words, (const uint64_t*)L.tok_full, L.h_buf, L.ldh, y0, ny);
   else
-    launch(k_up_mfma<GATED, NT, TR, W, false>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
+    launch(k_up_mfma<GATED, NT, TR, W, false, HALF>, dim3(L.g_up), dim3(64 * W), 0, s, tev, L.w_act, L.act_ld,
            L.b_act, static_cast<const u32x4*>(L.x_hl), L.d, L.n, B, idx_w, cnt_w, tok_w,
            (const uint64_t*)nullptr, tok_by_neuron, L.h_buf, L.ldh, y0, ny);
 }
@@ -1225,7 +1234,8 @@ void up_tile_launch_t(const LayerDev& L, int B, const int32_t* idx, const int32_
 // paired workgroup needs more registers than let two of them share a compute unit, and
 // the pairs then outnumber the compute units (measured no faster at 32 tokens); below 16
 // tokens eight waves on one row tile measured slower (2 tokens 18.3 vs 17.5 us, 8 tokens
-// 30.9 vs 26.7 us on the Llama-7B shape).
+// 30.9 vs 26.7 us on the Llama-7B shape). Up to L.up_half_b tokens (a union expected to
+// fill at most half the compute units with 16-row tiles) a tile takes 8 listed rows.
 template <bool GATED, int NT, int TR, int W>
 void up_sk_launch(const LayerDev& L, int B, int32_t* idx, int32_t* count, uint64_t* tokmask,
                   float* y0, int ny, hipStream_t s, const hipEvent_t* tev, int grid) {
@@ -1270,7 +1280,12 @@ void up_tile_launch(const LayerDev& L, int B, const int32_t* idx, const int32_t*
     return;
   }
   switch (nt) {
-    case 1: up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
+    case 1:
+      if (B <= L.up_half_b)
+        up_tile_launch_t<GATED, 1, 1, 4, true>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw);
+      else
+        up_tile_launch_t<GATED, 1, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw);
+      break;
     case 2: up_tile_launch_t<GATED, 2, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
     case 3: up_tile_launch_t<GATED, 3, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;
     default: up_tile_launch_t<GATED, 4, 1, 4>(L, B, idx, count, tokmask, tok_by_neuron, y0, ny, s, tev, fw); break;

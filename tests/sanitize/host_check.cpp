@@ -94,6 +94,21 @@ int main() {
     } else {
       CHECK(uni_at(64) <= thr);
     }
+    // half-tile batches: the last batch whose expected union stays within the bound
+    const double rows = uni(0.0, 1.2) * n;
+    const int hb = sffn::host::union_within_batch(nofreq ? nullptr : f.data(), n, rows, 15);
+    CHECK(hb == 0 || (hb >= 2 && hb <= 15));
+    if (nofreq) {
+      CHECK(hb == (n <= rows ? 15 : 0));
+    } else {
+      auto rows_at = [&](int bb) {
+        double u = 0.0;
+        for (int i = 0; i < n; ++i) u += 1.0 - std::pow(1.0 - sffn::host::clamp_freq(f[i]), (double)bb);
+        return u;
+      };
+      if (hb >= 2) CHECK(rows_at(hb) <= rows);
+      if (hb < 15) CHECK(rows_at(hb < 2 ? 2 : hb + 1) > rows);
+    }
   }
 
   // ---- permutation: the library's and the oracle's, equal, and valid
