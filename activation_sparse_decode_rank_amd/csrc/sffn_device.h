@@ -40,6 +40,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Buffer resources for the raw buffer load/store builtins: word 3 of the descriptor for
+// the gfx9 family (untyped 32-bit data, no swizzle), and the cache-policy bit that makes an
+// access device-coherent (sc1: what agent-scope atomic loads and stores use on this part).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+constexpr int CPOL_SC1 = 16;
+
 // A "chunk" is 16 bytes of weights: 8 fp16 or 4 fp32 elements.
 template <bool F16>
 struct Elt {

@@ -1096,9 +1096,14 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
   __syncthreads();
   if (JOIN && KS > 1) {
     // every split takes part, an empty one with zeros; slot o of split kq holds output o
+    // The slots are written and read 16 bytes a lane with the device-coherent cache policy
+    // (sc1, as agent-scope atomic stores and loads use), so every store fills whole lines:
+    // one 4-byte coherent store per value would write each line through four times.
     constexpr int NO = 4 * NT * 64;
     __shared__ int s_last;
     float* slot = dn_part + (size_t)cb * KS * NO * 4;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(slot, 0, KS * NO * 16, BUF_RSRC_WORD3);
     float4_t mine[NT];
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
@@ -1109,11 +1114,9 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
       mine[it] = ((s_acc[0][cg][tt][l] + s_acc[1][cg][tt][l]) + s_acc[2][cg][tt][l]) +
                  s_acc[3][cg][tt][l];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mine[it][j] += bo;
-        __hip_atomic_store(slot + ((size_t)kq * NO + o) * 4 + j, mine[it][j], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int j = 0; j < 4; ++j) mine[it][j] += bo;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[it]), rsrc,
+                                             (kq * NO + o) * 16, 0, CPOL_SC1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -1130,14 +1133,11 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
         float4_t pv[KS_JOIN_MAX];
 #pragma unroll
         for (int q = 0; q < KS_JOIN_MAX; ++q) {
-          if (q < KS && q != kq) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              pv[q][j] = __hip_atomic_load(slot + ((size_t)q * NO + o) * 4 + j, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-          } else {
+          if (q < KS && q != kq)
+            pv[q] = __builtin_bit_cast(
+                float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (q * NO + o) * 16, 0, CPOL_SC1));
+          else
             pv[q] = mine[it];
-          }
         }
         float4_t a = pv[0];
 #pragma unroll
