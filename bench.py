@@ -25,8 +25,8 @@ Also measured, beside the headline number:
     (`cache_cold`);
   - per-kernel durations from HIP events that each kernel dispatch stamps itself (start and
     end of execution, on the library's stream) over a second eager pass of --kernel-tokens
-    steps (the first warms the launch path): the mean of the middle 90% of the dispatches,
-    with the median and the plain mean beside it, and each kernel's algorithmic bytes (and,
+    steps (the first warms the launch path): the median dispatch, with the mean and the
+    p10 / p90 beside it, and each kernel's algorithmic bytes (and,
     for the matrix-core kernels, flops) per launch; the roofline object also times a plain
     read of the dominant kernel's byte count;
   - a plain read stream over 4 GiB (the library's read probe) at 1, 2 and 8 workgroups a
@@ -659,16 +659,17 @@ def main():
     hev.close()
     kernels = {}
     for k in names:
-        # mean of the middle 90% of the dispatches: an eager dispatch now and then runs
-        # long (seen as a mean that moved by 10% between runs on one device while the
-        # median stayed within 2%); the kernel trace of graph replays shows no such tail
+        # the median dispatch: the eager event pass has a tail of slow dispatches (its mean
+        # moved by 10% between runs on one device) that the graph replays of the timed
+        # region do not show; their kernel-trace mean agrees with this median within 1%
         v = np.sort(np.asarray(kus[k]))
-        cut = len(v) // 20
-        us = float(np.mean(v[cut:len(v) - cut])) if len(v) > 2 * cut else float(np.mean(v))
+        us = float(np.median(v))
         gb = float(np.mean(kbytes[k])) / (us * 1e-6) / 1e9
         kernels[k] = {"avg_us": round(us, 3), "algorithmic_bytes": int(np.mean(kbytes[k])),
-                      "gbps": round(gb, 1), "p50_us": round(float(np.median(v)), 3),
-                      "mean_us_all": round(float(np.mean(v)), 3)}
+                      "gbps": round(gb, 1), "estimator": "median of the event pass",
+                      "mean_us": round(float(np.mean(v)), 3),
+                      "p10_us": round(float(np.percentile(v, 10)), 3),
+                      "p90_us": round(float(np.percentile(v, 90)), 3)}
         if np.mean(kflops[k]) > 0:
             tf = float(np.mean(kflops[k])) / (us * 1e-6) / 1e12
             kernels[k]["algorithmic_flops"] = int(np.mean(kflops[k]))
