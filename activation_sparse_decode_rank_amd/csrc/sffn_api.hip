@@ -235,6 +235,12 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
         const int want = (int)std::ceil(ea / sffn::DOWN_B1_BATCH);
         L.ks_down = std::min(std::max(L.ks_down, want), std::min(8, sffn::KS_MAX));
       }
+      // joined splits: no more than keep every split's workgroup resident at once (on the
+      // OPT-175B slice 4 splits instead of 5: 60.1 against 60.6 us a layer, and the
+      // look-ahead decode 56.9 against 59.6; the fast mode's atomics measured better with
+      // 5, 57.5 against 59.8)
+      const int occ_dn = sffn::occ_down_b1(L);
+      const int ks_resident = occ_dn > 0 ? std::max(1, occ_dn * cus / sffn::down_blocks(L)) : 8;
       // Deterministic mode: at most two splits add into y (two addends into a zeroed y give
       // the same sum in either order). When the expected rows need more splits than two
       // (more than two batches), the fast mode's splits meet in a fixed-order join instead:
@@ -243,9 +249,10 @@ int sparse_ffn_create(const sffn_desc* desc, sparse_ffn_t* out) {
       L.b1_ok = sffn::occ_mid_b1(L) >= 0;
       if (desc->deterministic && L.b1_ok) {
         const int want = desc->neuron_freq ? (int)std::ceil(ea / sffn::DOWN_B1_BATCH) : 0;
-        if (want > 2) {
-          const int ks = (L.n_cus + sffn::down_blocks(L) - 1) / sffn::down_blocks(L);
-          L.ks_down = std::min(std::max(ks, want), sffn::KS_JOIN_MAX);
+        const int ks = (L.n_cus + sffn::down_blocks(L) - 1) / sffn::down_blocks(L);
+        const int kj = std::min(std::max(ks, std::min(want, ks_resident)), sffn::KS_JOIN_MAX);
+        if (want > 2 && kj > 2) {
+          L.ks_down = kj;
           L.join_b1 = true;
         }
       }

@@ -875,6 +875,18 @@ bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
   return L.gated ? mid_b1_any<false, true>(L, x, scores, s, tev) : mid_b1_any<false, false>(L, x, scores, s, tev);
 }
 
+template <bool F16>
+int down_b1_occ() {
+  // the widest form (eight ranges a thread) bounds the others' registers
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_down_b1<F16, 8, true>, TPB,
+                                                   (size_t)LIST_CAP * 4) != hipSuccess)
+    occ = 0;
+  return occ;
+}
+
+int occ_down_b1(const LayerDev& L) { return L.w_f16 ? down_b1_occ<true>() : down_b1_occ<false>(); }
+
 int occ_mid_b1(const LayerDev& L) {
   if (L.w_f16 != L.p_f16) return -1;
   if (L.w_f16) return L.gated ? mid_b1_occ_any<true, true>(L) : mid_b1_occ_any<true, false>(L);

@@ -126,6 +126,7 @@ void run_stage1(const LayerDev& L, const float* x, int B, hipStream_t s, const h
                 float* y0, int ny, bool split_x);
 bool run_mid_b1(const LayerDev& L, const float* x, float* scores, hipStream_t s,
                 const hipEvent_t* tev);
+int occ_down_b1(const LayerDev& L);  // workgroups per CU of the single-token down kernel
 int occ_mid_b1(const LayerDev& L);  // workgroups per CU, -1 when no batch-1 kernel applies
 // look-ahead decode (one token): which layers its kernels cover; begin (stage 1 and the
 // scores of layer Nx on x, leaving Nx's range words); one layer C on x over its held set,
