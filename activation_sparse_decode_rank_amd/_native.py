@@ -15,6 +15,7 @@ SFFN_STATIC_SCRATCH_BYTES = 16 << 20
 SFFN_F32, SFFN_F16 = 0, 1
 SFFN_LAYOUT_SPLIT, SFFN_LAYOUT_BUNDLE = 0, 1
 SFFN_UP_ROWS, SFFN_UP_COLUMNS = 0, 1
+SFFN_PREFILL_FP16_ACT = 1
 SFFN_MAX_BATCH = 64
 
 
@@ -66,6 +67,7 @@ def _load():
         "sparse_ffn_up_probe_work_bytes": (SZ, [I32]),
         "sparse_ffn_prefill_work_bytes": (SZ, [P, I32]),
         "sparse_ffn_prefill": (C.c_int, [P, P, I32, P, P, SZ, P]),
+        "sparse_ffn_prefill_ex": (C.c_int, [P, P, I32, P, P, SZ, I32, P]),
         "sparse_ffn_up_probe": (C.c_int, [P, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -83,7 +85,7 @@ EXPORTED = ("sparse_ffn_workspace_bytes", "sparse_ffn_create", "sparse_ffn_destr
             "sparse_ffn_status_string", "sparse_ffn_set_timing_events",
             "sparse_ffn_profile_counts", "sparse_ffn_permutation", "sparse_ffn_pack_rows",
             "sparse_ffn_read_probe", "sparse_ffn_up_probe_work_bytes", "sparse_ffn_up_probe",
-            "sparse_ffn_prefill_work_bytes", "sparse_ffn_prefill")
+            "sparse_ffn_prefill_work_bytes", "sparse_ffn_prefill", "sparse_ffn_prefill_ex")
 
 
 def lib():
@@ -177,6 +179,11 @@ def sparse_ffn_prefill_work_bytes(handle, chunk_tokens) -> int:
 
 def sparse_ffn_prefill(handle, x, B, y, work, work_bytes, stream) -> None:
     _ck(_lib.sparse_ffn_prefill(handle, x, B, y, work, work_bytes, stream), "sparse_ffn_prefill")
+
+
+def sparse_ffn_prefill_ex(handle, x, B, y, work, work_bytes, flags, stream) -> None:
+    _ck(_lib.sparse_ffn_prefill_ex(handle, x, B, y, work, work_bytes, flags, stream),
+        "sparse_ffn_prefill_ex")
 
 
 def sparse_ffn_up_probe_work_bytes(d_ffn) -> int:

@@ -383,17 +383,23 @@ size_t sparse_ffn_prefill_work_bytes(sparse_ffn_t h, int32_t chunk_tokens) {
   return sffn::prefill_work_bytes(h->L, chunk_tokens);
 }
 
-int sparse_ffn_prefill(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
-                       size_t work_bytes, void* stream) {
+int sparse_ffn_prefill_ex(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
+                          size_t work_bytes, int32_t flags, void* stream) {
   if (!h || !x || !y || !work || B < 1) return SFFN_ERR_INVALID;
+  if ((flags & ~SFFN_PREFILL_FP16_ACT) != 0) return SFFN_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(work) & 255u))
     return SFFN_ERR_INVALID;
   if (!sffn::prefill_ok(h->L)) return SFFN_ERR_UNSUPPORTED;
   if (sffn::prefill_chunk(h->L, work_bytes) < 1) return SFFN_ERR_INVALID;
-  return sffn::run_prefill(h->L, x, B, y, work, work_bytes, static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
+  return sffn::run_prefill(h->L, x, B, y, work, work_bytes, (flags & SFFN_PREFILL_FP16_ACT) != 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
              ? SFFN_OK
              : SFFN_ERR_HIP;
+}
+
+int sparse_ffn_prefill(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
+                       size_t work_bytes, void* stream) {
+  return sparse_ffn_prefill_ex(h, x, B, y, work, work_bytes, 0, stream);
 }
 
 int sparse_ffn_decode_static(sparse_ffn_t h, const float* x, int32_t B, float* y, int32_t* idx,

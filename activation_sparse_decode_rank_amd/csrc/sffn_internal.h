@@ -233,7 +233,7 @@ bool prefill_ok(const LayerDev& L);
 size_t prefill_work_bytes(const LayerDev& L, int chunk);
 int prefill_chunk(const LayerDev& L, size_t work_bytes);
 hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void* work,
-                       size_t work_bytes, hipStream_t s);
+                       size_t work_bytes, bool fp16_act, hipStream_t s);
 // input-sparse up projection probe: layout 0 rows [n][d], 1 columns [d][n] (fp16)
 size_t up_probe_work_bytes(int n);
 hipError_t launch_up_probe(const void* w, int layout, int d, int n, const float* x,

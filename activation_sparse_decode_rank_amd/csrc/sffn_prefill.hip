@@ -6,7 +6,9 @@
 //
 // Arithmetic as on the decode path's matrix-core kernels: fp16 weights as stored, fp32
 // activations carried as fp16 hi + lo pairs (two products each, about 22 significant bits),
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation. The kernels' LO = false form (asked for
+// with SFFN_PREFILL_FP16_ACT) rounds the activations (x and h) to fp16 once and runs one
+// product each, half the matrix-core work and operand traffic, at fp16 activation precision.
 //
 // Three kernels per chunk of Bp tokens (Bp a multiple of 128; rows past the chunk's tokens
 // are zero):
@@ -40,7 +42,8 @@ __device__ __forceinline__ half8_t lds_get(const _Float16* base, int row, int k)
   return *reinterpret_cast<const half8_t*>(base + row * PF_P + k);
 }
 
-// x [B][d] fp32 -> hi, lo [Bp][d] fp16, rows B .. Bp-1 zero
+// x [B][d] fp32 -> hi, lo [Bp][d] fp16 (LO: lo as well), rows B .. Bp-1 zero
+template <bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, int B, int Bp, int d,
                                                   u32x4* __restrict__ xh, u32x4* __restrict__ xl) {
   const int nch = d / 8;
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, i
     half8_t hi, lo;
     split_hi_lo(a, e, hi, lo);
     xh[q] = __builtin_bit_cast(u32x4, hi);
-    xl[q] = __builtin_bit_cast(u32x4, lo);
+    if (LO) xl[q] = __builtin_bit_cast(u32x4, lo);
   }
 }
 
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, i
 // the neuron tile count is padded to a multiple of 8, so the workgroups sharing a weight
 // tile run on one XCD.
 constexpr int PFD_K = 32;  // inputs per stage
-template <bool GATED, int IT>
+template <bool GATED, int IT, bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, int ld_act,
                                                const float* __restrict__ b_act,
                                                const u32x4* __restrict__ xh,
@@ -84,9 +87,10 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   constexpr int MR = 32 * IT;                  // neurons per workgroup
   constexpr int GA = MR / 16, GB = PF_T / 16;  // 16-row groups of a weight / token operand
   constexpr int BLK_A = MR * PFD_K, BLK_B = PF_T * PFD_K;  // halfs per operand block
-  constexpr int STAGE = NM * BLK_A + 2 * BLK_B;            // halfs per stage
+  constexpr int NB = LO ? 2 : 1;                           // token blocks (hi, lo)
+  constexpr int STAGE = NM * BLK_A + NB * BLK_B;           // halfs per stage
   constexpr int NS = STAGE * 2 * 4 <= 128 * 1024 ? 4 : 3;  // stages held in LDS
-  constexpr int NG = NM * GA + 2 * GB;                     // 1 KB loads a stage
+  constexpr int NG = NM * GA + NB * GB;                    // 1 KB loads a stage
   constexpr int DPS = NG / (TPB / 64);                     // load instructions per wave a stage
   static_assert(NG % (TPB / 64) == 0, "whole loads per wave");
   __shared__ __attribute__((aligned(16))) _Float16 sbuf[NS * STAGE];
@@ -157,11 +161,11 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
     asm volatile("" ::: "memory");
     if (st + NS - 1 < nk) issue(st + NS - 1);  // into the buffer every wave has finished with
     const _Float16* base = sbuf + (st % NS) * STAGE;
-    half8_t bx[2][4];
+    half8_t bx[NB][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bx[0][t] = frag(base, NM * BLK_A, wn * 64 + t * 16);
-      bx[1][t] = frag(base, NM * BLK_A + BLK_B, wn * 64 + t * 16);
+      if constexpr (LO) bx[NB - 1][t] = frag(base, NM * BLK_A + BLK_B, wn * 64 + t * 16);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
       for (int i = 0; i < IT; ++i) {
         const half8_t aw = frag(base, m * BLK_A, wm * 16 * IT + i * 16);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NB; ++h)
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(aw, bx[h][t], acc[m][i][t]);
       }
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
       }
       const size_t o = (size_t)tok * np + i0;
       *reinterpret_cast<uint2*>(hh + o) = __builtin_bit_cast(uint2, hv);
-      *reinterpret_cast<uint2*>(hl + o) = __builtin_bit_cast(uint2, lv);
+      if (LO) *reinterpret_cast<uint2*>(hl + o) = __builtin_bit_cast(uint2, lv);
     }
   }
 }
@@ -210,13 +214,15 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
 // pair of neurons as one 32-bit word (the 32 lanes of a half wave write 32 consecutive
 // words). One LDS buffer; two workgroups fit a compute unit. S == 1 writes y (+ b_out) for
 // the chunk's real tokens; otherwise the split's sums go to part[s][Bp][d].
+template <bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down_t, int ld_down,
                                                  const float* __restrict__ b_out,
                                                  const _Float16* __restrict__ hh,
                                                  const _Float16* __restrict__ hl, int d, int n,
                                                  int np, int B, int Bp, int S,
                                                  float* __restrict__ y, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) _Float16 sH[2][PF_T * PF_P];
+  constexpr int NB = LO ? 2 : 1;  // activation halves (hi, lo)
+  __shared__ __attribute__((aligned(16))) _Float16 sH[NB][PF_T * PF_P];
   __shared__ __attribute__((aligned(16))) _Float16 sW[PF_T * PF_P];
   const int nct = d / PF_T, nbt = Bp / PF_T;
   const int ct = blockIdx.x % nct, bt = (blockIdx.x / nct) % nbt, s = blockIdx.x / (nct * nbt);
@@ -238,13 +244,13 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
     hseg[j] = q & 7;
   }
   const int wp = tid & 31, wcs = tid >> 5;  // neuron pair, 8-column piece (and + 8)
-  u32x4 rh[2][4], rw[2][2];                 // rw[piece][neuron of the pair]
+  u32x4 rh[NB][4], rw[2][2];                // rw[piece][neuron of the pair]
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const size_t o = (size_t)(b0 + hrow[j]) * np + k0 + hseg[j] * 8;
       rh[0][j] = *reinterpret_cast<const u32x4*>(hh + o);
-      rh[1][j] = *reinterpret_cast<const u32x4*>(hl + o);
+      if constexpr (LO) rh[NB - 1][j] = *reinterpret_cast<const u32x4*>(hl + o);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       lds_put(sH[0], hrow[j], hseg[j], rh[0][j]);
-      lds_put(sH[1], hrow[j], hseg[j], rh[1][j]);
+      if constexpr (LO) lds_put(sH[NB - 1], hrow[j], hseg[j], rh[NB - 1][j]);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -285,16 +291,16 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
 #pragma unroll
     for (int ks = 0; ks < PF_K; ks += 32) {
       const int k = ks + 8 * g;
-      half8_t bw[4], ah[2][4];
+      half8_t bw[4], ah[NB][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) bw[t] = lds_get(sW, wn * 64 + t * 16 + r16, k);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ah[0][i] = lds_get(sH[0], wm * 64 + i * 16 + r16, k);
-        ah[1][i] = lds_get(sH[1], wm * 64 + i * 16 + r16, k);
+        if constexpr (LO) ah[NB - 1][i] = lds_get(sH[NB - 1], wm * 64 + i * 16 + r16, k);
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NB; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -335,12 +341,49 @@ __global__ __launch_bounds__(TPB) void k_pf_sum(const float* __restrict__ part, 
 // H row length for the scratch: d_ffn rounded up to both neuron tiles (128 and 192)
 size_t pf_np(int n) { return (size_t)(n + 383) / 384 * 384; }
 
-template <bool GATED, int IT>
+template <bool GATED, int IT, bool LO>
 void pf_up_launch(const LayerDev& L, const u32x4* xh, const u32x4* xl, int np, int nbt,
                   _Float16* hh, _Float16* hl, hipStream_t s) {
   const int nmt = np / (32 * IT);
-  hipLaunchKernelGGL((k_pf_up<GATED, IT>), dim3((nmt + 7) / 8 * 8 * nbt), dim3(TPB), 0, s,
+  hipLaunchKernelGGL((k_pf_up<GATED, IT, LO>), dim3((nmt + 7) / 8 * 8 * nbt), dim3(TPB), 0, s,
                      L.w_act, L.act_ld, L.b_act, xh, xl, L.d, L.n, np, nmt, hh, hl);
+}
+
+template <bool LO>
+void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32x4* xh,
+              u32x4* xl, _Float16* hh, _Float16* hl, float* part, hipStream_t s) {
+  const int d = L.d, n = L.n;
+  const int nct = d / PF_T;
+  const int items = Bp * (d / 8);
+  hipLaunchKernelGGL(k_pf_split<LO>, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)),
+                     dim3(TPB), 0, s, xc, bc, Bp, d, xh, xl);
+  const int nbt = Bp / PF_T;
+  // neuron tile 128 or 192, whichever finishes first with one tile a compute unit at a
+  // time: rounds of tiles x the tile's size (ties: 128)
+  auto cost = [&](int mr) {
+    const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
+    return (tiles + L.n_cus - 1) / L.n_cus * mr;
+  };
+  const int mr = cost(192) < cost(128) ? 192 : 128;
+  const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
+  if (L.gated) {
+    if (mr == 192) pf_up_launch<true, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else pf_up_launch<true, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
+  } else {
+    if (mr == 192) pf_up_launch<false, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
+  }
+  // split the neurons until there are two workgroups a compute unit (the down kernel
+  // keeps one LDS buffer and relies on the second workgroup to cover its loads)
+  int S = 1;
+  while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
+  hipLaunchKernelGGL(k_pf_down<LO>, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
+                     L.b_out, hh, hl, d, n, np, bc, Bp, S, yc, part);
+  if (S > 1) {
+    const size_t tot = (size_t)bc * d;
+    hipLaunchKernelGGL(k_pf_sum, dim3((unsigned)std::min<size_t>((tot + TPB - 1) / TPB, 8 * L.n_cus)),
+                       dim3(TPB), 0, s, part, S, bc, Bp, d, L.b_out, yc);
+  }
 }
 
 }  // namespace
@@ -370,11 +413,10 @@ int prefill_chunk(const LayerDev& L, size_t work_bytes) {
 }
 
 hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void* work,
-                       size_t work_bytes, hipStream_t s) {
+                       size_t work_bytes, bool fp16_act, hipStream_t s) {
   const int chunk = prefill_chunk(L, work_bytes);
   if (chunk < PF_T) return hipErrorInvalidValue;
   const int d = L.d, n = L.n;
-  const int nct = d / PF_T;
   for (int b0 = 0; b0 < B; b0 += chunk) {
     const int bc = std::min(chunk, B - b0);
     const int Bp = (bc + PF_T - 1) / PF_T * PF_T;
@@ -387,36 +429,10 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
     float* part = reinterpret_cast<float*>(take((size_t)PF_SMAX * Bp * d * 4));
     const float* xc = x + (size_t)b0 * d;
     float* yc = y + (size_t)b0 * d;
-    const int items = Bp * (d / 8);
-    hipLaunchKernelGGL(k_pf_split, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)), dim3(TPB),
-                       0, s, xc, bc, Bp, d, xh, xl);
-    const int nbt = Bp / PF_T;
-    // neuron tile 128 or 192, whichever finishes first with one tile a compute unit at a
-    // time: rounds of tiles x the tile's size (ties: 128)
-    auto cost = [&](int mr) {
-      const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
-      return (tiles + L.n_cus - 1) / L.n_cus * mr;
-    };
-    const int mr = cost(192) < cost(128) ? 192 : 128;
-    const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
-    if (L.gated) {
-      if (mr == 192) pf_up_launch<true, 6>(L, xh, xl, np, nbt, hh, hl, s);
-      else pf_up_launch<true, 4>(L, xh, xl, np, nbt, hh, hl, s);
-    } else {
-      if (mr == 192) pf_up_launch<false, 6>(L, xh, xl, np, nbt, hh, hl, s);
-      else pf_up_launch<false, 4>(L, xh, xl, np, nbt, hh, hl, s);
-    }
-    // split the neurons until there are two workgroups a compute unit (the down kernel
-    // keeps one LDS buffer and relies on the second workgroup to cover its loads)
-    int S = 1;
-    while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
-    hipLaunchKernelGGL(k_pf_down, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
-                       L.b_out, hh, hl, d, n, np, bc, Bp, S, yc, part);
-    if (S > 1) {
-      const size_t tot = (size_t)bc * d;
-      hipLaunchKernelGGL(k_pf_sum, dim3((unsigned)std::min<size_t>((tot + TPB - 1) / TPB, 8 * L.n_cus)),
-                         dim3(TPB), 0, s, part, S, bc, Bp, d, L.b_out, yc);
-    }
+    if (fp16_act)
+      pf_chunk<false>(L, xc, bc, Bp, yc, xh, xl, hh, hl, part, s);
+    else
+      pf_chunk<true>(L, xc, bc, Bp, yc, xh, xl, hh, hl, part, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

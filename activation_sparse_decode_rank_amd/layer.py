@@ -261,11 +261,12 @@ class SparseFFN:
             return None
         return torch.empty(nb, dtype=torch.uint8, device=self.w_act.device)
 
-    def prefill(self, x, y=None, work=None, stream=None):
+    def prefill(self, x, y=None, work=None, stream=None, fp16_activations=False):
         """The dense FFN over every neuron for x ([B, d] fp32, any B) on the matrix cores with
-        the weights reused across 128-token tiles (sparse_ffn_prefill); layers it does not
+        the weights reused across 128-token tiles (sparse_ffn_prefill_ex); layers it does not
         cover take sparse_ffn_dense. work: scratch from prefill_work (allocated here when
-        None)."""
+        None). fp16_activations: round x and h to fp16 once and run each product once
+        (SFFN_PREFILL_FP16_ACT) instead of as an fp16 hi + lo pair."""
         if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != self.d:
             raise ValueError("x must be a contiguous fp32 [B, d] device tensor")
         B = x.shape[0]
@@ -276,8 +277,9 @@ class SparseFFN:
         if work is None:
             N.sparse_ffn_dense(self.handle, x.data_ptr(), B, y.data_ptr(), _stream(stream))
             return y
-        N.sparse_ffn_prefill(self.handle, x.data_ptr(), B, y.data_ptr(), work.data_ptr(),
-                             work.numel(), _stream(stream))
+        N.sparse_ffn_prefill_ex(self.handle, x.data_ptr(), B, y.data_ptr(), work.data_ptr(),
+                                work.numel(), N.SFFN_PREFILL_FP16_ACT if fp16_activations else 0,
+                                _stream(stream))
         return y
 
     def lookahead_begin(self, x, stream=None):

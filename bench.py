@@ -1033,6 +1033,8 @@ def run_crossover(torch, args, cap):
     lib_ms = time_fn(lambda: [layers[l].dense(Xp[l], y=yp[l]) for l in range(LP)])
     pf_work = layers[0].prefill_work(P)
     pf_ms = time_fn(lambda: [layers[l].prefill(Xp[l], y=yp[l], work=pf_work) for l in range(LP)])
+    pf16_ms = time_fn(lambda: [layers[l].prefill(Xp[l], y=yp[l], work=pf_work,
+                                                 fp16_activations=True) for l in range(LP)])
     Xh = Xp.half()
 
     def torch_prefill():
@@ -1050,12 +1052,16 @@ def run_crossover(torch, args, cap):
         "prefill_tokens_per_s": round(P / (pf_ms / LP * 1e-3), 1),
         "prefill_tflops": round(pf_flops / (pf_ms / LP * 1e-3) / 1e12, 2),
         "prefill_mfma_frac": round(pf_flops / (pf_ms / LP * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "prefill_fp16_act_ms_per_layer": round(pf16_ms / LP, 4),
+        "prefill_fp16_act_tflops": round(pf_flops / (pf16_ms / LP * 1e-3) / 1e12, 2),
         "dense_route_ms_per_layer": round(lib_ms / LP, 4),
         "torch_ms_per_layer": round(th_ms / LP, 4),
         "torch_fp16_tokens_per_s": round(P / (th_ms / LP * 1e-3), 1),
         "note": "per layer. prefill: sparse_ffn_prefill (128 x 128 tiles on the matrix cores, each "
                 "weight tile read once per 128 tokens; fp32 activations as hi + lo fp16 pairs, so "
-                "the matrix cores run twice the algorithmic products). dense_route: "
+                "the matrix cores run twice the algorithmic products); prefill_fp16_act: the same "
+                "kernels with x and h rounded to fp16 once (SFFN_PREFILL_FP16_ACT), one product "
+                "each, torch's activation precision. dense_route: "
                 "sparse_ffn_dense over the decode kernels, 64 tokens per pass. torch: fp16 "
                 "activations through hipBLASLt"}
     out = {"workload": f"{cfg.name}: {cfg.description}", "rows": rows,
@@ -1065,7 +1071,8 @@ def run_crossover(torch, args, cap):
                    "the expected union exceeds it",
            "prefill_512_tokens": out_pf}
     log(f"prefill 512 tokens: library prefill {pf_ms / LP:.3f} ms/layer "
-        f"({out_pf['prefill_tflops']} TFLOP/s), dense route {lib_ms / LP:.3f}, torch "
+        f"({out_pf['prefill_tflops']} TFLOP/s), fp16 activations {pf16_ms / LP:.3f}, "
+        f"dense route {lib_ms / LP:.3f}, torch "
         f"{th_ms / LP:.3f} ms/layer")
     del layers, originals
     return out

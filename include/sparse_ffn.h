@@ -308,6 +308,17 @@ size_t sparse_ffn_prefill_work_bytes(sparse_ffn_t h, int32_t chunk_tokens);
 int sparse_ffn_prefill(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
                        size_t work_bytes, void* stream);
 
+/* sparse_ffn_prefill with flags (0: exactly sparse_ffn_prefill). SFFN_PREFILL_FP16_ACT
+ * rounds the activations to fp16 once, x before the up products and h before the down
+ * product (round to nearest even; the same |x|, |h| < 65504 limit), and runs each product
+ * once instead of as a hi + lo pair: half the matrix-core work and activation traffic, at
+ * fp16 activation precision (about 11 significant bits per activation; the weights, the
+ * fp32 accumulation and the bitwise reproducibility are unchanged). Same arguments,
+ * scratch and errors as sparse_ffn_prefill; other flag bits give SFFN_ERR_INVALID. */
+#define SFFN_PREFILL_FP16_ACT 1
+int sparse_ffn_prefill_ex(sparse_ffn_t h, const float* x, int32_t B, float* y, void* work,
+                          size_t work_bytes, int32_t flags, void* stream);
+
 /* Input-sparse up projection probe: a measurement, not a step of the decode path. The
  * second ReLU-fication stage puts a ReLU after RMSNorm, so about half of the up
  * projection's input x is zero (novita.ai activation-sparsity article, section 第二階段).

@@ -38,7 +38,7 @@ def test_header_compiles_as_c():
 
 def test_library_exports_every_declared_symbol(N):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     lib = C.CDLL(N.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -148,6 +148,9 @@ def test_calls_reject_null_handle_and_bad_batch(N):
     # prefill: a NULL handle is refused before anything else
     assert L.sparse_ffn_prefill_work_bytes(None, 128) == 0
     assert L.sparse_ffn_prefill(None, 0x10000, 4, 0x10000, 0x10000, 1 << 20, None) == N.SFFN_ERR_INVALID
+    for flags in (0, N.SFFN_PREFILL_FP16_ACT, 2, -1):
+        assert L.sparse_ffn_prefill_ex(None, 0x10000, 4, 0x10000, 0x10000, 1 << 20, flags,
+                                       None) == N.SFFN_ERR_INVALID
     # the input-sparse up probe: every argument check fires before anything is enqueued
     A = 0x10000
     W = L.sparse_ffn_up_probe_work_bytes(1104)

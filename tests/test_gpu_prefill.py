@@ -3,7 +3,11 @@ FFN (oracle.dense): every neuron for many tokens, the pages' dense prefill (Powe
 article, section 4.1.1 NPU-Centric Prefill). Ragged token counts and neuron counts, plain
 and gated, split and bundle layouts, several chunks, the full gated Llama-7B layer at 512
 tokens (sampled tokens against the oracle). y within 1e-3 of max|y| per token (reading of
-the fp32 accumulation bound), bitwise equal from run to run."""
+the fp32 accumulation bound), bitwise equal from run to run.
+
+The fp16-activation form (SFFN_PREFILL_FP16_ACT) rounds x and h to fp16 once: it is checked
+against the oracle's arithmetic with those two roundings applied (the same 1e-3 reading),
+and against the exact FFN within the first-order bound those roundings allow."""
 
 import numpy as np
 import pytest
@@ -27,11 +31,11 @@ def cfg(name):
     return get_config(name)
 
 
-def _prefill(s, X, chunk):
+def _prefill(s, X, chunk, fp16_act=False):
     work = s.prefill_work(chunk)
     assert work is not None
-    y1 = s.prefill(X, work=work)
-    y2 = s.prefill(X, work=work)
+    y1 = s.prefill(X, work=work, fp16_activations=fp16_act)
+    y2 = s.prefill(X, work=work, fp16_activations=fp16_act)
     torch.cuda.synchronize()
     a, b = to_np(y1), to_np(y2)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
@@ -124,3 +128,111 @@ def test_prefill_rejects():
     yf = s32.prefill(torch.zeros((3, 256), dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
     assert yf.shape == (3, 256)
+
+
+U16 = 2.0 ** -11  # unit roundoff of round-to-nearest fp16 (normal range)
+
+
+def _fp16(a):
+    return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
+
+
+def _dense_fp16_act(X, L):
+    """The dense FFN with the two roundings of the fp16-activation prefill applied (x before
+    the up products, h before the down product), fp64 everywhere else. Returns y and the
+    first-order bound on |y - FFN(x)| that those roundings allow (worst-case signs):
+    u (sum_k |W_o[k]| (dh_k + |h_k|)) with dh_k <= u A_k, A_k = |W_a[k]| . |x| (plain), or
+    |W_g[k]| . |x| |v_k| + relu(g_k) |W_u[k]| . |x| (gated, v = W_u x)."""
+    X = np.asarray(X, np.float64)
+    Wa = np.asarray(L["w_a"], np.float64)
+    Wo = np.asarray(L["w_o"], np.float64)
+    Wu = None if L["w_u"] is None else np.asarray(L["w_u"], np.float64)
+    ba = 0.0 if L["b_a"] is None else np.asarray(L["b_a"], np.float64)
+    bo = 0.0 if L["b_o"] is None else np.asarray(L["b_o"], np.float64)
+    Xr = _fp16(X)
+    g = Xr @ Wa.T + ba
+    h = np.maximum(g, 0.0)
+    if Wu is not None:
+        v = Xr @ Wu.T
+        h = h * v
+    y = _fp16(h) @ Wo + bo
+    # the bound, from the exact quantities
+    ax = np.abs(X)
+    ge = X @ Wa.T + ba
+    he = np.maximum(ge, 0.0)
+    A = ax @ np.abs(Wa).T
+    if Wu is not None:
+        ve = X @ Wu.T
+        A = A * np.abs(ve) + he * (ax @ np.abs(Wu).T)
+        he = he * ve
+    bound = U16 * (A + np.abs(he)) @ np.abs(Wo)
+    return y, bound
+
+
+@pytest.mark.parametrize("name,d,n,B,chunk,bundle", [
+    ("C3", 512, 1100, 130, 128, False),   # gated, two chunks, the last of 2 tokens
+    ("C2", 1024, 2000, 300, 256, False),  # plain, two chunks of 256
+    ("C3", 1024, 1408, 257, 512, True),   # gated bundle layout, one chunk
+    ("C2", 512, 9000, 512, 512, False),   # 192-neuron tiles
+    ("C3", 2048, 3000, 384, 384, False),  # split down projection
+])
+def test_prefill_fp16_act(name, d, n, B, chunk, bundle):
+    c = cfg(name)
+    say(f"prefill fp16 activations {name} d={d} n={n} B={B} chunk={chunk} bundle={bundle}")
+    s, L, _ = build(c, 0, d=d, n=n, rank=64, max_batch=4, bundle=bundle)
+    from synth import make_tokens
+    X = make_tokens(c, B, 523, "cuda", d=d)
+    y = _prefill(s, X, chunk, fp16_act=True)
+    sel = sorted(set([0, 1, B // 2, B - 1] + list(range(0, B, max(1, B // 8)))))
+    Xh = to_np(X)[sel]
+    R, bound = _dense_fp16_act(Xh, L)
+    errs = rel_err_rows(y[sel], R)
+    say(f"  err vs rounded reference={max(errs):.2e}")
+    assert max(errs) <= REL_TOL, max(errs)
+    Y = oracle.dense(Xh, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    scale = np.max(np.abs(Y), axis=1, keepdims=True)
+    excess = np.abs(y[sel] - Y) - (2.0 * bound + REL_TOL * scale)
+    say(f"  err vs exact={max(rel_err_rows(y[sel], Y)):.2e}, worst margin={excess.max():.2e}")
+    assert np.all(excess <= 0.0)
+    # the fp32-activation form is closer to the exact FFN than this one's bound
+    y32 = _prefill(s, X, chunk)
+    assert max(rel_err_rows(y32[sel], Y)) <= REL_TOL
+
+
+def test_prefill_fp16_act_full_size_gated():
+    """The full Llama-7B-shaped gated layer at 512 tokens with fp16 activations: sampled
+    tokens against the rounded reference."""
+    c = cfg("C3")
+    say("prefill fp16 activations, full C3 layer, 512 tokens")
+    s, L, _ = build(c, 0, max_batch=4, profile_tokens=256)
+    from synth import make_tokens
+    X = make_tokens(c, 512, 524, "cuda")
+    y = _prefill(s, X, 512, fp16_act=True)
+    sel = [0, 100, 255, 511]
+    R, _ = _dense_fp16_act(to_np(X)[sel], L)
+    errs = rel_err_rows(y[sel], R)
+    say(f"  err={max(errs):.2e}")
+    assert max(errs) <= REL_TOL, max(errs)
+
+
+def test_prefill_ex_flags():
+    """Unknown flag bits are refused; flags 0 is sparse_ffn_prefill itself, bit for bit."""
+    from activation_sparse_decode_rank_amd import _native as N
+    say("prefill_ex flags")
+    s, _, _ = build(cfg("C2"), 0, d=512, n=1000, rank=64)
+    need = N.sparse_ffn_prefill_work_bytes(s.handle, 128)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda")
+    from synth import make_tokens
+    X = make_tokens(cfg("C2"), 5, 525, "cuda", d=512)
+    y0 = torch.empty_like(X)
+    y1 = torch.empty_like(X)
+    L = N.lib()
+    for bad in (2, 4, -1, 1 << 30):
+        assert L.sparse_ffn_prefill_ex(s.handle, X.data_ptr(), 5, y0.data_ptr(), work.data_ptr(),
+                                       need, bad, None) == N.SFFN_ERR_INVALID
+    assert L.sparse_ffn_prefill_ex(s.handle, X.data_ptr(), 5, y0.data_ptr(), work.data_ptr(),
+                                   need, 0, None) == N.SFFN_OK
+    assert L.sparse_ffn_prefill(s.handle, X.data_ptr(), 5, y1.data_ptr(), work.data_ptr(),
+                                need, None) == N.SFFN_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(y0).view(np.uint32), to_np(y1).view(np.uint32))
