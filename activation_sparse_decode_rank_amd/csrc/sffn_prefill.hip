@@ -14,32 +14,28 @@
 // are zero):
 //  - k_pf_split: x [B][d] fp32 -> xh, xl [Bp][d] fp16;
 //  - k_pf_up:    h = relu(W_act x + b_act) (gated: times W_up x) for every neuron and token,
-//                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to 128; neurons past
-//                d_ffn are 0);
+//                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to the neuron tile, 96, 128
+//                or 192; neurons past d_ffn are 0);
 //  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S = 1, 2 or 4) when the
 //                output tiles alone do not fill the GPU; the S partial sums go to scratch
 //                and k_pf_sum adds them in split order (y bitwise reproducible).
+// Both products stream their operands from memory straight into LDS through a pipeline of
+// several stages; the down kernel reads W_down's rows there with the LDS transpose read.
 #include "sffn_device.h"
 
 namespace sffn {
 namespace {
 
 constexpr int PF_T = 128;  // tile edge: rows (neurons or columns) and tokens per workgroup
-constexpr int PF_K = 64;   // K step: 64 fp16 = one 128-byte line of a row
-constexpr int PF_P = 72;   // LDS row pitch in halfs (64 + 8): rows start 16 bytes apart in the banks
 constexpr int PF_SMAX = 4;
+// s_waitcnt operand (gfx9 encoding) that waits for LDS reads only: lgkmcnt 0, vmcnt and
+// expcnt at their maximum
+constexpr int WAIT_LGKM0 = 0xC07F;
 
 size_t pf_align(size_t v) { return (v + 255) & ~(size_t)255; }
 
 __device__ __forceinline__ float4_t pf_mfma(const half8_t& a, const half8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void lds_put(_Float16* base, int row, int col8, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(base + row * PF_P + col8 * 8) = v;
-}
-__device__ __forceinline__ half8_t lds_get(const _Float16* base, int row, int k) {
-  return *reinterpret_cast<const half8_t*>(base + row * PF_P + k);
 }
 
 // x [B][d] fp32 -> hi, lo [Bp][d] fp16 (LO: lo as well), rows B .. Bp-1 zero
@@ -64,17 +60,19 @@ __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, i
 }
 
 // Up projection: workgroup (mt, bt) computes neurons [MR mt, +MR) x tokens [128 bt, +128)
-// (MR = 32 IT: 128 or 192) over all d inputs, in stages of 32 inputs. Wave w takes neurons
-// 16 IT (w & 1) .. +16 IT and tokens 64 (w >> 1) .. +64 (IT x 4 tiles of 16 x 16, for the
-// gate and, gated, the up matrix). The operands reach LDS without passing through
+// (MR = 32 IT: 96, 128 or 192) over all d inputs, in stages of 32 inputs. Wave w takes
+// neurons 16 IT (w & 1) .. +16 IT and tokens 64 (w >> 1) .. +64 (IT x 4 tiles of 16 x 16,
+// for the gate and, gated, the up matrix). The operands reach LDS without passing through
 // registers (global_load_lds_dwordx4: each lane's 16 bytes land at the next 16 bytes of a
-// 1 KB block), NS stages deep, so NS - 1 stages of loads are in flight while the matrix
-// cores take one. A stage holds, per operand (each weight matrix, the tokens' hi and lo
-// halves), its rows x 64 bytes; within each 16-row group, row r's 16-byte chunk c sits at
-// position (c + r / 4) mod 4 of the row, so that a fragment read (16 rows, one chunk each)
-// touches every LDS bank once. Neuron tiles mt of the same bt are 8 apart in the grid when
-// the neuron tile count is padded to a multiple of 8, so the workgroups sharing a weight
-// tile run on one XCD.
+// 1 KB block), NS stages deep. A stage holds, per operand (each weight matrix, the tokens'
+// hi and lo halves), its rows x 64 bytes; within each 16-row group, row r's 16-byte chunk c
+// sits at position (c + r / 4) mod 4 of the row, so that a fragment read (16 rows, one
+// chunk each) touches every LDS bank once. Each step waits for the next stage, refills the
+// buffer just read with the stage NS ahead, and reads the next stage's fragments into
+// registers while the matrix cores take the current ones; two fragment sets alternate, so
+// the loop runs two steps a turn. Neuron tiles mt of the same bt are 8 apart in the grid
+// when the neuron tile count is padded to a multiple of 8, so the workgroups sharing a
+// weight tile run on one XCD.
 constexpr int PFD_K = 32;  // inputs per stage
 template <bool GATED, int IT, bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, int ld_act,
@@ -108,9 +106,9 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   // the lane's row in a 16-row group and the global chunk its LDS position holds
   const int lr = lane >> 2;
   const int lc = ((lane & 3) - (lr >> 2)) & 3;
-  auto issue = [&](int st) {
+  auto issue = [&](int st, int buf) {
     const int kc = st * (PFD_K / 8) + lc;
-    _Float16* base = sbuf + (st % NS) * STAGE;
+    _Float16* base = sbuf + buf * STAGE;
 #pragma unroll
     for (int v = 0; v < DPS; ++v) {
       const int u = wave + (TPB / 64) * v;  // 16-row group of some operand, wave-uniform
@@ -142,42 +140,58 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[m][i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st);
-  for (int st = 0; st < nk; ++st) {
-    // this stage's loads have landed (up to NS - 2 later stages may stay in flight), in
-    // every wave
-    const int later = min(NS - 2, nk - 1 - st);
-    if (later >= 2) {
-      if (NS - 2 >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPS) : "memory");
-    } else if (later == 1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // a bare barrier: __syncthreads() would also wait for the stages still in flight
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NS - 1 < nk) issue(st + NS - 1);  // into the buffer every wave has finished with
+  struct Frags {
+    half8_t b[NB][4];
+    half8_t a[NM][IT];
+  };
+  auto read_frags = [&](Frags& F, int st) {
     const _Float16* base = sbuf + (st % NS) * STAGE;
-    half8_t bx[NB][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      bx[0][t] = frag(base, NM * BLK_A, wn * 64 + t * 16);
-      if constexpr (LO) bx[NB - 1][t] = frag(base, NM * BLK_A + BLK_B, wn * 64 + t * 16);
+      F.b[0][t] = frag(base, NM * BLK_A, wn * 64 + t * 16);
+      if constexpr (LO) F.b[NB - 1][t] = frag(base, NM * BLK_A + BLK_B, wn * 64 + t * 16);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        const half8_t aw = frag(base, m * BLK_A, wm * 16 * IT + i * 16);
+      for (int i = 0; i < IT; ++i) F.a[m][i] = frag(base, m * BLK_A, wm * 16 * IT + i * 16);
+  };
+  auto mfmas = [&](const Frags& F) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < IT; ++i)
 #pragma unroll
         for (int h = 0; h < NB; ++h)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(aw, bx[h][t], acc[m][i][t]);
-      }
+          for (int t = 0; t < 4; ++t) acc[m][i][t] = pf_mfma(F.a[m][i], F.b[h][t], acc[m][i][t]);
+  };
+  // Stage st's fragments are in Fc. Wait for stage st + 1, refill stage st's buffer (every
+  // wave has read it) with stage st + NS, read stage st + 1's fragments into Fn, then run Fc
+  // on the matrix cores. Past the last stage the refill loads the last stage again (in
+  // bounds, never read), so every step has the same loads in flight and no branch.
+  auto step = [&](int st, Frags& Fc, Frags& Fn) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * DPS) : "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // this wave's reads of stage st are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(st + NS, nk - 1), st % NS);
+    read_frags(Fn, st + 1);
+    mfmas(Fc);
+  };
+  static_assert(NS >= 2 && NS <= 4 && (NS - 1) * DPS <= 63, "vmcnt range");
+#pragma unroll
+  for (int st = 0; st < NS; ++st) issue(min(st, nk - 1), st);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * DPS) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  Frags F0, F1;
+  read_frags(F0, 0);
+  for (int st = 0; st < nk; st += 2) {  // nk = d / 32 is even
+    step(st, F0, F1);
+    step(st + 1, F1, F0);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the loop
   // epilogue: lane holds token 16t + r16 and neurons 16i + 4g .. +3 of the wave's block
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
@@ -205,60 +219,89 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   }
 }
 
-// Down projection: workgroup (ct, bt, s) computes columns [128 ct, +128) x tokens
-// [128 bt, +128) over neurons [s np / S, (s + 1) np / S) (whole K steps of 64). Wave w takes
-// tokens 64 (w & 1) .. +64 and columns 64 (w >> 1) .. +64. W_down^T rows are stored
-// transposed in LDS (column-major: [column][neuron]), so the right operand's 8 consecutive
-// neurons of one column are one 16-byte read: thread t loads the 16-byte pieces (8 columns)
-// cs = t / 32 and cs + 8 of neurons 2p and 2p + 1 (p = t % 32) and stores each column's
-// pair of neurons as one 32-bit word (the 32 lanes of a half wave write 32 consecutive
-// words). One LDS buffer; two workgroups fit a compute unit. S == 1 writes y (+ b_out) for
-// the chunk's real tokens; otherwise the split's sums go to part[s][Bp][d].
+// Down projection on the direct-to-LDS pipeline: workgroup (ct, bt, s) computes columns
+// [128 ct, +128) x tokens [128 bt, +128) over stages of 32 neurons of its split. Both
+// operands go straight from memory to LDS. H rows (tokens, 64 bytes a stage) are swizzled
+// as in the up kernel. W_down^T rows (32 neurons x 256 bytes a stage) keep their row-major
+// layout with row k's 16-byte chunk c at position c ^ wsw(k); the matrix cores' operand
+// (8 consecutive neurons of one column) is read with two LDS transpose reads
+// (ds_read_b64_tr_b16): in each 16-lane group, lane i names row k0 + i / 4 at column
+// n0 + 4 (i % 4), and lane j receives column n0 + j of rows k0 .. k0 + 3. Wave w takes
+// tokens 64 (w & 1) .. +64 and columns 64 (w >> 1) .. +64; two workgroups share a compute
+// unit.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int pf_wsw(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 template <bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down_t, int ld_down,
-                                                 const float* __restrict__ b_out,
-                                                 const _Float16* __restrict__ hh,
-                                                 const _Float16* __restrict__ hl, int d, int n,
-                                                 int np, int B, int Bp, int S,
-                                                 float* __restrict__ y, float* __restrict__ part) {
-  constexpr int NB = LO ? 2 : 1;  // activation halves (hi, lo)
-  __shared__ __attribute__((aligned(16))) _Float16 sH[NB][PF_T * PF_P];
-  __shared__ __attribute__((aligned(16))) _Float16 sW[PF_T * PF_P];
+                                               const float* __restrict__ b_out,
+                                               const u32x4* __restrict__ hh,
+                                               const u32x4* __restrict__ hl, int d, int n,
+                                               int np, int B, int Bp, int S,
+                                               float* __restrict__ y, float* __restrict__ part) {
+  constexpr int NB = LO ? 2 : 1;           // activation halves (hi, lo)
+  constexpr int KS = 32;                   // neurons a stage
+  constexpr int BLK_W = KS * PF_T;         // halfs: 32 neurons x 128 columns
+  constexpr int BLK_H = PF_T * KS;         // halfs: 128 tokens x 32 neurons
+  constexpr int STAGE = BLK_W + NB * BLK_H;
+  constexpr int NS = LO ? 3 : 4;           // 72 or 64 KB
+  constexpr int NGW = BLK_W / 512, NGH = BLK_H / 512;  // 1 KB loads per block
+  constexpr int NG = NGW + NB * NGH;
+  constexpr int DPS = NG / (TPB / 64);
+  static_assert(NG % (TPB / 64) == 0, "whole loads per wave");
+  __shared__ __attribute__((aligned(16))) _Float16 sbuf[NS * STAGE];
   const int nct = d / PF_T, nbt = Bp / PF_T;
   const int ct = blockIdx.x % nct, bt = (blockIdx.x / nct) % nbt, s = blockIdx.x / (nct * nbt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, g = lane >> 4;
   const int c0 = ct * PF_T, b0 = bt * PF_T;
-  const int ksteps = np / PF_K;
-  const int kb = (int)((long long)ksteps * s / S), ke = (int)((long long)ksteps * (s + 1) / S);
+  const int nks = np / KS;
+  const int kb = (int)((long long)nks * s / S), ke = (int)((long long)nks * (s + 1) / S);
+  const int nk = ke - kb;
   const u32x4* w = static_cast<const u32x4*>(w_down_t);
-  uint32_t* sW32 = reinterpret_cast<uint32_t*>(sW);
+  const int hch = np / 8;  // 16-byte chunks of an H row
 
-  // H slots: q = tid + 256 j -> token q / 8, piece q % 8
-  int hrow[4], hseg[4];
+  const int lr = lane >> 2;                    // H: row within a 16-row group
+  const int lc = ((lane & 3) - (lr >> 2)) & 3;  // H: global chunk this lane's position holds
+  auto issue = [&](int st) {
+    _Float16* base = sbuf + (st % NS) * STAGE;
+    const int k0 = (kb + st) * KS;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = tid + TPB * j;
-    hrow[j] = q >> 3;
-    hseg[j] = q & 7;
-  }
-  const int wp = tid & 31, wcs = tid >> 5;  // neuron pair, 8-column piece (and + 8)
-  u32x4 rh[NB][4], rw[2][2];                // rw[piece][neuron of the pair]
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const size_t o = (size_t)(b0 + hrow[j]) * np + k0 + hseg[j] * 8;
-      rh[0][j] = *reinterpret_cast<const u32x4*>(hh + o);
-      if constexpr (LO) rh[NB - 1][j] = *reinterpret_cast<const u32x4*>(hl + o);
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = min(k0 + 2 * wp + e, n - 1);  // neurons past d_ffn meet h = 0
-        rw[c][e] = ld_stream(w, (size_t)i * ld_down + c0 / 8 + wcs + 8 * c);
+    for (int v = 0; v < DPS; ++v) {
+      const int u = wave + (TPB / 64) * v;  // wave-uniform
+      const u32x4* src;
+      int off;
+      if (u < NGW) {
+        const int kr = 4 * u + (lane >> 4);
+        const int c = (lane & 15) ^ pf_wsw(kr);
+        src = w + (size_t)min(k0 + kr, n - 1) * ld_down + c0 / 8 + c;  // neurons past d_ffn meet h = 0
+        off = u * 512;
+      } else {
+        const int o = (u - NGW) / NGH, q = (u - NGW) % NGH;
+        src = (o == 0 ? hh : hl) + (size_t)(b0 + q * 16 + lr) * hch + (kb + st) * (KS / 8) + lc;
+        off = BLK_W + o * BLK_H + q * 16 * KS;
       }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + off),
+                                       16, 0, 0);
+    }
+  };
+  auto hfrag = [&](const _Float16* base, int o, int R) {
+    return *reinterpret_cast<const half8_t*>(base + BLK_W + o * BLK_H + R * KS +
+                                             (r16 * 4 + ((g + (r16 >> 2)) & 3)) * 8);
+  };
+  // W operand for columns n0 .. n0 + 15: neurons 8g .. 8g + 7 of column n0 + r16
+  auto wfrag = [&](const _Float16* base, int n0) {
+    const int col = n0 + 4 * (r16 & 3);
+    const int ka = 8 * g + (r16 >> 2), kc = ka + 4;
+    const _Float16* pa = base + ka * PF_T + (((col >> 3) ^ pf_wsw(ka)) << 3) + (col & 7);
+    const _Float16* pc = base + kc * PF_T + (((col >> 3) ^ pf_wsw(kc)) << 3) + (col & 7);
+    const short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(pa));
+    const short4_t c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(pc));
+    const half4_t ha = __builtin_bit_cast(half4_t, a), hc = __builtin_bit_cast(half4_t, c);
+    return __builtin_shufflevector(ha, hc, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   float4_t acc[4][4];
 #pragma unroll
@@ -266,46 +309,36 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (kb < ke) fetch(kb * PF_K);
-  for (int kk = kb; kk < ke; ++kk) {
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lds_put(sH[0], hrow[j], hseg[j], rh[0][j]);
-      if constexpr (LO) lds_put(sH[NB - 1], hrow[j], hseg[j], rh[NB - 1][j]);
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st);
+  for (int st = 0; st < nk; ++st) {
+    const int later = min(NS - 2, nk - 1 - st);
+    if (later >= 2) {
+      if constexpr (NS - 2 >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPS) : "memory");
+    } else if (later == 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nk) issue(st + NS - 1);  // into the buffer every wave has finished with
+    const _Float16* base = sbuf + (st % NS) * STAGE;
+    half8_t bw[4], ah[NB][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bw[t] = wfrag(base, wn * 64 + t * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[0][i] = hfrag(base, 0, wm * 64 + i * 16);
+      if constexpr (LO) ah[NB - 1][i] = hfrag(base, 1, wm * 64 + i * 16);
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const half8_t v0 = __builtin_bit_cast(half8_t, rw[c][0]);
-      const half8_t v1 = __builtin_bit_cast(half8_t, rw[c][1]);
+    for (int h = 0; h < NB; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = (wcs + 8 * c) * 8 + e;
-        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-        const half2_t pr = {v0[e], v1[e]};
-        sW32[col * (PF_P / 2) + wp] = __builtin_bit_cast(uint32_t, pr);
-      }
-    }
-    __syncthreads();
-    if (kk + 1 < ke) fetch((kk + 1) * PF_K);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int ks = 0; ks < PF_K; ks += 32) {
-      const int k = ks + 8 * g;
-      half8_t bw[4], ah[NB][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bw[t] = lds_get(sW, wn * 64 + t * 16 + r16, k);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ah[0][i] = lds_get(sH[0], wm * 64 + i * 16 + r16, k);
-        if constexpr (LO) ah[NB - 1][i] = lds_get(sH[NB - 1], wm * 64 + i * 16 + r16, k);
-      }
-#pragma unroll
-      for (int h = 0; h < NB; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][t] = pf_mfma(ah[h][i], bw[t], acc[i][t]);
-    }
+        for (int t = 0; t < 4; ++t) acc[i][t] = pf_mfma(ah[h][i], bw[t], acc[i][t]);
   }
   // lane holds column 16t + r16 and tokens 16i + 4g .. +3 of the wave's block
 #pragma unroll
@@ -358,27 +391,31 @@ void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32
   hipLaunchKernelGGL(k_pf_split<LO>, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)),
                      dim3(TPB), 0, s, xc, bc, Bp, d, xh, xl);
   const int nbt = Bp / PF_T;
-  // neuron tile 128 or 192, whichever finishes first with one tile a compute unit at a
-  // time: rounds of tiles x the tile's size (ties: 128)
+  // Neuron tile. The gated one-product form takes 96 neurons: its 20 KB stages let two
+  // workgroups share a compute unit, one computing while the other waits at its barrier.
+  // Otherwise 128 or 192, whichever finishes first with one tile a compute unit at a time:
+  // rounds of tiles x the tile's size (ties: 128).
   auto cost = [&](int mr) {
     const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
     return (tiles + L.n_cus - 1) / L.n_cus * mr;
   };
-  const int mr = cost(192) < cost(128) ? 192 : 128;
+  const int mr = (L.gated && !LO) ? 96 : (cost(192) < cost(128) ? 192 : 128);
   const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
   if (L.gated) {
-    if (mr == 192) pf_up_launch<true, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    if (mr == 96) pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else if (mr == 192) pf_up_launch<true, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
     else pf_up_launch<true, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
   } else {
     if (mr == 192) pf_up_launch<false, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
     else pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
   }
-  // split the neurons until there are two workgroups a compute unit (the down kernel
-  // keeps one LDS buffer and relies on the second workgroup to cover its loads)
+  // split the neurons until there are two workgroups a compute unit (64 or 72 KB of LDS
+  // each), keeping at least 8 stages of 32 neurons a split
   int S = 1;
-  while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / PF_K >= 2 * S * 2) S *= 2;
+  while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / 32 >= 8 * 2 * S) S *= 2;
   hipLaunchKernelGGL(k_pf_down<LO>, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
-                     L.b_out, hh, hl, d, n, np, bc, Bp, S, yc, part);
+                     L.b_out, reinterpret_cast<const u32x4*>(hh), reinterpret_cast<const u32x4*>(hl),
+                     d, n, np, bc, Bp, S, yc, part);
   if (S > 1) {
     const size_t tot = (size_t)bc * d;
     hipLaunchKernelGGL(k_pf_sum, dim3((unsigned)std::min<size_t>((tot + TPB - 1) / TPB, 8 * L.n_cus)),
