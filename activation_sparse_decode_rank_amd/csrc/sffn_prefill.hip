@@ -87,7 +87,10 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   constexpr int BLK_A = MR * PFD_K, BLK_B = PF_T * PFD_K;  // halfs per operand block
   constexpr int NB = LO ? 2 : 1;                           // token blocks (hi, lo)
   constexpr int STAGE = NM * BLK_A + NB * BLK_B;           // halfs per stage
-  constexpr int NS = STAGE * 2 * 4 <= 128 * 1024 ? 4 : 3;  // stages held in LDS
+  // stages held in LDS: 96-neuron tiles keep two workgroups a compute unit (80 KB each),
+  // the larger tiles one (up to 128 KB)
+  constexpr int NS = IT == 3 ? ((80 * 1024) / (STAGE * 2) < 4 ? (80 * 1024) / (STAGE * 2) : 4)
+                             : (STAGE * 2 * 4 <= 128 * 1024 ? 4 : 3);
   constexpr int NG = NM * GA + NB * GB;                    // 1 KB loads a stage
   constexpr int DPS = NG / (TPB / 64);                     // load instructions per wave a stage
   static_assert(NG % (TPB / 64) == 0, "whole loads per wave");
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
 // (ds_read_b64_tr_b16): in each 16-lane group, lane i names row k0 + i / 4 at column
 // n0 + 4 (i % 4), and lane j receives column n0 + j of rows k0 .. k0 + 3. Wave w takes
 // tokens 64 (w & 1) .. +64 and columns 64 (w >> 1) .. +64; two workgroups share a compute
-// unit.
+// unit. The loop steps as the up kernel's (the next stage's fragments are read while the
+// matrix cores take the current ones); a split with an odd stage count ends on one step.
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int pf_wsw(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
@@ -264,8 +268,8 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
 
   const int lr = lane >> 2;                    // H: row within a 16-row group
   const int lc = ((lane & 3) - (lr >> 2)) & 3;  // H: global chunk this lane's position holds
-  auto issue = [&](int st) {
-    _Float16* base = sbuf + (st % NS) * STAGE;
+  auto issue = [&](int st, int buf) {
+    _Float16* base = sbuf + buf * STAGE;
     const int k0 = (kb + st) * KS;
 #pragma unroll
     for (int v = 0; v < DPS; ++v) {
@@ -309,36 +313,52 @@ __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st);
-  for (int st = 0; st < nk; ++st) {
-    const int later = min(NS - 2, nk - 1 - st);
-    if (later >= 2) {
-      if constexpr (NS - 2 >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPS) : "memory");
-    } else if (later == 1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NS - 1 < nk) issue(st + NS - 1);  // into the buffer every wave has finished with
+  struct Frags {
+    half8_t b[4];
+    half8_t a[NB][4];
+  };
+  auto read_frags = [&](Frags& F, int st) {
     const _Float16* base = sbuf + (st % NS) * STAGE;
-    half8_t bw[4], ah[NB][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bw[t] = wfrag(base, wn * 64 + t * 16);
+    for (int t = 0; t < 4; ++t) F.b[t] = wfrag(base, wn * 64 + t * 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ah[0][i] = hfrag(base, 0, wm * 64 + i * 16);
-      if constexpr (LO) ah[NB - 1][i] = hfrag(base, 1, wm * 64 + i * 16);
+      F.a[0][i] = hfrag(base, 0, wm * 64 + i * 16);
+      if constexpr (LO) F.a[NB - 1][i] = hfrag(base, 1, wm * 64 + i * 16);
     }
+  };
+  auto mfmas = [&](const Frags& F) {
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = pf_mfma(ah[h][i], bw[t], acc[i][t]);
+        for (int t = 0; t < 4; ++t) acc[i][t] = pf_mfma(F.a[h][i], F.b[t], acc[i][t]);
+  };
+  auto step = [&](int st, Frags& Fc, Frags& Fn) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * DPS) : "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);  // this wave's reads of stage st are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(st + NS, nk - 1), st % NS);
+    read_frags(Fn, st + 1);
+    mfmas(Fc);
+  };
+  if (nk > 0) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(min(st, nk - 1), st);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * DPS) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Frags F0, F1;
+    read_frags(F0, 0);
+    int st = 0;
+    for (; st + 1 < nk; st += 2) {
+      step(st, F0, F1);
+      step(st + 1, F1, F0);
+    }
+    if (st < nk) step(st, F0, F1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the loop
   }
   // lane holds column 16t + r16 and tokens 16i + 4g .. +3 of the wave's block
 #pragma unroll
@@ -391,20 +411,18 @@ void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32
   hipLaunchKernelGGL(k_pf_split<LO>, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)),
                      dim3(TPB), 0, s, xc, bc, Bp, d, xh, xl);
   const int nbt = Bp / PF_T;
-  // Neuron tile. The gated one-product form takes 96 neurons: its 20 KB stages let two
-  // workgroups share a compute unit, one computing while the other waits at its barrier.
-  // Otherwise 128 or 192, whichever finishes first with one tile a compute unit at a time:
-  // rounds of tiles x the tile's size (ties: 128).
+  // Neuron tile. The gated forms take 96 neurons, whose stages (20 KB, or 28 KB with the lo
+  // halves) let two workgroups share a compute unit, one computing while the other waits
+  // at its barrier. The plain form takes 128 or 192, whichever finishes first with one
+  // tile a compute unit at a time: rounds of tiles x the tile's size (ties: 128).
   auto cost = [&](int mr) {
     const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
     return (tiles + L.n_cus - 1) / L.n_cus * mr;
   };
-  const int mr = (L.gated && !LO) ? 96 : (cost(192) < cost(128) ? 192 : 128);
+  const int mr = L.gated ? 96 : (cost(192) < cost(128) ? 192 : 128);
   const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
   if (L.gated) {
-    if (mr == 96) pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
-    else if (mr == 192) pf_up_launch<true, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
-    else pf_up_launch<true, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
   } else {
     if (mr == 192) pf_up_launch<false, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
     else pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
