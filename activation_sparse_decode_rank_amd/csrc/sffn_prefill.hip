@@ -14,10 +14,10 @@
 // are zero):
 //  - k_pf_split: x [B][d] fp32 -> xh, xl [Bp][d] fp16;
 //  - k_pf_up:    h = relu(W_act x + b_act) (gated: times W_up x) for every neuron and token,
-//                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to the neuron tile, 96, 128
-//                or 192; neurons past d_ffn are 0);
-//  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S = 1, 2 or 4) when the
-//                output tiles alone do not fill the GPU; the S partial sums go to scratch
+//                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to the neuron tile, 64 to
+//                192; neurons past d_ffn are 0);
+//  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S a power of 2 up to 16)
+//                when the output tiles alone do not fill the GPU; the S partial sums go to scratch
 //                and k_pf_sum adds them in split order (y bitwise reproducible).
 // Both products stream their operands from memory straight into LDS through a pipeline of
 // several stages; the down kernel reads W_down's rows there with the LDS transpose read.
@@ -27,7 +27,7 @@ namespace sffn {
 namespace {
 
 constexpr int PF_T = 128;  // tile edge: rows (neurons or columns) and tokens per workgroup
-constexpr int PF_SMAX = 4;
+constexpr int PF_SMAX = 16;  // most neuron splits of the down projection
 // s_waitcnt operand (gfx9 encoding) that waits for LDS reads only: lgkmcnt 0, vmcnt and
 // expcnt at their maximum
 constexpr int WAIT_LGKM0 = 0xC07F;
@@ -87,9 +87,9 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
   constexpr int BLK_A = MR * PFD_K, BLK_B = PF_T * PFD_K;  // halfs per operand block
   constexpr int NB = LO ? 2 : 1;                           // token blocks (hi, lo)
   constexpr int STAGE = NM * BLK_A + NB * BLK_B;           // halfs per stage
-  // stages held in LDS: 96-neuron tiles keep two workgroups a compute unit (80 KB each),
-  // the larger tiles one (up to 128 KB)
-  constexpr int NS = IT == 3 ? ((80 * 1024) / (STAGE * 2) < 4 ? (80 * 1024) / (STAGE * 2) : 4)
+  // stages held in LDS: tiles of up to 96 neurons keep two workgroups a compute unit (80 KB
+  // each), the larger tiles one (up to 128 KB)
+  constexpr int NS = IT <= 3 ? ((80 * 1024) / (STAGE * 2) < 4 ? (80 * 1024) / (STAGE * 2) : 4)
                              : (STAGE * 2 * 4 <= 128 * 1024 ? 4 : 3);
   constexpr int NG = NM * GA + NB * GB;                    // 1 KB loads a stage
   constexpr int DPS = NG / (TPB / 64);                     // load instructions per wave a stage
@@ -391,8 +391,31 @@ __global__ __launch_bounds__(TPB) void k_pf_sum(const float* __restrict__ part, 
   }
 }
 
-// H row length for the scratch: d_ffn rounded up to both neuron tiles (128 and 192)
+// H row length for the scratch: d_ffn rounded up to every neuron tile (64 to 192)
 size_t pf_np(int n) { return (size_t)(n + 383) / 384 * 384; }
+
+// Neuron splits of the down projection for nbt token tiles and H rows of np: doubled until
+// two workgroups a compute unit (64 or 72 KB of LDS each), keeping at least 8 stages of 32
+// neurons a split.
+int pf_splits(const LayerDev& L, int nbt, size_t np) {
+  const long long tiles = (long long)(L.d / PF_T) * nbt;
+  int S = 1;
+  while (S < PF_SMAX && tiles * S < 2LL * L.n_cus && np / 32 >= (size_t)16 * S) S *= 2;
+  return S;
+}
+
+// partial-sum scratch for chunks of up to Bp tokens: the largest splits x tokens of any
+// chunk size up to Bp (the splits never grow with the tokens, so the scan ends at the
+// first size that needs none)
+size_t pf_part_bytes(const LayerDev& L, size_t Bp) {
+  size_t m = 0;
+  for (size_t t = PF_T; t <= Bp; t += PF_T) {
+    const int S = pf_splits(L, (int)(t / PF_T), pf_np(L.n));
+    if (S == 1) break;
+    m = std::max(m, (size_t)S * t * L.d * 4);
+  }
+  return m;
+}
 
 template <bool GATED, int IT, bool LO>
 void pf_up_launch(const LayerDev& L, const u32x4* xh, const u32x4* xl, int np, int nbt,
@@ -411,26 +434,35 @@ void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32
   hipLaunchKernelGGL(k_pf_split<LO>, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)),
                      dim3(TPB), 0, s, xc, bc, Bp, d, xh, xl);
   const int nbt = Bp / PF_T;
-  // Neuron tile. The gated forms take 96 neurons, whose stages (20 KB, or 28 KB with the lo
-  // halves) let two workgroups share a compute unit, one computing while the other waits
-  // at its barrier. The plain form takes 128 or 192, whichever finishes first with one
-  // tile a compute unit at a time: rounds of tiles x the tile's size (ties: 128).
+  // Neuron tile (32 it neurons). The gated forms take 96 neurons, whose stages (20 KB, or
+  // 28 KB with the lo halves) let two workgroups share a compute unit, one computing while
+  // the other waits at its barrier. The plain form takes 128 or 192, whichever finishes
+  // first with one tile a compute unit at a time: rounds of tiles x the tile's size (ties:
+  // 128). With few token tiles a 64-neuron tile can finish first: it stages fewer weight
+  // rows per token block but loads the token block for twice as many tiles. Measured time
+  // follows rounds over the compute units x bytes a workgroup stages, so that decides.
   auto cost = [&](int mr) {
     const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
     return (tiles + L.n_cus - 1) / L.n_cus * mr;
   };
-  const int mr = L.gated ? 96 : (cost(192) < cost(128) ? 192 : 128);
+  auto staged = [&](int it) {
+    const long long tiles = (long long)((n + 32 * it - 1) / (32 * it)) * nbt;
+    const long long per_stage = (L.gated ? 2 : 1) * 32 * it + (LO ? 2 : 1) * PF_T;  // rows
+    return (tiles + L.n_cus - 1) / L.n_cus * per_stage;
+  };
+  int it = L.gated ? 3 : (cost(192) < cost(128) ? 6 : 4);
+  if (staged(2) < staged(it)) it = 2;
+  const int mr = 32 * it;
   const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
   if (L.gated) {
-    pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    if (it == 3) pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else pf_up_launch<true, 2, LO>(L, xh, xl, np, nbt, hh, hl, s);
   } else {
-    if (mr == 192) pf_up_launch<false, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
-    else pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    if (it == 6) pf_up_launch<false, 6, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else if (it == 4) pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
+    else pf_up_launch<false, 2, LO>(L, xh, xl, np, nbt, hh, hl, s);
   }
-  // split the neurons until there are two workgroups a compute unit (64 or 72 KB of LDS
-  // each), keeping at least 8 stages of 32 neurons a split
-  int S = 1;
-  while (S < PF_SMAX && nct * nbt * S < 2 * L.n_cus && np / 32 >= 8 * 2 * S) S *= 2;
+  const int S = pf_splits(L, nbt, np);
   hipLaunchKernelGGL(k_pf_down<LO>, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
                      L.b_out, reinterpret_cast<const u32x4*>(hh), reinterpret_cast<const u32x4*>(hl),
                      d, n, np, bc, Bp, S, yc, part);
@@ -453,7 +485,7 @@ size_t prefill_work_bytes(const LayerDev& L, int chunk) {
   size_t b = 0;
   b += 2 * pf_align(Bp * L.d * 2);           // xh, xl
   b += 2 * pf_align(Bp * np * 2);            // hh, hl
-  b += pf_align((size_t)PF_SMAX * Bp * L.d * 4);  // split partial sums
+  b += pf_align(pf_part_bytes(L, Bp));       // split partial sums
   return b;
 }
 
@@ -481,7 +513,7 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
     u32x4* xl = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
     _Float16* hh = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));  // rows np <= pf_np(n)
     _Float16* hl = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));
-    float* part = reinterpret_cast<float*>(take((size_t)PF_SMAX * Bp * d * 4));
+    float* part = reinterpret_cast<float*>(take(pf_part_bytes(L, Bp)));
     const float* xc = x + (size_t)b0 * d;
     float* yc = y + (size_t)b0 * d;
     if (fp16_act)

@@ -49,6 +49,7 @@ def _prefill(s, X, chunk, fp16_act=False):
     ("C3", 1024, 1408, 257, 512, True),   # gated bundle layout, one chunk
     ("C2", 256, 700, 64, 128, True),      # plain bundle
     ("C3", 2048, 3000, 384, 384, False),  # split down projection (few output tiles)
+    ("C2", 512, 8192, 512, 512, False),   # plain, 128-neuron tiles (64 elsewhere at these sizes)
 ])
 def test_prefill_matches_oracle(name, d, n, B, chunk, bundle):
     c = cfg(name)
