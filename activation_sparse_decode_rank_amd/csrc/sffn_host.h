@@ -8,7 +8,9 @@
 //    often they activate);
 //  - the batch size from which the decode step computes every neuron (the union of the
 //    tokens' active sets grows with the batch: novita.ai activation-sparsity article,
-//    section 批次大小影響).
+//    section 批次大小影響);
+//  - the dense prefill's plan: its up-projection tile, the down projection's neuron
+//    splits and the layout of the caller's scratch.
 #pragma once
 #include <algorithm>
 #include <cmath>
@@ -154,6 +156,92 @@ inline int union_within_batch(const float* freq, int n, double max_rows, int max
   }
   return best;
 }
+
+// ---- dense prefill plan
+constexpr int kPfTile = 128;      // tokens per tile, and output columns per down tile
+constexpr int kPfMaxSplits = 16;  // most neuron splits of the down projection
+
+inline size_t pf_align(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// H row length the scratch holds: d_ffn rounded up to every neuron tile (64 to 192)
+inline size_t pf_rows(int n) { return (size_t)(n + 383) / 384 * 384; }
+
+// H row length of a run with up tiles of 32 it neurons: whole tiles
+inline int pf_np(int n, int it) { return (n + 32 * it - 1) / (32 * it) * (32 * it); }
+
+// Up tile (32 it neurons) for nbt token tiles. Gated layers take it = 3, plain ones 4 or 6,
+// whichever finishes first with one tile a compute unit at a time (rounds of tiles x the
+// tile's size; ties: 4). it = 2 replaces either when it needs fewer rounds over the compute
+// units x rows staged per workgroup (weight rows plus one or two token blocks), the measure
+// the kernel's times follow: with few token tiles the larger tiles leave units idle.
+inline int pf_up_it(int n, bool gated, bool lo, int nbt, int n_cus) {
+  auto cost = [&](int mr) {
+    const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
+    return (tiles + n_cus - 1) / n_cus * mr;
+  };
+  auto staged = [&](int it) {
+    const long long tiles = (long long)((n + 32 * it - 1) / (32 * it)) * nbt;
+    const long long rows = (gated ? 2 : 1) * 32 * it + (lo ? 2 : 1) * kPfTile;
+    return (tiles + n_cus - 1) / n_cus * rows;
+  };
+  int it = gated ? 3 : (cost(192) < cost(128) ? 6 : 4);
+  if (staged(2) < staged(it)) it = 2;
+  return it;
+}
+
+// Neuron splits of the down projection for nbt token tiles and H rows of np: doubled until
+// two workgroups a compute unit, keeping at least 8 stages of 32 neurons a split. Never
+// smaller for a larger np, never larger for more token tiles.
+inline int pf_splits(int d, int n_cus, int nbt, size_t np) {
+  const long long tiles = (long long)(d / kPfTile) * nbt;
+  int S = 1;
+  while (S < kPfMaxSplits && tiles * S < 2LL * n_cus && np / 32 >= (size_t)16 * S) S *= 2;
+  return S;
+}
+
+// Partial-sum scratch for chunks of up to Bp tokens: the largest splits x tokens of any
+// chunk size up to Bp, at the largest H row length (the scan ends at the first size that
+// needs no split).
+inline size_t pf_part_bytes(int d, int n, int n_cus, size_t Bp) {
+  size_t m = 0;
+  for (size_t t = kPfTile; t <= Bp; t += kPfTile) {
+    const int S = pf_splits(d, n_cus, (int)(t / kPfTile), pf_rows(n));
+    if (S == 1) break;
+    m = std::max(m, (size_t)S * t * (size_t)d * 4);
+  }
+  return m;
+}
+
+// Layout of the scratch for a chunk of Bp tokens (byte offsets, 256-byte aligned): x's fp16
+// hi and lo rows [Bp][d], h's hi and lo rows [Bp][pf_rows(n)], the split partial sums;
+// end = the bytes it spans.
+struct PfCarve {
+  size_t xh, xl, hh, hl, part, end;
+};
+inline PfCarve pf_carve(int d, int n, int n_cus, size_t Bp) {
+  PfCarve c;
+  size_t p = 0;
+  c.xh = p;
+  p += pf_align(Bp * (size_t)d * 2);
+  c.xl = p;
+  p += pf_align(Bp * (size_t)d * 2);
+  c.hh = p;
+  p += pf_align(Bp * pf_rows(n) * 2);
+  c.hl = p;
+  p += pf_align(Bp * pf_rows(n) * 2);
+  c.part = p;
+  p += pf_align(pf_part_bytes(d, n, n_cus, Bp));
+  c.end = p;
+  return c;
+}
+
+// Scratch for chunks of up to chunk tokens (rounded up to a whole tile); 0 for chunk < 1
+inline size_t pf_work_bytes(int d, int n, int n_cus, int chunk) {
+  if (chunk < 1) return 0;
+  const size_t Bp = (size_t)(chunk + kPfTile - 1) / kPfTile * kPfTile;
+  return pf_carve(d, n, n_cus, Bp).end;
+}
+
 
 }  // namespace host
 }  // namespace sffn

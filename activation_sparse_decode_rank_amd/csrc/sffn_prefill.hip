@@ -22,17 +22,15 @@
 // Both products stream their operands from memory straight into LDS through a pipeline of
 // several stages; the down kernel reads W_down's rows there with the LDS transpose read.
 #include "sffn_device.h"
+#include "sffn_host.h"
 
 namespace sffn {
 namespace {
 
-constexpr int PF_T = 128;  // tile edge: rows (neurons or columns) and tokens per workgroup
-constexpr int PF_SMAX = 16;  // most neuron splits of the down projection
+constexpr int PF_T = host::kPfTile;  // tokens per tile, and output columns per down tile
 // s_waitcnt operand (gfx9 encoding) that waits for LDS reads only: lgkmcnt 0, vmcnt and
 // expcnt at their maximum
 constexpr int WAIT_LGKM0 = 0xC07F;
-
-size_t pf_align(size_t v) { return (v + 255) & ~(size_t)255; }
 
 __device__ __forceinline__ float4_t pf_mfma(const half8_t& a, const half8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -391,32 +389,6 @@ __global__ __launch_bounds__(TPB) void k_pf_sum(const float* __restrict__ part, 
   }
 }
 
-// H row length for the scratch: d_ffn rounded up to every neuron tile (64 to 192)
-size_t pf_np(int n) { return (size_t)(n + 383) / 384 * 384; }
-
-// Neuron splits of the down projection for nbt token tiles and H rows of np: doubled until
-// two workgroups a compute unit (64 or 72 KB of LDS each), keeping at least 8 stages of 32
-// neurons a split.
-int pf_splits(const LayerDev& L, int nbt, size_t np) {
-  const long long tiles = (long long)(L.d / PF_T) * nbt;
-  int S = 1;
-  while (S < PF_SMAX && tiles * S < 2LL * L.n_cus && np / 32 >= (size_t)16 * S) S *= 2;
-  return S;
-}
-
-// partial-sum scratch for chunks of up to Bp tokens: the largest splits x tokens of any
-// chunk size up to Bp (the splits never grow with the tokens, so the scan ends at the
-// first size that needs none)
-size_t pf_part_bytes(const LayerDev& L, size_t Bp) {
-  size_t m = 0;
-  for (size_t t = PF_T; t <= Bp; t += PF_T) {
-    const int S = pf_splits(L, (int)(t / PF_T), pf_np(L.n));
-    if (S == 1) break;
-    m = std::max(m, (size_t)S * t * L.d * 4);
-  }
-  return m;
-}
-
 template <bool GATED, int IT, bool LO>
 void pf_up_launch(const LayerDev& L, const u32x4* xh, const u32x4* xl, int np, int nbt,
                   _Float16* hh, _Float16* hl, hipStream_t s) {
@@ -434,26 +406,9 @@ void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32
   hipLaunchKernelGGL(k_pf_split<LO>, dim3(std::min((items + TPB - 1) / TPB, 4 * L.n_cus)),
                      dim3(TPB), 0, s, xc, bc, Bp, d, xh, xl);
   const int nbt = Bp / PF_T;
-  // Neuron tile (32 it neurons). The gated forms take 96 neurons, whose stages (20 KB, or
-  // 28 KB with the lo halves) let two workgroups share a compute unit, one computing while
-  // the other waits at its barrier. The plain form takes 128 or 192, whichever finishes
-  // first with one tile a compute unit at a time: rounds of tiles x the tile's size (ties:
-  // 128). With few token tiles a 64-neuron tile can finish first: it stages fewer weight
-  // rows per token block but loads the token block for twice as many tiles. Measured time
-  // follows rounds over the compute units x bytes a workgroup stages, so that decides.
-  auto cost = [&](int mr) {
-    const long long tiles = (long long)((n + mr - 1) / mr) * nbt;
-    return (tiles + L.n_cus - 1) / L.n_cus * mr;
-  };
-  auto staged = [&](int it) {
-    const long long tiles = (long long)((n + 32 * it - 1) / (32 * it)) * nbt;
-    const long long per_stage = (L.gated ? 2 : 1) * 32 * it + (LO ? 2 : 1) * PF_T;  // rows
-    return (tiles + L.n_cus - 1) / L.n_cus * per_stage;
-  };
-  int it = L.gated ? 3 : (cost(192) < cost(128) ? 6 : 4);
-  if (staged(2) < staged(it)) it = 2;
-  const int mr = 32 * it;
-  const int np = (n + mr - 1) / mr * mr;  // H row length: whole neuron tiles
+  // up tile and down splits: the plan of sffn_host.h (pf_up_it, pf_splits)
+  const int it = host::pf_up_it(n, L.gated, LO, nbt, L.n_cus);
+  const int np = host::pf_np(n, it);  // H row length: whole neuron tiles
   if (L.gated) {
     if (it == 3) pf_up_launch<true, 3, LO>(L, xh, xl, np, nbt, hh, hl, s);
     else pf_up_launch<true, 2, LO>(L, xh, xl, np, nbt, hh, hl, s);
@@ -462,7 +417,7 @@ void pf_chunk(const LayerDev& L, const float* xc, int bc, int Bp, float* yc, u32
     else if (it == 4) pf_up_launch<false, 4, LO>(L, xh, xl, np, nbt, hh, hl, s);
     else pf_up_launch<false, 2, LO>(L, xh, xl, np, nbt, hh, hl, s);
   }
-  const int S = pf_splits(L, nbt, np);
+  const int S = host::pf_splits(d, L.n_cus, nbt, (size_t)np);
   hipLaunchKernelGGL(k_pf_down<LO>, dim3(nct * nbt * S), dim3(TPB), 0, s, L.w_down_t, L.down_ld,
                      L.b_out, reinterpret_cast<const u32x4*>(hh), reinterpret_cast<const u32x4*>(hl),
                      d, n, np, bc, Bp, S, yc, part);
@@ -479,14 +434,7 @@ bool prefill_ok(const LayerDev& L) { return L.w_f16 && L.d % PF_T == 0 && L.d <=
 
 // scratch for chunks of up to `chunk` tokens (rounded up to 128)
 size_t prefill_work_bytes(const LayerDev& L, int chunk) {
-  if (chunk < 1) return 0;
-  const size_t Bp = (size_t)(chunk + PF_T - 1) / PF_T * PF_T;
-  const size_t np = pf_np(L.n);
-  size_t b = 0;
-  b += 2 * pf_align(Bp * L.d * 2);           // xh, xl
-  b += 2 * pf_align(Bp * np * 2);            // hh, hl
-  b += pf_align(pf_part_bytes(L, Bp));       // split partial sums
-  return b;
+  return host::pf_work_bytes(L.d, L.n, L.n_cus, chunk);
 }
 
 // tokens the scratch holds per chunk (a multiple of 128; 0 when not even 128)
@@ -508,12 +456,12 @@ hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void*
     const int bc = std::min(chunk, B - b0);
     const int Bp = (bc + PF_T - 1) / PF_T * PF_T;
     char* p = static_cast<char*>(work);
-    auto take = [&](size_t bytes) { char* q = p; p += pf_align(bytes); return q; };
-    u32x4* xh = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
-    u32x4* xl = reinterpret_cast<u32x4*>(take((size_t)Bp * d * 2));
-    _Float16* hh = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));  // rows np <= pf_np(n)
-    _Float16* hl = reinterpret_cast<_Float16*>(take(Bp * pf_np(n) * 2));
-    float* part = reinterpret_cast<float*>(take(pf_part_bytes(L, Bp)));
+    const host::PfCarve c = host::pf_carve(d, n, L.n_cus, (size_t)Bp);  // within work_bytes
+    u32x4* xh = reinterpret_cast<u32x4*>(p + c.xh);
+    u32x4* xl = reinterpret_cast<u32x4*>(p + c.xl);
+    _Float16* hh = reinterpret_cast<_Float16*>(p + c.hh);  // rows np <= pf_rows(n)
+    _Float16* hl = reinterpret_cast<_Float16*>(p + c.hl);
+    float* part = reinterpret_cast<float*>(p + c.part);
     const float* xc = x + (size_t)b0 * d;
     float* yc = y + (size_t)b0 * d;
     if (fp16_act)

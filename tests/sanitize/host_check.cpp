@@ -111,6 +111,38 @@ int main() {
     }
   }
 
+  // ---- dense prefill plan: for random shapes, compute-unit counts and chunk sizes, every
+  // chunk up to the requested size fits the scratch sized for it, its h rows cover the
+  // row length of the tile its plan takes, and its partial-sum region covers its splits
+  for (int it = 0; it < 400; ++it) {
+    const int d = 128 * irand(1, 64), n = irand(1, 60000), cus = irand(1, 320);
+    const int chunk = irand(1, 3000);
+    const size_t work = sffn::host::pf_work_bytes(d, n, cus, chunk);
+    CHECK(sffn::host::pf_work_bytes(d, n, cus, 0) == 0);
+    const int cbp = (chunk + 127) / 128 * 128;
+    for (int bp = 128; bp <= cbp; bp += 128) {
+      const sffn::host::PfCarve c = sffn::host::pf_carve(d, n, cus, (size_t)bp);
+      CHECK(c.end <= work);
+      CHECK(c.xh == 0 && c.xl % 256 == 0 && c.hh % 256 == 0 && c.hl % 256 == 0 && c.part % 256 == 0);
+      CHECK(c.xl - c.xh >= (size_t)bp * d * 2 && c.hh - c.xl >= (size_t)bp * d * 2);
+      for (int gated = 0; gated < 2; ++gated) {
+        for (int lo = 0; lo < 2; ++lo) {
+          const int ut = sffn::host::pf_up_it(n, gated, lo, bp / 128, cus);
+          CHECK(gated ? (ut == 2 || ut == 3) : (ut == 2 || ut == 4 || ut == 6));
+          const int np = sffn::host::pf_np(n, ut);
+          CHECK(np >= n && np % (32 * ut) == 0 && (size_t)np <= sffn::host::pf_rows(n));
+          CHECK(c.hl - c.hh >= (size_t)bp * np * 2 && c.part - c.hl >= (size_t)bp * np * 2);
+          const int S = sffn::host::pf_splits(d, cus, bp / 128, (size_t)np);
+          CHECK(S >= 1 && S <= sffn::host::kPfMaxSplits && (S & (S - 1)) == 0);
+          if (S > 1) {
+            CHECK(c.end - c.part >= (size_t)S * bp * d * 4);
+            CHECK(np / 32 >= 8 * S);  // each split keeps at least 8 stages of 32 neurons
+          }
+        }
+      }
+    }
+  }
+
   // ---- permutation: the library's and the oracle's, equal, and valid
   for (int it = 0; it < 200; ++it) {
     const int n = irand(1, 5000), n_hot = irand(0, n);
