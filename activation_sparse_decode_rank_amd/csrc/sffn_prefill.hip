@@ -10,15 +10,15 @@
 // with SFFN_PREFILL_FP16_ACT) rounds the activations (x and h) to fp16 once and runs one
 // product each, half the matrix-core work and operand traffic, at fp16 activation precision.
 //
-// Three kernels per chunk of Bp tokens (Bp a multiple of 128; rows past the chunk's tokens
+// The kernels of a chunk of Bp tokens (Bp a multiple of 128; rows past the chunk's tokens
 // are zero):
 //  - k_pf_split: x [B][d] fp32 -> xh, xl [Bp][d] fp16;
 //  - k_pf_up:    h = relu(W_act x + b_act) (gated: times W_up x) for every neuron and token,
 //                as hh, hl [Bp][np] fp16 (np = d_ffn rounded up to the neuron tile, 64 to
 //                192; neurons past d_ffn are 0);
-//  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S a power of 2 up to 16)
-//                when the output tiles alone do not fill the GPU; the S partial sums go to scratch
-//                and k_pf_sum adds them in split order (y bitwise reproducible).
+//  - k_pf_down:  y = h W_down^T + b_out, the neurons split S ways (S a power of 2 up to
+//                16) when the output tiles alone do not fill the GPU; the S partial sums go
+//                to scratch and k_pf_sum adds them in split order (y bitwise reproducible).
 // Both products stream their operands from memory straight into LDS through a pipeline of
 // several stages; the down kernel reads W_down's rows there with the LDS transpose read.
 #include "sffn_device.h"
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(TPB) void k_pf_split(const float* __restrict__ x, i
 }
 
 // Up projection: workgroup (mt, bt) computes neurons [MR mt, +MR) x tokens [128 bt, +128)
-// (MR = 32 IT: 96, 128 or 192) over all d inputs, in stages of 32 inputs. Wave w takes
+// (MR = 32 IT: 64, 96, 128 or 192) over all d inputs, in stages of 32 inputs. Wave w takes
 // neurons 16 IT (w & 1) .. +16 IT and tokens 64 (w >> 1) .. +64 (IT x 4 tiles of 16 x 16,
 // for the gate and, gated, the up matrix). The operands reach LDS without passing through
 // registers (global_load_lds_dwordx4: each lane's 16 bytes land at the next 16 bytes of a
