@@ -1064,16 +1064,39 @@ def run_crossover(torch, args, cap):
                 "each, torch's activation precision. dense_route: "
                 "sparse_ffn_dense over the decode kernels, 64 tokens per pass. torch: fp16 "
                 "activations through hipBLASLt"}
+    # a short prompt: 128 tokens (one token tile) of the same layers
+    S_ = 128
+    pf_ms_s = time_fn(lambda: [layers[l].prefill(Xp[l][:S_], y=yp[l][:S_], work=pf_work)
+                               for l in range(LP)])
+    pf16_ms_s = time_fn(lambda: [layers[l].prefill(Xp[l][:S_], y=yp[l][:S_], work=pf_work,
+                                                   fp16_activations=True) for l in range(LP)])
+    lib_ms_s = time_fn(lambda: [layers[l].dense(Xp[l][:S_], y=yp[l][:S_]) for l in range(LP)])
+
+    def torch_prefill_short():
+        for l in range(LP):
+            o = originals[l]
+            a = F.linear(Xh[l][:S_], o.w_a, o.b_a.half())
+            h = F.relu(a) * F.linear(Xh[l][:S_], o.w_u)
+            _ = torch.matmul(h, o.w_o) + o.b_o.half()
+
+    th_ms_s = time_fn(torch_prefill_short)
+    out_pf_short = {
+        "prefill_ms_per_layer": round(pf_ms_s / LP, 4),
+        "prefill_fp16_act_ms_per_layer": round(pf16_ms_s / LP, 4),
+        "dense_route_ms_per_layer": round(lib_ms_s / LP, 4),
+        "torch_ms_per_layer": round(th_ms_s / LP, 4)}
     out = {"workload": f"{cfg.name}: {cfg.description}", "rows": rows,
            "crossover_union_fraction": cross,
            "note": "dense route = every neuron through the forward kernels (tile path), no "
                    "predictor; the decode switches to it when sffn_desc.dense_union is set and "
                    "the expected union exceeds it",
-           "prefill_512_tokens": out_pf}
+           "prefill_512_tokens": out_pf, "prefill_128_tokens": out_pf_short}
     log(f"prefill 512 tokens: library prefill {pf_ms / LP:.3f} ms/layer "
         f"({out_pf['prefill_tflops']} TFLOP/s), fp16 activations {pf16_ms / LP:.3f}, "
         f"dense route {lib_ms / LP:.3f}, torch "
         f"{th_ms / LP:.3f} ms/layer")
+    log(f"prefill 128 tokens: library prefill {pf_ms_s / LP:.3f} ms/layer, fp16 activations "
+        f"{pf16_ms_s / LP:.3f}, dense route {lib_ms_s / LP:.3f}, torch {th_ms_s / LP:.3f}")
     del layers, originals
     return out
 
