@@ -104,6 +104,24 @@ def test_prefill_full_size_gated():
     assert max(errs) <= REL_TOL, max(errs)
 
 
+def test_prefill_full_size_opt175b_slice():
+    """The full OPT-175B-shaped slice (d 12288, d_ffn 49152, plain) at 256 tokens in one
+    chunk: 96 output column tiles, two token tiles, the down projection split; three sampled
+    tokens against the oracle."""
+    c = cfg("C5")
+    say("prefill full C5 slice, 256 tokens")
+    s, L, _ = build(c, 0, max_batch=4, profile_tokens=256)
+    from synth import make_tokens
+    X = make_tokens(c, 256, 522, "cuda")
+    y = _prefill(s, X, 256)
+    sel = [0, 130, 255]
+    Xh = to_np(X)[sel]
+    Y = oracle.dense(Xh, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
+    errs = rel_err_rows(y[sel], Y)
+    say(f"  err={max(errs):.2e}")
+    assert max(errs) <= REL_TOL, max(errs)
+
+
 def test_prefill_rejects():
     """fp32 weights have no matrix-core prefill (SFFN_ERR_UNSUPPORTED; the Python layer then
     takes the dense route); scratch below one 128-token chunk is refused."""
