@@ -7,6 +7,12 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# torch first: its wheel carries its own HIP runtime, which its libraries load by file
+# name. Loaded after this library (which binds the system runtime of the same soname), it
+# would be a second runtime in the process, and device memory torch allocates would not be
+# valid for this library's launches. Loaded before, this library binds torch's runtime.
+import torch  # noqa: F401,E402
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_ffn.so")
 
