@@ -39,6 +39,8 @@ constexpr int X_LDS_MAX = 48 * 1024;  // tokens are staged in LDS when they fit 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));   // LDS transpose-read result
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 // Buffer resources for the raw buffer load/store builtins: word 3 of the descriptor for
 // the gfx9 family (untyped 32-bit data, no swizzle), and the cache-policy bit that makes an

@@ -231,8 +231,6 @@ __global__ __launch_bounds__(TPB) void k_pf_up(const void* __restrict__ w_act, i
 // tokens 64 (w & 1) .. +64 and columns 64 (w >> 1) .. +64; two workgroups share a compute
 // unit. The loop steps as the up kernel's (the next stage's fragments are read while the
 // matrix cores take the current ones); a split with an odd stage count ends on one step.
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int pf_wsw(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 template <bool LO>
 __global__ __launch_bounds__(TPB) void k_pf_down(const void* __restrict__ w_down_t, int ld_down,

@@ -928,8 +928,10 @@ __global__ __launch_bounds__(TPB) void k_split_x(const float* __restrict__ x, in
 // multiple of 32 positions each). Each wave streams its own 32-position chunks (chunk k of
 // the split goes to wave k % 4): lane l reads row l/8 + 8j (j < 4) of the chunk, 16-byte
 // piece l%8 of the block (whole 128-byte lines), stores the piece as is in the wave's own
-// LDS buffer, and gathers 8 consecutive positions of one column as the right operand of
-// v_mfma_f32_16x16x32_f16; the activations (token l%16, positions
+// LDS buffer, and reads 8 consecutive positions of one column back as the right operand of
+// v_mfma_f32_16x16x32_f16 with two LDS transpose reads (ds_read_b64_tr_b16: in each
+// 16-lane group, lane i names position k0 + i / 4 at column n0 + 4 (i % 4), and lane j
+// receives column n0 + j of positions k0 .. k0 + 3); the activations (token l%16, positions
 // 8*(l/16)..+7) are the left one, as a hi + lo fp16 pair. No workgroup barrier in the
 // loop; loads run one batch of KB chunks ahead. At the end the four waves' sums are added
 // in wave order through LDS and leave as plain stores for KS == 1; else as float atomics
@@ -947,9 +949,9 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
                                                    float* __restrict__ dn_part,
                                                    int32_t* __restrict__ dn_cnt) {
   constexpr int KB = NT <= 2 ? 2 : 1;   // chunks per load batch
-  // chunk buffer: [32 positions][64 columns] fp16 at a pitch of 33 words, so a wave's gather
-  // of one position row per lane group (8 rows apart) touches all 32 banks
-  constexpr int WP = 66;
+  // chunk buffer: [32 positions][64 columns] fp16 at a pitch of 34 words (the transpose
+  // reads take 8-byte aligned addresses)
+  constexpr int WP = 68;
   __shared__ __attribute__((aligned(16))) _Float16 s_wt[TPB / 64][KB][DCH * WP];
   __shared__ float4_t s_acc[TPB / 64][4][NT][64];
   __shared__ int32_t s_idx[IDX_CAP];
@@ -1049,9 +1051,15 @@ __global__ __launch_bounds__(TPB) void k_down_mfma(const void* __restrict__ w_do
           }
 #pragma unroll
           for (int cg = 0; cg < 4; ++cg) {
-            half8_t bw;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bw[e] = bufk[(8 * g + e) * WP + 16 * cg + r16];
+            // positions 8g .. 8g + 7 of column 16 cg + r16
+            const int col = 16 * cg + 4 * (r16 & 3), ra = 8 * g + (r16 >> 2);
+            const short4_t ta = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4_t*)(bufk + ra * WP + col));
+            const short4_t tb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4_t*)(bufk + (ra + 4) * WP + col));
+            const half8_t bw = __builtin_shufflevector(__builtin_bit_cast(half4_t, ta),
+                                                       __builtin_bit_cast(half4_t, tb), 0, 1, 2, 3,
+                                                       4, 5, 6, 7);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
               acc[cg][tt] = mfma16(ah[tt], bw, acc[cg][tt]);
