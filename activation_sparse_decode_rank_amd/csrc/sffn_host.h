@@ -242,6 +242,21 @@ inline size_t pf_work_bytes(int d, int n, int n_cus, int chunk) {
   return pf_carve(d, n, n_cus, Bp).end;
 }
 
+// Tokens a scratch of work_bytes holds per chunk: the largest multiple of the tile, up to
+// 2^20 tokens, whose scratch fits (0 when not even one tile fits). pf_work_bytes never
+// falls as the chunk grows, so a binary search over the tile counts finds it.
+inline int pf_chunk_tokens(int d, int n, int n_cus, size_t work_bytes) {
+  int lo = 0, hi = (1 << 20) / kPfTile;  // tiles: lo fits (0 trivially), answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (pf_work_bytes(d, n, n_cus, mid * kPfTile) <= work_bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo * kPfTile;
+}
+
 
 }  // namespace host
 }  // namespace sffn

@@ -437,12 +437,7 @@ size_t prefill_work_bytes(const LayerDev& L, int chunk) {
 
 // tokens the scratch holds per chunk (a multiple of 128; 0 when not even 128)
 int prefill_chunk(const LayerDev& L, size_t work_bytes) {
-  int c = 0;
-  for (int t = PF_T; t <= (1 << 20); t += PF_T) {
-    if (prefill_work_bytes(L, t) > work_bytes) break;
-    c = t;
-  }
-  return c;
+  return host::pf_chunk_tokens(L.d, L.n, L.n_cus, work_bytes);
 }
 
 hipError_t run_prefill(const LayerDev& L, const float* x, int B, float* y, void* work,

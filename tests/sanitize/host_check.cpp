@@ -119,6 +119,18 @@ int main() {
     const int chunk = irand(1, 3000);
     const size_t work = sffn::host::pf_work_bytes(d, n, cus, chunk);
     CHECK(sffn::host::pf_work_bytes(d, n, cus, 0) == 0);
+    // the chunk a scratch holds: the largest tile multiple whose scratch fits, checked
+    // against a linear scan from there (the scratch size never falls as the chunk grows)
+    for (int probe = 0; probe < 3; ++probe) {
+      const size_t wb = probe == 0 ? work : probe == 1 ? work - 1 : work + (size_t)irand(0, 1 << 26);
+      const int ct = sffn::host::pf_chunk_tokens(d, n, cus, wb);
+      CHECK(ct % 128 == 0 && ct >= 0 && ct <= (1 << 20));
+      if (ct > 0) CHECK(sffn::host::pf_work_bytes(d, n, cus, ct) <= wb);
+      if (ct < (1 << 20)) CHECK(sffn::host::pf_work_bytes(d, n, cus, ct + 128) > wb);
+      if (probe == 0) CHECK(ct >= (chunk + 127) / 128 * 128);
+    }
+    for (int t = 128; t + 128 <= 4096; t += 128)
+      CHECK(sffn::host::pf_work_bytes(d, n, cus, t) <= sffn::host::pf_work_bytes(d, n, cus, t + 128));
     const int cbp = (chunk + 127) / 128 * 128;
     for (int bp = 128; bp <= cbp; bp += 128) {
       const sffn::host::PfCarve c = sffn::host::pf_carve(d, n, cus, (size_t)bp);
