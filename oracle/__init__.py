@@ -11,6 +11,6 @@ against true activations, which needs trained predictors the pages describe but 
 """
 from .oracle import (  # noqa: F401
     F16, F32, F64, build, load, half_to_double, predict, threshold, compact, forward, dense,
-    preact, profile_counts, permutation, pack_rows, n_hot_for, threads, open_library,
+    dense_f16act, round_half, preact, profile_counts, permutation, pack_rows, n_hot_for, threads, open_library,
     set_library, OMP_LIB_PATH,
 )

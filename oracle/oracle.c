@@ -24,6 +24,10 @@
  *               the gated form puts the ReLU on the gate (section 第一階段).
  *  - dense:     the same FFN over every neuron with no mask (the definition the sparse
  *               output must reduce to when the mask covers every true activation).
+ *  - dense_f16act: dense with x rounded to binary16 before the up products and h before
+ *               the down product (the library's optional fp16-activation prefill; the
+ *               pages run prefill dense and fix no precision for it: PowerInfer-2
+ *               article, section 4.1.1 NPU-Centric Prefill).
  *  - profile, permutation, pack: offline activation counts, hot neurons first, and a
  *               neuron table back to the original positions ("Fase fuera de línea" and
  *               "Colocación y gestión de neuronas" on the unite.ai overview).
@@ -226,6 +230,66 @@ int oracle_dense(int32_t d, int32_t n, int32_t B, int32_t gated, const float* X,
     if (b_o)
       for (int32_t j = 0; j < d; ++j) y[j] += (double)b_o[j];
   }
+  return ORC_OK;
+}
+
+/* A double rounded to the nearest IEEE 754 binary16 value, ties to even. The format has
+ * normal numbers from 2^-14 up, spaced 2^(e-10) in the binade [2^e, 2^(e+1)); below 2^-14
+ * the subnormals keep the spacing 2^-24; the largest finite value is 65504 = (2 - 2^-10)
+ * 2^15, and magnitudes from the midpoint 65520 on round to infinity. Zeros, infinities and
+ * NaN pass through. */
+double oracle_round_half(double v) {
+  if (v != v || v == 0.0) return v;
+  const double a = fabs(v);
+  if (a >= 65520.0) return copysign(INFINITY, v);
+  int ex;
+  (void)frexp(a, &ex); /* a = m 2^ex, m in [0.5, 1): a lies in [2^(ex-1), 2^ex) */
+  int e = ex - 1;
+  if (e < -14) e = -14; /* subnormals: the smallest binade's spacing */
+  const double q = ldexp(1.0, e - 10);
+  /* a / q is exact (q is a power of two); nearbyint rounds to nearest, ties to even, in
+   * the default rounding mode */
+  return copysign(nearbyint(a / q) * q, v);
+}
+
+int oracle_round_half_array(int64_t count, const double* in, double* out) {
+  if (count < 0 || (count > 0 && (!in || !out))) return ORC_ERR;
+  for (int64_t k = 0; k < count; ++k) out[k] = oracle_round_half(in[k]);
+  return ORC_OK;
+}
+
+/* dense with fp16 activations: x rounded to binary16 before the up (and gate) products, h
+ * rounded before the down product; every other step as in oracle_dense, in double. */
+int oracle_dense_f16act(int32_t d, int32_t n, int32_t B, int32_t gated, const float* X,
+                        const void* Wa, const void* Wu, const void* Wo, int32_t w_dtype,
+                        const float* b_a, const float* b_o, double* Y) {
+  if (d <= 0 || n <= 0 || B <= 0 || !X || !Wa || !Wo || !Y || !dtype_ok(w_dtype) ||
+      (gated && !Wu))
+    return ORC_ERR;
+  double* xr = (double*)malloc((size_t)d * sizeof(double));
+  if (!xr) return ORC_ERR;
+  for (int32_t b = 0; b < B; ++b) {
+    const float* x = X + (size_t)b * d;
+    double* y = Y + (size_t)b * d;
+    for (int32_t t = 0; t < d; ++t) xr[t] = oracle_round_half((double)x[t]);
+    for (int32_t j = 0; j < d; ++j) y[j] = 0.0;
+    for (int32_t i = 0; i < n; ++i) {
+      double a = 0.0;
+      for (int32_t t = 0; t < d; ++t) a += elem(Wa, w_dtype, (size_t)i * d + t) * xr[t];
+      a += b_a ? (double)b_a[i] : 0.0;
+      double h = (a > 0.0) ? a : 0.0;
+      if (gated) {
+        double u = 0.0;
+        for (int32_t t = 0; t < d; ++t) u += elem(Wu, w_dtype, (size_t)i * d + t) * xr[t];
+        h = h * u;
+      }
+      h = oracle_round_half(h);
+      for (int32_t j = 0; j < d; ++j) y[j] += h * elem(Wo, w_dtype, (size_t)i * d + j);
+    }
+    if (b_o)
+      for (int32_t j = 0; j < d; ++j) y[j] += (double)b_o[j];
+  }
+  free(xr);
   return ORC_OK;
 }
 

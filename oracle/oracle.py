@@ -47,12 +47,14 @@ def _configure(lib):
     lib.oracle_compact.argtypes = [I32, I32, P, P, P, P]
     lib.oracle_forward.argtypes = [I32, I32, I32, I32, P, P, P, P, I32, P, P, P, I32, P, P]
     lib.oracle_dense.argtypes = [I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
+    lib.oracle_dense_f16act.argtypes = [I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
+    lib.oracle_round_half_array.argtypes = [I64, P, P]
     lib.oracle_preact.argtypes = [I32, I32, I32, P, P, I32, P, P]
     lib.oracle_profile_counts.argtypes = [I32, I32, I32, P, P, I32, P, P]
     lib.oracle_permutation.argtypes = [P, I32, I32, P]
     lib.oracle_pack_rows.argtypes = [P, P, P, I32, I64]
-    for name in ("predict", "threshold", "compact", "forward", "dense", "preact",
-                 "profile_counts", "permutation", "pack_rows"):
+    for name in ("predict", "threshold", "compact", "forward", "dense", "dense_f16act",
+                 "round_half_array", "preact", "profile_counts", "permutation", "pack_rows"):
         getattr(lib, "oracle_" + name).restype = C.c_int
     if hasattr(lib, "oracle_threads"):
         lib.oracle_threads.argtypes = []
@@ -196,6 +198,30 @@ def dense(X, Wa, Wo, *, Wu=None, b_a=None, b_o=None):
     _check(load().oracle_dense(d, n, B, 1 if Wu is not None else 0, _ptr(X), _ptr(Wa), _ptr(Wu),
                                _ptr(Wo), _dtype_code(Wa), _ptr(b_a), _ptr(b_o), _ptr(Y)), "dense")
     return Y
+
+
+def dense_f16act(X, Wa, Wo, *, Wu=None, b_a=None, b_o=None):
+    """Y[B, d] (fp64): dense with fp16 activations, x rounded to binary16 (nearest, ties
+    to even) before the up products and h before the down product."""
+    X = _c(X, np.float32)
+    Wa, Wo, Wu = _c(Wa), _c(Wo), _c(Wu)
+    b_a, b_o = _c(b_a, np.float32), _c(b_o, np.float32)
+    B, d = X.shape
+    n = Wa.shape[0]
+    Y = np.empty((B, d), np.float64)
+    _check(load().oracle_dense_f16act(d, n, B, 1 if Wu is not None else 0, _ptr(X), _ptr(Wa),
+                                      _ptr(Wu), _ptr(Wo), _dtype_code(Wa), _ptr(b_a), _ptr(b_o),
+                                      _ptr(Y)), "dense_f16act")
+    return Y
+
+
+def round_half(v):
+    """Each value (fp64) rounded to the nearest binary16 value, ties to even (overflow to
+    infinity from 65520 on), returned as fp64."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty_like(v)
+    _check(load().oracle_round_half_array(v.size, _ptr(v), _ptr(out)), "round_half")
+    return out
 
 
 def preact(X, Wa, b_a=None):

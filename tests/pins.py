@@ -298,6 +298,70 @@ def pin_pack_rows():
         assert np.array_equal(oracle.pack_rows(dst, inv), src)
 
 
+def pin_round_half_ieee():
+    """binary16 rounding equals numpy's IEEE 754 conversion (a library routine: nearest,
+    ties to even) on random magnitudes over the normal and subnormal ranges, on exact ties
+    in every binade and among the subnormals, and at the overflow boundary (65504 stays,
+    65520 and above go to infinity), for both signs."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    v = np.concatenate([
+        rng.standard_normal(20000) * np.exp2(rng.uniform(-30.0, 17.0, 20000)),
+        # ties: (m + 1/2) spacings in binade [2^e, 2^(e+1)), spacing 2^(e-10)
+        np.array([(2 * m + 1) * 2.0 ** (e - 11) for e in range(-14, 16) for m in (1024, 1500, 2045)]),
+        # ties among the subnormals (spacing 2^-24)
+        np.array([(2 * k + 1) * 2.0 ** -25 for k in range(0, 1024, 37)]),
+        np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e300, 2.0 ** -25, 2.0 ** -26, 0.0]),
+    ])
+    v = np.concatenate([v, -v])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).astype(np.float64)
+    got = oracle.round_half(v)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+
+
+def pin_dense_f16act_exact_inputs():
+    """With every x and every h exactly representable in binary16 (small integers, |h| <
+    2048), both roundings are identities and the fp16-activation dense FFN equals the dense
+    FFN bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    for gated, d, n, B in ((False, 24, 40, 3), (True, 8, 33, 2)):
+        Wa = rng.integers(-1, 2, (n, d)).astype(np.float16)
+        Wu = rng.integers(-1, 2, (n, d)).astype(np.float16) if gated else None
+        Wo = rng.integers(-2, 3, (n, d)).astype(np.float16)
+        X = rng.integers(-2, 3, (B, d)).astype(np.float32)
+        b_a = rng.integers(-3, 4, n).astype(np.float32)
+        b_o = rng.integers(-3, 4, d).astype(np.float32)
+        g = X.astype(np.float64) @ Wa.astype(np.float64).T + b_a
+        h = np.maximum(g, 0.0) * (X.astype(np.float64) @ Wu.astype(np.float64).T if gated else 1.0)
+        assert np.abs(h).max() < 2048 and np.any(h != 0)
+        Y = oracle.dense(X, Wa, Wo, Wu=Wu, b_a=b_a, b_o=b_o)
+        Yf = oracle.dense_f16act(X, Wa, Wo, Wu=Wu, b_a=b_a, b_o=b_o)
+        assert np.array_equal(Y, Yf)
+
+
+def pin_dense_f16act_rounds_x_and_h():
+    """Each rounding alone, on a one-neuron layer with unit weights. x = 1 + 2^-11 lies
+    halfway between 1 and 1 + 2^-10 and enters the product as 1 (ties to even); x = 1 +
+    3 2^-11 enters as 1 + 2^-9. With x = 0 and b_act = 2049 (halfway between 2048 and 2050)
+    h enters the down product as 2048; with 2051, as 2052. The dense FFN keeps them all."""
+    W = np.ones((1, 1), np.float16)
+    X = np.array([[1 + 2.0 ** -11], [1 + 3 * 2.0 ** -11]], np.float32)
+    assert np.array_equal(oracle.dense_f16act(X, W, W), [[1.0], [1 + 2.0 ** -9]])
+    assert np.array_equal(oracle.dense(X, W, W), X.astype(np.float64))
+    # the x rounding where h's cannot hide it: W_act = (1, -1), x = (1 + 2^-11, 1) gives
+    # h = 0 from the rounded x but 2^-11 (exact in binary16) from x as given
+    Wa2 = np.array([[1.0, -1.0]], np.float16)
+    Wo2 = np.ones((1, 2), np.float16)
+    X2 = np.array([[1 + 2.0 ** -11, 1.0]], np.float32)
+    assert np.array_equal(oracle.dense_f16act(X2, Wa2, Wo2), [[0.0, 0.0]])
+    assert np.array_equal(oracle.dense(X2, Wa2, Wo2), [[2.0 ** -11, 2.0 ** -11]])
+    X0 = np.zeros((1, 1), np.float32)
+    for b, r in ((2049.0, 2048.0), (2051.0, 2052.0)):
+        ba = np.array([b], np.float32)
+        assert oracle.dense_f16act(X0, W, W, b_a=ba)[0, 0] == r
+        assert oracle.dense(X0, W, W, b_a=ba)[0, 0] == b
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

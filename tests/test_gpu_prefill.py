@@ -6,8 +6,9 @@ tokens (sampled tokens against the oracle). y within 1e-3 of max|y| per token (r
 the fp32 accumulation bound), bitwise equal from run to run.
 
 The fp16-activation form (SFFN_PREFILL_FP16_ACT) rounds x and h to fp16 once: it is checked
-against the oracle's arithmetic with those two roundings applied (the same 1e-3 reading),
-and against the exact FFN within the first-order bound those roundings allow."""
+against the oracle's fp16-activation FFN (oracle.dense_f16act, the same two roundings; the
+same 1e-3 reading), and against the exact FFN within the first-order bound those roundings
+allow."""
 
 import numpy as np
 import pytest
@@ -152,30 +153,17 @@ def test_prefill_rejects():
 U16 = 2.0 ** -11  # unit roundoff of round-to-nearest fp16 (normal range)
 
 
-def _fp16(a):
-    return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)
-
-
-def _dense_fp16_act(X, L):
-    """The dense FFN with the two roundings of the fp16-activation prefill applied (x before
-    the up products, h before the down product), fp64 everywhere else. Returns y and the
-    first-order bound on |y - FFN(x)| that those roundings allow (worst-case signs):
+def _f16act_bound(X, L):
+    """First-order bound on |y - FFN(x)| that the two roundings of the fp16-activation
+    prefill allow (x before the up products, h before the down product; worst-case signs):
     u (sum_k |W_o[k]| (dh_k + |h_k|)) with dh_k <= u A_k, A_k = |W_a[k]| . |x| (plain), or
-    |W_g[k]| . |x| |v_k| + relu(g_k) |W_u[k]| . |x| (gated, v = W_u x)."""
+    |W_g[k]| . |x| |v_k| + relu(g_k) |W_u[k]| . |x| (gated, v = W_u x); all from the exact
+    quantities, in fp64."""
     X = np.asarray(X, np.float64)
     Wa = np.asarray(L["w_a"], np.float64)
     Wo = np.asarray(L["w_o"], np.float64)
     Wu = None if L["w_u"] is None else np.asarray(L["w_u"], np.float64)
     ba = 0.0 if L["b_a"] is None else np.asarray(L["b_a"], np.float64)
-    bo = 0.0 if L["b_o"] is None else np.asarray(L["b_o"], np.float64)
-    Xr = _fp16(X)
-    g = Xr @ Wa.T + ba
-    h = np.maximum(g, 0.0)
-    if Wu is not None:
-        v = Xr @ Wu.T
-        h = h * v
-    y = _fp16(h) @ Wo + bo
-    # the bound, from the exact quantities
     ax = np.abs(X)
     ge = X @ Wa.T + ba
     he = np.maximum(ge, 0.0)
@@ -184,8 +172,11 @@ def _dense_fp16_act(X, L):
         ve = X @ Wu.T
         A = A * np.abs(ve) + he * (ax @ np.abs(Wu).T)
         he = he * ve
-    bound = U16 * (A + np.abs(he)) @ np.abs(Wo)
-    return y, bound
+    return U16 * (A + np.abs(he)) @ np.abs(Wo)
+
+
+def _oracle_f16act(X, L):
+    return oracle.dense_f16act(X, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
 
 
 @pytest.mark.parametrize("name,d,n,B,chunk,bundle", [
@@ -204,9 +195,9 @@ def test_prefill_fp16_act(name, d, n, B, chunk, bundle):
     y = _prefill(s, X, chunk, fp16_act=True)
     sel = sorted(set([0, 1, B // 2, B - 1] + list(range(0, B, max(1, B // 8)))))
     Xh = to_np(X)[sel]
-    R, bound = _dense_fp16_act(Xh, L)
+    R, bound = _oracle_f16act(Xh, L), _f16act_bound(Xh, L)
     errs = rel_err_rows(y[sel], R)
-    say(f"  err vs rounded reference={max(errs):.2e}")
+    say(f"  err vs the oracle's fp16-activation FFN={max(errs):.2e}")
     assert max(errs) <= REL_TOL, max(errs)
     Y = oracle.dense(Xh, L["w_a"], L["w_o"], Wu=L["w_u"], b_a=L["b_a"], b_o=L["b_o"])
     scale = np.max(np.abs(Y), axis=1, keepdims=True)
@@ -220,7 +211,7 @@ def test_prefill_fp16_act(name, d, n, B, chunk, bundle):
 
 def test_prefill_fp16_act_full_size_gated():
     """The full Llama-7B-shaped gated layer at 512 tokens with fp16 activations: sampled
-    tokens against the rounded reference."""
+    tokens against the oracle's fp16-activation FFN."""
     c = cfg("C3")
     say("prefill fp16 activations, full C3 layer, 512 tokens")
     s, L, _ = build(c, 0, max_batch=4, profile_tokens=256)
@@ -228,7 +219,7 @@ def test_prefill_fp16_act_full_size_gated():
     X = make_tokens(c, 512, 524, "cuda")
     y = _prefill(s, X, 512, fp16_act=True)
     sel = [0, 100, 255, 511]
-    R, _ = _dense_fp16_act(to_np(X)[sel], L)
+    R = _oracle_f16act(to_np(X)[sel], L)
     errs = rel_err_rows(y[sel], R)
     say(f"  err={max(errs):.2e}")
     assert max(errs) <= REL_TOL, max(errs)

@@ -44,6 +44,12 @@ MUTANTS = [
     ("pack_inverse", "memcpy((char*)dst + (size_t)i * row_bytes, (const char*)src + (size_t)perm[i] * row_bytes,",
      "memcpy((char*)dst + (size_t)perm[i] * row_bytes, (const char*)src + (size_t)i * row_bytes,", 0),
     ("profile_counts_ge", "if (a > 0.0) ++cnt;", "if (a >= 0.0) ++cnt;", 0),
+    ("round_half_ties_away", "return copysign(nearbyint(a / q) * q, v);",
+     "return copysign(round(a / q) * q, v);", 0),
+    ("round_half_no_subnormal_spacing", "  if (e < -14) e = -14;", "  if (e < -24) e = -24;", 0),
+    ("round_half_overflow_early", "if (a >= 65520.0)", "if (a > 65504.0)", 0),
+    ("f16act_h_unrounded", "      h = oracle_round_half(h);\n", "", 0),
+    ("f16act_x_unrounded", "xr[t] = oracle_round_half((double)x[t]);", "xr[t] = (double)x[t];", 0),
 ]
 
 
